@@ -1,0 +1,139 @@
+"""Throughput of the KDA forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+One step = one kda_fwd call over the training-prefill workload B=4, H=32, T=16384, d_k = d_v = 128
+(bf16 q/k/v/o, float32 g/beta/state, chunk 32) with its inputs already resident in HBM.  Prints one
+JSON line with the whole-job tokens/s, the roofline position of the kernel (algorithmic bytes per
+launch over the average launch time measured with HIP events on the launch stream) and the float64
+CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s at H=32,d=128,T=16K + % bf16 MFMA peak (1 GPU)"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix
+WORKLOAD = 2
+
+
+def algorithmic_bytes(B, T, H, Dk, Dv, io_bytes=2, has_S0=False):
+    """HBM bytes one launch must move: q, k, v, o (io dtype), g (float32), beta (float32), S_T (+ S0)."""
+    per_token_head = (2 * Dk + 2 * Dv) * io_bytes + 4 * Dk + 4
+    state = B * H * Dk * Dv * 4 * (2 if has_S0 else 1)
+    return B * T * H * per_token_head + state
+
+
+def algorithmic_flops(B, T, H, Dk, Dv, C=32):
+    """Matrix-product flops of the chunkwise form per launch (exact lower triangles, no padding):
+    per chunk of C tokens and head: L, A (C(C-1)/2, C(C+1)/2 dot products of length Dk), W = T Kg and
+    U_tilde = T V (C(C+1)/2 * (Dk + Dv) multiply-adds), W S and Q S (2 C Dk Dv), A U (C(C+1)/2 Dv),
+    Kbar^T U (C Dk Dv); 2 flops per multiply-add."""
+    tri = C * (C + 1) // 2
+    stri = C * (C - 1) // 2
+    per_chunk = 2 * ((stri + tri) * Dk + tri * (Dk + Dv) + 2 * C * Dk * Dv + tri * Dv + C * Dk * Dv)
+    return B * H * (T / C) * per_chunk
+
+
+def cpu_baseline(d, threads):
+    """float64 oracle on batch row 0 (all 32 heads, all 16384 tokens) of the workload."""
+    import oracle
+    s = {n: np.ascontiguousarray(d[n][:1]) for n in ("q", "k", "v", "g", "beta")}
+    t = time.perf_counter()
+    oracle.recurrence(s["q"], s["k"], s["v"], s["g"], s["beta"], threads=threads)
+    dt = time.perf_counter() - t
+    T = s["q"].shape[1]
+    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"batch row 0 of the workload: B=1, H=32, T={T} (float64 token recurrence, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU; --gpus N with N > 1 is not supported "
+              "(heads are independent, so N GPUs would each take a share of B*H)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import linear_recurrent_attention_amd as kda
+
+    w = synth.WORKLOADS[WORKLOAD]
+    B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
+    d = synth.core_inputs(WORKLOAD, seed=0)
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v", "g", "beta")}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(torch.bfloat16)
+    o = torch.empty((B, T, H, Dv), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step():
+        kda.kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], out=o, state_out=ST)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        stream.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            step()
+            b.record(stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+
+    tokens = B * T
+    value = tokens / (wall / args.steps)
+    abytes = algorithmic_bytes(B, T, H, Dk, Dv)
+    aflops = algorithmic_flops(B, T, H, Dk, Dv)
+    achieved_gbs = abytes / avg_launch_s / 1e9
+    achieved_tflops = aflops / avg_launch_s / 1e12
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "Dk": Dk, "Dv": Dv, "chunk": 32,
+                   "io": "bf16 q/k/v/o, float32 g/beta/state"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kda_fwd_bf16_kernel", "avg_launch_ms": avg_launch_s * 1e3,
+                     "algorithmic_bytes": abytes},
+        "mfma": {"achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": achieved_tflops / BF16_PEAK_TFLOPS, "algorithmic_flops": aflops},
+    }
+    if not args.no_cpu:
+        try:
+            threads = len(os.sched_getaffinity(0))
+        except AttributeError:
+            threads = os.cpu_count() or 1
+        out["cpu_baseline"] = cpu_baseline(d, threads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,73 @@
+// C-ABI entry points: argument validation and dispatch to the gfx950 kernels.
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+kda_status check_fwd(const kda_fwd_desc* d, const void* q, const void* k, const void* v, const float* g,
+                     const float* beta, const float* S0, const void* o, const float* S_T) {
+    if (!d) return KDA_ERR_INVALID_ARG;
+    if (d->B < 1 || d->H < 1 || d->T < 0 || d->Dk < 1 || d->Dv < 1) return KDA_ERR_INVALID_ARG;
+    if (d->flags != 0) return KDA_ERR_INVALID_ARG;
+    if (d->io_dtype != KDA_F32 && d->io_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+    if (d->o_dtype != KDA_F32 && d->o_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+    if (d->io_dtype == KDA_F32 && d->o_dtype != KDA_F32) return KDA_ERR_INVALID_ARG;
+    if (!(d->scale == d->scale)) return KDA_ERR_INVALID_ARG;  // NaN scale
+    // sizes the kernels index with 32-bit ints: tokens and heads per call
+    if ((long long)d->B * d->H > (1LL << 30) || d->T > (1 << 30)) return KDA_ERR_INVALID_ARG;
+    if (d->T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(o, 4)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(g, 8) || !aligned(beta, 4) || !aligned(S0, 8) || !aligned(S_T, 8)) return KDA_ERR_INVALID_ARG;
+    if (d->io_dtype == KDA_BF16) {
+        if (d->Dk != 128 || d->Dv != 128) return KDA_ERR_UNSUPPORTED;
+        if (d->chunk != 0 && d->chunk != 32) return KDA_ERR_UNSUPPORTED;
+    } else {
+        if (d->Dk != d->Dv || (d->Dk != 64 && d->Dk != 128)) return KDA_ERR_UNSUPPORTED;
+        if (d->chunk != 0 && d->chunk != 16) return KDA_ERR_UNSUPPORTED;
+    }
+    // outputs must not alias inputs (S_T == S0 is the one allowed overlap)
+    if (o && (o == q || o == k || o == v || o == (const void*)g)) return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, const float* S0, void* o, float* S_T, hipStream_t stream) {
+    const kda_status st = check_fwd(desc, q, k, v, g, beta, S0, o, S_T);
+    if (st != KDA_OK) return st;
+    kda::Params p;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0; p.o = o; p.S_T = S_T;
+    p.B = desc->B; p.T = desc->T; p.H = desc->H; p.Dk = desc->Dk; p.Dv = desc->Dv;
+    p.scale = desc->scale;
+    p.o_f32 = desc->o_dtype == KDA_F32;
+    hipError_t e;
+    if (desc->T == 0)
+        e = kda::launch_state_copy(p, stream);
+    else if (desc->io_dtype == KDA_BF16)
+        e = kda::launch_fwd_bf16(p, stream);
+    else
+        e = kda::launch_fwd_f32(p, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+const char* kda_error_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: no kernel for this configuration";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error at launch";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+    }
+    return "unknown kda_status";
+}
+
+int kda_version(void) { return 100; }
+
+}  // extern "C"

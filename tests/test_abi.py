@@ -1,0 +1,103 @@
+"""C-ABI: the library loads, exports what include/kda.h declares, and rejects bad arguments
+before touching the GPU (no compute call is made in these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_recurrent_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_\s\*]*?\b(kda_[a-z0-9_]+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    decl = declared_functions()
+    assert "kda_fwd" in decl and "kda_error_string" in decl
+    for name in decl:
+        assert hasattr(L, name), name
+    assert set(decl) == set(_lib.EXPORTS)
+
+
+def test_version_and_error_strings():
+    L = _lib.lib()
+    assert L.kda_version() >= 100
+    for code in (0, -1, -2, -3, -4, 7):
+        assert L.kda_error_string(code)
+
+
+def desc(**kw):
+    d = dict(B=1, T=64, H=2, Dk=128, Dv=128, chunk=0, io_dtype=_lib.KDA_BF16, o_dtype=_lib.KDA_BF16, scale=1.0,
+             flags=0)
+    d.update(kw)
+    return _lib.FwdDesc(**d)
+
+
+FAKE = 0x10000  # never dereferenced: validation fails first, or T = 0 makes no launch
+
+
+def call(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=0, o=FAKE + 0x100000, S_T=0):
+    return _lib.fwd_raw(d, q, k, v, g, beta, S0, o, S_T, None)
+
+
+def test_null_descriptor():
+    assert _lib.lib().kda_fwd(None, *([None] * 9)) == _lib.KDA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field,value", [("B", 0), ("H", 0), ("T", -1), ("Dk", 0), ("Dv", -3), ("flags", 1),
+                                         ("io_dtype", 5), ("o_dtype", 9)])
+def test_bad_sizes_and_enums(field, value):
+    assert call(desc(**{field: value})) == _lib.KDA_ERR_INVALID_ARG
+
+
+def test_nan_scale():
+    assert call(desc(scale=float("nan"))) == _lib.KDA_ERR_INVALID_ARG
+
+
+def test_f32_inputs_need_f32_output():
+    assert call(desc(io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_BF16, Dk=64, Dv=64)) == _lib.KDA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("ptr", ["q", "k", "v", "g", "beta", "o"])
+def test_null_required_pointer(ptr):
+    assert call(desc(), **{ptr: 0}) == _lib.KDA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("ptr,off", [("q", 2), ("v", 1), ("g", 4), ("o", 2), ("S0", 4), ("S_T", 4)])
+def test_misaligned_pointer(ptr, off):
+    assert call(desc(), **{ptr: FAKE + 0x20000 + off}) == _lib.KDA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(Dk=64, Dv=64), dict(Dk=128, Dv=64), dict(chunk=64),
+                                dict(io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_F32, Dk=96, Dv=96),
+                                dict(io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_F32, Dk=64, Dv=64, chunk=32)])
+def test_unsupported_shapes(kw):
+    assert call(desc(**kw)) == _lib.KDA_ERR_UNSUPPORTED
+
+
+def test_output_aliasing_input_rejected():
+    assert call(desc(), o=FAKE) == _lib.KDA_ERR_INVALID_ARG
+
+
+def test_empty_sequence_without_state_output_is_a_no_op():
+    # T = 0 and S_T = NULL: nothing to compute, nothing launched
+    assert call(desc(T=0), q=0, k=0, v=0, g=0, beta=0, o=0) == _lib.KDA_OK
+
+
+def test_python_binding_checks_shapes():
+    torch = pytest.importorskip("torch")
+    import linear_recurrent_attention_amd as kda
+    q = torch.zeros(1, 4, 2, 128)
+    with pytest.raises(ValueError):
+        kda.kda_fwd(q, q, q, q, torch.zeros(1, 4, 2))  # CPU tensors are rejected before any call

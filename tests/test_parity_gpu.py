@@ -1,0 +1,181 @@
+"""GPU parity: libkda.so (through the C ABI) against the float64 CPU oracle on seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _metrics import TOL_BF16, TOL_F32, rel_max, rel_max_bf16_out
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _kda():
+    import linear_recurrent_attention_amd as kda
+    return kda
+
+
+def to_dev(d, io):
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    t = {n: torch.from_numpy(np.ascontiguousarray(d[n])).to(DEV) for n in ("q", "k", "v", "g", "beta")}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(dt)
+    return t
+
+
+def gpu_fwd(d, io, S0=None, o_dtype=None, scale=1.0):
+    t = to_dev(d, io)
+    S0t = None if S0 is None else torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).to(DEV)
+    o, ST = _kda().kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=S0t, scale=scale, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), ST.cpu().numpy()
+
+
+def sub(d, b=None, h=None, T=None):
+    out = {}
+    for n in ("q", "k", "v", "g", "beta"):
+        a = d[n]
+        if b is not None:
+            a = a[b]
+        if T is not None:
+            a = a[:, :T]
+        if h is not None:
+            a = a[:, :, h]
+        out[n] = np.ascontiguousarray(a)
+    return out
+
+
+def rand_small(seed, B, T, H, D=128, io="bf16", s0=True):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, H, D))
+    k = rng.standard_normal((B, T, H, D))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    rnd = synth.bf16_round if io == "bf16" else (lambda x: x.astype(np.float32))
+    d = dict(q=rnd(q), k=rnd(k), v=rnd(rng.standard_normal((B, T, H, D))),
+             g=(-5.0 / (1 + np.exp(-rng.standard_normal((B, T, H, D)) * 1.5))).astype(np.float32),
+             beta=(1 / (1 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32))
+    S0 = (rng.standard_normal((B, H, D, D)) * 0.3).astype(np.float32) if s0 else None
+    return d, S0
+
+
+# ---- the workloads ------------------------------------------------------------------------------------
+
+def test_workload0_f32():
+    """B1 H2 T256 D64, float32 end to end: max|err|/rms <= 1e-4 on o and S_T."""
+    d = synth.core_inputs(0, seed=0)
+    o, ST = gpu_fwd(d, "f32")
+    o_ref, S_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    assert rel_max(o, o_ref) <= TOL_F32
+    assert rel_max(ST, S_ref) <= TOL_F32
+
+
+def test_workload1_bf16():
+    """B1 H16 T4096 D128 with S0: bf16 o (format allowance), float32 o (literal), S_T (literal)."""
+    d = synth.core_inputs(1, seed=0)
+    o_ref, S_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
+    o, ST = gpu_fwd(d, "bf16", S0=d["S0"])
+    assert rel_max_bf16_out(o, o_ref) <= TOL_BF16
+    assert rel_max(ST, S_ref) <= TOL_BF16
+    o32, ST32 = gpu_fwd(d, "bf16", S0=d["S0"], o_dtype=torch.float32)
+    assert rel_max(o32, o_ref) <= TOL_BF16
+    assert np.array_equal(ST32, ST)
+
+
+def test_workload2_full_launch_sampled_heads():
+    """B4 H32 T16384 D128 in the benchmark's launch; the oracle recomputes 6 sampled (b, h) sequences."""
+    d = synth.core_inputs(2, seed=0)
+    o, ST = gpu_fwd(d, "bf16")
+    rng = np.random.default_rng(2)
+    picks = [(0, 0), (3, 31)] + [(int(rng.integers(4)), int(rng.integers(32))) for _ in range(4)]
+    for b, h in picks:
+        s = {n: d[n][b:b + 1, :, h:h + 1] for n in ("q", "k", "v", "g", "beta")}
+        o_ref, S_ref = oracle.recurrence(s["q"], s["k"], s["v"], s["g"], s["beta"])
+        assert rel_max_bf16_out(o[b:b + 1, :, h:h + 1], o_ref) <= TOL_BF16, (b, h)
+        assert rel_max(ST[b:b + 1, h:h + 1], S_ref) <= TOL_BF16, (b, h)
+
+
+# ---- edge cases ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 2, 17, 31, 32, 33, 95, 160])
+def test_ragged_lengths_bf16(T):
+    d, S0 = rand_small(T, 1, T, 3)
+    o_ref, S_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=S0)
+    o, ST = gpu_fwd(d, "bf16", S0=S0, o_dtype=torch.float32)
+    assert rel_max(o, o_ref) <= TOL_BF16
+    assert rel_max(ST, S_ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("T,D", [(1, 64), (15, 64), (16, 64), (47, 64), (100, 128)])
+def test_ragged_lengths_f32(T, D):
+    d, S0 = rand_small(T, 2, T, 2, D=D, io="f32")
+    o_ref, S_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=S0, scale=0.7)
+    o, ST = gpu_fwd(d, "f32", S0=S0, scale=0.7)
+    assert rel_max(o, o_ref) <= TOL_F32
+    assert rel_max(ST, S_ref) <= TOL_F32
+
+
+def test_batch_heads_not_multiple_of_eight():
+    """B*H = 15 takes the plain workgroup mapping; scale != 1."""
+    d, S0 = rand_small(5, 3, 70, 5)
+    o_ref, S_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=S0, scale=0.5)
+    o, ST = gpu_fwd(d, "bf16", S0=S0, o_dtype=torch.float32, scale=0.5)
+    assert rel_max(o, o_ref) <= TOL_BF16
+    assert rel_max(ST, S_ref) <= TOL_BF16
+
+
+def test_decay_at_bound_and_no_decay():
+    """g = -5 on half of the channels (largest in-chunk factors) and g = 0 (no decay) on the rest."""
+    d, S0 = rand_small(6, 1, 96, 8)
+    d["g"][..., ::2] = -5.0
+    d["g"][..., 1::2] = 0.0
+    o_ref, S_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=S0)
+    o, ST = gpu_fwd(d, "bf16", S0=S0, o_dtype=torch.float32)
+    assert rel_max(o, o_ref) <= TOL_BF16
+    assert rel_max(ST, S_ref) <= TOL_BF16
+
+
+def test_beta_zero_pure_decay_on_gpu():
+    """beta = 0: S_T = Diag(exp(sum g)) S0 exactly in form; o_t = S0^T (exp(b_t) q_t)."""
+    d, S0 = rand_small(7, 1, 64, 8)
+    d["beta"][:] = 0
+    d["g"] *= 0.01  # keep exp(sum g) well inside float32 range over 64 tokens
+    o, ST = gpu_fwd(d, "bf16", S0=S0, o_dtype=torch.float32)
+    bsum = np.cumsum(d["g"].astype(np.float64), axis=1)
+    want_S = np.exp(bsum[:, -1])[..., None] * S0
+    want_o = np.einsum("bhij,bthi->bthj", S0.astype(np.float64), np.exp(bsum) * d["q"])
+    assert rel_max(ST, want_S) <= TOL_BF16
+    assert rel_max(o, want_o) <= TOL_BF16
+
+
+def test_empty_sequence_copies_state():
+    kda = _kda()
+    S0 = torch.randn(2, 3, 128, 128, device=DEV)
+    e = torch.empty(2, 0, 3, 128, device=DEV, dtype=torch.bfloat16)
+    o, ST = kda.kda_fwd(e, e, e, torch.empty(2, 0, 3, 128, device=DEV), torch.empty(2, 0, 3, device=DEV), S0=S0)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 3, 128) and torch.equal(ST, S0)
+
+
+def test_state_in_place_and_segment_split_bitwise():
+    """S_T == S0 is allowed; two calls split on the chunk grid equal one call bit for bit."""
+    kda = _kda()
+    d, S0 = rand_small(8, 2, 128, 4)
+    t = to_dev(d, "bf16")
+    S = torch.from_numpy(S0).to(DEV)
+    o_full, S_full = kda.kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=S)
+    Sc = S.clone()
+    o1, _ = kda.kda_fwd(*(t[n][:, :64].contiguous() for n in ("q", "k", "v", "g", "beta")), S0=Sc, state_out=Sc)
+    o2, _ = kda.kda_fwd(*(t[n][:, 64:].contiguous() for n in ("q", "k", "v", "g", "beta")), S0=Sc, state_out=Sc)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o1, o2], dim=1), o_full)
+    assert torch.equal(Sc, S_full)
+
+
+def test_deterministic_across_runs():
+    d, S0 = rand_small(9, 2, 200, 8)
+    a = gpu_fwd(d, "bf16", S0=S0)
+    b = gpu_fwd(d, "bf16", S0=S0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
