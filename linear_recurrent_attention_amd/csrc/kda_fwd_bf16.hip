@@ -7,29 +7,35 @@
 // chunk, with incoming state S, cumulative log-decay b_r = sum_{j<=r} g_j and Gamma = exp(b):
 //   L = strictly lower part of (K*Gamma)(K/Gamma)^T,  A = lower part of (Q*Gamma)(K/Gamma)^T,
 //   T = (I + Diag(beta) L)^{-1} Diag(beta)            (the triangular "UT" inverse),
-//   W = T (K*Gamma),  U_tilde = T V,  U = U_tilde - W S,
+//   U = T (V - (K*Gamma) S),
 //   O = (Q*Gamma) S + A U,
 //   S <- Diag(Gamma_last) S + (K*exp(b_last - b))^T U.
 // The 1/Gamma factors are formed only inside 16-token sub-tiles, relative to the cumulative decay
-// at the sub-tile's midpoint token, so every factor lies in [e^-40, e^40] (section 3.1-3.2: the
-// lower bound g >= -5 is what keeps these in range).  A product that couples the two sub-tiles
-// moves the earlier sub-tile's factor to the later sub-tile's reference first.
+// at the sub-tile's token 7, so every factor lies in [e^-40, e^40] (sections 3.1-3.2: the lower
+// bound g >= -5 is what keeps these in range).  The block of L and A that couples the two
+// sub-tiles uses the earlier sub-tile's K/Gamma moved to the later sub-tile's reference.
 //
-// Mapping: one workgroup of 4 waves per (batch, head, value half): the 128 value columns are
-// split over two workgroups that recompute the key-side products, so 2*B*H workgroups fill the
-// chip.  Each wave owns 16 value columns of the float32 state in matrix-core accumulator layout
-// for the whole sequence; chunk inputs are prefetched one chunk ahead into registers.
+// Mapping.  One workgroup per (batch, head, value half): the 128 value columns are split over two
+// workgroups that both compute the key-side products, so 2*B*H workgroups fill the chip; the two
+// halves of a head are placed on the same XCD so their common reads of q, k, g share its L2.
+// Each workgroup runs 8 waves as a two-stage pipeline over chunks:
+//   key waves 0-3   chunk n:   element-wise decay factors, then the Gram products L and A;
+//   value waves 4-7 chunk n-1: UT inverse (wave 4), then the state-dependent products and the
+//                              output; wave 4+w owns 16 value columns of the float32 state in
+//                              matrix-core accumulator layout for the whole run.
+// Both groups execute the same three workgroup barriers per step; data passes from the key waves
+// to the value waves through LDS buffers indexed by chunk parity.  Chunk inputs are prefetched
+// one chunk ahead into registers.
 //
 // Matrix-core operands (v_mfma_f32_16x16x32_{bf16,f16}, float32 accumulate):
 //   L = Km Kh^T                      bf16
 //   A = Qm Kh^T                      split bf16 (hi*hi + hi*lo + lo*hi)
-//   W = T Kg                         f16
-//   U_tilde = T V                    T split bf16, V bf16
-//   U = U_tilde - W S, Q S           f16
+//   X = V - Kg S,  Q S               f16
+//   U = T X                          split bf16
 //   A U                              split bf16
 //   Kbar^T U                         f16
-// The inverse T is a float32 forward substitution on the two 16x16 diagonal blocks plus one
-// off-diagonal block product.
+// The inverse solves the two 16x16 diagonal blocks of (I + Diag(beta) L) by forward substitution
+// in float32 registers and forms the off-diagonal block with float32 matrix-core products.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -41,33 +47,42 @@ constexpr int SUB = 16;     // tokens per sub-tile
 constexpr int DK = 128;
 constexpr int DV = 128;
 constexpr int DVH = 64;     // value columns per workgroup
-constexpr int NTHR = 256;   // 4 waves
+constexpr int NTHR = 512;   // 8 waves: 4 key waves + 4 value waves
 constexpr int LDK = DK + 8; // padded row (16-bit elements) of token-major [C][DK] tiles
-constexpr int LDT = C + 8;  // padded row of channel-major [DK][C] tiles
-constexpr int LDA = C + 8;  // padded row of [C][C] 16-bit tiles
-constexpr int LDF = C + 1;  // padded row of [C][C] float tiles
-constexpr int LDO = DVH + 4;
+constexpr int LDT = C + 8;  // padded row of channel-major [DV][C] tiles
+constexpr int LDT8 = C + 4; // padded row of channel-major tiles read 8 bytes at a time
+constexpr int LDA = C + 8;  // [C][C] 16-bit tiles
+constexpr int LDA8 = C + 4; // [C][C] 16-bit tiles read 8 bytes at a time
+constexpr int LDF = C + 4;  // [C][C] float tiles
 
-struct alignas(16) Smem {
-    uint16_t qmh[C][LDK], qml[C][LDK];     // Q * exp(b - b_mid)      split bf16
-    uint16_t km[C][LDK];                   // K * exp(b - b_mid)      bf16
-    uint16_t khh[C][LDK], khl[C][LDK];     // K * exp(b_mid - b)      split bf16
-    uint16_t k1h[SUB][LDK], k1l[SUB][LDK]; // sub-tile 0 rows of K/Gamma at sub-tile 1's reference
-    uint16_t qg[C][LDK];                   // Q * Gamma               f16
-    uint16_t wn[C][LDK];                   // -W = -T (K * Gamma)     f16
-    uint16_t kgt[DK][LDT];                 // (K * Gamma)^T           f16
-    uint16_t kbt[DK][LDT];                 // (K * exp(b_last - b))^T f16
-    uint16_t vt[DVH][LDT];                 // V^T (this value half)   bf16
-    uint16_t ah[C][LDA], al[C][LDA];       // A                       split bf16
-    uint16_t th[C][LDA], tl[C][LDA];       // T                       split bf16
-    uint16_t tf[C][LDA];                   // T                       f16
-    float lf[C][LDF];                      // L (strictly lower)
-    float xf[C][LDF];                      // (I + Diag(beta) L)^{-1}
-    float yf[SUB][SUB + 1];
-    float ost[C][LDO];                     // output staging
-    float tot[4][DK];                      // per 8-token octet sums of g
-    float gamc[DK];                        // Gamma of the chunk's last token
+struct alignas(16) KeyTiles {                // written and read by the key waves within one step
+    uint16_t qmh[C][LDK], qml[C][LDK];       // Q * exp(b - b_ref)      split bf16
+    uint16_t km[C][LDK];                     // K * exp(b - b_ref)      bf16
+    uint16_t khh[C][LDK], khl[C][LDK];       // K * exp(b_ref - b)      split bf16
+    uint16_t k1h[SUB][LDK], k1l[SUB][LDK];   // sub-tile 0 rows of K/Gamma at sub-tile 1's reference
+    float tot[4][DK];                        // per 8-token octet sums of g
+};
+struct alignas(16) Handoff2 {                // key -> value, double buffered by chunk parity
+    uint16_t qg[C][LDK];                     // Q * Gamma                 f16
+    uint16_t kgn[C][LDK];                    // -(K * Gamma)              f16
+    uint16_t kbt[DK][LDT8];                  // (K * exp(b_last - b))^T   f16
+    uint16_t ah[C][LDA8], al[C][LDA8];       // A                         split bf16
+    float gamc[DK];                          // Gamma of the chunk's last token
+};
+struct alignas(16) Handoff1 {                // key -> value, one buffer (written after the reader is done)
+    float lf[C][LDF];                        // L (strictly lower within the diagonal blocks)
+    uint16_t vt[DVH][LDT];                   // V^T (this value half)     bf16
     float beta[C];
+};
+struct alignas(16) ValueTiles {              // value waves only
+    uint16_t th[C][LDA], tl[C][LDA];         // T split bf16
+    float xf[C][LDF];                        // diagonal blocks of (I + Diag(beta) L)^{-1}
+};
+struct alignas(16) Smem {
+    KeyTiles key;
+    Handoff2 h2[2];
+    Handoff1 h1;
+    ValueTiles val;
 };
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -77,71 +92,294 @@ __device__ __forceinline__ u32x4 ld8x2(const uint16_t* p0, const uint16_t* p1) {
     u32x2 b = *reinterpret_cast<const u32x2*>(p1);
     return u32x4{a.x, a.y, b.x, b.y};
 }
+// Low 16-bit halves of a and b as one word (a's in the low half); likewise the high halves.
+__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
-struct Raw {  // one thread's share of one chunk of input, as loaded
+struct Raw {  // one key thread's share of one chunk of input, as loaded
     uint32_t q[8], k[8], v[8];
-    float2 g[8];
+    f32x2 g[8];
     float beta;
 };
 
-__device__ __forceinline__ void load_chunk(Raw& r, const Params& p, size_t bh_tok0, int t0, int wave, int lane,
-                                           int half) {
-    // tokens t0 + 8*wave + i; this thread's key channels 2*lane, 2*lane+1; value columns
-    // half*64 + 2*lane (+1) for lane < 32; beta for token t0 + 8*wave + lane for lane < 8.
-    // Tokens past the end read a clamped (valid) address and are replaced by zeros, which leaves
-    // the state unchanged (k = v = 0, beta = 0, g = 0).  Requires T >= 1.
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = t0 + 8 * wave + i;
-        const bool ok = t < p.T;
-        const size_t row = bh_tok0 + (size_t)(ok ? t : p.T - 1) * p.H;  // (b*T + t)*H + h
-        const size_t tk = row * DK + 2 * lane;
-        const uint32_t qv = *reinterpret_cast<const uint32_t*>((const uint16_t*)p.q + tk);
-        const uint32_t kv = *reinterpret_cast<const uint32_t*>((const uint16_t*)p.k + tk);
-        const float2 gv = *reinterpret_cast<const float2*>(p.g + tk);
-        const uint32_t vv = *reinterpret_cast<const uint32_t*>((const uint16_t*)p.v + row * DV + half * DVH +
-                                                               2 * (lane & 31));
-        r.q[i] = ok ? qv : 0u;
-        r.k[i] = ok ? kv : 0u;
-        r.g[i] = ok ? gv : make_float2(0.f, 0.f);
-        r.v[i] = (ok && lane < 32) ? vv : 0u;
-    }
-    const int tb = t0 + 8 * wave + (lane & 7);
-    const bool okb = lane < 8 && tb < p.T;
-    const float bv = p.beta[bh_tok0 + (size_t)(tb < p.T ? tb : p.T - 1) * p.H];
-    r.beta = okb ? bv : 0.f;
+// Per-thread constants of the key waves' chunk loads (byte offsets within a chunk).
+struct KeyLoad {
+    uint32_t off[8];   // token 8*kw + i, key channels 2*lane, 2*lane+1 of q/k (g: twice this)
+    uint32_t voff[8];  // token 8*kw + i, value columns half*64 + 2*(lane & 31) (+1)
+    uint32_t boff;     // beta of token 8*kw + (lane & 7)
+    uint32_t lane_b, vlane_b, tok_b;  // for the clamped tail loads
+    int kw, lane;
+};
+
+// A global-memory pointer every lane agrees on, held in scalar registers, so that loads and stores
+// use a scalar base plus a 32-bit per-lane offset.
+typedef __attribute__((address_space(1))) char gchar;
+__device__ __forceinline__ gchar* uniform_gptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (gchar*)(((uint64_t)hi << 32) | lo);
+}
+template <typename Tv>
+__device__ __forceinline__ Tv gload(const gchar* base, uint32_t off) {
+    return *reinterpret_cast<const __attribute__((address_space(1))) Tv*>(base + off);
+}
+template <typename Tv>
+__device__ __forceinline__ void gstore(gchar* base, uint32_t off, Tv v) {
+    *reinterpret_cast<__attribute__((address_space(1))) Tv*>(base + off) = v;
 }
 
-template <bool OUT_F32>
-__global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
-    __shared__ Smem sm;
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int l16 = lane & 15, g4 = lane >> 4;
-
-    // workgroup -> (batch*head, value half); siblings of one head land on the same XCD
-    int bh, half;
-    const int nbh = p.B * p.H;
-    if ((nbh & 7) == 0) {
-        const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-        half = local & 1;
-        bh = (local >> 1) * 8 + xcd;
+// Tokens t0 + 8*kw + i: key channels 2*lane, 2*lane+1; value columns half*64 + 2*(lane & 31) (+1);
+// beta of token t0 + 8*kw + (lane & 7).  Tokens past the end read the last valid row; mask_tail()
+// zeroes them when the chunk is consumed.  Nothing here uses the loaded values, so the loads stay
+// in flight until their first use one step later.  Requires T >= 1 and t0 < T.
+__device__ __forceinline__ void load_chunk(Raw& r, const Params& p, const KeyLoad& kl, size_t row0, int t0) {
+    const size_t ce = (row0 + (size_t)t0 * p.H) * DK;  // element offset of the chunk's first row
+    const gchar* qc = uniform_gptr((const uint16_t*)p.q + ce);
+    const gchar* kc = uniform_gptr((const uint16_t*)p.k + ce);
+    const gchar* gc = uniform_gptr(p.g + ce);
+    const gchar* vc = uniform_gptr((const uint16_t*)p.v + ce);
+    const gchar* bc = uniform_gptr(p.beta + row0 + (size_t)t0 * p.H);
+    if (t0 + C <= p.T) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            r.q[i] = gload<uint32_t>(qc, kl.off[i]);
+            r.k[i] = gload<uint32_t>(kc, kl.off[i]);
+            r.g[i] = gload<f32x2>(gc, 2 * kl.off[i]);
+            r.v[i] = gload<uint32_t>(vc, kl.voff[i]);
+        }
+        r.beta = gload<float>(bc, kl.boff);
     } else {
-        bh = blockIdx.x >> 1;
-        half = blockIdx.x & 1;
+        const int lim = p.T - 1 - t0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t tb = (uint32_t)min(8 * kl.kw + i, lim) * kl.tok_b;
+            const uint32_t o = tb + kl.lane_b, ov = tb + kl.vlane_b;  // both non-negative, < 2^31
+            r.q[i] = gload<uint32_t>(qc, o);
+            r.k[i] = gload<uint32_t>(kc, o);
+            r.g[i] = gload<f32x2>(gc, 2 * o);
+            r.v[i] = gload<uint32_t>(vc, ov);
+        }
+        r.beta = gload<float>(bc, (uint32_t)min(8 * kl.kw + (kl.lane & 7), lim) * 4u * p.H);
     }
-    const int b = bh / p.H, h = bh - b * p.H;
-    const size_t bh_tok0 = (size_t)b * p.T * p.H + h;  // row index of token 0: (b*T + 0)*H + h
+}
 
-    // zero the parts of the [C][C] tiles that no chunk writes (upper block of A, T)
-    for (int e = tid; e < SUB * SUB; e += NTHR) {
-        const int r = e >> 4, c = SUB + (e & 15);
-        sm.ah[r][c] = 0; sm.al[r][c] = 0; sm.th[r][c] = 0; sm.tl[r][c] = 0; sm.tf[r][c] = 0;
+// Zero the tokens at or past T (k = v = 0, beta = 0, g = 0 leaves the state unchanged).
+__device__ __forceinline__ void mask_tail(Raw& r, int T, int t0, int kw, int lane) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (t0 + 8 * kw + i >= T) {
+            r.q[i] = 0u; r.k[i] = 0u; r.v[i] = 0u;
+            r.g[i] = f32x2{0.f, 0.f};
+        }
+    }
+    if (t0 + 8 * kw + (lane & 7) >= T) r.beta = 0.f;
+}
+
+// ------------------------------------------------------------------------------------------------
+// key waves: one step = chunk n (nothing when n == nchunk); three barriers
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoad& kl, size_t row0, int n,
+                                         int nchunk, Raw& cur, Raw& nxt) {
+    const int kw = kl.kw, lane = kl.lane;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int c0 = 2 * lane;   // key channels c0, c0 + 1
+    const int sig = kw >> 1;   // sub-tile of this thread's octet
+    const int hf = kw & 1;     // first or second octet of the sub-tile
+    const bool work = n < nchunk;
+    const int t0 = n * C;
+    Handoff2& H = sm.h2[n & 1];
+
+    // ---------------- part 1: octet cumulative decay and sub-tile factors
+    float qm0[8], qm1[8], km0[8], km1[8], kh0[8], kh1[8];
+    if (work) {
+        if (t0 + C > p.T) mask_tail(cur, p.T, t0, kw, lane);
+        float s0[8], s1[8];
+        {
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                a0 += cur.g[i][0]; a1 += cur.g[i][1];
+                s0[i] = a0; s1[i] = a1;
+            }
+        }
+        *reinterpret_cast<float2*>(&sm.key.tot[kw][c0]) = make_float2(s0[7], s1[7]);
+        // reference = cumulative decay at the sub-tile's token 7 (end of its first octet)
+        const float r0 = hf ? 0.f : s0[7] * kLog2e, r1 = hf ? 0.f : s1[7] * kLog2e;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = 8 * kw + i;
+            const float y0 = s0[i] * kLog2e - r0, y1 = s1[i] * kLog2e - r1;
+            const float e0 = __builtin_amdgcn_exp2f(y0), e1 = __builtin_amdgcn_exp2f(y1);
+            const float f0 = __builtin_amdgcn_exp2f(-y0), f1 = __builtin_amdgcn_exp2f(-y1);
+            const float q0 = bf16lo_to_f(cur.q[i]), q1 = bf16hi_to_f(cur.q[i]);
+            const float k0 = bf16lo_to_f(cur.k[i]), k1 = bf16hi_to_f(cur.k[i]);
+            qm0[i] = q0 * e0; qm1[i] = q1 * e1;
+            km0[i] = k0 * e0; km1[i] = k1 * e1;
+            kh0[i] = k0 * f0; kh1[i] = k1 * f1;
+            uint32_t hi, lo;
+            split_bf16(qm0[i], qm1[i], hi, lo);
+            *reinterpret_cast<uint32_t*>(&sm.key.qmh[t][c0]) = hi;
+            *reinterpret_cast<uint32_t*>(&sm.key.qml[t][c0]) = lo;
+            *reinterpret_cast<uint32_t*>(&sm.key.km[t][c0]) = pack_bf16(km0[i], km1[i]);
+            split_bf16(kh0[i], kh1[i], hi, lo);
+            *reinterpret_cast<uint32_t*>(&sm.key.khh[t][c0]) = hi;
+            *reinterpret_cast<uint32_t*>(&sm.key.khl[t][c0]) = lo;
+        }
+        if (n + 1 < nchunk) load_chunk(nxt, p, kl, row0, t0 + C);  // prefetch the next chunk
+    }
+    lds_barrier();  // ---- barrier 1
+
+    // ---------------- part 2: factors referenced to the chunk start and chunk end
+    if (work) {
+        float tt0[4], tt1[4];
+#pragma unroll
+        for (int o = 0; o < 4; ++o) { tt0[o] = sm.key.tot[o][c0]; tt1[o] = sm.key.tot[o][c0 + 1]; }
+        const float pA0 = tt0[0], pA1 = tt1[0];                                      // b at token 7
+        const float pB0 = tt0[0] + tt0[1] + tt0[2], pB1 = tt1[0] + tt1[1] + tt1[2];  // b at token 23
+        const float bC0 = pB0 + tt0[3], bC1 = pB1 + tt1[3];                          // b at token 31
+        const float p0 = sig ? pB0 : pA0, p1 = sig ? pB1 : pA1;
+        const float eP0 = fexp(p0), eP1 = fexp(p1);
+        const float eC0 = fexp(bC0 - p0), eC1 = fexp(bC1 - p1);
+        uint32_t kb[8];
+        const float nP0 = -eP0, nP1 = -eP1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = 8 * kw + i;
+            *reinterpret_cast<uint32_t*>(&H.qg[t][c0]) = pack_f16(qm0[i] * eP0, qm1[i] * eP1);
+            *reinterpret_cast<uint32_t*>(&H.kgn[t][c0]) = pack_f16(km0[i] * nP0, km1[i] * nP1);
+            kb[i] = pack_f16(kh0[i] * eC0, kh1[i] * eC1);
+        }
+        // token pairs of channel c0 (low halves) and of channel c0 + 1 (high halves)
+        const u32x4 b0 = {perm_lo(kb[0], kb[1]), perm_lo(kb[2], kb[3]), perm_lo(kb[4], kb[5]), perm_lo(kb[6], kb[7])};
+        const u32x4 b1 = {perm_hi(kb[0], kb[1]), perm_hi(kb[2], kb[3]), perm_hi(kb[4], kb[5]), perm_hi(kb[6], kb[7])};
+        *reinterpret_cast<u32x2*>(&H.kbt[c0][8 * kw]) = u32x2{b0.x, b0.y};
+        *reinterpret_cast<u32x2*>(&H.kbt[c0][8 * kw + 4]) = u32x2{b0.z, b0.w};
+        *reinterpret_cast<u32x2*>(&H.kbt[c0 + 1][8 * kw]) = u32x2{b1.x, b1.y};
+        *reinterpret_cast<u32x2*>(&H.kbt[c0 + 1][8 * kw + 4]) = u32x2{b1.z, b1.w};
+        if (sig == 0) {
+            // K/Gamma rows of sub-tile 0 moved to sub-tile 1's reference: factor exp(b_23 - b_7) <= 1
+            const float f0 = fexp(pB0 - pA0), f1 = fexp(pB1 - pA1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int t = 8 * kw + i;
+                uint32_t hi, lo;
+                split_bf16(kh0[i] * f0, kh1[i] * f1, hi, lo);
+                *reinterpret_cast<uint32_t*>(&sm.key.k1h[t][c0]) = hi;
+                *reinterpret_cast<uint32_t*>(&sm.key.k1l[t][c0]) = lo;
+            }
+        }
+        if (kw == 0) *reinterpret_cast<float2*>(&H.gamc[c0]) = make_float2(fexp(bC0), fexp(bC1));
+    }
+    lds_barrier();  // ---- barrier 2
+
+    // ---------------- part 3: Gram products, and the inputs the value waves read next step
+    if (work) {
+        if (kw < 3) {
+            // A(0,0), A(1,0), A(1,1): split bf16 with three independent accumulators
+            const int R = kw == 0 ? 0 : 1, S = kw == 2 ? 1 : 0;
+            const uint16_t(*rh)[LDK] = (kw == 1) ? sm.key.k1h : (S ? sm.key.khh + SUB : sm.key.khh);
+            const uint16_t(*rl)[LDK] = (kw == 1) ? sm.key.k1l : (S ? sm.key.khl + SUB : sm.key.khl);
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int kc = 32 * m + 8 * g4;
+                const u32x4 aH = ld16(&sm.key.qmh[SUB * R + l16][kc]);
+                const u32x4 aL = ld16(&sm.key.qml[SUB * R + l16][kc]);
+                const u32x4 bH = ld16(&rh[l16][kc]);
+                const u32x4 bL = ld16(&rl[l16][kc]);
+                a0 = mfma_bf16(aH, bH, a0);
+                a1 = mfma_bf16(aH, bL, a1);
+                a2 = mfma_bf16(aL, bH, a2);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 4 * g4 + r;
+                float v = (a0[r] + a1[r]) + a2[r];
+                if (R == S && l16 > i) v = 0.f;  // lower triangle including the diagonal
+                const uint32_t hi = pack_bf16(v, 0.f);
+                H.ah[SUB * R + i][SUB * S + l16] = hi & 0xffffu;
+                H.al[SUB * R + i][SUB * S + l16] = pack_bf16(v - bf16lo_to_f(hi), 0.f) & 0xffffu;
+            }
+        } else {
+            // L(0,0), L(1,0), L(1,1) in bf16
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int kc = 32 * m + 8 * g4;
+                const u32x4 a0 = ld16(&sm.key.km[l16][kc]);
+                const u32x4 a1 = ld16(&sm.key.km[SUB + l16][kc]);
+                acc0 = mfma_bf16(a0, ld16(&sm.key.khh[l16][kc]), acc0);
+                acc1 = mfma_bf16(a1, ld16(&sm.key.k1h[l16][kc]), acc1);
+                acc2 = mfma_bf16(a1, ld16(&sm.key.khh[SUB + l16][kc]), acc2);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 4 * g4 + r;
+                sm.h1.lf[i][l16] = (l16 >= i) ? 0.f : acc0[r];  // strictly lower
+                sm.h1.lf[SUB + i][l16] = acc1[r];
+                sm.h1.lf[SUB + i][SUB + l16] = (l16 >= i) ? 0.f : acc2[r];
+            }
+        }
+        // V^T and beta of this chunk (the value waves are done with the previous ones)
+        if (lane < 32) {  // value columns 2*lane, 2*lane+1 of this half
+            const uint32_t* v = cur.v;
+            *reinterpret_cast<u32x4*>(&sm.h1.vt[2 * lane][8 * kw]) =
+                u32x4{perm_lo(v[0], v[1]), perm_lo(v[2], v[3]), perm_lo(v[4], v[5]), perm_lo(v[6], v[7])};
+            *reinterpret_cast<u32x4*>(&sm.h1.vt[2 * lane + 1][8 * kw]) =
+                u32x4{perm_hi(v[0], v[1]), perm_hi(v[2], v[3]), perm_hi(v[4], v[5]), perm_hi(v[6], v[7])};
+        }
+        if (lane < 8) sm.h1.beta[8 * kw + lane] = cur.beta;
+    }
+    lds_barrier();  // ---- barrier 3
+}
+
+__device__ void key_waves(Smem& sm, const Params& p, size_t row0, int half, int kw, int lane, int nchunk) {
+    // A's block (0,1) is zero in both buffers; no chunk writes it
+    for (int e = 64 * kw + lane; e < 2 * SUB * SUB; e += 256) {
+        Handoff2& Hz = sm.h2[e >> 8];
+        const int r = (e >> 4) & 15, c = SUB + (e & 15);
+        Hz.ah[r][c] = 0; Hz.al[r][c] = 0;
+    }
+    KeyLoad kl;
+    kl.kw = kw;
+    kl.lane = lane;
+    kl.tok_b = (uint32_t)p.H * DK * 2;
+    kl.lane_b = 4 * lane;
+    kl.vlane_b = 2 * (half * DVH + 2 * (lane & 31));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        kl.off[i] = (uint32_t)(8 * kw + i) * kl.tok_b + kl.lane_b;
+        kl.voff[i] = (uint32_t)(8 * kw + i) * kl.tok_b + kl.vlane_b;
+    }
+    kl.boff = (uint32_t)(8 * kw + (lane & 7)) * 4u * p.H;
+    Raw ra, rb;
+    if (p.T > 0) load_chunk(ra, p, kl, row0, 0);
+    // two steps per iteration so the prefetch target alternates between two register sets
+    for (int n = 0; n <= nchunk; n += 2) {
+        key_step(sm, p, kl, row0, n, nchunk, ra, rb);
+        if (n + 1 <= nchunk) key_step(sm, p, kl, row0, n + 1, nchunk, rb, ra);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// value waves: one step = chunk n-1 (nothing when n == 0); three barriers
+// ------------------------------------------------------------------------------------------------
+template <bool OUT_F32>
+__device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int half, int vw, int lane, int nchunk) {
+    const int l16 = lane & 15, g4 = lane >> 4;
+    ValueTiles& V = sm.val;
+    // T's block (0,1) is zero; nothing else writes it
+    if (vw == 0) {
+        for (int e = lane; e < SUB * SUB; e += 64) {
+            const int r = e >> 4, c = SUB + (e & 15);
+            V.th[r][c] = 0; V.tl[r][c] = 0;
+        }
     }
 
-    // state: st[cb][r] = S[16*cb + 4*g4 + r][half*64 + 16*wave + l16]
+    // state: st[cb][r] = S[16*cb + 4*g4 + r][col]
+    const int col = half * DVH + 16 * vw + l16;
     f32x4 st[8];
-    const int col = half * DVH + 16 * wave + l16;
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
 #pragma unroll
@@ -150,8 +388,8 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
             st[cb][r] = p.S0 ? p.S0[((size_t)bh * DK + c) * DV + col] : 0.f;
         }
     }
-    // state as f16 B operands of the channel contraction, K-step m covering channels 32m..32m+31 in
-    // the order {32m + 4*g4 + r} then {32m + 16 + 4*g4 + r}
+    // state as f16 operands of the channel contraction, K-step m over channels 32m..32m+31 in the
+    // order {32m + 4*g4 + r} then {32m + 16 + 4*g4 + r}; as an A operand it is S^T
     u32x4 sb[4];
     auto make_sb = [&]() {
 #pragma unroll
@@ -160,302 +398,184 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
                           pack_f16(st[2 * m + 1][0], st[2 * m + 1][1]), pack_f16(st[2 * m + 1][2], st[2 * m + 1][3])};
     };
     make_sb();
+    // byte offsets of this lane's output (token 16R + l16 of a chunk, value columns 4*g4..4*g4+3)
+    uint32_t ooff[2];
+#pragma unroll
+    for (int R = 0; R < 2; ++R)
+        ooff[R] = ((uint32_t)(SUB * R + l16) * (uint32_t)p.H * DV + half * DVH + 16 * vw + 4 * g4) * (OUT_F32 ? 4u : 2u);
 
-    Raw raw;
-    if (p.T > 0) load_chunk(raw, p, bh_tok0, 0, wave, lane, half);
-    const int nchunk = (p.T + C - 1) / C;
-    const int c0 = 2 * lane;       // this thread's key channels c0, c0 + 1
-    const int sig = wave >> 1;     // sub-tile of this thread's octet
-    const int hf = wave & 1;       // first or second octet of the sub-tile
-
-    for (int ch = 0; ch < nchunk; ++ch) {
-        const int t0 = ch * C;
-        // ---- element-wise key side, part 1: cumulative decay within the octet, sub-tile factors
-        float s0[8], s1[8];
-        {
-            float a0 = 0.f, a1 = 0.f;
+    for (int n = 0; n <= nchunk; ++n) {
+        const bool work = n >= 1;  // this step handles chunk n-1
+        const int t0 = (n - 1) * C;
+        const Handoff2& H = sm.h2[(n - 1) & 1];
+        // ---------------- part 1: UT inverse (one wave)
+        if (work && vw == 0) {
+            const float* beta = sm.h1.beta;
+            // diagonal blocks by right-looking forward substitution in registers:
+            // lanes 0-15 column j of block 0, lanes 16-31 column j of block 1
+            if (lane < 32) {
+                const int o = SUB * (lane >> 4);
+                int j = l16;
+                asm volatile("" : "+v"(j));  // keep the unit-vector selects inside the chunk loop
+                float Lr[SUB][SUB];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                a0 += raw.g[i].x; a1 += raw.g[i].y;
-                s0[i] = a0; s1[i] = a1;
-            }
-        }
-        *reinterpret_cast<float2*>(&sm.tot[wave][c0]) = make_float2(s0[7], s1[7]);
-        // reference = cumulative decay at the sub-tile's token 7 (end of its first octet)
-        const float ref0 = hf ? 0.f : s0[7], ref1 = hf ? 0.f : s1[7];
-        float qm0[8], qm1[8], km0[8], km1[8], kh0[8], kh1[8];
+                for (int i = 1; i < SUB; ++i) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = 8 * wave + i;
-            const float x0 = s0[i] - ref0, x1 = s1[i] - ref1;
-            const float e0 = fexp(x0), e1 = fexp(x1);
-            const float r0 = fexp(-x0), r1 = fexp(-x1);
-            const float q0 = bf16lo_to_f(raw.q[i]), q1 = bf16hi_to_f(raw.q[i]);
-            const float k0 = bf16lo_to_f(raw.k[i]), k1 = bf16hi_to_f(raw.k[i]);
-            qm0[i] = q0 * e0; qm1[i] = q1 * e1;
-            km0[i] = k0 * e0; km1[i] = k1 * e1;
-            kh0[i] = k0 * r0; kh1[i] = k1 * r1;
-            uint32_t hi, lo;
-            split_bf16(qm0[i], qm1[i], hi, lo);
-            *reinterpret_cast<uint32_t*>(&sm.qmh[t][c0]) = hi;
-            *reinterpret_cast<uint32_t*>(&sm.qml[t][c0]) = lo;
-            *reinterpret_cast<uint32_t*>(&sm.km[t][c0]) = pack_bf16(km0[i], km1[i]);
-            split_bf16(kh0[i], kh1[i], hi, lo);
-            *reinterpret_cast<uint32_t*>(&sm.khh[t][c0]) = hi;
-            *reinterpret_cast<uint32_t*>(&sm.khl[t][c0]) = lo;
-        }
-        if (lane < 32) {  // V^T for value columns 2*lane, 2*lane+1 of this half
-            uint32_t a[4], bb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = (raw.v[2 * i] & 0xffffu) | (raw.v[2 * i + 1] << 16);
-                bb[i] = (raw.v[2 * i] >> 16) | (raw.v[2 * i + 1] & 0xffff0000u);
-            }
-            *reinterpret_cast<u32x4*>(&sm.vt[2 * lane][8 * wave]) = u32x4{a[0], a[1], a[2], a[3]};
-            *reinterpret_cast<u32x4*>(&sm.vt[2 * lane + 1][8 * wave]) = u32x4{bb[0], bb[1], bb[2], bb[3]};
-        }
-        if (lane < 8) sm.beta[8 * wave + lane] = raw.beta;
-
-        // the raw registers are consumed: prefetch the next chunk
-        if (ch + 1 < nchunk) load_chunk(raw, p, bh_tok0, t0 + C, wave, lane, half);
-        lds_barrier();
-
-        // ---- element-wise key side, part 2: factors referenced to the chunk start and chunk end
-        {
-            float tt0[4], tt1[4];
-#pragma unroll
-            for (int o = 0; o < 4; ++o) { tt0[o] = sm.tot[o][c0]; tt1[o] = sm.tot[o][c0 + 1]; }
-            const float pA0 = tt0[0], pA1 = tt1[0];                          // b at token 7
-            const float pB0 = tt0[0] + tt0[1] + tt0[2], pB1 = tt1[0] + tt1[1] + tt1[2];  // b at token 23
-            const float bC0 = pB0 + tt0[3], bC1 = pB1 + tt1[3];              // b at token 31
-            const float p0 = sig ? pB0 : pA0, p1 = sig ? pB1 : pA1;
-            const float eP0 = fexp(p0), eP1 = fexp(p1);
-            const float eC0 = fexp(bC0 - p0), eC1 = fexp(bC1 - p1);
-            uint16_t kg0[8], kg1[8], kb0[8], kb1[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int t = 8 * wave + i;
-                *reinterpret_cast<uint32_t*>(&sm.qg[t][c0]) = pack_f16(qm0[i] * eP0, qm1[i] * eP1);
-                const uint32_t kg = pack_f16(km0[i] * eP0, km1[i] * eP1);
-                const uint32_t kb = pack_f16(kh0[i] * eC0, kh1[i] * eC1);
-                kg0[i] = kg & 0xffffu; kg1[i] = kg >> 16;
-                kb0[i] = kb & 0xffffu; kb1[i] = kb >> 16;
-            }
-            auto pack8 = [](const uint16_t* e) {
-                return u32x4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
-                             e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)};
-            };
-            *reinterpret_cast<u32x4*>(&sm.kgt[c0][8 * wave]) = pack8(kg0);
-            *reinterpret_cast<u32x4*>(&sm.kgt[c0 + 1][8 * wave]) = pack8(kg1);
-            *reinterpret_cast<u32x4*>(&sm.kbt[c0][8 * wave]) = pack8(kb0);
-            *reinterpret_cast<u32x4*>(&sm.kbt[c0 + 1][8 * wave]) = pack8(kb1);
-            if (sig == 0) {
-                // K/Gamma rows of sub-tile 0 moved to sub-tile 1's reference: factor exp(b_23 - b_7) <= 1
-                const float f0 = fexp(pB0 - pA0), f1 = fexp(pB1 - pA1);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int t = 8 * wave + i;
-                    uint32_t hi, lo;
-                    split_bf16(kh0[i] * f0, kh1[i] * f1, hi, lo);
-                    *reinterpret_cast<uint32_t*>(&sm.k1h[t][c0]) = hi;
-                    *reinterpret_cast<uint32_t*>(&sm.k1l[t][c0]) = lo;
+                    for (int q4 = 0; q4 <= (i - 1) / 4; ++q4) {
+                        const f32x4 t = *reinterpret_cast<const f32x4*>(&sm.h1.lf[o + i][o + 4 * q4]);
+                        Lr[i][4 * q4] = t[0]; Lr[i][4 * q4 + 1] = t[1]; Lr[i][4 * q4 + 2] = t[2]; Lr[i][4 * q4 + 3] = t[3];
+                    }
                 }
+                float bt[SUB];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 t = *reinterpret_cast<const f32x4*>(&beta[o + 4 * q4]);
+                    bt[4 * q4] = t[0]; bt[4 * q4 + 1] = t[1]; bt[4 * q4 + 2] = t[2]; bt[4 * q4 + 3] = t[3];
+                }
+                float x[SUB], acc[SUB];
+#pragma unroll
+                for (int i = 0; i < SUB; ++i) acc[i] = 0.f;
+#pragma unroll
+                for (int m = 0; m < SUB; ++m) {
+                    x[m] = (m == j ? 1.f : 0.f) - bt[m] * acc[m];
+#pragma unroll
+                    for (int i = m + 1; i < SUB; ++i) acc[i] = __builtin_fmaf(Lr[i][m], x[m], acc[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < SUB; ++i) V.xf[o + i][o + j] = x[i];
             }
-            if (wave == 0) *reinterpret_cast<float2*>(&sm.gamc[c0]) = make_float2(fexp(bC0), fexp(bC1));
+            // T = X Diag(beta) on the diagonal blocks, 8 entries per lane
+            {
+                const int o = SUB * (lane >> 5), i = (lane >> 1) & 15, j0 = 8 * (lane & 1);
+                const f32x4 xa = *reinterpret_cast<const f32x4*>(&V.xf[o + i][o + j0]);
+                const f32x4 xb = *reinterpret_cast<const f32x4*>(&V.xf[o + i][o + j0 + 4]);
+                const f32x4 ba = *reinterpret_cast<const f32x4*>(&beta[o + j0]);
+                const f32x4 bb = *reinterpret_cast<const f32x4*>(&beta[o + j0 + 4]);
+                const f32x4 ta = xa * ba, tb = xb * bb;
+                uint32_t h0, h1, h2, h3, q0, q1, q2, q3;
+                split_bf16(ta[0], ta[1], h0, q0);
+                split_bf16(ta[2], ta[3], h1, q1);
+                split_bf16(tb[0], tb[1], h2, q2);
+                split_bf16(tb[2], tb[3], h3, q3);
+                *reinterpret_cast<u32x4*>(&V.th[o + i][o + j0]) = u32x4{h0, h1, h2, h3};
+                *reinterpret_cast<u32x4*>(&V.tl[o + i][o + j0]) = u32x4{q0, q1, q2, q3};
+            }
+            // off-diagonal block: Y = Diag(beta_1) L_10 X_00, X_10 = -X_11 Y on float32 matrix cores;
+            // the K index of step s in lane group g4 is 4*g4 + s
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int k = 4 * g4 + s;
+                const float a = beta[SUB + l16] * sm.h1.lf[SUB + l16][k];
+                const float b = V.xf[k][l16];
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, y, 0, 0, 0);
+            }
+            f32x4 x10 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float a = V.xf[SUB + l16][SUB + 4 * g4 + s];
+                x10 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, y[s], x10, 0, 0, 0);
+            }
+            const float bj = beta[l16];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float tv = -x10[r] * bj;
+                const int i = SUB + 4 * g4 + r;
+                const uint32_t hi = pack_bf16(tv, 0.f);
+                V.th[i][l16] = hi & 0xffffu;
+                V.tl[i][l16] = pack_bf16(tv - bf16lo_to_f(hi), 0.f) & 0xffffu;
+            }
         }
-        lds_barrier();
+        lds_barrier();  // ---- barrier 1
 
-        // ---- Gram matrices on the matrix cores: A(0,0), A(1,0), A(1,1) split bf16; L blocks bf16
-        if (wave < 3) {
-            const int R = wave == 0 ? 0 : 1;  // row sub-tile
-            const int S = wave == 2 ? 1 : 0;  // column sub-tile
-            const uint16_t(*rh)[LDK] = (wave == 1) ? sm.k1h : (S ? sm.khh + SUB : sm.khh);
-            const uint16_t(*rl)[LDK] = (wave == 1) ? sm.k1l : (S ? sm.khl + SUB : sm.khl);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // ---------------- part 2: U = T (V - (K*Gamma) S), and (Q*Gamma) S
+        f32x4 oacc[2];
+        u32x4 uf, uh, ul;
+        if (work) {
+            // X = V - (K*Gamma) S, started from V in accumulator layout
+            f32x4 xr[2];
+#pragma unroll
+            for (int R = 0; R < 2; ++R) {
+                const u32x2 vv = *reinterpret_cast<const u32x2*>(&sm.h1.vt[16 * vw + l16][SUB * R + 4 * g4]);
+                xr[R] = f32x4{bf16lo_to_f(vv.x), bf16hi_to_f(vv.x), bf16lo_to_f(vv.y), bf16hi_to_f(vv.y)};
+            }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const int kc = 32 * m + 8 * g4;
-                const u32x4 aH = ld16(&sm.qmh[SUB * R + l16][kc]);
-                const u32x4 aL = ld16(&sm.qml[SUB * R + l16][kc]);
-                const u32x4 bH = ld16(&rh[l16][kc]);
-                const u32x4 bL = ld16(&rl[l16][kc]);
-                acc = mfma_bf16(aH, bH, acc);
-                acc = mfma_bf16(aH, bL, acc);
-                acc = mfma_bf16(aL, bH, acc);
-            }
+                const int cbase = 32 * m + 4 * g4;
 #pragma unroll
-            for (int r = 0; r < 4; r += 2) {
-                const int i0 = 4 * g4 + r;
-                float v0 = acc[r], v1 = acc[r + 1];
-                if (R == S) {  // keep the lower triangle including the diagonal
-                    if (l16 > i0) v0 = 0.f;
-                    if (l16 > i0 + 1) v1 = 0.f;
-                }
-                // rows i0 and i0+1, column l16: store element-wise
-                const uint32_t hi0 = pack_bf16(v0, v1);
-                const uint32_t lo0 = pack_bf16(v0 - bf16lo_to_f(hi0), v1 - bf16hi_to_f(hi0));
-                sm.ah[SUB * R + i0][SUB * S + l16] = hi0 & 0xffffu;
-                sm.ah[SUB * R + i0 + 1][SUB * S + l16] = hi0 >> 16;
-                sm.al[SUB * R + i0][SUB * S + l16] = lo0 & 0xffffu;
-                sm.al[SUB * R + i0 + 1][SUB * S + l16] = lo0 >> 16;
+                for (int R = 0; R < 2; ++R)
+                    xr[R] = mfma_f16(ld8x2(&H.kgn[SUB * R + l16][cbase], &H.kgn[SUB * R + l16][cbase + 16]), sb[m],
+                                     xr[R]);
             }
-        } else {
+            // (Q*Gamma) S as O^T: lane (token l16, group g4) gets value columns 4*g4..4*g4+3
 #pragma unroll
-            for (int blk = 0; blk < 3; ++blk) {
-                const int R = blk == 0 ? 0 : 1, S = blk == 2 ? 1 : 0;
-                const uint16_t(*rh)[LDK] = (blk == 1) ? sm.k1h : (S ? sm.khh + SUB : sm.khh);
+            for (int R = 0; R < 2; ++R) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const int kc = 32 * m + 8 * g4;
-                    acc = mfma_bf16(ld16(&sm.km[SUB * R + l16][kc]), ld16(&rh[l16][kc]), acc);
+                    const int cbase = 32 * m + 4 * g4;
+                    acc = mfma_f16(sb[m], ld8x2(&H.qg[SUB * R + l16][cbase], &H.qg[SUB * R + l16][cbase + 16]), acc);
                 }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 4 * g4 + r;
-                    float v = acc[r];
-                    if (R == S && l16 >= i) v = 0.f;  // strictly lower
-                    sm.lf[SUB * R + i][SUB * S + l16] = v;
-                }
+                oacc[R] = acc;
             }
-        }
-        lds_barrier();
-
-        // ---- UT inverse: X = (I + Diag(beta) L)^{-1}, diagonal 16x16 blocks by forward substitution
-        if (wave == 0 && lane < 32) {
-            const int o = SUB * (lane >> 4), j = l16;
-            float acc[SUB];
-#pragma unroll
-            for (int i = 0; i < SUB; ++i) acc[i] = 0.f;
-            float x[SUB];
-#pragma unroll
-            for (int m = 0; m < SUB; ++m) {
-                x[m] = (m == j) ? 1.f : -acc[m];
-#pragma unroll
-                for (int i = m + 1; i < SUB; ++i) acc[i] += sm.beta[o + i] * sm.lf[o + i][o + m] * x[m];
-            }
-#pragma unroll
-            for (int i = 0; i < SUB; ++i) sm.xf[o + i][o + j] = x[i];
-        }
-        lds_barrier();
-        {
-            // Y = Diag(beta_1) L_10 X_00, then X_10 = -X_11 Y
-            const int i = tid >> 4, j = tid & 15;
-            float y = 0.f;
-#pragma unroll
-            for (int m = 0; m < SUB; ++m) y += sm.lf[SUB + i][m] * sm.xf[m][j];
-            sm.yf[i][j] = sm.beta[SUB + i] * y;
-        }
-        lds_barrier();
-        {
-            const int i = tid >> 4, j = tid & 15;
-            float x10 = 0.f;
-#pragma unroll
-            for (int m = 0; m < SUB; ++m) x10 -= sm.xf[SUB + i][SUB + m] * sm.yf[m][j];
-            // T = X Diag(beta): blocks (0,0), (1,1) and (1,0), entry (i, j) of each
-            const float b0 = sm.beta[j], b1 = sm.beta[SUB + j];
-            const float t00 = sm.xf[i][j] * b0, t11 = sm.xf[SUB + i][SUB + j] * b1, t10 = x10 * b0;
-            auto put = [&](int r, int c, float v) {
-                const uint32_t hi = pack_bf16(v, 0.f);
-                sm.th[r][c] = hi & 0xffffu;
-                sm.tl[r][c] = pack_bf16(v - bf16lo_to_f(hi), 0.f) & 0xffffu;
-                sm.tf[r][c] = pack_f16(v, 0.f) & 0xffffu;
-            };
-            put(i, j, t00);
-            put(SUB + i, SUB + j, t11);
-            put(SUB + i, j, t10);
-        }
-        lds_barrier();
-
-        // ---- W = T (K*Gamma) (stored negated) and this wave's U_tilde = T V
-        f32x4 ut[2];
-        {
+            // X as operands over the chunk's tokens, order {4*g4 + r} then {16 + 4*g4 + r}; split bf16
+            uint32_t xh0, xh1, xh2, xh3, xl0, xl1, xl2, xl3;
+            split_bf16(xr[0][0], xr[0][1], xh0, xl0);
+            split_bf16(xr[0][2], xr[0][3], xh1, xl1);
+            split_bf16(xr[1][0], xr[1][1], xh2, xl2);
+            split_bf16(xr[1][2], xr[1][3], xh3, xl3);
+            const u32x4 xh = {xh0, xh1, xh2, xh3}, xl = {xl0, xl1, xl2, xl3};
+            f32x4 u[2];
 #pragma unroll
             for (int R = 0; R < 2; ++R) {
-                const u32x4 tfa = ld16(&sm.tf[SUB * R + l16][8 * g4]);
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const int ct = 2 * wave + cc;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    acc = mfma_f16(tfa, ld16(&sm.kgt[16 * ct + l16][8 * g4]), acc);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        sm.wn[SUB * R + 4 * g4 + r][16 * ct + l16] = pack_f16(-acc[r], 0.f) & 0xffffu;
-                }
-                const u32x4 bv = ld16(&sm.vt[16 * wave + l16][8 * g4]);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mfma_bf16(ld16(&sm.th[SUB * R + l16][8 * g4]), bv, acc);
-                acc = mfma_bf16(ld16(&sm.tl[SUB * R + l16][8 * g4]), bv, acc);
-                ut[R] = acc;
+                const u32x4 tH = ld8x2(&V.th[SUB * R + l16][4 * g4], &V.th[SUB * R + l16][SUB + 4 * g4]);
+                const u32x4 tL = ld8x2(&V.tl[SUB * R + l16][4 * g4], &V.tl[SUB * R + l16][SUB + 4 * g4]);
+                f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+                a0 = mfma_bf16(tH, xh, a0);
+                a1 = mfma_bf16(tH, xl, a1);
+                a2 = mfma_bf16(tL, xh, a2);
+                u[R] = (a0 + a1) + a2;
             }
+            uf = u32x4{pack_f16(u[0][0], u[0][1]), pack_f16(u[0][2], u[0][3]), pack_f16(u[1][0], u[1][1]),
+                       pack_f16(u[1][2], u[1][3])};
+            uint32_t uh0, uh1, uh2, uh3, ul0, ul1, ul2, ul3;
+            split_bf16(u[0][0], u[0][1], uh0, ul0);
+            split_bf16(u[0][2], u[0][3], uh1, ul1);
+            split_bf16(u[1][0], u[1][1], uh2, ul2);
+            split_bf16(u[1][2], u[1][3], uh3, ul3);
+            uh = u32x4{uh0, uh1, uh2, uh3};
+            ul = u32x4{ul0, ul1, ul2, ul3};
         }
-        lds_barrier();
+        lds_barrier();  // ---- barrier 2
 
-        // ---- state-dependent part (this wave's 16 value columns)
-        // U = U_tilde - W S
+        // ---------------- part 3: O += A U, output; S <- Diag(Gamma_last) S + Kbar^T U
+        if (work) {
+            gchar* ob = (gchar*)uniform_gptr((const char*)p.o + ((row0 + (size_t)t0 * p.H) * DV) * (OUT_F32 ? 4 : 2));
 #pragma unroll
-        for (int R = 0; R < 2; ++R) {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int cbase = 32 * m + 4 * g4;
-                ut[R] = mfma_f16(ld8x2(&sm.wn[SUB * R + l16][cbase], &sm.wn[SUB * R + l16][cbase + 16]), sb[m], ut[R]);
-            }
-        }
-        // U as B operands over the chunk's tokens, in the order {4*g4 + r} then {16 + 4*g4 + r}
-        const u32x4 uf = {pack_f16(ut[0][0], ut[0][1]), pack_f16(ut[0][2], ut[0][3]), pack_f16(ut[1][0], ut[1][1]),
-                          pack_f16(ut[1][2], ut[1][3])};
-        uint32_t uh0, uh1, uh2, uh3, ul0, ul1, ul2, ul3;
-        split_bf16(ut[0][0], ut[0][1], uh0, ul0);
-        split_bf16(ut[0][2], ut[0][3], uh1, ul1);
-        split_bf16(ut[1][0], ut[1][1], uh2, ul2);
-        split_bf16(ut[1][2], ut[1][3], uh3, ul3);
-        const u32x4 uh = {uh0, uh1, uh2, uh3}, ul = {ul0, ul1, ul2, ul3};
-        // O = (Q*Gamma) S + A U
-#pragma unroll
-        for (int R = 0; R < 2; ++R) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int cbase = 32 * m + 4 * g4;
-                acc = mfma_f16(ld8x2(&sm.qg[SUB * R + l16][cbase], &sm.qg[SUB * R + l16][cbase + 16]), sb[m], acc);
-            }
-            const u32x4 aH = ld8x2(&sm.ah[SUB * R + l16][4 * g4], &sm.ah[SUB * R + l16][SUB + 4 * g4]);
-            const u32x4 aL = ld8x2(&sm.al[SUB * R + l16][4 * g4], &sm.al[SUB * R + l16][SUB + 4 * g4]);
-            acc = mfma_bf16(aH, uh, acc);
-            acc = mfma_bf16(aH, ul, acc);
-            acc = mfma_bf16(aL, uh, acc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.ost[SUB * R + 4 * g4 + r][16 * wave + l16] = acc[r] * p.scale;
-        }
-        // S <- Diag(Gamma_last) S + Kbar^T U
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) st[cb][r] *= sm.gamc[16 * cb + 4 * g4 + r];
-            const u32x4 a = ld8x2(&sm.kbt[16 * cb + l16][4 * g4], &sm.kbt[16 * cb + l16][SUB + 4 * g4]);
-            st[cb] = mfma_f16(a, uf, st[cb]);
-        }
-        make_sb();
-        lds_barrier();
-
-        // ---- store this chunk's output rows (32 tokens x 64 columns)
-        {
-            const int r = tid >> 3, cseg = (tid & 7) * 8;
-            const int t = t0 + r;
-            if (t < p.T) {
-                const size_t off = (bh_tok0 + (size_t)t * p.H) * DV + half * DVH + cseg;
-                const float* src = &sm.ost[r][cseg];
-                if constexpr (OUT_F32) {
-                    float4* dst = reinterpret_cast<float4*>((float*)p.o + off);
-                    dst[0] = make_float4(src[0], src[1], src[2], src[3]);
-                    dst[1] = make_float4(src[4], src[5], src[6], src[7]);
-                } else {
-                    *reinterpret_cast<u32x4*>((uint16_t*)p.o + off) =
-                        u32x4{pack_bf16(src[0], src[1]), pack_bf16(src[2], src[3]), pack_bf16(src[4], src[5]),
-                              pack_bf16(src[6], src[7])};
+            for (int R = 0; R < 2; ++R) {
+                const u32x4 aH = ld8x2(&H.ah[SUB * R + l16][4 * g4], &H.ah[SUB * R + l16][SUB + 4 * g4]);
+                const u32x4 aL = ld8x2(&H.al[SUB * R + l16][4 * g4], &H.al[SUB * R + l16][SUB + 4 * g4]);
+                f32x4 ax = {0.f, 0.f, 0.f, 0.f}, ay = ax, acc = oacc[R];
+                ax = mfma_bf16(uh, aH, ax);
+                ay = mfma_bf16(ul, aH, ay);
+                acc = mfma_bf16(uh, aL, acc);
+                acc = (acc + ax + ay) * p.scale;
+                if (t0 + SUB * R + l16 < p.T) {
+                    if constexpr (OUT_F32)
+                        gstore<f32x4>(ob, ooff[R], acc);
+                    else
+                        gstore<u32x2>(ob, ooff[R], u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])});
                 }
             }
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) {
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(&H.gamc[16 * cb + 4 * g4]);
+                const u32x4 a = ld8x2(&H.kbt[16 * cb + l16][4 * g4], &H.kbt[16 * cb + l16][SUB + 4 * g4]);
+                st[cb] = mfma_f16(a, uf, st[cb] * gm);
+            }
+            make_sb();
         }
+        lds_barrier();  // ---- barrier 3
     }
 
     if (p.S_T) {
@@ -468,6 +588,32 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
             }
         }
     }
+}
+
+template <bool OUT_F32>
+__global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
+    __shared__ Smem sm;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+    // workgroup -> (batch*head, value half); both halves of a head land on the same XCD
+    int bh, half;
+    const int nbh = p.B * p.H;
+    if ((nbh & 7) == 0) {
+        const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+        half = local & 1;
+        bh = (local >> 1) * 8 + xcd;
+    } else {
+        bh = blockIdx.x >> 1;
+        half = blockIdx.x & 1;
+    }
+    const int b = bh / p.H, h = bh - b * p.H;
+    const size_t row0 = (size_t)b * p.T * p.H + h;  // row of token 0: (b*T + t)*H + h = row0 + t*H
+    const int nchunk = (p.T + C - 1) / C;
+
+    if (wave < 4)
+        key_waves(sm, p, row0, half, wave, lane, nchunk);
+    else
+        value_waves<OUT_F32>(sm, p, bh, row0, half, wave - 4, lane, nchunk);
 }
 
 }  // namespace bf16path
