@@ -25,6 +25,13 @@ METRIC = "KDA prefill tokens/s at H=32,d=128,T=16K + % bf16 MFMA peak (1 GPU)"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix
 WORKLOAD = 2
+COPY_BYTES = 512 << 20
+KERNEL_SRC = os.path.join(ROOT, "linear_recurrent_attention_amd", "csrc", "kda_fwd_bf16.hip")
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by the same counters on a
+# 512 MiB copy (factors 2.0 and 1.0); valid only for the kernel source with this hash.
+MEASURED_TRAFFIC = {"kernel_sha256": "7b4b54cc971af6fe67f2702a71c94bd634166bf266caf316488bd8826c04da58",
+                    "bytes": (1343655 * 2.0 + 532480 * 1.0) * 1024,
+                    "profile": "profiles/kda_fwd_bf16_B4_H32_T16384_D128.md"}
 
 
 def algorithmic_bytes(B, T, H, Dk, Dv, io_bytes=2, has_S0=False):
@@ -35,14 +42,22 @@ def algorithmic_bytes(B, T, H, Dk, Dv, io_bytes=2, has_S0=False):
 
 
 def algorithmic_flops(B, T, H, Dk, Dv, C=32):
-    """Matrix-product flops of the chunkwise form per launch (exact lower triangles, no padding):
-    per chunk of C tokens and head: L, A (C(C-1)/2, C(C+1)/2 dot products of length Dk), W = T Kg and
-    U_tilde = T V (C(C+1)/2 * (Dk + Dv) multiply-adds), W S and Q S (2 C Dk Dv), A U (C(C+1)/2 Dv),
-    Kbar^T U (C Dk Dv); 2 flops per multiply-add."""
+    """Matrix-product flops of the chunkwise form the kernel evaluates, per launch (exact lower
+    triangles, no padding, no split-precision repeats).  Per chunk of C tokens and head, in
+    multiply-adds: L and A (C(C-1)/2 + C(C+1)/2 dot products of length Dk), (K*Gamma) S, (Q*Gamma) S
+    and Kbar^T U (C Dk Dv each), T X and A U (C(C+1)/2 Dv each); 2 flops per multiply-add."""
     tri = C * (C + 1) // 2
     stri = C * (C - 1) // 2
-    per_chunk = 2 * ((stri + tri) * Dk + tri * (Dk + Dv) + 2 * C * Dk * Dv + tri * Dv + C * Dk * Dv)
+    per_chunk = 2 * ((stri + tri) * Dk + 3 * C * Dk * Dv + 2 * tri * Dv)
     return B * H * (T / C) * per_chunk
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter profile, or None if the kernel changed since."""
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    return MEASURED_TRAFFIC["bytes"] if digest == MEASURED_TRAFFIC["kernel_sha256"] else None
 
 
 def cpu_baseline(d, threads):
@@ -63,6 +78,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run one plain 512 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus N with N > 1 is not supported "
@@ -103,6 +120,13 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
     launch_ms = [a.elapsed_time(b) for a, b in ev]
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     avg_launch_s = float(np.mean(launch_ms)) / 1e3
     ms_per_step = wall / args.steps * 1e3
 
@@ -120,7 +144,7 @@ def main():
         "config": {"workload": w.name, "B": B, "H": H, "T": T, "Dk": Dk, "Dv": Dv, "chunk": 32,
                    "io": "bf16 q/k/v/o, float32 g/beta/state"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "kda_fwd_bf16_kernel", "avg_launch_ms": avg_launch_s * 1e3,
                      "algorithmic_bytes": abytes},
         "mfma": {"achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
