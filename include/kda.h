@@ -17,7 +17,8 @@
  *     covers argument validation and launch errors only; a fault inside a kernel surfaces at the
  *     caller's next synchronisation.
  *   - Tensors are dense, row-major, without padding, in the layouts given per argument.
- *   - No global mutable state: calls from several host threads are safe.
+ *   - kda_fwd keeps no global mutable state; kda_layer_fwd keeps one rocBLAS handle per device,
+ *     created on first use under a lock.  Calls from several host threads are safe.
  *   - Outputs must not alias inputs, except S_T == S0 (in-place state carry), which is allowed:
  *     each workgroup reads its slice of S0 before it writes the same slice of S_T.
  */
@@ -50,8 +51,15 @@ typedef struct {
     kda_dtype io_dtype; /* dtype of q, k, v */
     kda_dtype o_dtype;  /* dtype of o: io_dtype, or KDA_F32 with bf16 inputs (diagnostic output) */
     float scale;        /* o_t = S_t^T (scale * q_t); 1.0 reads the state with q as given */
-    int flags;          /* reserved, must be 0 */
+    int flags;          /* 0 or KDA_FWD_PRECISE; other bits are reserved and must be 0 */
 } kda_fwd_desc;
+
+/* kda_fwd_desc.flags: bf16 I/O only (the f32 path computes in float32 throughout and ignores it).
+ * Forms the intra-chunk key Gram matrix and the state update with split-bf16 operands instead of
+ * single bf16 / f16 ones.  Worth it when keys within a chunk are strongly correlated (e.g. after a
+ * Swish activation), which makes I + Diag(beta) L ill-conditioned and amplifies rounding in S_T;
+ * costs about 10% of throughput. */
+#define KDA_FWD_PRECISE 1
 
 /*
  * kda_fwd -- forward pass of the gated delta rule over B*H independent sequences.
@@ -67,7 +75,8 @@ typedef struct {
  *
  * Pointer alignment: q, k, v, o 4-byte aligned; g, beta, S0, S_T 8-byte aligned.
  * bf16 path numerics: intermediate products use bf16/f16 matrix-core operands with float32
- * accumulation (split-bf16 where a single rounding is too coarse); the state is float32.
+ * accumulation (split-bf16 where a single rounding is too coarse, and for more products with
+ * KDA_FWD_PRECISE); the state is float32.
  * The value path uses f16 operands, so |v| and the state entries must stay below 6.5e4;
  * beyond that o and S_T become non-finite.
  * Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP.
@@ -75,6 +84,68 @@ typedef struct {
 kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const void* v,
                    const float* g, const float* beta, const float* S0,
                    void* o, float* S_T, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Fused layer forward.  The layer of the explainer page "Kimi K3：开放前沿智能":
+ *   section 2.4 (paper Eq. 2): q, k = L2norm(Swish(ShortConv(x W))); v = x W_v;
+ *   section 2.3 (paper Eq. 2): decay logit z = W_up W_down x + b_alpha (low rank);
+ *   section 3.2 (paper Eq. 5): log(alpha) = -5 * sigmoid(exp(A_h) * z), A per head;
+ *   beta = sigmoid(x W_beta) (not on the page: the plainest reading);
+ *   the gated delta rule above (kda_fwd's matrix-core path on float32 q, k, v with KDA_FWD_PRECISE,
+ *   float32 output);
+ *   section 3.3 (paper Eq. 6): per-head RMSNorm of o, times the full-rank data-dependent gate
+ *   sigmoid(x W_g); then the output projection W_o.
+ * Short convolution: causal, depthwise, 4 taps, no bias; tap 3 multiplies the current token.
+ * L2 norm: x / sqrt(sum x^2 + 1e-6); RMSNorm: x / sqrt(mean x^2 + 1e-6) * rms_w.
+ * --------------------------------------------------------------------------------------------- */
+typedef struct {
+    int B, T;           /* batch, tokens (T >= 1) */
+    int d_model;        /* width of x and y (multiple of 8) */
+    int H, Dk, Dv;      /* heads; Dk = Dv = 128 */
+    int rank;           /* rank of the decay projection W_down W_up (multiple of 8) */
+    int conv;           /* short-convolution taps; 4 */
+    float scale;        /* multiplies q in the readout; 1.0 for the plain readout */
+    int flags;          /* reserved, must be 0 */
+} kda_layer_desc;
+
+/* Layer parameters, all DEVICE pointers owned by the caller.  Matrices are row-major [in, out],
+ * so a projection is x @ W. */
+typedef struct {
+    const void* Wq;       /* [d_model, H*Dk] bf16 */
+    const void* Wk;       /* [d_model, H*Dk] bf16 */
+    const void* Wv;       /* [d_model, H*Dv] bf16 */
+    const void* Wg;       /* [d_model, H*Dv] bf16  output gate */
+    const void* Wo;       /* [H*Dv, d_model] bf16  output projection */
+    const void* Wbeta;    /* [d_model, H]    bf16 */
+    const void* Wdown;    /* [d_model, rank] bf16 */
+    const void* Wup;      /* [rank, H*Dk]    bf16 */
+    const float* conv_q;  /* [H*Dk, conv] float32 */
+    const float* conv_k;  /* [H*Dk, conv] float32 */
+    const float* b_alpha; /* [H*Dk] float32 */
+    const float* A;       /* [H] float32 */
+    const float* rms_w;   /* [Dv] float32 */
+} kda_layer_weights;
+
+/* Bytes of device workspace kda_layer_fwd needs for this problem (0 for an invalid descriptor). */
+size_t kda_layer_workspace_size(const kda_layer_desc* desc);
+
+/*
+ * kda_layer_fwd -- y = layer(x).
+ *   x              : [B, T, d_model] bf16
+ *   S0, S_T        : [B, H, Dk, Dv] float32 KDA state in / out (NULL: zeros / not written; may alias)
+ *   conv_state_in  : [B, 3, 2*H*Dk] float32, the last 3 pre-convolution q rows then k rows of the
+ *                    previous segment, oldest first (NULL: zeros)
+ *   conv_state_out : same layout for this segment's end (NULL: not written); must not alias the input
+ *   y              : [B, T, d_model] bf16
+ *   ws             : device workspace of at least kda_layer_workspace_size(desc) bytes, 256-byte aligned
+ * The eight projections run through rocBLAS (bf16 operands, float32 accumulation; the rank-R
+ * up-projection in float32); rocBLAS keeps one handle per device for the life of the process and
+ * may allocate its own device memory on first use.  Returns KDA_OK, KDA_ERR_INVALID_ARG,
+ * KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE or KDA_ERR_HIP.
+ */
+kda_status kda_layer_fwd(const kda_layer_desc* desc, const void* x, const kda_layer_weights* weights,
+                         const float* S0, const float* conv_state_in, void* y, float* S_T,
+                         float* conv_state_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kda_error_string(kda_status status);

@@ -10,7 +10,7 @@ import torch
 from . import _lib
 from ._lib import KdaError  # noqa: F401
 
-__all__ = ["kda_fwd", "KdaError"]
+__all__ = ["kda_fwd", "kda_layer_fwd", "KdaError"]
 
 _DT = {torch.float32: _lib.KDA_F32, torch.bfloat16: _lib.KDA_BF16}
 
@@ -24,9 +24,10 @@ def _stream(device):
 
 
 def kda_fwd(q, k, v, g, beta, S0=None, scale: float = 1.0, o_dtype=None, want_state: bool = True,
-            out=None, state_out=None, chunk: int = 0):
+            out=None, state_out=None, chunk: int = 0, precise: bool = False):
     """Gated delta rule forward.  Shapes: q, k, g [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H];
     S0 [B,H,Dk,Dv] float32 or None.  q, k, v float32 or bfloat16; g, beta float32.
+    precise: split-bf16 key Gram matrix and state update on the bf16 path (KDA_FWD_PRECISE).
 
     Returns (o [B,T,H,Dv], S_T [B,H,Dk,Dv] float32 or None).
     """
@@ -49,8 +50,39 @@ def kda_fwd(q, k, v, g, beta, S0=None, scale: float = 1.0, o_dtype=None, want_st
     if want_state:
         ST = state_out if state_out is not None else torch.empty((B, H, Dk, Dv), dtype=torch.float32,
                                                                  device=q.device)
-    desc = _lib.FwdDesc(B, T, H, Dk, Dv, chunk, _DT[q.dtype], _DT[o_dtype], float(scale), 0)
+    desc = _lib.FwdDesc(B, T, H, Dk, Dv, chunk, _DT[q.dtype], _DT[o_dtype], float(scale),
+                        _lib.KDA_FWD_PRECISE if precise else 0)
     code = _lib.fwd_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(ST),
                         _stream(q.device))
     _lib.check(code)
     return o, ST
+
+
+def kda_layer_fwd(x, weights: dict, S0=None, conv_state=None, scale: float = 1.0, want_state: bool = True,
+                  workspace=None):
+    """Fused KDA layer.  x [B,T,d_model] bf16; weights: dict with the kda_layer_weights fields
+    (bf16 matrices [in, out]; float32 conv taps [H*Dk, 4], b_alpha [H*Dk], A [H], rms_w [Dv]).
+    Returns (y [B,T,d_model] bf16, S_T [B,H,Dk,Dv] float32 or None, conv_state [B,3,2*H*Dk] float32)."""
+    B, T, dm = x.shape
+    H = weights["A"].shape[0]
+    HD = weights["Wq"].shape[1]
+    Dk = HD // H
+    Dv = weights["Wv"].shape[1] // H
+    R = weights["Wdown"].shape[1]
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 GPU tensor")
+    for n in _lib.LAYER_WEIGHT_FIELDS:
+        t = weights[n]
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"weight {n} must be a contiguous GPU tensor")
+    desc = _lib.LayerDesc(B, T, dm, H, Dk, Dv, R, 4, float(scale), 0)
+    need = _lib.layer_workspace_size(desc)
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=x.device)
+    y = torch.empty((B, T, dm), dtype=torch.bfloat16, device=x.device)
+    ST = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=x.device) if want_state else None
+    cs = torch.empty((B, 3, 2 * HD), dtype=torch.float32, device=x.device)
+    W = _lib.LayerWeights(*[weights[n].data_ptr() for n in _lib.LAYER_WEIGHT_FIELDS])
+    code = _lib.layer_fwd_raw(desc, x.data_ptr(), W, _ptr(S0), _ptr(conv_state), y.data_ptr(), _ptr(ST),
+                              cs.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device))
+    _lib.check(code)
+    return y, ST, cs

@@ -15,9 +15,10 @@ KDA_ERR_HIP = -3
 KDA_ERR_WORKSPACE = -4
 KDA_F32 = 0
 KDA_BF16 = 1
+KDA_FWD_PRECISE = 1  # kda_fwd_desc.flags
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_fwd", "kda_error_string", "kda_version")
+EXPORTS = ("kda_fwd", "kda_layer_workspace_size", "kda_layer_fwd", "kda_error_string", "kda_version")
 
 
 class FwdDesc(ctypes.Structure):
@@ -27,6 +28,22 @@ class FwdDesc(ctypes.Structure):
         ("io_dtype", ctypes.c_int), ("o_dtype", ctypes.c_int),
         ("scale", ctypes.c_float), ("flags", ctypes.c_int),
     ]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int), ("T", ctypes.c_int), ("d_model", ctypes.c_int), ("H", ctypes.c_int),
+        ("Dk", ctypes.c_int), ("Dv", ctypes.c_int), ("rank", ctypes.c_int), ("conv", ctypes.c_int),
+        ("scale", ctypes.c_float), ("flags", ctypes.c_int),
+    ]
+
+
+LAYER_WEIGHT_FIELDS = ("Wq", "Wk", "Wv", "Wg", "Wo", "Wbeta", "Wdown", "Wup", "conv_q", "conv_k", "b_alpha", "A",
+                       "rms_w")
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHT_FIELDS]
 
 
 class KdaError(RuntimeError):
@@ -49,6 +66,11 @@ def lib():
             L = ctypes.CDLL(LIB_PATH)
             L.kda_fwd.restype = ctypes.c_int
             L.kda_fwd.argtypes = [ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 9
+            L.kda_layer_workspace_size.restype = ctypes.c_size_t
+            L.kda_layer_workspace_size.argtypes = [ctypes.POINTER(LayerDesc)]
+            L.kda_layer_fwd.restype = ctypes.c_int
+            L.kda_layer_fwd.argtypes = ([ctypes.POINTER(LayerDesc), ctypes.c_void_p, ctypes.POINTER(LayerWeights)] +
+                                        [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p])
             L.kda_error_string.restype = ctypes.c_char_p
             L.kda_error_string.argtypes = [ctypes.c_int]
             L.kda_version.restype = ctypes.c_int
@@ -60,6 +82,17 @@ def lib():
 def check(code: int):
     if code != KDA_OK:
         raise KdaError(code, lib().kda_error_string(code).decode())
+
+
+def layer_workspace_size(desc: LayerDesc) -> int:
+    return lib().kda_layer_workspace_size(ctypes.byref(desc))
+
+
+def layer_fwd_raw(desc: LayerDesc, x, weights: LayerWeights, S0, conv_in, y, S_T, conv_out, ws, ws_bytes,
+                  stream) -> int:
+    """Call kda_layer_fwd with integer device addresses (0 = NULL); returns the status code."""
+    return lib().kda_layer_fwd(ctypes.byref(desc), x, ctypes.byref(weights), S0, conv_in, y, S_T, conv_out, ws,
+                               ws_bytes, stream)
 
 
 def fwd_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, stream) -> int:

@@ -12,7 +12,7 @@ kda_status check_fwd(const kda_fwd_desc* d, const void* q, const void* k, const 
                      const float* beta, const float* S0, const void* o, const float* S_T) {
     if (!d) return KDA_ERR_INVALID_ARG;
     if (d->B < 1 || d->H < 1 || d->T < 0 || d->Dk < 1 || d->Dv < 1) return KDA_ERR_INVALID_ARG;
-    if (d->flags != 0) return KDA_ERR_INVALID_ARG;
+    if (d->flags & ~KDA_FWD_PRECISE) return KDA_ERR_INVALID_ARG;
     if (d->io_dtype != KDA_F32 && d->io_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
     if (d->o_dtype != KDA_F32 && d->o_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
     if (d->io_dtype == KDA_F32 && d->o_dtype != KDA_F32) return KDA_ERR_INVALID_ARG;
@@ -47,6 +47,8 @@ kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const
     p.B = desc->B; p.T = desc->T; p.H = desc->H; p.Dk = desc->Dk; p.Dv = desc->Dv;
     p.scale = desc->scale;
     p.o_f32 = desc->o_dtype == KDA_F32;
+    p.in_f32 = 0;
+    p.precise = (desc->flags & KDA_FWD_PRECISE) != 0;
     hipError_t e;
     if (desc->T == 0)
         e = kda::launch_state_copy(p, stream);

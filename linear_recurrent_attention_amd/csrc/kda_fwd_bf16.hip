@@ -28,16 +28,20 @@
 // one chunk ahead into registers.
 //
 // Matrix-core operands (v_mfma_f32_16x16x32_{bf16,f16}, float32 accumulate):
-//   L = Km Kh^T                      bf16
+//   L = Km Kh^T                      bf16                  HP: bf16 Km, split bf16 Kh
 //   A = Qm Kh^T                      split bf16 (hi*hi + hi*lo + lo*hi)
 //   X = V - Kg S,  Q S               f16
 //   U = T X                          split bf16
 //   A U                              split bf16
-//   Kbar^T U                         f16
+//   Kbar^T U                         f16                   HP: split bf16
+// HP is the variant for correlated keys (the layer's Swish-activated ones): the rounding of L and
+// of Kbar^T U grows with the conditioning of I + Diag(beta) L, and HP takes both to split bf16.
 // The inverse solves the two 16x16 diagonal blocks of (I + Diag(beta) L) by forward substitution
 // in float32 registers and forms the off-diagonal block with float32 matrix-core products.
 #include "kda_common.h"
 #include "kda_internal.h"
+
+#include <type_traits>
 
 namespace kda {
 namespace bf16path {
@@ -65,7 +69,7 @@ struct alignas(16) KeyTiles {                // written and read by the key wave
 struct alignas(16) Handoff2 {                // key -> value, double buffered by chunk parity
     uint16_t qg[C][LDK];                     // Q * Gamma                 f16
     uint16_t kgn[C][LDK];                    // -(K * Gamma)              f16
-    uint16_t kbt[DK][LDT8];                  // (K * exp(b_last - b))^T   f16
+    uint16_t kbh[DK][LDT8], kbl[DK][LDT8];   // (K * exp(b_last - b))^T   split bf16 (HP), else f16 in kbh
     uint16_t ah[C][LDA8], al[C][LDA8];       // A                         split bf16
     float gamc[DK];                          // Gamma of the chunk's last token
 };
@@ -96,11 +100,24 @@ __device__ __forceinline__ u32x4 ld8x2(const uint16_t* p0, const uint16_t* p1) {
 __device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
-struct Raw {  // one key thread's share of one chunk of input, as loaded
+// One key thread's share of one chunk of input, as loaded.  bf16 inputs: q, k, v as packed pairs;
+// float32 inputs: q, k as float pairs, and v is read by the value waves themselves.
+template <bool IN_F32>
+struct Raw;
+template <>
+struct Raw<false> {
     uint32_t q[8], k[8], v[8];
     f32x2 g[8];
     float beta;
 };
+template <>
+struct Raw<true> {
+    f32x2 q[8], k[8];
+    f32x2 g[8];
+    float beta;
+};
+__device__ __forceinline__ f32x2 unpack_q(uint32_t w) { return f32x2{bf16lo_to_f(w), bf16hi_to_f(w)}; }
+__device__ __forceinline__ f32x2 unpack_q(f32x2 w) { return w; }
 
 // Per-thread constants of the key waves' chunk loads (byte offsets within a chunk).
 struct KeyLoad {
@@ -133,20 +150,23 @@ __device__ __forceinline__ void gstore(gchar* base, uint32_t off, Tv v) {
 // beta of token t0 + 8*kw + (lane & 7).  Tokens past the end read the last valid row; mask_tail()
 // zeroes them when the chunk is consumed.  Nothing here uses the loaded values, so the loads stay
 // in flight until their first use one step later.  Requires T >= 1 and t0 < T.
-__device__ __forceinline__ void load_chunk(Raw& r, const Params& p, const KeyLoad& kl, size_t row0, int t0) {
+template <bool IN_F32>
+__device__ __forceinline__ void load_chunk(Raw<IN_F32>& r, const Params& p, const KeyLoad& kl, size_t row0, int t0) {
     const size_t ce = (row0 + (size_t)t0 * p.H) * DK;  // element offset of the chunk's first row
-    const gchar* qc = uniform_gptr((const uint16_t*)p.q + ce);
-    const gchar* kc = uniform_gptr((const uint16_t*)p.k + ce);
+    constexpr uint32_t qs = IN_F32 ? 2 : 1;            // q/k byte offsets scale with the element size
+    const gchar* qc = uniform_gptr((const char*)p.q + ce * 2 * qs);
+    const gchar* kc = uniform_gptr((const char*)p.k + ce * 2 * qs);
     const gchar* gc = uniform_gptr(p.g + ce);
     const gchar* vc = uniform_gptr((const uint16_t*)p.v + ce);
     const gchar* bc = uniform_gptr(p.beta + row0 + (size_t)t0 * p.H);
+    using QT = typename std::conditional<IN_F32, f32x2, uint32_t>::type;
     if (t0 + C <= p.T) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            r.q[i] = gload<uint32_t>(qc, kl.off[i]);
-            r.k[i] = gload<uint32_t>(kc, kl.off[i]);
+            r.q[i] = gload<QT>(qc, qs * kl.off[i]);
+            r.k[i] = gload<QT>(kc, qs * kl.off[i]);
             r.g[i] = gload<f32x2>(gc, 2 * kl.off[i]);
-            r.v[i] = gload<uint32_t>(vc, kl.voff[i]);
+            if constexpr (!IN_F32) r.v[i] = gload<uint32_t>(vc, kl.voff[i]);
         }
         r.beta = gload<float>(bc, kl.boff);
     } else {
@@ -155,21 +175,24 @@ __device__ __forceinline__ void load_chunk(Raw& r, const Params& p, const KeyLoa
         for (int i = 0; i < 8; ++i) {
             const uint32_t tb = (uint32_t)min(8 * kl.kw + i, lim) * kl.tok_b;
             const uint32_t o = tb + kl.lane_b, ov = tb + kl.vlane_b;  // both non-negative, < 2^31
-            r.q[i] = gload<uint32_t>(qc, o);
-            r.k[i] = gload<uint32_t>(kc, o);
+            r.q[i] = gload<QT>(qc, qs * o);
+            r.k[i] = gload<QT>(kc, qs * o);
             r.g[i] = gload<f32x2>(gc, 2 * o);
-            r.v[i] = gload<uint32_t>(vc, ov);
+            if constexpr (!IN_F32) r.v[i] = gload<uint32_t>(vc, ov);
         }
         r.beta = gload<float>(bc, (uint32_t)min(8 * kl.kw + (kl.lane & 7), lim) * 4u * p.H);
     }
 }
 
 // Zero the tokens at or past T (k = v = 0, beta = 0, g = 0 leaves the state unchanged).
-__device__ __forceinline__ void mask_tail(Raw& r, int T, int t0, int kw, int lane) {
+template <bool IN_F32>
+__device__ __forceinline__ void mask_tail(Raw<IN_F32>& r, int T, int t0, int kw, int lane) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         if (t0 + 8 * kw + i >= T) {
-            r.q[i] = 0u; r.k[i] = 0u; r.v[i] = 0u;
+            r.q[i] = {};
+            r.k[i] = {};
+            if constexpr (!IN_F32) r.v[i] = 0u;
             r.g[i] = f32x2{0.f, 0.f};
         }
     }
@@ -179,8 +202,9 @@ __device__ __forceinline__ void mask_tail(Raw& r, int T, int t0, int kw, int lan
 // ------------------------------------------------------------------------------------------------
 // key waves: one step = chunk n (nothing when n == nchunk); three barriers
 // ------------------------------------------------------------------------------------------------
+template <bool IN_F32, bool HP>
 __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoad& kl, size_t row0, int n,
-                                         int nchunk, Raw& cur, Raw& nxt) {
+                                         int nchunk, Raw<IN_F32>& cur, Raw<IN_F32>& nxt) {
     const int kw = kl.kw, lane = kl.lane;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int c0 = 2 * lane;   // key channels c0, c0 + 1
@@ -212,8 +236,8 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
             const float y0 = s0[i] * kLog2e - r0, y1 = s1[i] * kLog2e - r1;
             const float e0 = __builtin_amdgcn_exp2f(y0), e1 = __builtin_amdgcn_exp2f(y1);
             const float f0 = __builtin_amdgcn_exp2f(-y0), f1 = __builtin_amdgcn_exp2f(-y1);
-            const float q0 = bf16lo_to_f(cur.q[i]), q1 = bf16hi_to_f(cur.q[i]);
-            const float k0 = bf16lo_to_f(cur.k[i]), k1 = bf16hi_to_f(cur.k[i]);
+            const f32x2 qq = unpack_q(cur.q[i]), kk = unpack_q(cur.k[i]);
+            const float q0 = qq[0], q1 = qq[1], k0 = kk[0], k1 = kk[1];
             qm0[i] = q0 * e0; qm1[i] = q1 * e1;
             km0[i] = k0 * e0; km1[i] = k1 * e1;
             kh0[i] = k0 * f0; kh1[i] = k1 * f1;
@@ -241,22 +265,29 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         const float p0 = sig ? pB0 : pA0, p1 = sig ? pB1 : pA1;
         const float eP0 = fexp(p0), eP1 = fexp(p1);
         const float eC0 = fexp(bC0 - p0), eC1 = fexp(bC1 - p1);
-        uint32_t kb[8];
+        uint32_t kb[8], kl8[8];
         const float nP0 = -eP0, nP1 = -eP1;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int t = 8 * kw + i;
             *reinterpret_cast<uint32_t*>(&H.qg[t][c0]) = pack_f16(qm0[i] * eP0, qm1[i] * eP1);
             *reinterpret_cast<uint32_t*>(&H.kgn[t][c0]) = pack_f16(km0[i] * nP0, km1[i] * nP1);
-            kb[i] = pack_f16(kh0[i] * eC0, kh1[i] * eC1);
+            if constexpr (HP)
+                split_bf16(kh0[i] * eC0, kh1[i] * eC1, kb[i], kl8[i]);
+            else
+                kb[i] = pack_f16(kh0[i] * eC0, kh1[i] * eC1);
         }
         // token pairs of channel c0 (low halves) and of channel c0 + 1 (high halves)
-        const u32x4 b0 = {perm_lo(kb[0], kb[1]), perm_lo(kb[2], kb[3]), perm_lo(kb[4], kb[5]), perm_lo(kb[6], kb[7])};
-        const u32x4 b1 = {perm_hi(kb[0], kb[1]), perm_hi(kb[2], kb[3]), perm_hi(kb[4], kb[5]), perm_hi(kb[6], kb[7])};
-        *reinterpret_cast<u32x2*>(&H.kbt[c0][8 * kw]) = u32x2{b0.x, b0.y};
-        *reinterpret_cast<u32x2*>(&H.kbt[c0][8 * kw + 4]) = u32x2{b0.z, b0.w};
-        *reinterpret_cast<u32x2*>(&H.kbt[c0 + 1][8 * kw]) = u32x2{b1.x, b1.y};
-        *reinterpret_cast<u32x2*>(&H.kbt[c0 + 1][8 * kw + 4]) = u32x2{b1.z, b1.w};
+        auto put_t = [&](uint16_t (*dst)[LDT8], const uint32_t* w) {
+            const u32x4 b0 = {perm_lo(w[0], w[1]), perm_lo(w[2], w[3]), perm_lo(w[4], w[5]), perm_lo(w[6], w[7])};
+            const u32x4 b1 = {perm_hi(w[0], w[1]), perm_hi(w[2], w[3]), perm_hi(w[4], w[5]), perm_hi(w[6], w[7])};
+            *reinterpret_cast<u32x2*>(&dst[c0][8 * kw]) = u32x2{b0.x, b0.y};
+            *reinterpret_cast<u32x2*>(&dst[c0][8 * kw + 4]) = u32x2{b0.z, b0.w};
+            *reinterpret_cast<u32x2*>(&dst[c0 + 1][8 * kw]) = u32x2{b1.x, b1.y};
+            *reinterpret_cast<u32x2*>(&dst[c0 + 1][8 * kw + 4]) = u32x2{b1.z, b1.w};
+        };
+        put_t(H.kbh, kb);
+        if constexpr (HP) put_t(H.kbl, kl8);
         if (sig == 0) {
             // K/Gamma rows of sub-tile 0 moved to sub-tile 1's reference: factor exp(b_23 - b_7) <= 1
             const float f0 = fexp(pB0 - pA0), f1 = fexp(pB1 - pA1);
@@ -302,7 +333,7 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
                 H.al[SUB * R + i][SUB * S + l16] = pack_bf16(v - bf16lo_to_f(hi), 0.f) & 0xffffu;
             }
         } else {
-            // L(0,0), L(1,0), L(1,1) in bf16
+            // L(0,0), L(1,0), L(1,1): bf16 Km against K/Gamma (split bf16 when HP, else its high part)
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -312,6 +343,11 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
                 acc0 = mfma_bf16(a0, ld16(&sm.key.khh[l16][kc]), acc0);
                 acc1 = mfma_bf16(a1, ld16(&sm.key.k1h[l16][kc]), acc1);
                 acc2 = mfma_bf16(a1, ld16(&sm.key.khh[SUB + l16][kc]), acc2);
+                if constexpr (HP) {
+                    acc0 = mfma_bf16(a0, ld16(&sm.key.khl[l16][kc]), acc0);
+                    acc1 = mfma_bf16(a1, ld16(&sm.key.k1l[l16][kc]), acc1);
+                    acc2 = mfma_bf16(a1, ld16(&sm.key.khl[SUB + l16][kc]), acc2);
+                }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -322,18 +358,21 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
             }
         }
         // V^T and beta of this chunk (the value waves are done with the previous ones)
-        if (lane < 32) {  // value columns 2*lane, 2*lane+1 of this half
-            const uint32_t* v = cur.v;
-            *reinterpret_cast<u32x4*>(&sm.h1.vt[2 * lane][8 * kw]) =
-                u32x4{perm_lo(v[0], v[1]), perm_lo(v[2], v[3]), perm_lo(v[4], v[5]), perm_lo(v[6], v[7])};
-            *reinterpret_cast<u32x4*>(&sm.h1.vt[2 * lane + 1][8 * kw]) =
-                u32x4{perm_hi(v[0], v[1]), perm_hi(v[2], v[3]), perm_hi(v[4], v[5]), perm_hi(v[6], v[7])};
+        if constexpr (!IN_F32) {
+            if (lane < 32) {  // V^T for value columns 2*lane, 2*lane+1 of this half
+                const uint32_t* v = cur.v;
+                *reinterpret_cast<u32x4*>(&sm.h1.vt[2 * lane][8 * kw]) =
+                    u32x4{perm_lo(v[0], v[1]), perm_lo(v[2], v[3]), perm_lo(v[4], v[5]), perm_lo(v[6], v[7])};
+                *reinterpret_cast<u32x4*>(&sm.h1.vt[2 * lane + 1][8 * kw]) =
+                    u32x4{perm_hi(v[0], v[1]), perm_hi(v[2], v[3]), perm_hi(v[4], v[5]), perm_hi(v[6], v[7])};
+            }
         }
         if (lane < 8) sm.h1.beta[8 * kw + lane] = cur.beta;
     }
     lds_barrier();  // ---- barrier 3
 }
 
+template <bool IN_F32, bool HP>
 __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int half, int kw, int lane, int nchunk) {
     // A's block (0,1) is zero in both buffers; no chunk writes it
     for (int e = 64 * kw + lane; e < 2 * SUB * SUB; e += 256) {
@@ -353,19 +392,19 @@ __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int half, int 
         kl.voff[i] = (uint32_t)(8 * kw + i) * kl.tok_b + kl.vlane_b;
     }
     kl.boff = (uint32_t)(8 * kw + (lane & 7)) * 4u * p.H;
-    Raw ra, rb;
+    Raw<IN_F32> ra, rb;
     if (p.T > 0) load_chunk(ra, p, kl, row0, 0);
     // two steps per iteration so the prefetch target alternates between two register sets
     for (int n = 0; n <= nchunk; n += 2) {
-        key_step(sm, p, kl, row0, n, nchunk, ra, rb);
-        if (n + 1 <= nchunk) key_step(sm, p, kl, row0, n + 1, nchunk, rb, ra);
+        key_step<IN_F32, HP>(sm, p, kl, row0, n, nchunk, ra, rb);
+        if (n + 1 <= nchunk) key_step<IN_F32, HP>(sm, p, kl, row0, n + 1, nchunk, rb, ra);
     }
 }
 
 // ------------------------------------------------------------------------------------------------
 // value waves: one step = chunk n-1 (nothing when n == 0); three barriers
 // ------------------------------------------------------------------------------------------------
-template <bool OUT_F32>
+template <bool OUT_F32, bool IN_F32, bool HP>
 __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int half, int vw, int lane, int nchunk) {
     const int l16 = lane & 15, g4 = lane >> 4;
     ValueTiles& V = sm.val;
@@ -403,6 +442,21 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
 #pragma unroll
     for (int R = 0; R < 2; ++R)
         ooff[R] = ((uint32_t)(SUB * R + l16) * (uint32_t)p.H * DV + half * DVH + 16 * vw + 4 * g4) * (OUT_F32 ? 4u : 2u);
+
+    // float32 inputs: this lane's V values (tokens 16R + 4*g4 + r of a chunk, column col), read one
+    // step ahead; rows past T read the last valid row (their U rows come out zero: beta = 0 there)
+    f32x4 vnext[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    auto load_v = [&](int tc0) {
+        const gchar* vb = uniform_gptr((const char*)p.v + ((row0 + (size_t)tc0 * p.H) * DV) * 4);
+        const int lim = p.T - 1 - tc0;
+#pragma unroll
+        for (int R = 0; R < 2; ++R)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vnext[R][r] = gload<float>(vb, ((uint32_t)min(SUB * R + 4 * g4 + r, lim) * (uint32_t)p.H * DV + col) * 4u);
+    };
+    if constexpr (IN_F32)
+        if (nchunk > 0) load_v(0);
 
     for (int n = 0; n <= nchunk; ++n) {
         const bool work = n >= 1;  // this step handles chunk n-1
@@ -494,10 +548,16 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
         if (work) {
             // X = V - (K*Gamma) S, started from V in accumulator layout
             f32x4 xr[2];
+            if constexpr (IN_F32) {
+                xr[0] = vnext[0];
+                xr[1] = vnext[1];
+                if (n < nchunk) load_v(n * C);  // V of the chunk handled next step
+            } else {
 #pragma unroll
-            for (int R = 0; R < 2; ++R) {
-                const u32x2 vv = *reinterpret_cast<const u32x2*>(&sm.h1.vt[16 * vw + l16][SUB * R + 4 * g4]);
-                xr[R] = f32x4{bf16lo_to_f(vv.x), bf16hi_to_f(vv.x), bf16lo_to_f(vv.y), bf16hi_to_f(vv.y)};
+                for (int R = 0; R < 2; ++R) {
+                    const u32x2 vv = *reinterpret_cast<const u32x2*>(&sm.h1.vt[16 * vw + l16][SUB * R + 4 * g4]);
+                    xr[R] = f32x4{bf16lo_to_f(vv.x), bf16hi_to_f(vv.x), bf16lo_to_f(vv.y), bf16hi_to_f(vv.y)};
+                }
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -536,8 +596,6 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
                 a2 = mfma_bf16(tL, xh, a2);
                 u[R] = (a0 + a1) + a2;
             }
-            uf = u32x4{pack_f16(u[0][0], u[0][1]), pack_f16(u[0][2], u[0][3]), pack_f16(u[1][0], u[1][1]),
-                       pack_f16(u[1][2], u[1][3])};
             uint32_t uh0, uh1, uh2, uh3, ul0, ul1, ul2, ul3;
             split_bf16(u[0][0], u[0][1], uh0, ul0);
             split_bf16(u[0][2], u[0][3], uh1, ul1);
@@ -545,6 +603,9 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
             split_bf16(u[1][2], u[1][3], uh3, ul3);
             uh = u32x4{uh0, uh1, uh2, uh3};
             ul = u32x4{ul0, ul1, ul2, ul3};
+            if constexpr (!HP)
+                uf = u32x4{pack_f16(u[0][0], u[0][1]), pack_f16(u[0][2], u[0][3]), pack_f16(u[1][0], u[1][1]),
+                           pack_f16(u[1][2], u[1][3])};
         }
         lds_barrier();  // ---- barrier 2
 
@@ -570,8 +631,15 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) {
                 const f32x4 gm = *reinterpret_cast<const f32x4*>(&H.gamc[16 * cb + 4 * g4]);
-                const u32x4 a = ld8x2(&H.kbt[16 * cb + l16][4 * g4], &H.kbt[16 * cb + l16][SUB + 4 * g4]);
-                st[cb] = mfma_f16(a, uf, st[cb] * gm);
+                const u32x4 aH = ld8x2(&H.kbh[16 * cb + l16][4 * g4], &H.kbh[16 * cb + l16][SUB + 4 * g4]);
+                if constexpr (HP) {
+                    const u32x4 aL = ld8x2(&H.kbl[16 * cb + l16][4 * g4], &H.kbl[16 * cb + l16][SUB + 4 * g4]);
+                    f32x4 acc = mfma_bf16(aH, uh, st[cb] * gm);
+                    acc = mfma_bf16(aH, ul, acc);
+                    st[cb] = mfma_bf16(aL, uh, acc);
+                } else {
+                    st[cb] = mfma_f16(aH, uf, st[cb] * gm);
+                }
             }
             make_sb();
         }
@@ -590,7 +658,7 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
     }
 }
 
-template <bool OUT_F32>
+template <bool OUT_F32, bool IN_F32, bool HP>
 __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
     __shared__ Smem sm;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -611,19 +679,26 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
     const int nchunk = (p.T + C - 1) / C;
 
     if (wave < 4)
-        key_waves(sm, p, row0, half, wave, lane, nchunk);
+        key_waves<IN_F32, HP>(sm, p, row0, half, wave, lane, nchunk);
     else
-        value_waves<OUT_F32>(sm, p, bh, row0, half, wave - 4, lane, nchunk);
+        value_waves<OUT_F32, IN_F32, HP>(sm, p, bh, row0, half, wave - 4, lane, nchunk);
 }
 
 }  // namespace bf16path
 
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t stream) {
-    const int nblk = 2 * p.B * p.H;
-    if (p.o_f32)
-        hipLaunchKernelGGL(bf16path::kda_fwd_bf16_kernel<true>, dim3(nblk), dim3(bf16path::NTHR), 0, stream, p);
+    using namespace bf16path;
+    const dim3 grid(2 * p.B * p.H), block(NTHR);
+    if (p.in_f32)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, true, true>), grid, block, 0, stream, p);
+    else if (p.o_f32 && p.precise)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, false, true>), grid, block, 0, stream, p);
+    else if (p.o_f32)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, false, false>), grid, block, 0, stream, p);
+    else if (p.precise)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, false, true>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL(bf16path::kda_fwd_bf16_kernel<false>, dim3(nblk), dim3(bf16path::NTHR), 0, stream, p);
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, false, false>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

@@ -17,9 +17,11 @@ struct Params {
     int B, T, H, Dk, Dv;
     float scale;
     int o_f32;         // bf16 inputs with a float32 output
+    int in_f32;        // matrix-core path with float32 q, k, v (and float32 output); layer use
+    int precise;       // matrix-core path: split-bf16 L and state update (always on with in_f32)
 };
 
-hipError_t launch_fwd_bf16(const Params& p, hipStream_t stream);  // Dk = Dv = 128, chunk 32
+hipError_t launch_fwd_bf16(const Params& p, hipStream_t stream);  // Dk = Dv = 128, chunk 32 (in_f32 too)
 hipError_t launch_fwd_f32(const Params& p, hipStream_t stream);   // Dk = Dv in {64, 128}, chunk 16
 hipError_t launch_state_copy(const Params& p, hipStream_t stream); // T = 0: S_T = S0 (or 0)
 

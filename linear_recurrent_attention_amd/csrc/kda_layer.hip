@@ -1,0 +1,294 @@
+// Fused KDA layer forward on gfx950: projections, short convolution, gates, the KDA core, norm.
+//
+// The layer of the explainer page "Kimi K3：开放前沿智能":
+//   section 2.4 (paper Eq. 2): q, k = L2norm(Swish(ShortConv(x W))), v = x W_v;
+//   section 2.3 (paper Eq. 2): decay logit z = W_up W_down x + b_alpha (low-rank), and
+//   section 3.2 (paper Eq. 5): log(alpha) = -5 * sigmoid(exp(A_h) z), A a per-head log-scale;
+//   beta = sigmoid(x W_beta) (not stated on the page; the plainest reading);
+//   section 2.2/2.4: the gated delta rule and its readout (the bf16 KDA core of this library);
+//   section 3.3 (paper Eq. 6): per-head RMSNorm, then a full-rank data-dependent gate
+//   sigmoid(x W_g) with W_g of size d x d; finally the output projection W_o.
+// Short convolution: causal, depthwise, 4 taps, no bias, tap 3 on the current token; the window
+// of the previous 3 tokens comes from conv_state_in (zeros if absent) and the last 3 pre-conv
+// rows go to conv_state_out.  L2 and RMSNorm use eps = 1e-6 inside the square root.
+//
+// The plain projections run on rocBLAS (bf16 operands, float32 accumulate and output; the
+// rank-128 up-projection in float32).  The element-wise work around the core is fused into two
+// kernels, one wave per (token, head) with two channels per lane:
+//   prologue: short conv + SiLU + L2 on q and k, the decay gate, beta (q, k, v stay float32:
+//             the core's float32-input variant reads them, so the per-head RMSNorm does not
+//             amplify a bf16 rounding of the core's inputs);
+//   epilogue: RMSNorm of the core output, times sigmoid(gate), to bf16 for the output projection.
+#include "kda_common.h"
+#include "kda_internal.h"
+#include "../../include/kda.h"
+
+#include <rocblas/rocblas.h>
+
+#include <mutex>
+#include <vector>
+
+namespace kda {
+namespace layer {
+
+constexpr int D = 128;  // head size (key and value)
+constexpr float EPS = 1e-6f;
+
+struct ProParams {
+    int B, T, H, HD;
+    const float* pq;       // [B*T, HD] pre-conv q projection
+    const float* pk;       // [B*T, HD] pre-conv k projection
+    const float* pv;       // [B*T, HD]
+    const float* pz;       // [B*T, HD] low-rank decay logit (without bias)
+    const float* pbeta;    // [B*T, H]  beta logit
+    const float* conv_q;   // [HD, 4]
+    const float* conv_k;   // [HD, 4]
+    const float* b_alpha;  // [HD]
+    const float* A;        // [H]
+    const float* state_in; // [B, 3, 2*HD] or null
+    float* q;              // [B*T, HD] = [B, T, H, D]
+    float* k;
+    float* v;
+    float* g;              // [B*T, HD]
+    float* beta;           // [B*T, H]
+};
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + fexp(-x)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// conv + SiLU on channels c, c+1 of row (b, t); `which` 0 = q, 1 = k
+__device__ __forceinline__ float2 conv_silu(const ProParams& p, const float* src, const float* taps, int which, int b,
+                                            int t, int c) {
+    const float4 w0 = *reinterpret_cast<const float4*>(taps + (size_t)c * 4);
+    const float4 w1 = *reinterpret_cast<const float4*>(taps + (size_t)(c + 1) * 4);
+    const float wa[4] = {w0.x, w0.y, w0.z, w0.w}, wb[4] = {w1.x, w1.y, w1.z, w1.w};
+    float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tt = t - 3 + j;
+        float2 x = make_float2(0.f, 0.f);
+        if (tt >= 0) {
+            x = *reinterpret_cast<const float2*>(src + ((size_t)b * p.T + tt) * p.HD + c);
+        } else if (p.state_in) {
+            x = *reinterpret_cast<const float2*>(p.state_in + ((size_t)b * 3 + (3 + tt)) * 2 * p.HD + which * p.HD + c);
+        }
+        y0 += wa[j] * x.x;
+        y1 += wb[j] * x.y;
+    }
+    return make_float2(y0 * sigmoidf_(y0), y1 * sigmoidf_(y1));
+}
+
+__global__ void __launch_bounds__(256) prologue_kernel(ProParams p) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long gw = (long)blockIdx.x * 4 + wave;  // (row, head)
+    if (gw >= (long)p.B * p.T * p.H) return;
+    const long row = gw / p.H;
+    const int h = (int)(gw - row * p.H);
+    const int b = (int)(row / p.T), t = (int)(row - (long)b * p.T);
+    const int c = h * D + 2 * lane;
+    const size_t rc = (size_t)row * p.HD + c;
+
+    const float2 qs = conv_silu(p, p.pq, p.conv_q, 0, b, t, c);
+    const float2 ks = conv_silu(p, p.pk, p.conv_k, 1, b, t, c);
+    const float qn = rsqrtf(wave_sum(qs.x * qs.x + qs.y * qs.y) + EPS);
+    const float kn = rsqrtf(wave_sum(ks.x * ks.x + ks.y * ks.y) + EPS);
+    *reinterpret_cast<float2*>(p.q + rc) = make_float2(qs.x * qn, qs.y * qn);
+    *reinterpret_cast<float2*>(p.k + rc) = make_float2(ks.x * kn, ks.y * kn);
+    const float2 z = *reinterpret_cast<const float2*>(p.pz + rc);
+    const float2 ba = *reinterpret_cast<const float2*>(p.b_alpha + c);
+    const float ea = fexp(p.A[h]);
+    *reinterpret_cast<float2*>(p.g + rc) =
+        make_float2(-5.f * sigmoidf_(ea * (z.x + ba.x)), -5.f * sigmoidf_(ea * (z.y + ba.y)));
+    if (lane == 0) p.beta[(size_t)row * p.H + h] = sigmoidf_(p.pbeta[(size_t)row * p.H + h]);
+}
+
+// Last three pre-conv rows of each sequence (from this call's projections, or the incoming window
+// when T < 3): the window the next segment continues from.
+__global__ void conv_state_kernel(int B, int T, int HD, const float* pq, const float* pk, const float* state_in,
+                                  float* state_out) {
+    const long n = (long)B * 3 * 2 * HD;
+    for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
+        const int ch = (int)(e % (2 * HD));
+        const long r = e / (2 * HD);
+        const int s = (int)(r % 3), b = (int)(r / 3);
+        const int tt = T - 3 + s;
+        float val = 0.f;
+        if (tt >= 0) {
+            const float* src = ch < HD ? pq : pk;
+            val = src[((size_t)b * T + tt) * HD + (ch % HD)];
+        } else if (state_in) {
+            val = state_in[((size_t)b * 3 + (3 + tt)) * 2 * HD + ch];
+        }
+        state_out[e] = val;
+    }
+}
+
+__global__ void __launch_bounds__(256) epilogue_kernel(int rows, int H, int HD, const float* o, const float* pg,
+                                                      const float* rms_w, uint16_t* gated) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long gw = (long)blockIdx.x * 4 + wave;
+    if (gw >= (long)rows * H) return;
+    const long row = gw / H;
+    const int h = (int)(gw - row * H);
+    const size_t rc = (size_t)row * HD + h * D + 2 * lane;
+    const float2 ov = *reinterpret_cast<const float2*>(o + rc);
+    const float inv = rsqrtf(wave_sum(ov.x * ov.x + ov.y * ov.y) * (1.f / D) + EPS);
+    const float2 w = *reinterpret_cast<const float2*>(rms_w + 2 * lane);
+    const float2 gl = *reinterpret_cast<const float2*>(pg + rc);
+    *reinterpret_cast<uint32_t*>(gated + rc) =
+        pack_bf16(ov.x * inv * w.x * sigmoidf_(gl.x), ov.y * inv * w.y * sigmoidf_(gl.y));
+}
+
+__global__ void bf16_to_f32_kernel(const uint16_t* src, float* dst, long n) {
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+        dst[i] = __uint_as_float((uint32_t)src[i] << 16);
+}
+
+// ------------------------------------------------------------------------------------------------
+// rocBLAS handles, one per device, created on first use and kept for the process
+std::mutex g_blas_mu;
+std::vector<rocblas_handle> g_blas;
+
+rocblas_handle blas_handle(int dev) {
+    std::lock_guard<std::mutex> lk(g_blas_mu);
+    if ((int)g_blas.size() <= dev) g_blas.resize(dev + 1, nullptr);
+    if (!g_blas[dev]) {
+        rocblas_handle hd = nullptr;
+        if (rocblas_create_handle(&hd) != rocblas_status_success) return nullptr;
+        g_blas[dev] = hd;
+    }
+    return g_blas[dev];
+}
+
+// row-major C[M,N] = A[M,K] B[K,N], i.e. column-major C^T = B^T A^T
+rocblas_status gemm_rm(rocblas_handle hd, int M, int N, int K, const void* Am, rocblas_datatype at, const void* Bm,
+                       rocblas_datatype bt, void* Cm, rocblas_datatype ct) {
+    const float alpha = 1.f, beta = 0.f;
+    return rocblas_gemm_ex(hd, rocblas_operation_none, rocblas_operation_none, N, M, K, &alpha, Bm, bt, N, Am, at, K,
+                           &beta, Cm, ct, N, Cm, ct, N, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+}
+
+struct Workspace {
+    float *pq, *pk, *pv, *pg, *pz, *pdown, *pbeta, *wup32, *g, *beta, *o, *q, *k;
+    uint16_t* gated;
+    size_t bytes;
+};
+
+Workspace carve(const kda_layer_desc* d, char* base) {
+    const size_t BT = (size_t)d->B * d->T, HD = (size_t)d->H * D;
+    size_t off = 0;
+    auto take = [&](size_t nbytes) {
+        char* p = base ? base + off : nullptr;
+        off += (nbytes + 255) & ~(size_t)255;
+        return p;
+    };
+    Workspace w;
+    w.pq = (float*)take(BT * HD * 4);
+    w.pk = (float*)take(BT * HD * 4);
+    w.pv = (float*)take(BT * HD * 4);
+    w.pg = (float*)take(BT * HD * 4);
+    w.pz = (float*)take(BT * HD * 4);
+    w.pdown = (float*)take(BT * d->rank * 4);
+    w.pbeta = (float*)take(BT * d->H * 4);
+    w.wup32 = (float*)take((size_t)d->rank * HD * 4);
+    w.g = (float*)take(BT * HD * 4);
+    w.beta = (float*)take(BT * d->H * 4);
+    w.o = (float*)take(BT * HD * 4);
+    w.q = (float*)take(BT * HD * 4);
+    w.k = (float*)take(BT * HD * 4);
+    w.gated = (uint16_t*)take(BT * HD * 2);
+    w.bytes = off;
+    return w;
+}
+
+}  // namespace layer
+}  // namespace kda
+
+using namespace kda::layer;
+
+namespace {
+kda_status check_layer(const kda_layer_desc* d, const void* x, const kda_layer_weights* w, const void* y) {
+    if (!d || !w || !x || !y) return KDA_ERR_INVALID_ARG;
+    if (d->B < 1 || d->T < 1 || d->H < 1 || d->d_model < 1 || d->rank < 1 || d->flags != 0) return KDA_ERR_INVALID_ARG;
+    if (d->Dk != D || d->Dv != D || d->conv != 4) return KDA_ERR_UNSUPPORTED;
+    if (d->d_model % 8 != 0 || d->rank % 8 != 0) return KDA_ERR_UNSUPPORTED;
+    if ((long long)d->B * d->T > (1LL << 30) || (long long)d->B * d->T * d->H * D > (1LL << 40)) return KDA_ERR_INVALID_ARG;
+    if (!w->Wq || !w->Wk || !w->Wv || !w->Wg || !w->Wo || !w->Wbeta || !w->Wdown || !w->Wup || !w->conv_q ||
+        !w->conv_k || !w->b_alpha || !w->A || !w->rms_w)
+        return KDA_ERR_INVALID_ARG;
+    if (!(d->scale == d->scale)) return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t kda_layer_workspace_size(const kda_layer_desc* desc) {
+    if (!desc || desc->B < 1 || desc->T < 1 || desc->H < 1 || desc->rank < 1) return 0;
+    return carve(desc, nullptr).bytes;
+}
+
+kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer_weights* w, const float* S0,
+                         const float* conv_state_in, void* y, float* S_T, float* conv_state_out, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+    const kda_status st = check_layer(d, x, w, y);
+    if (st != KDA_OK) return st;
+    const Workspace W = carve(d, (char*)ws);
+    if (!ws || ws_bytes < W.bytes) return KDA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return KDA_ERR_INVALID_ARG;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+    rocblas_handle hd = blas_handle(dev);
+    if (!hd) return KDA_ERR_HIP;
+    const int M = d->B * d->T, HD = d->H * D, dm = d->d_model, R = d->rank;
+    const rocblas_datatype bf = rocblas_datatype_bf16_r, f32 = rocblas_datatype_f32_r;
+
+    std::lock_guard<std::mutex> lk(g_blas_mu);  // the handle's stream is per call
+    if (rocblas_set_stream(hd, stream) != rocblas_status_success) return KDA_ERR_HIP;
+    bool ok = true;
+    ok &= gemm_rm(hd, M, HD, dm, x, bf, w->Wq, bf, W.pq, f32) == rocblas_status_success;
+    ok &= gemm_rm(hd, M, HD, dm, x, bf, w->Wk, bf, W.pk, f32) == rocblas_status_success;
+    ok &= gemm_rm(hd, M, HD, dm, x, bf, w->Wv, bf, W.pv, f32) == rocblas_status_success;
+    ok &= gemm_rm(hd, M, HD, dm, x, bf, w->Wg, bf, W.pg, f32) == rocblas_status_success;
+    ok &= gemm_rm(hd, M, R, dm, x, bf, w->Wdown, bf, W.pdown, f32) == rocblas_status_success;
+    ok &= gemm_rm(hd, M, d->H, dm, x, bf, w->Wbeta, bf, W.pbeta, f32) == rocblas_status_success;
+    if (!ok) return KDA_ERR_HIP;
+    {
+        const long n = (long)R * HD;
+        hipLaunchKernelGGL(bf16_to_f32_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
+                           dim3(256), 0, stream, (const uint16_t*)w->Wup, W.wup32, n);
+    }
+    if (gemm_rm(hd, M, HD, R, W.pdown, f32, W.wup32, f32, W.pz, f32) != rocblas_status_success) return KDA_ERR_HIP;
+
+    ProParams pp;
+    pp.B = d->B; pp.T = d->T; pp.H = d->H; pp.HD = HD;
+    pp.pq = W.pq; pp.pk = W.pk; pp.pv = W.pv; pp.pz = W.pz; pp.pbeta = W.pbeta;
+    pp.conv_q = w->conv_q; pp.conv_k = w->conv_k; pp.b_alpha = w->b_alpha; pp.A = w->A;
+    pp.state_in = conv_state_in;
+    pp.q = W.q; pp.k = W.k; pp.v = nullptr; pp.g = W.g; pp.beta = W.beta;
+    const long nw = (long)M * d->H;
+    hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, stream, pp);
+    if (conv_state_out)
+        hipLaunchKernelGGL(conv_state_kernel, dim3(256), dim3(256), 0, stream, d->B, d->T, HD, W.pq, W.pk,
+                           conv_state_in, conv_state_out);
+
+    kda::Params p;
+    // the core reads q, k, v in float32 (v straight from the projection output): rounding them to
+    // bf16 first would be amplified by the per-head RMSNorm wherever a head's output is small
+    p.q = W.q; p.k = W.k; p.v = W.pv; p.g = W.g; p.beta = W.beta; p.S0 = S0; p.o = W.o; p.S_T = S_T;
+    p.B = d->B; p.T = d->T; p.H = d->H; p.Dk = D; p.Dv = D; p.scale = d->scale; p.o_f32 = 1; p.in_f32 = 1; p.precise = 1;
+    if (kda::launch_fwd_bf16(p, stream) != hipSuccess) return KDA_ERR_HIP;
+
+    hipLaunchKernelGGL(epilogue_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, stream, M, d->H, HD, W.o, W.pg,
+                       w->rms_w, W.gated);
+    if (gemm_rm(hd, M, dm, HD, W.gated, bf, w->Wo, bf, y, bf) != rocblas_status_success) return KDA_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

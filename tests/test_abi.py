@@ -55,10 +55,17 @@ def test_null_descriptor():
     assert _lib.lib().kda_fwd(None, *([None] * 9)) == _lib.KDA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("field,value", [("B", 0), ("H", 0), ("T", -1), ("Dk", 0), ("Dv", -3), ("flags", 1),
+@pytest.mark.parametrize("field,value", [("B", 0), ("H", 0), ("T", -1), ("Dk", 0), ("Dv", -3), ("flags", 2), ("flags", -1),
                                          ("io_dtype", 5), ("o_dtype", 9)])
 def test_bad_sizes_and_enums(field, value):
     assert call(desc(**{field: value})) == _lib.KDA_ERR_INVALID_ARG
+
+
+def test_precise_flag_accepted_with_empty_sequence():
+    # T = 0 launches only the state copy; the flag is a valid request on either path
+    for io in (_lib.KDA_BF16, _lib.KDA_F32):
+        d = desc(T=0, flags=_lib.KDA_FWD_PRECISE, io_dtype=io, o_dtype=io)
+        assert _lib.fwd_raw(d, 0, 0, 0, 0, 0, 0, 0, 0, None) == _lib.KDA_OK
 
 
 def test_nan_scale():

@@ -25,10 +25,11 @@ def to_dev(d, io):
     return t
 
 
-def gpu_fwd(d, io, S0=None, o_dtype=None, scale=1.0):
+def gpu_fwd(d, io, S0=None, o_dtype=None, scale=1.0, precise=False):
     t = to_dev(d, io)
     S0t = None if S0 is None else torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).to(DEV)
-    o, ST = _kda().kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=S0t, scale=scale, o_dtype=o_dtype)
+    o, ST = _kda().kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=S0t, scale=scale, o_dtype=o_dtype,
+                           precise=precise)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), ST.cpu().numpy()
 
@@ -95,6 +96,45 @@ def test_workload2_full_launch_sampled_heads():
         o_ref, S_ref = oracle.recurrence(s["q"], s["k"], s["v"], s["g"], s["beta"])
         assert rel_max_bf16_out(o[b:b + 1, :, h:h + 1], o_ref) <= TOL_BF16, (b, h)
         assert rel_max(ST[b:b + 1, h:h + 1], S_ref) <= TOL_BF16, (b, h)
+
+
+def correlated_keys(seed, B, T, H, D=128, cos=0.5):
+    """bf16 inputs whose keys share one random direction per head (pairwise cosine about `cos`), as
+    the layer's Swish-activated, convolved keys do; g and beta as in the workloads."""
+    rng = np.random.default_rng(seed)
+    d, _ = rand_small(seed, B, T, H, D, s0=False)
+    u = rng.standard_normal((H, D))
+    u *= np.sqrt(D * cos / (1 - cos)) / np.linalg.norm(u, axis=-1, keepdims=True)
+    k = rng.standard_normal((B, T, H, D)) + u[None, None]
+    d["k"] = synth.bf16_round(k / np.linalg.norm(k, axis=-1, keepdims=True))
+    return d
+
+
+def test_precise_flag_correlated_keys():
+    """KDA_FWD_PRECISE on keys with pairwise cosine 0.5 (B1 H4 T2048, S0 in): o and S_T within 1e-2.
+    The default plan's errors are printed for reference."""
+    d = correlated_keys(11, 1, 2048, 4)
+    S0 = (np.random.default_rng(12).standard_normal((1, 4, 128, 128)) * 0.3).astype(np.float32)
+    o_ref, S_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=S0)
+    o, ST = gpu_fwd(d, "bf16", S0=S0, precise=True)
+    o_d, ST_d = gpu_fwd(d, "bf16", S0=S0)
+    print(f"precise: o {rel_max_bf16_out(o, o_ref):.4g} S_T {rel_max(ST, S_ref):.4g}; "
+          f"default: o {rel_max_bf16_out(o_d, o_ref):.4g} S_T {rel_max(ST_d, S_ref):.4g}")
+    assert rel_max_bf16_out(o, o_ref) <= TOL_BF16
+    assert rel_max(ST, S_ref) <= TOL_BF16
+    o32, ST32 = gpu_fwd(d, "bf16", S0=S0, o_dtype=torch.float32, precise=True)
+    assert rel_max(o32, o_ref) <= TOL_BF16
+    assert np.array_equal(ST32, ST)
+
+
+def test_precise_flag_workload1():
+    """The precise plan also meets the bound on the B1 H16 T4096 workload, and is no worse there."""
+    d = synth.core_inputs(1, seed=0)
+    o_ref, S_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
+    o, ST = gpu_fwd(d, "bf16", S0=d["S0"], precise=True)
+    o_d, ST_d = gpu_fwd(d, "bf16", S0=d["S0"])
+    assert rel_max_bf16_out(o, o_ref) <= TOL_BF16
+    assert rel_max(ST, S_ref) <= min(TOL_BF16, 1.05 * rel_max(ST_d, S_ref))
 
 
 # ---- edge cases ---------------------------------------------------------------------------------------
