@@ -23,10 +23,12 @@ def lib_path() -> str:
 
 
 def build(force: bool = True) -> str:
-    """Compile the C oracle with gcc (float64, OpenMP)."""
+    """Compile the C oracle with gcc (float64, OpenMP).  -O3 vectorises the element-wise loops over
+    value columns only (no reductions are reordered, and baseline x86-64 has no fused multiply-add),
+    so the results are bit-for-bit those of an unoptimised build's arithmetic order."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", _SRC, "-o", tmp, "-lm"])
+        subprocess.check_call(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c99", _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 

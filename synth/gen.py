@@ -5,11 +5,12 @@ the dtype the kernel receives.  Both the GPU path and the CPU oracle consume
 the *rounded* values (bf16 values are carried as float32 arrays, which hold
 them exactly), so rounding of the inputs is never a source of disagreement.
 
-Draws are made per block of tokens, each block from its own
-``SeedSequence([seed, workload, 1, block])`` stream, so a block can be
-regenerated on its own (the million-token workload is streamed this way) and
-blocks can be drawn on several threads.  Per-head parameters come from the
-stream ``[seed, workload, 0]``.
+Draws are made per (block of tokens, head), each from its own
+``SeedSequence([seed, workload, 1, block, head])`` stream, in the order q, k,
+v, beta logit, z, so a block can be regenerated on its own (the
+million-token workload is streamed this way) and the pieces can be drawn on
+several threads.  Per-head parameters come from the stream
+``[seed, workload, 0]``.
 
 Input recipe (the reading of the workload descriptions):
   * q, k: N(0,1) per element, then scaled to unit L2 norm per (token, head);
@@ -61,14 +62,19 @@ LAYER = dict(name="kda_layer_fwd_bf16_B2_T8192_d2048_H16_D128", B=2, T=8192, d=2
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32/float64 values to bfloat16 (nearest, ties to even); return the uint16 bit patterns."""
     x32 = np.ascontiguousarray(x, dtype=np.float32)
-    u = x32.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    u = x32.view(np.uint32)
+    # finite values stay below 2^32 after the rounding increment (|x| <= 0x7F7FFFFF + 0x8000 with sign)
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    r += u
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """bf16-rounded values carried in a float32 array (exact)."""
-    b = bf16_bits(x).astype(np.uint32) << 16
+    b = bf16_bits(x).astype(np.uint32)
+    b <<= 16
     return b.view(np.float32)
 
 
@@ -96,19 +102,17 @@ def head_params(wid: int, seed: int = 0, H: int | None = None):
     return A, S0
 
 
-def core_inputs_block(wid: int, j: int, seed: int = 0, A: np.ndarray | None = None, need_q: bool = True):
-    """Inputs for token block j of workload wid: dict of float32 arrays shaped [B, block, H, *]."""
+def _unit(wid: int, j: int, h: int, seed: int, A_h: float, need_q: bool):
+    """Draws of token block j, head h: dict of float32 arrays shaped [B, block, *]."""
     w = WORKLOADS[wid]
-    if A is None:
-        A, _ = head_params(wid, seed)
     TB = min(w.block, w.T)
-    rng = _rng(seed, wid, 1, j)
-    shp_k = (w.B, TB, w.H, w.Dk)
+    rng = _rng(seed, wid, 1, j, h)
+    shp_k = (w.B, TB, w.Dk)
     q_raw = rng.standard_normal(shp_k)
     k_raw = rng.standard_normal(shp_k)
-    v = rng.standard_normal((w.B, TB, w.H, w.Dv))
-    beta_logit = rng.standard_normal((w.B, TB, w.H))
-    z = rng.standard_normal(shp_k) * np.sqrt(w.var_z)
+    v = rng.standard_normal((w.B, TB, w.Dv))
+    beta_logit = rng.standard_normal((w.B, TB))
+    z = rng.standard_normal(shp_k)
     out = {}
     if need_q:
         out["q"] = _io_round(q_raw / np.linalg.norm(q_raw, axis=-1, keepdims=True), w.io)
@@ -116,12 +120,39 @@ def core_inputs_block(wid: int, j: int, seed: int = 0, A: np.ndarray | None = No
     out["k"] = _io_round(k_raw / np.linalg.norm(k_raw, axis=-1, keepdims=True), w.io)
     out["v"] = _io_round(v, w.io)
     out["beta"] = _sigmoid(beta_logit).astype(np.float32)
-    out["g"] = (G_MIN * _sigmoid(np.exp(A)[None, None, :, None] * z)).astype(np.float32)
+    z *= np.sqrt(w.var_z) * np.exp(A_h)
+    out["g"] = (G_MIN * _sigmoid(z)).astype(np.float32)
+    return out
+
+
+def _pool(threads: int | None):
+    return _cf.ThreadPoolExecutor(max_workers=threads or min(16, os.cpu_count() or 1))
+
+
+def core_inputs_block(wid: int, j: int, seed: int = 0, A: np.ndarray | None = None, need_q: bool = True,
+                      threads: int | None = None):
+    """Inputs for token block j of workload wid: dict of float32 arrays shaped [B, block, H, *].
+    Heads are drawn on up to `threads` threads (each head has its own stream)."""
+    w = WORKLOADS[wid]
+    if A is None:
+        A, _ = head_params(wid, seed)
+    TB = min(w.block, w.T)
+    out = {"k": np.empty((w.B, TB, w.H, w.Dk), np.float32), "v": np.empty((w.B, TB, w.H, w.Dv), np.float32),
+           "g": np.empty((w.B, TB, w.H, w.Dk), np.float32), "beta": np.empty((w.B, TB, w.H), np.float32)}
+    if need_q:
+        out["q"] = np.empty((w.B, TB, w.H, w.Dk), np.float32)
+
+    def fill(h):
+        for name, arr in _unit(wid, j, h, seed, float(A[h]), need_q).items():
+            out[name][:, :, h] = arr
+
+    with _pool(threads) as ex:
+        list(ex.map(fill, range(w.H)))
     return out
 
 
 def core_inputs(wid: int, seed: int = 0, T: int | None = None, threads: int | None = None):
-    """All inputs of workload wid (optionally only its first T tokens, T a multiple of the block or < block).
+    """All inputs of workload wid (optionally only its first T tokens).
 
     Returns dict(q, k, v, g, beta: float32 [B,T,H,*]; S0: float32 [B,H,Dk,Dv] or None; A: float64 [H]).
     """
@@ -138,15 +169,14 @@ def core_inputs(wid: int, seed: int = 0, T: int | None = None, threads: int | No
         "beta": np.empty((w.B, T, w.H), np.float32),
     }
 
-    def fill(j):
-        blk = core_inputs_block(wid, j, seed, A)
+    def fill(jh):
+        j, h = divmod(jh, w.H)
         t0, t1 = j * TB, min(T, (j + 1) * TB)
-        for name, arr in blk.items():
-            out[name][:, t0:t1] = arr[:, : t1 - t0]
+        for name, arr in _unit(wid, j, h, seed, float(A[h]), True).items():
+            out[name][:, t0:t1, h] = arr[:, : t1 - t0]
 
-    threads = threads or min(16, os.cpu_count() or 1)
-    with _cf.ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(fill, range(nblk)))
+    with _pool(threads) as ex:
+        list(ex.map(fill, range(nblk * w.H)))
     out["S0"] = S0
     out["A"] = A
     return out
