@@ -53,11 +53,19 @@ constexpr int DV = 128;
 constexpr int DVH = 64;     // value columns per workgroup
 constexpr int NTHR = 512;   // 8 waves: 4 key waves + 4 value waves
 constexpr int LDK = DK + 8; // padded row (16-bit elements) of token-major [C][DK] tiles
-constexpr int LDT = C + 8;  // padded row of channel-major [DV][C] tiles
-constexpr int LDT8 = C + 4; // padded row of channel-major tiles read 8 bytes at a time
+constexpr int LDT = C + 8;  // padded row of channel-major [D][C] tiles
 constexpr int LDA = C + 8;  // [C][C] 16-bit tiles
-constexpr int LDA8 = C + 4; // [C][C] 16-bit tiles read 8 bytes at a time
 constexpr int LDF = C + 4;  // [C][C] float tiles
+
+// Matrix-core operand order.  A 16x16x32 product takes, in lane group g (lanes 16g..16g+15), the
+// eight contraction indices 8g..8g+7.  Accumulator registers hold rows 4g..4g+3 of a 16-row block,
+// so to feed accumulators back in as operands the contraction index j of a 32-long sum is mapped to
+// {4g + r} (j < 16) and {16 + 4g + r} (j >= 16).  Tiles read as operands store their contraction
+// index permuted, position 8g + 4h + r for j = 16h + 4g + r, so that each lane's eight elements are
+// contiguous and one 16-byte LDS read fetches them.
+__device__ __forceinline__ constexpr int tperm(int j) { return ((j >> 2) & 3) * 8 + (j >> 4) * 4 + (j & 3); }
+// the same within each 32-channel block of a 128-channel row
+__device__ __forceinline__ constexpr int cperm(int c) { return (c & ~31) + tperm(c & 31); }
 
 struct alignas(16) KeyTiles {                // written and read by the key waves within one step
     uint16_t qmh[C][LDK], qml[C][LDK];       // Q * exp(b - b_ref)      split bf16
@@ -67,19 +75,20 @@ struct alignas(16) KeyTiles {                // written and read by the key wave
     float tot[4][DK];                        // per 8-token octet sums of g
 };
 struct alignas(16) Handoff2 {                // key -> value, double buffered by chunk parity
-    uint16_t qg[C][LDK];                     // Q * Gamma                 f16
-    uint16_t kgn[C][LDK];                    // -(K * Gamma)              f16
-    uint16_t kbh[DK][LDT8], kbl[DK][LDT8];   // (K * exp(b_last - b))^T   split bf16 (HP), else f16 in kbh
-    uint16_t ah[C][LDA8], al[C][LDA8];       // A                         split bf16
+    uint16_t qg[C][LDK];                     // Q * Gamma                 f16, channels cperm'd
+    uint16_t kgn[C][LDK];                    // -(K * Gamma)              f16, channels cperm'd
+    uint16_t kbh[DK][LDT], kbl[DK][LDT];     // (K * exp(b_last - b))^T   split bf16 (HP), else f16 in kbh;
+                                             //                           tokens tperm'd
+    uint16_t ah[C][LDA], al[C][LDA];         // A                         split bf16, columns tperm'd
     float gamc[DK];                          // Gamma of the chunk's last token
 };
 struct alignas(16) Handoff1 {                // key -> value, one buffer (written after the reader is done)
     float lf[C][LDF];                        // L (strictly lower within the diagonal blocks)
-    uint16_t vt[DVH][LDT];                   // V^T (this value half)     bf16
+    uint16_t vt[DVH][LDT];                   // V^T (this value half)     bf16, tokens tperm'd
     float beta[C];
 };
 struct alignas(16) ValueTiles {              // value waves only
-    uint16_t th[C][LDA], tl[C][LDA];         // T split bf16
+    uint16_t th[C][LDA], tl[C][LDA];         // T split bf16, columns tperm'd
     float xf[C][LDF];                        // diagonal blocks of (I + Diag(beta) L)^{-1}
 };
 struct alignas(16) Smem {
@@ -90,12 +99,6 @@ struct alignas(16) Smem {
 };
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-// Two 8-byte pieces: elements [p0, p0+4) and [p1, p1+4).
-__device__ __forceinline__ u32x4 ld8x2(const uint16_t* p0, const uint16_t* p1) {
-    u32x2 a = *reinterpret_cast<const u32x2*>(p0);
-    u32x2 b = *reinterpret_cast<const u32x2*>(p1);
-    return u32x4{a.x, a.y, b.x, b.y};
-}
 // Low 16-bit halves of a and b as one word (a's in the low half); likewise the high halves.
 __device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
@@ -267,24 +270,27 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         const float eC0 = fexp(bC0 - p0), eC1 = fexp(bC1 - p1);
         uint32_t kb[8], kl8[8];
         const float nP0 = -eP0, nP1 = -eP1;
+        const int pc0 = cperm(c0);  // c0 even: c0 + 1 follows it
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int t = 8 * kw + i;
-            *reinterpret_cast<uint32_t*>(&H.qg[t][c0]) = pack_f16(qm0[i] * eP0, qm1[i] * eP1);
-            *reinterpret_cast<uint32_t*>(&H.kgn[t][c0]) = pack_f16(km0[i] * nP0, km1[i] * nP1);
+            *reinterpret_cast<uint32_t*>(&H.qg[t][pc0]) = pack_f16(qm0[i] * eP0, qm1[i] * eP1);
+            *reinterpret_cast<uint32_t*>(&H.kgn[t][pc0]) = pack_f16(km0[i] * nP0, km1[i] * nP1);
             if constexpr (HP)
                 split_bf16(kh0[i] * eC0, kh1[i] * eC1, kb[i], kl8[i]);
             else
                 kb[i] = pack_f16(kh0[i] * eC0, kh1[i] * eC1);
         }
-        // token pairs of channel c0 (low halves) and of channel c0 + 1 (high halves)
-        auto put_t = [&](uint16_t (*dst)[LDT8], const uint32_t* w) {
+        // token pairs of channel c0 (low halves) and of channel c0 + 1 (high halves); tokens
+        // 8kw..8kw+3 and 8kw+4..8kw+7 are each contiguous after tperm
+        auto put_t = [&](uint16_t (*dst)[LDT], const uint32_t* w) {
             const u32x4 b0 = {perm_lo(w[0], w[1]), perm_lo(w[2], w[3]), perm_lo(w[4], w[5]), perm_lo(w[6], w[7])};
             const u32x4 b1 = {perm_hi(w[0], w[1]), perm_hi(w[2], w[3]), perm_hi(w[4], w[5]), perm_hi(w[6], w[7])};
-            *reinterpret_cast<u32x2*>(&dst[c0][8 * kw]) = u32x2{b0.x, b0.y};
-            *reinterpret_cast<u32x2*>(&dst[c0][8 * kw + 4]) = u32x2{b0.z, b0.w};
-            *reinterpret_cast<u32x2*>(&dst[c0 + 1][8 * kw]) = u32x2{b1.x, b1.y};
-            *reinterpret_cast<u32x2*>(&dst[c0 + 1][8 * kw + 4]) = u32x2{b1.z, b1.w};
+            const int pa = tperm(8 * kw), pb = tperm(8 * kw + 4);
+            *reinterpret_cast<u32x2*>(&dst[c0][pa]) = u32x2{b0.x, b0.y};
+            *reinterpret_cast<u32x2*>(&dst[c0][pb]) = u32x2{b0.z, b0.w};
+            *reinterpret_cast<u32x2*>(&dst[c0 + 1][pa]) = u32x2{b1.x, b1.y};
+            *reinterpret_cast<u32x2*>(&dst[c0 + 1][pb]) = u32x2{b1.z, b1.w};
         };
         put_t(H.kbh, kb);
         if constexpr (HP) put_t(H.kbl, kl8);
@@ -329,8 +335,8 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
                 float v = (a0[r] + a1[r]) + a2[r];
                 if (R == S && l16 > i) v = 0.f;  // lower triangle including the diagonal
                 const uint32_t hi = pack_bf16(v, 0.f);
-                H.ah[SUB * R + i][SUB * S + l16] = hi & 0xffffu;
-                H.al[SUB * R + i][SUB * S + l16] = pack_bf16(v - bf16lo_to_f(hi), 0.f) & 0xffffu;
+                H.ah[SUB * R + i][tperm(SUB * S + l16)] = hi & 0xffffu;
+                H.al[SUB * R + i][tperm(SUB * S + l16)] = pack_bf16(v - bf16lo_to_f(hi), 0.f) & 0xffffu;
             }
         } else {
             // L(0,0), L(1,0), L(1,1): bf16 Km against K/Gamma (split bf16 when HP, else its high part)
@@ -353,18 +359,22 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
             for (int r = 0; r < 4; ++r) {
                 const int i = 4 * g4 + r;
                 sm.h1.lf[i][l16] = (l16 >= i) ? 0.f : acc0[r];  // strictly lower
-                sm.h1.lf[SUB + i][l16] = acc1[r];
                 sm.h1.lf[SUB + i][SUB + l16] = (l16 >= i) ? 0.f : acc2[r];
+                // L(1,0) as a split-bf16 operand, in the block of the T tile that T itself leaves unused
+                const uint32_t hi = pack_bf16(acc1[r], 0.f);
+                sm.val.th[SUB + i][tperm(l16)] = hi & 0xffffu;
+                sm.val.tl[SUB + i][tperm(l16)] = pack_bf16(acc1[r] - bf16lo_to_f(hi), 0.f) & 0xffffu;
             }
         }
         // V^T and beta of this chunk (the value waves are done with the previous ones)
         if constexpr (!IN_F32) {
             if (lane < 32) {  // V^T for value columns 2*lane, 2*lane+1 of this half
                 const uint32_t* v = cur.v;
-                *reinterpret_cast<u32x4*>(&sm.h1.vt[2 * lane][8 * kw]) =
-                    u32x4{perm_lo(v[0], v[1]), perm_lo(v[2], v[3]), perm_lo(v[4], v[5]), perm_lo(v[6], v[7])};
-                *reinterpret_cast<u32x4*>(&sm.h1.vt[2 * lane + 1][8 * kw]) =
-                    u32x4{perm_hi(v[0], v[1]), perm_hi(v[2], v[3]), perm_hi(v[4], v[5]), perm_hi(v[6], v[7])};
+                const int pa = tperm(8 * kw), pb = tperm(8 * kw + 4);
+                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane][pa]) = u32x2{perm_lo(v[0], v[1]), perm_lo(v[2], v[3])};
+                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane][pb]) = u32x2{perm_lo(v[4], v[5]), perm_lo(v[6], v[7])};
+                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane + 1][pa]) = u32x2{perm_hi(v[0], v[1]), perm_hi(v[2], v[3])};
+                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane + 1][pb]) = u32x2{perm_hi(v[4], v[5]), perm_hi(v[6], v[7])};
             }
         }
         if (lane < 8) sm.h1.beta[8 * kw + lane] = cur.beta;
@@ -377,7 +387,7 @@ __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int half, int 
     // A's block (0,1) is zero in both buffers; no chunk writes it
     for (int e = 64 * kw + lane; e < 2 * SUB * SUB; e += 256) {
         Handoff2& Hz = sm.h2[e >> 8];
-        const int r = (e >> 4) & 15, c = SUB + (e & 15);
+        const int r = (e >> 4) & 15, c = tperm(SUB + (e & 15));
         Hz.ah[r][c] = 0; Hz.al[r][c] = 0;
     }
     KeyLoad kl;
@@ -408,13 +418,6 @@ template <bool OUT_F32, bool IN_F32, bool HP>
 __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int half, int vw, int lane, int nchunk) {
     const int l16 = lane & 15, g4 = lane >> 4;
     ValueTiles& V = sm.val;
-    // T's block (0,1) is zero; nothing else writes it
-    if (vw == 0) {
-        for (int e = lane; e < SUB * SUB; e += 64) {
-            const int r = e >> 4, c = SUB + (e & 15);
-            V.th[r][c] = 0; V.tl[r][c] = 0;
-        }
-    }
 
     // state: st[cb][r] = S[16*cb + 4*g4 + r][col]
     const int col = half * DVH + 16 * vw + l16;
@@ -511,33 +514,11 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
                 split_bf16(ta[2], ta[3], h1, q1);
                 split_bf16(tb[0], tb[1], h2, q2);
                 split_bf16(tb[2], tb[3], h3, q3);
-                *reinterpret_cast<u32x4*>(&V.th[o + i][o + j0]) = u32x4{h0, h1, h2, h3};
-                *reinterpret_cast<u32x4*>(&V.tl[o + i][o + j0]) = u32x4{q0, q1, q2, q3};
-            }
-            // off-diagonal block: Y = Diag(beta_1) L_10 X_00, X_10 = -X_11 Y on float32 matrix cores;
-            // the K index of step s in lane group g4 is 4*g4 + s
-            f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int k = 4 * g4 + s;
-                const float a = beta[SUB + l16] * sm.h1.lf[SUB + l16][k];
-                const float b = V.xf[k][l16];
-                y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, y, 0, 0, 0);
-            }
-            f32x4 x10 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const float a = V.xf[SUB + l16][SUB + 4 * g4 + s];
-                x10 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, y[s], x10, 0, 0, 0);
-            }
-            const float bj = beta[l16];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float tv = -x10[r] * bj;
-                const int i = SUB + 4 * g4 + r;
-                const uint32_t hi = pack_bf16(tv, 0.f);
-                V.th[i][l16] = hi & 0xffffu;
-                V.tl[i][l16] = pack_bf16(tv - bf16lo_to_f(hi), 0.f) & 0xffffu;
+                const int pa = tperm(o + j0), pb = tperm(o + j0 + 4);
+                *reinterpret_cast<u32x2*>(&V.th[o + i][pa]) = u32x2{h0, h1};
+                *reinterpret_cast<u32x2*>(&V.th[o + i][pb]) = u32x2{h2, h3};
+                *reinterpret_cast<u32x2*>(&V.tl[o + i][pa]) = u32x2{q0, q1};
+                *reinterpret_cast<u32x2*>(&V.tl[o + i][pb]) = u32x2{q2, q3};
             }
         }
         lds_barrier();  // ---- barrier 1
@@ -553,49 +534,53 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
                 xr[1] = vnext[1];
                 if (n < nchunk) load_v(n * C);  // V of the chunk handled next step
             } else {
-#pragma unroll
-                for (int R = 0; R < 2; ++R) {
-                    const u32x2 vv = *reinterpret_cast<const u32x2*>(&sm.h1.vt[16 * vw + l16][SUB * R + 4 * g4]);
-                    xr[R] = f32x4{bf16lo_to_f(vv.x), bf16hi_to_f(vv.x), bf16lo_to_f(vv.y), bf16hi_to_f(vv.y)};
-                }
+                const u32x4 vv = ld16(&sm.h1.vt[16 * vw + l16][8 * g4]);  // tokens 4g4+r, then 16+4g4+r
+                xr[0] = f32x4{bf16lo_to_f(vv.x), bf16hi_to_f(vv.x), bf16lo_to_f(vv.y), bf16hi_to_f(vv.y)};
+                xr[1] = f32x4{bf16lo_to_f(vv.z), bf16hi_to_f(vv.z), bf16lo_to_f(vv.w), bf16hi_to_f(vv.w)};
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const int cbase = 32 * m + 4 * g4;
 #pragma unroll
                 for (int R = 0; R < 2; ++R)
-                    xr[R] = mfma_f16(ld8x2(&H.kgn[SUB * R + l16][cbase], &H.kgn[SUB * R + l16][cbase + 16]), sb[m],
-                                     xr[R]);
+                    xr[R] = mfma_f16(ld16(&H.kgn[SUB * R + l16][32 * m + 8 * g4]), sb[m], xr[R]);
             }
             // (Q*Gamma) S as O^T: lane (token l16, group g4) gets value columns 4*g4..4*g4+3
 #pragma unroll
             for (int R = 0; R < 2; ++R) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int cbase = 32 * m + 4 * g4;
-                    acc = mfma_f16(sb[m], ld8x2(&H.qg[SUB * R + l16][cbase], &H.qg[SUB * R + l16][cbase + 16]), acc);
-                }
+                for (int m = 0; m < 4; ++m) acc = mfma_f16(sb[m], ld16(&H.qg[SUB * R + l16][32 * m + 8 * g4]), acc);
                 oacc[R] = acc;
             }
-            // X as operands over the chunk's tokens, order {4*g4 + r} then {16 + 4*g4 + r}; split bf16
-            uint32_t xh0, xh1, xh2, xh3, xl0, xl1, xl2, xl3;
-            split_bf16(xr[0][0], xr[0][1], xh0, xl0);
-            split_bf16(xr[0][2], xr[0][3], xh1, xl1);
-            split_bf16(xr[1][0], xr[1][1], xh2, xl2);
-            split_bf16(xr[1][2], xr[1][3], xh3, xl3);
-            const u32x4 xh = {xh0, xh1, xh2, xh3}, xl = {xl0, xl1, xl2, xl3};
-            f32x4 u[2];
-#pragma unroll
-            for (int R = 0; R < 2; ++R) {
-                const u32x4 tH = ld8x2(&V.th[SUB * R + l16][4 * g4], &V.th[SUB * R + l16][SUB + 4 * g4]);
-                const u32x4 tL = ld8x2(&V.tl[SUB * R + l16][4 * g4], &V.tl[SUB * R + l16][SUB + 4 * g4]);
+            // U by block forward substitution over the two sub-tiles (T is block lower triangular):
+            //   U0 = T00 X0,   U1 = T11 (X1 - L10 U0),
+            // as split-bf16 16x16x16 products whose contraction index is token 4*g4 + r of a sub-tile
+            auto split4 = [](const f32x4 x, u32x2& h, u32x2& l) {
+                uint32_t h0, h1, l0, l1;
+                split_bf16(x[0], x[1], h0, l0);
+                split_bf16(x[2], x[3], h1, l1);
+                h = u32x2{h0, h1};
+                l = u32x2{l0, l1};
+            };
+            auto prod3 = [](u32x2 aH, u32x2 aL, u32x2 bH, u32x2 bL) {
                 f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
-                a0 = mfma_bf16(tH, xh, a0);
-                a1 = mfma_bf16(tH, xl, a1);
-                a2 = mfma_bf16(tL, xh, a2);
-                u[R] = (a0 + a1) + a2;
-            }
+                a0 = mfma_bf16_k16(aH, bH, a0);
+                a1 = mfma_bf16_k16(aH, bL, a1);
+                a2 = mfma_bf16_k16(aL, bH, a2);
+                return (a0 + a1) + a2;
+            };
+            auto ld8 = [](const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); };
+            f32x4 u[2];
+            u32x2 bh, bl;
+            split4(xr[0], bh, bl);
+            u[0] = prod3(ld8(&V.th[l16][8 * g4]), ld8(&V.tl[l16][8 * g4]), bh, bl);
+            split4(u[0], bh, bl);
+            const f32x4 lu = prod3(ld8(&V.th[SUB + l16][8 * g4]), ld8(&V.tl[SUB + l16][8 * g4]), bh, bl);
+            split4(xr[1] - lu, bh, bl);
+            u[1] = prod3(ld8(&V.th[SUB + l16][8 * g4 + 4]), ld8(&V.tl[SUB + l16][8 * g4 + 4]), bh, bl);
+            if constexpr (!HP)
+                uf = u32x4{pack_f16(u[0][0], u[0][1]), pack_f16(u[0][2], u[0][3]), pack_f16(u[1][0], u[1][1]),
+                           pack_f16(u[1][2], u[1][3])};
             uint32_t uh0, uh1, uh2, uh3, ul0, ul1, ul2, ul3;
             split_bf16(u[0][0], u[0][1], uh0, ul0);
             split_bf16(u[0][2], u[0][3], uh1, ul1);
@@ -603,9 +588,6 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
             split_bf16(u[1][2], u[1][3], uh3, ul3);
             uh = u32x4{uh0, uh1, uh2, uh3};
             ul = u32x4{ul0, ul1, ul2, ul3};
-            if constexpr (!HP)
-                uf = u32x4{pack_f16(u[0][0], u[0][1]), pack_f16(u[0][2], u[0][3]), pack_f16(u[1][0], u[1][1]),
-                           pack_f16(u[1][2], u[1][3])};
         }
         lds_barrier();  // ---- barrier 2
 
@@ -614,8 +596,8 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
             gchar* ob = (gchar*)uniform_gptr((const char*)p.o + ((row0 + (size_t)t0 * p.H) * DV) * (OUT_F32 ? 4 : 2));
 #pragma unroll
             for (int R = 0; R < 2; ++R) {
-                const u32x4 aH = ld8x2(&H.ah[SUB * R + l16][4 * g4], &H.ah[SUB * R + l16][SUB + 4 * g4]);
-                const u32x4 aL = ld8x2(&H.al[SUB * R + l16][4 * g4], &H.al[SUB * R + l16][SUB + 4 * g4]);
+                const u32x4 aH = ld16(&H.ah[SUB * R + l16][8 * g4]);
+                const u32x4 aL = ld16(&H.al[SUB * R + l16][8 * g4]);
                 f32x4 ax = {0.f, 0.f, 0.f, 0.f}, ay = ax, acc = oacc[R];
                 ax = mfma_bf16(uh, aH, ax);
                 ay = mfma_bf16(ul, aH, ay);
@@ -631,9 +613,9 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) {
                 const f32x4 gm = *reinterpret_cast<const f32x4*>(&H.gamc[16 * cb + 4 * g4]);
-                const u32x4 aH = ld8x2(&H.kbh[16 * cb + l16][4 * g4], &H.kbh[16 * cb + l16][SUB + 4 * g4]);
+                const u32x4 aH = ld16(&H.kbh[16 * cb + l16][8 * g4]);
                 if constexpr (HP) {
-                    const u32x4 aL = ld8x2(&H.kbl[16 * cb + l16][4 * g4], &H.kbl[16 * cb + l16][SUB + 4 * g4]);
+                    const u32x4 aL = ld16(&H.kbl[16 * cb + l16][8 * g4]);
                     f32x4 acc = mfma_bf16(aH, uh, st[cb] * gm);
                     acc = mfma_bf16(aH, ul, acc);
                     st[cb] = mfma_bf16(aL, uh, acc);
