@@ -87,9 +87,8 @@ struct alignas(16) Handoff1 {                // key -> value, one buffer (writte
     uint16_t vt[DVH][LDT];                   // V^T (this value half)     bf16, tokens tperm'd
     float beta[C];
 };
-struct alignas(16) ValueTiles {              // value waves only
-    uint16_t th[C][LDA], tl[C][LDA];         // T split bf16, columns tperm'd
-    float xf[C][LDF];                        // diagonal blocks of (I + Diag(beta) L)^{-1}
+struct alignas(16) ValueTiles {              // value waves only (the key waves write L(1,0) here)
+    uint16_t th[C][LDA], tl[C][LDA];         // T split bf16, columns tperm'd; block (1,0) holds L(1,0)
 };
 struct alignas(16) Smem {
     KeyTiles key;
@@ -99,6 +98,11 @@ struct alignas(16) Smem {
 };
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Lane M of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int M>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + M, 0xf, 0xf, false));
+}
 // Low 16-bit halves of a and b as one word (a's in the low half); likewise the high halves.
 __device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
@@ -465,61 +469,43 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
         const bool work = n >= 1;  // this step handles chunk n-1
         const int t0 = (n - 1) * C;
         const Handoff2& H = sm.h2[(n - 1) & 1];
-        // ---------------- part 1: UT inverse (one wave)
-        if (work && vw == 0) {
+        // ---------------- part 1: UT inverse of the two diagonal blocks, spread over the value waves
+        // Wave vw solves columns j = 8*(vw & 1) + g4 and j + 4 of block vw >> 1 of (I + Diag(beta) L) X = I;
+        // lane l16 of a 16-lane row holds matrix row i = l16.  Forward substitution: at step m every lane
+        // forms its candidate x_i = [i == j] - beta_i acc_i, row m's (final) candidate is broadcast along
+        // the 16-lane row, and rows below take acc_i += L[i][m] x_m (L is zero on and above the diagonal).
+        if (work) {
             const float* beta = sm.h1.beta;
-            // diagonal blocks by right-looking forward substitution in registers:
-            // lanes 0-15 column j of block 0, lanes 16-31 column j of block 1
-            if (lane < 32) {
-                const int o = SUB * (lane >> 4);
-                int j = l16;
-                asm volatile("" : "+v"(j));  // keep the unit-vector selects inside the chunk loop
-                float Lr[SUB][SUB];
+            const int o = SUB * (vw >> 1), i = l16, ja = 8 * (vw & 1) + g4, jb = ja + 4;
+            float Lr[SUB];
 #pragma unroll
-                for (int i = 1; i < SUB; ++i) {
-#pragma unroll
-                    for (int q4 = 0; q4 <= (i - 1) / 4; ++q4) {
-                        const f32x4 t = *reinterpret_cast<const f32x4*>(&sm.h1.lf[o + i][o + 4 * q4]);
-                        Lr[i][4 * q4] = t[0]; Lr[i][4 * q4 + 1] = t[1]; Lr[i][4 * q4 + 2] = t[2]; Lr[i][4 * q4 + 3] = t[3];
-                    }
-                }
-                float bt[SUB];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const f32x4 t = *reinterpret_cast<const f32x4*>(&beta[o + 4 * q4]);
-                    bt[4 * q4] = t[0]; bt[4 * q4 + 1] = t[1]; bt[4 * q4 + 2] = t[2]; bt[4 * q4 + 3] = t[3];
-                }
-                float x[SUB], acc[SUB];
-#pragma unroll
-                for (int i = 0; i < SUB; ++i) acc[i] = 0.f;
-#pragma unroll
-                for (int m = 0; m < SUB; ++m) {
-                    x[m] = (m == j ? 1.f : 0.f) - bt[m] * acc[m];
-#pragma unroll
-                    for (int i = m + 1; i < SUB; ++i) acc[i] = __builtin_fmaf(Lr[i][m], x[m], acc[i]);
-                }
-#pragma unroll
-                for (int i = 0; i < SUB; ++i) V.xf[o + i][o + j] = x[i];
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 t = *reinterpret_cast<const f32x4*>(&sm.h1.lf[o + i][o + 4 * q4]);
+                Lr[4 * q4] = t[0]; Lr[4 * q4 + 1] = t[1]; Lr[4 * q4 + 2] = t[2]; Lr[4 * q4 + 3] = t[3];
             }
-            // T = X Diag(beta) on the diagonal blocks, 8 entries per lane
-            {
-                const int o = SUB * (lane >> 5), i = (lane >> 1) & 15, j0 = 8 * (lane & 1);
-                const f32x4 xa = *reinterpret_cast<const f32x4*>(&V.xf[o + i][o + j0]);
-                const f32x4 xb = *reinterpret_cast<const f32x4*>(&V.xf[o + i][o + j0 + 4]);
-                const f32x4 ba = *reinterpret_cast<const f32x4*>(&beta[o + j0]);
-                const f32x4 bb = *reinterpret_cast<const f32x4*>(&beta[o + j0 + 4]);
-                const f32x4 ta = xa * ba, tb = xb * bb;
-                uint32_t h0, h1, h2, h3, q0, q1, q2, q3;
-                split_bf16(ta[0], ta[1], h0, q0);
-                split_bf16(ta[2], ta[3], h1, q1);
-                split_bf16(tb[0], tb[1], h2, q2);
-                split_bf16(tb[2], tb[3], h3, q3);
-                const int pa = tperm(o + j0), pb = tperm(o + j0 + 4);
-                *reinterpret_cast<u32x2*>(&V.th[o + i][pa]) = u32x2{h0, h1};
-                *reinterpret_cast<u32x2*>(&V.th[o + i][pb]) = u32x2{h2, h3};
-                *reinterpret_cast<u32x2*>(&V.tl[o + i][pa]) = u32x2{q0, q1};
-                *reinterpret_cast<u32x2*>(&V.tl[o + i][pb]) = u32x2{q2, q3};
+            const float nbi = -beta[o + i];
+            const float da = i == ja ? 1.f : 0.f, db = i == jb ? 1.f : 0.f;
+            float aa = 0.f, ab = 0.f;
+#define KDA_SUBST_STEP(m)                                                                        \
+            {                                                                                    \
+                const float xa = row_bcast<m>(__builtin_fmaf(nbi, aa, da));                      \
+                const float xb = row_bcast<m>(__builtin_fmaf(nbi, ab, db));                      \
+                aa = __builtin_fmaf(Lr[m], xa, aa);                                              \
+                ab = __builtin_fmaf(Lr[m], xb, ab);                                              \
             }
+            KDA_SUBST_STEP(0) KDA_SUBST_STEP(1) KDA_SUBST_STEP(2) KDA_SUBST_STEP(3) KDA_SUBST_STEP(4)
+            KDA_SUBST_STEP(5) KDA_SUBST_STEP(6) KDA_SUBST_STEP(7) KDA_SUBST_STEP(8) KDA_SUBST_STEP(9)
+            KDA_SUBST_STEP(10) KDA_SUBST_STEP(11) KDA_SUBST_STEP(12) KDA_SUBST_STEP(13) KDA_SUBST_STEP(14)
+#undef KDA_SUBST_STEP
+            // T = X Diag(beta), as split bf16 in the tperm'd columns of T's tile
+            const float ta = __builtin_fmaf(nbi, aa, da) * beta[o + ja];
+            const float tb = __builtin_fmaf(nbi, ab, db) * beta[o + jb];
+            uint32_t hi, lo;
+            split_bf16(ta, tb, hi, lo);
+            V.th[o + i][tperm(o + ja)] = hi & 0xffffu;
+            V.th[o + i][tperm(o + jb)] = hi >> 16;
+            V.tl[o + i][tperm(o + ja)] = lo & 0xffffu;
+            V.tl[o + i][tperm(o + jb)] = lo >> 16;
         }
         lds_barrier();  // ---- barrier 1
 
