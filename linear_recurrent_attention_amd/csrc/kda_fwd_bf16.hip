@@ -10,19 +10,19 @@
 //   U = T (V - (K*Gamma) S),
 //   O = (Q*Gamma) S + A U,
 //   S <- Diag(Gamma_last) S + (K*exp(b_last - b))^T U.
-// The 1/Gamma factors are formed only inside 16-token sub-tiles, relative to the cumulative decay
-// at the sub-tile's token 7, so every factor lies in [e^-40, e^40] (sections 3.1-3.2: the lower
-// bound g >= -5 is what keeps these in range).  The block of L and A that couples the two
-// sub-tiles uses the earlier sub-tile's K/Gamma moved to the later sub-tile's reference.
+// The factors exp(+-(b - b_15)) are taken relative to the cumulative decay at the chunk's token 15,
+// so with the lower bound g >= -5 of sections 3.1-3.2 each lies in [e^-80, e^80], inside the
+// normal range of float32 and bf16; the products that enter L and A (t >= s) are at most 1.  The
+// 32x32 products are formed as 16x16 blocks (two 16-token sub-tiles).
 //
 // Mapping.  One workgroup per (batch, head, value half): the 128 value columns are split over two
 // workgroups that both compute the key-side products, so 2*B*H workgroups fill the chip; the two
 // halves of a head are placed on the same XCD so their common reads of q, k, g share its L2.
 // Each workgroup runs 8 waves as a two-stage pipeline over chunks:
-//   key waves 0-3   chunk n:   element-wise decay factors, then the Gram products L and A;
-//   value waves 4-7 chunk n-1: UT inverse (wave 4), then the state-dependent products and the
-//                              output; wave 4+w owns 16 value columns of the float32 state in
-//                              matrix-core accumulator layout for the whole run.
+//   key waves 0-3   chunk n:   octet decay sums, then all decay factors, then the Gram products;
+//   value waves 4-7 chunk n-1: UT inverse, then the state-dependent products and the output;
+//                              wave 4+w owns 16 value columns of the float32 state in matrix-core
+//                              accumulator layout for the whole run.
 // Both groups execute the same three workgroup barriers per step; data passes from the key waves
 // to the value waves through LDS buffers indexed by chunk parity.  Chunk inputs are prefetched
 // one chunk ahead into registers.
@@ -31,13 +31,13 @@
 //   L = Km Kh^T                      bf16                  HP: bf16 Km, split bf16 Kh
 //   A = Qm Kh^T                      split bf16 (hi*hi + hi*lo + lo*hi)
 //   X = V - Kg S,  Q S               f16
-//   U = T X                          split bf16
+//   U = T X                          split bf16 (by blocks: U0 = T00 X0, U1 = T11 (X1 - L10 U0))
 //   A U                              split bf16
 //   Kbar^T U                         f16                   HP: split bf16
 // HP is the variant for correlated keys (the layer's Swish-activated ones): the rounding of L and
 // of Kbar^T U grows with the conditioning of I + Diag(beta) L, and HP takes both to split bf16.
 // The inverse solves the two 16x16 diagonal blocks of (I + Diag(beta) L) by forward substitution
-// in float32 registers and forms the off-diagonal block with float32 matrix-core products.
+// in float32, one matrix row per lane, spread over the four value waves.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -51,7 +51,9 @@ constexpr int SUB = 16;     // tokens per sub-tile
 constexpr int DK = 128;
 constexpr int DV = 128;
 constexpr int DVH = 64;     // value columns per workgroup
-constexpr int NTHR = 512;   // 8 waves: 4 key waves + 4 value waves
+constexpr int NKW = 8;      // key waves, one 4-token quad of the chunk each
+constexpr int TPW = C / NKW; // tokens per key wave
+constexpr int NTHR = 64 * (NKW + 4);  // and 4 value waves, 16 value columns each
 constexpr int LDK = DK + 8; // padded row (16-bit elements) of token-major [C][DK] tiles
 constexpr int LDT = C + 8;  // padded row of channel-major [D][C] tiles
 constexpr int LDA = C + 8;  // [C][C] 16-bit tiles
@@ -68,11 +70,10 @@ __device__ __forceinline__ constexpr int tperm(int j) { return ((j >> 2) & 3) * 
 __device__ __forceinline__ constexpr int cperm(int c) { return (c & ~31) + tperm(c & 31); }
 
 struct alignas(16) KeyTiles {                // written and read by the key waves within one step
-    uint16_t qmh[C][LDK], qml[C][LDK];       // Q * exp(b - b_ref)      split bf16
-    uint16_t km[C][LDK];                     // K * exp(b - b_ref)      bf16
-    uint16_t khh[C][LDK], khl[C][LDK];       // K * exp(b_ref - b)      split bf16
-    uint16_t k1h[SUB][LDK], k1l[SUB][LDK];   // sub-tile 0 rows of K/Gamma at sub-tile 1's reference
-    float tot[4][DK];                        // per 8-token octet sums of g
+    uint16_t qmh[C][LDK], qml[C][LDK];       // Q * exp(b - b_15)       split bf16
+    uint16_t km[C][LDK];                     // K * exp(b - b_15)       bf16
+    uint16_t khh[C][LDK], khl[C][LDK];       // K * exp(b_15 - b)       split bf16
+    float tot[NKW][DK];                      // per-quad sums of g (log decay)
 };
 struct alignas(16) Handoff2 {                // key -> value, double buffered by chunk parity
     uint16_t qg[C][LDK];                     // Q * Gamma                 f16, channels cperm'd
@@ -113,14 +114,14 @@ template <bool IN_F32>
 struct Raw;
 template <>
 struct Raw<false> {
-    uint32_t q[8], k[8], v[8];
-    f32x2 g[8];
+    uint32_t q[TPW], k[TPW], v[TPW];
+    f32x2 g[TPW];
     float beta;
 };
 template <>
 struct Raw<true> {
-    f32x2 q[8], k[8];
-    f32x2 g[8];
+    f32x2 q[TPW], k[TPW];
+    f32x2 g[TPW];
     float beta;
 };
 __device__ __forceinline__ f32x2 unpack_q(uint32_t w) { return f32x2{bf16lo_to_f(w), bf16hi_to_f(w)}; }
@@ -128,9 +129,9 @@ __device__ __forceinline__ f32x2 unpack_q(f32x2 w) { return w; }
 
 // Per-thread constants of the key waves' chunk loads (byte offsets within a chunk).
 struct KeyLoad {
-    uint32_t off[8];   // token 8*kw + i, key channels 2*lane, 2*lane+1 of q/k (g: twice this)
-    uint32_t voff[8];  // token 8*kw + i, value columns half*64 + 2*(lane & 31) (+1)
-    uint32_t boff;     // beta of token 8*kw + (lane & 7)
+    uint32_t off[TPW];   // token TPW*kw + i, key channels 2*lane, 2*lane+1 of q/k (g: twice this)
+    uint32_t voff[TPW];  // token TPW*kw + i, value columns half*64 + 2*(lane & 31) (+1)
+    uint32_t boff;       // beta of token TPW*kw + (lane % TPW)
     uint32_t lane_b, vlane_b, tok_b;  // for the clamped tail loads
     int kw, lane;
 };
@@ -153,8 +154,8 @@ __device__ __forceinline__ void gstore(gchar* base, uint32_t off, Tv v) {
     *reinterpret_cast<__attribute__((address_space(1))) Tv*>(base + off) = v;
 }
 
-// Tokens t0 + 8*kw + i: key channels 2*lane, 2*lane+1; value columns half*64 + 2*(lane & 31) (+1);
-// beta of token t0 + 8*kw + (lane & 7).  Tokens past the end read the last valid row; mask_tail()
+// Tokens t0 + TPW*kw + i: key channels 2*lane, 2*lane+1; value columns half*64 + 2*(lane & 31) (+1);
+// beta of token t0 + TPW*kw + (lane % TPW).  Tokens past the end read the last valid row; mask_tail()
 // zeroes them when the chunk is consumed.  Nothing here uses the loaded values, so the loads stay
 // in flight until their first use one step later.  Requires T >= 1 and t0 < T.
 template <bool IN_F32>
@@ -169,7 +170,7 @@ __device__ __forceinline__ void load_chunk(Raw<IN_F32>& r, const Params& p, cons
     using QT = typename std::conditional<IN_F32, f32x2, uint32_t>::type;
     if (t0 + C <= p.T) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < TPW; ++i) {
             r.q[i] = gload<QT>(qc, qs * kl.off[i]);
             r.k[i] = gload<QT>(kc, qs * kl.off[i]);
             r.g[i] = gload<f32x2>(gc, 2 * kl.off[i]);
@@ -179,15 +180,15 @@ __device__ __forceinline__ void load_chunk(Raw<IN_F32>& r, const Params& p, cons
     } else {
         const int lim = p.T - 1 - t0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t tb = (uint32_t)min(8 * kl.kw + i, lim) * kl.tok_b;
+        for (int i = 0; i < TPW; ++i) {
+            const uint32_t tb = (uint32_t)min(TPW * kl.kw + i, lim) * kl.tok_b;
             const uint32_t o = tb + kl.lane_b, ov = tb + kl.vlane_b;  // both non-negative, < 2^31
             r.q[i] = gload<QT>(qc, qs * o);
             r.k[i] = gload<QT>(kc, qs * o);
             r.g[i] = gload<f32x2>(gc, 2 * o);
             if constexpr (!IN_F32) r.v[i] = gload<uint32_t>(vc, ov);
         }
-        r.beta = gload<float>(bc, (uint32_t)min(8 * kl.kw + (kl.lane & 7), lim) * 4u * p.H);
+        r.beta = gload<float>(bc, (uint32_t)min(TPW * kl.kw + (kl.lane % TPW), lim) * 4u * p.H);
     }
 }
 
@@ -195,15 +196,15 @@ __device__ __forceinline__ void load_chunk(Raw<IN_F32>& r, const Params& p, cons
 template <bool IN_F32>
 __device__ __forceinline__ void mask_tail(Raw<IN_F32>& r, int T, int t0, int kw, int lane) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (t0 + 8 * kw + i >= T) {
+    for (int i = 0; i < TPW; ++i) {
+        if (t0 + TPW * kw + i >= T) {
             r.q[i] = {};
             r.k[i] = {};
             if constexpr (!IN_F32) r.v[i] = 0u;
             r.g[i] = f32x2{0.f, 0.f};
         }
     }
-    if (t0 + 8 * kw + (lane & 7) >= T) r.beta = 0.f;
+    if (t0 + TPW * kw + (lane % TPW) >= T) r.beta = 0.f;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -215,101 +216,89 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
     const int kw = kl.kw, lane = kl.lane;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int c0 = 2 * lane;   // key channels c0, c0 + 1
-    const int sig = kw >> 1;   // sub-tile of this thread's octet
-    const int hf = kw & 1;     // first or second octet of the sub-tile
     const bool work = n < nchunk;
     const int t0 = n * C;
     Handoff2& H = sm.h2[n & 1];
 
-    // ---------------- part 1: octet cumulative decay and sub-tile factors
-    float qm0[8], qm1[8], km0[8], km1[8], kh0[8], kh1[8];
+    // ---------------- part 1: decay sums over the quad; prefetch of the next chunk
     if (work) {
         if (t0 + C > p.T) mask_tail(cur, p.T, t0, kw, lane);
-        float s0[8], s1[8];
-        {
-            float a0 = 0.f, a1 = 0.f;
+        float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                a0 += cur.g[i][0]; a1 += cur.g[i][1];
-                s0[i] = a0; s1[i] = a1;
-            }
-        }
-        *reinterpret_cast<float2*>(&sm.key.tot[kw][c0]) = make_float2(s0[7], s1[7]);
-        // reference = cumulative decay at the sub-tile's token 7 (end of its first octet)
-        const float r0 = hf ? 0.f : s0[7] * kLog2e, r1 = hf ? 0.f : s1[7] * kLog2e;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = 8 * kw + i;
-            const float y0 = s0[i] * kLog2e - r0, y1 = s1[i] * kLog2e - r1;
-            const float e0 = __builtin_amdgcn_exp2f(y0), e1 = __builtin_amdgcn_exp2f(y1);
-            const float f0 = __builtin_amdgcn_exp2f(-y0), f1 = __builtin_amdgcn_exp2f(-y1);
-            const f32x2 qq = unpack_q(cur.q[i]), kk = unpack_q(cur.k[i]);
-            const float q0 = qq[0], q1 = qq[1], k0 = kk[0], k1 = kk[1];
-            qm0[i] = q0 * e0; qm1[i] = q1 * e1;
-            km0[i] = k0 * e0; km1[i] = k1 * e1;
-            kh0[i] = k0 * f0; kh1[i] = k1 * f1;
-            uint32_t hi, lo;
-            split_bf16(qm0[i], qm1[i], hi, lo);
-            *reinterpret_cast<uint32_t*>(&sm.key.qmh[t][c0]) = hi;
-            *reinterpret_cast<uint32_t*>(&sm.key.qml[t][c0]) = lo;
-            *reinterpret_cast<uint32_t*>(&sm.key.km[t][c0]) = pack_bf16(km0[i], km1[i]);
-            split_bf16(kh0[i], kh1[i], hi, lo);
-            *reinterpret_cast<uint32_t*>(&sm.key.khh[t][c0]) = hi;
-            *reinterpret_cast<uint32_t*>(&sm.key.khl[t][c0]) = lo;
-        }
+        for (int i = 0; i < TPW; ++i) { a0 += cur.g[i][0]; a1 += cur.g[i][1]; }
+        *reinterpret_cast<float2*>(&sm.key.tot[kw][c0]) = make_float2(a0, a1);
         if (n + 1 < nchunk) load_chunk(nxt, p, kl, row0, t0 + C);  // prefetch the next chunk
     }
     lds_barrier();  // ---- barrier 1
 
-    // ---------------- part 2: factors referenced to the chunk start and chunk end
+    // ---------------- part 2: all decay factors, relative to the cumulative decay at token 15
     if (work) {
-        float tt0[4], tt1[4];
+        float tt0[NKW], tt1[NKW];
 #pragma unroll
-        for (int o = 0; o < 4; ++o) { tt0[o] = sm.key.tot[o][c0]; tt1[o] = sm.key.tot[o][c0 + 1]; }
-        const float pA0 = tt0[0], pA1 = tt1[0];                                      // b at token 7
-        const float pB0 = tt0[0] + tt0[1] + tt0[2], pB1 = tt1[0] + tt1[1] + tt1[2];  // b at token 23
-        const float bC0 = pB0 + tt0[3], bC1 = pB1 + tt1[3];                          // b at token 31
-        const float p0 = sig ? pB0 : pA0, p1 = sig ? pB1 : pA1;
+        for (int o = 0; o < NKW; ++o) {
+            const float2 t = *reinterpret_cast<const float2*>(&sm.key.tot[o][c0]);
+            tt0[o] = t.x; tt1[o] = t.y;
+        }
+        float p0 = 0.f, p1 = 0.f, bC0 = 0.f, bC1 = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+        for (int o = 0; o < NKW; ++o) {
+            if (o < NKW / 2) { p0 += tt0[o]; p1 += tt1[o]; }  // b at token 15
+            bC0 += tt0[o]; bC1 += tt1[o];                    // b at token 31
+            if (o < kw) { o0 += tt0[o]; o1 += tt1[o]; }      // b at the token before this quad
+        }
+        o0 = (o0 - p0) * kLog2e; o1 = (o1 - p1) * kLog2e;
         const float eP0 = fexp(p0), eP1 = fexp(p1);
         const float eC0 = fexp(bC0 - p0), eC1 = fexp(bC1 - p1);
-        uint32_t kb[8], kl8[8];
         const float nP0 = -eP0, nP1 = -eP1;
         const int pc0 = cperm(c0);  // c0 even: c0 + 1 follows it
+        uint32_t kb[TPW], kl8[TPW];
+        uint32_t wqh[TPW], wql[TPW], wkm[TPW], wkh[TPW], wkl[TPW], wqg[TPW], wkg[TPW];
+        float y0 = o0, y1 = o1;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = 8 * kw + i;
-            *reinterpret_cast<uint32_t*>(&H.qg[t][pc0]) = pack_f16(qm0[i] * eP0, qm1[i] * eP1);
-            *reinterpret_cast<uint32_t*>(&H.kgn[t][pc0]) = pack_f16(km0[i] * nP0, km1[i] * nP1);
+        for (int i = 0; i < TPW; ++i) {
+            y0 = __builtin_fmaf(cur.g[i][0], kLog2e, y0);  // (b_t - b_15) log2(e)
+            y1 = __builtin_fmaf(cur.g[i][1], kLog2e, y1);
+            const float e0 = __builtin_amdgcn_exp2f(y0), e1 = __builtin_amdgcn_exp2f(y1);
+            const float f0 = __builtin_amdgcn_exp2f(-y0), f1 = __builtin_amdgcn_exp2f(-y1);
+            const f32x2 qq = unpack_q(cur.q[i]), kk = unpack_q(cur.k[i]);
+            const float qm0 = qq[0] * e0, qm1 = qq[1] * e1;
+            const float km0 = kk[0] * e0, km1 = kk[1] * e1;
+            const float kh0 = kk[0] * f0, kh1 = kk[1] * f1;
+            split_bf16(qm0, qm1, wqh[i], wql[i]);
+            wkm[i] = pack_bf16(km0, km1);
+            split_bf16(kh0, kh1, wkh[i], wkl[i]);
+            wqg[i] = pack_f16(qm0 * eP0, qm1 * eP1);
+            wkg[i] = pack_f16(km0 * nP0, km1 * nP1);
             if constexpr (HP)
-                split_bf16(kh0[i] * eC0, kh1[i] * eC1, kb[i], kl8[i]);
+                split_bf16(kh0 * eC0, kh1 * eC1, kb[i], kl8[i]);
             else
-                kb[i] = pack_f16(kh0[i] * eC0, kh1[i] * eC1);
+                kb[i] = pack_f16(kh0 * eC0, kh1 * eC1);
         }
-        // token pairs of channel c0 (low halves) and of channel c0 + 1 (high halves); tokens
-        // 8kw..8kw+3 and 8kw+4..8kw+7 are each contiguous after tperm
+        // one array at a time, so that stores of neighbouring tokens pair up
+        const int tq = TPW * kw;
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.qmh[tq + i][c0]) = wqh[i];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.qml[tq + i][c0]) = wql[i];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.km[tq + i][c0]) = wkm[i];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khh[tq + i][c0]) = wkh[i];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khl[tq + i][c0]) = wkl[i];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&H.qg[tq + i][pc0]) = wqg[i];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&H.kgn[tq + i][pc0]) = wkg[i];
+        // token pairs of channel c0 (low halves) and of channel c0 + 1 (high halves); the quad's
+        // four tokens are contiguous after tperm
+        const int pt = tperm(TPW * kw);
         auto put_t = [&](uint16_t (*dst)[LDT], const uint32_t* w) {
-            const u32x4 b0 = {perm_lo(w[0], w[1]), perm_lo(w[2], w[3]), perm_lo(w[4], w[5]), perm_lo(w[6], w[7])};
-            const u32x4 b1 = {perm_hi(w[0], w[1]), perm_hi(w[2], w[3]), perm_hi(w[4], w[5]), perm_hi(w[6], w[7])};
-            const int pa = tperm(8 * kw), pb = tperm(8 * kw + 4);
-            *reinterpret_cast<u32x2*>(&dst[c0][pa]) = u32x2{b0.x, b0.y};
-            *reinterpret_cast<u32x2*>(&dst[c0][pb]) = u32x2{b0.z, b0.w};
-            *reinterpret_cast<u32x2*>(&dst[c0 + 1][pa]) = u32x2{b1.x, b1.y};
-            *reinterpret_cast<u32x2*>(&dst[c0 + 1][pb]) = u32x2{b1.z, b1.w};
+            *reinterpret_cast<u32x2*>(&dst[c0][pt]) = u32x2{perm_lo(w[0], w[1]), perm_lo(w[2], w[3])};
+            *reinterpret_cast<u32x2*>(&dst[c0 + 1][pt]) = u32x2{perm_hi(w[0], w[1]), perm_hi(w[2], w[3])};
         };
         put_t(H.kbh, kb);
         if constexpr (HP) put_t(H.kbl, kl8);
-        if (sig == 0) {
-            // K/Gamma rows of sub-tile 0 moved to sub-tile 1's reference: factor exp(b_23 - b_7) <= 1
-            const float f0 = fexp(pB0 - pA0), f1 = fexp(pB1 - pA1);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int t = 8 * kw + i;
-                uint32_t hi, lo;
-                split_bf16(kh0[i] * f0, kh1[i] * f1, hi, lo);
-                *reinterpret_cast<uint32_t*>(&sm.key.k1h[t][c0]) = hi;
-                *reinterpret_cast<uint32_t*>(&sm.key.k1l[t][c0]) = lo;
-            }
-        }
         if (kw == 0) *reinterpret_cast<float2*>(&H.gamc[c0]) = make_float2(fexp(bC0), fexp(bC1));
     }
     lds_barrier();  // ---- barrier 2
@@ -319,9 +308,9 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         if (kw < 3) {
             // A(0,0), A(1,0), A(1,1): split bf16 with three independent accumulators
             const int R = kw == 0 ? 0 : 1, S = kw == 2 ? 1 : 0;
-            const uint16_t(*rh)[LDK] = (kw == 1) ? sm.key.k1h : (S ? sm.key.khh + SUB : sm.key.khh);
-            const uint16_t(*rl)[LDK] = (kw == 1) ? sm.key.k1l : (S ? sm.key.khl + SUB : sm.key.khl);
-            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+            const uint16_t(*rh)[LDK] = sm.key.khh + SUB * S;
+            const uint16_t(*rl)[LDK] = sm.key.khl + SUB * S;
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;  // two chains over alternate channel blocks
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int kc = 32 * m + 8 * g4;
@@ -329,20 +318,21 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
                 const u32x4 aL = ld16(&sm.key.qml[SUB * R + l16][kc]);
                 const u32x4 bH = ld16(&rh[l16][kc]);
                 const u32x4 bL = ld16(&rl[l16][kc]);
-                a0 = mfma_bf16(aH, bH, a0);
-                a1 = mfma_bf16(aH, bL, a1);
-                a2 = mfma_bf16(aL, bH, a2);
+                f32x4& a = (m & 1) ? a1 : a0;
+                a = mfma_bf16(aH, bH, a);
+                a = mfma_bf16(aH, bL, a);
+                a = mfma_bf16(aL, bH, a);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 4 * g4 + r;
-                float v = (a0[r] + a1[r]) + a2[r];
+                float v = a0[r] + a1[r];
                 if (R == S && l16 > i) v = 0.f;  // lower triangle including the diagonal
                 const uint32_t hi = pack_bf16(v, 0.f);
                 H.ah[SUB * R + i][tperm(SUB * S + l16)] = hi & 0xffffu;
                 H.al[SUB * R + i][tperm(SUB * S + l16)] = pack_bf16(v - bf16lo_to_f(hi), 0.f) & 0xffffu;
             }
-        } else {
+        } else if (kw == 3) {
             // L(0,0), L(1,0), L(1,1): bf16 Km against K/Gamma (split bf16 when HP, else its high part)
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
 #pragma unroll
@@ -351,11 +341,11 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
                 const u32x4 a0 = ld16(&sm.key.km[l16][kc]);
                 const u32x4 a1 = ld16(&sm.key.km[SUB + l16][kc]);
                 acc0 = mfma_bf16(a0, ld16(&sm.key.khh[l16][kc]), acc0);
-                acc1 = mfma_bf16(a1, ld16(&sm.key.k1h[l16][kc]), acc1);
+                acc1 = mfma_bf16(a1, ld16(&sm.key.khh[l16][kc]), acc1);
                 acc2 = mfma_bf16(a1, ld16(&sm.key.khh[SUB + l16][kc]), acc2);
                 if constexpr (HP) {
                     acc0 = mfma_bf16(a0, ld16(&sm.key.khl[l16][kc]), acc0);
-                    acc1 = mfma_bf16(a1, ld16(&sm.key.k1l[l16][kc]), acc1);
+                    acc1 = mfma_bf16(a1, ld16(&sm.key.khl[l16][kc]), acc1);
                     acc2 = mfma_bf16(a1, ld16(&sm.key.khl[SUB + l16][kc]), acc2);
                 }
             }
@@ -374,14 +364,12 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         if constexpr (!IN_F32) {
             if (lane < 32) {  // V^T for value columns 2*lane, 2*lane+1 of this half
                 const uint32_t* v = cur.v;
-                const int pa = tperm(8 * kw), pb = tperm(8 * kw + 4);
-                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane][pa]) = u32x2{perm_lo(v[0], v[1]), perm_lo(v[2], v[3])};
-                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane][pb]) = u32x2{perm_lo(v[4], v[5]), perm_lo(v[6], v[7])};
-                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane + 1][pa]) = u32x2{perm_hi(v[0], v[1]), perm_hi(v[2], v[3])};
-                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane + 1][pb]) = u32x2{perm_hi(v[4], v[5]), perm_hi(v[6], v[7])};
+                const int pt = tperm(TPW * kw);
+                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane][pt]) = u32x2{perm_lo(v[0], v[1]), perm_lo(v[2], v[3])};
+                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane + 1][pt]) = u32x2{perm_hi(v[0], v[1]), perm_hi(v[2], v[3])};
             }
         }
-        if (lane < 8) sm.h1.beta[8 * kw + lane] = cur.beta;
+        if (lane < TPW) sm.h1.beta[TPW * kw + lane] = cur.beta;
     }
     lds_barrier();  // ---- barrier 3
 }
@@ -389,7 +377,7 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
 template <bool IN_F32, bool HP>
 __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int half, int kw, int lane, int nchunk) {
     // A's block (0,1) is zero in both buffers; no chunk writes it
-    for (int e = 64 * kw + lane; e < 2 * SUB * SUB; e += 256) {
+    for (int e = 64 * kw + lane; e < 2 * SUB * SUB; e += 64 * NKW) {
         Handoff2& Hz = sm.h2[e >> 8];
         const int r = (e >> 4) & 15, c = tperm(SUB + (e & 15));
         Hz.ah[r][c] = 0; Hz.al[r][c] = 0;
@@ -401,11 +389,11 @@ __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int half, int 
     kl.lane_b = 4 * lane;
     kl.vlane_b = 2 * (half * DVH + 2 * (lane & 31));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        kl.off[i] = (uint32_t)(8 * kw + i) * kl.tok_b + kl.lane_b;
-        kl.voff[i] = (uint32_t)(8 * kw + i) * kl.tok_b + kl.vlane_b;
+    for (int i = 0; i < TPW; ++i) {
+        kl.off[i] = (uint32_t)(TPW * kw + i) * kl.tok_b + kl.lane_b;
+        kl.voff[i] = (uint32_t)(TPW * kw + i) * kl.tok_b + kl.vlane_b;
     }
-    kl.boff = (uint32_t)(8 * kw + (lane & 7)) * 4u * p.H;
+    kl.boff = (uint32_t)(TPW * kw + (lane % TPW)) * 4u * p.H;
     Raw<IN_F32> ra, rb;
     if (p.T > 0) load_chunk(ra, p, kl, row0, 0);
     // two steps per iteration so the prefetch target alternates between two register sets
@@ -493,9 +481,13 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
                 aa = __builtin_fmaf(Lr[m], xa, aa);                                              \
                 ab = __builtin_fmaf(Lr[m], xb, ab);                                              \
             }
-            KDA_SUBST_STEP(0) KDA_SUBST_STEP(1) KDA_SUBST_STEP(2) KDA_SUBST_STEP(3) KDA_SUBST_STEP(4)
-            KDA_SUBST_STEP(5) KDA_SUBST_STEP(6) KDA_SUBST_STEP(7) KDA_SUBST_STEP(8) KDA_SUBST_STEP(9)
-            KDA_SUBST_STEP(10) KDA_SUBST_STEP(11) KDA_SUBST_STEP(12) KDA_SUBST_STEP(13) KDA_SUBST_STEP(14)
+            // for columns j >= 8 the first eight unknowns are zero (the inverse is lower triangular)
+            if ((vw & 1) == 0) {
+                KDA_SUBST_STEP(0) KDA_SUBST_STEP(1) KDA_SUBST_STEP(2) KDA_SUBST_STEP(3)
+                KDA_SUBST_STEP(4) KDA_SUBST_STEP(5) KDA_SUBST_STEP(6) KDA_SUBST_STEP(7)
+            }
+            KDA_SUBST_STEP(8) KDA_SUBST_STEP(9) KDA_SUBST_STEP(10) KDA_SUBST_STEP(11)
+            KDA_SUBST_STEP(12) KDA_SUBST_STEP(13) KDA_SUBST_STEP(14)
 #undef KDA_SUBST_STEP
             // T = X Diag(beta), as split bf16 in the tperm'd columns of T's tile
             const float ta = __builtin_fmaf(nbi, aa, da) * beta[o + ja];
@@ -549,11 +541,9 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
                 l = u32x2{l0, l1};
             };
             auto prod3 = [](u32x2 aH, u32x2 aL, u32x2 bH, u32x2 bL) {
-                f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
-                a0 = mfma_bf16_k16(aH, bH, a0);
-                a1 = mfma_bf16_k16(aH, bL, a1);
-                a2 = mfma_bf16_k16(aL, bH, a2);
-                return (a0 + a1) + a2;
+                f32x4 a = mfma_bf16_k16(aH, bH, f32x4{0.f, 0.f, 0.f, 0.f});
+                a = mfma_bf16_k16(aH, bL, a);
+                return mfma_bf16_k16(aL, bH, a);
             };
             auto ld8 = [](const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); };
             f32x4 u[2];
@@ -584,11 +574,10 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
             for (int R = 0; R < 2; ++R) {
                 const u32x4 aH = ld16(&H.ah[SUB * R + l16][8 * g4]);
                 const u32x4 aL = ld16(&H.al[SUB * R + l16][8 * g4]);
-                f32x4 ax = {0.f, 0.f, 0.f, 0.f}, ay = ax, acc = oacc[R];
-                ax = mfma_bf16(uh, aH, ax);
-                ay = mfma_bf16(ul, aH, ay);
+                f32x4 acc = mfma_bf16(uh, aH, oacc[R]);
+                acc = mfma_bf16(ul, aH, acc);
                 acc = mfma_bf16(uh, aL, acc);
-                acc = (acc + ax + ay) * p.scale;
+                if (p.scale != 1.f) acc *= p.scale;
                 if (t0 + SUB * R + l16 < p.T) {
                     if constexpr (OUT_F32)
                         gstore<f32x4>(ob, ooff[R], acc);
@@ -629,7 +618,7 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
 template <bool OUT_F32, bool IN_F32, bool HP>
 __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
     __shared__ Smem sm;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 
     // workgroup -> (batch*head, value half); both halves of a head land on the same XCD
     int bh, half;
@@ -646,10 +635,10 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
     const size_t row0 = (size_t)b * p.T * p.H + h;  // row of token 0: (b*T + t)*H + h = row0 + t*H
     const int nchunk = (p.T + C - 1) / C;
 
-    if (wave < 4)
+    if (wave < NKW)
         key_waves<IN_F32, HP>(sm, p, row0, half, wave, lane, nchunk);
     else
-        value_waves<OUT_F32, IN_F32, HP>(sm, p, bh, row0, half, wave - 4, lane, nchunk);
+        value_waves<OUT_F32, IN_F32, HP>(sm, p, bh, row0, half, wave - NKW, lane, nchunk);
 }
 
 }  // namespace bf16path
