@@ -239,16 +239,21 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
             const float2 t = *reinterpret_cast<const float2*>(&sm.key.tot[o][c0]);
             tt0[o] = t.x; tt1[o] = t.y;
         }
-        float p0 = 0.f, p1 = 0.f, bC0 = 0.f, bC1 = 0.f, o0 = 0.f, o1 = 0.f;
+        // p = b at token 15 (the reference), q = b at token 31 minus p, and o = b at the token before
+        // this quad minus p: a signed sum of quad totals with wave-uniform coefficients
+        float p0 = 0.f, p1 = 0.f, q0 = 0.f, q1 = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
         for (int o = 0; o < NKW; ++o) {
-            if (o < NKW / 2) { p0 += tt0[o]; p1 += tt1[o]; }  // b at token 15
-            bC0 += tt0[o]; bC1 += tt1[o];                    // b at token 31
-            if (o < kw) { o0 += tt0[o]; o1 += tt1[o]; }      // b at the token before this quad
+            if (o < NKW / 2) { p0 += tt0[o]; p1 += tt1[o]; }
+            else { q0 += tt0[o]; q1 += tt1[o]; }
+            const float w = (o < kw ? 1.f : 0.f) - (o < NKW / 2 ? 1.f : 0.f);
+            o0 = __builtin_fmaf(w, tt0[o], o0);
+            o1 = __builtin_fmaf(w, tt1[o], o1);
         }
-        o0 = (o0 - p0) * kLog2e; o1 = (o1 - p1) * kLog2e;
+        o0 *= kLog2e; o1 *= kLog2e;
         const float eP0 = fexp(p0), eP1 = fexp(p1);
-        const float eC0 = fexp(bC0 - p0), eC1 = fexp(bC1 - p1);
+        const float eC0 = fexp(q0), eC1 = fexp(q1);
+        const float bC0 = p0 + q0, bC1 = p1 + q1;
         const float nP0 = -eP0, nP1 = -eP1;
         const int pc0 = cperm(c0);  // c0 even: c0 + 1 follows it
         uint32_t kb[TPW], kl8[TPW];
