@@ -73,6 +73,69 @@ def cpu_baseline(d, threads):
                       f"{dt:.1f} s wall on {threads} threads)"}
 
 
+def layer_flops(B, T, d, H, D, R):
+    """Matrix-product flops of one fused-layer call: the q, k, v, gate and output projections, beta,
+    the rank-R decay projection, and the chunkwise core (as algorithmic_flops)."""
+    HD = H * D
+    per_token = 2 * (4 * d * HD + d * H + d * R + R * HD + HD * d)
+    return B * T * per_token + algorithmic_flops(B, T, H, D, D)
+
+
+def bench_layer(args, torch, synth, kda):
+    """kda_layer_fwd on B=2, T=8192, d_model=2048, H=16, D=128, rank 128: tokens/s and matrix-core
+    fraction.  Buffers are allocated once; every kernel of the layer is inside each timed call."""
+    from linear_recurrent_attention_amd import _lib
+    L = synth.gen.LAYER
+    B, T, d, H, D, R = L["B"], L["T"], L["d"], L["H"], L["Dk"], L["rank"]
+    x, p = synth.layer_inputs(seed=0)
+    dev = torch.device("cuda:0")
+    bf = ("Wq", "Wk", "Wv", "Wg", "Wo", "Wbeta", "Wdown", "Wup")
+    W = {n: torch.from_numpy(np.ascontiguousarray(a)).to(dev) for n, a in p.items()}
+    for n in bf:
+        W[n] = W[n].to(torch.bfloat16)
+    xt = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    desc = _lib.LayerDesc(B, T, d, H, D, D, R, 4, 1.0, 0)
+    ws = torch.empty(_lib.layer_workspace_size(desc), dtype=torch.uint8, device=dev)
+    y = torch.empty((B, T, d), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    cs = torch.empty((B, 3, 2 * H * D), dtype=torch.float32, device=dev)
+    Wc = _lib.LayerWeights(*[W[n].data_ptr() for n in _lib.LAYER_WEIGHT_FIELDS])
+    stream = torch.cuda.Stream(device=dev)
+
+    def step():
+        _lib.check(_lib.layer_fwd_raw(desc, xt.data_ptr(), Wc, 0, 0, y.data_ptr(), ST.data_ptr(), cs.data_ptr(),
+                                      ws.data_ptr(), ws.numel(), stream.cuda_stream))
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    stream.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    avg_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    flops = layer_flops(B, T, d, H, D, R)
+    tflops = flops / avg_s / 1e12
+    out = {
+        "metric": "KDA layer forward tokens/s (B2 T8192 d2048 H16 D128)", "value": B * T / (wall / args.steps),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": L["name"], "B": B, "T": T, "d_model": d, "H": H, "D": D, "rank": R, "conv": 4},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "kda_layer_fwd (all kernels)",
+                     "avg_call_ms": avg_s * 1e3, "algorithmic_flops": flops},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,6 +144,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run one plain 512 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--workload", choices=("core", "layer"), default="core",
+                    help="core: kda_fwd on B4 H32 T16384 (the headline line); layer: kda_layer_fwd on "
+                         "B2 T8192 d_model 2048 H16 (a second, separate line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus N with N > 1 is not supported "
@@ -91,6 +157,9 @@ def main():
     import synth
     import linear_recurrent_attention_amd as kda
 
+    if args.workload == "layer":
+        bench_layer(args, torch, synth, kda)
+        return
     w = synth.WORKLOADS[WORKLOAD]
     B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
     d = synth.core_inputs(WORKLOAD, seed=0)

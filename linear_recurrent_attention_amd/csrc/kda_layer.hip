@@ -61,50 +61,74 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// conv + SiLU on channels c, c+1 of row (b, t); `which` 0 = q, 1 = k
-__device__ __forceinline__ float2 conv_silu(const ProParams& p, const float* src, const float* taps, int which, int b,
-                                            int t, int c) {
-    const float4 w0 = *reinterpret_cast<const float4*>(taps + (size_t)c * 4);
-    const float4 w1 = *reinterpret_cast<const float4*>(taps + (size_t)(c + 1) * 4);
-    const float wa[4] = {w0.x, w0.y, w0.z, w0.w}, wb[4] = {w1.x, w1.y, w1.z, w1.w};
-    float y0 = 0.f, y1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tt = t - 3 + j;
-        float2 x = make_float2(0.f, 0.f);
-        if (tt >= 0) {
-            x = *reinterpret_cast<const float2*>(src + ((size_t)b * p.T + tt) * p.HD + c);
-        } else if (p.state_in) {
-            x = *reinterpret_cast<const float2*>(p.state_in + ((size_t)b * 3 + (3 + tt)) * 2 * p.HD + which * p.HD + c);
-        }
-        y0 += wa[j] * x.x;
-        y1 += wb[j] * x.y;
-    }
-    return make_float2(y0 * sigmoidf_(y0), y1 * sigmoidf_(y1));
-}
+// Prologue: one wave per (batch, head, block of PRO_TOK tokens); lane l holds channels c, c+1 with
+// c = h*D + 2l.  The short convolution's window (the 3 previous pre-conv rows of q and k) is carried
+// in registers along the tokens, so each projection row is read once.
+constexpr int PRO_TOK = 32;
+
+__device__ __forceinline__ float silu(float x) { return x * sigmoidf_(x); }
 
 __global__ void __launch_bounds__(256) prologue_kernel(ProParams p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const long gw = (long)blockIdx.x * 4 + wave;  // (row, head)
-    if (gw >= (long)p.B * p.T * p.H) return;
-    const long row = gw / p.H;
-    const int h = (int)(gw - row * p.H);
-    const int b = (int)(row / p.T), t = (int)(row - (long)b * p.T);
+    const int nblk = (p.T + PRO_TOK - 1) / PRO_TOK;
+    const long gw = (long)blockIdx.x * 4 + wave;  // ((b * H) + h) * nblk + blk
+    if (gw >= (long)p.B * p.H * nblk) return;
+    const int blk = (int)(gw % nblk);
+    const long bh = gw / nblk;
+    const int h = (int)(bh % p.H), b = (int)(bh / p.H);
     const int c = h * D + 2 * lane;
-    const size_t rc = (size_t)row * p.HD + c;
+    const int t0 = blk * PRO_TOK, t1 = min(t0 + PRO_TOK, p.T);
 
-    const float2 qs = conv_silu(p, p.pq, p.conv_q, 0, b, t, c);
-    const float2 ks = conv_silu(p, p.pk, p.conv_k, 1, b, t, c);
-    const float qn = rsqrtf(wave_sum(qs.x * qs.x + qs.y * qs.y) + EPS);
-    const float kn = rsqrtf(wave_sum(ks.x * ks.x + ks.y * ks.y) + EPS);
-    *reinterpret_cast<float2*>(p.q + rc) = make_float2(qs.x * qn, qs.y * qn);
-    *reinterpret_cast<float2*>(p.k + rc) = make_float2(ks.x * kn, ks.y * kn);
-    const float2 z = *reinterpret_cast<const float2*>(p.pz + rc);
+    float wq[2][4], wk[2][4];  // taps of channels c, c+1; tap 3 multiplies the current token
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const float4 a = *reinterpret_cast<const float4*>(p.conv_q + (size_t)(c + e) * 4);
+        const float4 k = *reinterpret_cast<const float4*>(p.conv_k + (size_t)(c + e) * 4);
+        wq[e][0] = a.x; wq[e][1] = a.y; wq[e][2] = a.z; wq[e][3] = a.w;
+        wk[e][0] = k.x; wk[e][1] = k.y; wk[e][2] = k.z; wk[e][3] = k.w;
+    }
+    // window: rows t0-3, t0-2, t0-1 (from this call's projections, the incoming window, or zeros)
+    float2 xq[3], xk[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int tt = t0 - 3 + j;
+        xq[j] = xk[j] = make_float2(0.f, 0.f);
+        if (tt >= 0) {
+            xq[j] = *reinterpret_cast<const float2*>(p.pq + ((size_t)b * p.T + tt) * p.HD + c);
+            xk[j] = *reinterpret_cast<const float2*>(p.pk + ((size_t)b * p.T + tt) * p.HD + c);
+        } else if (p.state_in) {
+            const float* sw = p.state_in + ((size_t)b * 3 + (3 + tt)) * 2 * p.HD;
+            xq[j] = *reinterpret_cast<const float2*>(sw + c);
+            xk[j] = *reinterpret_cast<const float2*>(sw + p.HD + c);
+        }
+    }
     const float2 ba = *reinterpret_cast<const float2*>(p.b_alpha + c);
     const float ea = fexp(p.A[h]);
-    *reinterpret_cast<float2*>(p.g + rc) =
-        make_float2(-5.f * sigmoidf_(ea * (z.x + ba.x)), -5.f * sigmoidf_(ea * (z.y + ba.y)));
-    if (lane == 0) p.beta[(size_t)row * p.H + h] = sigmoidf_(p.pbeta[(size_t)row * p.H + h]);
+    for (int t = t0; t < t1; ++t) {
+        const size_t rc = ((size_t)b * p.T + t) * p.HD + c;
+        const size_t row = (size_t)b * p.T + t;
+        const float2 cq = *reinterpret_cast<const float2*>(p.pq + rc);
+        const float2 ck = *reinterpret_cast<const float2*>(p.pk + rc);
+        const float2 z = *reinterpret_cast<const float2*>(p.pz + rc);
+        float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            q0 += wq[0][j] * xq[j].x; q1 += wq[1][j] * xq[j].y;
+            k0 += wk[0][j] * xk[j].x; k1 += wk[1][j] * xk[j].y;
+        }
+        q0 += wq[0][3] * cq.x; q1 += wq[1][3] * cq.y;
+        k0 += wk[0][3] * ck.x; k1 += wk[1][3] * ck.y;
+        xq[0] = xq[1]; xq[1] = xq[2]; xq[2] = cq;
+        xk[0] = xk[1]; xk[1] = xk[2]; xk[2] = ck;
+        q0 = silu(q0); q1 = silu(q1); k0 = silu(k0); k1 = silu(k1);
+        const float qn = rsqrtf(wave_sum(q0 * q0 + q1 * q1) + EPS);
+        const float kn = rsqrtf(wave_sum(k0 * k0 + k1 * k1) + EPS);
+        *reinterpret_cast<float2*>(p.q + rc) = make_float2(q0 * qn, q1 * qn);
+        *reinterpret_cast<float2*>(p.k + rc) = make_float2(k0 * kn, k1 * kn);
+        *reinterpret_cast<float2*>(p.g + rc) =
+            make_float2(-5.f * sigmoidf_(ea * (z.x + ba.x)), -5.f * sigmoidf_(ea * (z.y + ba.y)));
+        if (lane == 0) p.beta[row * p.H + h] = sigmoidf_(p.pbeta[row * p.H + h]);
+    }
 }
 
 // Last three pre-conv rows of each sequence (from this call's projections, or the incoming window
@@ -273,7 +297,10 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
     pp.state_in = conv_state_in;
     pp.q = W.q; pp.k = W.k; pp.v = nullptr; pp.g = W.g; pp.beta = W.beta;
     const long nw = (long)M * d->H;
-    hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, stream, pp);
+    {
+        const long npw = (long)d->B * d->H * ((d->T + PRO_TOK - 1) / PRO_TOK);  // prologue waves
+        hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)((npw + 3) / 4)), dim3(256), 0, stream, pp);
+    }
     if (conv_state_out)
         hipLaunchKernelGGL(conv_state_kernel, dim3(256), dim3(256), 0, stream, d->B, d->T, HD, W.pq, W.pk,
                            conv_state_in, conv_state_out);
