@@ -207,20 +207,28 @@ __device__ __forceinline__ void mask_tail(Raw<IN_F32>& r, int T, int t0, int kw,
     if (t0 + TPW * kw + (lane % TPW) >= T) r.beta = 0.f;
 }
 
+// Factors of the previous chunk that the value-side tiles are made from, kept in registers from
+// part 2 of one step to part 1 of the next (the value waves read those tiles only a step later).
+struct Carry {
+    float qm[TPW][2], km[TPW][2], kh[TPW][2];  // Q, K times exp(b - b_15); K times exp(b_15 - b)
+    float eP[2], eC[2], gam[2];                // exp(b_15), exp(b_31 - b_15), exp(b_31)
+};
+
 // ------------------------------------------------------------------------------------------------
 // key waves: one step = chunk n (nothing when n == nchunk); three barriers
 // ------------------------------------------------------------------------------------------------
 template <bool IN_F32, bool HP>
 __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoad& kl, size_t row0, int n,
-                                         int nchunk, Raw<IN_F32>& cur, Raw<IN_F32>& nxt) {
+                                         int nchunk, Raw<IN_F32>& cur, Raw<IN_F32>& nxt, Carry& cy) {
     const int kw = kl.kw, lane = kl.lane;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int c0 = 2 * lane;   // key channels c0, c0 + 1
     const bool work = n < nchunk;
     const int t0 = n * C;
-    Handoff2& H = sm.h2[n & 1];
+    Handoff2& H = sm.h2[n & 1];  // A of chunk n (part 3); its other tiles are written next step
 
-    // ---------------- part 1: decay sums over the quad; prefetch of the next chunk
+    // ---------------- part 1: decay sums over the quad; prefetch of the next chunk; the previous
+    // chunk's value-side tiles (Q*Gamma, -(K*Gamma), Kbar^T, Gamma_last), which its value step reads
     if (work) {
         if (t0 + C > p.T) mask_tail(cur, p.T, t0, kw, lane);
         float a0 = 0.f, a1 = 0.f;
@@ -228,6 +236,35 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         for (int i = 0; i < TPW; ++i) { a0 += cur.g[i][0]; a1 += cur.g[i][1]; }
         *reinterpret_cast<float2*>(&sm.key.tot[kw][c0]) = make_float2(a0, a1);
         if (n + 1 < nchunk) load_chunk(nxt, p, kl, row0, t0 + C);  // prefetch the next chunk
+    }
+    if (n >= 1) {
+        Handoff2& Hp = sm.h2[(n - 1) & 1];
+        const int pc0 = cperm(c0);  // c0 even: c0 + 1 follows it
+        const int tq = TPW * kw;
+        uint32_t kb[TPW], kl8[TPW], wqg[TPW], wkg[TPW];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            wqg[i] = pack_f16(cy.qm[i][0] * cy.eP[0], cy.qm[i][1] * cy.eP[1]);
+            wkg[i] = pack_f16(-(cy.km[i][0] * cy.eP[0]), -(cy.km[i][1] * cy.eP[1]));
+            if constexpr (HP)
+                split_bf16(cy.kh[i][0] * cy.eC[0], cy.kh[i][1] * cy.eC[1], kb[i], kl8[i]);
+            else
+                kb[i] = pack_f16(cy.kh[i][0] * cy.eC[0], cy.kh[i][1] * cy.eC[1]);
+        }
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&Hp.qg[tq + i][pc0]) = wqg[i];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&Hp.kgn[tq + i][pc0]) = wkg[i];
+        // token pairs of channel c0 (low halves) and of channel c0 + 1 (high halves); the quad's
+        // four tokens are contiguous after tperm
+        const int pt = tperm(tq);
+        auto put_t = [&](uint16_t (*dst)[LDT], const uint32_t* w) {
+            *reinterpret_cast<u32x2*>(&dst[c0][pt]) = u32x2{perm_lo(w[0], w[1]), perm_lo(w[2], w[3])};
+            *reinterpret_cast<u32x2*>(&dst[c0 + 1][pt]) = u32x2{perm_hi(w[0], w[1]), perm_hi(w[2], w[3])};
+        };
+        put_t(Hp.kbh, kb);
+        if constexpr (HP) put_t(Hp.kbl, kl8);
+        if (kw == 0) *reinterpret_cast<float2*>(&Hp.gamc[c0]) = make_float2(cy.gam[0], cy.gam[1]);
     }
     lds_barrier();  // ---- barrier 1
 
@@ -251,13 +288,10 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
             o1 = __builtin_fmaf(w, tt1[o], o1);
         }
         o0 *= kLog2e; o1 *= kLog2e;
-        const float eP0 = fexp(p0), eP1 = fexp(p1);
-        const float eC0 = fexp(q0), eC1 = fexp(q1);
-        const float bC0 = p0 + q0, bC1 = p1 + q1;
-        const float nP0 = -eP0, nP1 = -eP1;
-        const int pc0 = cperm(c0);  // c0 even: c0 + 1 follows it
-        uint32_t kb[TPW], kl8[TPW];
-        uint32_t wqh[TPW], wql[TPW], wkm[TPW], wkh[TPW], wkl[TPW], wqg[TPW], wkg[TPW];
+        cy.eP[0] = fexp(p0); cy.eP[1] = fexp(p1);
+        cy.eC[0] = fexp(q0); cy.eC[1] = fexp(q1);
+        cy.gam[0] = fexp(p0 + q0); cy.gam[1] = fexp(p1 + q1);
+        uint32_t wqh[TPW], wql[TPW], wkm[TPW], wkh[TPW], wkl[TPW];
         float y0 = o0, y1 = o1;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
@@ -266,18 +300,12 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
             const float e0 = __builtin_amdgcn_exp2f(y0), e1 = __builtin_amdgcn_exp2f(y1);
             const float f0 = __builtin_amdgcn_exp2f(-y0), f1 = __builtin_amdgcn_exp2f(-y1);
             const f32x2 qq = unpack_q(cur.q[i]), kk = unpack_q(cur.k[i]);
-            const float qm0 = qq[0] * e0, qm1 = qq[1] * e1;
-            const float km0 = kk[0] * e0, km1 = kk[1] * e1;
-            const float kh0 = kk[0] * f0, kh1 = kk[1] * f1;
-            split_bf16(qm0, qm1, wqh[i], wql[i]);
-            wkm[i] = pack_bf16(km0, km1);
-            split_bf16(kh0, kh1, wkh[i], wkl[i]);
-            wqg[i] = pack_f16(qm0 * eP0, qm1 * eP1);
-            wkg[i] = pack_f16(km0 * nP0, km1 * nP1);
-            if constexpr (HP)
-                split_bf16(kh0 * eC0, kh1 * eC1, kb[i], kl8[i]);
-            else
-                kb[i] = pack_f16(kh0 * eC0, kh1 * eC1);
+            cy.qm[i][0] = qq[0] * e0; cy.qm[i][1] = qq[1] * e1;
+            cy.km[i][0] = kk[0] * e0; cy.km[i][1] = kk[1] * e1;
+            cy.kh[i][0] = kk[0] * f0; cy.kh[i][1] = kk[1] * f1;
+            split_bf16(cy.qm[i][0], cy.qm[i][1], wqh[i], wql[i]);
+            wkm[i] = pack_bf16(cy.km[i][0], cy.km[i][1]);
+            split_bf16(cy.kh[i][0], cy.kh[i][1], wkh[i], wkl[i]);
         }
         // one array at a time, so that stores of neighbouring tokens pair up
         const int tq = TPW * kw;
@@ -291,20 +319,6 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khh[tq + i][c0]) = wkh[i];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khl[tq + i][c0]) = wkl[i];
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&H.qg[tq + i][pc0]) = wqg[i];
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&H.kgn[tq + i][pc0]) = wkg[i];
-        // token pairs of channel c0 (low halves) and of channel c0 + 1 (high halves); the quad's
-        // four tokens are contiguous after tperm
-        const int pt = tperm(TPW * kw);
-        auto put_t = [&](uint16_t (*dst)[LDT], const uint32_t* w) {
-            *reinterpret_cast<u32x2*>(&dst[c0][pt]) = u32x2{perm_lo(w[0], w[1]), perm_lo(w[2], w[3])};
-            *reinterpret_cast<u32x2*>(&dst[c0 + 1][pt]) = u32x2{perm_hi(w[0], w[1]), perm_hi(w[2], w[3])};
-        };
-        put_t(H.kbh, kb);
-        if constexpr (HP) put_t(H.kbl, kl8);
-        if (kw == 0) *reinterpret_cast<float2*>(&H.gamc[c0]) = make_float2(fexp(bC0), fexp(bC1));
     }
     lds_barrier();  // ---- barrier 2
 
@@ -400,11 +414,12 @@ __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int half, int 
     }
     kl.boff = (uint32_t)(TPW * kw + (lane % TPW)) * 4u * p.H;
     Raw<IN_F32> ra, rb;
+    Carry cy;
     if (p.T > 0) load_chunk(ra, p, kl, row0, 0);
     // two steps per iteration so the prefetch target alternates between two register sets
     for (int n = 0; n <= nchunk; n += 2) {
-        key_step<IN_F32, HP>(sm, p, kl, row0, n, nchunk, ra, rb);
-        if (n + 1 <= nchunk) key_step<IN_F32, HP>(sm, p, kl, row0, n + 1, nchunk, rb, ra);
+        key_step<IN_F32, HP>(sm, p, kl, row0, n, nchunk, ra, rb, cy);
+        if (n + 1 <= nchunk) key_step<IN_F32, HP>(sm, p, kl, row0, n + 1, nchunk, rb, ra, cy);
     }
 }
 
