@@ -478,13 +478,16 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
         const int t0 = (n - 1) * C;
         const Handoff2& H = sm.h2[(n - 1) & 1];
         // ---------------- part 1: UT inverse of the two diagonal blocks, spread over the value waves
-        // Wave vw solves columns j = 8*(vw & 1) + g4 and j + 4 of block vw >> 1 of (I + Diag(beta) L) X = I;
-        // lane l16 of a 16-lane row holds matrix row i = l16.  Forward substitution: at step m every lane
-        // forms its candidate x_i = [i == j] - beta_i acc_i, row m's (final) candidate is broadcast along
-        // the 16-lane row, and rows below take acc_i += L[i][m] x_m (L is zero on and above the diagonal).
+        // Wave vw solves two columns ja, jb of block vw >> 1 of (I + Diag(beta) L) X = I per 16-lane row
+        // g4: ja = g4, jb = 12 + g4 (even vw) or ja = 4 + g4, jb = 8 + g4 (odd vw); lane l16 holds matrix
+        // row i = l16.  Forward substitution: at step m every lane forms its candidate
+        // x_i = [i == j] - beta_i acc_i, row m's (final) candidate is broadcast along the 16-lane row, and
+        // rows below take acc_i += L[i][m] x_m (L is zero on and above the diagonal).  Column j needs
+        // steps m >= j only (the unknowns above row j are zero), which the column pairing balances.
         if (work) {
             const float* beta = sm.h1.beta;
-            const int o = SUB * (vw >> 1), i = l16, ja = 8 * (vw & 1) + g4, jb = ja + 4;
+            const bool odd = vw & 1;
+            const int o = SUB * (vw >> 1), i = l16, ja = (odd ? 4 : 0) + g4, jb = (odd ? 8 : 12) + g4;
             float Lr[SUB];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
@@ -494,21 +497,29 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
             const float nbi = -beta[o + i];
             const float da = i == ja ? 1.f : 0.f, db = i == jb ? 1.f : 0.f;
             float aa = 0.f, ab = 0.f;
-#define KDA_SUBST_STEP(m)                                                                        \
+#define KDA_STEP_A(m)                                                                            \
+            {                                                                                    \
+                const float xa = row_bcast<m>(__builtin_fmaf(nbi, aa, da));                      \
+                aa = __builtin_fmaf(Lr[m], xa, aa);                                              \
+            }
+#define KDA_STEP_AB(m)                                                                           \
             {                                                                                    \
                 const float xa = row_bcast<m>(__builtin_fmaf(nbi, aa, da));                      \
                 const float xb = row_bcast<m>(__builtin_fmaf(nbi, ab, db));                      \
                 aa = __builtin_fmaf(Lr[m], xa, aa);                                              \
                 ab = __builtin_fmaf(Lr[m], xb, ab);                                              \
             }
-            // for columns j >= 8 the first eight unknowns are zero (the inverse is lower triangular)
-            if ((vw & 1) == 0) {
-                KDA_SUBST_STEP(0) KDA_SUBST_STEP(1) KDA_SUBST_STEP(2) KDA_SUBST_STEP(3)
-                KDA_SUBST_STEP(4) KDA_SUBST_STEP(5) KDA_SUBST_STEP(6) KDA_SUBST_STEP(7)
+            if (!odd) {  // columns 0-3 from step 0, columns 12-15 from step 12
+                KDA_STEP_A(0) KDA_STEP_A(1) KDA_STEP_A(2) KDA_STEP_A(3) KDA_STEP_A(4) KDA_STEP_A(5)
+                KDA_STEP_A(6) KDA_STEP_A(7) KDA_STEP_A(8) KDA_STEP_A(9) KDA_STEP_A(10) KDA_STEP_A(11)
+                KDA_STEP_AB(12) KDA_STEP_AB(13) KDA_STEP_AB(14)
+            } else {     // columns 4-7 from step 4, columns 8-11 from step 8
+                KDA_STEP_A(4) KDA_STEP_A(5) KDA_STEP_A(6) KDA_STEP_A(7)
+                KDA_STEP_AB(8) KDA_STEP_AB(9) KDA_STEP_AB(10) KDA_STEP_AB(11) KDA_STEP_AB(12)
+                KDA_STEP_AB(13) KDA_STEP_AB(14)
             }
-            KDA_SUBST_STEP(8) KDA_SUBST_STEP(9) KDA_SUBST_STEP(10) KDA_SUBST_STEP(11)
-            KDA_SUBST_STEP(12) KDA_SUBST_STEP(13) KDA_SUBST_STEP(14)
-#undef KDA_SUBST_STEP
+#undef KDA_STEP_A
+#undef KDA_STEP_AB
             // T = X Diag(beta), as split bf16 in the tperm'd columns of T's tile
             const float ta = __builtin_fmaf(nbi, aa, da) * beta[o + ja];
             const float tb = __builtin_fmaf(nbi, ab, db) * beta[o + jb];
