@@ -44,7 +44,7 @@ kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const
     if (st != KDA_OK) return st;
     kda::Params p;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0; p.o = o; p.S_T = S_T;
-    p.B = desc->B; p.T = desc->T; p.H = desc->H; p.Dk = desc->Dk; p.Dv = desc->Dv;
+    p.B = desc->B; p.T = desc->T; p.H = desc->H; p.Dk = desc->Dk; p.Dv = desc->Dv; p.tstride = desc->T;
     p.scale = desc->scale;
     p.o_f32 = desc->o_dtype == KDA_F32;
     p.in_f32 = 0;

@@ -663,7 +663,7 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
         half = blockIdx.x & 1;
     }
     const int b = bh / p.H, h = bh - b * p.H;
-    const size_t row0 = (size_t)b * p.T * p.H + h;  // row of token 0: (b*T + t)*H + h = row0 + t*H
+    const size_t row0 = (size_t)b * p.tstride * p.H + h;  // row of token 0: (b*tstride + t)*H + h = row0 + t*H
     const int nchunk = (p.T + C - 1) / C;
 
     if (wave < NKW)

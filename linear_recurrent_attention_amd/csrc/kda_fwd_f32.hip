@@ -33,7 +33,7 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_f32_kernel(Params p) {
     const int tid = threadIdx.x;
     const int bh = blockIdx.x;
     const int b = bh / p.H, h = bh - b * p.H;
-    const size_t row0 = (size_t)b * p.T * p.H + h;  // (b*T + t)*H + h = row0 + t*H
+    const size_t row0 = (size_t)b * p.tstride * p.H + h;  // (b*tstride + t)*H + h = row0 + t*H
     const float* q = (const float*)p.q;
     const float* k = (const float*)p.k;
     const float* v = (const float*)p.v;

@@ -15,6 +15,7 @@ struct Params {
     void* o;
     float* S_T;        // may be null
     int B, T, H, Dk, Dv;
+    int tstride;       // tokens between consecutive batch rows of every [B, *, H, D] tensor (>= T)
     float scale;
     int o_f32;         // bf16 inputs with a float32 output
     int in_f32;        // matrix-core path with float32 q, k, v (and float32 output); layer use

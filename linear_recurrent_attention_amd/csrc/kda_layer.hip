@@ -309,7 +309,8 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
     // the core reads q, k, v in float32 (v straight from the projection output): rounding them to
     // bf16 first would be amplified by the per-head RMSNorm wherever a head's output is small
     p.q = W.q; p.k = W.k; p.v = W.pv; p.g = W.g; p.beta = W.beta; p.S0 = S0; p.o = W.o; p.S_T = S_T;
-    p.B = d->B; p.T = d->T; p.H = d->H; p.Dk = D; p.Dv = D; p.scale = d->scale; p.o_f32 = 1; p.in_f32 = 1; p.precise = 1;
+    p.B = d->B; p.T = d->T; p.tstride = d->T; p.H = d->H; p.Dk = D; p.Dv = D; p.scale = d->scale;
+    p.o_f32 = 1; p.in_f32 = 1; p.precise = 1;
     if (kda::launch_fwd_bf16(p, stream) != hipSuccess) return KDA_ERR_HIP;
 
     hipLaunchKernelGGL(epilogue_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, stream, M, d->H, HD, W.o, W.pg,

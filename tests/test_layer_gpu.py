@@ -82,3 +82,17 @@ def test_layer_workload4_full():
     y_ref, S_ref, _ = L.forward(x, p)
     assert rel_max_bf16_out(y, y_ref) <= TOL_BF16
     assert rel_max(ST, S_ref) <= TOL_BF16
+
+
+def test_layer_long_ragged_with_state_and_window():
+    """T = 1100 (35 chunks, the last one ragged; 35 prologue blocks), with S0 and an incoming
+    convolution window."""
+    x, p = small(7, B=2, T=1100)
+    rng = np.random.default_rng(8)
+    S0 = (rng.standard_normal((2, 2, 128, 128)) * 0.3).astype(np.float32)
+    cs0 = rng.standard_normal((2, 3, 2 * 256)).astype(np.float32)
+    y_ref, S_ref, cs_ref = L.forward(x, p, S0=S0, conv_state=cs0)
+    y, ST, cs = run(x, p, S0=S0, cs=cs0)
+    assert rel_max_bf16_out(y, y_ref) <= TOL_BF16
+    assert rel_max(ST, S_ref) <= TOL_BF16
+    np.testing.assert_allclose(cs, cs_ref, rtol=1e-5, atol=1e-5)
