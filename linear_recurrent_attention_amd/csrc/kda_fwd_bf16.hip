@@ -58,6 +58,7 @@ constexpr int LDK = DK + 8; // padded row (16-bit elements) of token-major [C][D
 constexpr int LDT = C + 8;  // padded row of channel-major [D][C] tiles
 constexpr int LDA = C + 8;  // [C][C] 16-bit tiles
 constexpr int LDF = C + 4;  // [C][C] float tiles
+constexpr int LDQ = 2 * NKW + 4;  // padded row of the quad-sum table (16-byte reads hit distinct banks)
 
 // Matrix-core operand order.  A 16x16x32 product takes, in lane group g (lanes 16g..16g+15), the
 // eight contraction indices 8g..8g+7.  Accumulator registers hold rows 4g..4g+3 of a 16-row block,
@@ -73,7 +74,8 @@ struct alignas(16) KeyTiles {                // written and read by the key wave
     uint16_t qmh[C][LDK], qml[C][LDK];       // Q * exp(b - b_15)       split bf16
     uint16_t km[C][LDK];                     // K * exp(b - b_15)       bf16
     uint16_t khh[C][LDK], khl[C][LDK];       // K * exp(b_15 - b)       split bf16
-    float tot[NKW][DK];                      // per-quad sums of g (log decay)
+    float tot[DK / 2][LDQ];                  // per-quad sums of g (log decay): row = channel pair,
+                                             // element 2*quad + (channel & 1)
 };
 struct alignas(16) Handoff2 {                // key -> value, double buffered by chunk parity
     uint16_t qg[C][LDK];                     // Q * Gamma                 f16, channels cperm'd
@@ -102,7 +104,7 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_c
 // Lane M of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
 template <int M>
 __device__ __forceinline__ float row_bcast(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + M, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + M, 0xf, 0xf, true));
 }
 // Low 16-bit halves of a and b as one word (a's in the low half); likewise the high halves.
 __device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
@@ -234,7 +236,7 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) { a0 += cur.g[i][0]; a1 += cur.g[i][1]; }
-        *reinterpret_cast<float2*>(&sm.key.tot[kw][c0]) = make_float2(a0, a1);
+        *reinterpret_cast<float2*>(&sm.key.tot[lane][2 * kw]) = make_float2(a0, a1);
         if (n + 1 < nchunk) load_chunk(nxt, p, kl, row0, t0 + C);  // prefetch the next chunk
     }
     if (n >= 1) {
@@ -272,25 +274,31 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
     if (work) {
         float tt0[NKW], tt1[NKW];
 #pragma unroll
-        for (int o = 0; o < NKW; ++o) {
-            const float2 t = *reinterpret_cast<const float2*>(&sm.key.tot[o][c0]);
-            tt0[o] = t.x; tt1[o] = t.y;
+        for (int o = 0; o < NKW; o += 2) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(&sm.key.tot[lane][2 * o]);
+            tt0[o] = t[0]; tt1[o] = t[1]; tt0[o + 1] = t[2]; tt1[o + 1] = t[3];
         }
         // p = b at token 15 (the reference), q = b at token 31 minus p, and o = b at the token before
-        // this quad minus p: a signed sum of quad totals with wave-uniform coefficients
-        float p0 = 0.f, p1 = 0.f, q0 = 0.f, q1 = 0.f, o0 = 0.f, o1 = 0.f;
-#pragma unroll
-        for (int o = 0; o < NKW; ++o) {
-            if (o < NKW / 2) { p0 += tt0[o]; p1 += tt1[o]; }
-            else { q0 += tt0[o]; q1 += tt1[o]; }
-            const float w = (o < kw ? 1.f : 0.f) - (o < NKW / 2 ? 1.f : 0.f);
-            o0 = __builtin_fmaf(w, tt0[o], o0);
-            o1 = __builtin_fmaf(w, tt1[o], o1);
+        // this quad minus p, from pair sums of the quad totals (kw is wave-uniform: no divergence)
+        const float s01a = tt0[0] + tt0[1], s23a = tt0[2] + tt0[3], s45a = tt0[4] + tt0[5], s67a = tt0[6] + tt0[7];
+        const float s01b = tt1[0] + tt1[1], s23b = tt1[2] + tt1[3], s45b = tt1[4] + tt1[5], s67b = tt1[6] + tt1[7];
+        const float p0 = s01a + s23a, p1 = s01b + s23b, q0 = s45a + s67a, q1 = s45b + s67b;
+        float o0, o1;
+        static_assert(NKW == 8, "pair sums below assume eight quads");
+        switch (kw) {
+            case 0: o0 = -p0; o1 = -p1; break;
+            case 1: o0 = -(tt0[1] + s23a); o1 = -(tt1[1] + s23b); break;
+            case 2: o0 = -s23a; o1 = -s23b; break;
+            case 3: o0 = -tt0[3]; o1 = -tt1[3]; break;
+            case 4: o0 = 0.f; o1 = 0.f; break;
+            case 5: o0 = tt0[4]; o1 = tt1[4]; break;
+            case 6: o0 = s45a; o1 = s45b; break;
+            default: o0 = s45a + tt0[6]; o1 = s45b + tt1[6]; break;
         }
         o0 *= kLog2e; o1 *= kLog2e;
         cy.eP[0] = fexp(p0); cy.eP[1] = fexp(p1);
         cy.eC[0] = fexp(q0); cy.eC[1] = fexp(q1);
-        cy.gam[0] = fexp(p0 + q0); cy.gam[1] = fexp(p1 + q1);
+        cy.gam[0] = cy.eP[0] * cy.eC[0]; cy.gam[1] = cy.eP[1] * cy.eC[1];
         uint32_t wqh[TPW], wql[TPW], wkm[TPW], wkh[TPW], wkl[TPW];
         float y0 = o0, y1 = o1;
 #pragma unroll
@@ -319,6 +327,8 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khh[tq + i][c0]) = wkh[i];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khl[tq + i][c0]) = wkl[i];
+        // beta of this chunk (the value waves read the previous chunk's before barrier 1)
+        if (lane < TPW) sm.h1.beta[TPW * kw + lane] = cur.beta;
     }
     lds_barrier();  // ---- barrier 2
 
@@ -368,11 +378,14 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
                     acc2 = mfma_bf16(a1, ld16(&sm.key.khl[SUB + l16][kc]), acc2);
                 }
             }
+            // the diagonal blocks as -Diag(beta) L, the form the substitution uses
+            const f32x4 nb0 = -*reinterpret_cast<const f32x4*>(&sm.h1.beta[4 * g4]);
+            const f32x4 nb1 = -*reinterpret_cast<const f32x4*>(&sm.h1.beta[SUB + 4 * g4]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 4 * g4 + r;
-                sm.h1.lf[i][l16] = (l16 >= i) ? 0.f : acc0[r];  // strictly lower
-                sm.h1.lf[SUB + i][SUB + l16] = (l16 >= i) ? 0.f : acc2[r];
+                sm.h1.lf[i][l16] = (l16 >= i) ? 0.f : nb0[r] * acc0[r];  // strictly lower
+                sm.h1.lf[SUB + i][SUB + l16] = (l16 >= i) ? 0.f : nb1[r] * acc2[r];
                 // L(1,0) as a split-bf16 operand, in the block of the T tile that T itself leaves unused
                 const uint32_t hi = pack_bf16(acc1[r], 0.f);
                 sm.val.th[SUB + i][tperm(l16)] = hi & 0xffffu;
@@ -388,7 +401,6 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
                 *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane + 1][pt]) = u32x2{perm_hi(v[0], v[1]), perm_hi(v[2], v[3])};
             }
         }
-        if (lane < TPW) sm.h1.beta[TPW * kw + lane] = cur.beta;
     }
     lds_barrier();  // ---- barrier 3
 }
@@ -480,49 +492,41 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
         // ---------------- part 1: UT inverse of the two diagonal blocks, spread over the value waves
         // Wave vw solves two columns ja, jb of block vw >> 1 of (I + Diag(beta) L) X = I per 16-lane row
         // g4: ja = g4, jb = 12 + g4 (even vw) or ja = 4 + g4, jb = 8 + g4 (odd vw); lane l16 holds matrix
-        // row i = l16.  Forward substitution: at step m every lane forms its candidate
-        // x_i = [i == j] - beta_i acc_i, row m's (final) candidate is broadcast along the 16-lane row, and
-        // rows below take acc_i += L[i][m] x_m (L is zero on and above the diagonal).  Column j needs
-        // steps m >= j only (the unknowns above row j are zero), which the column pairing balances.
+        // row i = l16 of N = -Diag(beta) L.  With x_i = [i == j] + y_i, forward substitution reads
+        // y = N e_j + N y: y starts as column j of N, and at step m row m's (final) y_m is broadcast along
+        // the 16-lane row and rows below take y_i += N[i][m] y_m.  Rows at or above j keep y = 0, so
+        // column j needs steps m > j only, which the column pairing balances.
         if (work) {
             const float* beta = sm.h1.beta;
             const bool odd = vw & 1;
             const int o = SUB * (vw >> 1), i = l16, ja = (odd ? 4 : 0) + g4, jb = (odd ? 8 : 12) + g4;
-            float Lr[SUB];
+            float Nr[SUB];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const f32x4 t = *reinterpret_cast<const f32x4*>(&sm.h1.lf[o + i][o + 4 * q4]);
-                Lr[4 * q4] = t[0]; Lr[4 * q4 + 1] = t[1]; Lr[4 * q4 + 2] = t[2]; Lr[4 * q4 + 3] = t[3];
+                Nr[4 * q4] = t[0]; Nr[4 * q4 + 1] = t[1]; Nr[4 * q4 + 2] = t[2]; Nr[4 * q4 + 3] = t[3];
             }
-            const float nbi = -beta[o + i];
-            const float da = i == ja ? 1.f : 0.f, db = i == jb ? 1.f : 0.f;
-            float aa = 0.f, ab = 0.f;
-#define KDA_STEP_A(m)                                                                            \
-            {                                                                                    \
-                const float xa = row_bcast<m>(__builtin_fmaf(nbi, aa, da));                      \
-                aa = __builtin_fmaf(Lr[m], xa, aa);                                              \
-            }
+            float ya = sm.h1.lf[o + i][o + ja], yb = sm.h1.lf[o + i][o + jb];
+#define KDA_STEP_A(m) ya = __builtin_fmaf(Nr[m], row_bcast<m>(ya), ya);
 #define KDA_STEP_AB(m)                                                                           \
             {                                                                                    \
-                const float xa = row_bcast<m>(__builtin_fmaf(nbi, aa, da));                      \
-                const float xb = row_bcast<m>(__builtin_fmaf(nbi, ab, db));                      \
-                aa = __builtin_fmaf(Lr[m], xa, aa);                                              \
-                ab = __builtin_fmaf(Lr[m], xb, ab);                                              \
+                const float xa = row_bcast<m>(ya), xb = row_bcast<m>(yb);                        \
+                ya = __builtin_fmaf(Nr[m], xa, ya);                                              \
+                yb = __builtin_fmaf(Nr[m], xb, yb);                                              \
             }
-            if (!odd) {  // columns 0-3 from step 0, columns 12-15 from step 12
-                KDA_STEP_A(0) KDA_STEP_A(1) KDA_STEP_A(2) KDA_STEP_A(3) KDA_STEP_A(4) KDA_STEP_A(5)
-                KDA_STEP_A(6) KDA_STEP_A(7) KDA_STEP_A(8) KDA_STEP_A(9) KDA_STEP_A(10) KDA_STEP_A(11)
-                KDA_STEP_AB(12) KDA_STEP_AB(13) KDA_STEP_AB(14)
-            } else {     // columns 4-7 from step 4, columns 8-11 from step 8
-                KDA_STEP_A(4) KDA_STEP_A(5) KDA_STEP_A(6) KDA_STEP_A(7)
-                KDA_STEP_AB(8) KDA_STEP_AB(9) KDA_STEP_AB(10) KDA_STEP_AB(11) KDA_STEP_AB(12)
+            if (!odd) {  // columns 0-3 from step 1, columns 12-15 from step 13
+                KDA_STEP_A(1) KDA_STEP_A(2) KDA_STEP_A(3) KDA_STEP_A(4) KDA_STEP_A(5) KDA_STEP_A(6)
+                KDA_STEP_A(7) KDA_STEP_A(8) KDA_STEP_A(9) KDA_STEP_A(10) KDA_STEP_A(11) KDA_STEP_A(12)
                 KDA_STEP_AB(13) KDA_STEP_AB(14)
+            } else {     // columns 4-7 from step 5, columns 8-11 from step 9
+                KDA_STEP_A(5) KDA_STEP_A(6) KDA_STEP_A(7) KDA_STEP_A(8)
+                KDA_STEP_AB(9) KDA_STEP_AB(10) KDA_STEP_AB(11) KDA_STEP_AB(12) KDA_STEP_AB(13) KDA_STEP_AB(14)
             }
 #undef KDA_STEP_A
 #undef KDA_STEP_AB
             // T = X Diag(beta), as split bf16 in the tperm'd columns of T's tile
-            const float ta = __builtin_fmaf(nbi, aa, da) * beta[o + ja];
-            const float tb = __builtin_fmaf(nbi, ab, db) * beta[o + jb];
+            const float ta = ((i == ja ? 1.f : 0.f) + ya) * beta[o + ja];
+            const float tb = ((i == jb ? 1.f : 0.f) + yb) * beta[o + jb];
             uint32_t hi, lo;
             split_bf16(ta, tb, hi, lo);
             V.th[o + i][tperm(o + ja)] = hi & 0xffffu;
