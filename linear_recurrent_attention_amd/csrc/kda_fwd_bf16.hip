@@ -159,9 +159,12 @@ __device__ __forceinline__ void gstore(gchar* base, uint32_t off, Tv v) {
 // Tokens t0 + TPW*kw + i: key channels 2*lane, 2*lane+1; value columns half*64 + 2*(lane & 31) (+1);
 // beta of token t0 + TPW*kw + (lane % TPW).  Tokens past the end read the last valid row; mask_tail()
 // zeroes them when the chunk is consumed.  Nothing here uses the loaded values, so the loads stay
-// in flight until their first use one step later.  Requires T >= 1 and t0 < T.
-template <bool IN_F32>
+// in flight until their first use in the next step.  Requires T >= 1 and t0 < T.
+// PART selects what is loaded: LOAD_ALL, LOAD_GVB (decays, values, beta) or LOAD_QK (queries, keys).
+enum { LOAD_ALL = 3, LOAD_GVB = 1, LOAD_QK = 2 };
+template <int PART, bool IN_F32>
 __device__ __forceinline__ void load_chunk(Raw<IN_F32>& r, const Params& p, const KeyLoad& kl, size_t row0, int t0) {
+    constexpr bool LG = PART & LOAD_GVB, LQ = PART & LOAD_QK;
     const size_t ce = (row0 + (size_t)t0 * p.H) * DK;  // element offset of the chunk's first row
     constexpr uint32_t qs = IN_F32 ? 2 : 1;            // q/k byte offsets scale with the element size
     const gchar* qc = uniform_gptr((const char*)p.q + ce * 2 * qs);
@@ -173,24 +176,24 @@ __device__ __forceinline__ void load_chunk(Raw<IN_F32>& r, const Params& p, cons
     if (t0 + C <= p.T) {
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-            r.q[i] = gload<QT>(qc, qs * kl.off[i]);
-            r.k[i] = gload<QT>(kc, qs * kl.off[i]);
-            r.g[i] = gload<f32x2>(gc, 2 * kl.off[i]);
-            if constexpr (!IN_F32) r.v[i] = gload<uint32_t>(vc, kl.voff[i]);
+            if constexpr (LQ) r.q[i] = gload<QT>(qc, qs * kl.off[i]);
+            if constexpr (LQ) r.k[i] = gload<QT>(kc, qs * kl.off[i]);
+            if constexpr (LG) r.g[i] = gload<f32x2>(gc, 2 * kl.off[i]);
+            if constexpr (LG && !IN_F32) r.v[i] = gload<uint32_t>(vc, kl.voff[i]);
         }
-        r.beta = gload<float>(bc, kl.boff);
+        if constexpr (LG) r.beta = gload<float>(bc, kl.boff);
     } else {
         const int lim = p.T - 1 - t0;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const uint32_t tb = (uint32_t)min(TPW * kl.kw + i, lim) * kl.tok_b;
             const uint32_t o = tb + kl.lane_b, ov = tb + kl.vlane_b;  // both non-negative, < 2^31
-            r.q[i] = gload<QT>(qc, qs * o);
-            r.k[i] = gload<QT>(kc, qs * o);
-            r.g[i] = gload<f32x2>(gc, 2 * o);
-            if constexpr (!IN_F32) r.v[i] = gload<uint32_t>(vc, ov);
+            if constexpr (LQ) r.q[i] = gload<QT>(qc, qs * o);
+            if constexpr (LQ) r.k[i] = gload<QT>(kc, qs * o);
+            if constexpr (LG) r.g[i] = gload<f32x2>(gc, 2 * o);
+            if constexpr (LG && !IN_F32) r.v[i] = gload<uint32_t>(vc, ov);
         }
-        r.beta = gload<float>(bc, (uint32_t)min(TPW * kl.kw + (kl.lane % TPW), lim) * 4u * p.H);
+        if constexpr (LG) r.beta = gload<float>(bc, (uint32_t)min(TPW * kl.kw + (kl.lane % TPW), lim) * 4u * p.H);
     }
 }
 
@@ -237,7 +240,7 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
 #pragma unroll
         for (int i = 0; i < TPW; ++i) { a0 += cur.g[i][0]; a1 += cur.g[i][1]; }
         *reinterpret_cast<float2*>(&sm.key.tot[lane][2 * kw]) = make_float2(a0, a1);
-        if (n + 1 < nchunk) load_chunk(nxt, p, kl, row0, t0 + C);  // prefetch the next chunk
+        if (n + 1 < nchunk) load_chunk<LOAD_GVB>(nxt, p, kl, row0, t0 + C);  // part of the next chunk
     }
     if (n >= 1) {
         Handoff2& Hp = sm.h2[(n - 1) & 1];
@@ -334,6 +337,9 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
 
     // ---------------- part 3: Gram products, and the inputs the value waves read next step
     if (work) {
+        // the rest of the next chunk (first read in part 2 of the next step), issued here so that the
+        // loads are spread over the step rather than queued all at once
+        if (n + 1 < nchunk) load_chunk<LOAD_QK>(nxt, p, kl, row0, t0 + C);
         if (kw < 3) {
             // A(0,0), A(1,0), A(1,1): split bf16 with three independent accumulators
             const int R = kw == 0 ? 0 : 1, S = kw == 2 ? 1 : 0;
@@ -427,7 +433,7 @@ __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int half, int 
     kl.boff = (uint32_t)(TPW * kw + (lane % TPW)) * 4u * p.H;
     Raw<IN_F32> ra, rb;
     Carry cy;
-    if (p.T > 0) load_chunk(ra, p, kl, row0, 0);
+    if (p.T > 0) load_chunk<LOAD_ALL>(ra, p, kl, row0, 0);
     // two steps per iteration so the prefetch target alternates between two register sets
     for (int n = 0; n <= nchunk; n += 2) {
         key_step<IN_F32, HP>(sm, p, kl, row0, n, nchunk, ra, rb, cy);
