@@ -85,6 +85,24 @@ kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const
                    const float* g, const float* beta, const float* S0,
                    void* o, float* S_T, hipStream_t stream);
 
+/*
+ * kda_fwd_ckpt -- kda_fwd that also records the state at regular token boundaries: the KDA half of
+ * the prefix cache of the explainer page, section 13.9, where a cached prefix can be resumed only
+ * at a boundary that holds a state checkpoint (the page places them every 512 tokens, its hash-block
+ * size).
+ *   every  : tokens between checkpoints; a positive multiple of the chunk (32 for bf16 I/O, 16 for
+ *            float32 I/O)
+ *   S_ckpt : [B, H, n_ckpt, Dk, Dv] float32 with n_ckpt = T / every (rounded down).  Entry m of
+ *            sequence (b, h) is the state after its tokens [0, (m+1)*every): the S0 that resumes the
+ *            sequence at token (m+1)*every.  Resuming there with kda_fwd reproduces the remaining
+ *            outputs and S_T of the uninterrupted call bit for bit.  May be NULL only when n_ckpt = 0;
+ *            must not alias any other argument; 8-byte aligned.
+ * Every other argument and the return codes are those of kda_fwd.
+ */
+kda_status kda_fwd_ckpt(const kda_fwd_desc* desc, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* S0,
+                        void* o, float* S_T, float* S_ckpt, int every, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Fused layer forward.  The layer of the explainer page "Kimi K3：开放前沿智能":
  *   section 2.4 (paper Eq. 2): q, k = L2norm(Swish(ShortConv(x W))); v = x W_v;

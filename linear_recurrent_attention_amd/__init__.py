@@ -10,7 +10,7 @@ import torch
 from . import _lib
 from ._lib import KdaError  # noqa: F401
 
-__all__ = ["kda_fwd", "kda_layer_fwd", "KdaError"]
+__all__ = ["kda_fwd", "kda_fwd_ckpt", "kda_layer_fwd", "KdaError"]
 
 _DT = {torch.float32: _lib.KDA_F32, torch.bfloat16: _lib.KDA_BF16}
 
@@ -23,14 +23,7 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def kda_fwd(q, k, v, g, beta, S0=None, scale: float = 1.0, o_dtype=None, want_state: bool = True,
-            out=None, state_out=None, chunk: int = 0, precise: bool = False):
-    """Gated delta rule forward.  Shapes: q, k, g [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H];
-    S0 [B,H,Dk,Dv] float32 or None.  q, k, v float32 or bfloat16; g, beta float32.
-    precise: split-bf16 key Gram matrix and state update on the bf16 path (KDA_FWD_PRECISE).
-
-    Returns (o [B,T,H,Dv], S_T [B,H,Dk,Dv] float32 or None).
-    """
+def _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, chunk, precise, scale):
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     for t in (q, k, v, g, beta):
@@ -52,10 +45,38 @@ def kda_fwd(q, k, v, g, beta, S0=None, scale: float = 1.0, o_dtype=None, want_st
                                                                  device=q.device)
     desc = _lib.FwdDesc(B, T, H, Dk, Dv, chunk, _DT[q.dtype], _DT[o_dtype], float(scale),
                         _lib.KDA_FWD_PRECISE if precise else 0)
+    return desc, o, ST
+
+
+def kda_fwd(q, k, v, g, beta, S0=None, scale: float = 1.0, o_dtype=None, want_state: bool = True,
+            out=None, state_out=None, chunk: int = 0, precise: bool = False):
+    """Gated delta rule forward.  Shapes: q, k, g [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H];
+    S0 [B,H,Dk,Dv] float32 or None.  q, k, v float32 or bfloat16; g, beta float32.
+    precise: split-bf16 key Gram matrix and state update on the bf16 path (KDA_FWD_PRECISE).
+
+    Returns (o [B,T,H,Dv], S_T [B,H,Dk,Dv] float32 or None).
+    """
+    desc, o, ST = _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, chunk, precise, scale)
     code = _lib.fwd_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(ST),
                         _stream(q.device))
     _lib.check(code)
     return o, ST
+
+
+def kda_fwd_ckpt(q, k, v, g, beta, every: int, S0=None, scale: float = 1.0, o_dtype=None,
+                 want_state: bool = True, chunk: int = 0, precise: bool = False):
+    """kda_fwd that also returns state checkpoints: S_ckpt [B,H,T//every,Dk,Dv] float32, entry m being
+    the state after tokens [0, (m+1)*every) (the S0 that resumes the sequence there).
+
+    Returns (o, S_T, S_ckpt)."""
+    desc, o, ST = _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, None, None, chunk, precise, scale)
+    B, T, H, Dk = q.shape
+    n = T // every if every > 0 else 0
+    ck = torch.empty((B, H, n, Dk, v.shape[-1]), dtype=torch.float32, device=q.device)
+    code = _lib.fwd_ckpt_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(ST),
+                             _ptr(ck) if n > 0 else 0, int(every), _stream(q.device))
+    _lib.check(code)
+    return o, ST, ck
 
 
 def kda_layer_fwd(x, weights: dict, S0=None, conv_state=None, scale: float = 1.0, want_state: bool = True,

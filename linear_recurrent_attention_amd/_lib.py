@@ -18,7 +18,7 @@ KDA_BF16 = 1
 KDA_FWD_PRECISE = 1  # kda_fwd_desc.flags
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_fwd", "kda_layer_workspace_size", "kda_layer_fwd", "kda_error_string", "kda_version")
+EXPORTS = ("kda_fwd", "kda_fwd_ckpt", "kda_layer_workspace_size", "kda_layer_fwd", "kda_error_string", "kda_version")
 
 
 class FwdDesc(ctypes.Structure):
@@ -66,6 +66,9 @@ def lib():
             L = ctypes.CDLL(LIB_PATH)
             L.kda_fwd.restype = ctypes.c_int
             L.kda_fwd.argtypes = [ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 9
+            L.kda_fwd_ckpt.restype = ctypes.c_int
+            L.kda_fwd_ckpt.argtypes = ([ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 9 + [ctypes.c_int] +
+                                       [ctypes.c_void_p])
             L.kda_layer_workspace_size.restype = ctypes.c_size_t
             L.kda_layer_workspace_size.argtypes = [ctypes.POINTER(LayerDesc)]
             L.kda_layer_fwd.restype = ctypes.c_int
@@ -98,3 +101,8 @@ def layer_fwd_raw(desc: LayerDesc, x, weights: LayerWeights, S0, conv_in, y, S_T
 def fwd_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, stream) -> int:
     """Call kda_fwd with integer device addresses (0 = NULL); returns the status code."""
     return lib().kda_fwd(ctypes.byref(desc), q, k, v, g, beta, S0, o, S_T, stream)
+
+
+def fwd_ckpt_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, S_ckpt, every, stream) -> int:
+    """Call kda_fwd_ckpt with integer device addresses (0 = NULL); returns the status code."""
+    return lib().kda_fwd_ckpt(ctypes.byref(desc), q, k, v, g, beta, S0, o, S_T, S_ckpt, every, stream)

@@ -34,15 +34,15 @@ kda_status check_fwd(const kda_fwd_desc* d, const void* q, const void* k, const 
     return KDA_OK;
 }
 
-}  // namespace
+int chunk_of(const kda_fwd_desc* d) { return d->io_dtype == KDA_BF16 ? 32 : 16; }
 
-extern "C" {
-
-kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
-                   const float* beta, const float* S0, void* o, float* S_T, hipStream_t stream) {
-    const kda_status st = check_fwd(desc, q, k, v, g, beta, S0, o, S_T);
-    if (st != KDA_OK) return st;
+kda_status run_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, const float* S0, void* o, float* S_T, float* S_ckpt, int every,
+                   hipStream_t stream) {
     kda::Params p;
+    p.S_ckpt = S_ckpt;
+    p.ckpt_chunks = S_ckpt ? every / chunk_of(desc) : 1;
+    p.n_ckpt = S_ckpt ? desc->T / every : 0;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0; p.o = o; p.S_T = S_T;
     p.B = desc->B; p.T = desc->T; p.H = desc->H; p.Dk = desc->Dk; p.Dv = desc->Dv; p.tstride = desc->T;
     p.scale = desc->scale;
@@ -57,6 +57,30 @@ kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const
     else
         e = kda::launch_fwd_f32(p, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, const float* S0, void* o, float* S_T, hipStream_t stream) {
+    const kda_status st = check_fwd(desc, q, k, v, g, beta, S0, o, S_T);
+    if (st != KDA_OK) return st;
+    return run_fwd(desc, q, k, v, g, beta, S0, o, S_T, nullptr, 0, stream);
+}
+
+kda_status kda_fwd_ckpt(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* S0, void* o, float* S_T, float* S_ckpt, int every,
+                        hipStream_t stream) {
+    const kda_status st = check_fwd(desc, q, k, v, g, beta, S0, o, S_T);
+    if (st != KDA_OK) return st;
+    if (every <= 0 || every % chunk_of(desc) != 0) return KDA_ERR_INVALID_ARG;
+    const int n_ckpt = desc->T / every;
+    if (n_ckpt > 0 && !S_ckpt) return KDA_ERR_INVALID_ARG;
+    if (!aligned(S_ckpt, 8)) return KDA_ERR_INVALID_ARG;
+    if (S_ckpt && ((const void*)S_ckpt == o || S_ckpt == S_T || S_ckpt == S0)) return KDA_ERR_INVALID_ARG;
+    return run_fwd(desc, q, k, v, g, beta, S0, o, S_T, n_ckpt > 0 ? S_ckpt : nullptr, every, stream);
 }
 
 const char* kda_error_string(kda_status s) {

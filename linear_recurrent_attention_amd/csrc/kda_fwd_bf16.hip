@@ -444,7 +444,7 @@ __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int half, int 
 // ------------------------------------------------------------------------------------------------
 // value waves: one step = chunk n-1 (nothing when n == 0); three barriers
 // ------------------------------------------------------------------------------------------------
-template <bool OUT_F32, bool IN_F32, bool HP>
+template <bool OUT_F32, bool IN_F32, bool HP, bool CKPT>
 __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int half, int vw, int lane, int nchunk) {
     const int l16 = lane & 15, g4 = lane >> 4;
     ValueTiles& V = sm.val;
@@ -640,6 +640,14 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
                 }
             }
             make_sb();
+            if (CKPT && n % p.ckpt_chunks == 0 && n / p.ckpt_chunks <= p.n_ckpt) {
+                // the state after tokens [0, n*C): checkpoint n / ckpt_chunks - 1
+                float* dst = p.S_ckpt + ((size_t)bh * p.n_ckpt + (n / p.ckpt_chunks - 1)) * DK * DV;
+#pragma unroll
+                for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * g4 + r) * DV + col] = st[cb][r];
+            }
         }
         lds_barrier();  // ---- barrier 3
     }
@@ -656,7 +664,8 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
     }
 }
 
-template <bool OUT_F32, bool IN_F32, bool HP>
+// CKPT: S_ckpt is set (a separate instantiation keeps the plain forward free of the checkpoint code)
+template <bool OUT_F32, bool IN_F32, bool HP, bool CKPT>
 __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
     __shared__ Smem sm;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -679,24 +688,34 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
     if (wave < NKW)
         key_waves<IN_F32, HP>(sm, p, row0, half, wave, lane, nchunk);
     else
-        value_waves<OUT_F32, IN_F32, HP>(sm, p, bh, row0, half, wave - NKW, lane, nchunk);
+        value_waves<OUT_F32, IN_F32, HP, CKPT>(sm, p, bh, row0, half, wave - NKW, lane, nchunk);
 }
 
+}  // namespace bf16path
+
+namespace bf16path {
+template <bool CKPT>
+void launch_bf16_io(const Params& p, hipStream_t stream, dim3 grid, dim3 block) {
+    if (p.o_f32 && p.precise)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, false, true, CKPT>), grid, block, 0, stream, p);
+    else if (p.o_f32)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, false, false, CKPT>), grid, block, 0, stream, p);
+    else if (p.precise)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, false, true, CKPT>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, false, false, CKPT>), grid, block, 0, stream, p);
+}
 }  // namespace bf16path
 
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t stream) {
     using namespace bf16path;
     const dim3 grid(2 * p.B * p.H), block(NTHR);
-    if (p.in_f32)
-        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, true, true>), grid, block, 0, stream, p);
-    else if (p.o_f32 && p.precise)
-        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, false, true>), grid, block, 0, stream, p);
-    else if (p.o_f32)
-        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, false, false>), grid, block, 0, stream, p);
-    else if (p.precise)
-        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, false, true>), grid, block, 0, stream, p);
+    if (p.in_f32)  // the layer's variant (it records no checkpoints)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, true, true, false>), grid, block, 0, stream, p);
+    else if (p.S_ckpt)
+        launch_bf16_io<true>(p, stream, grid, block);
     else
-        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, false, false>), grid, block, 0, stream, p);
+        launch_bf16_io<false>(p, stream, grid, block);
     return hipGetLastError();
 }
 

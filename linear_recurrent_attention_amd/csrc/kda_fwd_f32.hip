@@ -144,6 +144,11 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_f32_kernel(Params p) {
             for (int s = 0; s < C; ++s) acc += sm.kb[s][c] * sm.u[s][j];
             sm.S[c][j] = acc;
         }
+        if (p.S_ckpt && (ch + 1) % p.ckpt_chunks == 0 && (ch + 1) / p.ckpt_chunks <= p.n_ckpt) {
+            // the state after tokens [0, (ch+1)*C); each thread copies the entries it just wrote
+            float* dst = p.S_ckpt + ((size_t)bh * p.n_ckpt + ((ch + 1) / p.ckpt_chunks - 1)) * D * D;
+            for (int e = tid; e < D * D; e += NTHR) dst[e] = sm.S[e / D][e % D];
+        }
     }
     __syncthreads();
     if (p.S_T)

@@ -20,6 +20,9 @@ struct Params {
     int o_f32;         // bf16 inputs with a float32 output
     int in_f32;        // matrix-core path with float32 q, k, v (and float32 output); layer use
     int precise;       // matrix-core path: split-bf16 L and state update (always on with in_f32)
+    float* S_ckpt;     // may be null: [B, H, n_ckpt, Dk, Dv] states at every ckpt_chunks-th chunk boundary
+    int ckpt_chunks;   // chunks between checkpoints (>= 1 when S_ckpt is set)
+    int n_ckpt;        // checkpoints per sequence: full multiples of ckpt_chunks chunks within T
 };
 
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t stream);  // Dk = Dv = 128, chunk 32 (in_f32 too)

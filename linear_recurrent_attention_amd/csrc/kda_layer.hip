@@ -311,6 +311,7 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
     p.q = W.q; p.k = W.k; p.v = W.pv; p.g = W.g; p.beta = W.beta; p.S0 = S0; p.o = W.o; p.S_T = S_T;
     p.B = d->B; p.T = d->T; p.tstride = d->T; p.H = d->H; p.Dk = D; p.Dv = D; p.scale = d->scale;
     p.o_f32 = 1; p.in_f32 = 1; p.precise = 1;
+    p.S_ckpt = nullptr; p.ckpt_chunks = 1; p.n_ckpt = 0;
     if (kda::launch_fwd_bf16(p, stream) != hipSuccess) return KDA_ERR_HIP;
 
     hipLaunchKernelGGL(epilogue_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, stream, M, d->H, HD, W.o, W.pg,

@@ -108,3 +108,37 @@ def test_python_binding_checks_shapes():
     q = torch.zeros(1, 4, 2, 128)
     with pytest.raises(ValueError):
         kda.kda_fwd(q, q, q, q, torch.zeros(1, 4, 2))  # CPU tensors are rejected before any call
+
+
+def call_ckpt(d, every, S_ckpt=FAKE + 0x200000, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=0, o=FAKE + 0x100000, S_T=0)
+    a.update(kw)
+    return _lib.fwd_ckpt_raw(d, a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["o"], a["S_T"], S_ckpt,
+                             every, None)
+
+
+@pytest.mark.parametrize("every", [0, -32, 16, 48, 33])
+def test_checkpoint_interval_must_be_a_chunk_multiple(every):
+    # bf16 I/O runs 32-token chunks
+    assert call_ckpt(desc(), every) == _lib.KDA_ERR_INVALID_ARG
+
+
+def test_checkpoint_interval_f32_chunk():
+    # float32 I/O runs 16-token chunks: 48 is valid (T = 0: nothing launched), 24 is not
+    d = desc(T=0, io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_F32, Dk=64, Dv=64)
+    assert _lib.fwd_ckpt_raw(d, 0, 0, 0, 0, 0, 0, 0, 0, 0, 48, None) == _lib.KDA_OK
+    assert _lib.fwd_ckpt_raw(d, 0, 0, 0, 0, 0, 0, 0, 0, 0, 24, None) == _lib.KDA_ERR_INVALID_ARG
+
+
+def test_checkpoint_buffer_required_when_any_checkpoint_falls_in_range():
+    assert call_ckpt(desc(T=64), 64, S_ckpt=0) == _lib.KDA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(S_ckpt=FAKE + 0x100000), dict(S_ckpt=FAKE + 0x200004)])
+def test_checkpoint_buffer_aliasing_or_misaligned(kw):
+    assert call_ckpt(desc(T=64), 32, **kw) == _lib.KDA_ERR_INVALID_ARG
+
+
+def test_checkpoint_call_validates_the_descriptor_first():
+    assert call_ckpt(desc(B=0), 32) == _lib.KDA_ERR_INVALID_ARG
+    assert call_ckpt(desc(Dk=64, Dv=64), 32) == _lib.KDA_ERR_UNSUPPORTED
