@@ -73,6 +73,77 @@ def cpu_baseline(d, threads):
                       f"{dt:.1f} s wall on {threads} threads)"}
 
 
+def time_steps(torch, step, stream, args):
+    """W untimed warmup steps, then K steps between synchronisations, each bracketed by HIP events on
+    the launch stream.  Returns (wall seconds for the K steps, per-step event milliseconds)."""
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        stream.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            step()
+            b.record(stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def decode_bytes(B, H, D, T=1, io_bytes=2):
+    """HBM bytes of one kda_decode call: the float32 state read and written once, plus q, k, v, o (io
+    dtype), g and beta (float32) of each token."""
+    return B * H * (2 * D * D * 4 + T * ((4 * D) * io_bytes + 4 * D + 4))
+
+
+def bench_decode(args, torch, synth, kda):
+    """kda_decode on B=128 sequences x H=32 heads, one new token each (D=128, bf16 q/k/v/o), with the
+    state updated in place: tokens/s and HBM roofline (state read + write dominates)."""
+    w = synth.DECODE
+    B, H, D, T = w["B"], w["H"], w["D"], w["T"]
+    d, S0 = synth.decode_inputs(seed=0)
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v", "g", "beta")}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(torch.bfloat16)
+    S = torch.from_numpy(S0).to(dev)
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step():  # the in-place update of a serving loop (the state keeps evolving across steps)
+        kda.kda_decode(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=S, out=o, state_out=S)
+
+    wall, launch_ms = time_steps(torch, step, stream, args)
+    avg_s = float(np.mean(launch_ms)) / 1e3
+    abytes = decode_bytes(B, H, D, T)
+    gbs = abytes / avg_s / 1e9
+    out = {
+        "metric": "KDA decode tokens/s (B128 H32 D128, one token per sequence, state in place)",
+        "value": B * T / (wall / args.steps), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w["name"], "B": B, "H": H, "T": T, "D": D,
+                   "io": "bf16 q/k/v/o, float32 g/beta/state"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "kda_decode_kernel",
+                     "avg_launch_ms": avg_s * 1e3, "algorithmic_bytes": abytes},
+    }
+    if not args.no_cpu:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        tc = time.perf_counter()
+        oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=S0, threads=threads)
+        dt = time.perf_counter() - tc
+        out["cpu_baseline"] = {"value": B * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"the whole decode workload ({B * H} heads, one token; float64 token "
+                                         f"recurrence, {dt:.3f} s wall on {threads} threads)"}
+    print(json.dumps(out), flush=True)
+
+
 def layer_flops(B, T, d, H, D, R):
     """Matrix-product flops of one fused-layer call: the q, k, v, gate and output projections, beta,
     the rank-R decay projection, and the chunkwise core (as algorithmic_flops)."""
@@ -144,9 +215,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run one plain 512 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=("core", "layer"), default="core",
+    ap.add_argument("--workload", choices=("core", "layer", "decode"), default="core",
                     help="core: kda_fwd on B4 H32 T16384 (the headline line); layer: kda_layer_fwd on "
-                         "B2 T8192 d_model 2048 H16 (a second, separate line)")
+                         "B2 T8192 d_model 2048 H16; decode: kda_decode on B128 H32, one token (separate lines)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus N with N > 1 is not supported "
@@ -159,6 +230,9 @@ def main():
 
     if args.workload == "layer":
         bench_layer(args, torch, synth, kda)
+        return
+    if args.workload == "decode":
+        bench_decode(args, torch, synth, kda)
         return
     w = synth.WORKLOADS[WORKLOAD]
     B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
@@ -174,22 +248,7 @@ def main():
     def step():
         kda.kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], out=o, state_out=ST)
 
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            step()
-        stream.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for a, b in ev:
-            a.record(stream)
-            step()
-            b.record(stream)
-        stream.synchronize()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t_start
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    wall, launch_ms = time_steps(torch, step, stream, args)
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

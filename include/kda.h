@@ -103,6 +103,22 @@ kda_status kda_fwd_ckpt(const kda_fwd_desc* desc, const void* q, const void* k, 
                         const float* g, const float* beta, const float* S0,
                         void* o, float* S_T, float* S_ckpt, int every, hipStream_t stream);
 
+/*
+ * kda_decode -- the same operation as kda_fwd, evaluated token by token (no chunking): the decode
+ * step of the explainer page, section 13.10 (state update and readout of each newly generated
+ * token; the projections around it are the caller's).  For a few tokens per call; its cost is one
+ * read and one write of the float32 state per call, plus O(T * Dk * Dv) arithmetic.
+ *   desc   : as kda_fwd, with chunk = 0 (anything else is KDA_ERR_INVALID_ARG) and Dk = Dv in
+ *            {64, 128} for both io_dtypes; flags as kda_fwd (KDA_FWD_PRECISE has no effect here).
+ *   tensors: layouts, dtypes and alignment as kda_fwd; S_T may equal S0 (the usual in-place decode
+ *            update: each thread reads its state entries before writing the same entries).
+ * Arithmetic is float32 throughout (bf16 inputs are widened exactly, a bf16 o is rounded once).
+ * Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP.
+ */
+kda_status kda_decode(const kda_fwd_desc* desc, const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, const float* S0,
+                      void* o, float* S_T, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Fused layer forward.  The layer of the explainer page "Kimi K3：开放前沿智能":
  *   section 2.4 (paper Eq. 2): q, k = L2norm(Swish(ShortConv(x W))); v = x W_v;

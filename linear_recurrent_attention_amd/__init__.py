@@ -10,7 +10,7 @@ import torch
 from . import _lib
 from ._lib import KdaError  # noqa: F401
 
-__all__ = ["kda_fwd", "kda_fwd_ckpt", "kda_layer_fwd", "KdaError"]
+__all__ = ["kda_fwd", "kda_fwd_ckpt", "kda_decode", "kda_layer_fwd", "KdaError"]
 
 _DT = {torch.float32: _lib.KDA_F32, torch.bfloat16: _lib.KDA_BF16}
 
@@ -77,6 +77,17 @@ def kda_fwd_ckpt(q, k, v, g, beta, every: int, S0=None, scale: float = 1.0, o_dt
                              _ptr(ck) if n > 0 else 0, int(every), _stream(q.device))
     _lib.check(code)
     return o, ST, ck
+
+
+def kda_decode(q, k, v, g, beta, S0=None, scale: float = 1.0, o_dtype=None, want_state: bool = True,
+               out=None, state_out=None):
+    """Token-by-token step (kda_decode): the same result as kda_fwd for a few tokens per call.
+    state_out may be S0 itself (in-place update).  Returns (o, S_T)."""
+    desc, o, ST = _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, 0, False, scale)
+    code = _lib.decode_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(ST),
+                           _stream(q.device))
+    _lib.check(code)
+    return o, ST
 
 
 def kda_layer_fwd(x, weights: dict, S0=None, conv_state=None, scale: float = 1.0, want_state: bool = True,

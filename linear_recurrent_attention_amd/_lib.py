@@ -18,7 +18,7 @@ KDA_BF16 = 1
 KDA_FWD_PRECISE = 1  # kda_fwd_desc.flags
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_fwd", "kda_fwd_ckpt", "kda_layer_workspace_size", "kda_layer_fwd", "kda_error_string", "kda_version")
+EXPORTS = ("kda_fwd", "kda_fwd_ckpt", "kda_decode", "kda_layer_workspace_size", "kda_layer_fwd", "kda_error_string", "kda_version")
 
 
 class FwdDesc(ctypes.Structure):
@@ -66,6 +66,8 @@ def lib():
             L = ctypes.CDLL(LIB_PATH)
             L.kda_fwd.restype = ctypes.c_int
             L.kda_fwd.argtypes = [ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 9
+            L.kda_decode.restype = ctypes.c_int
+            L.kda_decode.argtypes = [ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 9
             L.kda_fwd_ckpt.restype = ctypes.c_int
             L.kda_fwd_ckpt.argtypes = ([ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 9 + [ctypes.c_int] +
                                        [ctypes.c_void_p])
@@ -106,3 +108,8 @@ def fwd_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, stream) -> int:
 def fwd_ckpt_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, S_ckpt, every, stream) -> int:
     """Call kda_fwd_ckpt with integer device addresses (0 = NULL); returns the status code."""
     return lib().kda_fwd_ckpt(ctypes.byref(desc), q, k, v, g, beta, S0, o, S_T, S_ckpt, every, stream)
+
+
+def decode_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, stream) -> int:
+    """Call kda_decode with integer device addresses (0 = NULL); returns the status code."""
+    return lib().kda_decode(ctypes.byref(desc), q, k, v, g, beta, S0, o, S_T, stream)

@@ -8,8 +8,9 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-kda_status check_fwd(const kda_fwd_desc* d, const void* q, const void* k, const void* v, const float* g,
-                     const float* beta, const float* S0, const void* o, const float* S_T) {
+// Checks shared by the forward entry points: sizes, dtypes, pointers, alignment, aliasing.
+kda_status check_common(const kda_fwd_desc* d, const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* S0, const void* o, const float* S_T) {
     if (!d) return KDA_ERR_INVALID_ARG;
     if (d->B < 1 || d->H < 1 || d->T < 0 || d->Dk < 1 || d->Dv < 1) return KDA_ERR_INVALID_ARG;
     if (d->flags & ~KDA_FWD_PRECISE) return KDA_ERR_INVALID_ARG;
@@ -22,6 +23,15 @@ kda_status check_fwd(const kda_fwd_desc* d, const void* q, const void* k, const 
     if (d->T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
     if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(o, 4)) return KDA_ERR_INVALID_ARG;
     if (!aligned(g, 8) || !aligned(beta, 4) || !aligned(S0, 8) || !aligned(S_T, 8)) return KDA_ERR_INVALID_ARG;
+    // outputs must not alias inputs (S_T == S0 is the one allowed overlap)
+    if (o && (o == q || o == k || o == v || o == (const void*)g)) return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
+kda_status check_fwd(const kda_fwd_desc* d, const void* q, const void* k, const void* v, const float* g,
+                     const float* beta, const float* S0, const void* o, const float* S_T) {
+    const kda_status st = check_common(d, q, k, v, g, beta, S0, o, S_T);
+    if (st != KDA_OK) return st;
     if (d->io_dtype == KDA_BF16) {
         if (d->Dk != 128 || d->Dv != 128) return KDA_ERR_UNSUPPORTED;
         if (d->chunk != 0 && d->chunk != 32) return KDA_ERR_UNSUPPORTED;
@@ -29,8 +39,16 @@ kda_status check_fwd(const kda_fwd_desc* d, const void* q, const void* k, const 
         if (d->Dk != d->Dv || (d->Dk != 64 && d->Dk != 128)) return KDA_ERR_UNSUPPORTED;
         if (d->chunk != 0 && d->chunk != 16) return KDA_ERR_UNSUPPORTED;
     }
-    // outputs must not alias inputs (S_T == S0 is the one allowed overlap)
-    if (o && (o == q || o == k || o == v || o == (const void*)g)) return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
+kda_status check_decode(const kda_fwd_desc* d, const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* S0, const void* o, const float* S_T) {
+    const kda_status st = check_common(d, q, k, v, g, beta, S0, o, S_T);
+    if (st != KDA_OK) return st;
+    if (d->chunk != 0) return KDA_ERR_INVALID_ARG;  // no chunking on this path
+    if (d->Dk != d->Dv || (d->Dk != 64 && d->Dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if ((long long)d->B * d->H * (d->Dv / 64) > 0x7fffffffLL) return KDA_ERR_INVALID_ARG;  // grid size
     return KDA_OK;
 }
 
@@ -81,6 +99,23 @@ kda_status kda_fwd_ckpt(const kda_fwd_desc* desc, const void* q, const void* k, 
     if (!aligned(S_ckpt, 8)) return KDA_ERR_INVALID_ARG;
     if (S_ckpt && ((const void*)S_ckpt == o || S_ckpt == S_T || S_ckpt == S0)) return KDA_ERR_INVALID_ARG;
     return run_fwd(desc, q, k, v, g, beta, S0, o, S_T, n_ckpt > 0 ? S_ckpt : nullptr, every, stream);
+}
+
+kda_status kda_decode(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, const float* S0, void* o, float* S_T, hipStream_t stream) {
+    const kda_status st = check_decode(desc, q, k, v, g, beta, S0, o, S_T);
+    if (st != KDA_OK) return st;
+    kda::Params p;
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0; p.o = o; p.S_T = S_T;
+    p.B = desc->B; p.T = desc->T; p.H = desc->H; p.Dk = desc->Dk; p.Dv = desc->Dv; p.tstride = desc->T;
+    p.scale = desc->scale;
+    p.o_f32 = desc->o_dtype == KDA_F32;
+    p.in_f32 = 0;
+    p.precise = 0;
+    p.S_ckpt = nullptr; p.ckpt_chunks = 1; p.n_ckpt = 0;
+    const hipError_t e = desc->T == 0 ? kda::launch_state_copy(p, stream)
+                                      : kda::launch_decode(p, desc->io_dtype == KDA_BF16, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 const char* kda_error_string(kda_status s) {

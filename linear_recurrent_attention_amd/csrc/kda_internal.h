@@ -28,5 +28,6 @@ struct Params {
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t stream);  // Dk = Dv = 128, chunk 32 (in_f32 too)
 hipError_t launch_fwd_f32(const Params& p, hipStream_t stream);   // Dk = Dv in {64, 128}, chunk 16
 hipError_t launch_state_copy(const Params& p, hipStream_t stream); // T = 0: S_T = S0 (or 0)
+hipError_t launch_decode(const Params& p, bool in_bf16, hipStream_t stream);  // token by token, Dk = Dv in {64, 128}
 
 }  // namespace kda

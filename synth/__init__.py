@@ -6,12 +6,14 @@ distributions of the five workloads; it performs none of the KDA
 computation itself (no recurrence, no chunk algebra, no layer maths).
 """
 from .gen import (  # noqa: F401
+    DECODE,
     WORKLOADS,
     Workload,
     bf16_bits,
     bf16_round,
     core_inputs,
     core_inputs_block,
+    decode_inputs,
     layer_inputs,
     window_start,
 )

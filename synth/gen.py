@@ -55,6 +55,9 @@ WORKLOADS = {
                 block=1 << 16),
 }
 
+# decode: one new token for each of B sequences, after a prefill (S0 stands for the prefill's state)
+DECODE = dict(name="kda_decode_bf16_B128_H32_T1_D128", B=128, H=32, T=1, D=128, var_S0=0.1)
+
 LAYER = dict(name="kda_layer_fwd_bf16_B2_T8192_d2048_H16_D128", B=2, T=8192, d=2048, H=16, Dk=128, Dv=128,
              rank=128, conv=4)
 
@@ -217,3 +220,28 @@ def layer_inputs(seed: int = 0, B: int | None = None, T: int | None = None, d: i
         "b_alpha": np.zeros(HD, np.float32), "A": np.zeros(H, np.float32), "rms_w": np.ones(D, np.float32),
     }
     return x, p
+
+
+def decode_inputs(seed: int = 0, B: int | None = None, H: int | None = None, D: int | None = None,
+                  T: int | None = None):
+    """Inputs of the decode workload: the workload-1 distributions (A ~ U(-1,1) per head, z ~ N(0,1),
+    bf16 q/k/v) for T new tokens per sequence, and S0 ~ N(0, 0.1) float32.
+    Returns (dict(q, k, v, g, beta) of float32 arrays [B,T,H,*], S0 [B,H,D,D])."""
+    w = DECODE
+    B = w["B"] if B is None else B
+    H = w["H"] if H is None else H
+    D = w["D"] if D is None else D
+    T = w["T"] if T is None else T
+    rng = _rng(seed, 5, 0)
+    A = rng.uniform(-1.0, 1.0, size=H)
+    q = rng.standard_normal((B, T, H, D))
+    k = rng.standard_normal((B, T, H, D))
+    v = rng.standard_normal((B, T, H, D))
+    beta_logit = rng.standard_normal((B, T, H))
+    z = rng.standard_normal((B, T, H, D)) * np.exp(A)[None, None, :, None]
+    S0 = (rng.standard_normal((B, H, D, D)) * np.sqrt(w["var_S0"])).astype(np.float32)
+    d = {"q": bf16_round(q / np.linalg.norm(q, axis=-1, keepdims=True)),
+         "k": bf16_round(k / np.linalg.norm(k, axis=-1, keepdims=True)),
+         "v": bf16_round(v), "beta": _sigmoid(beta_logit).astype(np.float32),
+         "g": (G_MIN * _sigmoid(z)).astype(np.float32)}
+    return d, S0

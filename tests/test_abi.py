@@ -142,3 +142,26 @@ def test_checkpoint_buffer_aliasing_or_misaligned(kw):
 def test_checkpoint_call_validates_the_descriptor_first():
     assert call_ckpt(desc(B=0), 32) == _lib.KDA_ERR_INVALID_ARG
     assert call_ckpt(desc(Dk=64, Dv=64), 32) == _lib.KDA_ERR_UNSUPPORTED
+
+
+def call_decode(d, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=0, o=FAKE + 0x100000, S_T=0)
+    a.update(kw)
+    return _lib.decode_raw(d, a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["o"], a["S_T"], None)
+
+
+def test_decode_rejects_a_chunk_size():
+    assert call_decode(desc(chunk=32)) == _lib.KDA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(Dk=96, Dv=96), dict(Dk=128, Dv=64), dict(Dk=32, Dv=32)])
+def test_decode_unsupported_head_sizes(kw):
+    assert call_decode(desc(**kw)) == _lib.KDA_ERR_UNSUPPORTED
+
+
+def test_decode_shares_the_forward_argument_checks():
+    assert call_decode(desc(B=0)) == _lib.KDA_ERR_INVALID_ARG
+    assert call_decode(desc(), o=FAKE) == _lib.KDA_ERR_INVALID_ARG        # output aliases q
+    assert call_decode(desc(), g=FAKE + 0x20004) == _lib.KDA_ERR_INVALID_ARG  # misaligned g
+    # T = 0 with Dk = 64 bf16 (valid on this path) launches nothing without S_T
+    assert call_decode(desc(T=0, Dk=64, Dv=64), q=0, k=0, v=0, g=0, beta=0, o=0) == _lib.KDA_OK
