@@ -119,6 +119,31 @@ kda_status kda_decode(const kda_fwd_desc* desc, const void* q, const void* k, co
                       const float* g, const float* beta, const float* S0,
                       void* o, float* S_T, hipStream_t stream);
 
+/*
+ * kda_fwd_cp -- kda_fwd for few, long sequences: in-device context parallelism (explainer page,
+ * section 13.3.1, with the decomposition of section 13.3.2: the state after a segment is its
+ * accumulated transition M_i times its initial state plus its local state estimate S_hat_i).
+ * Each sequence is cut into nseg segments that run side by side: a pass from S = 0 gives every
+ * S_hat_i, a pass with v = 0 from S = I gives every M_i, a float32 scan over segments gives every
+ * initial state, and a last pass from those states writes o and S_T.  About three times the work
+ * of kda_fwd spread over nseg times more workgroups: it pays when 2*B*H is well below the 256
+ * compute units (e.g. B = 1, H = 16 at a million tokens).
+ *   desc    : as kda_fwd, bf16 I/O only (Dk = Dv = 128; float32 I/O is KDA_ERR_UNSUPPORTED)
+ *   nseg    : segments per sequence; 0 = automatic (enough for about one workgroup per compute
+ *             unit, segments of at least 1024 tokens), 1 = kda_fwd.  T need not be a multiple of
+ *             anything: the largest multiple of nseg*32 tokens is run in segments and the rest
+ *             after it, from the last segment's state.
+ *   ws      : device workspace of at least kda_fwd_cp_workspace_size(desc, nseg) bytes, 256-byte
+ *             aligned (may be NULL when that size is 0); its contents are scratch.
+ * Other arguments as kda_fwd (S_T may equal S0).  The result matches kda_fwd to within the bf16
+ * path's rounding, not bit for bit (the segments start from scanned states).
+ * Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE or KDA_ERR_HIP.
+ */
+size_t kda_fwd_cp_workspace_size(const kda_fwd_desc* desc, int nseg);  /* 0 if none is needed or desc is invalid */
+kda_status kda_fwd_cp(const kda_fwd_desc* desc, const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, const float* S0,
+                      void* o, float* S_T, int nseg, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Fused layer forward.  The layer of the explainer page "Kimi K3：开放前沿智能":
  *   section 2.4 (paper Eq. 2): q, k = L2norm(Swish(ShortConv(x W))); v = x W_v;

@@ -10,7 +10,7 @@ import torch
 from . import _lib
 from ._lib import KdaError  # noqa: F401
 
-__all__ = ["kda_fwd", "kda_fwd_ckpt", "kda_decode", "kda_layer_fwd", "KdaError"]
+__all__ = ["kda_fwd", "kda_fwd_ckpt", "kda_fwd_cp", "kda_decode", "kda_layer_fwd", "KdaError"]
 
 _DT = {torch.float32: _lib.KDA_F32, torch.bfloat16: _lib.KDA_BF16}
 
@@ -77,6 +77,22 @@ def kda_fwd_ckpt(q, k, v, g, beta, every: int, S0=None, scale: float = 1.0, o_dt
                              _ptr(ck) if n > 0 else 0, int(every), _stream(q.device))
     _lib.check(code)
     return o, ST, ck
+
+
+def kda_fwd_cp(q, k, v, g, beta, S0=None, nseg: int = 0, scale: float = 1.0, o_dtype=None,
+               want_state: bool = True, out=None, state_out=None, precise: bool = False, workspace=None):
+    """kda_fwd with in-device context parallelism (kda_fwd_cp): each sequence is split into nseg
+    segments (0 = automatic) that run side by side.  bf16 q/k/v only.  Returns (o, S_T)."""
+    desc, o, ST = _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, 0, precise, scale)
+    need = _lib.cp_workspace_size(desc, int(nseg))
+    ws = workspace
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    code = _lib.fwd_cp_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(ST),
+                           int(nseg), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                           _stream(q.device))
+    _lib.check(code)
+    return o, ST
 
 
 def kda_decode(q, k, v, g, beta, S0=None, scale: float = 1.0, o_dtype=None, want_state: bool = True,

@@ -18,7 +18,7 @@ KDA_BF16 = 1
 KDA_FWD_PRECISE = 1  # kda_fwd_desc.flags
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_fwd", "kda_fwd_ckpt", "kda_decode", "kda_layer_workspace_size", "kda_layer_fwd", "kda_error_string", "kda_version")
+EXPORTS = ("kda_fwd", "kda_fwd_ckpt", "kda_decode", "kda_fwd_cp_workspace_size", "kda_fwd_cp", "kda_layer_workspace_size", "kda_layer_fwd", "kda_error_string", "kda_version")
 
 
 class FwdDesc(ctypes.Structure):
@@ -66,6 +66,11 @@ def lib():
             L = ctypes.CDLL(LIB_PATH)
             L.kda_fwd.restype = ctypes.c_int
             L.kda_fwd.argtypes = [ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 9
+            L.kda_fwd_cp_workspace_size.restype = ctypes.c_size_t
+            L.kda_fwd_cp_workspace_size.argtypes = [ctypes.POINTER(FwdDesc), ctypes.c_int]
+            L.kda_fwd_cp.restype = ctypes.c_int
+            L.kda_fwd_cp.argtypes = ([ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 8 + [ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p])
             L.kda_decode.restype = ctypes.c_int
             L.kda_decode.argtypes = [ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 9
             L.kda_fwd_ckpt.restype = ctypes.c_int
@@ -113,3 +118,12 @@ def fwd_ckpt_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, S_ckpt, every, str
 def decode_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, stream) -> int:
     """Call kda_decode with integer device addresses (0 = NULL); returns the status code."""
     return lib().kda_decode(ctypes.byref(desc), q, k, v, g, beta, S0, o, S_T, stream)
+
+
+def cp_workspace_size(desc: FwdDesc, nseg: int) -> int:
+    return lib().kda_fwd_cp_workspace_size(ctypes.byref(desc), nseg)
+
+
+def fwd_cp_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, nseg, ws, ws_bytes, stream) -> int:
+    """Call kda_fwd_cp with integer device addresses (0 = NULL); returns the status code."""
+    return lib().kda_fwd_cp(ctypes.byref(desc), q, k, v, g, beta, S0, o, S_T, nseg, ws, ws_bytes, stream)

@@ -57,7 +57,7 @@ int chunk_of(const kda_fwd_desc* d) { return d->io_dtype == KDA_BF16 ? 32 : 16; 
 kda_status run_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
                    const float* beta, const float* S0, void* o, float* S_T, float* S_ckpt, int every,
                    hipStream_t stream) {
-    kda::Params p;
+    kda::Params p{};  // zero: every optional field off
     p.S_ckpt = S_ckpt;
     p.ckpt_chunks = S_ckpt ? every / chunk_of(desc) : 1;
     p.n_ckpt = S_ckpt ? desc->T / every : 0;
@@ -105,7 +105,7 @@ kda_status kda_decode(const kda_fwd_desc* desc, const void* q, const void* k, co
                       const float* beta, const float* S0, void* o, float* S_T, hipStream_t stream) {
     const kda_status st = check_decode(desc, q, k, v, g, beta, S0, o, S_T);
     if (st != KDA_OK) return st;
-    kda::Params p;
+    kda::Params p{};  // zero: every optional field off
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0; p.o = o; p.S_T = S_T;
     p.B = desc->B; p.T = desc->T; p.H = desc->H; p.Dk = desc->Dk; p.Dv = desc->Dv; p.tstride = desc->T;
     p.scale = desc->scale;
@@ -115,6 +115,34 @@ kda_status kda_decode(const kda_fwd_desc* desc, const void* q, const void* k, co
     p.S_ckpt = nullptr; p.ckpt_chunks = 1; p.n_ckpt = 0;
     const hipError_t e = desc->T == 0 ? kda::launch_state_copy(p, stream)
                                       : kda::launch_decode(p, desc->io_dtype == KDA_BF16, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_fwd_cp_workspace_size(const kda_fwd_desc* desc, int nseg) {
+    if (!desc || nseg < 0 || desc->B < 1 || desc->H < 1 || desc->T < 0 || desc->io_dtype != KDA_BF16) return 0;
+    if ((long long)desc->B * desc->H > (1LL << 30)) return 0;
+    return kda::cp_workspace_bytes(desc->B, desc->T, desc->H, nseg);
+}
+
+kda_status kda_fwd_cp(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, const float* S0, void* o, float* S_T, int nseg, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+    const kda_status st = check_fwd(desc, q, k, v, g, beta, S0, o, S_T);
+    if (st != KDA_OK) return st;
+    if (nseg < 0 || nseg > 4096) return KDA_ERR_INVALID_ARG;
+    if (desc->io_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if ((long long)desc->B * desc->H * (nseg ? nseg : 1) > (1LL << 30)) return KDA_ERR_INVALID_ARG;
+    const size_t need = kda::cp_workspace_bytes(desc->B, desc->T, desc->H, nseg);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return KDA_ERR_WORKSPACE;
+    if (desc->T == 0) return run_fwd(desc, q, k, v, g, beta, S0, o, S_T, nullptr, 0, stream);
+    kda::Params p{};  // zero: every optional field off
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0; p.o = o; p.S_T = S_T;
+    p.B = desc->B; p.T = desc->T; p.H = desc->H; p.Dk = desc->Dk; p.Dv = desc->Dv; p.tstride = desc->T;
+    p.scale = desc->scale;
+    p.o_f32 = desc->o_dtype == KDA_F32;
+    p.precise = (desc->flags & KDA_FWD_PRECISE) != 0;
+    p.ckpt_chunks = 1;
+    const hipError_t e = kda::launch_fwd_cp(p, nseg, static_cast<float*>(ws), stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -170,7 +170,10 @@ __device__ __forceinline__ void load_chunk(Raw<IN_F32>& r, const Params& p, cons
     const gchar* qc = uniform_gptr((const char*)p.q + ce * 2 * qs);
     const gchar* kc = uniform_gptr((const char*)p.k + ce * 2 * qs);
     const gchar* gc = uniform_gptr(p.g + ce);
-    const gchar* vc = uniform_gptr((const uint16_t*)p.v + ce);
+    // v == NULL stands for v = 0 (the transition-matrix run of the in-device context parallelism): the
+    // value loads then read the chunk's g instead (a valid address at every value offset, g having
+    // twice v's row size) and the values are replaced by zeros
+    const gchar* vc = uniform_gptr(p.v ? (const void*)((const uint16_t*)p.v + ce) : (const void*)(p.g + ce));
     const gchar* bc = uniform_gptr(p.beta + row0 + (size_t)t0 * p.H);
     using QT = typename std::conditional<IN_F32, f32x2, uint32_t>::type;
     if (t0 + C <= p.T) {
@@ -194,6 +197,12 @@ __device__ __forceinline__ void load_chunk(Raw<IN_F32>& r, const Params& p, cons
             if constexpr (LG && !IN_F32) r.v[i] = gload<uint32_t>(vc, ov);
         }
         if constexpr (LG) r.beta = gload<float>(bc, (uint32_t)min(TPW * kl.kw + (kl.lane % TPW), lim) * 4u * p.H);
+    }
+    if constexpr (LG && !IN_F32) {
+        if (!p.v) {  // v = 0 (what was read came from g, see above)
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) r.v[i] = 0u;
+        }
     }
 }
 
@@ -610,20 +619,22 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
 
         // ---------------- part 3: O += A U, output; S <- Diag(Gamma_last) S + Kbar^T U
         if (work) {
-            gchar* ob = (gchar*)uniform_gptr((const char*)p.o + ((row0 + (size_t)t0 * p.H) * DV) * (OUT_F32 ? 4 : 2));
+            if (p.o) {  // (o == NULL: a state-only run of the in-device context parallelism)
+                gchar* ob = (gchar*)uniform_gptr((const char*)p.o + ((row0 + (size_t)t0 * p.H) * DV) * (OUT_F32 ? 4 : 2));
 #pragma unroll
-            for (int R = 0; R < 2; ++R) {
-                const u32x4 aH = ld16(&H.ah[SUB * R + l16][8 * g4]);
-                const u32x4 aL = ld16(&H.al[SUB * R + l16][8 * g4]);
-                f32x4 acc = mfma_bf16(uh, aH, oacc[R]);
-                acc = mfma_bf16(ul, aH, acc);
-                acc = mfma_bf16(uh, aL, acc);
-                if (p.scale != 1.f) acc *= p.scale;
-                if (t0 + SUB * R + l16 < p.T) {
-                    if constexpr (OUT_F32)
-                        gstore<f32x4>(ob, ooff[R], acc);
-                    else
-                        gstore<u32x2>(ob, ooff[R], u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])});
+                for (int R = 0; R < 2; ++R) {
+                    const u32x4 aH = ld16(&H.ah[SUB * R + l16][8 * g4]);
+                    const u32x4 aL = ld16(&H.al[SUB * R + l16][8 * g4]);
+                    f32x4 acc = mfma_bf16(uh, aH, oacc[R]);
+                    acc = mfma_bf16(ul, aH, acc);
+                    acc = mfma_bf16(uh, aL, acc);
+                    if (p.scale != 1.f) acc *= p.scale;
+                    if (t0 + SUB * R + l16 < p.T) {
+                        if constexpr (OUT_F32)
+                            gstore<f32x4>(ob, ooff[R], acc);
+                        else
+                            gstore<u32x2>(ob, ooff[R], u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])});
+                    }
                 }
             }
 #pragma unroll

@@ -29,5 +29,8 @@ hipError_t launch_fwd_bf16(const Params& p, hipStream_t stream);  // Dk = Dv = 1
 hipError_t launch_fwd_f32(const Params& p, hipStream_t stream);   // Dk = Dv in {64, 128}, chunk 16
 hipError_t launch_state_copy(const Params& p, hipStream_t stream); // T = 0: S_T = S0 (or 0)
 hipError_t launch_decode(const Params& p, bool in_bf16, hipStream_t stream);  // token by token, Dk = Dv in {64, 128}
+// in-device context parallelism (bf16 I/O, Dk = Dv = 128): segment count nseg_req (0 = automatic)
+size_t cp_workspace_bytes(int B, int T, int H, int nseg_req);
+hipError_t launch_fwd_cp(const Params& p, int nseg_req, float* ws, hipStream_t stream);
 
 }  // namespace kda

@@ -305,7 +305,7 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
         hipLaunchKernelGGL(conv_state_kernel, dim3(256), dim3(256), 0, stream, d->B, d->T, HD, W.pq, W.pk,
                            conv_state_in, conv_state_out);
 
-    kda::Params p;
+    kda::Params p{};  // zero: every optional field off
     // the core reads q, k, v in float32 (v straight from the projection output): rounding them to
     // bf16 first would be amplified by the per-head RMSNorm wherever a head's output is small
     p.q = W.q; p.k = W.k; p.v = W.pv; p.g = W.g; p.beta = W.beta; p.S0 = S0; p.o = W.o; p.S_T = S_T;

@@ -165,3 +165,43 @@ def test_decode_shares_the_forward_argument_checks():
     assert call_decode(desc(), g=FAKE + 0x20004) == _lib.KDA_ERR_INVALID_ARG  # misaligned g
     # T = 0 with Dk = 64 bf16 (valid on this path) launches nothing without S_T
     assert call_decode(desc(T=0, Dk=64, Dv=64), q=0, k=0, v=0, g=0, beta=0, o=0) == _lib.KDA_OK
+
+
+def test_cp_workspace_size_plan():
+    # B=1, H=16, T=2^20: automatic plan = 8 segments of 2^17 tokens -> three [8, 16, 128, 128] float buffers
+    d = desc(B=1, T=1 << 20, H=16)
+    assert _lib.cp_workspace_size(d, 0) == 3 * 8 * 16 * 128 * 128 * 4
+    assert _lib.cp_workspace_size(d, 4) == 3 * 4 * 16 * 128 * 128 * 4
+    assert _lib.cp_workspace_size(d, 1) == 0                       # nseg = 1 is kda_fwd
+    # enough heads already: the automatic plan is one segment
+    assert _lib.cp_workspace_size(desc(B=4, T=16384, H=32), 0) == 0
+    # a ragged T runs the segments per sequence: one batch row of buffers
+    assert _lib.cp_workspace_size(desc(B=2, T=4096 + 5, H=2), 4) == 3 * 4 * 2 * 128 * 128 * 4
+    assert _lib.cp_workspace_size(desc(B=2, T=4096, H=2), 4) == 3 * 2 * 4 * 2 * 128 * 128 * 4
+    # too short for the requested segments (T < nseg * 32)
+    assert _lib.cp_workspace_size(desc(T=100), 4) == 0
+    # invalid descriptors
+    assert _lib.cp_workspace_size(desc(io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_F32), 4) == 0
+    assert _lib.cp_workspace_size(desc(B=0), 4) == 0
+    assert _lib.cp_workspace_size(d, -1) == 0
+
+
+def call_cp(d, nseg, ws=0, ws_bytes=0, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=0, o=FAKE + 0x100000, S_T=0)
+    a.update(kw)
+    return _lib.fwd_cp_raw(d, a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["o"], a["S_T"], nseg, ws,
+                           ws_bytes, None)
+
+
+def test_cp_argument_checks():
+    d = desc(B=1, T=1 << 16, H=2)
+    need = _lib.cp_workspace_size(d, 4)
+    assert need > 0
+    assert call_cp(d, 4) == _lib.KDA_ERR_WORKSPACE                                  # no workspace
+    assert call_cp(d, 4, ws=FAKE + 0x400000, ws_bytes=need - 1) == _lib.KDA_ERR_WORKSPACE
+    assert call_cp(d, 4, ws=FAKE + 0x400010, ws_bytes=need) == _lib.KDA_ERR_WORKSPACE  # not 256-aligned
+    assert call_cp(d, -2) == _lib.KDA_ERR_INVALID_ARG
+    assert call_cp(desc(io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_F32, Dk=64, Dv=64), 2) == _lib.KDA_ERR_UNSUPPORTED
+    assert call_cp(desc(B=0), 2) == _lib.KDA_ERR_INVALID_ARG
+    # T = 0: the state copy only (nothing launched without S_T)
+    assert call_cp(desc(T=0), 4, q=0, k=0, v=0, g=0, beta=0, o=0) == _lib.KDA_OK
