@@ -26,12 +26,19 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix
 WORKLOAD = 2
 COPY_BYTES = 512 << 20
-KERNEL_SRC = os.path.join(ROOT, "linear_recurrent_attention_amd", "csrc", "kda_fwd_bf16.hip")
+CSRC = os.path.join(ROOT, "linear_recurrent_attention_amd", "csrc")
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by the same counters on a
-# 512 MiB copy (factors 2.0 and 1.0); valid only for the kernel source with this hash.
-MEASURED_TRAFFIC = {"kernel_sha256": "2d3d6f8c94394ab55927187840c39901903bb5fee40c3244bc212f3e94991ecb",
-                    "bytes": (1343706 * 2.0 + 532480 * 1.0) * 1024,
-                    "profile": "profiles/kda_fwd_bf16_B4_H32_T16384_D128.md"}
+# 512 MiB copy (factors 2.0 and 1.0); valid only for the kernel source with the recorded hash.
+MEASURED_TRAFFIC = {
+    "core": {"source": "kda_fwd_bf16.hip",
+             "kernel_sha256": "c94a3cf1fa32ccb945430edae7bb15cce194dee77280d167d51acb4b218eac23",
+             "bytes": (1343623 * 2.0 + 532480 * 1.0) * 1024,
+             "profile": "profiles/kda_fwd_bf16_B4_H32_T16384_D128.md"},
+    "decode": {"source": "kda_decode.hip",
+               "kernel_sha256": "cd969b686b6b0e06382e0dbd651015bdea5d1895790e77c3248f0d1df9a3c844",
+               "bytes": (135790 * 2.0 + 263168 * 1.0) * 1024,
+               "profile": "profiles/kda_decode_bf16_B128_H32_T1_D128.md"},
+}
 
 
 def algorithmic_bytes(B, T, H, Dk, Dv, io_bytes=2, has_S0=False):
@@ -52,12 +59,13 @@ def algorithmic_flops(B, T, H, Dk, Dv, C=32):
     return B * H * (T / C) * per_chunk
 
 
-def measured_traffic():
+def measured_traffic(which="core"):
     """HBM bytes per launch from the committed counter profile, or None if the kernel changed since."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
+    m = MEASURED_TRAFFIC[which]
+    with open(os.path.join(CSRC, m["source"]), "rb") as f:
         digest = hashlib.sha256(f.read()).hexdigest()
-    return MEASURED_TRAFFIC["bytes"] if digest == MEASURED_TRAFFIC["kernel_sha256"] else None
+    return m["bytes"] if digest == m["kernel_sha256"] else None
 
 
 def cpu_baseline(d, threads):
@@ -129,7 +137,7 @@ def bench_decode(args, torch, synth, kda):
         "config": {"workload": w["name"], "B": B, "H": H, "T": T, "D": D,
                    "io": "bf16 q/k/v/o, float32 g/beta/state"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "kda_decode_kernel",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"), "kernel": "kda_decode_kernel",
                      "avg_launch_ms": avg_s * 1e3, "algorithmic_bytes": abytes},
     }
     if not args.no_cpu:
@@ -141,6 +149,69 @@ def bench_decode(args, torch, synth, kda):
         out["cpu_baseline"] = {"value": B * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                                "sample": f"the whole decode workload ({B * H} heads, one token; float64 token "
                                          f"recurrence, {dt:.3f} s wall on {threads} threads)"}
+    print(json.dumps(out), flush=True)
+
+
+def bench_longctx(args, torch, synth, kda):
+    """kda_fwd_cp (in-device context parallelism, automatic plan) on the million-token workload
+    B=1, H=16, T=2^20, D=128 with S0: tokens/s, and the plain kda_fwd call timed once beside it."""
+    w = synth.WORKLOADS[3]
+    B, T, H, D, TB = w.B, w.T, w.H, w.Dk, w.block
+    A, S0 = synth.gen.head_params(3, 0)
+    dev = torch.device("cuda:0")
+    t = {n: torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev) for n in ("q", "k", "v")}
+    t["g"] = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
+    t["beta"] = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    first = None
+    for j in range(T // TB):  # generated and uploaded block by block (the host never holds it all)
+        blk = synth.core_inputs_block(3, j, seed=0, A=A)
+        for n, x in t.items():
+            x[:, j * TB:(j + 1) * TB].copy_(torch.from_numpy(blk[n]).to(dev))
+        if j == 0:
+            first = blk
+        print(f"bench.py: longctx inputs, block {j + 1}/{T // TB} on the device", file=sys.stderr, flush=True)
+    S0d = torch.from_numpy(S0).to(dev)
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    from linear_recurrent_attention_amd import _lib
+    desc = _lib.FwdDesc(B, T, H, D, D, 0, _lib.KDA_BF16, _lib.KDA_BF16, 1.0, 0)
+    ws = torch.empty(max(1, _lib.cp_workspace_size(desc, 0)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step():
+        kda.kda_fwd_cp(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=S0d, out=o, state_out=ST, workspace=ws)
+
+    wall, launch_ms = time_steps(torch, step, stream, args)
+
+    def plain():
+        kda.kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=S0d, out=o, state_out=ST)
+
+    import types
+    _, plain_ms = time_steps(torch, plain, stream, types.SimpleNamespace(steps=1, warmup=1))
+    avg_s = float(np.mean(launch_ms)) / 1e3
+    abytes = algorithmic_bytes(B, T, H, D, D, has_S0=True)
+    gbs = abytes / avg_s / 1e9
+    out = {
+        "metric": "KDA long-context prefill tokens/s (B1 H16 T1M D128, in-device context parallelism)",
+        "value": B * T / (wall / args.steps), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "D": D, "segments": "automatic (8)",
+                   "io": "bf16 q/k/v/o, float32 g/beta/state"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "kda_fwd_cp (all passes)",
+                     "avg_call_ms": avg_s * 1e3, "algorithmic_bytes": abytes},
+        "plain_kda_fwd_ms": plain_ms[0],
+    }
+    if not args.no_cpu:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        tc = time.perf_counter()
+        oracle.recurrence(first["q"], first["k"], first["v"], first["g"], first["beta"], S0=S0, threads=threads)
+        dt = time.perf_counter() - tc
+        out["cpu_baseline"] = {"value": B * TB / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"the first {TB}-token block of all {H} heads (float64 token recurrence, "
+                                         f"{dt:.1f} s wall on {threads} threads)"}
     print(json.dumps(out), flush=True)
 
 
@@ -215,9 +286,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run one plain 512 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=("core", "layer", "decode"), default="core",
+    ap.add_argument("--workload", choices=("core", "layer", "decode", "longctx"), default="core",
                     help="core: kda_fwd on B4 H32 T16384 (the headline line); layer: kda_layer_fwd on "
-                         "B2 T8192 d_model 2048 H16; decode: kda_decode on B128 H32, one token (separate lines)")
+                         "B2 T8192 d_model 2048 H16; decode: kda_decode on B128 H32, one token; longctx: "
+                         "kda_fwd_cp on B1 H16 T1M (separate lines)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus N with N > 1 is not supported "
@@ -233,6 +305,9 @@ def main():
         return
     if args.workload == "decode":
         bench_decode(args, torch, synth, kda)
+        return
+    if args.workload == "longctx":
+        bench_longctx(args, torch, synth, kda)
         return
     w = synth.WORKLOADS[WORKLOAD]
     B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
