@@ -44,6 +44,10 @@ def _load():
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 6 + [ctypes.c_double] + [ctypes.c_void_p] * 2 + [
                 ctypes.c_int]
+            fb = lib.kda_oracle_backward
+            fb.restype = ctypes.c_int
+            fb.argtypes = ([ctypes.c_int] * 6 + [ctypes.c_void_p] * 6 + [ctypes.c_double] + [ctypes.c_void_p] * 8 +
+                           [ctypes.c_int])
             _lib = lib
     return _lib
 
@@ -82,6 +86,38 @@ def recurrence(q, k, v, g, beta, S0=None, scale: float = 1.0, want_o: bool = Tru
     if rc != 0:
         raise RuntimeError(f"kda_oracle_recurrence failed ({rc})")
     return o, ST
+
+
+def backward(q, k, v, g, beta, S0=None, dO=None, dST=None, scale: float = 1.0, threads: int | None = None):
+    """float64 gradients of the gated delta rule (reverse-mode through the token steps), for output
+    gradients dO [B,T,H,Dv] and dST [B,H,Dk,Dv] (None = zero).
+
+    Returns dict(dq, dk, dg [B,T,H,Dk], dv [B,T,H,Dv], dbeta [B,T,H], dS0 [B,H,Dk,Dv]), float64.
+    """
+    lib = _load()
+    f64 = q.dtype == np.float64
+    dt = np.float64 if f64 else np.float32
+    q, k, v, g, beta = (np.ascontiguousarray(a, dtype=dt) for a in (q, k, v, g, beta))
+    B, T, H, Dk = k.shape
+    Dv = v.shape[-1]
+    assert q.shape == k.shape == g.shape and v.shape[:3] == (B, T, H) and beta.shape == (B, T, H)
+    arrs = {}
+    for name, a, shp in (("S0", S0, (B, H, Dk, Dv)), ("dO", dO, (B, T, H, Dv)), ("dST", dST, (B, H, Dk, Dv))):
+        if a is not None:
+            a = np.ascontiguousarray(a, dtype=np.float64)
+            assert a.shape == shp, name
+        arrs[name] = a
+    out = {"dq": np.empty((B, T, H, Dk)), "dk": np.empty((B, T, H, Dk)), "dv": np.empty((B, T, H, Dv)),
+           "dg": np.empty((B, T, H, Dk)), "dbeta": np.empty((B, T, H)), "dS0": np.empty((B, H, Dk, Dv))}
+    ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
+    rc = lib.kda_oracle_backward(B, T, H, Dk, Dv, int(f64), q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                 g.ctypes.data, beta.ctypes.data, ptr(arrs["S0"]), float(scale), ptr(arrs["dO"]),
+                                 ptr(arrs["dST"]), out["dq"].ctypes.data, out["dk"].ctypes.data,
+                                 out["dv"].ctypes.data, out["dg"].ctypes.data, out["dbeta"].ctypes.data,
+                                 out["dS0"].ctypes.data, _threads(threads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_backward failed ({rc})")
+    return out
 
 
 def recurrence_np(q, k, v, g, beta, S0=None, scale: float = 1.0):
