@@ -144,6 +144,32 @@ kda_status kda_fwd_cp(const kda_fwd_desc* desc, const void* q, const void* k, co
                       const float* g, const float* beta, const float* S0,
                       void* o, float* S_T, int nseg, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * kda_bwd -- gradients of kda_fwd (training; the explainer page's P3 section 5.1 says FlashKDA covers
+ * training, and the pages give no backward formulas: these are reverse-mode through the chunkwise
+ * form of section 2.5).  Same desc and inputs as the forward call; given the gradients of a loss
+ * with respect to o and S_T it returns those with respect to every input.
+ *   dO     : [B, T, H, Dv] o_dtype   dL/do, or NULL for zero
+ *   dS_T   : [B, H, Dk, Dv] float32  dL/dS_T, or NULL for zero
+ *   dq, dk, dg : [B, T, H, Dk] float32;  dv : [B, T, H, Dv] float32;  dbeta : [B, T, H] float32;
+ *   dS0    : [B, H, Dk, Dv] float32 (the gradient for S0, or for a zero initial state when S0 is NULL)
+ *            Each output may be NULL (not computed); outputs must not alias inputs or each other.
+ *   ws     : device workspace of at least kda_bwd_workspace_size(desc) bytes, 256-byte aligned:
+ *            the forward state and the state gradient at every 32-token (bf16 inputs) or 16-token
+ *            (float32 inputs) boundary, 2 * B * H * ceil(T / interval) * Dk * Dv floats.
+ *   desc   : chunk must be 0; bf16 I/O needs Dk = Dv = 128, float32 I/O Dk = Dv in {64, 128};
+ *            KDA_FWD_PRECISE is implied for the state recompute of bf16 inputs.
+ * Arithmetic is float32 (bf16 inputs and dO are widened exactly; the recomputed states carry the
+ * forward path's rounding).  Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED,
+ * KDA_ERR_WORKSPACE or KDA_ERR_HIP.
+ */
+size_t kda_bwd_workspace_size(const kda_fwd_desc* desc);  /* 0 for an invalid descriptor */
+kda_status kda_bwd(const kda_fwd_desc* desc, const void* q, const void* k, const void* v,
+                   const float* g, const float* beta, const float* S0,
+                   const void* dO, const float* dS_T,
+                   float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dS0,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Fused layer forward.  The layer of the explainer page "Kimi K3：开放前沿智能":
  *   section 2.4 (paper Eq. 2): q, k = L2norm(Swish(ShortConv(x W))); v = x W_v;

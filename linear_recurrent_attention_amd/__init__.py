@@ -10,7 +10,7 @@ import torch
 from . import _lib
 from ._lib import KdaError  # noqa: F401
 
-__all__ = ["kda_fwd", "kda_fwd_ckpt", "kda_fwd_cp", "kda_decode", "kda_layer_fwd", "KdaError"]
+__all__ = ["kda_fwd", "kda_fwd_ckpt", "kda_fwd_cp", "kda_bwd", "kda_decode", "kda_layer_fwd", "KdaError"]
 
 _DT = {torch.float32: _lib.KDA_F32, torch.bfloat16: _lib.KDA_BF16}
 
@@ -93,6 +93,31 @@ def kda_fwd_cp(q, k, v, g, beta, S0=None, nseg: int = 0, scale: float = 1.0, o_d
                            _stream(q.device))
     _lib.check(code)
     return o, ST
+
+
+def kda_bwd(q, k, v, g, beta, dO=None, dS_T=None, S0=None, scale: float = 1.0, workspace=None):
+    """Gradients of kda_fwd (kda_bwd) for dL/do = dO (o's dtype, or None) and dL/dS_T = dS_T
+    (float32, or None).  Returns dict(dq, dk, dv, dg, dbeta, dS0) of float32 tensors."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    o_dtype = q.dtype if dO is None else dO.dtype
+    if dO is not None and (dO.shape != (B, T, H, Dv) or not dO.is_contiguous() or not dO.is_cuda):
+        raise ValueError("dO must be a contiguous GPU [B,T,H,Dv] tensor")
+    if dS_T is not None and (dS_T.dtype != torch.float32 or dS_T.shape != (B, H, Dk, Dv) or not dS_T.is_contiguous()):
+        raise ValueError("dS_T must be a contiguous float32 [B,H,Dk,Dv] tensor")
+    desc, _, _ = _fwd_args(q, k, v, g, beta, S0, o_dtype, False, q, None, 0, False, scale)
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((B, T, H, Dk), **f32), "dk": torch.empty((B, T, H, Dk), **f32),
+           "dv": torch.empty((B, T, H, Dv), **f32), "dg": torch.empty((B, T, H, Dk), **f32),
+           "dbeta": torch.empty((B, T, H), **f32), "dS0": torch.empty((B, H, Dk, Dv), **f32)}
+    need = _lib.bwd_workspace_size(desc)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    code = _lib.bwd_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
+                        *[out[n].data_ptr() for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0")], ws.data_ptr(),
+                        ws.numel() * ws.element_size(), _stream(dev))
+    _lib.check(code)
+    return out
 
 
 def kda_decode(q, k, v, g, beta, S0=None, scale: float = 1.0, o_dtype=None, want_state: bool = True,

@@ -18,7 +18,8 @@ KDA_BF16 = 1
 KDA_FWD_PRECISE = 1  # kda_fwd_desc.flags
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_fwd", "kda_fwd_ckpt", "kda_decode", "kda_fwd_cp_workspace_size", "kda_fwd_cp", "kda_layer_workspace_size", "kda_layer_fwd", "kda_error_string", "kda_version")
+EXPORTS = ("kda_fwd", "kda_fwd_ckpt", "kda_decode", "kda_fwd_cp_workspace_size", "kda_fwd_cp",
+           "kda_bwd_workspace_size", "kda_bwd", "kda_layer_workspace_size", "kda_layer_fwd", "kda_error_string", "kda_version")
 
 
 class FwdDesc(ctypes.Structure):
@@ -71,6 +72,10 @@ def lib():
             L.kda_fwd_cp.restype = ctypes.c_int
             L.kda_fwd_cp.argtypes = ([ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 8 + [ctypes.c_int, ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p])
+            L.kda_bwd_workspace_size.restype = ctypes.c_size_t
+            L.kda_bwd_workspace_size.argtypes = [ctypes.POINTER(FwdDesc)]
+            L.kda_bwd.restype = ctypes.c_int
+            L.kda_bwd.argtypes = ([ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 15 + [ctypes.c_size_t, ctypes.c_void_p])
             L.kda_decode.restype = ctypes.c_int
             L.kda_decode.argtypes = [ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 9
             L.kda_fwd_ckpt.restype = ctypes.c_int
@@ -127,3 +132,13 @@ def cp_workspace_size(desc: FwdDesc, nseg: int) -> int:
 def fwd_cp_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, nseg, ws, ws_bytes, stream) -> int:
     """Call kda_fwd_cp with integer device addresses (0 = NULL); returns the status code."""
     return lib().kda_fwd_cp(ctypes.byref(desc), q, k, v, g, beta, S0, o, S_T, nseg, ws, ws_bytes, stream)
+
+
+def bwd_workspace_size(desc: FwdDesc) -> int:
+    return lib().kda_bwd_workspace_size(ctypes.byref(desc))
+
+
+def bwd_raw(desc: FwdDesc, q, k, v, g, beta, S0, dO, dST, dq, dk, dv, dg, dbeta, dS0, ws, ws_bytes, stream) -> int:
+    """Call kda_bwd with integer device addresses (0 = NULL); returns the status code."""
+    return lib().kda_bwd(ctypes.byref(desc), q, k, v, g, beta, S0, dO, dST, dq, dk, dv, dg, dbeta, dS0, ws, ws_bytes,
+                         stream)

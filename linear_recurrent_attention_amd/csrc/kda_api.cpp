@@ -10,7 +10,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // Checks shared by the forward entry points: sizes, dtypes, pointers, alignment, aliasing.
 kda_status check_common(const kda_fwd_desc* d, const void* q, const void* k, const void* v, const float* g,
-                        const float* beta, const float* S0, const void* o, const float* S_T) {
+                        const float* beta, const float* S0, const void* o, const float* S_T, bool need_o = true) {
     if (!d) return KDA_ERR_INVALID_ARG;
     if (d->B < 1 || d->H < 1 || d->T < 0 || d->Dk < 1 || d->Dv < 1) return KDA_ERR_INVALID_ARG;
     if (d->flags & ~KDA_FWD_PRECISE) return KDA_ERR_INVALID_ARG;
@@ -20,7 +20,7 @@ kda_status check_common(const kda_fwd_desc* d, const void* q, const void* k, con
     if (!(d->scale == d->scale)) return KDA_ERR_INVALID_ARG;  // NaN scale
     // sizes the kernels index with 32-bit ints: tokens and heads per call
     if ((long long)d->B * d->H > (1LL << 30) || d->T > (1 << 30)) return KDA_ERR_INVALID_ARG;
-    if (d->T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
+    if (d->T > 0 && (!q || !k || !v || !g || !beta || (need_o && !o))) return KDA_ERR_INVALID_ARG;
     if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(o, 4)) return KDA_ERR_INVALID_ARG;
     if (!aligned(g, 8) || !aligned(beta, 4) || !aligned(S0, 8) || !aligned(S_T, 8)) return KDA_ERR_INVALID_ARG;
     // outputs must not alias inputs (S_T == S0 is the one allowed overlap)
@@ -143,6 +143,51 @@ kda_status kda_fwd_cp(const kda_fwd_desc* desc, const void* q, const void* k, co
     p.precise = (desc->flags & KDA_FWD_PRECISE) != 0;
     p.ckpt_chunks = 1;
     const hipError_t e = kda::launch_fwd_cp(p, nseg, static_cast<float*>(ws), stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_bwd_workspace_size(const kda_fwd_desc* desc) {
+    if (!desc || desc->B < 1 || desc->H < 1 || desc->T < 0 || desc->Dk != desc->Dv) return 0;
+    if (desc->io_dtype == KDA_BF16 ? desc->Dk != 128 : (desc->Dk != 64 && desc->Dk != 128)) return 0;
+    if ((long long)desc->B * desc->H > (1LL << 30)) return 0;
+    return kda::bwd_workspace_bytes(desc->B, desc->T, desc->H, desc->Dk, desc->io_dtype == KDA_BF16);
+}
+
+kda_status kda_bwd(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, const float* S0, const void* dO, const float* dS_T, float* dq, float* dk,
+                   float* dv, float* dg, float* dbeta, float* dS0, void* ws, size_t ws_bytes, hipStream_t stream) {
+    kda_status st = check_common(desc, q, k, v, g, beta, S0, dO, dS_T, /*need_o=*/false);
+    if (st != KDA_OK) return st;
+    if (desc->chunk != 0) return KDA_ERR_INVALID_ARG;
+    if (desc->Dk != desc->Dv) return KDA_ERR_UNSUPPORTED;
+    if (desc->io_dtype == KDA_BF16 ? desc->Dk != 128 : (desc->Dk != 64 && desc->Dk != 128)) return KDA_ERR_UNSUPPORTED;
+    const float* outs[6] = {dq, dk, dv, dg, dbeta, dS0};
+    const void* ins[8] = {q, k, v, g, beta, S0, dO, dS_T};
+    for (const float* a : outs) {
+        if (!a) continue;
+        if (!aligned(a, 4)) return KDA_ERR_INVALID_ARG;
+        for (const void* b : ins)
+            if (b == a) return KDA_ERR_INVALID_ARG;
+        int same = 0;
+        for (const float* b : outs) same += (b == a);
+        if (same > 1) return KDA_ERR_INVALID_ARG;
+    }
+    const size_t need = kda::bwd_workspace_bytes(desc->B, desc->T, desc->H, desc->Dk, desc->io_dtype == KDA_BF16);
+    if (desc->T > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return KDA_ERR_WORKSPACE;
+    kda::BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0; p.dO = dO; p.dST = dS_T;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.dbeta = dbeta; p.dS0 = dS0;
+    p.B = desc->B; p.T = desc->T; p.H = desc->H; p.D = desc->Dk; p.scale = desc->scale;
+    hipError_t e;
+    if (desc->T == 0) {  // dS0 = dS_T (or zero)
+        kda::Params c{};
+        c.B = desc->B; c.H = desc->H; c.Dk = desc->Dk; c.Dv = desc->Dv; c.S0 = dS_T; c.S_T = dS0;
+        e = kda::launch_state_copy(c, stream);
+    } else {
+        e = kda::launch_bwd(p, desc->io_dtype == KDA_BF16, desc->o_dtype == KDA_BF16,
+                            (desc->flags & KDA_FWD_PRECISE) != 0 || desc->io_dtype == KDA_BF16, static_cast<float*>(ws),
+                            stream);
+    }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -1,0 +1,485 @@
+// Backward pass of the chunkwise KDA forward, on gfx950.
+//
+// The forward is the gated delta rule of the explainer page "Kimi K3：开放前沿智能", section 2.2
+// (paper Eq. 1), read out after the update (section 2.4), in the chunkwise form of section 2.5
+// (paper Eq. 4).  The pages give no backward formulas; these kernels apply the chain rule to each
+// line of the chunkwise forward in reverse.  Per chunk of CS = 16 tokens, with the forward
+// quantities (Q scaled; b the cumulative log-decay from the chunk start, Gamma = exp(b))
+//   Qg = Q*Gamma, Kg = K*Gamma, Kh = K/Gamma, Kb = K*exp(b_last - b), gam = Gamma_last,
+//   L = tril(Kg Kh^T, -1), A = tril(Qg Kh^T), N = (I + Diag(beta) L)^{-1}, Tm = N Diag(beta),
+//   X = V - Kg S, U = Tm X, O = Qg S + A U, S' = Diag(gam) S + Kb^T U,
+// and the gradient dS of the state after the chunk, dO of its outputs:
+//   dU = Kb dS + A^T dO;  dX = Tm^T dU (= dV);  dS_in = Diag(gam) dS + Qg^T dO - Kg^T dX
+//   dKb = U dS^T;  dgam = rowsum(dS * S);  dQg = dO S^T + dA Kh;  dA = tril(dO U^T)
+//   dTm = dU X^T;  dKg = -dX S^T + dL Kh;  dKh = dL^T Kg + dA^T Qg
+//   dbeta = colsum(N * dTm) + rowsum(dM * L);  dM = -N^T (dTm Diag(beta)) N^T;  dL = tril(Diag(beta) dM, -1)
+//   dq = dQg*scale*Gamma;  dk = dKg*Gamma + dKh/Gamma + dKb*exp(b_last - b)
+//   db = dQg*Qg + dKg*Kg - dKh*Kh - dKb*Kb (+ sum_t dKb*Kb + dgam*gam on the last row);  dg = reverse cumsum of db.
+// Under the g >= -5 bound of section 3.2 the factors of a 16-token chunk stay within [e^-80, e^80].
+//
+// Three launches (float32 arithmetic throughout):
+//   1. the forward kernel with checkpoints: the state at every interval boundary (32 tokens on the
+//      matrix-core path, 16 on the float32 path), no output;
+//   2. kda_bwd_state_kernel, one workgroup per (sequence, value half), sequential in reverse over
+//      chunks: the state gradient dS at every interval boundary (its update needs no state);
+//   3. kda_bwd_chunk_kernel, one workgroup per (sequence, interval, value half), all in parallel:
+//      every input gradient of the interval, from the interval's start state and end gradient (a
+//      32-token interval first steps its state through the first 16-token chunk).
+// Every gradient is linear in (dO, dS), so each value half computes the contributions of its own
+// value columns; the two halves' contributions to dq, dk, dg and dbeta are added with float32
+// atomics onto zeroed outputs (exactly two addends per element: the sum does not depend on order).
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace bwd {
+
+constexpr int CS = 16;   // tokens per chunk
+constexpr int NT = 256;  // threads per workgroup
+
+template <bool BF16>
+__device__ __forceinline__ float ldx(const void* p, size_t i) {
+    if constexpr (BF16)
+        return __uint_as_float((uint32_t)(reinterpret_cast<const uint16_t*>(p)[i]) << 16);
+    else
+        return reinterpret_cast<const float*>(p)[i];
+}
+
+// out(m, n) = sum_k a(m, k) b(k, n) for m < M, n < N, each thread taking RM x RN blocks; f(m, n, v)
+// receives the result.  a and b are accessors (LDS or global).
+template <int M, int N, int K, int RM, int RN, typename FA, typename FB, typename F>
+__device__ __forceinline__ void gemm(FA a, FB b, F f) {
+    static_assert(M % RM == 0 && N % RN == 0, "block shape");
+    constexpr int NBN = N / RN;
+    for (int blk = threadIdx.x; blk < (M / RM) * NBN; blk += NT) {
+        const int m0 = (blk / NBN) * RM, n0 = (blk % NBN) * RN;
+        float acc[RM][RN];
+#pragma unroll
+        for (int i = 0; i < RM; ++i)
+#pragma unroll
+            for (int j = 0; j < RN; ++j) acc[i][j] = 0.f;
+#pragma unroll 4
+        for (int k = 0; k < K; ++k) {
+            float av[RM], bv[RN];
+#pragma unroll
+            for (int i = 0; i < RM; ++i) av[i] = a(m0 + i, k);
+#pragma unroll
+            for (int j = 0; j < RN; ++j) bv[j] = b(k, n0 + j);
+#pragma unroll
+            for (int i = 0; i < RM; ++i)
+#pragma unroll
+                for (int j = 0; j < RN; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+        }
+#pragma unroll
+        for (int i = 0; i < RM; ++i)
+#pragma unroll
+            for (int j = 0; j < RN; ++j) f(m0 + i, n0 + j, acc[i][j]);
+    }
+}
+
+// Factors of one chunk, its beta, and the value-half columns of dO (and V in X when wanted).
+template <int D>
+struct alignas(16) Chunk {
+    static constexpr int DH = D / 2;
+    float Qg[CS][D + 1], Kg[CS][D + 1], Kh[CS][D + 1], Kb[CS][D + 1], Gam[CS][D + 1];
+    float gam[D];
+    float X[CS][DH + 1], U[CS][DH + 1], dO[CS][DH + 1], dU[CS][DH + 1], dX[CS][DH + 1];
+    float L[CS][CS + 1], A[CS][CS + 1], N[CS][CS + 1], Tm[CS][CS + 1];
+    float beta[CS];
+};
+
+template <int D, bool IN_BF16, bool DO_BF16>
+__device__ __forceinline__ void load_chunk(Chunk<D>& c, const BwdParams& p, int b, int h, int c0, int half, bool want_v) {
+    constexpr int DH = D / 2;
+    const int tid = threadIdx.x;
+    const int n = min(CS, p.T - c0);  // valid tokens (>= 1)
+    auto row = [&](int r) { return ((size_t)b * p.T + c0 + min(r, n - 1)) * p.H + h; };
+    if (tid < D) {
+        const int ch = tid;
+        float bc[CS];
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < CS; ++r) {
+            const float gv = p.g[row(r) * D + ch];
+            s += r < n ? gv : 0.f;
+            bc[r] = s;
+        }
+        const float last = bc[CS - 1];
+        c.gam[ch] = fexp(last);
+#pragma unroll
+        for (int r = 0; r < CS; ++r) {
+            const float qv = ldx<IN_BF16>(p.q, row(r) * D + ch), kv = ldx<IN_BF16>(p.k, row(r) * D + ch);
+            const float q = r < n ? qv * p.scale : 0.f, k = r < n ? kv : 0.f;
+            const float e = fexp(bc[r]);
+            c.Gam[r][ch] = e;
+            c.Qg[r][ch] = q * e;
+            c.Kg[r][ch] = k * e;
+            c.Kh[r][ch] = k * fexp(-bc[r]);
+            c.Kb[r][ch] = k * fexp(last - bc[r]);
+        }
+    }
+    if (tid < CS) {
+        const float bv = p.beta[row(tid)];
+        c.beta[tid] = tid < n ? bv : 0.f;
+    }
+    for (int e = tid; e < CS * DH; e += NT) {
+        const int r = e / DH, j = e % DH;
+        const size_t idx = row(r) * D + half * DH + j;
+        float dov = 0.f;
+        if (p.dO) dov = ldx<DO_BF16>(p.dO, idx);
+        c.dO[r][j] = r < n ? dov : 0.f;
+        if (want_v) {
+            const float vv = ldx<IN_BF16>(p.v, idx);
+            c.X[r][j] = r < n ? vv : 0.f;
+        }
+    }
+}
+
+// L, A (one entry per thread), then N = (I + Diag(beta) L)^{-1} and Tm = N Diag(beta) by forward
+// substitution, one column per thread.
+template <int D>
+__device__ __forceinline__ void chunk_triangles(Chunk<D>& c) {
+    const int tid = threadIdx.x;
+    {
+        const int t = tid / CS, s = tid % CS;
+        float l = 0.f, a = 0.f;
+        for (int ch = 0; ch < D; ++ch) {
+            l = __builtin_fmaf(c.Kg[t][ch], c.Kh[s][ch], l);
+            a = __builtin_fmaf(c.Qg[t][ch], c.Kh[s][ch], a);
+        }
+        c.L[t][s] = s < t ? l : 0.f;
+        c.A[t][s] = s <= t ? a : 0.f;
+    }
+    __syncthreads();
+    if (tid < CS) {
+        const int j = tid;
+        float x[CS];
+#pragma unroll
+        for (int i = 0; i < CS; ++i) {
+            float acc = (i == j) ? 1.f : 0.f;
+            for (int m = 0; m < i; ++m) acc -= c.beta[i] * c.L[i][m] * x[m];
+            x[i] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < CS; ++i) {
+            c.N[i][j] = x[i];
+            c.Tm[i][j] = x[i] * c.beta[j];
+        }
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------------------
+// 2. state gradients at interval boundaries, sequential in reverse
+// ------------------------------------------------------------------------------------------------
+template <int D, int CK, bool IN_BF16, bool DO_BF16>
+__global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
+    constexpr int DH = D / 2;
+    __shared__ Chunk<D> c;
+    __shared__ float dS[D][DH + 1];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x >> 1, half = blockIdx.x & 1;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int nint = p.nint;
+    auto at = [&](int i) { return ((size_t)bh * nint + i) * D * D + half * DH; };  // [bh][i][row][half*DH + col]
+
+    for (int e = tid; e < D * DH; e += NT) {
+        const int r = e / DH, j = e % DH;
+        const float v = p.dST ? p.dST[(size_t)bh * D * D + (size_t)r * D + half * DH + j] : 0.f;
+        dS[r][j] = v;
+        p.dSb[at(nint - 1) + (size_t)r * D + j] = v;
+    }
+    __syncthreads();
+    for (int i = nint - 1; i >= 0; --i) {
+        const int nsub = (min(CK, p.T - i * CK) + CS - 1) / CS;
+        for (int s = nsub - 1; s >= 0; --s) {
+            load_chunk<D, IN_BF16, DO_BF16>(c, p, b, h, i * CK + s * CS, half, false);
+            __syncthreads();
+            chunk_triangles<D>(c);
+            // dU = Kb dS + A^T dO
+            gemm<CS, DH, D, 2, 4>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dS[k][n]; },
+                                  [&](int m, int n, float v) { c.dU[m][n] = v; });
+            gemm<CS, DH, CS, 2, 4>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+                                   [&](int m, int n, float v) { c.dU[m][n] += v; });
+            __syncthreads();
+            // dX = Tm^T dU
+            gemm<CS, DH, CS, 2, 4>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
+                                   [&](int m, int n, float v) { c.dX[m][n] = v; });
+            __syncthreads();
+            // dS <- Diag(gam) dS + Qg^T dO - Kg^T dX   (each entry read and written by its own thread)
+            gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Qg[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+                                  [&](int m, int n, float v) { dS[m][n] = __builtin_fmaf(c.gam[m], dS[m][n], v); });
+            gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Kg[k][m]; }, [&](int k, int n) { return c.dX[k][n]; },
+                                  [&](int m, int n, float v) { dS[m][n] -= v; });
+            __syncthreads();
+        }
+        if (i >= 1) {
+            for (int e = tid; e < D * DH; e += NT) {
+                const int r = e / DH, j = e % DH;
+                p.dSb[at(i - 1) + (size_t)r * D + j] = dS[r][j];
+            }
+        }
+    }
+    if (p.dS0) {
+        for (int e = tid; e < D * DH; e += NT) {
+            const int r = e / DH, j = e % DH;
+            p.dS0[(size_t)bh * D * D + (size_t)r * D + half * DH + j] = dS[r][j];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// 3. input gradients, one interval per workgroup (value half)
+// ------------------------------------------------------------------------------------------------
+template <int D>
+struct alignas(16) Grad {
+    static constexpr int DH = D / 2;
+    float G[CS][D + 1];       // one key-side gradient at a time (dKb, dQg, dKg, dKh)
+    float dK[CS][D + 1];      // dk, accumulated
+    float db[CS][D + 1];      // gradient of the cumulative decay, accumulated
+    float SM[D][DH + 1];      // the state after the interval's first chunk, then its gradient
+    float dA[CS][CS + 1], dTm[CS][CS + 1], dN[CS][CS + 1], dM[CS][CS + 1], T1[CS][CS + 1];
+    float dgam[D], dlast[D];
+    float dbeta[CS];
+};
+
+template <int D, int CK, bool IN_BF16, bool DO_BF16>
+__global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
+    constexpr int DH = D / 2;
+    __shared__ Chunk<D> c;
+    __shared__ Grad<D> gr;
+    const int tid = threadIdx.x;
+    const int half = blockIdx.x & 1;
+    const int wi = blockIdx.x >> 1;
+    const int bh = wi / p.nint, i = wi - bh * p.nint;
+    const int b = bh / p.H, h = bh - b * p.H;
+    // start state of the interval (global, full rows; this half's columns) and end gradient
+    const float* S0g = i == 0 ? (p.S0 ? p.S0 + (size_t)bh * D * D : nullptr) : p.Sck + ((size_t)bh * p.nck + i - 1) * D * D;
+    const float* dSe = p.dSb + ((size_t)bh * p.nint + i) * D * D;
+    const int col0 = half * DH;
+    const int nsub = (min(CK, p.T - i * CK) + CS - 1) / CS;
+    auto Sg = [&](int r, int j) { return S0g ? S0g[(size_t)r * D + col0 + j] : 0.f; };
+
+    if (nsub == 2) {  // the state after the first chunk: SM = Diag(gam) S + Kb^T Tm (V - Kg S)
+        load_chunk<D, IN_BF16, DO_BF16>(c, p, b, h, i * CK, half, true);
+        __syncthreads();
+        chunk_triangles<D>(c);
+        gemm<CS, DH, D, 2, 4>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return Sg(k, n); },
+                              [&](int m, int n, float v) { c.X[m][n] -= v; });
+        __syncthreads();
+        gemm<CS, DH, CS, 2, 4>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
+                               [&](int m, int n, float v) { c.U[m][n] = v; });
+        __syncthreads();
+        gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Kb[k][m]; }, [&](int k, int n) { return c.U[k][n]; },
+                              [&](int m, int n, float v) { gr.SM[m][n] = __builtin_fmaf(c.gam[m], Sg(m, n), v); });
+        __syncthreads();
+    }
+    for (int s = nsub - 1; s >= 0; --s) {
+        const int c0 = i * CK + s * CS;
+        const bool s_lds = s == 1;             // the chunk's start state is SM (else the interval's start state)
+        const bool ds_lds = s < nsub - 1;      // the chunk's end gradient is SM (else the interval's end gradient)
+        auto S = [&](int r, int j) { return s_lds ? gr.SM[r][j] : Sg(r, j); };
+        auto dS = [&](int r, int j) { return ds_lds ? gr.SM[r][j] : dSe[(size_t)r * D + col0 + j]; };
+        load_chunk<D, IN_BF16, DO_BF16>(c, p, b, h, c0, half, true);
+        __syncthreads();
+        chunk_triangles<D>(c);
+        // X = V - Kg S;  U = Tm X
+        gemm<CS, DH, D, 2, 4>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return S(k, n); },
+                              [&](int m, int n, float v) { c.X[m][n] -= v; });
+        __syncthreads();
+        gemm<CS, DH, CS, 2, 4>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
+                               [&](int m, int n, float v) { c.U[m][n] = v; });
+        __syncthreads();
+        // dU = Kb dS + A^T dO;  dKb = U dS^T;  dgam = rowsum(dS * S);  dA = tril(dO U^T)
+        gemm<CS, DH, D, 2, 4>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dS(k, n); },
+                              [&](int m, int n, float v) { c.dU[m][n] = v; });
+        gemm<CS, DH, CS, 2, 4>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+                               [&](int m, int n, float v) { c.dU[m][n] += v; });
+        gemm<CS, D, DH, 2, 4>([&](int m, int k) { return c.U[m][k]; }, [&](int k, int n) { return dS(n, k); },
+                              [&](int m, int n, float v) { gr.G[m][n] = v; });
+        if (tid < D) {
+            float a = 0.f;
+            for (int j = 0; j < DH; ++j) a = __builtin_fmaf(dS(tid, j), S(tid, j), a);
+            gr.dgam[tid] = a;
+        }
+        gemm<CS, CS, DH, 1, 1>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return c.U[n][k]; },
+                               [&](int m, int n, float v) { gr.dA[m][n] = n <= m ? v : 0.f; });
+        __syncthreads();
+        // fold dKb: dk = dKb exp(b_last - b);  db = -dKb Kb;  last row: sum_t dKb Kb + dgam gam
+        for (int e = tid; e < CS * D; e += NT) {
+            const int r = e / D, ch = e % D;
+            const float gk = gr.G[r][ch];
+            gr.dK[r][ch] = gk * (c.gam[ch] / c.Gam[r][ch]);
+            gr.db[r][ch] = -gk * c.Kb[r][ch];
+        }
+        if (tid < D) {
+            float a = gr.dgam[tid] * c.gam[tid];
+            for (int r = 0; r < CS; ++r) a = __builtin_fmaf(gr.G[r][tid], c.Kb[r][tid], a);
+            gr.dlast[tid] = a;
+        }
+        // dTm = dU X^T;  dX = Tm^T dU  (dv)
+        gemm<CS, CS, DH, 1, 1>([&](int m, int k) { return c.dU[m][k]; }, [&](int k, int n) { return c.X[n][k]; },
+                               [&](int m, int n, float v) { gr.dTm[m][n] = v; });
+        gemm<CS, DH, CS, 2, 4>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
+                               [&](int m, int n, float v) { c.dX[m][n] = v; });
+        __syncthreads();
+        // dN = dTm Diag(beta);  dbeta = colsum(N * dTm);  dM = -N^T dN N^T;  dbeta += rowsum(dM * L);
+        // dL = tril(Diag(beta) dM, -1) (kept in dM)
+        {
+            const int r = tid / CS, q = tid % CS;
+            gr.dN[r][q] = gr.dTm[r][q] * c.beta[q];
+        }
+        if (tid < CS) {
+            float a = 0.f;
+            for (int r = 0; r < CS; ++r) a = __builtin_fmaf(c.N[r][tid], gr.dTm[r][tid], a);
+            gr.dbeta[tid] = a;
+        }
+        __syncthreads();
+        gemm<CS, CS, CS, 1, 1>([&](int m, int k) { return c.N[k][m]; }, [&](int k, int n) { return gr.dN[k][n]; },
+                               [&](int m, int n, float v) { gr.T1[m][n] = v; });
+        __syncthreads();
+        gemm<CS, CS, CS, 1, 1>([&](int m, int k) { return gr.T1[m][k]; }, [&](int k, int n) { return c.N[n][k]; },
+                               [&](int m, int n, float v) { gr.dM[m][n] = -v; });
+        __syncthreads();
+        if (tid < CS) {
+            float a = 0.f;
+            for (int q = 0; q < CS; ++q) a = __builtin_fmaf(gr.dM[tid][q], c.L[tid][q], a);
+            gr.dbeta[tid] += a;
+        }
+        __syncthreads();
+        {
+            const int r = tid / CS, q = tid % CS;
+            gr.dM[r][q] = q < r ? c.beta[r] * gr.dM[r][q] : 0.f;  // now dL
+        }
+        __syncthreads();
+        // dQg = dO S^T + dA Kh  -> dq = dQg scale Gamma (Qg holds the scale), db += dQg Qg
+        gemm<CS, D, DH, 2, 4>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return S(n, k); },
+                              [&](int m, int n, float v) { gr.G[m][n] = v; });
+        gemm<CS, D, CS, 2, 4>([&](int m, int k) { return gr.dA[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
+                              [&](int m, int n, float v) { gr.G[m][n] += v; });
+        __syncthreads();
+        const int n_ok = min(CS, p.T - c0);
+        for (int e = tid; e < CS * D; e += NT) {
+            const int r = e / D, ch = e % D;
+            const float gq = gr.G[r][ch];
+            gr.db[r][ch] = __builtin_fmaf(gq, c.Qg[r][ch], gr.db[r][ch]);
+            if (r < n_ok && p.dq) atomicAdd(&p.dq[(((size_t)b * p.T + c0 + r) * p.H + h) * D + ch], gq * p.scale * c.Gam[r][ch]);
+        }
+        __syncthreads();
+        // dKg = -dX S^T + dL Kh -> dk += dKg Gamma, db += dKg Kg
+        gemm<CS, D, DH, 2, 4>([&](int m, int k) { return c.dX[m][k]; }, [&](int k, int n) { return S(n, k); },
+                              [&](int m, int n, float v) { gr.G[m][n] = -v; });
+        gemm<CS, D, CS, 2, 4>([&](int m, int k) { return gr.dM[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
+                              [&](int m, int n, float v) { gr.G[m][n] += v; });
+        __syncthreads();
+        for (int e = tid; e < CS * D; e += NT) {
+            const int r = e / D, ch = e % D;
+            const float gk = gr.G[r][ch];
+            gr.dK[r][ch] = __builtin_fmaf(gk, c.Gam[r][ch], gr.dK[r][ch]);
+            gr.db[r][ch] = __builtin_fmaf(gk, c.Kg[r][ch], gr.db[r][ch]);
+        }
+        __syncthreads();
+        // dKh = dL^T Kg + dA^T Qg -> dk += dKh / Gamma, db -= dKh Kh
+        gemm<CS, D, CS, 2, 4>([&](int m, int k) { return gr.dM[k][m]; }, [&](int k, int n) { return c.Kg[k][n]; },
+                              [&](int m, int n, float v) { gr.G[m][n] = v; });
+        gemm<CS, D, CS, 2, 4>([&](int m, int k) { return gr.dA[k][m]; }, [&](int k, int n) { return c.Qg[k][n]; },
+                              [&](int m, int n, float v) { gr.G[m][n] += v; });
+        __syncthreads();
+        for (int e = tid; e < CS * D; e += NT) {
+            const int r = e / D, ch = e % D;
+            const float gh = gr.G[r][ch];
+            gr.dK[r][ch] += gh / c.Gam[r][ch];
+            gr.db[r][ch] = __builtin_fmaf(-gh, c.Kh[r][ch], gr.db[r][ch]);
+        }
+        __syncthreads();
+        // outputs of the chunk: dk, dv, dbeta, dg (reverse cumulative sum of db)
+        for (int e = tid; e < CS * D; e += NT) {
+            const int r = e / D, ch = e % D;
+            if (r < n_ok && p.dk) atomicAdd(&p.dk[(((size_t)b * p.T + c0 + r) * p.H + h) * D + ch], gr.dK[r][ch]);
+        }
+        for (int e = tid; e < CS * DH; e += NT) {
+            const int r = e / DH, j = e % DH;
+            if (r < n_ok && p.dv) p.dv[(((size_t)b * p.T + c0 + r) * p.H + h) * D + col0 + j] = c.dX[r][j];
+        }
+        if (tid < CS && tid < n_ok && p.dbeta) atomicAdd(&p.dbeta[((size_t)b * p.T + c0 + tid) * p.H + h], gr.dbeta[tid]);
+        if (tid < D && p.dg) {
+            float a = gr.dlast[tid];
+            for (int r = CS - 1; r >= 0; --r) {
+                a += gr.db[r][tid];
+                if (r < n_ok) atomicAdd(&p.dg[(((size_t)b * p.T + c0 + r) * p.H + h) * D + tid], a);
+            }
+        }
+        if (s == 1) {
+            // the gradient of the state between the interval's two chunks:
+            // Diag(gam) dS + Qg^T dO - Kg^T dX, into SM once every read of SM (as S) is done
+            __syncthreads();
+            gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Qg[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+                                  [&](int m, int n, float v) { gr.SM[m][n] = __builtin_fmaf(c.gam[m], dSe[(size_t)m * D + col0 + n], v); });
+            gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Kg[k][m]; }, [&](int k, int n) { return c.dX[k][n]; },
+                                  [&](int m, int n, float v) { gr.SM[m][n] -= v; });
+        }
+        __syncthreads();
+    }
+}
+
+// Zero the accumulated outputs.
+__global__ void kda_bwd_zero_kernel(float* a, size_t na, float* b, size_t nb, float* c, size_t nc, float* d, size_t nd) {
+    const size_t st = (size_t)gridDim.x * blockDim.x;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < na + nb + nc + nd; e += st) {
+        if (e < na) { if (a) a[e] = 0.f; }
+        else if (e < na + nb) { if (b) b[e - na] = 0.f; }
+        else if (e < na + nb + nc) { if (c) c[e - na - nb] = 0.f; }
+        else if (d) d[e - na - nb - nc] = 0.f;
+    }
+}
+
+template <int D, int CK, bool IN_BF16, bool DO_BF16>
+hipError_t launch_kernels(const BwdParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL((kda_bwd_state_kernel<D, CK, IN_BF16, DO_BF16>), dim3((unsigned)(2 * p.B * p.H)), dim3(NT), 0,
+                       stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kda_bwd_chunk_kernel<D, CK, IN_BF16, DO_BF16>),
+                       dim3((unsigned)(2 * (size_t)p.B * p.H * p.nint)), dim3(NT), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace bwd
+
+size_t bwd_workspace_bytes(int B, int T, int H, int D, bool in_bf16) {
+    const int CK = in_bf16 ? 32 : 16;
+    const size_t nint = (size_t)(T + CK - 1) / CK;
+    return 2 * (size_t)B * H * nint * D * D * sizeof(float);
+}
+
+hipError_t launch_bwd(const BwdParams& p0, bool in_bf16, bool do_bf16, bool precise, float* ws, hipStream_t stream) {
+    BwdParams p = p0;
+    const int D = p.D;
+    const int CK = in_bf16 ? 32 : 16;
+    p.nint = (p.T + CK - 1) / CK;
+    p.nck = p.T / CK;  // checkpoints the forward records (entry i - 1 starts interval i)
+    const size_t per = (size_t)p.B * p.H * p.nint * D * D;
+    p.Sck = ws;
+    p.dSb = ws + per;
+    // 1. the forward's states at interval boundaries (entry i = after interval i)
+    Params f{};  // zero: every optional field off
+    f.q = p.q; f.k = p.k; f.v = p.v; f.g = p.g; f.beta = p.beta; f.S0 = p.S0; f.o = nullptr; f.S_T = nullptr;
+    f.B = p.B; f.T = p.T; f.H = p.H; f.Dk = D; f.Dv = D; f.tstride = p.T; f.scale = p.scale;
+    f.precise = precise;
+    f.S_ckpt = ws; f.ckpt_chunks = 1; f.n_ckpt = p.T / CK;
+    hipError_t e = hipSuccess;
+    if (f.n_ckpt > 0) e = in_bf16 ? launch_fwd_bf16(f, stream) : launch_fwd_f32(f, stream);
+    if (e != hipSuccess) return e;
+    // 2. zero the accumulated outputs
+    const size_t nk = (size_t)p.B * p.T * p.H * D;
+    hipLaunchKernelGGL(bwd::kda_bwd_zero_kernel, dim3(2048), dim3(256), 0, stream, p.dq, p.dq ? nk : 0, p.dk,
+                       p.dk ? nk : 0, p.dg, p.dg ? nk : 0, p.dbeta, p.dbeta ? (size_t)p.B * p.T * p.H : 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 3. state gradients, then the input gradients
+    if (!in_bf16) return D == 64 ? bwd::launch_kernels<64, 16, false, false>(p, stream)
+                                 : bwd::launch_kernels<128, 16, false, false>(p, stream);
+    return do_bf16 ? bwd::launch_kernels<128, 32, true, true>(p, stream)   // bf16 inputs: D = 128
+                   : bwd::launch_kernels<128, 32, true, false>(p, stream);
+}
+
+}  // namespace kda

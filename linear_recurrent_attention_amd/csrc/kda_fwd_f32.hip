@@ -127,8 +127,8 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_f32_kernel(Params p) {
             sm.u[r][j] = u;
         }
         __syncthreads();
-        // O = Qg S + A U
-        for (int e = tid; e < C * D; e += NTHR) {
+        // O = Qg S + A U (skipped when o == NULL: a state-only run)
+        for (int e = tid; o && e < C * D; e += NTHR) {
             const int r = e / D, j = e % D;
             if (r >= n) continue;
             float acc = 0.f;

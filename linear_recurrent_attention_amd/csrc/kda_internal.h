@@ -25,6 +25,29 @@ struct Params {
     int n_ckpt;        // checkpoints per sequence: full multiples of ckpt_chunks chunks within T
 };
 
+// Backward problem (all float32 gradients; NULL outputs are skipped).
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* S0;   // may be null
+    const void* dO;    // may be null (zero); dtype: bf16 or float32
+    const float* dST;  // may be null (zero)
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dg;
+    float* dbeta;
+    float* dS0;
+    const float* Sck;  // workspace: states after each full interval [B*H][nck][D][D]
+    float* dSb;        // workspace: state gradients after each interval [B*H][nint][D][D]
+    int B, T, H, D;
+    float scale;
+    int nint, nck;     // intervals (ceil(T / interval)), checkpoints (T / interval)
+};
+
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t stream);  // Dk = Dv = 128, chunk 32 (in_f32 too)
 hipError_t launch_fwd_f32(const Params& p, hipStream_t stream);   // Dk = Dv in {64, 128}, chunk 16
 hipError_t launch_state_copy(const Params& p, hipStream_t stream); // T = 0: S_T = S0 (or 0)
@@ -32,5 +55,8 @@ hipError_t launch_decode(const Params& p, bool in_bf16, hipStream_t stream);  //
 // in-device context parallelism (bf16 I/O, Dk = Dv = 128): segment count nseg_req (0 = automatic)
 size_t cp_workspace_bytes(int B, int T, int H, int nseg_req);
 hipError_t launch_fwd_cp(const Params& p, int nseg_req, float* ws, hipStream_t stream);
+// backward: intervals of 32 tokens (bf16 inputs, D = 128) or 16 (float32 inputs, D in {64, 128})
+size_t bwd_workspace_bytes(int B, int T, int H, int D, bool in_bf16);
+hipError_t launch_bwd(const BwdParams& p, bool in_bf16, bool do_bf16, bool precise, float* ws, hipStream_t stream);
 
 }  // namespace kda

@@ -205,3 +205,36 @@ def test_cp_argument_checks():
     assert call_cp(desc(B=0), 2) == _lib.KDA_ERR_INVALID_ARG
     # T = 0: the state copy only (nothing launched without S_T)
     assert call_cp(desc(T=0), 4, q=0, k=0, v=0, g=0, beta=0, o=0) == _lib.KDA_OK
+
+
+def test_bwd_workspace_size():
+    # bf16 inputs: 32-token intervals; float32 inputs: 16-token intervals; two [B, H, n, D, D] arrays
+    assert _lib.bwd_workspace_size(desc(B=2, T=100, H=3)) == 2 * 2 * 3 * 4 * 128 * 128 * 4
+    d32 = desc(B=1, T=100, H=2, Dk=64, Dv=64, io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_F32)
+    assert _lib.bwd_workspace_size(d32) == 2 * 1 * 2 * 7 * 64 * 64 * 4
+    assert _lib.bwd_workspace_size(desc(Dk=64, Dv=64)) == 0          # bf16 inputs need D = 128
+    assert _lib.bwd_workspace_size(desc(B=0)) == 0
+
+
+def call_bwd(d, ws=0, ws_bytes=0, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=0, dO=FAKE + 0x100000, dST=0, dq=FAKE + 0x200000,
+             dk=FAKE + 0x300000, dv=FAKE + 0x400000, dg=FAKE + 0x500000, dbeta=FAKE + 0x600000, dS0=0)
+    a.update(kw)
+    return _lib.bwd_raw(d, *[a[n] for n in ("q", "k", "v", "g", "beta", "S0", "dO", "dST", "dq", "dk", "dv", "dg",
+                                            "dbeta", "dS0")], ws, ws_bytes, None)
+
+
+def test_bwd_argument_checks():
+    d = desc(T=64)
+    need = _lib.bwd_workspace_size(d)
+    ws = FAKE + 0x1000000
+    assert call_bwd(d) == _lib.KDA_ERR_WORKSPACE
+    assert call_bwd(d, ws=ws, ws_bytes=need - 4) == _lib.KDA_ERR_WORKSPACE
+    assert call_bwd(desc(chunk=32), ws=ws, ws_bytes=need) == _lib.KDA_ERR_INVALID_ARG
+    assert call_bwd(desc(Dk=64, Dv=64), ws=ws, ws_bytes=need) == _lib.KDA_ERR_UNSUPPORTED
+    assert call_bwd(d, ws=ws, ws_bytes=need, dq=FAKE) == _lib.KDA_ERR_INVALID_ARG          # dq aliases q
+    assert call_bwd(d, ws=ws, ws_bytes=need, dk=FAKE + 0x200000) == _lib.KDA_ERR_INVALID_ARG  # dk aliases dq
+    assert call_bwd(d, ws=ws, ws_bytes=need, dg=FAKE + 0x500002) == _lib.KDA_ERR_INVALID_ARG  # misaligned
+    assert call_bwd(desc(B=0), ws=ws, ws_bytes=need) == _lib.KDA_ERR_INVALID_ARG
+    # T = 0: dS0 = dS_T; with dS0 = NULL nothing is launched
+    assert call_bwd(desc(T=0), q=0, k=0, v=0, g=0, beta=0, dO=0) == _lib.KDA_OK
