@@ -215,6 +215,51 @@ def bench_longctx(args, torch, synth, kda):
     print(json.dumps(out), flush=True)
 
 
+def bwd_bytes(B, T, H, D, io_bytes=2):
+    """HBM bytes kda_bwd must move at least: q, k, v, dO (io dtype), g, beta read; dq, dk, dg, dv
+    (float32) and dbeta written; the state gradient dS0 (float32)."""
+    per_token_head = 4 * D * io_bytes + 4 * D + 4 + 4 * 4 * D + 4
+    return B * T * H * per_token_head + B * H * D * D * 4
+
+
+def bench_bwd(args, torch, synth, kda):
+    """kda_bwd on the prefill workload B=4, H=32, T=16384, D=128 (bf16 q/k/v/dO, float32 gradients):
+    one step = the whole backward (state recompute, reverse state-gradient pass, input gradients)."""
+    w = synth.WORKLOADS[WORKLOAD]
+    B, T, H, D = w.B, w.T, w.H, w.Dk
+    d = synth.core_inputs(WORKLOAD, seed=0)
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v", "g", "beta")}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(torch.bfloat16)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    dO = torch.randn((B, T, H, D), device=dev, generator=gen).to(torch.bfloat16)
+    from linear_recurrent_attention_amd import _lib
+    desc = _lib.FwdDesc(B, T, H, D, D, 0, _lib.KDA_BF16, _lib.KDA_BF16, 1.0, 0)
+    ws = torch.empty(_lib.bwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step():
+        kda.kda_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], dO=dO, workspace=ws)
+
+    wall, launch_ms = time_steps(torch, step, stream, args)
+    avg_s = float(np.mean(launch_ms)) / 1e3
+    abytes = bwd_bytes(B, T, H, D)
+    gbs = abytes / avg_s / 1e9
+    out = {
+        "metric": "KDA backward tokens/s at H=32,d=128,T=16K (1 GPU)", "value": B * T / (wall / args.steps),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "kda_bwd_bf16_B4_H32_T16384_D128", "B": B, "H": H, "T": T, "D": D,
+                   "io": "bf16 q/k/v/dO, float32 g/beta and gradients"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "kda_bwd (all kernels)",
+                     "avg_call_ms": avg_s * 1e3, "algorithmic_bytes": abytes},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def layer_flops(B, T, d, H, D, R):
     """Matrix-product flops of one fused-layer call: the q, k, v, gate and output projections, beta,
     the rank-R decay projection, and the chunkwise core (as algorithmic_flops)."""
@@ -286,10 +331,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run one plain 512 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=("core", "layer", "decode", "longctx"), default="core",
+    ap.add_argument("--workload", choices=("core", "layer", "decode", "longctx", "bwd"), default="core",
                     help="core: kda_fwd on B4 H32 T16384 (the headline line); layer: kda_layer_fwd on "
                          "B2 T8192 d_model 2048 H16; decode: kda_decode on B128 H32, one token; longctx: "
-                         "kda_fwd_cp on B1 H16 T1M (separate lines)")
+                         "kda_fwd_cp on B1 H16 T1M; bwd: kda_bwd on B4 H32 T16384 (separate lines)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus N with N > 1 is not supported "
@@ -308,6 +353,9 @@ def main():
         return
     if args.workload == "longctx":
         bench_longctx(args, torch, synth, kda)
+        return
+    if args.workload == "bwd":
+        bench_bwd(args, torch, synth, kda)
         return
     w = synth.WORKLOADS[WORKLOAD]
     B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv

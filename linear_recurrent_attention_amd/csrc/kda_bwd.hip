@@ -35,7 +35,8 @@ namespace kda {
 namespace bwd {
 
 constexpr int CS = 16;   // tokens per chunk
-constexpr int NT = 256;  // threads per workgroup
+constexpr int NT = 512;  // threads per workgroup (8 waves)
+static_assert(NT >= CS * CS, "one thread per chunk-matrix entry");
 
 template <bool BF16>
 __device__ __forceinline__ float ldx(const void* p, size_t i) {
@@ -88,28 +89,64 @@ struct alignas(16) Chunk {
     float beta[CS];
 };
 
+// One chunk's inputs as this thread holds them: channel tid's q, k, g over the chunk's tokens
+// (tid < D), beta of token tid (tid < CS), and dO / V entries tid + NT*k of the value half.
+template <int D>
+struct Raw {
+    static constexpr int PV = CS * (D / 2) / NT;
+    float q[CS], k[CS], g[CS];
+    float beta;
+    float dO[PV], v[PV];
+    int n;  // valid tokens
+};
+
 template <int D, bool IN_BF16, bool DO_BF16>
-__device__ __forceinline__ void load_chunk(Chunk<D>& c, const BwdParams& p, int b, int h, int c0, int half, bool want_v) {
+__device__ __forceinline__ void fetch_chunk(Raw<D>& w, const BwdParams& p, int b, int h, int c0, int half, bool want_v) {
     constexpr int DH = D / 2;
     const int tid = threadIdx.x;
-    const int n = min(CS, p.T - c0);  // valid tokens (>= 1)
+    const int n = min(CS, p.T - c0);  // valid tokens (>= 1); rows past them read the last valid one
+    w.n = n;
     auto row = [&](int r) { return ((size_t)b * p.T + c0 + min(r, n - 1)) * p.H + h; };
+    if (tid < D) {
+#pragma unroll
+        for (int r = 0; r < CS; ++r) {
+            w.g[r] = p.g[row(r) * D + tid];
+            w.q[r] = ldx<IN_BF16>(p.q, row(r) * D + tid);
+            w.k[r] = ldx<IN_BF16>(p.k, row(r) * D + tid);
+        }
+    }
+    if (tid < CS) w.beta = p.beta[row(tid)];
+#pragma unroll
+    for (int k = 0; k < Raw<D>::PV; ++k) {
+        const int e = tid + NT * k, r = e / DH, j = e % DH;
+        const size_t idx = row(r) * D + half * DH + j;
+        w.dO[k] = 0.f;
+        if (p.dO) w.dO[k] = ldx<DO_BF16>(p.dO, idx);  // dO == NULL: zero (never dereferenced)
+        if (want_v) w.v[k] = ldx<IN_BF16>(p.v, idx);
+    }
+}
+
+// The chunk's factors from the fetched inputs (tokens past the valid ones are zeroed: k = q = v = 0,
+// g = 0, beta = 0, dO = 0).
+template <int D>
+__device__ __forceinline__ void build_chunk(Chunk<D>& c, const Raw<D>& w, float scale, bool want_v) {
+    constexpr int DH = D / 2;
+    const int tid = threadIdx.x;
+    const int n = w.n;
     if (tid < D) {
         const int ch = tid;
         float bc[CS];
         float s = 0.f;
 #pragma unroll
         for (int r = 0; r < CS; ++r) {
-            const float gv = p.g[row(r) * D + ch];
-            s += r < n ? gv : 0.f;
+            s += r < n ? w.g[r] : 0.f;
             bc[r] = s;
         }
         const float last = bc[CS - 1];
         c.gam[ch] = fexp(last);
 #pragma unroll
         for (int r = 0; r < CS; ++r) {
-            const float qv = ldx<IN_BF16>(p.q, row(r) * D + ch), kv = ldx<IN_BF16>(p.k, row(r) * D + ch);
-            const float q = r < n ? qv * p.scale : 0.f, k = r < n ? kv : 0.f;
+            const float q = r < n ? w.q[r] * scale : 0.f, k = r < n ? w.k[r] : 0.f;
             const float e = fexp(bc[r]);
             c.Gam[r][ch] = e;
             c.Qg[r][ch] = q * e;
@@ -118,21 +155,20 @@ __device__ __forceinline__ void load_chunk(Chunk<D>& c, const BwdParams& p, int 
             c.Kb[r][ch] = k * fexp(last - bc[r]);
         }
     }
-    if (tid < CS) {
-        const float bv = p.beta[row(tid)];
-        c.beta[tid] = tid < n ? bv : 0.f;
+    if (tid < CS) c.beta[tid] = tid < n ? w.beta : 0.f;
+#pragma unroll
+    for (int k = 0; k < Raw<D>::PV; ++k) {
+        const int e = tid + NT * k, r = e / DH, j = e % DH;
+        c.dO[r][j] = r < n ? w.dO[k] : 0.f;
+        if (want_v) c.X[r][j] = r < n ? w.v[k] : 0.f;
     }
-    for (int e = tid; e < CS * DH; e += NT) {
-        const int r = e / DH, j = e % DH;
-        const size_t idx = row(r) * D + half * DH + j;
-        float dov = 0.f;
-        if (p.dO) dov = ldx<DO_BF16>(p.dO, idx);
-        c.dO[r][j] = r < n ? dov : 0.f;
-        if (want_v) {
-            const float vv = ldx<IN_BF16>(p.v, idx);
-            c.X[r][j] = r < n ? vv : 0.f;
-        }
-    }
+}
+
+template <int D, bool IN_BF16, bool DO_BF16>
+__device__ __forceinline__ void load_chunk(Chunk<D>& c, const BwdParams& p, int b, int h, int c0, int half, bool want_v) {
+    Raw<D> w;
+    fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, c0, half, want_v);
+    build_chunk<D>(c, w, p.scale, want_v);
 }
 
 // L, A (one entry per thread), then N = (I + Diag(beta) L)^{-1} and Tm = N Diag(beta) by forward
@@ -140,7 +176,7 @@ __device__ __forceinline__ void load_chunk(Chunk<D>& c, const BwdParams& p, int 
 template <int D>
 __device__ __forceinline__ void chunk_triangles(Chunk<D>& c) {
     const int tid = threadIdx.x;
-    {
+    if (tid < CS * CS) {
         const int t = tid / CS, s = tid % CS;
         float l = 0.f, a = 0.f;
         for (int ch = 0; ch < D; ++ch) {
@@ -189,21 +225,27 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
         dS[r][j] = v;
         p.dSb[at(nint - 1) + (size_t)r * D + j] = v;
     }
+    // chunks in reverse order; the next one's inputs are fetched while the current one is processed
+    const int nch = (p.T + CS - 1) / CS;
+    Raw<D> w;
+    fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, (nch - 1) * CS, half, false);
     __syncthreads();
     for (int i = nint - 1; i >= 0; --i) {
         const int nsub = (min(CK, p.T - i * CK) + CS - 1) / CS;
         for (int s = nsub - 1; s >= 0; --s) {
-            load_chunk<D, IN_BF16, DO_BF16>(c, p, b, h, i * CK + s * CS, half, false);
+            const int cj = (i * CK + s * CS) / CS;  // chunk index
+            build_chunk<D>(c, w, p.scale, false);
             __syncthreads();
+            if (cj > 0) fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, (cj - 1) * CS, half, false);
             chunk_triangles<D>(c);
             // dU = Kb dS + A^T dO
-            gemm<CS, DH, D, 2, 4>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dS[k][n]; },
+            gemm<CS, DH, D, 1, 2>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dS[k][n]; },
                                   [&](int m, int n, float v) { c.dU[m][n] = v; });
-            gemm<CS, DH, CS, 2, 4>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+            gemm<CS, DH, CS, 1, 2>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
                                    [&](int m, int n, float v) { c.dU[m][n] += v; });
             __syncthreads();
             // dX = Tm^T dU
-            gemm<CS, DH, CS, 2, 4>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
+            gemm<CS, DH, CS, 1, 2>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
                                    [&](int m, int n, float v) { c.dX[m][n] = v; });
             __syncthreads();
             // dS <- Diag(gam) dS + Qg^T dO - Kg^T dX   (each entry read and written by its own thread)
@@ -234,18 +276,28 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
 template <int D>
 struct alignas(16) Grad {
     static constexpr int DH = D / 2;
-    float G[CS][D + 1];       // one key-side gradient at a time (dKb, dQg, dKg, dKh)
-    float dK[CS][D + 1];      // dk, accumulated
-    float db[CS][D + 1];      // gradient of the cumulative decay, accumulated
-    float SM[D][DH + 1];      // the state after the interval's first chunk, then its gradient
+    float G[CS][D + 1];       // one key-side gradient at a time (dKb, dQg, dKg, dKh), then db
+    float P[D][DH + 1];       // state / state-gradient tiles of the current chunk (this value half):
+    float Q[D][DH + 1];       // which is which depends on the chunk, see the kernel
     float dA[CS][CS + 1], dTm[CS][CS + 1], dN[CS][CS + 1], dM[CS][CS + 1], T1[CS][CS + 1];
     float dgam[D], dlast[D];
     float dbeta[CS];
 };
 
+// dst[r][j] = src[r][col0 + j] (a [D][D] float32 matrix in global memory, NULL = zeros)
+template <int D>
+__device__ __forceinline__ void load_state(float (*dst)[D / 2 + 1], const float* src, int col0) {
+    constexpr int DH = D / 2;
+    for (int e = threadIdx.x; e < D * DH; e += NT) {
+        const int r = e / DH, j = e % DH;
+        dst[r][j] = src ? src[(size_t)r * D + col0 + j] : 0.f;
+    }
+}
+
 template <int D, int CK, bool IN_BF16, bool DO_BF16>
 __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
     constexpr int DH = D / 2;
+    constexpr int PER = CS * D / NT;  // key-side tile entries per thread (e = tid + NT * k)
     __shared__ Chunk<D> c;
     __shared__ Grad<D> gr;
     const int tid = threadIdx.x;
@@ -253,64 +305,73 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
     const int wi = blockIdx.x >> 1;
     const int bh = wi / p.nint, i = wi - bh * p.nint;
     const int b = bh / p.H, h = bh - b * p.H;
-    // start state of the interval (global, full rows; this half's columns) and end gradient
+    // start state of the interval and the gradient of the state after it (global, full rows)
     const float* S0g = i == 0 ? (p.S0 ? p.S0 + (size_t)bh * D * D : nullptr) : p.Sck + ((size_t)bh * p.nck + i - 1) * D * D;
     const float* dSe = p.dSb + ((size_t)bh * p.nint + i) * D * D;
     const int col0 = half * DH;
     const int nsub = (min(CK, p.T - i * CK) + CS - 1) / CS;
-    auto Sg = [&](int r, int j) { return S0g ? S0g[(size_t)r * D + col0 + j] : 0.f; };
 
-    if (nsub == 2) {  // the state after the first chunk: SM = Diag(gam) S + Kb^T Tm (V - Kg S)
+    // Buffers: one chunk:  P = start state, Q = end gradient.
+    // Two chunks: P = start state -> Q = state after the first chunk; second chunk: S = Q, dS = P
+    // (the interval's end gradient); its start gradient goes to Q; first chunk: S = P (start state
+    // again), dS = Q.
+    load_state<D>(gr.P, S0g, col0);
+    __syncthreads();
+    if (nsub == 2) {  // Q = Diag(gam) S + Kb^T Tm (V - Kg S)
         load_chunk<D, IN_BF16, DO_BF16>(c, p, b, h, i * CK, half, true);
         __syncthreads();
         chunk_triangles<D>(c);
-        gemm<CS, DH, D, 2, 4>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return Sg(k, n); },
+        gemm<CS, DH, D, 1, 2>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return gr.P[k][n]; },
                               [&](int m, int n, float v) { c.X[m][n] -= v; });
         __syncthreads();
-        gemm<CS, DH, CS, 2, 4>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
+        gemm<CS, DH, CS, 1, 2>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
                                [&](int m, int n, float v) { c.U[m][n] = v; });
         __syncthreads();
         gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Kb[k][m]; }, [&](int k, int n) { return c.U[k][n]; },
-                              [&](int m, int n, float v) { gr.SM[m][n] = __builtin_fmaf(c.gam[m], Sg(m, n), v); });
+                              [&](int m, int n, float v) { gr.Q[m][n] = __builtin_fmaf(c.gam[m], gr.P[m][n], v); });
         __syncthreads();
+        load_state<D>(gr.P, dSe, col0);
+    } else {
+        load_state<D>(gr.Q, dSe, col0);
     }
+    __syncthreads();
     for (int s = nsub - 1; s >= 0; --s) {
         const int c0 = i * CK + s * CS;
-        const bool s_lds = s == 1;             // the chunk's start state is SM (else the interval's start state)
-        const bool ds_lds = s < nsub - 1;      // the chunk's end gradient is SM (else the interval's end gradient)
-        auto S = [&](int r, int j) { return s_lds ? gr.SM[r][j] : Sg(r, j); };
-        auto dS = [&](int r, int j) { return ds_lds ? gr.SM[r][j] : dSe[(size_t)r * D + col0 + j]; };
+        float (*Sb)[DH + 1] = (nsub == 2 && s == 1) ? gr.Q : gr.P;
+        float (*dSb)[DH + 1] = (nsub == 2 && s == 1) ? gr.P : gr.Q;
         load_chunk<D, IN_BF16, DO_BF16>(c, p, b, h, c0, half, true);
         __syncthreads();
         chunk_triangles<D>(c);
         // X = V - Kg S;  U = Tm X
-        gemm<CS, DH, D, 2, 4>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return S(k, n); },
+        gemm<CS, DH, D, 1, 2>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return Sb[k][n]; },
                               [&](int m, int n, float v) { c.X[m][n] -= v; });
         __syncthreads();
-        gemm<CS, DH, CS, 2, 4>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
+        gemm<CS, DH, CS, 1, 2>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
                                [&](int m, int n, float v) { c.U[m][n] = v; });
         __syncthreads();
         // dU = Kb dS + A^T dO;  dKb = U dS^T;  dgam = rowsum(dS * S);  dA = tril(dO U^T)
-        gemm<CS, DH, D, 2, 4>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dS(k, n); },
+        gemm<CS, DH, D, 1, 2>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dSb[k][n]; },
                               [&](int m, int n, float v) { c.dU[m][n] = v; });
-        gemm<CS, DH, CS, 2, 4>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+        gemm<CS, DH, CS, 1, 2>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
                                [&](int m, int n, float v) { c.dU[m][n] += v; });
-        gemm<CS, D, DH, 2, 4>([&](int m, int k) { return c.U[m][k]; }, [&](int k, int n) { return dS(n, k); },
+        gemm<CS, D, DH, 1, 4>([&](int m, int k) { return c.U[m][k]; }, [&](int k, int n) { return dSb[n][k]; },
                               [&](int m, int n, float v) { gr.G[m][n] = v; });
         if (tid < D) {
             float a = 0.f;
-            for (int j = 0; j < DH; ++j) a = __builtin_fmaf(dS(tid, j), S(tid, j), a);
+            for (int j = 0; j < DH; ++j) a = __builtin_fmaf(dSb[tid][j], Sb[tid][j], a);
             gr.dgam[tid] = a;
         }
         gemm<CS, CS, DH, 1, 1>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return c.U[n][k]; },
                                [&](int m, int n, float v) { gr.dA[m][n] = n <= m ? v : 0.f; });
         __syncthreads();
         // fold dKb: dk = dKb exp(b_last - b);  db = -dKb Kb;  last row: sum_t dKb Kb + dgam gam
-        for (int e = tid; e < CS * D; e += NT) {
-            const int r = e / D, ch = e % D;
+        float dKr[PER], dbr[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int e = tid + NT * k, r = e / D, ch = e % D;
             const float gk = gr.G[r][ch];
-            gr.dK[r][ch] = gk * (c.gam[ch] / c.Gam[r][ch]);
-            gr.db[r][ch] = -gk * c.Kb[r][ch];
+            dKr[k] = gk * (c.gam[ch] / c.Gam[r][ch]);
+            dbr[k] = -gk * c.Kb[r][ch];
         }
         if (tid < D) {
             float a = gr.dgam[tid] * c.gam[tid];
@@ -320,12 +381,12 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         // dTm = dU X^T;  dX = Tm^T dU  (dv)
         gemm<CS, CS, DH, 1, 1>([&](int m, int k) { return c.dU[m][k]; }, [&](int k, int n) { return c.X[n][k]; },
                                [&](int m, int n, float v) { gr.dTm[m][n] = v; });
-        gemm<CS, DH, CS, 2, 4>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
+        gemm<CS, DH, CS, 1, 2>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
                                [&](int m, int n, float v) { c.dX[m][n] = v; });
         __syncthreads();
         // dN = dTm Diag(beta);  dbeta = colsum(N * dTm);  dM = -N^T dN N^T;  dbeta += rowsum(dM * L);
         // dL = tril(Diag(beta) dM, -1) (kept in dM)
-        {
+        if (tid < CS * CS) {
             const int r = tid / CS, q = tid % CS;
             gr.dN[r][q] = gr.dTm[r][q] * c.beta[q];
         }
@@ -347,76 +408,85 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             gr.dbeta[tid] += a;
         }
         __syncthreads();
-        {
+        if (tid < CS * CS) {
             const int r = tid / CS, q = tid % CS;
             gr.dM[r][q] = q < r ? c.beta[r] * gr.dM[r][q] : 0.f;  // now dL
         }
         __syncthreads();
         // dQg = dO S^T + dA Kh  -> dq = dQg scale Gamma (Qg holds the scale), db += dQg Qg
-        gemm<CS, D, DH, 2, 4>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return S(n, k); },
+        gemm<CS, D, DH, 1, 4>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return Sb[n][k]; },
                               [&](int m, int n, float v) { gr.G[m][n] = v; });
-        gemm<CS, D, CS, 2, 4>([&](int m, int k) { return gr.dA[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
+        gemm<CS, D, CS, 1, 4>([&](int m, int k) { return gr.dA[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
                               [&](int m, int n, float v) { gr.G[m][n] += v; });
         __syncthreads();
         const int n_ok = min(CS, p.T - c0);
-        for (int e = tid; e < CS * D; e += NT) {
-            const int r = e / D, ch = e % D;
+        auto grow = [&](int r) { return ((size_t)b * p.T + c0 + r) * p.H + h; };
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int e = tid + NT * k, r = e / D, ch = e % D;
             const float gq = gr.G[r][ch];
-            gr.db[r][ch] = __builtin_fmaf(gq, c.Qg[r][ch], gr.db[r][ch]);
-            if (r < n_ok && p.dq) atomicAdd(&p.dq[(((size_t)b * p.T + c0 + r) * p.H + h) * D + ch], gq * p.scale * c.Gam[r][ch]);
+            dbr[k] = __builtin_fmaf(gq, c.Qg[r][ch], dbr[k]);
+            if (r < n_ok && p.dq) atomicAdd(&p.dq[grow(r) * D + ch], gq * p.scale * c.Gam[r][ch]);
         }
         __syncthreads();
         // dKg = -dX S^T + dL Kh -> dk += dKg Gamma, db += dKg Kg
-        gemm<CS, D, DH, 2, 4>([&](int m, int k) { return c.dX[m][k]; }, [&](int k, int n) { return S(n, k); },
+        gemm<CS, D, DH, 1, 4>([&](int m, int k) { return c.dX[m][k]; }, [&](int k, int n) { return Sb[n][k]; },
                               [&](int m, int n, float v) { gr.G[m][n] = -v; });
-        gemm<CS, D, CS, 2, 4>([&](int m, int k) { return gr.dM[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
+        gemm<CS, D, CS, 1, 4>([&](int m, int k) { return gr.dM[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
                               [&](int m, int n, float v) { gr.G[m][n] += v; });
         __syncthreads();
-        for (int e = tid; e < CS * D; e += NT) {
-            const int r = e / D, ch = e % D;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int e = tid + NT * k, r = e / D, ch = e % D;
             const float gk = gr.G[r][ch];
-            gr.dK[r][ch] = __builtin_fmaf(gk, c.Gam[r][ch], gr.dK[r][ch]);
-            gr.db[r][ch] = __builtin_fmaf(gk, c.Kg[r][ch], gr.db[r][ch]);
+            dKr[k] = __builtin_fmaf(gk, c.Gam[r][ch], dKr[k]);
+            dbr[k] = __builtin_fmaf(gk, c.Kg[r][ch], dbr[k]);
         }
         __syncthreads();
         // dKh = dL^T Kg + dA^T Qg -> dk += dKh / Gamma, db -= dKh Kh
-        gemm<CS, D, CS, 2, 4>([&](int m, int k) { return gr.dM[k][m]; }, [&](int k, int n) { return c.Kg[k][n]; },
+        gemm<CS, D, CS, 1, 4>([&](int m, int k) { return gr.dM[k][m]; }, [&](int k, int n) { return c.Kg[k][n]; },
                               [&](int m, int n, float v) { gr.G[m][n] = v; });
-        gemm<CS, D, CS, 2, 4>([&](int m, int k) { return gr.dA[k][m]; }, [&](int k, int n) { return c.Qg[k][n]; },
+        gemm<CS, D, CS, 1, 4>([&](int m, int k) { return gr.dA[k][m]; }, [&](int k, int n) { return c.Qg[k][n]; },
                               [&](int m, int n, float v) { gr.G[m][n] += v; });
         __syncthreads();
-        for (int e = tid; e < CS * D; e += NT) {
-            const int r = e / D, ch = e % D;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int e = tid + NT * k, r = e / D, ch = e % D;
             const float gh = gr.G[r][ch];
-            gr.dK[r][ch] += gh / c.Gam[r][ch];
-            gr.db[r][ch] = __builtin_fmaf(-gh, c.Kh[r][ch], gr.db[r][ch]);
+            dKr[k] += gh / c.Gam[r][ch];
+            dbr[k] = __builtin_fmaf(-gh, c.Kh[r][ch], dbr[k]);
+            if (r < n_ok && p.dk) atomicAdd(&p.dk[grow(r) * D + ch], dKr[k]);
         }
         __syncthreads();
-        // outputs of the chunk: dk, dv, dbeta, dg (reverse cumulative sum of db)
-        for (int e = tid; e < CS * D; e += NT) {
-            const int r = e / D, ch = e % D;
-            if (r < n_ok && p.dk) atomicAdd(&p.dk[(((size_t)b * p.T + c0 + r) * p.H + h) * D + ch], gr.dK[r][ch]);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int e = tid + NT * k;
+            gr.G[e / D][e % D] = dbr[k];
         }
+        // outputs of the chunk: dv, dbeta, dg (reverse cumulative sum of db)
         for (int e = tid; e < CS * DH; e += NT) {
             const int r = e / DH, j = e % DH;
-            if (r < n_ok && p.dv) p.dv[(((size_t)b * p.T + c0 + r) * p.H + h) * D + col0 + j] = c.dX[r][j];
+            if (r < n_ok && p.dv) p.dv[grow(r) * D + col0 + j] = c.dX[r][j];
         }
-        if (tid < CS && tid < n_ok && p.dbeta) atomicAdd(&p.dbeta[((size_t)b * p.T + c0 + tid) * p.H + h], gr.dbeta[tid]);
+        if (tid < CS && tid < n_ok && p.dbeta) atomicAdd(&p.dbeta[grow(tid)], gr.dbeta[tid]);
+        __syncthreads();
         if (tid < D && p.dg) {
             float a = gr.dlast[tid];
             for (int r = CS - 1; r >= 0; --r) {
-                a += gr.db[r][tid];
-                if (r < n_ok) atomicAdd(&p.dg[(((size_t)b * p.T + c0 + r) * p.H + h) * D + tid], a);
+                a += gr.G[r][tid];
+                if (r < n_ok) atomicAdd(&p.dg[grow(r) * D + tid], a);
             }
         }
-        if (s == 1) {
-            // the gradient of the state between the interval's two chunks:
-            // Diag(gam) dS + Qg^T dO - Kg^T dX, into SM once every read of SM (as S) is done
+        if (nsub == 2 && s == 1) {
+            // the gradient of the state between the two chunks, Diag(gam) dS + Qg^T dO - Kg^T dX,
+            // into Q (the state S of this chunk, no longer read); then P gets the start state back
             __syncthreads();
             gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Qg[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
-                                  [&](int m, int n, float v) { gr.SM[m][n] = __builtin_fmaf(c.gam[m], dSe[(size_t)m * D + col0 + n], v); });
+                                  [&](int m, int n, float v) { gr.Q[m][n] = __builtin_fmaf(c.gam[m], gr.P[m][n], v); });
             gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Kg[k][m]; }, [&](int k, int n) { return c.dX[k][n]; },
-                                  [&](int m, int n, float v) { gr.SM[m][n] -= v; });
+                                  [&](int m, int n, float v) { gr.Q[m][n] -= v; });
+            __syncthreads();
+            load_state<D>(gr.P, S0g, col0);
         }
         __syncthreads();
     }
