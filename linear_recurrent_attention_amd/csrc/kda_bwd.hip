@@ -46,35 +46,25 @@ __device__ __forceinline__ float ldx(const void* p, size_t i) {
         return reinterpret_cast<const float*>(p)[i];
 }
 
-// out(m, n) = sum_k a(m, k) b(k, n) for m < M, n < N, each thread taking RM x RN blocks; f(m, n, v)
-// receives the result.  a and b are accessors (LDS or global).
-template <int M, int N, int K, int RM, int RN, typename FA, typename FB, typename F>
-__device__ __forceinline__ void gemm(FA a, FB b, F f) {
-    static_assert(M % RM == 0 && N % RN == 0, "block shape");
-    constexpr int NBN = N / RN;
-    for (int blk = threadIdx.x; blk < (M / RM) * NBN; blk += NT) {
-        const int m0 = (blk / NBN) * RM, n0 = (blk % NBN) * RN;
-        float acc[RM][RN];
+// out(m, n) = sum_k a(m, k) b(k, n) for m < M, n < N on the matrix cores: float32
+// v_mfma_f32_16x16x4_f32 (exact float32 products, float32 accumulation), one 16 x 16 output tile per
+// wave at a time; a and b are accessors (LDS), f(m, n, v) receives the result.  Operand layout of that
+// instruction: A(m, k) in lane m + 16 k, B(k, n) in lane n + 16 k, result (4 g + r, n) in lane
+// n + 16 g, register r.
+template <int M, int N, int K, typename FA, typename FB, typename F>
+__device__ __forceinline__ void mgemm(FA a, FB b, F f) {
+    static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "tile shape");
+    constexpr int TN = N / 16;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l16 = lane & 15, g = lane >> 4;
+    for (int tile = wave; tile < (M / 16) * TN; tile += NT / 64) {
+        const int m0 = (tile / TN) * 16, n0 = (tile % TN) * 16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int k = 0; k < K; k += 4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(m0 + l16, k + g), b(k + g, n0 + l16), acc, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < RM; ++i)
-#pragma unroll
-            for (int j = 0; j < RN; ++j) acc[i][j] = 0.f;
-#pragma unroll 4
-        for (int k = 0; k < K; ++k) {
-            float av[RM], bv[RN];
-#pragma unroll
-            for (int i = 0; i < RM; ++i) av[i] = a(m0 + i, k);
-#pragma unroll
-            for (int j = 0; j < RN; ++j) bv[j] = b(k, n0 + j);
-#pragma unroll
-            for (int i = 0; i < RM; ++i)
-#pragma unroll
-                for (int j = 0; j < RN; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
-        }
-#pragma unroll
-        for (int i = 0; i < RM; ++i)
-#pragma unroll
-            for (int j = 0; j < RN; ++j) f(m0 + i, n0 + j, acc[i][j]);
+        for (int r = 0; r < 4; ++r) f(m0 + 4 * g + r, n0 + l16, acc[r]);
     }
 }
 
@@ -171,21 +161,15 @@ __device__ __forceinline__ void load_chunk(Chunk<D>& c, const BwdParams& p, int 
     build_chunk<D>(c, w, p.scale, want_v);
 }
 
-// L, A (one entry per thread), then N = (I + Diag(beta) L)^{-1} and Tm = N Diag(beta) by forward
+// L, A on the matrix cores, then N = (I + Diag(beta) L)^{-1} and Tm = N Diag(beta) by forward
 // substitution, one column per thread.
 template <int D>
 __device__ __forceinline__ void chunk_triangles(Chunk<D>& c) {
     const int tid = threadIdx.x;
-    if (tid < CS * CS) {
-        const int t = tid / CS, s = tid % CS;
-        float l = 0.f, a = 0.f;
-        for (int ch = 0; ch < D; ++ch) {
-            l = __builtin_fmaf(c.Kg[t][ch], c.Kh[s][ch], l);
-            a = __builtin_fmaf(c.Qg[t][ch], c.Kh[s][ch], a);
-        }
-        c.L[t][s] = s < t ? l : 0.f;
-        c.A[t][s] = s <= t ? a : 0.f;
-    }
+    mgemm<CS, CS, D>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
+                     [&](int m, int n, float v) { c.L[m][n] = n < m ? v : 0.f; });
+    mgemm<CS, CS, D>([&](int m, int k) { return c.Qg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
+                     [&](int m, int n, float v) { c.A[m][n] = n <= m ? v : 0.f; });
     __syncthreads();
     if (tid < CS) {
         const int j = tid;
@@ -239,19 +223,19 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
             if (cj > 0) fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, (cj - 1) * CS, half, false);
             chunk_triangles<D>(c);
             // dU = Kb dS + A^T dO
-            gemm<CS, DH, D, 1, 2>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dS[k][n]; },
+            mgemm<CS, DH, D>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dS[k][n]; },
                                   [&](int m, int n, float v) { c.dU[m][n] = v; });
-            gemm<CS, DH, CS, 1, 2>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+            mgemm<CS, DH, CS>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
                                    [&](int m, int n, float v) { c.dU[m][n] += v; });
             __syncthreads();
             // dX = Tm^T dU
-            gemm<CS, DH, CS, 1, 2>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
+            mgemm<CS, DH, CS>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
                                    [&](int m, int n, float v) { c.dX[m][n] = v; });
             __syncthreads();
             // dS <- Diag(gam) dS + Qg^T dO - Kg^T dX   (each entry read and written by its own thread)
-            gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Qg[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+            mgemm<D, DH, CS>([&](int m, int k) { return c.Qg[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
                                   [&](int m, int n, float v) { dS[m][n] = __builtin_fmaf(c.gam[m], dS[m][n], v); });
-            gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Kg[k][m]; }, [&](int k, int n) { return c.dX[k][n]; },
+            mgemm<D, DH, CS>([&](int m, int k) { return c.Kg[k][m]; }, [&](int k, int n) { return c.dX[k][n]; },
                                   [&](int m, int n, float v) { dS[m][n] -= v; });
             __syncthreads();
         }
@@ -321,13 +305,13 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         load_chunk<D, IN_BF16, DO_BF16>(c, p, b, h, i * CK, half, true);
         __syncthreads();
         chunk_triangles<D>(c);
-        gemm<CS, DH, D, 1, 2>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return gr.P[k][n]; },
+        mgemm<CS, DH, D>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return gr.P[k][n]; },
                               [&](int m, int n, float v) { c.X[m][n] -= v; });
         __syncthreads();
-        gemm<CS, DH, CS, 1, 2>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
+        mgemm<CS, DH, CS>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
                                [&](int m, int n, float v) { c.U[m][n] = v; });
         __syncthreads();
-        gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Kb[k][m]; }, [&](int k, int n) { return c.U[k][n]; },
+        mgemm<D, DH, CS>([&](int m, int k) { return c.Kb[k][m]; }, [&](int k, int n) { return c.U[k][n]; },
                               [&](int m, int n, float v) { gr.Q[m][n] = __builtin_fmaf(c.gam[m], gr.P[m][n], v); });
         __syncthreads();
         load_state<D>(gr.P, dSe, col0);
@@ -343,25 +327,25 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         __syncthreads();
         chunk_triangles<D>(c);
         // X = V - Kg S;  U = Tm X
-        gemm<CS, DH, D, 1, 2>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return Sb[k][n]; },
+        mgemm<CS, DH, D>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return Sb[k][n]; },
                               [&](int m, int n, float v) { c.X[m][n] -= v; });
         __syncthreads();
-        gemm<CS, DH, CS, 1, 2>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
+        mgemm<CS, DH, CS>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
                                [&](int m, int n, float v) { c.U[m][n] = v; });
         __syncthreads();
         // dU = Kb dS + A^T dO;  dKb = U dS^T;  dgam = rowsum(dS * S);  dA = tril(dO U^T)
-        gemm<CS, DH, D, 1, 2>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dSb[k][n]; },
+        mgemm<CS, DH, D>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dSb[k][n]; },
                               [&](int m, int n, float v) { c.dU[m][n] = v; });
-        gemm<CS, DH, CS, 1, 2>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+        mgemm<CS, DH, CS>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
                                [&](int m, int n, float v) { c.dU[m][n] += v; });
-        gemm<CS, D, DH, 1, 4>([&](int m, int k) { return c.U[m][k]; }, [&](int k, int n) { return dSb[n][k]; },
+        mgemm<CS, D, DH>([&](int m, int k) { return c.U[m][k]; }, [&](int k, int n) { return dSb[n][k]; },
                               [&](int m, int n, float v) { gr.G[m][n] = v; });
         if (tid < D) {
             float a = 0.f;
             for (int j = 0; j < DH; ++j) a = __builtin_fmaf(dSb[tid][j], Sb[tid][j], a);
             gr.dgam[tid] = a;
         }
-        gemm<CS, CS, DH, 1, 1>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return c.U[n][k]; },
+        mgemm<CS, CS, DH>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return c.U[n][k]; },
                                [&](int m, int n, float v) { gr.dA[m][n] = n <= m ? v : 0.f; });
         __syncthreads();
         // fold dKb: dk = dKb exp(b_last - b);  db = -dKb Kb;  last row: sum_t dKb Kb + dgam gam
@@ -379,9 +363,9 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             gr.dlast[tid] = a;
         }
         // dTm = dU X^T;  dX = Tm^T dU  (dv)
-        gemm<CS, CS, DH, 1, 1>([&](int m, int k) { return c.dU[m][k]; }, [&](int k, int n) { return c.X[n][k]; },
+        mgemm<CS, CS, DH>([&](int m, int k) { return c.dU[m][k]; }, [&](int k, int n) { return c.X[n][k]; },
                                [&](int m, int n, float v) { gr.dTm[m][n] = v; });
-        gemm<CS, DH, CS, 1, 2>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
+        mgemm<CS, DH, CS>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
                                [&](int m, int n, float v) { c.dX[m][n] = v; });
         __syncthreads();
         // dN = dTm Diag(beta);  dbeta = colsum(N * dTm);  dM = -N^T dN N^T;  dbeta += rowsum(dM * L);
@@ -396,10 +380,10 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             gr.dbeta[tid] = a;
         }
         __syncthreads();
-        gemm<CS, CS, CS, 1, 1>([&](int m, int k) { return c.N[k][m]; }, [&](int k, int n) { return gr.dN[k][n]; },
+        mgemm<CS, CS, CS>([&](int m, int k) { return c.N[k][m]; }, [&](int k, int n) { return gr.dN[k][n]; },
                                [&](int m, int n, float v) { gr.T1[m][n] = v; });
         __syncthreads();
-        gemm<CS, CS, CS, 1, 1>([&](int m, int k) { return gr.T1[m][k]; }, [&](int k, int n) { return c.N[n][k]; },
+        mgemm<CS, CS, CS>([&](int m, int k) { return gr.T1[m][k]; }, [&](int k, int n) { return c.N[n][k]; },
                                [&](int m, int n, float v) { gr.dM[m][n] = -v; });
         __syncthreads();
         if (tid < CS) {
@@ -414,9 +398,9 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         }
         __syncthreads();
         // dQg = dO S^T + dA Kh  -> dq = dQg scale Gamma (Qg holds the scale), db += dQg Qg
-        gemm<CS, D, DH, 1, 4>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return Sb[n][k]; },
+        mgemm<CS, D, DH>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return Sb[n][k]; },
                               [&](int m, int n, float v) { gr.G[m][n] = v; });
-        gemm<CS, D, CS, 1, 4>([&](int m, int k) { return gr.dA[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
+        mgemm<CS, D, CS>([&](int m, int k) { return gr.dA[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
                               [&](int m, int n, float v) { gr.G[m][n] += v; });
         __syncthreads();
         const int n_ok = min(CS, p.T - c0);
@@ -430,9 +414,9 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         }
         __syncthreads();
         // dKg = -dX S^T + dL Kh -> dk += dKg Gamma, db += dKg Kg
-        gemm<CS, D, DH, 1, 4>([&](int m, int k) { return c.dX[m][k]; }, [&](int k, int n) { return Sb[n][k]; },
+        mgemm<CS, D, DH>([&](int m, int k) { return c.dX[m][k]; }, [&](int k, int n) { return Sb[n][k]; },
                               [&](int m, int n, float v) { gr.G[m][n] = -v; });
-        gemm<CS, D, CS, 1, 4>([&](int m, int k) { return gr.dM[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
+        mgemm<CS, D, CS>([&](int m, int k) { return gr.dM[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
                               [&](int m, int n, float v) { gr.G[m][n] += v; });
         __syncthreads();
 #pragma unroll
@@ -444,9 +428,9 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         }
         __syncthreads();
         // dKh = dL^T Kg + dA^T Qg -> dk += dKh / Gamma, db -= dKh Kh
-        gemm<CS, D, CS, 1, 4>([&](int m, int k) { return gr.dM[k][m]; }, [&](int k, int n) { return c.Kg[k][n]; },
+        mgemm<CS, D, CS>([&](int m, int k) { return gr.dM[k][m]; }, [&](int k, int n) { return c.Kg[k][n]; },
                               [&](int m, int n, float v) { gr.G[m][n] = v; });
-        gemm<CS, D, CS, 1, 4>([&](int m, int k) { return gr.dA[k][m]; }, [&](int k, int n) { return c.Qg[k][n]; },
+        mgemm<CS, D, CS>([&](int m, int k) { return gr.dA[k][m]; }, [&](int k, int n) { return c.Qg[k][n]; },
                               [&](int m, int n, float v) { gr.G[m][n] += v; });
         __syncthreads();
 #pragma unroll
@@ -481,9 +465,9 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             // the gradient of the state between the two chunks, Diag(gam) dS + Qg^T dO - Kg^T dX,
             // into Q (the state S of this chunk, no longer read); then P gets the start state back
             __syncthreads();
-            gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Qg[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+            mgemm<D, DH, CS>([&](int m, int k) { return c.Qg[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
                                   [&](int m, int n, float v) { gr.Q[m][n] = __builtin_fmaf(c.gam[m], gr.P[m][n], v); });
-            gemm<D, DH, CS, 4, 4>([&](int m, int k) { return c.Kg[k][m]; }, [&](int k, int n) { return c.dX[k][n]; },
+            mgemm<D, DH, CS>([&](int m, int k) { return c.Kg[k][m]; }, [&](int k, int n) { return c.dX[k][n]; },
                                   [&](int m, int n, float v) { gr.Q[m][n] -= v; });
             __syncthreads();
             load_state<D>(gr.P, S0g, col0);
