@@ -222,6 +222,18 @@ def bwd_bytes(B, T, H, D, io_bytes=2):
     return B * T * H * per_token_head + B * H * D * D * 4
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense float32 matrix
+
+
+def bwd_flops(B, T, H, D, C=16):
+    """Matrix-product flops of the chunkwise backward, per launch: per token and head, the products
+    with the state, X = V - Kg S, dU = Kb dS, dKb = U dS^T, dQg = dO S^T, dKg = -dX S^T, and the state
+    gradient's Qg^T dO and Kg^T dX (7 products of 2 D^2 flops), plus the chunk-sized ones (L, A, U,
+    A^T dO, dA, dTm, dX, dM, dL Kh, dA Kh, dL^T Kg, dA^T Qg: 15 of 2 C D flops); the state recompute
+    of the forward and the re-stepping inside 32-token intervals are not counted."""
+    return B * T * H * (7 * 2 * D * D + 15 * 2 * C * D)
+
+
 def bench_bwd(args, torch, synth, kda):
     """kda_bwd on the prefill workload B=4, H=32, T=16384, D=128 (bf16 q/k/v/dO, float32 gradients):
     one step = the whole backward (state recompute, reverse state-gradient pass, input gradients)."""
@@ -246,6 +258,8 @@ def bench_bwd(args, torch, synth, kda):
     avg_s = float(np.mean(launch_ms)) / 1e3
     abytes = bwd_bytes(B, T, H, D)
     gbs = abytes / avg_s / 1e9
+    aflops = bwd_flops(B, T, H, D)
+    tflops = aflops / avg_s / 1e12
     out = {
         "metric": "KDA backward tokens/s at H=32,d=128,T=16K (1 GPU)", "value": B * T / (wall / args.steps),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -253,9 +267,11 @@ def bench_bwd(args, torch, synth, kda):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "kda_bwd_bf16_B4_H32_T16384_D128", "B": B, "H": H, "T": T, "D": D,
                    "io": "bf16 q/k/v/dO, float32 g/beta and gradients"},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "kda_bwd (all kernels)",
-                     "avg_call_ms": avg_s * 1e3, "algorithmic_bytes": abytes},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / FP32_MFMA_PEAK_TFLOPS, "traffic": None, "kernel": "kda_bwd (all kernels)",
+                     "avg_call_ms": avg_s * 1e3, "algorithmic_flops": aflops},
+        "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                "algorithmic_bytes": abytes},
     }
     print(json.dumps(out), flush=True)
 
