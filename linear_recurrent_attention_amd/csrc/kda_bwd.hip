@@ -51,13 +51,15 @@ __device__ __forceinline__ float ldx(const void* p, size_t i) {
 // wave at a time; a and b are accessors (LDS), f(m, n, v) receives the result.  Operand layout of that
 // instruction: A(m, k) in lane m + 16 k, B(k, n) in lane n + 16 k, result (4 g + r, n) in lane
 // n + 16 g, register r.
+// Tile t goes to wave (first_wave + t) mod 8, so that small products issued back to back without a
+// barrier between them can run on different waves.
 template <int M, int N, int K, typename FA, typename FB, typename F>
-__device__ __forceinline__ void mgemm(FA a, FB b, F f) {
+__device__ __forceinline__ void mgemm(FA a, FB b, F f, int first_wave = 0) {
     static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "tile shape");
-    constexpr int TN = N / 16;
+    constexpr int TN = N / 16, NW = NT / 64;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, g = lane >> 4;
-    for (int tile = wave; tile < (M / 16) * TN; tile += NT / 64) {
+    for (int tile = (wave + NW - first_wave) % NW; tile < (M / 16) * TN; tile += NW) {
         const int m0 = (tile / TN) * 16, n0 = (tile % TN) * 16;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
@@ -69,10 +71,15 @@ __device__ __forceinline__ void mgemm(FA a, FB b, F f) {
 }
 
 // Factors of one chunk, its beta, and the value-half columns of dO (and V in X when wanted).
+// Row pitch of the [CS][D] key-side tiles: D + 20 floats (20 mod 64 banks), so that the matrix-core
+// operand reads hit distinct banks when a lane group walks rows (l16) and at most two lanes share a
+// bank when it walks columns.
+constexpr int KP = 20;
+
 template <int D>
 struct alignas(16) Chunk {
     static constexpr int DH = D / 2;
-    float Qg[CS][D + 1], Kg[CS][D + 1], Kh[CS][D + 1], Kb[CS][D + 1], Gam[CS][D + 1];
+    float Qg[CS][D + KP], Kg[CS][D + KP], Kh[CS][D + KP], Kb[CS][D + KP], Gam[CS][D + KP];
     float gam[D];
     float X[CS][DH + 1], U[CS][DH + 1], dO[CS][DH + 1], dU[CS][DH + 1], dX[CS][DH + 1];
     float L[CS][CS + 1], A[CS][CS + 1], N[CS][CS + 1], Tm[CS][CS + 1];
@@ -161,30 +168,49 @@ __device__ __forceinline__ void load_chunk(Chunk<D>& c, const BwdParams& p, int 
     build_chunk<D>(c, w, p.scale, want_v);
 }
 
+// Lane m of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int M>
+__device__ __forceinline__ float row_bcast_c(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + M, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_bcast(float x, int m) {
+    switch (m) {
+        case 0: return row_bcast_c<0>(x);   case 1: return row_bcast_c<1>(x);   case 2: return row_bcast_c<2>(x);
+        case 3: return row_bcast_c<3>(x);   case 4: return row_bcast_c<4>(x);   case 5: return row_bcast_c<5>(x);
+        case 6: return row_bcast_c<6>(x);   case 7: return row_bcast_c<7>(x);   case 8: return row_bcast_c<8>(x);
+        case 9: return row_bcast_c<9>(x);   case 10: return row_bcast_c<10>(x); case 11: return row_bcast_c<11>(x);
+        case 12: return row_bcast_c<12>(x); case 13: return row_bcast_c<13>(x); case 14: return row_bcast_c<14>(x);
+        default: return row_bcast_c<15>(x);
+    }
+}
+
 // L, A on the matrix cores, then N = (I + Diag(beta) L)^{-1} and Tm = N Diag(beta) by forward
-// substitution, one column per thread.
+// substitution, one matrix entry per lane.
 template <int D>
 __device__ __forceinline__ void chunk_triangles(Chunk<D>& c) {
     const int tid = threadIdx.x;
+    // on waves 4-7: waves 0-1 may still be issuing the next chunk's loads (state pass)
     mgemm<CS, CS, D>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
-                     [&](int m, int n, float v) { c.L[m][n] = n < m ? v : 0.f; });
+                     [&](int m, int n, float v) { c.L[m][n] = n < m ? v : 0.f; }, 4);
     mgemm<CS, CS, D>([&](int m, int k) { return c.Qg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
-                     [&](int m, int n, float v) { c.A[m][n] = n <= m ? v : 0.f; });
+                     [&](int m, int n, float v) { c.A[m][n] = n <= m ? v : 0.f; }, 5);
     __syncthreads();
-    if (tid < CS) {
-        const int j = tid;
-        float x[CS];
+    // column j of N per 16-lane row of lanes, lane i holding row i of -Diag(beta) L: with
+    // x_i = [i == j] + y_i the substitution is y = (-Diag(beta) L)(e_j + y), and at step m row m's
+    // final y_m is broadcast along the 16 lanes (DPP row_newbcast) for the rows below to take up
+    const int te = tid - (NT - CS * CS);  // the last CS*CS threads
+    if (te >= 0) {
+        const int j = te / CS, i = te % CS;
+        const float nb = -c.beta[i];
+        float nr[CS];
 #pragma unroll
-        for (int i = 0; i < CS; ++i) {
-            float acc = (i == j) ? 1.f : 0.f;
-            for (int m = 0; m < i; ++m) acc -= c.beta[i] * c.L[i][m] * x[m];
-            x[i] = acc;
-        }
+        for (int m = 0; m < CS; ++m) nr[m] = nb * c.L[i][m];
+        float y = nb * c.L[i][j];
 #pragma unroll
-        for (int i = 0; i < CS; ++i) {
-            c.N[i][j] = x[i];
-            c.Tm[i][j] = x[i] * c.beta[j];
-        }
+        for (int m = 0; m < CS - 1; ++m) y = __builtin_fmaf(nr[m], row_bcast(y, m), y);
+        const float x = (i == j ? 1.f : 0.f) + y;
+        c.N[i][j] = x;
+        c.Tm[i][j] = x * c.beta[j];
     }
     __syncthreads();
 }
@@ -260,7 +286,7 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
 template <int D>
 struct alignas(16) Grad {
     static constexpr int DH = D / 2;
-    float G[CS][D + 1];       // one key-side gradient at a time (dKb, dQg, dKg, dKh), then db
+    float G[CS][D + KP];      // one key-side gradient at a time (dKb, dQg, dKg, dKh), then db
     float P[D][DH + 1];       // state / state-gradient tiles of the current chunk (this value half):
     float Q[D][DH + 1];       // which is which depends on the chunk, see the kernel
     float dA[CS][CS + 1], dTm[CS][CS + 1], dN[CS][CS + 1], dM[CS][CS + 1], T1[CS][CS + 1];
@@ -346,7 +372,7 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             gr.dgam[tid] = a;
         }
         mgemm<CS, CS, DH>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return c.U[n][k]; },
-                               [&](int m, int n, float v) { gr.dA[m][n] = n <= m ? v : 0.f; });
+                               [&](int m, int n, float v) { gr.dA[m][n] = n <= m ? v : 0.f; }, 7);
         __syncthreads();
         // fold dKb: dk = dKb exp(b_last - b);  db = -dKb Kb;  last row: sum_t dKb Kb + dgam gam
         float dKr[PER], dbr[PER];
@@ -364,7 +390,7 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         }
         // dTm = dU X^T;  dX = Tm^T dU  (dv)
         mgemm<CS, CS, DH>([&](int m, int k) { return c.dU[m][k]; }, [&](int k, int n) { return c.X[n][k]; },
-                               [&](int m, int n, float v) { gr.dTm[m][n] = v; });
+                               [&](int m, int n, float v) { gr.dTm[m][n] = v; }, 4);
         mgemm<CS, DH, CS>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
                                [&](int m, int n, float v) { c.dX[m][n] = v; });
         __syncthreads();
