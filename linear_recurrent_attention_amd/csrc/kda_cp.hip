@@ -87,10 +87,10 @@ __global__ void kda_cp_identity_kernel(float* __restrict__ S, size_t n) {
 // Params of the chunkwise kernel over the nseg segments of Bg batches starting at batch b0: each
 // segment is a batch row of its own (row stride Ls tokens), which matches the [B, T, H, D] layout
 // when the group's sequences are exactly nseg * Ls tokens long, or when the group is one sequence.
-Params seg_params(const Params& u, int b0, int Bg, int nseg, int Ls, bool in_bf16) {
+Params seg_params(const Params& u, int b0, int Bg, int nseg, int Ls) {
     Params p = u;
     const size_t tok = (size_t)b0 * u.T * u.H;  // first row of batch b0
-    const size_t esz = in_bf16 ? 2 : 4;
+    const size_t esz = u.in_f32 ? 4 : 2;        // q, k, v element size
     p.q = (const char*)u.q + tok * D * esz;
     p.k = (const char*)u.k + tok * D * esz;
     p.v = (const char*)u.v + tok * D * esz;
@@ -138,7 +138,7 @@ hipError_t launch_fwd_cp(const Params& u, int nseg_req, float* ws, hipStream_t s
     hipError_t e = hipSuccess;
     for (int b0 = 0; b0 < u.B && e == hipSuccess; b0 += Bg) {
         // 1. local states and transitions of all segments
-        Params p = cp::seg_params(u, b0, Bg, nseg, Ls, true);
+        Params p = cp::seg_params(u, b0, Bg, nseg, Ls);
         p.S0 = nullptr; p.o = nullptr; p.S_T = Shat;
         if ((e = launch_fwd_bf16(p, stream)) != hipSuccess) break;
         const size_t nm = (size_t)Bg * nseg * u.H;  // identity initial states, in the buffer step 2 fills later
@@ -152,7 +152,7 @@ hipError_t launch_fwd_cp(const Params& u, int nseg_req, float* ws, hipStream_t s
                            stream, Shat, M, S0, Sst, nseg, u.H);
         if ((e = hipGetLastError()) != hipSuccess) break;
         // 3. outputs, and each segment's final state (into Shat, no longer needed)
-        p = cp::seg_params(u, b0, Bg, nseg, Ls, true);
+        p = cp::seg_params(u, b0, Bg, nseg, Ls);
         p.S0 = Sst; p.S_T = Shat;
         if ((e = launch_fwd_bf16(p, stream)) != hipSuccess) break;
         // the sequence's final state: the last segment's, or carried through the tail
@@ -164,9 +164,10 @@ hipError_t launch_fwd_cp(const Params& u, int nseg_req, float* ws, hipStream_t s
             t.S_ckpt = nullptr; t.ckpt_chunks = 1; t.n_ckpt = 0;
             if (Tm < u.T) {  // Bg == 1 here
                 const size_t tok = ((size_t)(b0 + b) * u.T + Tm) * u.H;
-                t.q = (const char*)u.q + tok * cp::D * 2;
-                t.k = (const char*)u.k + tok * cp::D * 2;
-                t.v = (const char*)u.v + tok * cp::D * 2;
+                const size_t esz = u.in_f32 ? 4 : 2;
+                t.q = (const char*)u.q + tok * cp::D * esz;
+                t.k = (const char*)u.k + tok * cp::D * esz;
+                t.v = (const char*)u.v + tok * cp::D * esz;
                 t.g = u.g + tok * cp::D;
                 t.beta = u.beta + tok;
                 t.o = (char*)u.o + tok * cp::D * (u.o_f32 ? 4 : 2);

@@ -488,14 +488,17 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
     // float32 inputs: this lane's V values (tokens 16R + 4*g4 + r of a chunk, column col), read one
     // step ahead; rows past T read the last valid row (their U rows come out zero: beta = 0 there)
     f32x4 vnext[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // (v == NULL stands for v = 0: the rows of g, which have v's float32 layout, are read and zeroed)
     auto load_v = [&](int tc0) {
-        const gchar* vb = uniform_gptr((const char*)p.v + ((row0 + (size_t)tc0 * p.H) * DV) * 4);
+        const size_t e0 = (row0 + (size_t)tc0 * p.H) * DV;
+        const gchar* vb = uniform_gptr(p.v ? (const void*)((const float*)p.v + e0) : (const void*)(p.g + e0));
         const int lim = p.T - 1 - tc0;
 #pragma unroll
         for (int R = 0; R < 2; ++R)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 vnext[R][r] = gload<float>(vb, ((uint32_t)min(SUB * R + 4 * g4 + r, lim) * (uint32_t)p.H * DV + col) * 4u);
+        if (!p.v) vnext[0] = vnext[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
     if constexpr (IN_F32)
         if (nchunk > 0) load_v(0);

@@ -198,7 +198,7 @@ rocblas_status gemm_rm(rocblas_handle hd, int M, int N, int K, const void* Am, r
 }
 
 struct Workspace {
-    float *pq, *pk, *pv, *pg, *pz, *pdown, *pbeta, *wup32, *g, *beta, *o, *q, *k;
+    float *pq, *pk, *pv, *pg, *pz, *pdown, *pbeta, *wup32, *g, *beta, *o, *q, *k, *cp;
     uint16_t* gated;
     size_t bytes;
 };
@@ -226,6 +226,7 @@ Workspace carve(const kda_layer_desc* d, char* base) {
     w.q = (float*)take(BT * HD * 4);
     w.k = (float*)take(BT * HD * 4);
     w.gated = (uint16_t*)take(BT * HD * 2);
+    w.cp = (float*)take(cp_workspace_bytes(d->B, d->T, d->H, 0));  // the core's context parallelism
     w.bytes = off;
     return w;
 }
@@ -312,7 +313,8 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
     p.B = d->B; p.T = d->T; p.tstride = d->T; p.H = d->H; p.Dk = D; p.Dv = D; p.scale = d->scale;
     p.o_f32 = 1; p.in_f32 = 1; p.precise = 1;
     p.S_ckpt = nullptr; p.ckpt_chunks = 1; p.n_ckpt = 0;
-    if (kda::launch_fwd_bf16(p, stream) != hipSuccess) return KDA_ERR_HIP;
+    // few heads (2*B*H workgroups well under the 256 CUs) run as segments side by side
+    if (kda::launch_fwd_cp(p, 0, W.cp, stream) != hipSuccess) return KDA_ERR_HIP;
 
     hipLaunchKernelGGL(epilogue_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, stream, M, d->H, HD, W.o, W.pg,
                        w->rms_w, W.gated);
