@@ -54,9 +54,14 @@ constexpr int DVH = 64;     // value columns per workgroup
 constexpr int NKW = 8;      // key waves, one 4-token quad of the chunk each
 constexpr int TPW = C / NKW; // tokens per key wave
 constexpr int NTHR = 64 * (NKW + 4);  // and 4 value waves, 16 value columns each
-constexpr int LDK = DK + 8; // padded row (16-bit elements) of token-major [C][DK] tiles
-constexpr int LDT = C + 8;  // padded row of channel-major [D][C] tiles
-constexpr int LDA = C + 8;  // [C][C] 16-bit tiles
+// LDS layouts.  A matrix-core operand read has lane (l16, g4) fetch 16 bytes from row r0 + l16 at
+// 16-byte column block b0 + g4.  Measured on gfx950, such reads run at the full 256 B/clock per CU
+// when token-major [C][DK] rows are padded to 288 bytes (272 or 320 bytes run ~1.8x slower), and
+// when 64-byte rows of the [rows][C] tiles store column block b at b ^ ((row >> 1) & 3) (unpadded
+// or 80-byte rows run ~1.8x slower).
+constexpr int LDK = DK + 16; // padded row (16-bit elements) of token-major [C][DK] tiles
+constexpr int LDT = C;       // row of the [rows][C] tiles (channel-major [D][C], and [C][C]), swizzled
+constexpr int LDA = C;
 constexpr int LDF = C + 4;  // [C][C] float tiles
 constexpr int LDQ = 2 * NKW + 4;  // padded row of the quad-sum table (16-byte reads hit distinct banks)
 
@@ -69,6 +74,8 @@ constexpr int LDQ = 2 * NKW + 4;  // padded row of the quad-sum table (16-byte r
 __device__ __forceinline__ constexpr int tperm(int j) { return ((j >> 2) & 3) * 8 + (j >> 4) * 4 + (j & 3); }
 // the same within each 32-channel block of a 128-channel row
 __device__ __forceinline__ constexpr int cperm(int c) { return (c & ~31) + tperm(c & 31); }
+// column position of element (row, col) of a [rows][C] tile: 16-byte blocks XOR-swizzled by row
+__device__ __forceinline__ constexpr int sw(int row, int col) { return col ^ (((row >> 1) & 3) << 3); }
 
 struct alignas(16) KeyTiles {                // written and read by the key waves within one step
     uint16_t qmh[C][LDK], qml[C][LDK];       // Q * exp(b - b_15)       split bf16
@@ -161,6 +168,9 @@ __device__ __forceinline__ void gstore(gchar* base, uint32_t off, Tv v) {
 // zeroes them when the chunk is consumed.  Nothing here uses the loaded values, so the loads stay
 // in flight until their first use in the next step.  Requires T >= 1 and t0 < T.
 // PART selects what is loaded: LOAD_ALL, LOAD_GVB (decays, values, beta) or LOAD_QK (queries, keys).
+// Every step issues the same loads whatever the chunk (past the last one, the last chunk is read
+// again and ignored): with no load under a condition the compiler can count the loads issued since
+// any register's own, and wait for exactly that one instead of for all of them.
 enum { LOAD_ALL = 3, LOAD_GVB = 1, LOAD_QK = 2 };
 template <int PART, bool IN_F32>
 __device__ __forceinline__ void load_chunk(Raw<IN_F32>& r, const Params& p, const KeyLoad& kl, size_t row0, int t0) {
@@ -172,7 +182,7 @@ __device__ __forceinline__ void load_chunk(Raw<IN_F32>& r, const Params& p, cons
     const gchar* gc = uniform_gptr(p.g + ce);
     // v == NULL stands for v = 0 (the transition-matrix run of the in-device context parallelism): the
     // value loads then read the chunk's g instead (a valid address at every value offset, g having
-    // twice v's row size) and the values are replaced by zeros
+    // twice v's row size) and the reader substitutes zeros
     const gchar* vc = uniform_gptr(p.v ? (const void*)((const uint16_t*)p.v + ce) : (const void*)(p.g + ce));
     const gchar* bc = uniform_gptr(p.beta + row0 + (size_t)t0 * p.H);
     using QT = typename std::conditional<IN_F32, f32x2, uint32_t>::type;
@@ -197,12 +207,6 @@ __device__ __forceinline__ void load_chunk(Raw<IN_F32>& r, const Params& p, cons
             if constexpr (LG && !IN_F32) r.v[i] = gload<uint32_t>(vc, ov);
         }
         if constexpr (LG) r.beta = gload<float>(bc, (uint32_t)min(TPW * kl.kw + (kl.lane % TPW), lim) * 4u * p.H);
-    }
-    if constexpr (LG && !IN_F32) {
-        if (!p.v) {  // v = 0 (what was read came from g, see above)
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) r.v[i] = 0u;
-        }
     }
 }
 
@@ -239,6 +243,7 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
     const int c0 = 2 * lane;   // key channels c0, c0 + 1
     const bool work = n < nchunk;
     const int t0 = n * C;
+    const int tn = min(t0 + C, (nchunk - 1) * C);  // the chunk prefetched this step (see load_chunk)
     Handoff2& H = sm.h2[n & 1];  // A of chunk n (part 3); its other tiles are written next step
 
     // ---------------- part 1: decay sums over the quad; prefetch of the next chunk; the previous
@@ -249,8 +254,8 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
 #pragma unroll
         for (int i = 0; i < TPW; ++i) { a0 += cur.g[i][0]; a1 += cur.g[i][1]; }
         *reinterpret_cast<float2*>(&sm.key.tot[lane][2 * kw]) = make_float2(a0, a1);
-        if (n + 1 < nchunk) load_chunk<LOAD_GVB>(nxt, p, kl, row0, t0 + C);  // part of the next chunk
     }
+    load_chunk<LOAD_GVB>(nxt, p, kl, row0, tn);  // part of the next chunk
     if (n >= 1) {
         Handoff2& Hp = sm.h2[(n - 1) & 1];
         const int pc0 = cperm(c0);  // c0 even: c0 + 1 follows it
@@ -273,8 +278,8 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         // four tokens are contiguous after tperm
         const int pt = tperm(tq);
         auto put_t = [&](uint16_t (*dst)[LDT], const uint32_t* w) {
-            *reinterpret_cast<u32x2*>(&dst[c0][pt]) = u32x2{perm_lo(w[0], w[1]), perm_lo(w[2], w[3])};
-            *reinterpret_cast<u32x2*>(&dst[c0 + 1][pt]) = u32x2{perm_hi(w[0], w[1]), perm_hi(w[2], w[3])};
+            *reinterpret_cast<u32x2*>(&dst[c0][sw(c0, pt)]) = u32x2{perm_lo(w[0], w[1]), perm_lo(w[2], w[3])};
+            *reinterpret_cast<u32x2*>(&dst[c0 + 1][sw(c0 + 1, pt)]) = u32x2{perm_hi(w[0], w[1]), perm_hi(w[2], w[3])};
         };
         put_t(Hp.kbh, kb);
         if constexpr (HP) put_t(Hp.kbl, kl8);
@@ -345,10 +350,10 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
     lds_barrier();  // ---- barrier 2
 
     // ---------------- part 3: Gram products, and the inputs the value waves read next step
+    // the rest of the next chunk (first read in part 2 of the next step), issued here so that the
+    // loads are spread over the step rather than queued all at once
+    load_chunk<LOAD_QK>(nxt, p, kl, row0, tn);
     if (work) {
-        // the rest of the next chunk (first read in part 2 of the next step), issued here so that the
-        // loads are spread over the step rather than queued all at once
-        if (n + 1 < nchunk) load_chunk<LOAD_QK>(nxt, p, kl, row0, t0 + C);
         if (kw < 3) {
             // A(0,0), A(1,0), A(1,1): split bf16 with three independent accumulators
             const int R = kw == 0 ? 0 : 1, S = kw == 2 ? 1 : 0;
@@ -373,8 +378,9 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
                 float v = a0[r] + a1[r];
                 if (R == S && l16 > i) v = 0.f;  // lower triangle including the diagonal
                 const uint32_t hi = pack_bf16(v, 0.f);
-                H.ah[SUB * R + i][tperm(SUB * S + l16)] = hi & 0xffffu;
-                H.al[SUB * R + i][tperm(SUB * S + l16)] = pack_bf16(v - bf16lo_to_f(hi), 0.f) & 0xffffu;
+                const int ac = sw(SUB * R + i, tperm(SUB * S + l16));
+                H.ah[SUB * R + i][ac] = hi & 0xffffu;
+                H.al[SUB * R + i][ac] = pack_bf16(v - bf16lo_to_f(hi), 0.f) & 0xffffu;
             }
         } else if (kw == 3) {
             // L(0,0), L(1,0), L(1,1): bf16 Km against K/Gamma (split bf16 when HP, else its high part)
@@ -403,17 +409,19 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
                 sm.h1.lf[SUB + i][SUB + l16] = (l16 >= i) ? 0.f : nb1[r] * acc2[r];
                 // L(1,0) as a split-bf16 operand, in the block of the T tile that T itself leaves unused
                 const uint32_t hi = pack_bf16(acc1[r], 0.f);
-                sm.val.th[SUB + i][tperm(l16)] = hi & 0xffffu;
-                sm.val.tl[SUB + i][tperm(l16)] = pack_bf16(acc1[r] - bf16lo_to_f(hi), 0.f) & 0xffffu;
+                sm.val.th[SUB + i][sw(SUB + i, tperm(l16))] = hi & 0xffffu;
+                sm.val.tl[SUB + i][sw(SUB + i, tperm(l16))] = pack_bf16(acc1[r] - bf16lo_to_f(hi), 0.f) & 0xffffu;
             }
         }
         // V^T and beta of this chunk (the value waves are done with the previous ones)
         if constexpr (!IN_F32) {
             if (lane < 32) {  // V^T for value columns 2*lane, 2*lane+1 of this half
-                const uint32_t* v = cur.v;
+                uint32_t v[TPW];
+#pragma unroll
+                for (int i = 0; i < TPW; ++i) v[i] = p.v ? cur.v[i] : 0u;  // v == NULL: v = 0
                 const int pt = tperm(TPW * kw);
-                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane][pt]) = u32x2{perm_lo(v[0], v[1]), perm_lo(v[2], v[3])};
-                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane + 1][pt]) = u32x2{perm_hi(v[0], v[1]), perm_hi(v[2], v[3])};
+                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane][sw(2 * lane, pt)]) = u32x2{perm_lo(v[0], v[1]), perm_lo(v[2], v[3])};
+                *reinterpret_cast<u32x2*>(&sm.h1.vt[2 * lane + 1][sw(2 * lane + 1, pt)]) = u32x2{perm_hi(v[0], v[1]), perm_hi(v[2], v[3])};
             }
         }
     }
@@ -426,7 +434,7 @@ __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int half, int 
     for (int e = 64 * kw + lane; e < 2 * SUB * SUB; e += 64 * NKW) {
         Handoff2& Hz = sm.h2[e >> 8];
         const int r = (e >> 4) & 15, c = tperm(SUB + (e & 15));
-        Hz.ah[r][c] = 0; Hz.al[r][c] = 0;
+        Hz.ah[r][sw(r, c)] = 0; Hz.al[r][sw(r, c)] = 0;
     }
     KeyLoad kl;
     kl.kw = kw;
@@ -442,7 +450,7 @@ __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int half, int 
     kl.boff = (uint32_t)(TPW * kw + (lane % TPW)) * 4u * p.H;
     Raw<IN_F32> ra, rb;
     Carry cy;
-    if (p.T > 0) load_chunk<LOAD_ALL>(ra, p, kl, row0, 0);
+    load_chunk<LOAD_ALL>(ra, p, kl, row0, 0);
     // two steps per iteration so the prefetch target alternates between two register sets
     for (int n = 0; n <= nchunk; n += 2) {
         key_step<IN_F32, HP>(sm, p, kl, row0, n, nchunk, ra, rb, cy);
@@ -498,10 +506,8 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 vnext[R][r] = gload<float>(vb, ((uint32_t)min(SUB * R + 4 * g4 + r, lim) * (uint32_t)p.H * DV + col) * 4u);
-        if (!p.v) vnext[0] = vnext[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
-    if constexpr (IN_F32)
-        if (nchunk > 0) load_v(0);
+    if constexpr (IN_F32) load_v(0);
 
     for (int n = 0; n <= nchunk; ++n) {
         const bool work = n >= 1;  // this step handles chunk n-1
@@ -547,10 +553,11 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
             const float tb = ((i == jb ? 1.f : 0.f) + yb) * beta[o + jb];
             uint32_t hi, lo;
             split_bf16(ta, tb, hi, lo);
-            V.th[o + i][tperm(o + ja)] = hi & 0xffffu;
-            V.th[o + i][tperm(o + jb)] = hi >> 16;
-            V.tl[o + i][tperm(o + ja)] = lo & 0xffffu;
-            V.tl[o + i][tperm(o + jb)] = lo >> 16;
+            const int ca = sw(o + i, tperm(o + ja)), cb = sw(o + i, tperm(o + jb));
+            V.th[o + i][ca] = hi & 0xffffu;
+            V.th[o + i][cb] = hi >> 16;
+            V.tl[o + i][ca] = lo & 0xffffu;
+            V.tl[o + i][cb] = lo >> 16;
         }
         lds_barrier();  // ---- barrier 1
 
@@ -561,11 +568,11 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
             // X = V - (K*Gamma) S, started from V in accumulator layout
             f32x4 xr[2];
             if constexpr (IN_F32) {
-                xr[0] = vnext[0];
-                xr[1] = vnext[1];
-                if (n < nchunk) load_v(n * C);  // V of the chunk handled next step
+                xr[0] = p.v ? vnext[0] : f32x4{0.f, 0.f, 0.f, 0.f};
+                xr[1] = p.v ? vnext[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+                load_v(min(n, nchunk - 1) * C);  // V of the chunk handled next step (unconditionally, as above)
             } else {
-                const u32x4 vv = ld16(&sm.h1.vt[16 * vw + l16][8 * g4]);  // tokens 4g4+r, then 16+4g4+r
+                const u32x4 vv = ld16(&sm.h1.vt[16 * vw + l16][sw(l16, 8 * g4)]);  // tokens 4g4+r, then 16+4g4+r
                 xr[0] = f32x4{bf16lo_to_f(vv.x), bf16hi_to_f(vv.x), bf16lo_to_f(vv.y), bf16hi_to_f(vv.y)};
                 xr[1] = f32x4{bf16lo_to_f(vv.z), bf16hi_to_f(vv.z), bf16lo_to_f(vv.w), bf16hi_to_f(vv.w)};
             }
@@ -602,11 +609,12 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
             f32x4 u[2];
             u32x2 bh, bl;
             split4(xr[0], bh, bl);
-            u[0] = prod3(ld8(&V.th[l16][8 * g4]), ld8(&V.tl[l16][8 * g4]), bh, bl);
+            const int c0s = sw(l16, 8 * g4);  // (rows l16 and SUB + l16 share the swizzle)
+            u[0] = prod3(ld8(&V.th[l16][c0s]), ld8(&V.tl[l16][c0s]), bh, bl);
             split4(u[0], bh, bl);
-            const f32x4 lu = prod3(ld8(&V.th[SUB + l16][8 * g4]), ld8(&V.tl[SUB + l16][8 * g4]), bh, bl);
+            const f32x4 lu = prod3(ld8(&V.th[SUB + l16][c0s]), ld8(&V.tl[SUB + l16][c0s]), bh, bl);
             split4(xr[1] - lu, bh, bl);
-            u[1] = prod3(ld8(&V.th[SUB + l16][8 * g4 + 4]), ld8(&V.tl[SUB + l16][8 * g4 + 4]), bh, bl);
+            u[1] = prod3(ld8(&V.th[SUB + l16][c0s + 4]), ld8(&V.tl[SUB + l16][c0s + 4]), bh, bl);
             if constexpr (!HP)
                 uf = u32x4{pack_f16(u[0][0], u[0][1]), pack_f16(u[0][2], u[0][3]), pack_f16(u[1][0], u[1][1]),
                            pack_f16(u[1][2], u[1][3])};
@@ -626,8 +634,8 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
                 gchar* ob = (gchar*)uniform_gptr((const char*)p.o + ((row0 + (size_t)t0 * p.H) * DV) * (OUT_F32 ? 4 : 2));
 #pragma unroll
                 for (int R = 0; R < 2; ++R) {
-                    const u32x4 aH = ld16(&H.ah[SUB * R + l16][8 * g4]);
-                    const u32x4 aL = ld16(&H.al[SUB * R + l16][8 * g4]);
+                    const u32x4 aH = ld16(&H.ah[SUB * R + l16][sw(l16, 8 * g4)]);
+                    const u32x4 aL = ld16(&H.al[SUB * R + l16][sw(l16, 8 * g4)]);
                     f32x4 acc = mfma_bf16(uh, aH, oacc[R]);
                     acc = mfma_bf16(ul, aH, acc);
                     acc = mfma_bf16(uh, aL, acc);
@@ -643,9 +651,9 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) {
                 const f32x4 gm = *reinterpret_cast<const f32x4*>(&H.gamc[16 * cb + 4 * g4]);
-                const u32x4 aH = ld16(&H.kbh[16 * cb + l16][8 * g4]);
+                const u32x4 aH = ld16(&H.kbh[16 * cb + l16][sw(l16, 8 * g4)]);
                 if constexpr (HP) {
-                    const u32x4 aL = ld16(&H.kbl[16 * cb + l16][8 * g4]);
+                    const u32x4 aL = ld16(&H.kbl[16 * cb + l16][sw(l16, 8 * g4)]);
                     f32x4 acc = mfma_bf16(aH, uh, st[cb] * gm);
                     acc = mfma_bf16(aH, ul, acc);
                     st[cb] = mfma_bf16(aL, uh, acc);
@@ -698,6 +706,7 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
     const int b = bh / p.H, h = bh - b * p.H;
     const size_t row0 = (size_t)b * p.tstride * p.H + h;  // row of token 0: (b*tstride + t)*H + h = row0 + t*H
     const int nchunk = (p.T + C - 1) / C;
+    if (nchunk == 0) return;  // (the host runs the state copy instead; every wave leaves here alike)
 
     if (wave < NKW)
         key_waves<IN_F32, HP>(sm, p, row0, half, wave, lane, nchunk);
@@ -723,6 +732,7 @@ void launch_bf16_io(const Params& p, hipStream_t stream, dim3 grid, dim3 block) 
 
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t stream) {
     using namespace bf16path;
+    if (p.T == 0) return launch_state_copy(p, stream);
     const dim3 grid(2 * p.B * p.H), block(NTHR);
     if (p.in_f32)  // the layer's variant (it records no checkpoints)
         hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, true, true, false>), grid, block, 0, stream, p);
