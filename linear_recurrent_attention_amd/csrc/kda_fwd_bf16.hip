@@ -18,11 +18,14 @@
 // Mapping.  One workgroup per (batch, head, value half): the 128 value columns are split over two
 // workgroups that both compute the key-side products, so 2*B*H workgroups fill the chip; the two
 // halves of a head are placed on the same XCD so their common reads of q, k, g share its L2.
-// Each workgroup runs 8 waves as a two-stage pipeline over chunks:
-//   key waves 0-3   chunk n:   octet decay sums, then all decay factors, then the Gram products;
-//   value waves 4-7 chunk n-1: UT inverse, then the state-dependent products and the output;
-//                              wave 4+w owns 16 value columns of the float32 state in matrix-core
-//                              accumulator layout for the whole run.
+// Each workgroup runs 12 waves as a two-stage pipeline over chunks:
+//   key waves 0-7    chunk n:   wave kw owns tokens 4kw..4kw+3 (two key channels per lane): quad
+//                               decay sums, then all decay factors, then the Gram products (waves
+//                               0-3); the chunk's value-side tiles are written at the start of the
+//                               next step;
+//   value waves 8-11 chunk n-1: UT inverse, then the state-dependent products and the output;
+//                               wave 8+w owns 16 value columns of the float32 state in matrix-core
+//                               accumulator layout for the whole run.
 // Both groups execute the same three workgroup barriers per step; data passes from the key waves
 // to the value waves through LDS buffers indexed by chunk parity.  Chunk inputs are prefetched
 // one chunk ahead into registers.
