@@ -113,13 +113,23 @@ __device__ __forceinline__ void fetch_chunk(Raw<D>& w, const BwdParams& p, int b
         }
     }
     if (tid < CS) w.beta = p.beta[row(tid)];
+    // (branches around whole groups of loads: a select per loaded value would make each load wait)
+    if (p.dO) {
 #pragma unroll
-    for (int k = 0; k < Raw<D>::PV; ++k) {
-        const int e = tid + NT * k, r = e / DH, j = e % DH;
-        const size_t idx = row(r) * D + half * DH + j;
-        w.dO[k] = 0.f;
-        if (p.dO) w.dO[k] = ldx<DO_BF16>(p.dO, idx);  // dO == NULL: zero (never dereferenced)
-        if (want_v) w.v[k] = ldx<IN_BF16>(p.v, idx);
+        for (int k = 0; k < Raw<D>::PV; ++k) {
+            const int e = tid + NT * k, r = e / DH, j = e % DH;
+            w.dO[k] = ldx<DO_BF16>(p.dO, row(r) * D + half * DH + j);
+        }
+    } else {  // dO == NULL: zero (never dereferenced)
+#pragma unroll
+        for (int k = 0; k < Raw<D>::PV; ++k) w.dO[k] = 0.f;
+    }
+    if (want_v) {
+#pragma unroll
+        for (int k = 0; k < Raw<D>::PV; ++k) {
+            const int e = tid + NT * k, r = e / DH, j = e % DH;
+            w.v[k] = ldx<IN_BF16>(p.v, row(r) * D + half * DH + j);
+        }
     }
 }
 
@@ -159,13 +169,6 @@ __device__ __forceinline__ void build_chunk(Chunk<D>& c, const Raw<D>& w, float 
         c.dO[r][j] = r < n ? w.dO[k] : 0.f;
         if (want_v) c.X[r][j] = r < n ? w.v[k] : 0.f;
     }
-}
-
-template <int D, bool IN_BF16, bool DO_BF16>
-__device__ __forceinline__ void load_chunk(Chunk<D>& c, const BwdParams& p, int b, int h, int c0, int half, bool want_v) {
-    Raw<D> w;
-    fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, c0, half, want_v);
-    build_chunk<D>(c, w, p.scale, want_v);
 }
 
 // Lane m of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
@@ -294,13 +297,31 @@ struct alignas(16) Grad {
     float dbeta[CS];
 };
 
-// dst[r][j] = src[r][col0 + j] (a [D][D] float32 matrix in global memory, NULL = zeros)
+// This thread's entries e = tid + NT*k of the value-half tile src[r][col0 + j] (r = e / DH,
+// j = e % DH) of a [D][D] float32 matrix in global memory (NULL = zeros), into registers; put_state
+// writes them to an LDS tile.
 template <int D>
-__device__ __forceinline__ void load_state(float (*dst)[D / 2 + 1], const float* src, int col0) {
+__device__ __forceinline__ void fetch_state(float* v, const float* src, int col0) {
     constexpr int DH = D / 2;
-    for (int e = threadIdx.x; e < D * DH; e += NT) {
-        const int r = e / DH, j = e % DH;
-        dst[r][j] = src ? src[(size_t)r * D + col0 + j] : 0.f;
+    // (one branch around all the loads: a select per loaded value would make each load wait)
+    if (src) {
+#pragma unroll
+        for (int k = 0; k < D * DH / NT; ++k) {
+            const int e = threadIdx.x + NT * k, r = e / DH, j = e % DH;
+            v[k] = src[(size_t)r * D + col0 + j];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < D * DH / NT; ++k) v[k] = 0.f;
+    }
+}
+template <int D>
+__device__ __forceinline__ void put_state(float (*dst)[D / 2 + 1], const float* v) {
+    constexpr int DH = D / 2;
+#pragma unroll
+    for (int k = 0; k < D * DH / NT; ++k) {
+        const int e = threadIdx.x + NT * k;
+        dst[e / DH][e % DH] = v[k];
     }
 }
 
@@ -325,11 +346,19 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
     // Two chunks: P = start state -> Q = state after the first chunk; second chunk: S = Q, dS = P
     // (the interval's end gradient); its start gradient goes to Q; first chunk: S = P (start state
     // again), dS = Q.
-    load_state<D>(gr.P, S0g, col0);
-    __syncthreads();
+    // Global reads: both state tiles and the first chunk's inputs are issued here, the other
+    // chunk's inputs one chunk ahead (each into registers), so that their latencies overlap work.
+    constexpr int SPT = D * DH / NT;
+    float s0r[SPT], dsr[SPT];
+    fetch_state<D>(s0r, S0g, col0);
+    fetch_state<D>(dsr, dSe, col0);
+    Raw<D> w;
+    fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, i * CK, half, true);
+    put_state<D>(gr.P, s0r);
     if (nsub == 2) {  // Q = Diag(gam) S + Kb^T Tm (V - Kg S)
-        load_chunk<D, IN_BF16, DO_BF16>(c, p, b, h, i * CK, half, true);
+        build_chunk<D>(c, w, p.scale, true);
         __syncthreads();
+        fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, i * CK + CS, half, true);  // the second chunk
         chunk_triangles<D>(c);
         mgemm<CS, DH, D>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return gr.P[k][n]; },
                               [&](int m, int n, float v) { c.X[m][n] -= v; });
@@ -340,16 +369,18 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         mgemm<D, DH, CS>([&](int m, int k) { return c.Kb[k][m]; }, [&](int k, int n) { return c.U[k][n]; },
                               [&](int m, int n, float v) { gr.Q[m][n] = __builtin_fmaf(c.gam[m], gr.P[m][n], v); });
         __syncthreads();
-        load_state<D>(gr.P, dSe, col0);
+        put_state<D>(gr.P, dsr);
     } else {
-        load_state<D>(gr.Q, dSe, col0);
+        put_state<D>(gr.Q, dsr);
     }
     __syncthreads();
-    for (int s = nsub - 1; s >= 0; --s) {
+    // the interval's chunks in reverse (written out twice rather than looped, so that the registers
+    // holding the prefetched inputs are live only where they are needed)
+    auto step = [&](const int s) {
         const int c0 = i * CK + s * CS;
         float (*Sb)[DH + 1] = (nsub == 2 && s == 1) ? gr.Q : gr.P;
         float (*dSb)[DH + 1] = (nsub == 2 && s == 1) ? gr.P : gr.Q;
-        load_chunk<D, IN_BF16, DO_BF16>(c, p, b, h, c0, half, true);
+        build_chunk<D>(c, w, p.scale, true);
         __syncthreads();
         chunk_triangles<D>(c);
         // X = V - Kg S;  U = Tm X
@@ -488,6 +519,8 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             }
         }
         if (nsub == 2 && s == 1) {
+            // the first chunk's inputs again, for the next step (issued after this chunk's atomics)
+            fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, i * CK, half, true);
             // the gradient of the state between the two chunks, Diag(gam) dS + Qg^T dO - Kg^T dX,
             // into Q (the state S of this chunk, no longer read); then P gets the start state back
             __syncthreads();
@@ -496,10 +529,12 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             mgemm<D, DH, CS>([&](int m, int k) { return c.Kg[k][m]; }, [&](int k, int n) { return c.dX[k][n]; },
                                   [&](int m, int n, float v) { gr.Q[m][n] -= v; });
             __syncthreads();
-            load_state<D>(gr.P, S0g, col0);
+            put_state<D>(gr.P, s0r);
         }
         __syncthreads();
-    }
+    };
+    if (nsub == 2) step(1);
+    step(0);
 }
 
 // Zero the accumulated outputs.
