@@ -31,6 +31,8 @@
 #include "kda_common.h"
 #include "kda_internal.h"
 
+#include <type_traits>
+
 namespace kda {
 namespace bwd {
 
@@ -38,12 +40,17 @@ constexpr int CS = 16;   // tokens per chunk
 constexpr int NT = 512;  // threads per workgroup (8 waves)
 static_assert(NT >= CS * CS, "one thread per chunk-matrix entry");
 
+// Element i of a bf16 or float32 array as raw bits: for bf16 the aligned 32-bit word holding it
+// (its half is selected when the value is used, cvt with odd = i & 1), for float32 the element.
+// Prefetched inputs stay raw until used: any conversion right after the load (a 16-bit load's
+// zero extension included) would make the load wait there.
 template <bool BF16>
-__device__ __forceinline__ float ldx(const void* p, size_t i) {
-    if constexpr (BF16)
-        return __uint_as_float((uint32_t)(reinterpret_cast<const uint16_t*>(p)[i]) << 16);
-    else
-        return reinterpret_cast<const float*>(p)[i];
+__device__ __forceinline__ uint32_t ldr(const void* p, size_t i) {
+    return reinterpret_cast<const uint32_t*>(p)[BF16 ? i >> 1 : i];
+}
+template <bool BF16>
+__device__ __forceinline__ float cvt(uint32_t x, bool odd) {
+    return __uint_as_float(BF16 ? (odd ? x & 0xffff0000u : x << 16) : x);
 }
 
 // out(m, n) = sum_k a(m, k) b(k, n) for m < M, n < N on the matrix cores: float32
@@ -91,9 +98,10 @@ struct alignas(16) Chunk {
 template <int D>
 struct Raw {
     static constexpr int PV = CS * (D / 2) / NT;
-    float q[CS], k[CS], g[CS];
+    uint32_t q[CS], k[CS];  // raw (see ldr)
+    float g[CS];
     float beta;
-    float dO[PV], v[PV];
+    uint32_t dO[PV], v[PV];
     int n;  // valid tokens
 };
 
@@ -103,39 +111,48 @@ __device__ __forceinline__ void fetch_chunk(Raw<D>& w, const BwdParams& p, int b
     const int tid = threadIdx.x;
     const int n = min(CS, p.T - c0);  // valid tokens (>= 1); rows past them read the last valid one
     w.n = n;
-    auto row = [&](int r) { return ((size_t)b * p.T + c0 + min(r, n - 1)) * p.H + h; };
+    // the chunk's first row (b, c0, h) as wave-uniform base pointers; rows r as 32-bit element offsets
+    const size_t rb = ((size_t)b * p.T + c0) * p.H + h;
+    const uint32_t rs = (uint32_t)p.H * D;
+    auto roff = [&](int r) { return (uint32_t)min(r, n - 1) * rs; };
+    constexpr size_t ie = IN_BF16 ? 2 : 4, oe = DO_BF16 ? 2 : 4;
     if (tid < D) {
+        const float* gb = p.g + rb * D;
+        const void* qb = (const char*)p.q + rb * D * ie;
+        const void* kb = (const char*)p.k + rb * D * ie;
 #pragma unroll
         for (int r = 0; r < CS; ++r) {
-            w.g[r] = p.g[row(r) * D + tid];
-            w.q[r] = ldx<IN_BF16>(p.q, row(r) * D + tid);
-            w.k[r] = ldx<IN_BF16>(p.k, row(r) * D + tid);
+            w.g[r] = gb[roff(r) + tid];
+            w.q[r] = ldr<IN_BF16>(qb, roff(r) + tid);
+            w.k[r] = ldr<IN_BF16>(kb, roff(r) + tid);
         }
     }
-    if (tid < CS) w.beta = p.beta[row(tid)];
+    if (tid < CS) w.beta = p.beta[rb + (size_t)min(tid, n - 1) * p.H];
     // (branches around whole groups of loads: a select per loaded value would make each load wait)
     if (p.dO) {
+        const void* ob = (const char*)p.dO + (rb * D + half * DH) * oe;
 #pragma unroll
         for (int k = 0; k < Raw<D>::PV; ++k) {
             const int e = tid + NT * k, r = e / DH, j = e % DH;
-            w.dO[k] = ldx<DO_BF16>(p.dO, row(r) * D + half * DH + j);
+            w.dO[k] = ldr<DO_BF16>(ob, roff(r) + j);
         }
     } else {  // dO == NULL: zero (never dereferenced)
 #pragma unroll
-        for (int k = 0; k < Raw<D>::PV; ++k) w.dO[k] = 0.f;
+        for (int k = 0; k < Raw<D>::PV; ++k) w.dO[k] = 0u;
     }
     if (want_v) {
+        const void* vb = (const char*)p.v + (rb * D + half * DH) * ie;
 #pragma unroll
         for (int k = 0; k < Raw<D>::PV; ++k) {
             const int e = tid + NT * k, r = e / DH, j = e % DH;
-            w.v[k] = ldx<IN_BF16>(p.v, row(r) * D + half * DH + j);
+            w.v[k] = ldr<IN_BF16>(vb, roff(r) + j);
         }
     }
 }
 
 // The chunk's factors from the fetched inputs (tokens past the valid ones are zeroed: k = q = v = 0,
 // g = 0, beta = 0, dO = 0).
-template <int D>
+template <int D, bool IN_BF16, bool DO_BF16>
 __device__ __forceinline__ void build_chunk(Chunk<D>& c, const Raw<D>& w, float scale, bool want_v) {
     constexpr int DH = D / 2;
     const int tid = threadIdx.x;
@@ -149,25 +166,26 @@ __device__ __forceinline__ void build_chunk(Chunk<D>& c, const Raw<D>& w, float 
             s += r < n ? w.g[r] : 0.f;
             bc[r] = s;
         }
-        const float last = bc[CS - 1];
-        c.gam[ch] = fexp(last);
+        const float last = bc[CS - 1], gl = fexp(last);
+        c.gam[ch] = gl;
 #pragma unroll
         for (int r = 0; r < CS; ++r) {
-            const float q = r < n ? w.q[r] * scale : 0.f, k = r < n ? w.k[r] : 0.f;
-            const float e = fexp(bc[r]);
+            const float q = r < n ? cvt<IN_BF16>(w.q[r], ch & 1) * scale : 0.f;
+            const float k = r < n ? cvt<IN_BF16>(w.k[r], ch & 1) : 0.f;
+            const float e = fexp(bc[r]), f = fexp(-bc[r]);  // exp(b), exp(-b), both within [e^-80, e^80]
             c.Gam[r][ch] = e;
             c.Qg[r][ch] = q * e;
             c.Kg[r][ch] = k * e;
-            c.Kh[r][ch] = k * fexp(-bc[r]);
-            c.Kb[r][ch] = k * fexp(last - bc[r]);
+            c.Kh[r][ch] = k * f;
+            c.Kb[r][ch] = k * (gl * f);  // exp(b_last - b)
         }
     }
     if (tid < CS) c.beta[tid] = tid < n ? w.beta : 0.f;
 #pragma unroll
     for (int k = 0; k < Raw<D>::PV; ++k) {
         const int e = tid + NT * k, r = e / DH, j = e % DH;
-        c.dO[r][j] = r < n ? w.dO[k] : 0.f;
-        if (want_v) c.X[r][j] = r < n ? w.v[k] : 0.f;
+        c.dO[r][j] = r < n ? cvt<DO_BF16>(w.dO[k], j & 1) : 0.f;
+        if (want_v) c.X[r][j] = r < n ? cvt<IN_BF16>(w.v[k], j & 1) : 0.f;
     }
 }
 
@@ -221,12 +239,172 @@ __device__ __forceinline__ void chunk_triangles(Chunk<D>& c) {
 // ------------------------------------------------------------------------------------------------
 // 2. state gradients at interval boundaries, sequential in reverse
 // ------------------------------------------------------------------------------------------------
+// out(m, n) = sum_k a(m, k) b(k, n) as in mgemm, on waves W0 .. W0 + NWU - 1 only (tile t on wave
+// W0 + t mod NWU); the other waves return at once.
+template <int M, int N, int K, int W0, int NWU, typename FA, typename FB, typename F>
+__device__ __forceinline__ void mgemm_w(FA a, FB b, F f) {
+    static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "tile shape");
+    constexpr int TN = N / 16;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (wave < W0 || wave >= W0 + NWU) return;
+    const int l16 = lane & 15, g = lane >> 4;
+    for (int tile = wave - W0; tile < (M / 16) * TN; tile += NWU) {
+        const int m0 = (tile / TN) * 16, n0 = (tile % TN) * 16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int k = 0; k < K; k += 4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(m0 + l16, k + g), b(k + g, n0 + l16), acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f(m0 + 4 * g + r, n0 + l16, acc[r]);
+    }
+}
+
+// What the state pass keeps of a chunk (two of these: the chunk being processed and the next one).
+template <int D>
+struct alignas(16) SChunk {
+    static constexpr int DH = D / 2;
+    float Qg[CS][D + KP], Kg[CS][D + KP], Kh[CS][D + KP], Kb[CS][D + KP];
+    float gam[D];
+    float dO[CS][DH + 1];
+    float L[CS][CS + 1], A[CS][CS + 1], N[CS][CS + 1], Tm[CS][CS + 1];
+    float beta[CS];
+};
+
+// One chunk's inputs as the state pass's factor waves (4-7, thread u = tid - NT/2) hold them:
+// channel u % D's g over the chunk's tokens and q, k over its share of them, tokens
+// TS*(u/D) .. TS*(u/D + 1) - 1 (the NT/2 threads split each channel's tokens into NT/2 / D shares),
+// beta of token u (u < CS), dO entries u + (NT/2)*k of the value half.
+constexpr int NTH = NT / 2;  // threads of the factor waves
+template <int D>
+struct SRaw {
+    static constexpr int PV = CS * (D / 2) / NTH;
+    static constexpr int TS = CS * D / NTH;  // tokens per thread (8 for D = 128, 4 for D = 64)
+    uint32_t q[TS], k[TS];  // raw (see ldr)
+    float g[CS];
+    float beta;
+    uint32_t dO[PV];
+    int n;  // valid tokens
+};
+
+template <int D, bool IN_BF16, bool DO_BF16>
+__device__ __forceinline__ void fetch_s(SRaw<D>& w, const BwdParams& p, int b, int h, int c0, int half) {
+    constexpr int DH = D / 2;
+    const int u = threadIdx.x - NTH;
+    const int n = min(CS, p.T - c0);  // valid tokens (>= 1); rows past them read the last valid one
+    w.n = n;
+    // the chunk's first row (b, c0, h) as wave-uniform base pointers; rows r as 32-bit element offsets
+    const size_t rb = ((size_t)b * p.T + c0) * p.H + h;
+    const uint32_t rs = (uint32_t)p.H * D;
+    auto roff = [&](int r) { return (uint32_t)min(r, n - 1) * rs; };
+    const float* gb = p.g + rb * D;
+    const void* qb = (const char*)p.q + rb * D * (IN_BF16 ? 2 : 4);
+    const void* kb = (const char*)p.k + rb * D * (IN_BF16 ? 2 : 4);
+    {
+        constexpr int TS = SRaw<D>::TS;
+        const int ch = u % D, r0 = TS * (u / D);
+#pragma unroll
+        for (int r = 0; r < CS; ++r) w.g[r] = gb[roff(r) + ch];  // (every share needs the cumulative sums)
+#pragma unroll
+        for (int r = 0; r < TS; ++r) {
+            w.q[r] = ldr<IN_BF16>(qb, roff(r0 + r) + ch);
+            w.k[r] = ldr<IN_BF16>(kb, roff(r0 + r) + ch);
+        }
+    }
+    if (u < CS) w.beta = p.beta[rb + (size_t)min(u, n - 1) * p.H];
+    if (p.dO) {  // (one branch around the loads: a select per loaded value would make each load wait)
+        const void* ob = (const char*)p.dO + (rb * D + half * DH) * (DO_BF16 ? 2 : 4);
+#pragma unroll
+        for (int k = 0; k < SRaw<D>::PV; ++k) {
+            const int e = u + NTH * k, r = e / DH, j = e % DH;
+            w.dO[k] = ldr<DO_BF16>(ob, roff(r) + j);
+        }
+    } else {  // dO == NULL: zero (never dereferenced)
+#pragma unroll
+        for (int k = 0; k < SRaw<D>::PV; ++k) w.dO[k] = 0u;
+    }
+}
+
+// The chunk's factors (tokens past the valid ones are zeroed: k = q = 0, g = 0, beta = 0, dO = 0).
+template <int D, bool IN_BF16, bool DO_BF16>
+__device__ __forceinline__ void build_s(SChunk<D>& c, const SRaw<D>& w, float scale) {
+    constexpr int DH = D / 2;
+    const int u = threadIdx.x - NTH;
+    const int n = w.n;
+    {
+        constexpr int TS = SRaw<D>::TS;
+        const int ch = u % D, r0 = TS * (u / D);
+        float bc[CS];
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < CS; ++r) {
+            s += r < n ? w.g[r] : 0.f;
+            bc[r] = s;
+        }
+        const float last = bc[CS - 1], gl = fexp(last);
+        if (r0 == 0) c.gam[ch] = gl;
+        // this thread's share of tokens (a compile-time offset per branch keeps bc in registers)
+        auto share = [&](auto r0c) {
+            constexpr int R0 = decltype(r0c)::value;
+#pragma unroll
+            for (int r = 0; r < TS; ++r) {
+                const int t = R0 + r;
+                const float q = t < n ? cvt<IN_BF16>(w.q[r], ch & 1) * scale : 0.f;
+                const float k = t < n ? cvt<IN_BF16>(w.k[r], ch & 1) : 0.f;
+                const float e = fexp(bc[t]), f = fexp(-bc[t]);  // exp(b), exp(-b), both within [e^-80, e^80]
+                c.Qg[t][ch] = q * e;
+                c.Kg[t][ch] = k * e;
+                c.Kh[t][ch] = k * f;
+                c.Kb[t][ch] = k * (gl * f);  // exp(b_last - b)
+            }
+        };
+        static_assert(CS / TS <= 4, "up to four shares per channel");
+        switch (r0 / TS) {  // wave-uniform
+            case 0: share(std::integral_constant<int, 0>{}); break;
+            case 1: if constexpr (CS / TS > 1) share(std::integral_constant<int, TS>{}); break;
+            case 2: if constexpr (CS / TS > 2) share(std::integral_constant<int, 2 * TS>{}); break;
+            default: if constexpr (CS / TS > 3) share(std::integral_constant<int, 3 * TS>{}); break;
+        }
+    }
+    if (u < CS) c.beta[u] = u < n ? w.beta : 0.f;
+#pragma unroll
+    for (int k = 0; k < SRaw<D>::PV; ++k) {
+        const int e = u + NTH * k, r = e / DH, j = e % DH;
+        c.dO[r][j] = r < n ? cvt<DO_BF16>(w.dO[k], j & 1) : 0.f;
+    }
+}
+
+// N = (I + Diag(beta) L)^{-1} and Tm = N Diag(beta) from the chunk's L, on the last CS*CS threads,
+// one matrix entry per lane (the substitution of chunk_triangles).
+template <typename CT>
+__device__ __forceinline__ void unit_inverse(CT& c) {
+    const int te = (int)threadIdx.x - (NT - CS * CS);
+    if (te < 0) return;
+    const int j = te / CS, i = te % CS;
+    const float nb = -c.beta[i];
+    float nr[CS];
+#pragma unroll
+    for (int m = 0; m < CS; ++m) nr[m] = nb * c.L[i][m];
+    float y = nb * c.L[i][j];
+#pragma unroll
+    for (int m = 0; m < CS - 1; ++m) y = __builtin_fmaf(nr[m], row_bcast(y, m), y);
+    const float x = (i == j ? 1.f : 0.f) + y;
+    c.N[i][j] = x;
+    c.Tm[i][j] = x * c.beta[j];
+}
+
+// One workgroup per (sequence, value half), reverse over 16-token chunks, as a two-stage pipeline:
+// waves 0-3 carry dS through chunk j (dU = Kb dS + A^T dO, dX = Tm^T dU), while waves 4-7 build
+// chunk j-1's factors, its Gram products L and A and its inverse, and fetch chunk j-3's inputs;
+// then all waves update dS <- Diag(gam) dS + Qg^T dO - Kg^T dX.  Three barriers per chunk.
 template <int D, int CK, bool IN_BF16, bool DO_BF16>
 __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
     constexpr int DH = D / 2;
-    __shared__ Chunk<D> c;
+    static_assert(NT - CS * CS >= NTH && D <= NTH && CS <= NTH, "the factor waves own the inverse and the build");
+    __shared__ SChunk<D> sc[2];
+    __shared__ float dU[CS][DH + 1], dX[CS][DH + 1];
     __shared__ float dS[D][DH + 1];
     const int tid = threadIdx.x;
+    const bool chain = tid < NTH;  // waves 0-3
     const int bh = blockIdx.x >> 1, half = blockIdx.x & 1;
     const int b = bh / p.H, h = bh - b * p.H;
     const int nint = p.nint;
@@ -238,42 +416,71 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
         dS[r][j] = v;
         p.dSb[at(nint - 1) + (size_t)r * D + j] = v;
     }
-    // chunks in reverse order; the next one's inputs are fetched while the current one is processed
     const int nch = (p.T + CS - 1) / CS;
-    Raw<D> w;
-    fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, (nch - 1) * CS, half, false);
+    constexpr int SPI = CK / CS;  // chunks per interval
+    // the last chunk's factors; the next two chunks' inputs in flight (iteration k of the loop below
+    // builds chunk nch-2-k from register set k & 1 and refills that set with chunk nch-4-k; chunk
+    // indices below 0 read chunk 0 again, unused)
+    SRaw<D> wa, wb;
+    if (!chain) {
+        fetch_s<D, IN_BF16, DO_BF16>(wb, p, b, h, (nch - 1) * CS, half);
+        build_s<D, IN_BF16, DO_BF16>(sc[(nch - 1) & 1], wb, p.scale);
+        fetch_s<D, IN_BF16, DO_BF16>(wa, p, b, h, max(nch - 2, 0) * CS, half);
+        fetch_s<D, IN_BF16, DO_BF16>(wb, p, b, h, max(nch - 3, 0) * CS, half);
+    }
     __syncthreads();
-    for (int i = nint - 1; i >= 0; --i) {
-        const int nsub = (min(CK, p.T - i * CK) + CS - 1) / CS;
-        for (int s = nsub - 1; s >= 0; --s) {
-            const int cj = (i * CK + s * CS) / CS;  // chunk index
-            build_chunk<D>(c, w, p.scale, false);
-            __syncthreads();
-            if (cj > 0) fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, (cj - 1) * CS, half, false);
-            chunk_triangles<D>(c);
-            // dU = Kb dS + A^T dO
-            mgemm<CS, DH, D>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dS[k][n]; },
-                                  [&](int m, int n, float v) { c.dU[m][n] = v; });
-            mgemm<CS, DH, CS>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
-                                   [&](int m, int n, float v) { c.dU[m][n] += v; });
-            __syncthreads();
-            // dX = Tm^T dU
-            mgemm<CS, DH, CS>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
-                                   [&](int m, int n, float v) { c.dX[m][n] = v; });
-            __syncthreads();
-            // dS <- Diag(gam) dS + Qg^T dO - Kg^T dX   (each entry read and written by its own thread)
-            mgemm<D, DH, CS>([&](int m, int k) { return c.Qg[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
-                                  [&](int m, int n, float v) { dS[m][n] = __builtin_fmaf(c.gam[m], dS[m][n], v); });
-            mgemm<D, DH, CS>([&](int m, int k) { return c.Kg[k][m]; }, [&](int k, int n) { return c.dX[k][n]; },
-                                  [&](int m, int n, float v) { dS[m][n] -= v; });
-            __syncthreads();
+    {
+        SChunk<D>& c = sc[(nch - 1) & 1];
+        mgemm_w<CS, CS, D, 4, 1>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
+                                 [&](int m, int n, float v) { c.L[m][n] = n < m ? v : 0.f; });
+        mgemm_w<CS, CS, D, 5, 1>([&](int m, int k) { return c.Qg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
+                                 [&](int m, int n, float v) { c.A[m][n] = n <= m ? v : 0.f; });
+        __syncthreads();
+        unit_inverse(c);
+        __syncthreads();
+    }
+    auto step = [&](const int cj, SRaw<D>& w) {
+        SChunk<D>& c = sc[cj & 1];         // this chunk
+        SChunk<D>& cn = sc[(cj - 1) & 1];  // the next one (chunk cj - 1)
+        const bool next = cj >= 1;
+        // dU = Kb dS + A^T dO  |  the next chunk's factors; its successor's inputs
+        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dS[k][n]; },
+                                 [&](int m, int n, float v) { dU[m][n] = v; });
+        mgemm_w<CS, DH, CS, 0, 4>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+                                  [&](int m, int n, float v) { dU[m][n] += v; });
+        if (!chain && next) {
+            build_s<D, IN_BF16, DO_BF16>(cn, w, p.scale);
+            fetch_s<D, IN_BF16, DO_BF16>(w, p, b, h, max(cj - 3, 0) * CS, half);
         }
-        if (i >= 1) {
+        __syncthreads();
+        // dX = Tm^T dU  |  the next chunk's L and A
+        mgemm_w<CS, DH, CS, 0, 4>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return dU[k][n]; },
+                                  [&](int m, int n, float v) { dX[m][n] = v; });
+        if (next) {
+            mgemm_w<CS, CS, D, 4, 1>([&](int m, int k) { return cn.Kg[m][k]; }, [&](int k, int n) { return cn.Kh[n][k]; },
+                                     [&](int m, int n, float v) { cn.L[m][n] = n < m ? v : 0.f; });
+            mgemm_w<CS, CS, D, 5, 1>([&](int m, int k) { return cn.Qg[m][k]; }, [&](int k, int n) { return cn.Kh[n][k]; },
+                                     [&](int m, int n, float v) { cn.A[m][n] = n <= m ? v : 0.f; });
+        }
+        __syncthreads();
+        // the next inverse (waves 4-7), then on all waves
+        // dS <- Diag(gam) dS + Qg^T dO - Kg^T dX   (each entry read and written by its own thread)
+        if (next) unit_inverse(cn);
+        mgemm_w<D, DH, CS, 0, NT / 64>([&](int m, int k) { return c.Qg[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+                                       [&](int m, int n, float v) { dS[m][n] = __builtin_fmaf(c.gam[m], dS[m][n], v); });
+        mgemm_w<D, DH, CS, 0, NT / 64>([&](int m, int k) { return c.Kg[k][m]; }, [&](int k, int n) { return dX[k][n]; },
+                                       [&](int m, int n, float v) { dS[m][n] -= v; });
+        __syncthreads();
+        if (cj % SPI == 0 && cj > 0) {  // the start of interval cj / SPI: the gradient of the state there
             for (int e = tid; e < D * DH; e += NT) {
                 const int r = e / DH, j = e % DH;
-                p.dSb[at(i - 1) + (size_t)r * D + j] = dS[r][j];
+                p.dSb[at(cj / SPI - 1) + (size_t)r * D + j] = dS[r][j];
             }
         }
+    };
+    for (int cj = nch - 1; cj >= 0; cj -= 2) {
+        step(cj, wa);
+        if (cj >= 1) step(cj - 1, wb);
     }
     if (p.dS0) {
         for (int e = tid; e < D * DH; e += NT) {
@@ -356,7 +563,7 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
     fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, i * CK, half, true);
     put_state<D>(gr.P, s0r);
     if (nsub == 2) {  // Q = Diag(gam) S + Kb^T Tm (V - Kg S)
-        build_chunk<D>(c, w, p.scale, true);
+        build_chunk<D, IN_BF16, DO_BF16>(c, w, p.scale, true);
         __syncthreads();
         fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, i * CK + CS, half, true);  // the second chunk
         chunk_triangles<D>(c);
@@ -380,7 +587,7 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         const int c0 = i * CK + s * CS;
         float (*Sb)[DH + 1] = (nsub == 2 && s == 1) ? gr.Q : gr.P;
         float (*dSb)[DH + 1] = (nsub == 2 && s == 1) ? gr.P : gr.Q;
-        build_chunk<D>(c, w, p.scale, true);
+        build_chunk<D, IN_BF16, DO_BF16>(c, w, p.scale, true);
         __syncthreads();
         chunk_triangles<D>(c);
         // X = V - Kg S;  U = Tm X
