@@ -93,17 +93,32 @@ struct alignas(16) Chunk {
     float beta[CS];
 };
 
-// One chunk's inputs as this thread holds them: channel tid's q, k, g over the chunk's tokens
-// (tid < D), beta of token tid (tid < CS), and dO / V entries tid + NT*k of the value half.
+// One chunk's inputs as thread tid holds them: channel tid % D's g over the chunk's tokens and q,
+// k over its share of them, tokens TS*(tid/D) .. TS*(tid/D + 1) - 1 (the NT threads split each
+// channel's tokens into NT/D shares), beta of token tid (tid < CS), and dO / V entries tid + NT*k
+// of the value half.
 template <int D>
 struct Raw {
     static constexpr int PV = CS * (D / 2) / NT;
-    uint32_t q[CS], k[CS];  // raw (see ldr)
+    static constexpr int TS = CS * D / NT;  // tokens per thread (4 for D = 128, 2 for D = 64)
+    uint32_t q[TS], k[TS];  // raw (see ldr)
     float g[CS];
     float beta;
     uint32_t dO[PV], v[PV];
     int n;  // valid tokens
 };
+
+// f(std::integral_constant<int, s>) for the wave-uniform share index sh < NS (a compile-time
+// token offset per share keeps register arrays indexed by constants).
+template <int NS, typename F>
+__device__ __forceinline__ void for_share(int sh, F f) {
+    if constexpr (NS > 0) {
+        if (sh == NS - 1)
+            f(std::integral_constant<int, NS - 1>{});
+        else
+            for_share<NS - 1>(sh, f);
+    }
+}
 
 template <int D, bool IN_BF16, bool DO_BF16>
 __device__ __forceinline__ void fetch_chunk(Raw<D>& w, const BwdParams& p, int b, int h, int c0, int half, bool want_v) {
@@ -116,15 +131,18 @@ __device__ __forceinline__ void fetch_chunk(Raw<D>& w, const BwdParams& p, int b
     const uint32_t rs = (uint32_t)p.H * D;
     auto roff = [&](int r) { return (uint32_t)min(r, n - 1) * rs; };
     constexpr size_t ie = IN_BF16 ? 2 : 4, oe = DO_BF16 ? 2 : 4;
-    if (tid < D) {
+    {
+        constexpr int TS = Raw<D>::TS;
+        const int ch = tid % D, r0 = TS * (tid / D);
         const float* gb = p.g + rb * D;
         const void* qb = (const char*)p.q + rb * D * ie;
         const void* kb = (const char*)p.k + rb * D * ie;
 #pragma unroll
-        for (int r = 0; r < CS; ++r) {
-            w.g[r] = gb[roff(r) + tid];
-            w.q[r] = ldr<IN_BF16>(qb, roff(r) + tid);
-            w.k[r] = ldr<IN_BF16>(kb, roff(r) + tid);
+        for (int r = 0; r < CS; ++r) w.g[r] = gb[roff(r) + ch];  // (every share needs the cumulative sums)
+#pragma unroll
+        for (int r = 0; r < TS; ++r) {
+            w.q[r] = ldr<IN_BF16>(qb, roff(r0 + r) + ch);
+            w.k[r] = ldr<IN_BF16>(kb, roff(r0 + r) + ch);
         }
     }
     if (tid < CS) w.beta = p.beta[rb + (size_t)min(tid, n - 1) * p.H];
@@ -157,8 +175,9 @@ __device__ __forceinline__ void build_chunk(Chunk<D>& c, const Raw<D>& w, float 
     constexpr int DH = D / 2;
     const int tid = threadIdx.x;
     const int n = w.n;
-    if (tid < D) {
-        const int ch = tid;
+    {
+        constexpr int TS = Raw<D>::TS;
+        const int ch = tid % D, sh = tid / D;
         float bc[CS];
         float s = 0.f;
 #pragma unroll
@@ -167,18 +186,22 @@ __device__ __forceinline__ void build_chunk(Chunk<D>& c, const Raw<D>& w, float 
             bc[r] = s;
         }
         const float last = bc[CS - 1], gl = fexp(last);
-        c.gam[ch] = gl;
+        if (sh == 0) c.gam[ch] = gl;
+        for_share<CS / TS>(sh, [&](auto shc) {
+            constexpr int R0 = TS * decltype(shc)::value;
 #pragma unroll
-        for (int r = 0; r < CS; ++r) {
-            const float q = r < n ? cvt<IN_BF16>(w.q[r], ch & 1) * scale : 0.f;
-            const float k = r < n ? cvt<IN_BF16>(w.k[r], ch & 1) : 0.f;
-            const float e = fexp(bc[r]), f = fexp(-bc[r]);  // exp(b), exp(-b), both within [e^-80, e^80]
-            c.Gam[r][ch] = e;
-            c.Qg[r][ch] = q * e;
-            c.Kg[r][ch] = k * e;
-            c.Kh[r][ch] = k * f;
-            c.Kb[r][ch] = k * (gl * f);  // exp(b_last - b)
-        }
+            for (int r = 0; r < TS; ++r) {
+                const int t = R0 + r;
+                const float q = t < n ? cvt<IN_BF16>(w.q[r], ch & 1) * scale : 0.f;
+                const float k = t < n ? cvt<IN_BF16>(w.k[r], ch & 1) : 0.f;
+                const float e = fexp(bc[t]), f = fexp(-bc[t]);  // exp(b), exp(-b), both within [e^-80, e^80]
+                c.Gam[t][ch] = e;
+                c.Qg[t][ch] = q * e;
+                c.Kg[t][ch] = k * e;
+                c.Kh[t][ch] = k * f;
+                c.Kb[t][ch] = k * (gl * f);  // exp(b_last - b)
+            }
+        });
     }
     if (tid < CS) c.beta[tid] = tid < n ? w.beta : 0.f;
 #pragma unroll
@@ -559,13 +582,13 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
     float s0r[SPT], dsr[SPT];
     fetch_state<D>(s0r, S0g, col0);
     fetch_state<D>(dsr, dSe, col0);
-    Raw<D> w;
+    Raw<D> w, w1;
     fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, i * CK, half, true);
+    fetch_chunk<D, IN_BF16, DO_BF16>(w1, p, b, h, i * CK + (nsub - 1) * CS, half, true);  // the second chunk (if any)
     put_state<D>(gr.P, s0r);
     if (nsub == 2) {  // Q = Diag(gam) S + Kb^T Tm (V - Kg S)
         build_chunk<D, IN_BF16, DO_BF16>(c, w, p.scale, true);
         __syncthreads();
-        fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, i * CK + CS, half, true);  // the second chunk
         chunk_triangles<D>(c);
         mgemm<CS, DH, D>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return gr.P[k][n]; },
                               [&](int m, int n, float v) { c.X[m][n] -= v; });
@@ -587,7 +610,10 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         const int c0 = i * CK + s * CS;
         float (*Sb)[DH + 1] = (nsub == 2 && s == 1) ? gr.Q : gr.P;
         float (*dSb)[DH + 1] = (nsub == 2 && s == 1) ? gr.P : gr.Q;
-        build_chunk<D, IN_BF16, DO_BF16>(c, w, p.scale, true);
+        if (nsub == 2 && s == 1)
+            build_chunk<D, IN_BF16, DO_BF16>(c, w1, p.scale, true);
+        else
+            build_chunk<D, IN_BF16, DO_BF16>(c, w, p.scale, true);
         __syncthreads();
         chunk_triangles<D>(c);
         // X = V - Kg S;  U = Tm X
@@ -726,8 +752,6 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             }
         }
         if (nsub == 2 && s == 1) {
-            // the first chunk's inputs again, for the next step (issued after this chunk's atomics)
-            fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, i * CK, half, true);
             // the gradient of the state between the two chunks, Diag(gam) dS + Qg^T dO - Kg^T dX,
             // into Q (the state S of this chunk, no longer read); then P gets the start state back
             __syncthreads();
