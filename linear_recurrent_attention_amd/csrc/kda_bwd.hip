@@ -630,10 +630,15 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
                                [&](int m, int n, float v) { c.dU[m][n] += v; });
         mgemm<CS, D, DH>([&](int m, int k) { return c.U[m][k]; }, [&](int k, int n) { return dSb[n][k]; },
                               [&](int m, int n, float v) { gr.G[m][n] = v; });
-        if (tid < D) {
+        {  // dgam: NT / D consecutive lanes per channel, each a slice of the columns, then a shuffle sum
+            constexpr int NP = NT / D, SL = DH / NP;
+            const int ch = tid / NP, pt = tid % NP;
             float a = 0.f;
-            for (int j = 0; j < DH; ++j) a = __builtin_fmaf(dSb[tid][j], Sb[tid][j], a);
-            gr.dgam[tid] = a;
+#pragma unroll
+            for (int j = 0; j < SL; ++j) a = __builtin_fmaf(dSb[ch][pt * SL + j], Sb[ch][pt * SL + j], a);
+#pragma unroll
+            for (int o = NP / 2; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
+            if (pt == 0) gr.dgam[ch] = a;
         }
         mgemm<CS, CS, DH>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return c.U[n][k]; },
                                [&](int m, int n, float v) { gr.dA[m][n] = n <= m ? v : 0.f; }, 7);
