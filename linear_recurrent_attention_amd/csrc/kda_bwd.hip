@@ -21,7 +21,8 @@
 //   1. the forward kernel with checkpoints: the state at every interval boundary (32 tokens on the
 //      matrix-core path, 16 on the float32 path), no output;
 //   2. kda_bwd_state_kernel, one workgroup per (sequence, value half), sequential in reverse over
-//      chunks: the state gradient dS at every interval boundary (its update needs no state);
+//      chunks: the state gradient dS at every interval boundary (its update needs no state); half
+//      the waves carry dS while the other half prepare the next chunk's factors;
 //   3. kda_bwd_chunk_kernel, one workgroup per (sequence, interval, value half), all in parallel:
 //      every input gradient of the interval, from the interval's start state and end gradient (a
 //      32-token interval first steps its state through the first 16-token chunk).
@@ -228,40 +229,6 @@ __device__ __forceinline__ float row_bcast(float x, int m) {
     }
 }
 
-// L, A on the matrix cores, then N = (I + Diag(beta) L)^{-1} and Tm = N Diag(beta) by forward
-// substitution, one matrix entry per lane.
-template <int D>
-__device__ __forceinline__ void chunk_triangles(Chunk<D>& c) {
-    const int tid = threadIdx.x;
-    // on waves 4-7: waves 0-1 may still be issuing the next chunk's loads (state pass)
-    mgemm<CS, CS, D>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
-                     [&](int m, int n, float v) { c.L[m][n] = n < m ? v : 0.f; }, 4);
-    mgemm<CS, CS, D>([&](int m, int k) { return c.Qg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
-                     [&](int m, int n, float v) { c.A[m][n] = n <= m ? v : 0.f; }, 5);
-    __syncthreads();
-    // column j of N per 16-lane row of lanes, lane i holding row i of -Diag(beta) L: with
-    // x_i = [i == j] + y_i the substitution is y = (-Diag(beta) L)(e_j + y), and at step m row m's
-    // final y_m is broadcast along the 16 lanes (DPP row_newbcast) for the rows below to take up
-    const int te = tid - (NT - CS * CS);  // the last CS*CS threads
-    if (te >= 0) {
-        const int j = te / CS, i = te % CS;
-        const float nb = -c.beta[i];
-        float nr[CS];
-#pragma unroll
-        for (int m = 0; m < CS; ++m) nr[m] = nb * c.L[i][m];
-        float y = nb * c.L[i][j];
-#pragma unroll
-        for (int m = 0; m < CS - 1; ++m) y = __builtin_fmaf(nr[m], row_bcast(y, m), y);
-        const float x = (i == j ? 1.f : 0.f) + y;
-        c.N[i][j] = x;
-        c.Tm[i][j] = x * c.beta[j];
-    }
-    __syncthreads();
-}
-
-// ------------------------------------------------------------------------------------------------
-// 2. state gradients at interval boundaries, sequential in reverse
-// ------------------------------------------------------------------------------------------------
 // out(m, n) = sum_k a(m, k) b(k, n) as in mgemm, on waves W0 .. W0 + NWU - 1 only (tile t on wave
 // W0 + t mod NWU); the other waves return at once.
 template <int M, int N, int K, int W0, int NWU, typename FA, typename FB, typename F>
@@ -282,6 +249,48 @@ __device__ __forceinline__ void mgemm_w(FA a, FB b, F f) {
     }
 }
 
+// L = tril(Kg Kh^T, -1) on wave W and A = tril(Qg Kh^T) on wave W + 1 (one 16 x 16 tile each).
+template <int D, int W, typename CT>
+__device__ __forceinline__ void gram_products(CT& c) {
+    mgemm_w<CS, CS, D, W, 1>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
+                             [&](int m, int n, float v) { c.L[m][n] = n < m ? v : 0.f; });
+    mgemm_w<CS, CS, D, W + 1, 1>([&](int m, int k) { return c.Qg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
+                                 [&](int m, int n, float v) { c.A[m][n] = n <= m ? v : 0.f; });
+}
+
+// N = (I + Diag(beta) L)^{-1} and Tm = N Diag(beta) by forward substitution on the last CS*CS
+// threads, one matrix entry per lane: column j of N per 16-lane row, lane i holding row i of
+// -Diag(beta) L.  With x_i = [i == j] + y_i the substitution is y = (-Diag(beta) L)(e_j + y); at
+// step m row m's final y_m is broadcast along the 16 lanes (DPP row_newbcast) for the rows below.
+template <typename CT>
+__device__ __forceinline__ void unit_inverse(CT& c) {
+    const int te = (int)threadIdx.x - (NT - CS * CS);
+    if (te < 0) return;
+    const int j = te / CS, i = te % CS;
+    const float nb = -c.beta[i];
+    float nr[CS];
+#pragma unroll
+    for (int m = 0; m < CS; ++m) nr[m] = nb * c.L[i][m];
+    float y = nb * c.L[i][j];
+#pragma unroll
+    for (int m = 0; m < CS - 1; ++m) y = __builtin_fmaf(nr[m], row_bcast(y, m), y);
+    const float x = (i == j ? 1.f : 0.f) + y;
+    c.N[i][j] = x;
+    c.Tm[i][j] = x * c.beta[j];
+}
+
+// L, A, then N and Tm, with the workgroup barriers between.
+template <int D>
+__device__ __forceinline__ void chunk_triangles(Chunk<D>& c) {
+    gram_products<D, 4>(c);
+    __syncthreads();
+    unit_inverse(c);
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------------------
+// 2. state gradients at interval boundaries, sequential in reverse
+// ------------------------------------------------------------------------------------------------
 // What the state pass keeps of a chunk (two of these: the chunk being processed and the next one).
 template <int D>
 struct alignas(16) SChunk {
@@ -396,25 +405,6 @@ __device__ __forceinline__ void build_s(SChunk<D>& c, const SRaw<D>& w, float sc
     }
 }
 
-// N = (I + Diag(beta) L)^{-1} and Tm = N Diag(beta) from the chunk's L, on the last CS*CS threads,
-// one matrix entry per lane (the substitution of chunk_triangles).
-template <typename CT>
-__device__ __forceinline__ void unit_inverse(CT& c) {
-    const int te = (int)threadIdx.x - (NT - CS * CS);
-    if (te < 0) return;
-    const int j = te / CS, i = te % CS;
-    const float nb = -c.beta[i];
-    float nr[CS];
-#pragma unroll
-    for (int m = 0; m < CS; ++m) nr[m] = nb * c.L[i][m];
-    float y = nb * c.L[i][j];
-#pragma unroll
-    for (int m = 0; m < CS - 1; ++m) y = __builtin_fmaf(nr[m], row_bcast(y, m), y);
-    const float x = (i == j ? 1.f : 0.f) + y;
-    c.N[i][j] = x;
-    c.Tm[i][j] = x * c.beta[j];
-}
-
 // One workgroup per (sequence, value half), reverse over 16-token chunks, as a two-stage pipeline:
 // waves 0-3 carry dS through chunk j (dU = Kb dS + A^T dO, dX = Tm^T dU), while waves 4-7 build
 // chunk j-1's factors, its Gram products L and A and its inverse, and fetch chunk j-3's inputs;
@@ -454,10 +444,7 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
     __syncthreads();
     {
         SChunk<D>& c = sc[(nch - 1) & 1];
-        mgemm_w<CS, CS, D, 4, 1>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
-                                 [&](int m, int n, float v) { c.L[m][n] = n < m ? v : 0.f; });
-        mgemm_w<CS, CS, D, 5, 1>([&](int m, int k) { return c.Qg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
-                                 [&](int m, int n, float v) { c.A[m][n] = n <= m ? v : 0.f; });
+        gram_products<D, 4>(c);
         __syncthreads();
         unit_inverse(c);
         __syncthreads();
@@ -479,12 +466,7 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
         // dX = Tm^T dU  |  the next chunk's L and A
         mgemm_w<CS, DH, CS, 0, 4>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return dU[k][n]; },
                                   [&](int m, int n, float v) { dX[m][n] = v; });
-        if (next) {
-            mgemm_w<CS, CS, D, 4, 1>([&](int m, int k) { return cn.Kg[m][k]; }, [&](int k, int n) { return cn.Kh[n][k]; },
-                                     [&](int m, int n, float v) { cn.L[m][n] = n < m ? v : 0.f; });
-            mgemm_w<CS, CS, D, 5, 1>([&](int m, int k) { return cn.Qg[m][k]; }, [&](int k, int n) { return cn.Kh[n][k]; },
-                                     [&](int m, int n, float v) { cn.A[m][n] = n <= m ? v : 0.f; });
-        }
+        if (next) gram_products<D, 4>(cn);
         __syncthreads();
         // the next inverse (waves 4-7), then on all waves
         // dS <- Diag(gam) dS + Qg^T dO - Kg^T dX   (each entry read and written by its own thread)
