@@ -279,15 +279,6 @@ __device__ __forceinline__ void unit_inverse(CT& c) {
     c.Tm[i][j] = x * c.beta[j];
 }
 
-// L, A, then N and Tm, with the workgroup barriers between.
-template <int D>
-__device__ __forceinline__ void chunk_triangles(Chunk<D>& c) {
-    gram_products<D, 4>(c);
-    __syncthreads();
-    unit_inverse(c);
-    __syncthreads();
-}
-
 // ------------------------------------------------------------------------------------------------
 // 2. state gradients at interval boundaries, sequential in reverse
 // ------------------------------------------------------------------------------------------------
@@ -509,6 +500,47 @@ struct alignas(16) Grad {
     float dbeta[CS];
 };
 
+// Order among the lanes of one wave: its LDS operations run in issue order, so keeping the compiler
+// from moving them across this point is enough.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// On one wave (lane 0..63, the last wave of the workgroup): dN = dTm Diag(beta);
+// dbeta = colsum(N * dTm);  dM = -N^T dN N^T;  dbeta += rowsum(dM * L);  dL = tril(Diag(beta) dM, -1),
+// kept in dM.
+template <int D>
+__device__ __forceinline__ void dl_chain(Chunk<D>& c, Grad<D>& gr, int lane) {
+    constexpr int W = NT / 64 - 1;
+#pragma unroll
+    for (int e = lane; e < CS * CS; e += 64) gr.dN[e / CS][e % CS] = gr.dTm[e / CS][e % CS] * c.beta[e % CS];
+    if (lane < CS) {
+        float a = 0.f;
+        for (int r = 0; r < CS; ++r) a = __builtin_fmaf(c.N[r][lane], gr.dTm[r][lane], a);
+        gr.dbeta[lane] = a;
+    }
+    wave_sync();
+    mgemm_w<CS, CS, CS, W, 1>([&](int m, int k) { return c.N[k][m]; }, [&](int k, int n) { return gr.dN[k][n]; },
+                              [&](int m, int n, float v) { gr.T1[m][n] = v; });
+    wave_sync();
+    mgemm_w<CS, CS, CS, W, 1>([&](int m, int k) { return gr.T1[m][k]; }, [&](int k, int n) { return c.N[n][k]; },
+                              [&](int m, int n, float v) { gr.dM[m][n] = -v; });
+    wave_sync();
+    if (lane < CS) {
+        float a = 0.f;
+        for (int q = 0; q < CS; ++q) a = __builtin_fmaf(gr.dM[lane][q], c.L[lane][q], a);
+        gr.dbeta[lane] += a;
+    }
+    wave_sync();
+#pragma unroll
+    for (int e = lane; e < CS * CS; e += 64) {
+        const int r = e / CS, q = e % CS;
+        gr.dM[r][q] = q < r ? c.beta[r] * gr.dM[r][q] : 0.f;
+    }
+}
+
 // This thread's entries e = tid + NT*k of the value-half tile src[r][col0 + j] (r = e / DH,
 // j = e % DH) of a [D][D] float32 matrix in global memory (NULL = zeros), into registers; put_state
 // writes them to an LDS tile.
@@ -571,9 +603,12 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
     if (nsub == 2) {  // Q = Diag(gam) S + Kb^T Tm (V - Kg S)
         build_chunk<D, IN_BF16, DO_BF16>(c, w, p.scale, true);
         __syncthreads();
-        chunk_triangles<D>(c);
-        mgemm<CS, DH, D>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return gr.P[k][n]; },
-                              [&](int m, int n, float v) { c.X[m][n] -= v; });
+        // L and A (waves 4, 5) beside X = V - Kg S (waves 0-3), then the inverse
+        gram_products<D, 4>(c);
+        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return gr.P[k][n]; },
+                                 [&](int m, int n, float v) { c.X[m][n] -= v; });
+        __syncthreads();
+        unit_inverse(c);
         __syncthreads();
         mgemm<CS, DH, CS>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
                                [&](int m, int n, float v) { c.U[m][n] = v; });
@@ -597,17 +632,20 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         else
             build_chunk<D, IN_BF16, DO_BF16>(c, w, p.scale, true);
         __syncthreads();
-        chunk_triangles<D>(c);
-        // X = V - Kg S;  U = Tm X
-        mgemm<CS, DH, D>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return Sb[k][n]; },
-                              [&](int m, int n, float v) { c.X[m][n] -= v; });
+        // L and A (waves 4, 5) beside X = V - Kg S (waves 0-3); the inverse (waves 4-7) beside Kb dS
+        gram_products<D, 4>(c);
+        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return Sb[k][n]; },
+                                 [&](int m, int n, float v) { c.X[m][n] -= v; });
         __syncthreads();
+        unit_inverse(c);
+        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dSb[k][n]; },
+                                 [&](int m, int n, float v) { c.dU[m][n] = v; });
+        __syncthreads();
+        // U = Tm X
         mgemm<CS, DH, CS>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
                                [&](int m, int n, float v) { c.U[m][n] = v; });
         __syncthreads();
-        // dU = Kb dS + A^T dO;  dKb = U dS^T;  dgam = rowsum(dS * S);  dA = tril(dO U^T)
-        mgemm<CS, DH, D>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dSb[k][n]; },
-                              [&](int m, int n, float v) { c.dU[m][n] = v; });
+        // dU += A^T dO;  dKb = U dS^T;  dgam = rowsum(dS * S);  dA = tril(dO U^T)
         mgemm<CS, DH, CS>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
                                [&](int m, int n, float v) { c.dU[m][n] += v; });
         mgemm<CS, D, DH>([&](int m, int k) { return c.U[m][k]; }, [&](int k, int n) { return dSb[n][k]; },
@@ -645,40 +683,13 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         mgemm<CS, DH, CS>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
                                [&](int m, int n, float v) { c.dX[m][n] = v; });
         __syncthreads();
-        // dN = dTm Diag(beta);  dbeta = colsum(N * dTm);  dM = -N^T dN N^T;  dbeta += rowsum(dM * L);
-        // dL = tril(Diag(beta) dM, -1) (kept in dM)
-        if (tid < CS * CS) {
-            const int r = tid / CS, q = tid % CS;
-            gr.dN[r][q] = gr.dTm[r][q] * c.beta[q];
-        }
-        if (tid < CS) {
-            float a = 0.f;
-            for (int r = 0; r < CS; ++r) a = __builtin_fmaf(c.N[r][tid], gr.dTm[r][tid], a);
-            gr.dbeta[tid] = a;
-        }
-        __syncthreads();
-        mgemm<CS, CS, CS>([&](int m, int k) { return c.N[k][m]; }, [&](int k, int n) { return gr.dN[k][n]; },
-                               [&](int m, int n, float v) { gr.T1[m][n] = v; });
-        __syncthreads();
-        mgemm<CS, CS, CS>([&](int m, int k) { return gr.T1[m][k]; }, [&](int k, int n) { return c.N[n][k]; },
-                               [&](int m, int n, float v) { gr.dM[m][n] = -v; });
-        __syncthreads();
-        if (tid < CS) {
-            float a = 0.f;
-            for (int q = 0; q < CS; ++q) a = __builtin_fmaf(gr.dM[tid][q], c.L[tid][q], a);
-            gr.dbeta[tid] += a;
-        }
-        __syncthreads();
-        if (tid < CS * CS) {
-            const int r = tid / CS, q = tid % CS;
-            gr.dM[r][q] = q < r ? c.beta[r] * gr.dM[r][q] : 0.f;  // now dL
-        }
-        __syncthreads();
-        // dQg = dO S^T + dA Kh  -> dq = dQg scale Gamma (Qg holds the scale), db += dQg Qg
-        mgemm<CS, D, DH>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return Sb[n][k]; },
-                              [&](int m, int n, float v) { gr.G[m][n] = v; });
-        mgemm<CS, D, CS>([&](int m, int k) { return gr.dA[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
-                              [&](int m, int n, float v) { gr.G[m][n] += v; });
+        // the dTm -> dL chain on wave 7 alone, beside dQg = dO S^T + dA Kh on waves 0-3 (then
+        // dq = dQg scale Gamma, Qg holding the scale, and db += dQg Qg)
+        if (tid >= NT - 64) dl_chain(c, gr, tid & 63);
+        mgemm_w<CS, D, DH, 0, 4>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return Sb[n][k]; },
+                                 [&](int m, int n, float v) { gr.G[m][n] = v; });
+        mgemm_w<CS, D, CS, 0, 4>([&](int m, int k) { return gr.dA[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
+                                 [&](int m, int n, float v) { gr.G[m][n] += v; });
         __syncthreads();
         const int n_ok = min(CS, p.T - c0);
         auto grow = [&](int r) { return ((size_t)b * p.T + c0 + r) * p.H + h; };
