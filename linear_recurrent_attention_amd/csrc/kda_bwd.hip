@@ -54,43 +54,71 @@ __device__ __forceinline__ float cvt(uint32_t x, bool odd) {
     return __uint_as_float(BF16 ? (odd ? x & 0xffff0000u : x << 16) : x);
 }
 
+// Four consecutive entries of an LDS tile: along row r from column c (16-byte aligned: c and the row
+// pitch multiples of 4), or down column c from row r.
+template <int W>
+__device__ __forceinline__ f32x4 row4(const float (*t)[W], int r, int c) {
+    static_assert(W % 4 == 0, "row pitch");
+    return *reinterpret_cast<const f32x4*>(&t[r][c]);
+}
+template <int W>
+__device__ __forceinline__ f32x4 col4(const float (*t)[W], int r, int c) {
+    return f32x4{t[r][c], t[r + 1][c], t[r + 2][c], t[r + 3][c]};
+}
+
+// acc += sum_k A(m, k) B(k, n) for this lane's row m and column n (see mgemm for the index order).
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ void tile_product(FA a, FB b, int m, int n, int g, f32x4& acc) {
+#pragma unroll
+    for (int q = 0; q < K / 16; ++q) {
+        const int k = 16 * q + 4 * g;
+        const f32x4 av = a(m, k), bv = b(k, n);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bv[r], acc, 0, 0, 0);
+    }
+}
+
 // out(m, n) = sum_k a(m, k) b(k, n) for m < M, n < N on the matrix cores: float32
 // v_mfma_f32_16x16x4_f32 (exact float32 products, float32 accumulation), one 16 x 16 output tile per
-// wave at a time; a and b are accessors (LDS), f(m, n, v) receives the result.  Operand layout of that
-// instruction: A(m, k) in lane m + 16 k, B(k, n) in lane n + 16 k, result (4 g + r, n) in lane
-// n + 16 g, register r.
+// wave at a time; f(m, n, v) receives the result.  Operand layout of that instruction: A(m, k_g) in
+// lane m + 16 g, B(k_g, n) in lane n + 16 g, result (4 g + r, n) in lane n + 16 g, register r; one
+// instruction adds the four products of lane groups g = 0..3.  Each lane group takes the contraction
+// indices 16 q + 4 g + r (q = 0 .. K/16 - 1, r = 0..3), four consecutive ones per 16-index block, so
+// that a(m, k) and b(k, n) return four consecutive indices k..k+3 at once (f32x4): one 16-byte LDS
+// read where the tile stores them contiguously (row4), four reads one row apart otherwise (col4).
 // Tile t goes to wave (first_wave + t) mod 8, so that small products issued back to back without a
 // barrier between them can run on different waves.
 template <int M, int N, int K, typename FA, typename FB, typename F>
 __device__ __forceinline__ void mgemm(FA a, FB b, F f, int first_wave = 0) {
-    static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "tile shape");
+    static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0, "tile shape");
     constexpr int TN = N / 16, NW = NT / 64;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, g = lane >> 4;
     for (int tile = (wave + NW - first_wave) % NW; tile < (M / 16) * TN; tile += NW) {
         const int m0 = (tile / TN) * 16, n0 = (tile % TN) * 16;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int k = 0; k < K; k += 4)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(m0 + l16, k + g), b(k + g, n0 + l16), acc, 0, 0, 0);
+        tile_product<K>(a, b, m0 + l16, n0 + l16, g, acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) f(m0 + 4 * g + r, n0 + l16, acc[r]);
     }
 }
 
 // Factors of one chunk, its beta, and the value-half columns of dO (and V in X when wanted).
-// Row pitch of the [CS][D] key-side tiles: D + 20 floats (20 mod 64 banks), so that the matrix-core
-// operand reads hit distinct banks when a lane group walks rows (l16) and at most two lanes share a
-// bank when it walks columns.
-constexpr int KP = 20;
+// Row pitches (floats): key-side [CS][D] tiles D + KP, value-half tiles DH + VP, chunk-square tiles
+// CS + SP, all multiples of 4 for 16-byte reads.  Measured on gfx950 with eight waves per CU, 16-byte
+// reads of 16 rows at one column block run at ~5.3 clocks per instruction when the pitch is 8 mod 64
+// floats (~9 at 4 mod 64), and column reads of rows 16 q + 4 g + r at ~4.4 (~3 at 4 mod 64).
+constexpr int KP = 8;
+constexpr int VP = 8;
+constexpr int SP = 4;
 
 template <int D>
 struct alignas(16) Chunk {
     static constexpr int DH = D / 2;
     float Qg[CS][D + KP], Kg[CS][D + KP], Kh[CS][D + KP], Kb[CS][D + KP], Gam[CS][D + KP];
     float gam[D];
-    float X[CS][DH + 1], U[CS][DH + 1], dO[CS][DH + 1], dU[CS][DH + 1], dX[CS][DH + 1];
-    float L[CS][CS + 1], A[CS][CS + 1], N[CS][CS + 1], Tm[CS][CS + 1];
+    float X[CS][DH + VP], U[CS][DH + VP], dO[CS][DH + VP], dU[CS][DH + VP], dX[CS][DH + VP];
+    float L[CS][CS + SP], A[CS][CS + SP], N[CS][CS + SP], Tm[CS][CS + SP];
     float beta[CS];
 };
 
@@ -233,7 +261,7 @@ __device__ __forceinline__ float row_bcast(float x, int m) {
 // W0 + t mod NWU); the other waves return at once.
 template <int M, int N, int K, int W0, int NWU, typename FA, typename FB, typename F>
 __device__ __forceinline__ void mgemm_w(FA a, FB b, F f) {
-    static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "tile shape");
+    static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0, "tile shape");
     constexpr int TN = N / 16;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if (wave < W0 || wave >= W0 + NWU) return;
@@ -241,9 +269,7 @@ __device__ __forceinline__ void mgemm_w(FA a, FB b, F f) {
     for (int tile = wave - W0; tile < (M / 16) * TN; tile += NWU) {
         const int m0 = (tile / TN) * 16, n0 = (tile % TN) * 16;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int k = 0; k < K; k += 4)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(m0 + l16, k + g), b(k + g, n0 + l16), acc, 0, 0, 0);
+        tile_product<K>(a, b, m0 + l16, n0 + l16, g, acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) f(m0 + 4 * g + r, n0 + l16, acc[r]);
     }
@@ -252,9 +278,9 @@ __device__ __forceinline__ void mgemm_w(FA a, FB b, F f) {
 // L = tril(Kg Kh^T, -1) on wave W and A = tril(Qg Kh^T) on wave W + 1 (one 16 x 16 tile each).
 template <int D, int W, typename CT>
 __device__ __forceinline__ void gram_products(CT& c) {
-    mgemm_w<CS, CS, D, W, 1>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
+    mgemm_w<CS, CS, D, W, 1>([&](int m, int k) { return row4(c.Kg, m, k); }, [&](int k, int n) { return row4(c.Kh, n, k); },
                              [&](int m, int n, float v) { c.L[m][n] = n < m ? v : 0.f; });
-    mgemm_w<CS, CS, D, W + 1, 1>([&](int m, int k) { return c.Qg[m][k]; }, [&](int k, int n) { return c.Kh[n][k]; },
+    mgemm_w<CS, CS, D, W + 1, 1>([&](int m, int k) { return row4(c.Qg, m, k); }, [&](int k, int n) { return row4(c.Kh, n, k); },
                                  [&](int m, int n, float v) { c.A[m][n] = n <= m ? v : 0.f; });
 }
 
@@ -288,8 +314,8 @@ struct alignas(16) SChunk {
     static constexpr int DH = D / 2;
     float Qg[CS][D + KP], Kg[CS][D + KP], Kh[CS][D + KP], Kb[CS][D + KP];
     float gam[D];
-    float dO[CS][DH + 1];
-    float L[CS][CS + 1], A[CS][CS + 1], N[CS][CS + 1], Tm[CS][CS + 1];
+    float dO[CS][DH + VP];
+    float L[CS][CS + SP], A[CS][CS + SP], N[CS][CS + SP], Tm[CS][CS + SP];
     float beta[CS];
 };
 
@@ -405,8 +431,8 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
     constexpr int DH = D / 2;
     static_assert(NT - CS * CS >= NTH && D <= NTH && CS <= NTH, "the factor waves own the inverse and the build");
     __shared__ SChunk<D> sc[2];
-    __shared__ float dU[CS][DH + 1], dX[CS][DH + 1];
-    __shared__ float dS[D][DH + 1];
+    __shared__ __attribute__((aligned(16))) float dU[CS][DH + VP], dX[CS][DH + VP];
+    __shared__ __attribute__((aligned(16))) float dS[D][DH + VP];
     const int tid = threadIdx.x;
     const bool chain = tid < NTH;  // waves 0-3
     const int bh = blockIdx.x >> 1, half = blockIdx.x & 1;
@@ -445,9 +471,9 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
         SChunk<D>& cn = sc[(cj - 1) & 1];  // the next one (chunk cj - 1)
         const bool next = cj >= 1;
         // dU = Kb dS + A^T dO  |  the next chunk's factors; its successor's inputs
-        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dS[k][n]; },
+        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return row4(c.Kb, m, k); }, [&](int k, int n) { return col4(dS, k, n); },
                                  [&](int m, int n, float v) { dU[m][n] = v; });
-        mgemm_w<CS, DH, CS, 0, 4>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+        mgemm_w<CS, DH, CS, 0, 4>([&](int m, int k) { return col4(c.A, k, m); }, [&](int k, int n) { return col4(c.dO, k, n); },
                                   [&](int m, int n, float v) { dU[m][n] += v; });
         if (!chain && next) {
             build_s<D, IN_BF16, DO_BF16>(cn, w, p.scale);
@@ -455,16 +481,16 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
         }
         __syncthreads();
         // dX = Tm^T dU  |  the next chunk's L and A
-        mgemm_w<CS, DH, CS, 0, 4>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return dU[k][n]; },
+        mgemm_w<CS, DH, CS, 0, 4>([&](int m, int k) { return col4(c.Tm, k, m); }, [&](int k, int n) { return col4(dU, k, n); },
                                   [&](int m, int n, float v) { dX[m][n] = v; });
         if (next) gram_products<D, 4>(cn);
         __syncthreads();
         // the next inverse (waves 4-7), then on all waves
         // dS <- Diag(gam) dS + Qg^T dO - Kg^T dX   (each entry read and written by its own thread)
         if (next) unit_inverse(cn);
-        mgemm_w<D, DH, CS, 0, NT / 64>([&](int m, int k) { return c.Qg[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+        mgemm_w<D, DH, CS, 0, NT / 64>([&](int m, int k) { return col4(c.Qg, k, m); }, [&](int k, int n) { return col4(c.dO, k, n); },
                                        [&](int m, int n, float v) { dS[m][n] = __builtin_fmaf(c.gam[m], dS[m][n], v); });
-        mgemm_w<D, DH, CS, 0, NT / 64>([&](int m, int k) { return c.Kg[k][m]; }, [&](int k, int n) { return dX[k][n]; },
+        mgemm_w<D, DH, CS, 0, NT / 64>([&](int m, int k) { return col4(c.Kg, k, m); }, [&](int k, int n) { return col4(dX, k, n); },
                                        [&](int m, int n, float v) { dS[m][n] -= v; });
         __syncthreads();
         if (cj % SPI == 0 && cj > 0) {  // the start of interval cj / SPI: the gradient of the state there
@@ -493,9 +519,9 @@ template <int D>
 struct alignas(16) Grad {
     static constexpr int DH = D / 2;
     float G[CS][D + KP];      // one key-side gradient at a time (dKb, dQg, dKg, dKh), then db
-    float P[D][DH + 1];       // state / state-gradient tiles of the current chunk (this value half):
-    float Q[D][DH + 1];       // which is which depends on the chunk, see the kernel
-    float dA[CS][CS + 1], dTm[CS][CS + 1], dN[CS][CS + 1], dM[CS][CS + 1], T1[CS][CS + 1];
+    float P[D][DH + VP];       // state / state-gradient tiles of the current chunk (this value half):
+    float Q[D][DH + VP];       // which is which depends on the chunk, see the kernel
+    float dA[CS][CS + SP], dTm[CS][CS + SP], dN[CS][CS + SP], dM[CS][CS + SP], T1[CS][CS + SP];
     float dgam[D], dlast[D];
     float dbeta[CS];
 };
@@ -522,10 +548,10 @@ __device__ __forceinline__ void dl_chain(Chunk<D>& c, Grad<D>& gr, int lane) {
         gr.dbeta[lane] = a;
     }
     wave_sync();
-    mgemm_w<CS, CS, CS, W, 1>([&](int m, int k) { return c.N[k][m]; }, [&](int k, int n) { return gr.dN[k][n]; },
+    mgemm_w<CS, CS, CS, W, 1>([&](int m, int k) { return col4(c.N, k, m); }, [&](int k, int n) { return col4(gr.dN, k, n); },
                               [&](int m, int n, float v) { gr.T1[m][n] = v; });
     wave_sync();
-    mgemm_w<CS, CS, CS, W, 1>([&](int m, int k) { return gr.T1[m][k]; }, [&](int k, int n) { return c.N[n][k]; },
+    mgemm_w<CS, CS, CS, W, 1>([&](int m, int k) { return row4(gr.T1, m, k); }, [&](int k, int n) { return row4(c.N, n, k); },
                               [&](int m, int n, float v) { gr.dM[m][n] = -v; });
     wave_sync();
     if (lane < CS) {
@@ -560,7 +586,7 @@ __device__ __forceinline__ void fetch_state(float* v, const float* src, int col0
     }
 }
 template <int D>
-__device__ __forceinline__ void put_state(float (*dst)[D / 2 + 1], const float* v) {
+__device__ __forceinline__ void put_state(float (*dst)[D / 2 + VP], const float* v) {
     constexpr int DH = D / 2;
 #pragma unroll
     for (int k = 0; k < D * DH / NT; ++k) {
@@ -605,15 +631,15 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         __syncthreads();
         // L and A (waves 4, 5) beside X = V - Kg S (waves 0-3), then the inverse
         gram_products<D, 4>(c);
-        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return gr.P[k][n]; },
+        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return row4(c.Kg, m, k); }, [&](int k, int n) { return col4(gr.P, k, n); },
                                  [&](int m, int n, float v) { c.X[m][n] -= v; });
         __syncthreads();
         unit_inverse(c);
         __syncthreads();
-        mgemm<CS, DH, CS>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
+        mgemm<CS, DH, CS>([&](int m, int k) { return row4(c.Tm, m, k); }, [&](int k, int n) { return col4(c.X, k, n); },
                                [&](int m, int n, float v) { c.U[m][n] = v; });
         __syncthreads();
-        mgemm<D, DH, CS>([&](int m, int k) { return c.Kb[k][m]; }, [&](int k, int n) { return c.U[k][n]; },
+        mgemm<D, DH, CS>([&](int m, int k) { return col4(c.Kb, k, m); }, [&](int k, int n) { return col4(c.U, k, n); },
                               [&](int m, int n, float v) { gr.Q[m][n] = __builtin_fmaf(c.gam[m], gr.P[m][n], v); });
         __syncthreads();
         put_state<D>(gr.P, dsr);
@@ -625,8 +651,8 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
     // holding the prefetched inputs are live only where they are needed)
     auto step = [&](const int s) {
         const int c0 = i * CK + s * CS;
-        float (*Sb)[DH + 1] = (nsub == 2 && s == 1) ? gr.Q : gr.P;
-        float (*dSb)[DH + 1] = (nsub == 2 && s == 1) ? gr.P : gr.Q;
+        float (*Sb)[DH + VP] = (nsub == 2 && s == 1) ? gr.Q : gr.P;
+        float (*dSb)[DH + VP] = (nsub == 2 && s == 1) ? gr.P : gr.Q;
         if (nsub == 2 && s == 1)
             build_chunk<D, IN_BF16, DO_BF16>(c, w1, p.scale, true);
         else
@@ -634,21 +660,21 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         __syncthreads();
         // L and A (waves 4, 5) beside X = V - Kg S (waves 0-3); the inverse (waves 4-7) beside Kb dS
         gram_products<D, 4>(c);
-        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return c.Kg[m][k]; }, [&](int k, int n) { return Sb[k][n]; },
+        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return row4(c.Kg, m, k); }, [&](int k, int n) { return col4(Sb, k, n); },
                                  [&](int m, int n, float v) { c.X[m][n] -= v; });
         __syncthreads();
         unit_inverse(c);
-        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return c.Kb[m][k]; }, [&](int k, int n) { return dSb[k][n]; },
+        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return row4(c.Kb, m, k); }, [&](int k, int n) { return col4(dSb, k, n); },
                                  [&](int m, int n, float v) { c.dU[m][n] = v; });
         __syncthreads();
         // U = Tm X
-        mgemm<CS, DH, CS>([&](int m, int k) { return c.Tm[m][k]; }, [&](int k, int n) { return c.X[k][n]; },
+        mgemm<CS, DH, CS>([&](int m, int k) { return row4(c.Tm, m, k); }, [&](int k, int n) { return col4(c.X, k, n); },
                                [&](int m, int n, float v) { c.U[m][n] = v; });
         __syncthreads();
         // dU += A^T dO;  dKb = U dS^T;  dgam = rowsum(dS * S);  dA = tril(dO U^T)
-        mgemm<CS, DH, CS>([&](int m, int k) { return c.A[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+        mgemm<CS, DH, CS>([&](int m, int k) { return col4(c.A, k, m); }, [&](int k, int n) { return col4(c.dO, k, n); },
                                [&](int m, int n, float v) { c.dU[m][n] += v; });
-        mgemm<CS, D, DH>([&](int m, int k) { return c.U[m][k]; }, [&](int k, int n) { return dSb[n][k]; },
+        mgemm<CS, D, DH>([&](int m, int k) { return row4(c.U, m, k); }, [&](int k, int n) { return row4(dSb, n, k); },
                               [&](int m, int n, float v) { gr.G[m][n] = v; });
         {  // dgam: NT / D consecutive lanes per channel, each a slice of the columns, then a shuffle sum
             constexpr int NP = NT / D, SL = DH / NP;
@@ -660,7 +686,7 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             for (int o = NP / 2; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
             if (pt == 0) gr.dgam[ch] = a;
         }
-        mgemm<CS, CS, DH>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return c.U[n][k]; },
+        mgemm<CS, CS, DH>([&](int m, int k) { return row4(c.dO, m, k); }, [&](int k, int n) { return row4(c.U, n, k); },
                                [&](int m, int n, float v) { gr.dA[m][n] = n <= m ? v : 0.f; }, 7);
         __syncthreads();
         // fold dKb: dk = dKb exp(b_last - b);  db = -dKb Kb;  last row: sum_t dKb Kb + dgam gam
@@ -678,17 +704,17 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             gr.dlast[tid] = a;
         }
         // dTm = dU X^T;  dX = Tm^T dU  (dv)
-        mgemm<CS, CS, DH>([&](int m, int k) { return c.dU[m][k]; }, [&](int k, int n) { return c.X[n][k]; },
+        mgemm<CS, CS, DH>([&](int m, int k) { return row4(c.dU, m, k); }, [&](int k, int n) { return row4(c.X, n, k); },
                                [&](int m, int n, float v) { gr.dTm[m][n] = v; }, 4);
-        mgemm<CS, DH, CS>([&](int m, int k) { return c.Tm[k][m]; }, [&](int k, int n) { return c.dU[k][n]; },
+        mgemm<CS, DH, CS>([&](int m, int k) { return col4(c.Tm, k, m); }, [&](int k, int n) { return col4(c.dU, k, n); },
                                [&](int m, int n, float v) { c.dX[m][n] = v; });
         __syncthreads();
         // the dTm -> dL chain on wave 7 alone, beside dQg = dO S^T + dA Kh on waves 0-3 (then
         // dq = dQg scale Gamma, Qg holding the scale, and db += dQg Qg)
         if (tid >= NT - 64) dl_chain(c, gr, tid & 63);
-        mgemm_w<CS, D, DH, 0, 4>([&](int m, int k) { return c.dO[m][k]; }, [&](int k, int n) { return Sb[n][k]; },
+        mgemm_w<CS, D, DH, 0, 4>([&](int m, int k) { return row4(c.dO, m, k); }, [&](int k, int n) { return row4(Sb, n, k); },
                                  [&](int m, int n, float v) { gr.G[m][n] = v; });
-        mgemm_w<CS, D, CS, 0, 4>([&](int m, int k) { return gr.dA[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
+        mgemm_w<CS, D, CS, 0, 4>([&](int m, int k) { return row4(gr.dA, m, k); }, [&](int k, int n) { return col4(c.Kh, k, n); },
                                  [&](int m, int n, float v) { gr.G[m][n] += v; });
         __syncthreads();
         const int n_ok = min(CS, p.T - c0);
@@ -702,9 +728,9 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         }
         __syncthreads();
         // dKg = -dX S^T + dL Kh -> dk += dKg Gamma, db += dKg Kg
-        mgemm<CS, D, DH>([&](int m, int k) { return c.dX[m][k]; }, [&](int k, int n) { return Sb[n][k]; },
+        mgemm<CS, D, DH>([&](int m, int k) { return row4(c.dX, m, k); }, [&](int k, int n) { return row4(Sb, n, k); },
                               [&](int m, int n, float v) { gr.G[m][n] = -v; });
-        mgemm<CS, D, CS>([&](int m, int k) { return gr.dM[m][k]; }, [&](int k, int n) { return c.Kh[k][n]; },
+        mgemm<CS, D, CS>([&](int m, int k) { return row4(gr.dM, m, k); }, [&](int k, int n) { return col4(c.Kh, k, n); },
                               [&](int m, int n, float v) { gr.G[m][n] += v; });
         __syncthreads();
 #pragma unroll
@@ -716,9 +742,9 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
         }
         __syncthreads();
         // dKh = dL^T Kg + dA^T Qg -> dk += dKh / Gamma, db -= dKh Kh
-        mgemm<CS, D, CS>([&](int m, int k) { return gr.dM[k][m]; }, [&](int k, int n) { return c.Kg[k][n]; },
+        mgemm<CS, D, CS>([&](int m, int k) { return col4(gr.dM, k, m); }, [&](int k, int n) { return col4(c.Kg, k, n); },
                               [&](int m, int n, float v) { gr.G[m][n] = v; });
-        mgemm<CS, D, CS>([&](int m, int k) { return gr.dA[k][m]; }, [&](int k, int n) { return c.Qg[k][n]; },
+        mgemm<CS, D, CS>([&](int m, int k) { return col4(gr.dA, k, m); }, [&](int k, int n) { return col4(c.Qg, k, n); },
                               [&](int m, int n, float v) { gr.G[m][n] += v; });
         __syncthreads();
 #pragma unroll
@@ -753,9 +779,9 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             // the gradient of the state between the two chunks, Diag(gam) dS + Qg^T dO - Kg^T dX,
             // into Q (the state S of this chunk, no longer read); then P gets the start state back
             __syncthreads();
-            mgemm<D, DH, CS>([&](int m, int k) { return c.Qg[k][m]; }, [&](int k, int n) { return c.dO[k][n]; },
+            mgemm<D, DH, CS>([&](int m, int k) { return col4(c.Qg, k, m); }, [&](int k, int n) { return col4(c.dO, k, n); },
                                   [&](int m, int n, float v) { gr.Q[m][n] = __builtin_fmaf(c.gam[m], gr.P[m][n], v); });
-            mgemm<D, DH, CS>([&](int m, int k) { return c.Kg[k][m]; }, [&](int k, int n) { return c.dX[k][n]; },
+            mgemm<D, DH, CS>([&](int m, int k) { return col4(c.Kg, k, m); }, [&](int k, int n) { return col4(c.dX, k, n); },
                                   [&](int m, int n, float v) { gr.Q[m][n] -= v; });
             __syncthreads();
             put_state<D>(gr.P, s0r);
