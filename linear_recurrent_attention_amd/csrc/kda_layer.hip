@@ -65,6 +65,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // c = h*D + 2l.  The short convolution's window (the 3 previous pre-conv rows of q and k) is carried
 // in registers along the tokens, so each projection row is read once.
 constexpr int PRO_TOK = 32;
+constexpr int PRO_U = 8;  // tokens whose rows are read together
 
 __device__ __forceinline__ float silu(float x) { return x * sigmoidf_(x); }
 
@@ -104,30 +105,43 @@ __global__ void __launch_bounds__(256) prologue_kernel(ProParams p) {
     }
     const float2 ba = *reinterpret_cast<const float2*>(p.b_alpha + c);
     const float ea = fexp(p.A[h]);
-    for (int t = t0; t < t1; ++t) {
-        const size_t rc = ((size_t)b * p.T + t) * p.HD + c;
-        const size_t row = (size_t)b * p.T + t;
-        const float2 cq = *reinterpret_cast<const float2*>(p.pq + rc);
-        const float2 ck = *reinterpret_cast<const float2*>(p.pk + rc);
-        const float2 z = *reinterpret_cast<const float2*>(p.pz + rc);
-        float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f;
+    // PRO_U tokens at a time: all their projection rows are read first (rows past t1 read row t1 - 1
+    // and are not used), so that each wave keeps 3 * PRO_U reads in flight instead of 3
+    for (int t = t0; t < t1; t += PRO_U) {
+        float2 cq[PRO_U], ck[PRO_U], z[PRO_U];
+        float bl[PRO_U];
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            q0 += wq[0][j] * xq[j].x; q1 += wq[1][j] * xq[j].y;
-            k0 += wk[0][j] * xk[j].x; k1 += wk[1][j] * xk[j].y;
+        for (int u = 0; u < PRO_U; ++u) {
+            const size_t row = (size_t)b * p.T + min(t + u, t1 - 1);
+            cq[u] = *reinterpret_cast<const float2*>(p.pq + row * p.HD + c);
+            ck[u] = *reinterpret_cast<const float2*>(p.pk + row * p.HD + c);
+            z[u] = *reinterpret_cast<const float2*>(p.pz + row * p.HD + c);
+            bl[u] = p.pbeta[row * p.H + h];
         }
-        q0 += wq[0][3] * cq.x; q1 += wq[1][3] * cq.y;
-        k0 += wk[0][3] * ck.x; k1 += wk[1][3] * ck.y;
-        xq[0] = xq[1]; xq[1] = xq[2]; xq[2] = cq;
-        xk[0] = xk[1]; xk[1] = xk[2]; xk[2] = ck;
-        q0 = silu(q0); q1 = silu(q1); k0 = silu(k0); k1 = silu(k1);
-        const float qn = rsqrtf(wave_sum(q0 * q0 + q1 * q1) + EPS);
-        const float kn = rsqrtf(wave_sum(k0 * k0 + k1 * k1) + EPS);
-        *reinterpret_cast<float2*>(p.q + rc) = make_float2(q0 * qn, q1 * qn);
-        *reinterpret_cast<float2*>(p.k + rc) = make_float2(k0 * kn, k1 * kn);
-        *reinterpret_cast<float2*>(p.g + rc) =
-            make_float2(-5.f * sigmoidf_(ea * (z.x + ba.x)), -5.f * sigmoidf_(ea * (z.y + ba.y)));
-        if (lane == 0) p.beta[row * p.H + h] = sigmoidf_(p.pbeta[row * p.H + h]);
+#pragma unroll
+        for (int u = 0; u < PRO_U; ++u) {
+            if (t + u >= t1) break;  // (wave-uniform)
+            const size_t row = (size_t)b * p.T + t + u;
+            const size_t rc = row * p.HD + c;
+            float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f;
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                q0 += wq[0][j] * xq[j].x; q1 += wq[1][j] * xq[j].y;
+                k0 += wk[0][j] * xk[j].x; k1 += wk[1][j] * xk[j].y;
+            }
+            q0 += wq[0][3] * cq[u].x; q1 += wq[1][3] * cq[u].y;
+            k0 += wk[0][3] * ck[u].x; k1 += wk[1][3] * ck[u].y;
+            xq[0] = xq[1]; xq[1] = xq[2]; xq[2] = cq[u];
+            xk[0] = xk[1]; xk[1] = xk[2]; xk[2] = ck[u];
+            q0 = silu(q0); q1 = silu(q1); k0 = silu(k0); k1 = silu(k1);
+            const float qn = rsqrtf(wave_sum(q0 * q0 + q1 * q1) + EPS);
+            const float kn = rsqrtf(wave_sum(k0 * k0 + k1 * k1) + EPS);
+            *reinterpret_cast<float2*>(p.q + rc) = make_float2(q0 * qn, q1 * qn);
+            *reinterpret_cast<float2*>(p.k + rc) = make_float2(k0 * kn, k1 * kn);
+            *reinterpret_cast<float2*>(p.g + rc) =
+                make_float2(-5.f * sigmoidf_(ea * (z[u].x + ba.x)), -5.f * sigmoidf_(ea * (z[u].y + ba.y)));
+            if (lane == 0) p.beta[row * p.H + h] = sigmoidf_(bl[u]);
+        }
     }
 }
 
