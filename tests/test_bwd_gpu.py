@@ -81,3 +81,28 @@ def test_bwd_bf16_long_sequence():
     got, ref = run("bf16", 1, 4096, 4, 128, seed=44)
     e = errors(got, ref)
     assert max(e.values()) <= TOL_BF16, e
+
+
+@pytest.mark.timeout(600)
+def test_bwd_workload2_full_launch_sampled_heads():
+    """The benchmark's backward: B4 H32 T16384 D128, bf16 q/k/v/dO, one kda_bwd over all 128
+    sequences; the float64 backward recomputes 3 sampled (b, h) sequences, every gradient within 1e-2
+    of it."""
+    import synth
+    d = synth.core_inputs(2, seed=0)
+    B, T, H, D = d["k"].shape
+    rng = np.random.default_rng(7)
+    dO = synth.bf16_round(rng.standard_normal((B, T, H, D)).astype(np.float32))
+    t = to_dev(d, "bf16")
+    gr = _kda().kda_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                        dO=torch.from_numpy(dO).to(DEV).to(torch.bfloat16))
+    torch.cuda.synchronize()
+    picks = [(0, 0), (3, 31), (int(rng.integers(B)), int(rng.integers(H)))]
+    for b, h in picks:
+        s = {n: d[n][b:b + 1, :, h:h + 1] for n in ("q", "k", "v", "g", "beta")}
+        ref = oracle.backward(s["q"], s["k"], s["v"], s["g"], s["beta"], dO=dO[b:b + 1, :, h:h + 1])
+        got = {n: (gr[n][b:b + 1, h:h + 1] if n == "dS0" else gr[n][b:b + 1, :, h:h + 1]).cpu().numpy()
+               for n in GRADS}
+        e = errors(got, ref)
+        print(f"(b, h) = ({b}, {h}):", {n: f"{v:.2e}" for n, v in e.items()}, flush=True)
+        assert max(e.values()) <= TOL_BF16, (b, h, e)
