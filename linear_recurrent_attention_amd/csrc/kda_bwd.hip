@@ -275,6 +275,36 @@ __device__ __forceinline__ void mgemm_w(FA a, FB b, F f) {
     }
 }
 
+// dst(m, n) = gam(m) src(m, n) + (Qg^T dO)(m, n) - (Kg^T dX)(m, n) for the D x DH state-gradient tile
+// (the gradient of the state before a chunk), on all waves: wave w takes value-column block w mod
+// (DH / 16) and every (NT / 64) / (DH / 16)-th channel block, so each wave reads its column block of
+// dO and dX once.  Rounding as two products applied one after the other.  dst may be src.
+template <int D, typename TQ, typename TO, typename TX, typename TS>
+__device__ __forceinline__ void state_grad_step(const TQ& Qg, const TQ& Kg, const TO& dO, const TX& dX,
+                                                const float* gam, const TS& src, TS& dst) {
+    static_assert(CS == 16, "one block of four contraction indices per lane group");
+    constexpr int DH = D / 2, TN = DH / 16, NW = NT / 64, TM = D / 16;
+    static_assert(NW % TN == 0, "column blocks per wave");
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l16 = lane & 15, g = lane >> 4, k = 4 * g, n0 = 16 * (wave % TN);
+    const f32x4 bo = col4(dO, k, n0 + l16), bx = col4(dX, k, n0 + l16);
+    for (int mb = wave / TN; mb < TM; mb += NW / TN) {
+        const int m0 = 16 * mb;
+        const f32x4 aq = col4(Qg, k, m0 + l16), ak = col4(Kg, k, m0 + l16);
+        f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pk = pq;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pq = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[r], bo[r], pq, 0, 0, 0);
+            pk = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bx[r], pk, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + 4 * g + r, n = n0 + l16;
+            dst[m][n] = __builtin_fmaf(gam[m], src[m][n], pq[r]) - pk[r];
+        }
+    }
+}
+
 // L = tril(Kg Kh^T, -1) on wave W and A = tril(Qg Kh^T) on wave W + 1 (one 16 x 16 tile each).
 template <int D, int W, typename CT>
 __device__ __forceinline__ void gram_products(CT& c) {
@@ -488,10 +518,7 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
         // the next inverse (waves 4-7), then on all waves
         // dS <- Diag(gam) dS + Qg^T dO - Kg^T dX   (each entry read and written by its own thread)
         if (next) unit_inverse(cn);
-        mgemm_w<D, DH, CS, 0, NT / 64>([&](int m, int k) { return col4(c.Qg, k, m); }, [&](int k, int n) { return col4(c.dO, k, n); },
-                                       [&](int m, int n, float v) { dS[m][n] = __builtin_fmaf(c.gam[m], dS[m][n], v); });
-        mgemm_w<D, DH, CS, 0, NT / 64>([&](int m, int k) { return col4(c.Kg, k, m); }, [&](int k, int n) { return col4(dX, k, n); },
-                                       [&](int m, int n, float v) { dS[m][n] -= v; });
+        state_grad_step<D>(c.Qg, c.Kg, c.dO, dX, c.gam, dS, dS);
         __syncthreads();
         if (cj % SPI == 0 && cj > 0) {  // the start of interval cj / SPI: the gradient of the state there
             for (int e = tid; e < D * DH; e += NT) {
@@ -779,10 +806,7 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             // the gradient of the state between the two chunks, Diag(gam) dS + Qg^T dO - Kg^T dX,
             // into Q (the state S of this chunk, no longer read); then P gets the start state back
             __syncthreads();
-            mgemm<D, DH, CS>([&](int m, int k) { return col4(c.Qg, k, m); }, [&](int k, int n) { return col4(c.dO, k, n); },
-                                  [&](int m, int n, float v) { gr.Q[m][n] = __builtin_fmaf(c.gam[m], gr.P[m][n], v); });
-            mgemm<D, DH, CS>([&](int m, int k) { return col4(c.Kg, k, m); }, [&](int k, int n) { return col4(c.dX, k, n); },
-                                  [&](int m, int n, float v) { gr.Q[m][n] -= v; });
+            state_grad_step<D>(c.Qg, c.Kg, c.dO, c.dX, c.gam, gr.P, gr.Q);
             __syncthreads();
             put_state<D>(gr.P, s0r);
         }
