@@ -509,6 +509,14 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
             build_s<D, IN_BF16, DO_BF16>(cn, w, p.scale);
             fetch_s<D, IN_BF16, DO_BF16>(w, p, b, h, max(cj - 3, 0) * CS, half);
         }
+        // the chain waves, done with dU long before the build, store the gradient of the state at the
+        // start of chunk cj + 1 when an interval starts there (dS changes only in the last phase)
+        if (chain && (cj + 1) % SPI == 0 && cj + 1 < nch) {
+            for (int e = tid; e < D * DH; e += NTH) {
+                const int r = e / DH, j = e % DH;
+                p.dSb[at((cj + 1) / SPI - 1) + (size_t)r * D + j] = dS[r][j];
+            }
+        }
         __syncthreads();
         // dX = Tm^T dU  |  the next chunk's L and A
         mgemm_w<CS, DH, CS, 0, 4>([&](int m, int k) { return col4(c.Tm, k, m); }, [&](int k, int n) { return col4(dU, k, n); },
@@ -520,12 +528,6 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
         if (next) unit_inverse(cn);
         state_grad_step<D>(c.Qg, c.Kg, c.dO, dX, c.gam, dS, dS);
         __syncthreads();
-        if (cj % SPI == 0 && cj > 0) {  // the start of interval cj / SPI: the gradient of the state there
-            for (int e = tid; e < D * DH; e += NT) {
-                const int r = e / DH, j = e % DH;
-                p.dSb[at(cj / SPI - 1) + (size_t)r * D + j] = dS[r][j];
-            }
-        }
     };
     for (int cj = nch - 1; cj >= 0; cj -= 2) {
         step(cj, wa);
