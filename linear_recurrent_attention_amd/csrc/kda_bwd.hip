@@ -32,6 +32,7 @@
 #include "kda_common.h"
 #include "kda_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace kda {
@@ -631,191 +632,206 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
     __shared__ Chunk<D> c;
     __shared__ Grad<D> gr;
     const int tid = threadIdx.x;
-    const int half = blockIdx.x & 1;
-    const int wi = blockIdx.x >> 1;
-    const int bh = wi / p.nint, i = wi - bh * p.nint;
-    const int b = bh / p.H, h = bh - b * p.H;
-    // start state of the interval and the gradient of the state after it (global, full rows)
-    const float* S0g = i == 0 ? (p.S0 ? p.S0 + (size_t)bh * D * D : nullptr) : p.Sck + ((size_t)bh * p.nck + i - 1) * D * D;
-    const float* dSe = p.dSb + ((size_t)bh * p.nint + i) * D * D;
-    const int col0 = half * DH;
-    const int nsub = (min(CK, p.T - i * CK) + CS - 1) / CS;
-
-    // Buffers: one chunk:  P = start state, Q = end gradient.
-    // Two chunks: P = start state -> Q = state after the first chunk; second chunk: S = Q, dS = P
-    // (the interval's end gradient); its start gradient goes to Q; first chunk: S = P (start state
-    // again), dS = Q.
-    // Global reads: both state tiles and the first chunk's inputs are issued here, the other
-    // chunk's inputs one chunk ahead (each into registers), so that their latencies overlap work.
+    // Work items (interval, value half), item = 2 * (bh * nint + i) + half, taken by the workgroups in
+    // turn (item = blockIdx.x + k * gridDim.x); each workgroup reads its next item's state tiles and
+    // inputs while it computes the last chunk of the current one.
+    const int nitems = 2 * p.B * p.H * p.nint;
     constexpr int SPT = D * DH / NT;
     float s0r[SPT], dsr[SPT];
-    fetch_state<D>(s0r, S0g, col0);
-    fetch_state<D>(dsr, dSe, col0);
     Raw<D> w, w1;
-    fetch_chunk<D, IN_BF16, DO_BF16>(w, p, b, h, i * CK, half, true);
-    fetch_chunk<D, IN_BF16, DO_BF16>(w1, p, b, h, i * CK + (nsub - 1) * CS, half, true);  // the second chunk (if any)
-    put_state<D>(gr.P, s0r);
-    if (nsub == 2) {  // Q = Diag(gam) S + Kb^T Tm (V - Kg S)
-        build_chunk<D, IN_BF16, DO_BF16>(c, w, p.scale, true);
-        __syncthreads();
-        // L and A (waves 4, 5) beside X = V - Kg S (waves 0-3), then the inverse
-        gram_products<D, 4>(c);
-        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return row4(c.Kg, m, k); }, [&](int k, int n) { return col4(gr.P, k, n); },
-                                 [&](int m, int n, float v) { c.X[m][n] -= v; });
-        __syncthreads();
-        unit_inverse(c);
-        __syncthreads();
-        mgemm<CS, DH, CS>([&](int m, int k) { return row4(c.Tm, m, k); }, [&](int k, int n) { return col4(c.X, k, n); },
-                               [&](int m, int n, float v) { c.U[m][n] = v; });
-        __syncthreads();
-        mgemm<D, DH, CS>([&](int m, int k) { return col4(c.Kb, k, m); }, [&](int k, int n) { return col4(c.U, k, n); },
-                              [&](int m, int n, float v) { gr.Q[m][n] = __builtin_fmaf(c.gam[m], gr.P[m][n], v); });
-        __syncthreads();
-        put_state<D>(gr.P, dsr);
-    } else {
-        put_state<D>(gr.Q, dsr);
-    }
-    __syncthreads();
-    // the interval's chunks in reverse (written out twice rather than looped, so that the registers
-    // holding the prefetched inputs are live only where they are needed)
-    auto step = [&](const int s) {
-        const int c0 = i * CK + s * CS;
-        float (*Sb)[DH + VP] = (nsub == 2 && s == 1) ? gr.Q : gr.P;
-        float (*dSb)[DH + VP] = (nsub == 2 && s == 1) ? gr.P : gr.Q;
-        if (nsub == 2 && s == 1)
-            build_chunk<D, IN_BF16, DO_BF16>(c, w1, p.scale, true);
-        else
-            build_chunk<D, IN_BF16, DO_BF16>(c, w, p.scale, true);
-        __syncthreads();
-        // L and A (waves 4, 5) beside X = V - Kg S (waves 0-3); the inverse (waves 4-7) beside Kb dS
-        gram_products<D, 4>(c);
-        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return row4(c.Kg, m, k); }, [&](int k, int n) { return col4(Sb, k, n); },
-                                 [&](int m, int n, float v) { c.X[m][n] -= v; });
-        __syncthreads();
-        unit_inverse(c);
-        mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return row4(c.Kb, m, k); }, [&](int k, int n) { return col4(dSb, k, n); },
-                                 [&](int m, int n, float v) { c.dU[m][n] = v; });
-        __syncthreads();
-        // U = Tm X
-        mgemm<CS, DH, CS>([&](int m, int k) { return row4(c.Tm, m, k); }, [&](int k, int n) { return col4(c.X, k, n); },
-                               [&](int m, int n, float v) { c.U[m][n] = v; });
-        __syncthreads();
-        // dU += A^T dO;  dKb = U dS^T;  dgam = rowsum(dS * S);  dA = tril(dO U^T)
-        mgemm<CS, DH, CS>([&](int m, int k) { return col4(c.A, k, m); }, [&](int k, int n) { return col4(c.dO, k, n); },
-                               [&](int m, int n, float v) { c.dU[m][n] += v; });
-        mgemm<CS, D, DH>([&](int m, int k) { return row4(c.U, m, k); }, [&](int k, int n) { return row4(dSb, n, k); },
-                              [&](int m, int n, float v) { gr.G[m][n] = v; });
-        {  // dgam: NT / D consecutive lanes per channel, each a slice of the columns, then a shuffle sum
-            constexpr int NP = NT / D, SL = DH / NP;
-            const int ch = tid / NP, pt = tid % NP;
-            float a = 0.f;
-#pragma unroll
-            for (int j = 0; j < SL; ++j) a = __builtin_fmaf(dSb[ch][pt * SL + j], Sb[ch][pt * SL + j], a);
-#pragma unroll
-            for (int o = NP / 2; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
-            if (pt == 0) gr.dgam[ch] = a;
-        }
-        mgemm<CS, CS, DH>([&](int m, int k) { return row4(c.dO, m, k); }, [&](int k, int n) { return row4(c.U, n, k); },
-                               [&](int m, int n, float v) { gr.dA[m][n] = n <= m ? v : 0.f; }, 7);
-        __syncthreads();
-        // fold dKb: dk = dKb exp(b_last - b);  db = -dKb Kb;  last row: sum_t dKb Kb + dgam gam
-        float dKr[PER], dbr[PER];
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int e = tid + NT * k, r = e / D, ch = e % D;
-            const float gk = gr.G[r][ch];
-            dKr[k] = gk * (c.gam[ch] / c.Gam[r][ch]);
-            dbr[k] = -gk * c.Kb[r][ch];
-        }
-        if (tid < D) {
-            float a = gr.dgam[tid] * c.gam[tid];
-            for (int r = 0; r < CS; ++r) a = __builtin_fmaf(gr.G[r][tid], c.Kb[r][tid], a);
-            gr.dlast[tid] = a;
-        }
-        // dTm = dU X^T;  dX = Tm^T dU  (dv)
-        mgemm<CS, CS, DH>([&](int m, int k) { return row4(c.dU, m, k); }, [&](int k, int n) { return row4(c.X, n, k); },
-                               [&](int m, int n, float v) { gr.dTm[m][n] = v; }, 4);
-        mgemm<CS, DH, CS>([&](int m, int k) { return col4(c.Tm, k, m); }, [&](int k, int n) { return col4(c.dU, k, n); },
-                               [&](int m, int n, float v) { c.dX[m][n] = v; });
-        __syncthreads();
-        // the dTm -> dL chain on wave 7 alone, beside dQg = dO S^T + dA Kh on waves 0-3 (then
-        // dq = dQg scale Gamma, Qg holding the scale, and db += dQg Qg)
-        if (tid >= NT - 64) dl_chain(c, gr, tid & 63);
-        mgemm_w<CS, D, DH, 0, 4>([&](int m, int k) { return row4(c.dO, m, k); }, [&](int k, int n) { return row4(Sb, n, k); },
-                                 [&](int m, int n, float v) { gr.G[m][n] = v; });
-        mgemm_w<CS, D, CS, 0, 4>([&](int m, int k) { return row4(gr.dA, m, k); }, [&](int k, int n) { return col4(c.Kh, k, n); },
-                                 [&](int m, int n, float v) { gr.G[m][n] += v; });
-        __syncthreads();
-        const int n_ok = min(CS, p.T - c0);
-        auto grow = [&](int r) { return ((size_t)b * p.T + c0 + r) * p.H + h; };
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int e = tid + NT * k, r = e / D, ch = e % D;
-            const float gq = gr.G[r][ch];
-            dbr[k] = __builtin_fmaf(gq, c.Qg[r][ch], dbr[k]);
-            if (r < n_ok && p.dq) atomicAdd(&p.dq[grow(r) * D + ch], gq * p.scale * c.Gam[r][ch]);
-        }
-        __syncthreads();
-        // dKg = -dX S^T + dL Kh -> dk += dKg Gamma, db += dKg Kg
-        mgemm<CS, D, DH>([&](int m, int k) { return row4(c.dX, m, k); }, [&](int k, int n) { return row4(Sb, n, k); },
-                              [&](int m, int n, float v) { gr.G[m][n] = -v; });
-        mgemm<CS, D, CS>([&](int m, int k) { return row4(gr.dM, m, k); }, [&](int k, int n) { return col4(c.Kh, k, n); },
-                              [&](int m, int n, float v) { gr.G[m][n] += v; });
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int e = tid + NT * k, r = e / D, ch = e % D;
-            const float gk = gr.G[r][ch];
-            dKr[k] = __builtin_fmaf(gk, c.Gam[r][ch], dKr[k]);
-            dbr[k] = __builtin_fmaf(gk, c.Kg[r][ch], dbr[k]);
-        }
-        __syncthreads();
-        // dKh = dL^T Kg + dA^T Qg -> dk += dKh / Gamma, db -= dKh Kh
-        mgemm<CS, D, CS>([&](int m, int k) { return col4(gr.dM, k, m); }, [&](int k, int n) { return col4(c.Kg, k, n); },
-                              [&](int m, int n, float v) { gr.G[m][n] = v; });
-        mgemm<CS, D, CS>([&](int m, int k) { return col4(gr.dA, k, m); }, [&](int k, int n) { return col4(c.Qg, k, n); },
-                              [&](int m, int n, float v) { gr.G[m][n] += v; });
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int e = tid + NT * k, r = e / D, ch = e % D;
-            const float gh = gr.G[r][ch];
-            dKr[k] += gh / c.Gam[r][ch];
-            dbr[k] = __builtin_fmaf(-gh, c.Kh[r][ch], dbr[k]);
-            if (r < n_ok && p.dk) atomicAdd(&p.dk[grow(r) * D + ch], dKr[k]);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int e = tid + NT * k;
-            gr.G[e / D][e % D] = dbr[k];
-        }
-        // outputs of the chunk: dv, dbeta, dg (reverse cumulative sum of db)
-        for (int e = tid; e < CS * DH; e += NT) {
-            const int r = e / DH, j = e % DH;
-            if (r < n_ok && p.dv) p.dv[grow(r) * D + col0 + j] = c.dX[r][j];
-        }
-        if (tid < CS && tid < n_ok && p.dbeta) atomicAdd(&p.dbeta[grow(tid)], gr.dbeta[tid]);
-        __syncthreads();
-        if (tid < D && p.dg) {
-            float a = gr.dlast[tid];
-            for (int r = CS - 1; r >= 0; --r) {
-                a += gr.G[r][tid];
-                if (r < n_ok) atomicAdd(&p.dg[grow(r) * D + tid], a);
-            }
-        }
-        if (nsub == 2 && s == 1) {
-            // the gradient of the state between the two chunks, Diag(gam) dS + Qg^T dO - Kg^T dX,
-            // into Q (the state S of this chunk, no longer read); then P gets the start state back
-            __syncthreads();
-            state_grad_step<D>(c.Qg, c.Kg, c.dO, c.dX, c.gam, gr.P, gr.Q);
-            __syncthreads();
-            put_state<D>(gr.P, s0r);
-        }
-        __syncthreads();
+    // start state of the interval and the gradient of the state after it (global, full rows), and the
+    // inputs of its first chunk, into registers
+    auto fetch_item = [&](int item) {
+        const int hf = item & 1, wj = item >> 1;
+        const int bj = wj / p.nint, ij = wj - bj * p.nint;
+        const int bb = bj / p.H, hh = bj - bb * p.H;
+        const int ns = (min(CK, p.T - ij * CK) + CS - 1) / CS;
+        const float* S0g = ij == 0 ? (p.S0 ? p.S0 + (size_t)bj * D * D : nullptr) : p.Sck + ((size_t)bj * p.nck + ij - 1) * D * D;
+        fetch_state<D>(s0r, S0g, hf * DH);
+        fetch_state<D>(dsr, p.dSb + ((size_t)bj * p.nint + ij) * D * D, hf * DH);
+        fetch_chunk<D, IN_BF16, DO_BF16>(w, p, bb, hh, ij * CK, hf, true);
     };
-    if (nsub == 2) step(1);
-    step(0);
+    fetch_item(blockIdx.x);
+    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+        const int half = item & 1;
+        const int wi = item >> 1;
+        const int bh = wi / p.nint, i = wi - bh * p.nint;
+        const int b = bh / p.H, h = bh - b * p.H;
+        const int col0 = half * DH;
+        const int nsub = (min(CK, p.T - i * CK) + CS - 1) / CS;
+        // the second chunk's inputs (if any), first needed after the first chunk's state step
+        fetch_chunk<D, IN_BF16, DO_BF16>(w1, p, b, h, i * CK + (nsub - 1) * CS, half, true);
+
+        // Buffers: one chunk:  P = start state, Q = end gradient.
+        // Two chunks: P = start state -> Q = state after the first chunk; second chunk: S = Q, dS = P
+        // (the interval's end gradient); its start gradient goes to Q; first chunk: S = P (start state
+        // again), dS = Q.
+        put_state<D>(gr.P, s0r);
+        if (nsub == 2) {  // Q = Diag(gam) S + Kb^T Tm (V - Kg S)
+            build_chunk<D, IN_BF16, DO_BF16>(c, w, p.scale, true);
+            __syncthreads();
+            // L and A (waves 4, 5) beside X = V - Kg S (waves 0-3), then the inverse
+            gram_products<D, 4>(c);
+            mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return row4(c.Kg, m, k); }, [&](int k, int n) { return col4(gr.P, k, n); },
+                                     [&](int m, int n, float v) { c.X[m][n] -= v; });
+            __syncthreads();
+            unit_inverse(c);
+            __syncthreads();
+            mgemm<CS, DH, CS>([&](int m, int k) { return row4(c.Tm, m, k); }, [&](int k, int n) { return col4(c.X, k, n); },
+                                   [&](int m, int n, float v) { c.U[m][n] = v; });
+            __syncthreads();
+            mgemm<D, DH, CS>([&](int m, int k) { return col4(c.Kb, k, m); }, [&](int k, int n) { return col4(c.U, k, n); },
+                                  [&](int m, int n, float v) { gr.Q[m][n] = __builtin_fmaf(c.gam[m], gr.P[m][n], v); });
+            __syncthreads();
+            put_state<D>(gr.P, dsr);
+        } else {
+            put_state<D>(gr.Q, dsr);
+        }
+        __syncthreads();
+        // the interval's chunks in reverse (written out twice rather than looped, so that the registers
+        // holding the prefetched inputs are live only where they are needed)
+        auto step = [&](const int s) {
+            const int c0 = i * CK + s * CS;
+            float (*Sb)[DH + VP] = (nsub == 2 && s == 1) ? gr.Q : gr.P;
+            float (*dSb)[DH + VP] = (nsub == 2 && s == 1) ? gr.P : gr.Q;
+            if (nsub == 2 && s == 1) {
+                build_chunk<D, IN_BF16, DO_BF16>(c, w1, p.scale, true);
+            } else {
+                build_chunk<D, IN_BF16, DO_BF16>(c, w, p.scale, true);
+                // every register input of this item is used: read the next item's
+                if (item + (int)gridDim.x < nitems) fetch_item(item + gridDim.x);
+            }
+            __syncthreads();
+            // L and A (waves 4, 5) beside X = V - Kg S (waves 0-3); the inverse (waves 4-7) beside Kb dS
+            gram_products<D, 4>(c);
+            mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return row4(c.Kg, m, k); }, [&](int k, int n) { return col4(Sb, k, n); },
+                                     [&](int m, int n, float v) { c.X[m][n] -= v; });
+            __syncthreads();
+            unit_inverse(c);
+            mgemm_w<CS, DH, D, 0, 4>([&](int m, int k) { return row4(c.Kb, m, k); }, [&](int k, int n) { return col4(dSb, k, n); },
+                                     [&](int m, int n, float v) { c.dU[m][n] = v; });
+            __syncthreads();
+            // U = Tm X
+            mgemm<CS, DH, CS>([&](int m, int k) { return row4(c.Tm, m, k); }, [&](int k, int n) { return col4(c.X, k, n); },
+                                   [&](int m, int n, float v) { c.U[m][n] = v; });
+            __syncthreads();
+            // dU += A^T dO;  dKb = U dS^T;  dgam = rowsum(dS * S);  dA = tril(dO U^T)
+            mgemm<CS, DH, CS>([&](int m, int k) { return col4(c.A, k, m); }, [&](int k, int n) { return col4(c.dO, k, n); },
+                                   [&](int m, int n, float v) { c.dU[m][n] += v; });
+            mgemm<CS, D, DH>([&](int m, int k) { return row4(c.U, m, k); }, [&](int k, int n) { return row4(dSb, n, k); },
+                                  [&](int m, int n, float v) { gr.G[m][n] = v; });
+            {  // dgam: NT / D consecutive lanes per channel, each a slice of the columns, then a shuffle sum
+                constexpr int NP = NT / D, SL = DH / NP;
+                const int ch = tid / NP, pt = tid % NP;
+                float a = 0.f;
+    #pragma unroll
+                for (int j = 0; j < SL; ++j) a = __builtin_fmaf(dSb[ch][pt * SL + j], Sb[ch][pt * SL + j], a);
+    #pragma unroll
+                for (int o = NP / 2; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
+                if (pt == 0) gr.dgam[ch] = a;
+            }
+            mgemm<CS, CS, DH>([&](int m, int k) { return row4(c.dO, m, k); }, [&](int k, int n) { return row4(c.U, n, k); },
+                                   [&](int m, int n, float v) { gr.dA[m][n] = n <= m ? v : 0.f; }, 7);
+            __syncthreads();
+            // fold dKb: dk = dKb exp(b_last - b);  db = -dKb Kb;  last row: sum_t dKb Kb + dgam gam
+            float dKr[PER], dbr[PER];
+    #pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int e = tid + NT * k, r = e / D, ch = e % D;
+                const float gk = gr.G[r][ch];
+                dKr[k] = gk * (c.gam[ch] / c.Gam[r][ch]);
+                dbr[k] = -gk * c.Kb[r][ch];
+            }
+            if (tid < D) {
+                float a = gr.dgam[tid] * c.gam[tid];
+                for (int r = 0; r < CS; ++r) a = __builtin_fmaf(gr.G[r][tid], c.Kb[r][tid], a);
+                gr.dlast[tid] = a;
+            }
+            // dTm = dU X^T;  dX = Tm^T dU  (dv)
+            mgemm<CS, CS, DH>([&](int m, int k) { return row4(c.dU, m, k); }, [&](int k, int n) { return row4(c.X, n, k); },
+                                   [&](int m, int n, float v) { gr.dTm[m][n] = v; }, 4);
+            mgemm<CS, DH, CS>([&](int m, int k) { return col4(c.Tm, k, m); }, [&](int k, int n) { return col4(c.dU, k, n); },
+                                   [&](int m, int n, float v) { c.dX[m][n] = v; });
+            __syncthreads();
+            // the dTm -> dL chain on wave 7 alone, beside dQg = dO S^T + dA Kh on waves 0-3 (then
+            // dq = dQg scale Gamma, Qg holding the scale, and db += dQg Qg)
+            if (tid >= NT - 64) dl_chain(c, gr, tid & 63);
+            mgemm_w<CS, D, DH, 0, 4>([&](int m, int k) { return row4(c.dO, m, k); }, [&](int k, int n) { return row4(Sb, n, k); },
+                                     [&](int m, int n, float v) { gr.G[m][n] = v; });
+            mgemm_w<CS, D, CS, 0, 4>([&](int m, int k) { return row4(gr.dA, m, k); }, [&](int k, int n) { return col4(c.Kh, k, n); },
+                                     [&](int m, int n, float v) { gr.G[m][n] += v; });
+            __syncthreads();
+            const int n_ok = min(CS, p.T - c0);
+            auto grow = [&](int r) { return ((size_t)b * p.T + c0 + r) * p.H + h; };
+    #pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int e = tid + NT * k, r = e / D, ch = e % D;
+                const float gq = gr.G[r][ch];
+                dbr[k] = __builtin_fmaf(gq, c.Qg[r][ch], dbr[k]);
+                if (r < n_ok && p.dq) atomicAdd(&p.dq[grow(r) * D + ch], gq * p.scale * c.Gam[r][ch]);
+            }
+            __syncthreads();
+            // dKg = -dX S^T + dL Kh -> dk += dKg Gamma, db += dKg Kg
+            mgemm<CS, D, DH>([&](int m, int k) { return row4(c.dX, m, k); }, [&](int k, int n) { return row4(Sb, n, k); },
+                                  [&](int m, int n, float v) { gr.G[m][n] = -v; });
+            mgemm<CS, D, CS>([&](int m, int k) { return row4(gr.dM, m, k); }, [&](int k, int n) { return col4(c.Kh, k, n); },
+                                  [&](int m, int n, float v) { gr.G[m][n] += v; });
+            __syncthreads();
+    #pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int e = tid + NT * k, r = e / D, ch = e % D;
+                const float gk = gr.G[r][ch];
+                dKr[k] = __builtin_fmaf(gk, c.Gam[r][ch], dKr[k]);
+                dbr[k] = __builtin_fmaf(gk, c.Kg[r][ch], dbr[k]);
+            }
+            __syncthreads();
+            // dKh = dL^T Kg + dA^T Qg -> dk += dKh / Gamma, db -= dKh Kh
+            mgemm<CS, D, CS>([&](int m, int k) { return col4(gr.dM, k, m); }, [&](int k, int n) { return col4(c.Kg, k, n); },
+                                  [&](int m, int n, float v) { gr.G[m][n] = v; });
+            mgemm<CS, D, CS>([&](int m, int k) { return col4(gr.dA, k, m); }, [&](int k, int n) { return col4(c.Qg, k, n); },
+                                  [&](int m, int n, float v) { gr.G[m][n] += v; });
+            __syncthreads();
+    #pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int e = tid + NT * k, r = e / D, ch = e % D;
+                const float gh = gr.G[r][ch];
+                dKr[k] += gh / c.Gam[r][ch];
+                dbr[k] = __builtin_fmaf(-gh, c.Kh[r][ch], dbr[k]);
+                if (r < n_ok && p.dk) atomicAdd(&p.dk[grow(r) * D + ch], dKr[k]);
+            }
+            __syncthreads();
+    #pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int e = tid + NT * k;
+                gr.G[e / D][e % D] = dbr[k];
+            }
+            // outputs of the chunk: dv, dbeta, dg (reverse cumulative sum of db)
+            for (int e = tid; e < CS * DH; e += NT) {
+                const int r = e / DH, j = e % DH;
+                if (r < n_ok && p.dv) p.dv[grow(r) * D + col0 + j] = c.dX[r][j];
+            }
+            if (tid < CS && tid < n_ok && p.dbeta) atomicAdd(&p.dbeta[grow(tid)], gr.dbeta[tid]);
+            __syncthreads();
+            if (tid < D && p.dg) {
+                float a = gr.dlast[tid];
+                for (int r = CS - 1; r >= 0; --r) {
+                    a += gr.G[r][tid];
+                    if (r < n_ok) atomicAdd(&p.dg[grow(r) * D + tid], a);
+                }
+            }
+            if (nsub == 2 && s == 1) {
+                // the gradient of the state between the two chunks, Diag(gam) dS + Qg^T dO - Kg^T dX,
+                // into Q (the state S of this chunk, no longer read); then P gets the start state back
+                __syncthreads();
+                state_grad_step<D>(c.Qg, c.Kg, c.dO, c.dX, c.gam, gr.P, gr.Q);
+                __syncthreads();
+                put_state<D>(gr.P, s0r);
+            }
+            __syncthreads();
+        };
+        if (nsub == 2) step(1);
+        step(0);
+    }
 }
 
 // Zero the accumulated outputs.
@@ -835,8 +851,13 @@ hipError_t launch_kernels(const BwdParams& p, hipStream_t stream) {
                        stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // one workgroup per compute unit (its LDS allows no second), each taking every gridDim-th item
+    int dev = 0, ncu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const size_t nitems = 2 * (size_t)p.B * p.H * p.nint;
     hipLaunchKernelGGL((kda_bwd_chunk_kernel<D, CK, IN_BF16, DO_BF16>),
-                       dim3((unsigned)(2 * (size_t)p.B * p.H * p.nint)), dim3(NT), 0, stream, p);
+                       dim3((unsigned)std::min(nitems, (size_t)std::max(ncu, 1))), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 
