@@ -497,6 +497,16 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
         unit_inverse(c);
         __syncthreads();
     }
+    // Zeroing of the outputs the input-gradient kernel accumulates into (when zero_in_state): dbeta
+    // here, and this workgroup's share of dq, dk and dg a few 16-byte stores per chain thread per
+    // step, in the chain waves' idle time of the first phase.
+    const size_t nz4 = p.zero_in_state ? (size_t)p.B * p.T * p.H * D / 4 : 0;
+    const size_t z0 = nz4 * blockIdx.x / gridDim.x, z1 = nz4 * (blockIdx.x + 1) / gridDim.x;
+    const size_t zps = (z1 - z0 + (size_t)nch * NTH - 1) / ((size_t)nch * NTH);  // per chain thread and step
+    if (p.zero_in_state && p.dbeta) {
+        const size_t nb = (size_t)p.B * p.T * p.H;
+        for (size_t e = nb * blockIdx.x / gridDim.x + tid; e < nb * (blockIdx.x + 1) / gridDim.x; e += NT) p.dbeta[e] = 0.f;
+    }
     auto step = [&](const int cj, SRaw<D>& w) {
         SChunk<D>& c = sc[cj & 1];         // this chunk
         SChunk<D>& cn = sc[(cj - 1) & 1];  // the next one (chunk cj - 1)
@@ -510,8 +520,21 @@ __global__ void __launch_bounds__(NT) kda_bwd_state_kernel(BwdParams p) {
             build_s<D, IN_BF16, DO_BF16>(cn, w, p.scale);
             fetch_s<D, IN_BF16, DO_BF16>(w, p, b, h, max(cj - 3, 0) * CS, half);
         }
-        // the chain waves, done with dU long before the build, store the gradient of the state at the
-        // start of chunk cj + 1 when an interval starts there (dS changes only in the last phase)
+        // the chain waves, done with dU long before the build: their share of the zeroing, and the
+        // gradient of the state at the start of chunk cj + 1 when an interval starts there (dS
+        // changes only in the last phase)
+        if (chain && zps > 0) {
+            const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+            const size_t zb = z0 + (size_t)(nch - 1 - cj) * zps * NTH + tid;
+            for (size_t j = 0; j < zps; ++j) {
+                const size_t z = zb + j * NTH;
+                if (z < z1) {
+                    if (p.dq) reinterpret_cast<float4*>(p.dq)[z] = zero;
+                    if (p.dk) reinterpret_cast<float4*>(p.dk)[z] = zero;
+                    if (p.dg) reinterpret_cast<float4*>(p.dg)[z] = zero;
+                }
+            }
+        }
         if (chain && (cj + 1) % SPI == 0 && cj + 1 < nch) {
             for (int e = tid; e < D * DH; e += NTH) {
                 const int r = e / DH, j = e % DH;
@@ -887,11 +910,16 @@ hipError_t launch_bwd(const BwdParams& p0, bool in_bf16, bool do_bf16, bool prec
     hipError_t e = hipSuccess;
     if (f.n_ckpt > 0) e = in_bf16 ? launch_fwd_bf16(f, stream) : launch_fwd_f32(f, stream);
     if (e != hipSuccess) return e;
-    // 2. zero the accumulated outputs
-    const size_t nk = (size_t)p.B * p.T * p.H * D;
-    hipLaunchKernelGGL(bwd::kda_bwd_zero_kernel, dim3(2048), dim3(256), 0, stream, p.dq, p.dq ? nk : 0, p.dk,
-                       p.dk ? nk : 0, p.dg, p.dg ? nk : 0, p.dbeta, p.dbeta ? (size_t)p.B * p.T * p.H : 0);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 2. zero the accumulated outputs: inside the state pass when the float32 outputs allow 16-byte
+    // stores, else by a kernel of its own
+    auto a16 = [](const float* q) { return ((uintptr_t)q & 15) == 0; };
+    p.zero_in_state = a16(p.dq) && a16(p.dk) && a16(p.dg);
+    if (!p.zero_in_state) {
+        const size_t nk = (size_t)p.B * p.T * p.H * D;
+        hipLaunchKernelGGL(bwd::kda_bwd_zero_kernel, dim3(2048), dim3(256), 0, stream, p.dq, p.dq ? nk : 0, p.dk,
+                           p.dk ? nk : 0, p.dg, p.dg ? nk : 0, p.dbeta, p.dbeta ? (size_t)p.B * p.T * p.H : 0);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     // 3. state gradients, then the input gradients
     if (!in_bf16) return D == 64 ? bwd::launch_kernels<64, 16, false, false>(p, stream)
                                  : bwd::launch_kernels<128, 16, false, false>(p, stream);

@@ -46,6 +46,7 @@ struct BwdParams {
     int B, T, H, D;
     float scale;
     int nint, nck;     // intervals (ceil(T / interval)), checkpoints (T / interval)
+    int zero_in_state; // the state pass zeroes dq, dk, dg (16-byte aligned) and dbeta
 };
 
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t stream);  // Dk = Dv = 128, chunk 32 (in_f32 too)

@@ -106,3 +106,34 @@ def test_bwd_workload2_full_launch_sampled_heads():
         e = errors(got, ref)
         print(f"(b, h) = ({b}, {h}):", {n: f"{v:.2e}" for n, v in e.items()}, flush=True)
         assert max(e.values()) <= TOL_BF16, (b, h, e)
+
+
+def test_bwd_unaligned_outputs_take_the_zeroing_kernel():
+    """Output gradients at addresses that are not 16-byte aligned (4 bytes past an allocation) make
+    the state pass leave the zeroing to a kernel of its own; the gradients are bitwise those of the
+    aligned call (two addends per element onto zero, so their order does not matter)."""
+    import linear_recurrent_attention_amd as kda
+    from linear_recurrent_attention_amd import _lib
+    B, T, H, D = 1, 200, 3, 128
+    d, S0 = rand_small(45, B, T, H, D=D, io="bf16", s0=True)
+    rng = np.random.default_rng(145)
+    import synth
+    dO = torch.from_numpy(synth.bf16_round(rng.standard_normal((B, T, H, D)).astype(np.float32))).to(DEV).to(torch.bfloat16)
+    t = to_dev(d, "bf16")
+    S0t = torch.from_numpy(S0).to(DEV)
+    ref = kda.kda_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], dO=dO, S0=S0t)
+    shapes = {"dq": (B, T, H, D), "dk": (B, T, H, D), "dv": (B, T, H, D), "dg": (B, T, H, D), "dbeta": (B, T, H),
+              "dS0": (B, H, D, D)}
+    bufs = {n: torch.full((int(np.prod(s)) + 1,), np.nan, dtype=torch.float32, device=DEV) for n, s in shapes.items()}
+    desc, _, _ = kda._fwd_args(t["q"], t["k"], t["v"], t["g"], t["beta"], S0t, torch.bfloat16, False, t["q"], None, 0,
+                               False, 1.0)
+    ws = torch.empty(_lib.bwd_workspace_size(desc), dtype=torch.uint8, device=DEV)
+    code = _lib.bwd_raw(desc, t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), t["g"].data_ptr(),
+                        t["beta"].data_ptr(), S0t.data_ptr(), dO.data_ptr(), 0,
+                        *[bufs[n].data_ptr() + 4 for n in GRADS], ws.data_ptr(), ws.numel(),
+                        torch.cuda.current_stream().cuda_stream)
+    _lib.check(code)
+    torch.cuda.synchronize()
+    for n in GRADS:
+        got = bufs[n][1:].view(shapes[n])
+        assert torch.equal(got, ref[n]), n
