@@ -22,10 +22,12 @@
 //      matrix-core path, 16 on the float32 path), no output;
 //   2. kda_bwd_state_kernel, one workgroup per (sequence, value half), sequential in reverse over
 //      chunks: the state gradient dS at every interval boundary (its update needs no state); half
-//      the waves carry dS while the other half prepare the next chunk's factors;
-//   3. kda_bwd_chunk_kernel, one workgroup per (sequence, interval, value half), all in parallel:
-//      every input gradient of the interval, from the interval's start state and end gradient (a
-//      32-token interval first steps its state through the first 16-token chunk).
+//      the waves carry dS while the other half prepare the next chunk's factors; it also zeroes the
+//      outputs step 3 accumulates into;
+//   3. kda_bwd_chunk_kernel, one work item per (sequence, interval, value half), all independent,
+//      taken in turn by one persistent workgroup per CU: every input gradient of the interval, from
+//      the interval's start state and end gradient (a 32-token interval first steps its state
+//      through the first 16-token chunk).
 // Every gradient is linear in (dO, dS), so each value half computes the contributions of its own
 // value columns; the two halves' contributions to dq, dk, dg and dbeta are added with float32
 // atomics onto zeroed outputs (exactly two addends per element: the sum does not depend on order).
