@@ -740,7 +740,7 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             mgemm<CS, DH, CS>([&](int m, int k) { return row4(c.Tm, m, k); }, [&](int k, int n) { return col4(c.X, k, n); },
                                    [&](int m, int n, float v) { c.U[m][n] = v; });
             __syncthreads();
-            // dU += A^T dO;  dKb = U dS^T;  dgam = rowsum(dS * S);  dA = tril(dO U^T)
+            // dU += A^T dO;  dKb = U dS^T;  dgam = rowsum(dS * S)
             mgemm<CS, DH, CS>([&](int m, int k) { return col4(c.A, k, m); }, [&](int k, int n) { return col4(c.dO, k, n); },
                                    [&](int m, int n, float v) { c.dU[m][n] += v; });
             mgemm<CS, D, DH>([&](int m, int k) { return row4(c.U, m, k); }, [&](int k, int n) { return row4(dSb, n, k); },
@@ -755,8 +755,6 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
                 for (int o = NP / 2; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
                 if (pt == 0) gr.dgam[ch] = a;
             }
-            mgemm<CS, CS, DH>([&](int m, int k) { return row4(c.dO, m, k); }, [&](int k, int n) { return row4(c.U, n, k); },
-                                   [&](int m, int n, float v) { gr.dA[m][n] = n <= m ? v : 0.f; }, 7);
             __syncthreads();
             // fold dKb: dk = dKb exp(b_last - b);  db = -dKb Kb;  last row: sum_t dKb Kb + dgam gam
             float dKr[PER], dbr[PER];
@@ -772,9 +770,11 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
                 for (int r = 0; r < CS; ++r) a = __builtin_fmaf(gr.G[r][tid], c.Kb[r][tid], a);
                 gr.dlast[tid] = a;
             }
-            // dTm = dU X^T;  dX = Tm^T dU  (dv)
+            // dTm = dU X^T (wave 4);  dA = tril(dO U^T) (wave 5);  dX = Tm^T dU  (dv)
             mgemm<CS, CS, DH>([&](int m, int k) { return row4(c.dU, m, k); }, [&](int k, int n) { return row4(c.X, n, k); },
                                    [&](int m, int n, float v) { gr.dTm[m][n] = v; }, 4);
+            mgemm<CS, CS, DH>([&](int m, int k) { return row4(c.dO, m, k); }, [&](int k, int n) { return row4(c.U, n, k); },
+                                   [&](int m, int n, float v) { gr.dA[m][n] = n <= m ? v : 0.f; }, 5);
             mgemm<CS, DH, CS>([&](int m, int k) { return col4(c.Tm, k, m); }, [&](int k, int n) { return col4(c.dU, k, n); },
                                    [&](int m, int n, float v) { c.dX[m][n] = v; });
             __syncthreads();
