@@ -576,50 +576,44 @@ struct alignas(16) Grad {
     float G[CS][D + KP];      // one key-side gradient at a time (dKb, dQg, dKg, dKh), then db
     float P[D][DH + VP];       // state / state-gradient tiles of the current chunk (this value half):
     float Q[D][DH + VP];       // which is which depends on the chunk, see the kernel
-    float dA[CS][CS + SP], dTm[CS][CS + SP], dN[CS][CS + SP], dM[CS][CS + SP], T1[CS][CS + SP];
+    float dA[CS][CS + SP], dTm[CS][CS + SP], dM[CS][CS + SP];
     float dgam[D], dlast[D];
     float dbeta[CS];
 };
 
-// Order among the lanes of one wave: its LDS operations run in issue order, so keeping the compiler
-// from moving them across this point is enough.
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// On one wave (lane 0..63, the last wave of the workgroup): dN = dTm Diag(beta);
-// dbeta = colsum(N * dTm);  dM = -N^T dN N^T;  dbeta += rowsum(dM * L);  dL = tril(Diag(beta) dM, -1),
-// kept in dM.
+// On one wave (lane 0..63): dN = dTm Diag(beta);  dbeta = colsum(N * dTm);  dM = -N^T dN N^T;
+// dbeta += rowsum(dM * L);  dL = tril(Diag(beta) dM, -1), kept in dM.  In registers: the first
+// product is formed transposed, T1^T = dN^T N, so that its accumulator (lane (l16, g) holds rows
+// 4g..4g+3 of column l16) is the B operand of the second, dM^T = -N T1^T, whose accumulator then holds
+// row l16 of dM, columns 4g..4g+3; the row and column sums reduce over the four lane groups.
 template <int D>
 __device__ __forceinline__ void dl_chain(Chunk<D>& c, Grad<D>& gr, int lane) {
-    constexpr int W = NT / 64 - 1;
+    static_assert(CS == 16, "one 16 x 16 tile");
+    const int l16 = lane & 15, g = lane >> 4, k = 4 * g;
+    const f32x4 dtm = col4(gr.dTm, k, l16), nc = col4(c.N, k, l16);  // rows 4g.. of column l16
+    const float bl = c.beta[l16];
+    f32x4 t = {0.f, 0.f, 0.f, 0.f}, d = t;
 #pragma unroll
-    for (int e = lane; e < CS * CS; e += 64) gr.dN[e / CS][e % CS] = gr.dTm[e / CS][e % CS] * c.beta[e % CS];
-    if (lane < CS) {
-        float a = 0.f;
-        for (int r = 0; r < CS; ++r) a = __builtin_fmaf(c.N[r][lane], gr.dTm[r][lane], a);
-        gr.dbeta[lane] = a;
-    }
-    wave_sync();
-    mgemm_w<CS, CS, CS, W, 1>([&](int m, int k) { return col4(c.N, k, m); }, [&](int k, int n) { return col4(gr.dN, k, n); },
-                              [&](int m, int n, float v) { gr.T1[m][n] = v; });
-    wave_sync();
-    mgemm_w<CS, CS, CS, W, 1>([&](int m, int k) { return row4(gr.T1, m, k); }, [&](int k, int n) { return row4(c.N, n, k); },
-                              [&](int m, int n, float v) { gr.dM[m][n] = -v; });
-    wave_sync();
-    if (lane < CS) {
-        float a = 0.f;
-        for (int q = 0; q < CS; ++q) a = __builtin_fmaf(gr.dM[lane][q], c.L[lane][q], a);
-        gr.dbeta[lane] += a;
-    }
-    wave_sync();
+    for (int r = 0; r < 4; ++r) t = __builtin_amdgcn_mfma_f32_16x16x4f32(dtm[r] * bl, nc[r], t, 0, 0, 0);
+    const f32x4 nr = row4(c.N, l16, k);
 #pragma unroll
-    for (int e = lane; e < CS * CS; e += 64) {
-        const int r = e / CS, q = e % CS;
-        gr.dM[r][q] = q < r ? c.beta[r] * gr.dM[r][q] : 0.f;
+    for (int r = 0; r < 4; ++r) d = __builtin_amdgcn_mfma_f32_16x16x4f32(nr[r], t[r], d, 0, 0, 0);
+    // d[r] = -dM[l16][4g + r]
+    const f32x4 lr = row4(c.L, l16, k);
+    float cs = 0.f, rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        cs = __builtin_fmaf(nc[r], dtm[r], cs);  // column l16 of N * dTm, rows 4g..
+        rs = __builtin_fmaf(-d[r], lr[r], rs);   // row l16 of dM * L, columns 4g..
     }
+    float a = cs + rs;
+    a += __shfl_xor(a, 16, 64);
+    a += __shfl_xor(a, 32, 64);
+    if (g == 0) gr.dbeta[l16] = a;
+    f32x4 dl;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dl[r] = k + r < l16 ? -bl * d[r] : 0.f;
+    *reinterpret_cast<f32x4*>(&gr.dM[l16][k]) = dl;
 }
 
 // This thread's entries e = tid + NT*k of the value-half tile src[r][col0 + j] (r = e / DH,
