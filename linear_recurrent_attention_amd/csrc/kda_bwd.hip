@@ -799,13 +799,13 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             mgemm<CS, DH, CS>([&](int m, int k) { return col4(c.Tm, k, m); }, [&](int k, int n) { return col4(c.dU, k, n); },
                                    [&](int m, int n, float v) { c.dX[m][n] = v; });
             __syncthreads();
-            // the dTm -> dL chain on wave 7 alone, beside dQg = dO S^T + dA Kh on waves 0-3 (then
+            // the dTm -> dL chain on wave 7, then dQg = dO S^T + dA Kh on all waves (then
             // dq = dQg scale Gamma, Qg holding the scale, and db += dQg Qg)
             if (tid >= NT - 64) dl_chain(c, gr, tid & 63);
-            mgemm_w<CS, D, DH, 0, 4>([&](int m, int k) { return row4(c.dO, m, k); }, [&](int k, int n) { return row4(Sb, n, k); },
-                                     [&](int m, int n, float v) { gr.G[m][n] = v; });
-            mgemm_w<CS, D, CS, 0, 4>([&](int m, int k) { return row4(gr.dA, m, k); }, [&](int k, int n) { return col4(c.Kh, k, n); },
-                                     [&](int m, int n, float v) { gr.G[m][n] += v; });
+            mgemm<CS, D, DH>([&](int m, int k) { return row4(c.dO, m, k); }, [&](int k, int n) { return row4(Sb, n, k); },
+                             [&](int m, int n, float v) { gr.G[m][n] = v; });
+            mgemm<CS, D, CS>([&](int m, int k) { return row4(gr.dA, m, k); }, [&](int k, int n) { return col4(c.Kh, k, n); },
+                             [&](int m, int n, float v) { gr.G[m][n] += v; });
             __syncthreads();
             const int n_ok = min(CS, p.T - c0);
             auto grow = [&](int r) { return ((size_t)b * p.T + c0 + r) * p.H + h; };
