@@ -335,6 +335,48 @@ __device__ __forceinline__ void state_grad_step(const TQ& Qg, const TQ& Kg, cons
     }
 }
 
+// dst(m, n) = gam(m) src(m, n) + (Kb^T U)(m, n): the state after a chunk from the state before it, in
+// the same tile order and (SPLIT) the same split-bf16 products as state_grad_step.
+template <int D, bool SPLIT, typename TK, typename TU, typename TS>
+__device__ __forceinline__ void state_fwd_step(const TK& Kb, const TU& U, const float* gam, const TS& src, TS& dst) {
+    static_assert(CS == 16, "one block of four contraction indices per lane group");
+    constexpr int DH = D / 2, TN = DH / 16, NW = NT / 64, TM = D / 16;
+    static_assert(NW % TN == 0, "column blocks per wave");
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l16 = lane & 15, g = lane >> 4, k = 4 * g, n0 = 16 * (wave % TN);
+    const f32x4 bu = col4(U, k, n0 + l16);
+    u32x2 buh, bul;
+    if constexpr (SPLIT) {
+        uint32_t h0, h1, l0, l1;
+        split_bf16(bu[0], bu[1], h0, l0);
+        split_bf16(bu[2], bu[3], h1, l1);
+        buh = u32x2{h0, h1};
+        bul = u32x2{l0, l1};
+    }
+    for (int mb = wave / TN; mb < TM; mb += NW / TN) {
+        const int m0 = 16 * mb;
+        const f32x4 ak = col4(Kb, k, m0 + l16);
+        f32x4 pu = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (SPLIT) {
+            uint32_t h0, h1, l0, l1;
+            split_bf16(ak[0], ak[1], h0, l0);
+            split_bf16(ak[2], ak[3], h1, l1);
+            const u32x2 akh{h0, h1}, akl{l0, l1};
+            pu = mfma_bf16_k16(akh, buh, pu);
+            pu = mfma_bf16_k16(akh, bul, pu);
+            pu = mfma_bf16_k16(akl, buh, pu);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pu = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bu[r], pu, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + 4 * g + r, n = n0 + l16;
+            dst[m][n] = __builtin_fmaf(gam[m], src[m][n], pu[r]);
+        }
+    }
+}
+
 // L = tril(Kg Kh^T, -1) on wave W and A = tril(Qg Kh^T) on wave W + 1 (one 16 x 16 tile each).
 template <int D, int W, typename CT>
 __device__ __forceinline__ void gram_products(CT& c) {
@@ -726,8 +768,7 @@ __global__ void __launch_bounds__(NT) kda_bwd_chunk_kernel(BwdParams p) {
             mgemm<CS, DH, CS>([&](int m, int k) { return row4(c.Tm, m, k); }, [&](int k, int n) { return col4(c.X, k, n); },
                                    [&](int m, int n, float v) { c.U[m][n] = v; });
             __syncthreads();
-            mgemm<D, DH, CS>([&](int m, int k) { return col4(c.Kb, k, m); }, [&](int k, int n) { return col4(c.U, k, n); },
-                                  [&](int m, int n, float v) { gr.Q[m][n] = __builtin_fmaf(c.gam[m], gr.P[m][n], v); });
+            state_fwd_step<D, IN_BF16>(c.Kb, c.U, c.gam, gr.P, gr.Q);
             __syncthreads();
             put_state<D>(gr.P, dsr);
         } else {
