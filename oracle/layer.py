@@ -21,8 +21,11 @@ with tap 3 on the current token and tap 0 on the token three steps back.
 The conv window state is [B, 3, 2*H*Dk] (q channels, then k channels; oldest
 token first).
 
-Parity status: pinned (each piece against a library routine or a closed form,
-the recurrence as pinned in the package).
+Parity status: pinned.  The composition against a hand-worked example
+(tests/golden/kda_layer_hand_example.json: T=4, two heads, nonzero conv taps,
+A and b_alpha nonzero, evaluated element by element at 40 digits), each piece
+against a library routine or a closed form, the recurrence as pinned in the
+package.
 """
 from __future__ import annotations
 

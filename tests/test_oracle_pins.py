@@ -314,3 +314,64 @@ def test_layer_zero_gate_weight_halves():
     on = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + L.EPS)
     want = 0.5 * on.reshape(2, 24, -1) @ p["Wo"].astype(np.float64)
     np.testing.assert_allclose(y0, want, rtol=1e-12, atol=1e-12)
+
+
+# -- the layer's composition against a hand-worked example ------------------------------------------------
+
+def _hand_layer():
+    ex = json.load(open(os.path.join(GOLD, "kda_layer_hand_example.json")))
+    inp = {n: np.array(a, np.float64) for n, a in ex["inputs"].items()}
+    x = inp.pop("x")[None]
+    return ex, x, inp
+
+
+def test_layer_hand_worked_example():
+    """oracle.layer.forward against a T=4, H=2 layer worked element by element at 40 digits: pins the order
+    conv -> SiLU -> per-head L2, z = W_up W_down x + b_alpha -> -5 sigmoid(e^A z), beta = sigmoid(x W_beta),
+    and RMSNorm * sigmoid(x W_g) @ W_o (sections 2.3, 2.4, 3.2, 3.3 of the explainer page)."""
+    ex, x, p = _hand_layer()
+    y, ST, _, parts = L.forward(x, p, return_parts=True)
+    w = ex["working"]
+    np.testing.assert_allclose(parts["q"][0].reshape(4, -1), w["q"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(parts["k"][0].reshape(4, -1), w["k"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(parts["g"][0].reshape(4, -1), w["g"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(parts["beta"][0], w["beta"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(parts["o"][0].reshape(4, -1), w["o"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(y[0], ex["y"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(ST[0], ex["S_T"], rtol=0, atol=1e-13)
+
+
+def _planted(monkeypatch, mistake):
+    """Run the layer oracle with one plausible mistake planted in it (on the CPU) and return y."""
+    ex, x, p = _hand_layer()
+    if mistake == "silu_after_l2":
+        real_l2 = L.l2norm
+        monkeypatch.setattr(L, "silu", lambda u: u)
+        monkeypatch.setattr(L, "l2norm", lambda u, eps=L.EPS: (lambda n: n * L.sigmoid(n))(real_l2(u, eps)))
+    elif mistake == "l2_over_all_heads":
+        real_l2 = L.l2norm
+        monkeypatch.setattr(L, "l2norm", lambda u, eps=L.EPS: real_l2(u.reshape(*u.shape[:-2], -1), eps).reshape(u.shape))
+    elif mistake == "bias_outside_gate_scale":  # -5 sigmoid(e^A (W_up W_down x) + b) instead of e^A (... + b)
+        b = p["b_alpha"].reshape(2, 2)
+        p = dict(p, b_alpha=np.zeros_like(p["b_alpha"]))
+        monkeypatch.setattr(L, "decay_gate", lambda z, A: -5.0 / (1.0 + np.exp(-(np.exp(A)[:, None] * z + b))))
+    elif mistake == "beta_without_sigmoid":
+        real_sig = L.sigmoid
+        calls = []
+        def sig(u):  # the first sigmoid forward() takes is beta's
+            calls.append(1)
+            return u if len(calls) == 1 else real_sig(u)
+        monkeypatch.setattr(L, "sigmoid", sig)
+    elif mistake == "gate_before_rmsnorm":
+        real_rms = L.rmsnorm
+        monkeypatch.setattr(L, "rmsnorm", lambda u, w, eps=L.EPS: u * w)
+    y, _, _ = L.forward(x, p)
+    return ex, y
+
+
+@pytest.mark.parametrize("mistake", ["silu_after_l2", "l2_over_all_heads", "bias_outside_gate_scale",
+                                     "beta_without_sigmoid", "gate_before_rmsnorm"])
+def test_layer_hand_example_rejects_planted_mistakes(monkeypatch, mistake):
+    """Each plausible misreading of the layer, planted in the oracle, moves y off the hand-worked values."""
+    ex, y = _planted(monkeypatch, mistake)
+    assert np.abs(y[0] - np.array(ex["y"])).max() > 1e-3
