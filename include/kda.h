@@ -12,7 +12,8 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent), owned by the caller.
- *     The library allocates no device memory in kda_fwd.
+ *     The library allocates no device memory in kda_fwd; a call that needs scratch memory takes
+ *     it from a caller workspace, sized by the query beside it.
  *   - Calls are asynchronous and ordered on `stream` (NULL = the default stream).  The return code
  *     covers argument validation and launch errors only; a fault inside a kernel surfaces at the
  *     caller's next synchronisation.
@@ -46,12 +47,19 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 typedef struct {
     int B, T, H;        /* batch, tokens, heads; B, H >= 1, T >= 0 */
     int Dk, Dv;         /* key / value head size.  bf16 I/O: Dk = Dv = 128.  f32 I/O: Dk = Dv in {64, 128} */
-    int chunk;          /* tokens per chunk of the chunkwise form; 0 = library default.
-                           Supported: 32 for bf16 I/O (two 16-token sub-tiles), 16 for f32 I/O. */
+    int chunk;          /* tokens per chunk of the chunkwise form that the caller asks for: 0 (library
+                           default) or a multiple of the kernel's chunk up to 64, i.e. 32 or 64 for bf16
+                           I/O and 16, 32, 48 or 64 for f32 I/O.  The kernels always block by their own
+                           chunk (bf16: 32 tokens as two 16-token sub-tiles, so a decay reference inside
+                           the chunk keeps every factor within float32 range; f32: 16); the chunkwise
+                           form (section 2.5) gives the same result for any chunk length in exact
+                           arithmetic, so a request for 64 is served by that blocking.  Other values
+                           are KDA_ERR_UNSUPPORTED. */
     kda_dtype io_dtype; /* dtype of q, k, v */
     kda_dtype o_dtype;  /* dtype of o: io_dtype, or KDA_F32 with bf16 inputs (diagnostic output) */
     float scale;        /* o_t = S_t^T (scale * q_t); 1.0 reads the state with q as given */
-    int flags;          /* 0 or KDA_FWD_PRECISE; other bits are reserved and must be 0 */
+    int flags;          /* KDA_FWD_PRECISE and/or KDA_VALIDATE (kda_fwd only); other bits are reserved
+                           and must be 0 */
 } kda_fwd_desc;
 
 /* kda_fwd_desc.flags: bf16 I/O only (the f32 path computes in float32 throughout and ignores it).
@@ -60,6 +68,15 @@ typedef struct {
  * Swish activation), which makes I + Diag(beta) L ill-conditioned and amplifies rounding in S_T;
  * costs about 10% of throughput. */
 #define KDA_FWD_PRECISE 1
+
+/* kda_fwd_desc.flags, kda_fwd only: check the inputs before computing (a debug mode).  A device
+ * pass scans g for values outside the section 3.2 bound [-5, 0] (NaN included; the kernels rely on
+ * the bound to keep their decay factors finite) and q, k, v, beta and S0 for non-finite values;
+ * any finding makes kda_fwd return KDA_ERR_INVALID_ARG without launching the forward.  The pass
+ * writes one flag word into the workspace (kda_fwd_workspace_size gives its size) and
+ * synchronises `stream` to read it, so this mode is not asynchronous and cannot be captured into a
+ * graph. */
+#define KDA_VALIDATE 2
 
 /*
  * kda_fwd -- forward pass of the gated delta rule over B*H independent sequences.
@@ -72,6 +89,8 @@ typedef struct {
  *   S0     : [B, H, Dk, Dv] float32    initial state (rows = key channels), or NULL for zeros
  *   o      : [B, T, H, Dv]  o_dtype    output
  *   S_T    : [B, H, Dk, Dv] float32    final state, or NULL to skip it; may equal S0
+ *   ws     : device workspace of at least kda_fwd_workspace_size(desc) bytes, 256-byte aligned; NULL
+ *            when that size is 0 (the plain forward needs none); contents are scratch
  *
  * Pointer alignment: q, k, v, o 4-byte aligned; g, beta, S0, S_T 8-byte aligned.
  * bf16 path numerics: intermediate products use bf16/f16 matrix-core operands with float32
@@ -79,11 +98,12 @@ typedef struct {
  * KDA_FWD_PRECISE); the state is float32.
  * The value path uses f16 operands, so |v| and the state entries must stay below 6.5e4;
  * beyond that o and S_T become non-finite.
- * Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP.
+ * Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE or KDA_ERR_HIP.
  */
+size_t kda_fwd_workspace_size(const kda_fwd_desc* desc);  /* 256 with KDA_VALIDATE, else 0 (NULL desc: 0) */
 kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const void* v,
                    const float* g, const float* beta, const float* S0,
-                   void* o, float* S_T, hipStream_t stream);
+                   void* o, float* S_T, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * kda_fwd_ckpt -- kda_fwd that also records the state at regular token boundaries: the KDA half of

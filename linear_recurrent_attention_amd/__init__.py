@@ -23,7 +23,7 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, chunk, precise, scale):
+def _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, chunk, precise, scale, validate=False):
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     for t in (q, k, v, g, beta):
@@ -44,21 +44,29 @@ def _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, chunk, 
         ST = state_out if state_out is not None else torch.empty((B, H, Dk, Dv), dtype=torch.float32,
                                                                  device=q.device)
     desc = _lib.FwdDesc(B, T, H, Dk, Dv, chunk, _DT[q.dtype], _DT[o_dtype], float(scale),
-                        _lib.KDA_FWD_PRECISE if precise else 0)
+                        (_lib.KDA_FWD_PRECISE if precise else 0) | (_lib.KDA_VALIDATE if validate else 0))
     return desc, o, ST
 
 
 def kda_fwd(q, k, v, g, beta, S0=None, scale: float = 1.0, o_dtype=None, want_state: bool = True,
-            out=None, state_out=None, chunk: int = 0, precise: bool = False):
+            out=None, state_out=None, chunk: int = 0, precise: bool = False, validate: bool = False,
+            workspace=None):
     """Gated delta rule forward.  Shapes: q, k, g [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H];
     S0 [B,H,Dk,Dv] float32 or None.  q, k, v float32 or bfloat16; g, beta float32.
     precise: split-bf16 key Gram matrix and state update on the bf16 path (KDA_FWD_PRECISE).
+    validate: check g in [-5, 0] and finite inputs first (KDA_VALIDATE; synchronises the stream and
+    raises KdaError with KDA_ERR_INVALID_ARG on a finding).
 
     Returns (o [B,T,H,Dv], S_T [B,H,Dk,Dv] float32 or None).
     """
-    desc, o, ST = _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, chunk, precise, scale)
+    desc, o, ST = _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, chunk, precise, scale,
+                            validate)
+    need = _lib.fwd_workspace_size(desc)
+    ws = workspace
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     code = _lib.fwd_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(ST),
-                        _stream(q.device))
+                        _stream(q.device), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size())
     _lib.check(code)
     return o, ST
 

@@ -16,9 +16,10 @@ KDA_ERR_WORKSPACE = -4
 KDA_F32 = 0
 KDA_BF16 = 1
 KDA_FWD_PRECISE = 1  # kda_fwd_desc.flags
+KDA_VALIDATE = 2
 
 # every symbol include/kda.h declares
-EXPORTS = ("kda_fwd", "kda_fwd_ckpt", "kda_decode", "kda_fwd_cp_workspace_size", "kda_fwd_cp",
+EXPORTS = ("kda_fwd_workspace_size", "kda_fwd", "kda_fwd_ckpt", "kda_decode", "kda_fwd_cp_workspace_size", "kda_fwd_cp",
            "kda_bwd_workspace_size", "kda_bwd", "kda_layer_workspace_size", "kda_layer_fwd", "kda_error_string", "kda_version")
 
 
@@ -66,7 +67,9 @@ def lib():
                 raise ImportError(f"{LIB_PATH} is missing: build it with `python -m linear_recurrent_attention_amd.build`")
             L = ctypes.CDLL(LIB_PATH)
             L.kda_fwd.restype = ctypes.c_int
-            L.kda_fwd.argtypes = [ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 9
+            L.kda_fwd.argtypes = [ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p]
+            L.kda_fwd_workspace_size.restype = ctypes.c_size_t
+            L.kda_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdDesc)]
             L.kda_fwd_cp_workspace_size.restype = ctypes.c_size_t
             L.kda_fwd_cp_workspace_size.argtypes = [ctypes.POINTER(FwdDesc), ctypes.c_int]
             L.kda_fwd_cp.restype = ctypes.c_int
@@ -110,9 +113,13 @@ def layer_fwd_raw(desc: LayerDesc, x, weights: LayerWeights, S0, conv_in, y, S_T
                                ws_bytes, stream)
 
 
-def fwd_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, stream) -> int:
+def fwd_workspace_size(desc: FwdDesc) -> int:
+    return lib().kda_fwd_workspace_size(ctypes.byref(desc))
+
+
+def fwd_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, stream, ws=0, ws_bytes=0) -> int:
     """Call kda_fwd with integer device addresses (0 = NULL); returns the status code."""
-    return lib().kda_fwd(ctypes.byref(desc), q, k, v, g, beta, S0, o, S_T, stream)
+    return lib().kda_fwd(ctypes.byref(desc), q, k, v, g, beta, S0, o, S_T, ws, ws_bytes, stream)
 
 
 def fwd_ckpt_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, S_ckpt, every, stream) -> int:

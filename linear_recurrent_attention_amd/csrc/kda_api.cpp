@@ -10,10 +10,11 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // Checks shared by the forward entry points: sizes, dtypes, pointers, alignment, aliasing.
 kda_status check_common(const kda_fwd_desc* d, const void* q, const void* k, const void* v, const float* g,
-                        const float* beta, const float* S0, const void* o, const float* S_T, bool need_o = true) {
+                        const float* beta, const float* S0, const void* o, const float* S_T, bool need_o = true,
+                        int allowed_flags = KDA_FWD_PRECISE) {
     if (!d) return KDA_ERR_INVALID_ARG;
     if (d->B < 1 || d->H < 1 || d->T < 0 || d->Dk < 1 || d->Dv < 1) return KDA_ERR_INVALID_ARG;
-    if (d->flags & ~KDA_FWD_PRECISE) return KDA_ERR_INVALID_ARG;
+    if (d->flags & ~allowed_flags) return KDA_ERR_INVALID_ARG;
     if (d->io_dtype != KDA_F32 && d->io_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
     if (d->o_dtype != KDA_F32 && d->o_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
     if (d->io_dtype == KDA_F32 && d->o_dtype != KDA_F32) return KDA_ERR_INVALID_ARG;
@@ -28,19 +29,29 @@ kda_status check_common(const kda_fwd_desc* d, const void* q, const void* k, con
     return KDA_OK;
 }
 
+// The chunk a request names is served by the kernel's own blocking (32 tokens on the bf16 path, 16 on
+// the float32 path): the chunkwise form gives the same result for any chunk length in exact
+// arithmetic, so a request for a multiple of the kernel's chunk, up to 64, is accepted.
+bool chunk_ok(const kda_fwd_desc* d, int kernel_chunk) {
+    return d->chunk == 0 || (d->chunk >= kernel_chunk && d->chunk <= 64 && d->chunk % kernel_chunk == 0);
+}
+
 kda_status check_fwd(const kda_fwd_desc* d, const void* q, const void* k, const void* v, const float* g,
-                     const float* beta, const float* S0, const void* o, const float* S_T) {
-    const kda_status st = check_common(d, q, k, v, g, beta, S0, o, S_T);
+                     const float* beta, const float* S0, const void* o, const float* S_T,
+                     int allowed_flags = KDA_FWD_PRECISE) {
+    const kda_status st = check_common(d, q, k, v, g, beta, S0, o, S_T, true, allowed_flags);
     if (st != KDA_OK) return st;
     if (d->io_dtype == KDA_BF16) {
         if (d->Dk != 128 || d->Dv != 128) return KDA_ERR_UNSUPPORTED;
-        if (d->chunk != 0 && d->chunk != 32) return KDA_ERR_UNSUPPORTED;
+        if (!chunk_ok(d, 32)) return KDA_ERR_UNSUPPORTED;
     } else {
         if (d->Dk != d->Dv || (d->Dk != 64 && d->Dk != 128)) return KDA_ERR_UNSUPPORTED;
-        if (d->chunk != 0 && d->chunk != 16) return KDA_ERR_UNSUPPORTED;
+        if (!chunk_ok(d, 16)) return KDA_ERR_UNSUPPORTED;
     }
     return KDA_OK;
 }
+
+constexpr size_t kValidateWs = 256;  // one flag word, padded to the workspace alignment
 
 kda_status check_decode(const kda_fwd_desc* d, const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const float* S0, const void* o, const float* S_T) {
@@ -81,10 +92,28 @@ kda_status run_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const
 
 extern "C" {
 
+size_t kda_fwd_workspace_size(const kda_fwd_desc* desc) {
+    return (desc && (desc->flags & KDA_VALIDATE)) ? kValidateWs : 0;
+}
+
 kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
-                   const float* beta, const float* S0, void* o, float* S_T, hipStream_t stream) {
-    const kda_status st = check_fwd(desc, q, k, v, g, beta, S0, o, S_T);
+                   const float* beta, const float* S0, void* o, float* S_T, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+    const kda_status st = check_fwd(desc, q, k, v, g, beta, S0, o, S_T, KDA_FWD_PRECISE | KDA_VALIDATE);
     if (st != KDA_OK) return st;
+    if ((desc->flags & KDA_VALIDATE) && desc->T > 0) {
+        if (!ws || ws_bytes < kValidateWs || !aligned(ws, 256)) return KDA_ERR_WORKSPACE;
+        kda::Params p{};
+        p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0;
+        p.B = desc->B; p.T = desc->T; p.H = desc->H; p.Dk = desc->Dk; p.Dv = desc->Dv;
+        uint32_t* flag = static_cast<uint32_t*>(ws);
+        if (kda::launch_validate(p, desc->io_dtype == KDA_BF16, flag, stream) != hipSuccess) return KDA_ERR_HIP;
+        uint32_t found = 0;
+        if (hipMemcpyAsync(&found, flag, sizeof(found), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+            return KDA_ERR_HIP;
+        if (found) return KDA_ERR_INVALID_ARG;
+    }
     return run_fwd(desc, q, k, v, g, beta, S0, o, S_T, nullptr, 0, stream);
 }
 

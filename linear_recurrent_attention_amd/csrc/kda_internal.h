@@ -1,6 +1,7 @@
 // Internal interface between the C-ABI entry points and the kernel launchers.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace kda {
 
@@ -52,6 +53,9 @@ struct BwdParams {
 hipError_t launch_fwd_bf16(const Params& p, hipStream_t stream);  // Dk = Dv = 128, chunk 32 (in_f32 too)
 hipError_t launch_fwd_f32(const Params& p, hipStream_t stream);   // Dk = Dv in {64, 128}, chunk 16
 hipError_t launch_state_copy(const Params& p, hipStream_t stream); // T = 0: S_T = S0 (or 0)
+// input checks of KDA_VALIDATE: clears *flags, then ORs in VALIDATE_* bits (device word, stream-ordered)
+enum : uint32_t { VALIDATE_G_RANGE = 1u, VALIDATE_NONFINITE = 2u };
+hipError_t launch_validate(const Params& p, bool in_bf16, uint32_t* flags, hipStream_t stream);
 hipError_t launch_decode(const Params& p, bool in_bf16, hipStream_t stream);  // token by token, Dk = Dv in {64, 128}
 // in-device context parallelism (bf16 I/O, Dk = Dv = 128): segment count nseg_req (0 = automatic)
 size_t cp_workspace_bytes(int B, int T, int H, int nseg_req);

@@ -52,10 +52,10 @@ def call(d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=0, o=FAKE + 0x100000, 
 
 
 def test_null_descriptor():
-    assert _lib.lib().kda_fwd(None, *([None] * 9)) == _lib.KDA_ERR_INVALID_ARG
+    assert _lib.lib().kda_fwd(None, *([None] * 9), 0, None) == _lib.KDA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("field,value", [("B", 0), ("H", 0), ("T", -1), ("Dk", 0), ("Dv", -3), ("flags", 2), ("flags", -1),
+@pytest.mark.parametrize("field,value", [("B", 0), ("H", 0), ("T", -1), ("Dk", 0), ("Dv", -3), ("flags", 4), ("flags", -1),
                                          ("io_dtype", 5), ("o_dtype", 9)])
 def test_bad_sizes_and_enums(field, value):
     assert call(desc(**{field: value})) == _lib.KDA_ERR_INVALID_ARG
@@ -86,11 +86,45 @@ def test_misaligned_pointer(ptr, off):
     assert call(desc(), **{ptr: FAKE + 0x20000 + off}) == _lib.KDA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kw", [dict(Dk=64, Dv=64), dict(Dk=128, Dv=64), dict(chunk=64),
+@pytest.mark.parametrize("kw", [dict(Dk=64, Dv=64), dict(Dk=128, Dv=64), dict(chunk=16), dict(chunk=48),
+                                dict(chunk=96), dict(chunk=-32),
                                 dict(io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_F32, Dk=96, Dv=96),
-                                dict(io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_F32, Dk=64, Dv=64, chunk=32)])
+                                dict(io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_F32, Dk=64, Dv=64, chunk=24),
+                                dict(io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_F32, Dk=64, Dv=64, chunk=128)])
 def test_unsupported_shapes(kw):
     assert call(desc(**kw)) == _lib.KDA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("io,chunk", [(_lib.KDA_BF16, 32), (_lib.KDA_BF16, 64), (_lib.KDA_F32, 16),
+                                      (_lib.KDA_F32, 32), (_lib.KDA_F32, 64)])
+def test_chunk_requests_served_by_kernel_blocking(io, chunk):
+    # the workloads' C = 64 (and any multiple of the kernel's own chunk up to 64) is a valid request
+    d = desc(T=0, chunk=chunk, io_dtype=io, o_dtype=io, Dk=64 if io == _lib.KDA_F32 else 128,
+             Dv=64 if io == _lib.KDA_F32 else 128)
+    assert _lib.fwd_raw(d, 0, 0, 0, 0, 0, 0, 0, 0, None) == _lib.KDA_OK
+
+
+def test_workspace_size_query():
+    assert _lib.fwd_workspace_size(desc()) == 0
+    assert _lib.fwd_workspace_size(desc(flags=_lib.KDA_FWD_PRECISE)) == 0
+    assert _lib.fwd_workspace_size(desc(flags=_lib.KDA_VALIDATE)) == 256
+    assert _lib.lib().kda_fwd_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("ws,ws_bytes", [(0, 0), (0, 256), (FAKE + 0x300000, 255), (FAKE + 0x300000 + 16, 256)])
+def test_validate_needs_its_workspace(ws, ws_bytes):
+    # missing, too small or misaligned workspace: rejected before any device call
+    d = desc(flags=_lib.KDA_VALIDATE)
+    assert _lib.fwd_raw(d, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE + 0x100000, 0, None, ws, ws_bytes) == \
+        _lib.KDA_ERR_WORKSPACE
+
+
+def test_validate_flag_only_on_kda_fwd():
+    d = desc(flags=_lib.KDA_VALIDATE)
+    assert _lib.fwd_ckpt_raw(d, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE + 0x100000, 0, FAKE + 0x200000, 32, None) == \
+        _lib.KDA_ERR_INVALID_ARG
+    assert _lib.decode_raw(desc(flags=_lib.KDA_VALIDATE, chunk=0), FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE + 0x100000,
+                           0, None) == _lib.KDA_ERR_INVALID_ARG
 
 
 def test_output_aliasing_input_rejected():
