@@ -30,18 +30,21 @@
 // Mapping.  One workgroup per (batch, head, value half): the 128 value columns are split over two
 // workgroups that both compute the key-side products, so 2*B*H workgroups fill the chip; the two
 // halves of a head are placed on the same XCD so their common reads of q, k, g share its L2.
-// Each workgroup runs 12 waves as a two-stage pipeline over chunks:
-//   key waves 0-7    chunk n:   wave kw owns tokens 4kw..4kw+3 (two key channels per lane): quad
-//                               decay sums, then all decay factors and operand tiles, then the Gram
-//                               products (waves 0-3); the chunk's Kbar^T tile is written at the
-//                               start of the next step from factors kept in registers;
-//   value waves 8-11 chunk n-1: UT inverse, then the state-dependent products and the output, then
-//                               the state update; wave 8+w owns 16 value columns of the float32
-//                               state in matrix-core accumulator layout for the whole run, and loads
-//                               its own values of v one chunk ahead.
-// Both groups execute the same three workgroup barriers per step; data passes from the key waves
-// to the value waves through LDS buffers indexed by chunk parity.
-//
+// Each workgroup runs 16 waves, four per SIMD, in three roles:
+//   key waves 0-7     wave kw owns tokens 4kw..4kw+3 of a chunk (two key channels per lane): decay
+//                     sums, exponentials and operand tiles, two chunks ahead of the value waves;
+//                     the A Gram products (six half-sums) and Kbar^T one chunk ahead;
+//   value waves 8-11  wave 8+w owns 16 value columns of the float32 state (all 128 rows) in
+//                     matrix-core accumulator layout for the whole run: the products with the state,
+//                     U, the output and the state update of one chunk per step;
+//   helper waves 12-15  the L Gram products, the UT inverse and A from its half-sums, one chunk ahead;
+//                     the v loads of the value waves (staged through LDS).
+// A step has three parts separated by workgroup barriers.  A single wave issues at most one vector
+// instruction every ~9 clocks on gfx950, while a SIMD shared by four waves issues one every ~2.5;
+// the parts are laid out so that each SIMD always has its four waves' work to interleave, and the
+// value waves, which carry the serial chain, issue at a raised priority.  Tiles pass between roles
+// through LDS, double buffered by chunk parity (the state scalings by chunk index mod 3).
+
 // Matrix-core operands (v_mfma_f32_16x16x32_bf16 and 16x16x16, float32 accumulate; "split" is
 // hi = bf16(x), lo = bf16(x - hi), products hi*hi + hi*lo + lo*hi):
 //   L = Km Kh^T         bf16 (PRECISE: Kh split)       A = Qm Kh^T        split
@@ -65,7 +68,9 @@ constexpr int DV = 128;
 constexpr int DVH = 64;     // value columns per workgroup
 constexpr int NKW = 8;      // key waves, one 4-token quad of the chunk each
 constexpr int TPW = C / NKW; // tokens per key wave
-constexpr int NTHR = 64 * (NKW + 4);  // and 4 value waves, 16 value columns each
+constexpr int NVW = 4;      // value waves, 16 value columns (all 128 state rows) each
+constexpr int NHW = 4;      // helper waves
+constexpr int NTHR = 64 * (NKW + NVW + NHW);
 constexpr float kUp = 18446744073709551616.f;     // 2^64
 constexpr float kDown = 5.42101086242752217e-20f;  // 2^-64
 // LDS layouts.  A matrix-core operand read has lane (l16, g4) fetch 16 bytes from row r0 + l16 at
@@ -94,32 +99,39 @@ __device__ __forceinline__ constexpr int sw(int row, int col) { return col ^ (((
 // Token-major tiles store channels in cperm order, so that a 16-byte read of a row gives the eight
 // channels a lane contracts over in the state products (whose operand comes straight from the
 // accumulator layout of the state); the Gram products see the same order on both sides.
-struct alignas(16) KeyTiles {                // written and read by the key waves within one step
+struct alignas(16) KeyTiles {                // key waves (written in part 3, read in part 2 of the next step)
     uint16_t khh[C][LDK], khl[C][LDK];       // K * exp(b_15 - b)         split bf16
     float tot[DK / 2][LDQ];                  // per-quad sums of g (log decay): row = channel pair,
                                              // element 2*quad + (channel & 1)
 };
-struct alignas(16) ChunkTiles {              // key -> value, double buffered by chunk parity
+struct alignas(16) ChunkTiles {              // between roles, double buffered by chunk parity
     uint16_t qmh[C][LDK], qml[C][LDK];       // Q * exp(b - b_15)         split bf16
     uint16_t km[C][LDK];                     // K * exp(b - b_15)         bf16
     uint16_t kbh[DK][LDT], kbl[DK][LDT];     // (K * exp(b_31 - b))^T     split bf16, tokens tperm'd
     uint16_t ah[C][LDA], al[C][LDA];         // -2^64 A                   split bf16, columns tperm'd
+    uint16_t th[C][LDA], tl[C][LDA];         // 2^-64 T split bf16, columns tperm'd; block (1,0) holds
+                                             // 2^64 L(1,0)
+    float beta[C];
+};
+struct alignas(16) Scalings {                // state scalings of one chunk, by chunk index mod 3
     float ep[DK];                            // -2^64 exp(b_15)           row scale of the state operand
     float gam[DK];                           // exp(b_31)
 };
-struct alignas(16) Single {                  // key -> value, one buffer (written after the reader is done)
-    float lf[C][LDF];                        // -Diag(beta) L on the two diagonal blocks
-    float beta[C];
+struct alignas(16) VStage {                  // 2^64 v of one chunk, loaded by the helper waves for the value
+    float x[NVW][64][8];                     // waves: [value wave][lane][4R + r] = token 16R + 4*g4 + r of the
+                                             // lane's column (zero past T, or when v == NULL)
 };
-struct alignas(16) ValueTiles {              // value waves (the key waves write L'(1,0) here)
-    uint16_t th[C][LDA], tl[C][LDA];         // 2^-64 T split bf16, columns tperm'd; block (1,0) holds
-                                             // 2^64 L(1,0)
+struct alignas(16) Single {                  // written and read within one step
+    float lf[C][LDF];                        // -Diag(beta) L on the two diagonal blocks
+    float apart[6][4][64];                   // A: partial sums over channels 0-63 / 64-127 of its three
+                                             // 16x16 blocks, in accumulator layout [block, half][r][lane]
 };
 struct alignas(16) Smem {
     KeyTiles key;
     ChunkTiles ch[2];
+    Scalings sc[3];
+    VStage vs[2];                            // by chunk parity
     Single s;
-    ValueTiles val;
 };
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -222,21 +234,23 @@ __device__ __forceinline__ void mask_tail(Raw<IN_F32>& r, int T, int t0, int kw,
     if (t0 + TPW * kw + (lane % TPW) >= T) r.beta = 0.f;
 }
 
-// Factors of one chunk that its Kbar^T tile is made from, kept in registers from part 2 of one step
-// to part 1 of the next (the value waves read that tile only a step later).
+// Values of one chunk kept in registers across parts and steps by a key wave: the exponentials of
+// part 2 (used in part 3), and the factors its Kbar^T tile is made from (used in part 1 of the next
+// step).
 struct Carry {
-    float kh[TPW][2];          // K times exp(b_15 - b)
-    float eC[2];               // exp(b_31 - b_15)
-    float ep[2], gam[2];       // -2^64 exp(b_15), exp(b_31)
+    float e[TPW][2], f[TPW][2];  // exp(b - b_15), exp(b_15 - b)
+    float kh[TPW][2];            // K times exp(b_15 - b)
+    float eC[2];                 // exp(b_31 - b_15)
 };
 
 // Split x into bf16 hi + lo, packing the pair (a, b) into one word of each (a in the low half).
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) { split_bf16(a, b, hi, lo); }
 
 // ------------------------------------------------------------------------------------------------
-// key waves: one step = chunk n (nothing when n == nchunk); three barriers
+// key waves.  Step n forms the factors of chunk n+1, and the A Gram products and the Kbar^T tile of
+// chunk n.  Three barriers per step; steps n = -1 .. nchunk.
 // ------------------------------------------------------------------------------------------------
-template <bool IN_F32, bool HP>
+template <bool IN_F32>
 __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoad& kl, size_t row0, int n,
                                          int nchunk, Raw<IN_F32>& cur, Raw<IN_F32>& nxt, Carry& cy) {
     const int kw = kl.kw, lane = kl.lane;
@@ -244,23 +258,24 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
     const int c0 = 2 * lane;   // key channels c0, c0 + 1
     const int pc0 = cperm(c0); // (c0 even: c0 + 1 follows it)
     const int tq = TPW * kw;
-    const bool work = n < nchunk;
-    const int t0 = n * C;
+    const int nf = n + 1;                     // chunk whose factors this step forms
+    const bool fwork = nf < nchunk;
+    const bool gwork = n >= 0 && n < nchunk;  // chunk n: A Gram products and Kbar^T
+    const int t0 = nf * C;
     const int tn = min(t0 + C, (nchunk - 1) * C);  // the chunk prefetched this step (see load_chunk)
-    ChunkTiles& H = sm.ch[n & 1];
+    ChunkTiles& Hf = sm.ch[nf & 1];
+    ChunkTiles& Hg = sm.ch[n & 1];
 
-    // ---------------- part 1: decay sums over the quad; prefetch of the next chunk; the previous
-    // chunk's Kbar^T tile and its state scalings, which its value step reads
-    if (work) {
+    // ---------------- part 1: decay sums of chunk n+1 over the quad; prefetch; Kbar^T of chunk n
+    if (fwork) {
         if (t0 + C > p.T) mask_tail(cur, p.T, t0, kw, lane);
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) { a0 += cur.g[i][0]; a1 += cur.g[i][1]; }
         *reinterpret_cast<float2*>(&sm.key.tot[lane][2 * kw]) = make_float2(a0, a1);
     }
-    load_chunk<LOAD_GB>(nxt, p, kl, row0, tn);  // part of the next chunk
-    if (n >= 1) {
-        ChunkTiles& Hp = sm.ch[(n - 1) & 1];
+    load_chunk<LOAD_GB>(nxt, p, kl, row0, tn);  // part of the chunk after
+    if (gwork) {
         // per channel, token pairs (0,1) and (2,3) of the quad, contiguous after tperm
         uint32_t h[2][2], l[2][2];
 #pragma unroll
@@ -271,18 +286,35 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         const int pt = tperm(tq);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            *reinterpret_cast<u32x2*>(&Hp.kbh[c0 + c][sw(c0 + c, pt)]) = u32x2{h[c][0], h[c][1]};
-            *reinterpret_cast<u32x2*>(&Hp.kbl[c0 + c][sw(c0 + c, pt)]) = u32x2{l[c][0], l[c][1]};
-        }
-        if (kw == 0) {
-            *reinterpret_cast<float2*>(&Hp.ep[c0]) = make_float2(cy.ep[0], cy.ep[1]);
-            *reinterpret_cast<float2*>(&Hp.gam[c0]) = make_float2(cy.gam[0], cy.gam[1]);
+            *reinterpret_cast<u32x2*>(&Hg.kbh[c0 + c][sw(c0 + c, pt)]) = u32x2{h[c][0], h[c][1]};
+            *reinterpret_cast<u32x2*>(&Hg.kbl[c0 + c][sw(c0 + c, pt)]) = u32x2{l[c][0], l[c][1]};
         }
     }
     lds_barrier();  // ---- barrier 1
 
-    // ---------------- part 2: all decay factors, relative to the cumulative decay at token 15
-    if (work) {
+    // ---------------- part 2: A Gram half-sums of chunk n (waves 0-5); decays and exponentials of n+1
+    if (gwork && kw < 6) {
+        // A block (R,S) = (0,0), (1,0), (1,1) for kw >> 1, over channel blocks 2(kw & 1), 2(kw & 1) + 1,
+        // split bf16; the float32 partial sum goes to apart (a helper wave adds the two halves)
+        const int blk = kw >> 1, mh = kw & 1;
+        const int R = blk == 0 ? 0 : 1, S = blk == 2 ? 1 : 0;
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+            const int kc = 32 * (2 * mh + mm) + 8 * g4;
+            const u32x4 aH = ld16(&Hg.qmh[SUB * R + l16][kc]);
+            const u32x4 aL = ld16(&Hg.qml[SUB * R + l16][kc]);
+            const u32x4 bH = ld16(&sm.key.khh[SUB * S + l16][kc]);
+            const u32x4 bL = ld16(&sm.key.khl[SUB * S + l16][kc]);
+            f32x4& a = mm ? a1 : a0;
+            a = mfma_bf16(aH, bH, a);
+            a = mfma_bf16(aH, bL, a);
+            a = mfma_bf16(aL, bH, a);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.s.apart[kw][r][lane] = a0[r] + a1[r];
+    }
+    if (fwork) {
         float tt0[NKW], tt1[NKW];
 #pragma unroll
         for (int o = 0; o < NKW; o += 2) {
@@ -308,119 +340,55 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         }
         o0 *= kLog2e; o1 *= kLog2e;
         cy.eC[0] = fexp(q0); cy.eC[1] = fexp(q1);
-        if (kw == 0) {
+        if (kw == 0) {  // the state scalings of chunk n+1, read by its value step
             const float e0 = fexp(p0), e1 = fexp(p1);
-            cy.ep[0] = -kUp * e0; cy.ep[1] = -kUp * e1;
-            cy.gam[0] = e0 * cy.eC[0]; cy.gam[1] = e1 * cy.eC[1];
+            Scalings& Sf = sm.sc[nf % 3];
+            *reinterpret_cast<float2*>(&Sf.ep[c0]) = make_float2(-kUp * e0, -kUp * e1);
+            *reinterpret_cast<float2*>(&Sf.gam[c0]) = make_float2(e0 * cy.eC[0], e1 * cy.eC[1]);
         }
-        uint32_t wqh[TPW], wql[TPW], wkm[TPW], wkh[TPW], wkl[TPW];
         float y0 = o0, y1 = o1;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             y0 = __builtin_fmaf(cur.g[i][0], kLog2e, y0);  // (b_t - b_15) log2(e)
             y1 = __builtin_fmaf(cur.g[i][1], kLog2e, y1);
-            const float e0 = __builtin_amdgcn_exp2f(y0), e1 = __builtin_amdgcn_exp2f(y1);
-            const float f0 = __builtin_amdgcn_exp2f(-y0), f1 = __builtin_amdgcn_exp2f(-y1);
+            cy.e[i][0] = __builtin_amdgcn_exp2f(y0); cy.e[i][1] = __builtin_amdgcn_exp2f(y1);
+            cy.f[i][0] = __builtin_amdgcn_exp2f(-y0); cy.f[i][1] = __builtin_amdgcn_exp2f(-y1);
+        }
+        if (lane < TPW) Hf.beta[TPW * kw + lane] = cur.beta;
+    }
+    lds_barrier();  // ---- barrier 2
+
+    // ---------------- part 3: operand tiles of chunk n+1
+    // the rest of the chunk after (first read in part 3 of the next step), issued here so that the
+    // loads are spread over the step rather than queued all at once
+    load_chunk<LOAD_QK>(nxt, p, kl, row0, tn);
+    if (fwork) {
+        uint32_t wqh[TPW], wql[TPW], wkm[TPW], wkh[TPW], wkl[TPW];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
             const f32x2 qq = unpack_q(cur.q[i]), kk = unpack_q(cur.k[i]);
-            split2(qq[0] * e0, qq[1] * e1, wqh[i], wql[i]);
-            wkm[i] = pack_bf16(kk[0] * e0, kk[1] * e1);
-            cy.kh[i][0] = kk[0] * f0; cy.kh[i][1] = kk[1] * f1;
+            split2(qq[0] * cy.e[i][0], qq[1] * cy.e[i][1], wqh[i], wql[i]);
+            wkm[i] = pack_bf16(kk[0] * cy.e[i][0], kk[1] * cy.e[i][1]);
+            cy.kh[i][0] = kk[0] * cy.f[i][0]; cy.kh[i][1] = kk[1] * cy.f[i][1];
             split2(cy.kh[i][0], cy.kh[i][1], wkh[i], wkl[i]);
         }
         // one array at a time, so that stores of neighbouring tokens pair up
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&H.qmh[tq + i][pc0]) = wqh[i];
+        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&Hf.qmh[tq + i][pc0]) = wqh[i];
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&H.qml[tq + i][pc0]) = wql[i];
+        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&Hf.qml[tq + i][pc0]) = wql[i];
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&H.km[tq + i][pc0]) = wkm[i];
+        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&Hf.km[tq + i][pc0]) = wkm[i];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khh[tq + i][pc0]) = wkh[i];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khl[tq + i][pc0]) = wkl[i];
-        // beta of this chunk (the value waves read the previous chunk's before barrier 1)
-        if (lane < TPW) sm.s.beta[TPW * kw + lane] = cur.beta;
-    }
-    lds_barrier();  // ---- barrier 2
-
-    // ---------------- part 3: Gram products
-    // the rest of the next chunk (first read in part 2 of the next step), issued here so that the
-    // loads are spread over the step rather than queued all at once
-    load_chunk<LOAD_QK>(nxt, p, kl, row0, tn);
-    if (work) {
-        if (kw < 3) {
-            // A(0,0), A(1,0), A(1,1): split bf16 with three independent accumulators
-            const int R = kw == 0 ? 0 : 1, S = kw == 2 ? 1 : 0;
-            const uint16_t(*rh)[LDK] = sm.key.khh + SUB * S;
-            const uint16_t(*rl)[LDK] = sm.key.khl + SUB * S;
-            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;  // two chains over alternate channel blocks
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int kc = 32 * m + 8 * g4;
-                const u32x4 aH = ld16(&H.qmh[SUB * R + l16][kc]);
-                const u32x4 aL = ld16(&H.qml[SUB * R + l16][kc]);
-                const u32x4 bH = ld16(&rh[l16][kc]);
-                const u32x4 bL = ld16(&rl[l16][kc]);
-                f32x4& a = (m & 1) ? a1 : a0;
-                a = mfma_bf16(aH, bH, a);
-                a = mfma_bf16(aH, bL, a);
-                a = mfma_bf16(aL, bH, a);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 4 * g4 + r;
-                float v = -kUp * (a0[r] + a1[r]);
-                if (R == S && l16 > i) v = 0.f;  // lower triangle including the diagonal
-                uint32_t hi, lo;
-                split2(v, 0.f, hi, lo);
-                const int ac = sw(SUB * R + i, tperm(SUB * S + l16));
-                H.ah[SUB * R + i][ac] = hi & 0xffffu;
-                H.al[SUB * R + i][ac] = lo & 0xffffu;
-            }
-        } else if (kw == 3) {
-            // L(0,0), L(1,0), L(1,1): bf16 Km against K/Gamma (split bf16 when HP, else its high part)
-            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int kc = 32 * m + 8 * g4;
-                const u32x4 a0 = ld16(&H.km[l16][kc]);
-                const u32x4 a1 = ld16(&H.km[SUB + l16][kc]);
-                acc0 = mfma_bf16(a0, ld16(&sm.key.khh[l16][kc]), acc0);
-                acc1 = mfma_bf16(a1, ld16(&sm.key.khh[l16][kc]), acc1);
-                acc2 = mfma_bf16(a1, ld16(&sm.key.khh[SUB + l16][kc]), acc2);
-                if constexpr (HP) {
-                    acc0 = mfma_bf16(a0, ld16(&sm.key.khl[l16][kc]), acc0);
-                    acc1 = mfma_bf16(a1, ld16(&sm.key.khl[l16][kc]), acc1);
-                    acc2 = mfma_bf16(a1, ld16(&sm.key.khl[SUB + l16][kc]), acc2);
-                }
-            }
-            // the diagonal blocks as -Diag(beta) L, the form the substitution uses
-            const f32x4 nb0 = -*reinterpret_cast<const f32x4*>(&sm.s.beta[4 * g4]);
-            const f32x4 nb1 = -*reinterpret_cast<const f32x4*>(&sm.s.beta[SUB + 4 * g4]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 4 * g4 + r;
-                sm.s.lf[i][l16] = (l16 >= i) ? 0.f : nb0[r] * acc0[r];  // strictly lower
-                sm.s.lf[SUB + i][SUB + l16] = (l16 >= i) ? 0.f : nb1[r] * acc2[r];
-                // 2^64 L(1,0) as a split-bf16 operand, in the block of the T tile that T itself leaves unused
-                uint32_t hi, lo;
-                split2(kUp * acc1[r], 0.f, hi, lo);
-                sm.val.th[SUB + i][sw(SUB + i, tperm(l16))] = hi & 0xffffu;
-                sm.val.tl[SUB + i][sw(SUB + i, tperm(l16))] = lo & 0xffffu;
-            }
-        }
     }
     lds_barrier();  // ---- barrier 3
 }
 
-template <bool IN_F32, bool HP>
+template <bool IN_F32>
 __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int kw, int lane, int nchunk) {
-    // A's block (0,1) is zero in both buffers; no chunk writes it
-    for (int e = 64 * kw + lane; e < 2 * SUB * SUB; e += 64 * NKW) {
-        ChunkTiles& Hz = sm.ch[e >> 8];
-        const int r = (e >> 4) & 15, c = tperm(SUB + (e & 15));
-        Hz.ah[r][sw(r, c)] = 0; Hz.al[r][sw(r, c)] = 0;
-    }
     KeyLoad kl;
     kl.kw = kw;
     kl.lane = lane;
@@ -433,73 +401,130 @@ __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int kw, int la
     Carry cy;
     load_chunk<LOAD_ALL>(ra, p, kl, row0, 0);
     // two steps per iteration so the prefetch target alternates between two register sets
-    for (int n = 0; n <= nchunk; n += 2) {
-        key_step<IN_F32, HP>(sm, p, kl, row0, n, nchunk, ra, rb, cy);
-        if (n + 1 <= nchunk) key_step<IN_F32, HP>(sm, p, kl, row0, n + 1, nchunk, rb, ra, cy);
+    for (int n = -1; n <= nchunk; n += 2) {
+        key_step<IN_F32>(sm, p, kl, row0, n, nchunk, ra, rb, cy);
+        if (n + 1 <= nchunk) key_step<IN_F32>(sm, p, kl, row0, n + 1, nchunk, rb, ra, cy);
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// value waves: one step = chunk n-1 (nothing when n == 0); three barriers
+// helper waves.  Step n: the L Gram products (part 2), then the UT inverse and A (part 3) of chunk n.
 // ------------------------------------------------------------------------------------------------
-template <bool OUT_F32, bool IN_F32, bool CKPT>
-__device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int half, int vw, int lane, int nchunk) {
+template <bool IN_F32, bool HP>
+__device__ void helper_waves(Smem& sm, const Params& p, size_t row0, int half, int hw, int lane, int nchunk) {
     const int l16 = lane & 15, g4 = lane >> 4;
-    ValueTiles& V = sm.val;
-
-    // state: st[cb][r] = S[16*cb + 4*g4 + r][col]
-    const int col = half * DVH + 16 * vw + l16;
-    // byte offset of state element (16*cb + 4*g4 + r, col) within a head's [DK][DV] float32 state
-    const uint32_t soff = (uint32_t)(4 * g4 * DV + col) * 4u;
-    auto sidx = [&](int cb, int r) { return soff + (uint32_t)((16 * cb + r) * DV * 4); };
-    f32x4 st[8];
-    {
-        const gchar* s0 = uniform_gptr(p.S0 ? (const void*)(p.S0 + (size_t)bh * DK * DV) : nullptr);
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) st[cb][r] = p.S0 ? gload<float>(s0, sidx(cb, r)) : 0.f;
-    }
-    // byte offsets of this lane's output (token 16R + l16 of a chunk, value columns 4*g4..4*g4+3)
-    uint32_t ooff[2];
-#pragma unroll
-    for (int R = 0; R < 2; ++R)
-        ooff[R] = ((uint32_t)(SUB * R + l16) * (uint32_t)p.H * DV + half * DVH + 16 * vw + 4 * g4) * (OUT_F32 ? 4u : 2u);
-    const float oscale = -kDown * p.scale;
-
-    // this lane's v values (tokens 16R + 4*g4 + r of a chunk, column col), read one step ahead; rows
-    // past T read the last valid row and are zeroed when used.  v == NULL stands for v = 0: the rows of
-    // g are read instead (valid at every offset v would use) and the values zeroed.
+    // v for value wave hw: this lane's values are tokens 16R + 4*g4 + r of a chunk, column col, read one
+    // step ahead into registers and staged in LDS a step before their use.  Rows past T read the last
+    // valid row and are zeroed when staged.  v == NULL stands for v = 0: the rows of g are read instead
+    // (valid at every offset v would use).  These waves store nothing to global memory, so waiting for
+    // their loads never waits for a store.
     using VT = typename std::conditional<IN_F32, float, uint16_t>::type;
-    VT vnext[2][4];
+    const int col = half * DVH + 16 * hw + l16;
+    const uint32_t vrow = (uint32_t)p.H * DV * (uint32_t)sizeof(VT);  // bytes between tokens
+    const uint32_t vcol = (uint32_t)col * (uint32_t)sizeof(VT);
+    VT vr[2][4];
     auto load_v = [&](int tc0) {
         const size_t e0 = (row0 + (size_t)tc0 * p.H) * DV;
         const gchar* vb = uniform_gptr(p.v ? (const void*)((const VT*)p.v + e0) : (const void*)(p.g + e0));
-        const int lim = p.T - 1 - tc0;
+        // offsets grow with the row, so a row past T is clamped to row T-1 by a min on the offset
+        const uint32_t last = (uint32_t)min(p.T - 1 - tc0, C - 1) * vrow + vcol;
 #pragma unroll
         for (int R = 0; R < 2; ++R)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                vnext[R][r] = gload<VT>(vb, ((uint32_t)min(SUB * R + 4 * g4 + r, lim) * (uint32_t)p.H * DV + col) *
-                                                (uint32_t)sizeof(VT));
+                vr[R][r] = gload<VT>(vb, min((uint32_t)(SUB * R + 4 * g4 + r) * vrow + vcol, last));
     };
     load_v(0);
-
-    for (int n = 0; n <= nchunk; ++n) {
-        const bool work = n >= 1;  // this step handles chunk n-1
-        const int t0 = (n - 1) * C;
-        const ChunkTiles& H = sm.ch[(n - 1) & 1];
-        // ---------------- part 1: UT inverse of the two diagonal blocks, spread over the value waves
-        // Wave vw solves two columns ja, jb of block vw >> 1 of (I + Diag(beta) L) X = I per 16-lane row
-        // g4: ja = g4, jb = 12 + g4 (even vw) or ja = 4 + g4, jb = 8 + g4 (odd vw); lane l16 holds matrix
-        // row i = l16 of N = -Diag(beta) L.  With x_i = [i == j] + y_i, forward substitution reads
-        // y = N e_j + N y: y starts as column j of N, and at step m row m's (final) y_m is broadcast along
-        // the 16-lane row and rows below take y_i += N[i][m] y_m.  Rows at or above j keep y = 0, so
-        // column j needs steps m > j only, which the column pairing balances.
-        if (work) {
-            const float* beta = sm.s.beta;
-            const bool odd = vw & 1;
-            const int o = SUB * (vw >> 1), i = l16, ja = (odd ? 4 : 0) + g4, jb = (odd ? 8 : 12) + g4;
+    // A's block (0,1) is zero in both buffers; no chunk writes it
+    for (int e = 64 * hw + lane; e < 2 * SUB * SUB; e += 64 * NHW) {
+        ChunkTiles& Hz = sm.ch[e >> 8];
+        const int r = (e >> 4) & 15, c = tperm(SUB + (e & 15));
+        Hz.ah[r][sw(r, c)] = 0; Hz.al[r][sw(r, c)] = 0;
+    }
+    // A from its half-sums: elements e = 256 hw' + ... of the 768 in blocks (0,0), (1,0), (1,1); each lane
+    // takes three, at fixed places (hoisted out of the loop: source index and destination column)
+    int asrc[3], adst[3];
+    bool azero[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int e = 256 * k + 64 * hw + lane;  // block k, element (r, ln) = ((e >> 6) & 3, e & 63)
+        const int r = (e >> 6) & 3, ln = e & 63;
+        const int R = k == 0 ? 0 : 1, S = k == 2 ? 1 : 0;
+        const int i = 4 * (ln >> 4) + r, jj = ln & 15;
+        asrc[k] = (r * 64 + ln);                                  // within apart[2k] / apart[2k+1]
+        adst[k] = (SUB * R + i) * LDA + sw(SUB * R + i, tperm(SUB * S + jj));
+        azero[k] = R == S && jj > i;                              // above the diagonal of a diagonal block
+    }
+    __builtin_amdgcn_s_setprio(3);  // the substitution is a chain of dependent steps: issue it first
+    for (int n = -1; n <= nchunk; ++n) {
+        const bool gwork = n >= 0 && n < nchunk;
+        ChunkTiles& H = sm.ch[n & 1];
+        // ---------------- part 1: 2^64 v of chunk n to LDS (the value waves use it in the next step)
+        if (gwork) {
+            float x[8];
+            const int t0 = n * C;
+#pragma unroll
+            for (int R = 0; R < 2; ++R)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v;
+                    if constexpr (IN_F32) v = vr[R][r];
+                    else v = __uint_as_float((uint32_t)vr[R][r] << 16);
+                    x[4 * R + r] = (p.v && t0 + SUB * R + 4 * g4 + r < p.T) ? kUp * v : 0.f;
+                }
+            f32x4* dst = reinterpret_cast<f32x4*>(&sm.vs[n & 1].x[hw][lane][0]);
+            dst[0] = f32x4{x[0], x[1], x[2], x[3]};
+            dst[1] = f32x4{x[4], x[5], x[6], x[7]};
+        }
+        load_v(min(n + 1, nchunk - 1) * C);  // v of the chunk after (unconditionally, as in load_chunk)
+        lds_barrier();  // ---- barrier 1
+        // ---------------- part 2: L(0,0), L(1,1) (wave 0) and 2^64 L(1,0) (wave 1) of chunk n
+        if (gwork && hw < 2) {
+            const int Ra = hw == 0 ? 0 : 1;   // L(0,0) or L(1,0)
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;  // acc1: L(1,1) (wave 0)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int kc = 32 * m + 8 * g4;
+                const u32x4 a0 = ld16(&H.km[SUB * Ra + l16][kc]);
+                acc0 = mfma_bf16(a0, ld16(&sm.key.khh[l16][kc]), acc0);
+                if constexpr (HP) acc0 = mfma_bf16(a0, ld16(&sm.key.khl[l16][kc]), acc0);
+                if (hw == 0) {
+                    const u32x4 a1 = ld16(&H.km[SUB + l16][kc]);
+                    acc1 = mfma_bf16(a1, ld16(&sm.key.khh[SUB + l16][kc]), acc1);
+                    if constexpr (HP) acc1 = mfma_bf16(a1, ld16(&sm.key.khl[SUB + l16][kc]), acc1);
+                }
+            }
+            if (hw == 0) {  // the diagonal blocks as -Diag(beta) L (strictly lower), the form the substitution uses
+                const f32x4 nb0 = -*reinterpret_cast<const f32x4*>(&H.beta[4 * g4]);
+                const f32x4 nb1 = -*reinterpret_cast<const f32x4*>(&H.beta[SUB + 4 * g4]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * g4 + r;
+                    sm.s.lf[i][l16] = (l16 >= i) ? 0.f : nb0[r] * acc0[r];
+                    sm.s.lf[SUB + i][SUB + l16] = (l16 >= i) ? 0.f : nb1[r] * acc1[r];
+                }
+            } else {        // 2^64 L(1,0) as a split-bf16 operand, in the block (1,0) of T's tile
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * g4 + r;
+                    uint32_t hi, lo;
+                    split2(kUp * acc0[r], 0.f, hi, lo);
+                    H.th[SUB + i][sw(SUB + i, tperm(l16))] = hi & 0xffffu;
+                    H.tl[SUB + i][sw(SUB + i, tperm(l16))] = lo & 0xffffu;
+                }
+            }
+        }
+        lds_barrier();  // ---- barrier 2
+        // ---------------- part 3: UT inverse of the two diagonal blocks; A'' = -2^64 A
+        if (gwork) {
+            // Wave hw solves two columns ja, jb of block hw >> 1 of (I + Diag(beta) L) X = I per 16-lane row
+            // g4: ja = g4, jb = 12 + g4 (even hw) or ja = 4 + g4, jb = 8 + g4 (odd hw); lane l16 holds matrix
+            // row i = l16 of N = -Diag(beta) L.  With x_i = [i == j] + y_i, forward substitution reads
+            // y = N e_j + N y: y starts as column j of N, and at step m row m's (final) y_m is broadcast along
+            // the 16-lane row and rows below take y_i += N[i][m] y_m.  Rows at or above j keep y = 0, so
+            // column j needs steps m > j only, which the column pairing balances.
+            const bool odd = hw & 1;
+            const int o = SUB * (hw >> 1), i = l16, ja = (odd ? 4 : 0) + g4, jb = (odd ? 8 : 12) + g4;
             float Nr[SUB];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
@@ -525,28 +550,83 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
 #undef KDA_STEP_A
 #undef KDA_STEP_AB
             // T' = 2^-64 X Diag(beta), as split bf16 in the tperm'd columns of T's tile
-            const float ta = ((i == ja ? 1.f : 0.f) + ya) * (beta[o + ja] * kDown);
-            const float tb = ((i == jb ? 1.f : 0.f) + yb) * (beta[o + jb] * kDown);
+            const float ta = ((i == ja ? 1.f : 0.f) + ya) * (H.beta[o + ja] * kDown);
+            const float tb = ((i == jb ? 1.f : 0.f) + yb) * (H.beta[o + jb] * kDown);
             uint32_t hi, lo;
             split2(ta, tb, hi, lo);
             const int ca = sw(o + i, tperm(o + ja)), cb = sw(o + i, tperm(o + jb));
-            V.th[o + i][ca] = hi & 0xffffu;
-            V.th[o + i][cb] = hi >> 16;
-            V.tl[o + i][ca] = lo & 0xffffu;
-            V.tl[o + i][cb] = lo >> 16;
+            H.th[o + i][ca] = hi & 0xffffu;
+            H.th[o + i][cb] = hi >> 16;
+            H.tl[o + i][ca] = lo & 0xffffu;
+            H.tl[o + i][cb] = lo >> 16;
+            // A'' = -2^64 A from the two channel-half sums (lower triangle on the diagonal blocks)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const float* ap = &sm.s.apart[2 * k][0][0];
+                float v = -kUp * (ap[asrc[k]] + ap[256 + asrc[k]]);
+                if (azero[k]) v = 0.f;
+                uint32_t h2, l2;
+                split2(v, 0.f, h2, l2);
+                (&H.ah[0][0])[adst[k]] = h2 & 0xffffu;
+                (&H.al[0][0])[adst[k]] = l2 & 0xffffu;
+            }
         }
-        lds_barrier();  // ---- barrier 1
+        lds_barrier();  // ---- barrier 3
+    }
+}
 
-        // ---------------- part 2: P = -2^64 Diag(exp(b_15)) S as split-bf16 operands; U; Qm P
+// ------------------------------------------------------------------------------------------------
+// value waves.  Step n handles chunk n-1 (nothing for n < 1); three barriers per step.
+// ------------------------------------------------------------------------------------------------
+template <bool OUT_F32, bool IN_F32, bool CKPT>
+__device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int half, int vw, int lane, int nchunk) {
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    // state: st[cb][r] = S[16*cb + 4*g4 + r][col]
+    const int col = half * DVH + 16 * vw + l16;
+    // byte offset of state element (16*cb + 4*g4 + r, col) within a head's [DK][DV] float32 state
+    const uint32_t soff = (uint32_t)(4 * g4 * DV + col) * 4u;
+    auto sidx = [&](int cb, int r) { return soff + (uint32_t)((16 * cb + r) * DV * 4); };
+    f32x4 st[8];
+    {
+        const gchar* s0 = uniform_gptr(p.S0 ? (const void*)(p.S0 + (size_t)bh * DK * DV) : nullptr);
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st[cb][r] = p.S0 ? gload<float>(s0, sidx(cb, r)) : 0.f;
+    }
+    // byte offsets of this lane's output (token 16R + l16 of a chunk, value columns 4*g4..4*g4+3)
+    uint32_t ooff[2];
+#pragma unroll
+    for (int R = 0; R < 2; ++R)
+        ooff[R] = ((uint32_t)(SUB * R + l16) * (uint32_t)p.H * DV + half * DVH + 16 * vw + 4 * g4) * (OUT_F32 ? 4u : 2u);
+    const float oscale = -kDown * p.scale;
+
+    __builtin_amdgcn_s_setprio(2);  // the value waves carry the serial chain: issue them first
+
+    for (int n = -1; n <= nchunk; ++n) {
+        const bool work = n >= 1;  // this step handles chunk n-1
+        const int c = n - 1;
+        const int t0 = c * C;
+        const ChunkTiles& H = sm.ch[c & 1];
+        const Scalings& Sc = sm.sc[(c + 3) % 3];
+        u32x4 ph[4];
         f32x4 oacc[2];
-        u32x4 uh, ul;
+        // ---------------- part 1: P = -2^64 Diag(exp(b_15)) S as split-bf16 operands; Qm P
+        // (each product chain below has its own accumulators, interleaved, so that consecutive matrix
+        // instructions never wait for each other's results)
         if (work) {
-            u32x4 ph[4], pl[4];  // P as the contraction operand over channels 32m..32m+31, order
-                                 // {32m + 4*g4 + r} then {32m + 16 + 4*g4 + r}; as an A operand, P^T
+            f32x4 q[2][3];
+#pragma unroll
+            for (int R = 0; R < 2; ++R)
+#pragma unroll
+                for (int t = 0; t < 3; ++t) q[R][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // K-step m over channels 32m..32m+31 in the order {32m + 4*g4 + r} then {32m + 16 + 4*g4 + r};
+            // as an A operand it is P^T.  Qm P as O^T: lane (token l16, group g4) gets columns 4*g4..4*g4+3
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const f32x4 e0 = *reinterpret_cast<const f32x4*>(&H.ep[32 * m + 4 * g4]);
-                const f32x4 e1 = *reinterpret_cast<const f32x4*>(&H.ep[32 * m + 16 + 4 * g4]);
+                const f32x4 e0 = *reinterpret_cast<const f32x4*>(&Sc.ep[32 * m + 4 * g4]);
+                const f32x4 e1 = *reinterpret_cast<const f32x4*>(&Sc.ep[32 * m + 16 + 4 * g4]);
                 const f32x4 a = st[2 * m] * e0, b = st[2 * m + 1] * e1;
                 uint32_t h0, h1, h2, h3, q0, q1, q2, q3;
                 split2(a[0], a[1], h0, q0);
@@ -554,43 +634,36 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
                 split2(b[0], b[1], h2, q2);
                 split2(b[2], b[3], h3, q3);
                 ph[m] = u32x4{h0, h1, h2, h3};
-                pl[m] = u32x4{q0, q1, q2, q3};
+                const u32x4 pl = u32x4{q0, q1, q2, q3};
+                const u32x4 bH0 = ld16(&H.qmh[l16][32 * m + 8 * g4]), bL0 = ld16(&H.qml[l16][32 * m + 8 * g4]);
+                const u32x4 bH1 = ld16(&H.qmh[SUB + l16][32 * m + 8 * g4]), bL1 = ld16(&H.qml[SUB + l16][32 * m + 8 * g4]);
+                q[0][0] = mfma_bf16(ph[m], bH0, q[0][0]);
+                q[1][0] = mfma_bf16(ph[m], bH1, q[1][0]);
+                q[0][1] = mfma_bf16(pl, bH0, q[0][1]);
+                q[1][1] = mfma_bf16(pl, bH1, q[1][1]);
+                q[0][2] = mfma_bf16(ph[m], bL0, q[0][2]);
+                q[1][2] = mfma_bf16(ph[m], bL1, q[1][2]);
             }
-            // X~ = 2^64 V + Km P, started from 2^64 V in accumulator layout (tokens 16R + 4*g4 + r)
-            f32x4 xr[2];
 #pragma unroll
-            for (int R = 0; R < 2; ++R)
+            for (int R = 0; R < 2; ++R) oacc[R] = q[R][0] + (q[R][1] + q[R][2]);
+        }
+        lds_barrier();  // ---- barrier 1
+
+        // ---------------- part 2: X~ = 2^64 V + Km P; U
+        u32x4 uh, ul;
+        if (work) {
+            // 2^64 V in accumulator layout (tokens 16R + 4*g4 + r, column col), staged by a helper wave
+            const f32x4* vx = reinterpret_cast<const f32x4*>(&sm.vs[c & 1].x[vw][lane][0]);
+            f32x4 xr[2] = {vx[0], vx[1]}, xs[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float x;
-                    if constexpr (IN_F32) x = vnext[R][r];
-                    else x = __uint_as_float((uint32_t)vnext[R][r] << 16);
-                    xr[R][r] = (p.v && t0 + SUB * R + 4 * g4 + r < p.T) ? kUp * x : 0.f;
-                }
-            load_v(min(n, nchunk - 1) * C);  // v of the chunk handled next step (unconditionally, as above)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
+            for (int m = 0; m < 4; m += 2)
 #pragma unroll
                 for (int R = 0; R < 2; ++R) {
-                    const u32x4 a = ld16(&H.km[SUB * R + l16][32 * m + 8 * g4]);
-                    xr[R] = mfma_bf16(a, ph[m], xr[R]);
-                    xr[R] = mfma_bf16(a, pl[m], xr[R]);
+                    xr[R] = mfma_bf16(ld16(&H.km[SUB * R + l16][32 * m + 8 * g4]), ph[m], xr[R]);
+                    xs[R] = mfma_bf16(ld16(&H.km[SUB * R + l16][32 * (m + 1) + 8 * g4]), ph[m + 1], xs[R]);
                 }
-            }
-            // Qm P as O^T: lane (token l16, group g4) gets value columns 4*g4..4*g4+3
-#pragma unroll
-            for (int R = 0; R < 2; ++R) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const u32x4 bH = ld16(&H.qmh[SUB * R + l16][32 * m + 8 * g4]);
-                    const u32x4 bL = ld16(&H.qml[SUB * R + l16][32 * m + 8 * g4]);
-                    acc = mfma_bf16(ph[m], bH, acc);
-                    acc = mfma_bf16(pl[m], bH, acc);
-                    acc = mfma_bf16(ph[m], bL, acc);
-                }
-                oacc[R] = acc;
-            }
+            xr[0] += xs[0];
+            xr[1] += xs[1];
             // U by block forward substitution over the two sub-tiles (T is block lower triangular):
             //   U0 = T'00 X~0,   U1 = T'11 (X~1 - L'10 U0),
             // as split-bf16 16x16x16 products whose contraction index is token 4*g4 + r of a sub-tile
@@ -606,16 +679,16 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
                 a = mfma_bf16_k16(aH, bL, a);
                 return mfma_bf16_k16(aL, bH, a);
             };
-            auto ld8 = [](const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); };
+            auto ld8 = [](const uint16_t* q) { return *reinterpret_cast<const u32x2*>(q); };
             f32x4 u[2];
-            u32x2 bh, bl;
-            split4(xr[0], bh, bl);
+            u32x2 sh, sl;
+            split4(xr[0], sh, sl);
             const int c0s = sw(l16, 8 * g4);  // (rows l16 and SUB + l16 share the swizzle)
-            u[0] = prod3(ld8(&V.th[l16][c0s]), ld8(&V.tl[l16][c0s]), bh, bl);
-            split4(u[0], bh, bl);
-            const f32x4 lu = prod3(ld8(&V.th[SUB + l16][c0s]), ld8(&V.tl[SUB + l16][c0s]), bh, bl);
-            split4(xr[1] - lu, bh, bl);
-            u[1] = prod3(ld8(&V.th[SUB + l16][c0s + 4]), ld8(&V.tl[SUB + l16][c0s + 4]), bh, bl);
+            u[0] = prod3(ld8(&H.th[l16][c0s]), ld8(&H.tl[l16][c0s]), sh, sl);
+            split4(u[0], sh, sl);
+            const f32x4 lu = prod3(ld8(&H.th[SUB + l16][c0s]), ld8(&H.tl[SUB + l16][c0s]), sh, sl);
+            split4(xr[1] - lu, sh, sl);
+            u[1] = prod3(ld8(&H.th[SUB + l16][c0s + 4]), ld8(&H.tl[SUB + l16][c0s + 4]), sh, sl);
             uint32_t uh0, uh1, uh2, uh3, ul0, ul1, ul2, ul3;
             split2(u[0][0], u[0][1], uh0, ul0);
             split2(u[0][2], u[0][3], uh1, ul1);
@@ -630,14 +703,18 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
         if (work) {
             if (p.o) {  // (o == NULL: a state-only run of the in-device context parallelism)
                 gchar* ob = (gchar*)uniform_gptr((const char*)p.o + ((row0 + (size_t)t0 * p.H) * DV) * (OUT_F32 ? 4 : 2));
+                f32x4 o1[2], o2[2];
 #pragma unroll
                 for (int R = 0; R < 2; ++R) {
                     const u32x4 aH = ld16(&H.ah[SUB * R + l16][sw(l16, 8 * g4)]);
                     const u32x4 aL = ld16(&H.al[SUB * R + l16][sw(l16, 8 * g4)]);
-                    f32x4 acc = mfma_bf16(uh, aH, oacc[R]);
-                    acc = mfma_bf16(ul, aH, acc);
-                    acc = mfma_bf16(uh, aL, acc);
-                    acc *= oscale;
+                    oacc[R] = mfma_bf16(uh, aH, oacc[R]);
+                    o1[R] = mfma_bf16(ul, aH, f32x4{0.f, 0.f, 0.f, 0.f});
+                    o2[R] = mfma_bf16(uh, aL, f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+#pragma unroll
+                for (int R = 0; R < 2; ++R) {
+                    const f32x4 acc = (oacc[R] + (o1[R] + o2[R])) * oscale;
                     if (t0 + SUB * R + l16 < p.T) {
                         if constexpr (OUT_F32)
                             gstore<f32x4>(ob, ooff[R], acc);
@@ -647,19 +724,27 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
                 }
             }
 #pragma unroll
-            for (int cb = 0; cb < 8; ++cb) {
-                const f32x4 gm = *reinterpret_cast<const f32x4*>(&H.gam[16 * cb + 4 * g4]);
-                const u32x4 aH = ld16(&H.kbh[16 * cb + l16][sw(l16, 8 * g4)]);
-                const u32x4 aL = ld16(&H.kbl[16 * cb + l16][sw(l16, 8 * g4)]);
-                f32x4 acc = mfma_bf16(aH, uh, st[cb] * gm);
-                acc = mfma_bf16(aH, ul, acc);
-                st[cb] = mfma_bf16(aL, uh, acc);
+            for (int c4 = 0; c4 < 8; c4 += 4) {  // four row blocks at a time, term by term
+                u32x4 aH[4], aL[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int cb = c4 + j;
+                    aH[j] = ld16(&H.kbh[16 * cb + l16][sw(l16, 8 * g4)]);
+                    aL[j] = ld16(&H.kbl[16 * cb + l16][sw(l16, 8 * g4)]);
+                    st[cb] *= *reinterpret_cast<const f32x4*>(&Sc.gam[16 * cb + 4 * g4]);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) st[c4 + j] = mfma_bf16(aH[j], uh, st[c4 + j]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) st[c4 + j] = mfma_bf16(aH[j], ul, st[c4 + j]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) st[c4 + j] = mfma_bf16(aL[j], uh, st[c4 + j]);
             }
             if (CKPT && n % p.ckpt_chunks == 0 && n / p.ckpt_chunks <= p.n_ckpt) {
                 // the state after tokens [0, n*C): checkpoint n / ckpt_chunks - 1
                 gchar* dst = uniform_gptr(p.S_ckpt + ((size_t)bh * p.n_ckpt + (n / p.ckpt_chunks - 1)) * DK * DV);
                 uint32_t o = soff;
-                asm volatile("" : "+v"(o));  // formed here: 32 offsets held across the loop would spill
+                asm volatile("" : "+v"(o));  // formed here: offsets held across the loop would spill
 #pragma unroll
                 for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
@@ -701,9 +786,11 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
     if (nchunk == 0) return;  // (the host runs the state copy instead; every wave leaves here alike)
 
     if (wave < NKW)
-        key_waves<IN_F32, HP>(sm, p, row0, wave, lane, nchunk);
-    else
+        key_waves<IN_F32>(sm, p, row0, wave, lane, nchunk);
+    else if (wave < NKW + NVW)
         value_waves<OUT_F32, IN_F32, CKPT>(sm, p, bh, row0, half, wave - NKW, lane, nchunk);
+    else
+        helper_waves<IN_F32, HP>(sm, p, row0, half, wave - NKW - NVW, lane, nchunk);
 }
 
 }  // namespace bf16path
