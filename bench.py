@@ -1,12 +1,15 @@
 """Throughput of the KDA forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--workload ...]
 
 One step = one kda_fwd call over the training-prefill workload B=4, H=32, T=16384, d_k = d_v = 128
 (bf16 q/k/v/o, float32 g/beta/state, chunk 32) with its inputs already resident in HBM.  Prints one
 JSON line with the whole-job tokens/s, the roofline position of the kernel (algorithmic bytes per
-launch over the average launch time measured with HIP events on the launch stream) and the float64
-CPU oracle's throughput on a bounded sample of the same workload.
+launch over the average launch time measured with HIP events on the launch stream; median and
+minimum beside it, and the fraction of the HBM bandwidth a plain device copy reaches in the same
+process) and the float64 CPU oracle's throughput on a bounded sample of the same workload.
+--workload f32_small / bf16_4k time the two smaller forward workloads (B1 H2 T256 D64 in float32;
+B1 H16 T4096 D128 bf16 with an initial state) the same way, one line each.
 """
 from __future__ import annotations
 
@@ -24,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA prefill tokens/s at H=32,d=128,T=16K + % bf16 MFMA peak (1 GPU)"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X float32 vector
 WORKLOAD = 2
 COPY_BYTES = 512 << 20
 CSRC = os.path.join(ROOT, "linear_recurrent_attention_amd", "csrc")
@@ -69,11 +73,12 @@ def measured_traffic(which="core"):
 
 
 def cpu_baseline(d, threads):
-    """float64 oracle over the whole workload (4 x 32 sequences of 16384 tokens; about 20 s of CPU work)."""
+    """float64 oracle over the whole workload (for the headline one, 4 x 32 sequences of 16384 tokens:
+    about 1 s of CPU work on 16 threads)."""
     import oracle
     s = {n: np.ascontiguousarray(d[n]) for n in ("q", "k", "v", "g", "beta")}
     t = time.perf_counter()
-    oracle.recurrence(s["q"], s["k"], s["v"], s["g"], s["beta"], want_o=True, threads=threads)
+    oracle.recurrence(s["q"], s["k"], s["v"], s["g"], s["beta"], S0=d.get("S0"), want_o=True, threads=threads)
     dt = time.perf_counter() - t
     B, T = s["q"].shape[:2]
     return {"value": B * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -100,6 +105,48 @@ def time_steps(torch, step, stream, args):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
     return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def launch_stats(launch_ms):
+    """Mean, median and minimum of per-step event times, in milliseconds."""
+    a = np.asarray(launch_ms, dtype=np.float64)
+    return {"avg_launch_ms": float(a.mean()), "median_launch_ms": float(np.median(a)), "min_launch_ms": float(a.min())}
+
+
+def copy_gbs(torch, stream, nbytes=COPY_BYTES, reps=10):
+    """HBM bandwidth a plain device-to-device copy of nbytes reaches (read + write bytes over the
+    median of reps event-timed copies on `stream`): the practical ceiling for a streaming kernel."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ms = []
+    with torch.cuda.stream(stream):
+        dst.copy_(src)
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dst.copy_(src)
+            b.record(stream)
+            ms.append((a, b))
+        stream.synchronize()
+    t = float(np.median([a.elapsed_time(b) for a, b in ms])) / 1e3
+    del src, dst
+    torch.cuda.synchronize()
+    return 2 * nbytes / t / 1e9
+
+
+def hbm_roofline(abytes, stats, copy, kernel, traffic=None):
+    """The `roofline` object of an HBM-bound line: algorithmic bytes over the mean launch time against
+    the spec peak, with the median/min launch times and the fraction of the measured copy rate."""
+    gbs = abytes / (stats["avg_launch_ms"] / 1e3) / 1e9
+    out = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+           "traffic": traffic, "kernel": kernel, **stats, "algorithmic_bytes": abytes}
+    if copy:
+        out["copy_measured_gbs"] = copy
+        out["frac_of_copy"] = gbs / copy
+        out["frac_of_copy_median"] = abytes / (stats["median_launch_ms"] / 1e3) / 1e9 / copy
+    return out
 
 
 def decode_bytes(B, H, D, T=1, io_bytes=2):
@@ -339,6 +386,68 @@ def bench_layer(args, torch, synth, kda):
     print(json.dumps(out), flush=True)
 
 
+def bench_core(args, torch, synth, kda, wid):
+    """kda_fwd on forward workload wid (2: the headline B4 H32 T16384 D128 bf16 line; 0: B1 H2 T256 D64
+    float32; 1: B1 H16 T4096 D128 bf16 with an initial state)."""
+    w = synth.WORKLOADS[wid]
+    B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
+    d = synth.core_inputs(wid, seed=0)
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v", "g", "beta")}
+    bf16 = w.io == "bf16"
+    io_dt = torch.bfloat16 if bf16 else torch.float32
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(io_dt)
+    S0 = None if d["S0"] is None else torch.from_numpy(d["S0"]).to(dev)
+    o = torch.empty((B, T, H, Dv), dtype=io_dt, device=dev)
+    ST = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step():
+        kda.kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=S0, out=o, state_out=ST)
+
+    wall, launch_ms = time_steps(torch, step, stream, args)
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    stats = launch_stats(launch_ms)
+    copy = None if args.calibrate_copy else copy_gbs(torch, stream)
+    avg_launch_s = stats["avg_launch_ms"] / 1e3
+    ms_per_step = wall / args.steps * 1e3
+
+    tokens = B * T
+    value = tokens / (wall / args.steps)
+    abytes = algorithmic_bytes(B, T, H, Dk, Dv, io_bytes=2 if bf16 else 4, has_S0=S0 is not None)
+    aflops = algorithmic_flops(B, T, H, Dk, Dv, C=32 if bf16 else 16)
+    achieved_tflops = aflops / avg_launch_s / 1e12
+    kernel = "kda_fwd_bf16_kernel" if bf16 else "kda_fwd_f32_kernel"
+    mm_peak = BF16_PEAK_TFLOPS if bf16 else FP32_VALU_PEAK_TFLOPS
+
+    out = {
+        "metric": METRIC if wid == WORKLOAD else f"KDA prefill tokens/s ({w.name})", "value": value,
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "Dk": Dk, "Dv": Dv, "chunk": 32 if bf16 else 16,
+                   "io": ("bf16 q/k/v/o" if bf16 else "float32 q/k/v/o") + ", float32 g/beta/state"
+                         + (", S0 given" if S0 is not None else "")},
+        "roofline": hbm_roofline(abytes, stats, copy, kernel, measured_traffic() if wid == WORKLOAD else None),
+        ("mfma" if bf16 else "valu"): {"achieved": achieved_tflops, "peak": mm_peak, "unit": "TFLOP/s",
+                                       "frac": achieved_tflops / mm_peak, "algorithmic_flops": aflops},
+    }
+    if not args.no_cpu:
+        try:
+            threads = len(os.sched_getaffinity(0))
+        except AttributeError:
+            threads = os.cpu_count() or 1
+        out["cpu_baseline"] = cpu_baseline(d, threads)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,10 +456,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run one plain 512 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=("core", "layer", "decode", "longctx", "bwd"), default="core",
+    ap.add_argument("--workload", choices=("core", "f32_small", "bf16_4k", "layer", "decode", "longctx", "bwd"),
+                    default="core",
                     help="core: kda_fwd on B4 H32 T16384 (the headline line); layer: kda_layer_fwd on "
                          "B2 T8192 d_model 2048 H16; decode: kda_decode on B128 H32, one token; longctx: "
-                         "kda_fwd_cp on B1 H16 T1M; bwd: kda_bwd on B4 H32 T16384 (separate lines)")
+                         "kda_fwd_cp on B1 H16 T1M; bwd: kda_bwd on B4 H32 T16384; f32_small: kda_fwd on "
+                         "B1 H2 T256 D64 float32; bf16_4k: kda_fwd on B1 H16 T4096 (separate lines)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus N with N > 1 is not supported "
@@ -373,58 +484,13 @@ def main():
     if args.workload == "bwd":
         bench_bwd(args, torch, synth, kda)
         return
-    w = synth.WORKLOADS[WORKLOAD]
-    B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
-    d = synth.core_inputs(WORKLOAD, seed=0)
-    dev = torch.device("cuda:0")
-    t = {n: torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v", "g", "beta")}
-    for n in ("q", "k", "v"):
-        t[n] = t[n].to(torch.bfloat16)
-    o = torch.empty((B, T, H, Dv), dtype=torch.bfloat16, device=dev)
-    ST = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
-    stream = torch.cuda.Stream(device=dev)
-
-    def step():
-        kda.kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], out=o, state_out=ST)
-
-    wall, launch_ms = time_steps(torch, step, stream, args)
-    if args.calibrate_copy:
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    avg_launch_s = float(np.mean(launch_ms)) / 1e3
-    ms_per_step = wall / args.steps * 1e3
-
-    tokens = B * T
-    value = tokens / (wall / args.steps)
-    abytes = algorithmic_bytes(B, T, H, Dk, Dv)
-    aflops = algorithmic_flops(B, T, H, Dk, Dv)
-    achieved_gbs = abytes / avg_launch_s / 1e9
-    achieved_tflops = aflops / avg_launch_s / 1e12
-
-    out = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "T": T, "Dk": Dk, "Dv": Dv, "chunk": 32,
-                   "io": "bf16 q/k/v/o, float32 g/beta/state"},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "kda_fwd_bf16_kernel", "avg_launch_ms": avg_launch_s * 1e3,
-                     "algorithmic_bytes": abytes},
-        "mfma": {"achieved": achieved_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": achieved_tflops / BF16_PEAK_TFLOPS, "algorithmic_flops": aflops},
-    }
-    if not args.no_cpu:
-        try:
-            threads = len(os.sched_getaffinity(0))
-        except AttributeError:
-            threads = os.cpu_count() or 1
-        out["cpu_baseline"] = cpu_baseline(d, threads)
-    print(json.dumps(out), flush=True)
+    if args.workload == "f32_small":
+        bench_core(args, torch, synth, kda, 0)
+        return
+    if args.workload == "bf16_4k":
+        bench_core(args, torch, synth, kda, 1)
+        return
+    bench_core(args, torch, synth, kda, WORKLOAD)
 
 
 if __name__ == "__main__":

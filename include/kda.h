@@ -63,10 +63,10 @@ typedef struct {
 } kda_fwd_desc;
 
 /* kda_fwd_desc.flags: bf16 I/O only (the f32 path computes in float32 throughout and ignores it).
- * Forms the intra-chunk key Gram matrix and the state update with split-bf16 operands instead of
- * single bf16 / f16 ones.  Worth it when keys within a chunk are strongly correlated (e.g. after a
- * Swish activation), which makes I + Diag(beta) L ill-conditioned and amplifies rounding in S_T;
- * costs about 10% of throughput. */
+ * Forms the intra-chunk key Gram matrix L with split-bf16 key operands instead of single bf16 ones
+ * (every other product of the bf16 path is split-bf16 already).  Worth it when keys within a chunk
+ * are strongly correlated (e.g. after a Swish activation), which makes I + Diag(beta) L
+ * ill-conditioned and amplifies the rounding of L in o and S_T; costs a few percent of throughput. */
 #define KDA_FWD_PRECISE 1
 
 /* kda_fwd_desc.flags, kda_fwd only: check the inputs before computing (a debug mode).  A device
@@ -93,11 +93,14 @@ typedef struct {
  *            when that size is 0 (the plain forward needs none); contents are scratch
  *
  * Pointer alignment: q, k, v, o 4-byte aligned; g, beta, S0, S_T 8-byte aligned.
- * bf16 path numerics: intermediate products use bf16/f16 matrix-core operands with float32
- * accumulation (split-bf16 where a single rounding is too coarse, and for more products with
- * KDA_FWD_PRECISE); the state is float32.
- * The value path uses f16 operands, so |v| and the state entries must stay below 6.5e4;
- * beyond that o and S_T become non-finite.
+ * bf16 path numerics: matrix-core products on bf16 operands with float32 accumulation, split-bf16
+ * (hi + lo, three products) wherever a value-path or state operand enters, and a float32 state.
+ * The value path works on the state scaled by exact powers of two, so the result does not depend
+ * on the magnitude of v and S0: it holds its accuracy while the state entries and |v| stay within
+ * 2^-75 <= |x| < 2^60 (entries below 2^-75 count as 0 against the rest).  Within a chunk the
+ * decay factors are taken relative to its middle token, so with g >= -5 they stay within
+ * [e^-80, e^80] and q, k of ordinary magnitude (e.g. L2-normalised) keep every key-side operand
+ * normal.
  * Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE or KDA_ERR_HIP.
  */
 size_t kda_fwd_workspace_size(const kda_fwd_desc* desc);  /* 256 with KDA_VALIDATE, else 0 (NULL desc: 0) */

@@ -52,7 +52,7 @@
 //   U = T' X~           split                          A'' U              split
 //   Kbar^T U            split
 // The inverse solves the two 16x16 diagonal blocks of (I + Diag(beta) L) by forward substitution
-// in float32, one matrix row per lane, spread over the four value waves.
+// in float32, one matrix row per lane, spread over the four helper waves.
 #include "kda_common.h"
 #include "kda_internal.h"
 
