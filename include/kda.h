@@ -12,14 +12,16 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent), owned by the caller.
- *     The library allocates no device memory in kda_fwd; a call that needs scratch memory takes
- *     it from a caller workspace, sized by the query beside it.
+ *     The library allocates no device memory in its calls; a call that needs scratch memory takes
+ *     it from a caller workspace, sized by the query beside it (kda_fwd_cp_noalloc: from a fixed
+ *     array that is part of the library's code object).
  *   - Calls are asynchronous and ordered on `stream` (NULL = the default stream).  The return code
  *     covers argument validation and launch errors only; a fault inside a kernel surfaces at the
  *     caller's next synchronisation.
  *   - Tensors are dense, row-major, without padding, in the layouts given per argument.
  *   - kda_fwd keeps no global mutable state; kda_layer_fwd keeps one rocBLAS handle per device,
- *     created on first use under a lock.  Calls from several host threads are safe.
+ *     created on first use under a lock.  Calls from several host threads are safe, except
+ *     overlapping calls of kda_fwd_cp_noalloc on one device, which share its fixed scratch array.
  *   - Outputs must not alias inputs, except S_T == S0 (in-place state carry), which is allowed:
  *     each workgroup reads its slice of S0 before it writes the same slice of S_T.
  */
@@ -38,7 +40,9 @@ typedef enum {
     KDA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned pointer, bad flag */
     KDA_ERR_UNSUPPORTED = -2,  /* valid request this build has no kernel for (e.g. a head size) */
     KDA_ERR_HIP = -3,          /* the HIP runtime reported an error at launch */
-    KDA_ERR_WORKSPACE = -4     /* workspace pointer missing or smaller than the size query said */
+    KDA_ERR_WORKSPACE = -4,    /* workspace pointer missing or smaller than the size query said */
+    KDA_ERR_SCRATCH_LIMIT = -5 /* an allocation-free entry point was given a problem whose scratch
+                                  exceeds its fixed buffer */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -166,6 +170,28 @@ size_t kda_fwd_cp_workspace_size(const kda_fwd_desc* desc, int nseg);  /* 0 if n
 kda_status kda_fwd_cp(const kda_fwd_desc* desc, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const float* S0,
                       void* o, float* S_T, int nseg, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * kda_fwd_cp_noalloc -- kda_fwd_cp for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no workspace argument and
+ * no allocation.  The segment states live in a fixed array of KDA_CP_NOALLOC_SCRATCH_BYTES per
+ * device, part of the library's code object, held from the library's first use on a device until
+ * the process ends; its device address is looked up once per device (hipGetSymbolAddress) on the
+ * first call made with that device current.
+ *   desc, tensors, nseg : as kda_fwd_cp.  The caller still owns and passes every input and output.
+ * A problem whose plan needs more than kda_fwd_cp_workspace_size(desc, nseg) <=
+ * KDA_CP_NOALLOC_SCRATCH_BYTES (about 170 segment-heads: e.g. B = 1, H = 16 with 8 segments needs
+ * 24 MiB) returns KDA_ERR_SCRATCH_LIMIT before anything is launched.  Every call on one device shares
+ * that device's array: calls that overlap in time on one device (different streams, or different
+ * host threads without ordering) race on it and give wrong results; calls ordered on one stream are
+ * safe.  Nothing in the array needs to start at zero.  The result is bit for bit that of kda_fwd_cp
+ * with the same arguments.
+ * Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_SCRATCH_LIMIT or KDA_ERR_HIP.
+ */
+#define KDA_CP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+kda_status kda_fwd_cp_noalloc(const kda_fwd_desc* desc, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* S0,
+                              void* o, float* S_T, int nseg, hipStream_t stream);
 
 /*
  * kda_bwd -- gradients of kda_fwd (training; the explainer page's P3 section 5.1 says FlashKDA covers

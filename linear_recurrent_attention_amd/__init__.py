@@ -10,7 +10,7 @@ import torch
 from . import _lib
 from ._lib import KdaError  # noqa: F401
 
-__all__ = ["kda_fwd", "kda_fwd_ckpt", "kda_fwd_cp", "kda_bwd", "kda_decode", "kda_layer_fwd", "KdaError"]
+__all__ = ["kda_fwd", "kda_fwd_ckpt", "kda_fwd_cp", "kda_fwd_cp_noalloc", "kda_bwd", "kda_decode", "kda_layer_fwd", "KdaError"]
 
 _DT = {torch.float32: _lib.KDA_F32, torch.bfloat16: _lib.KDA_BF16}
 
@@ -99,6 +99,19 @@ def kda_fwd_cp(q, k, v, g, beta, S0=None, nseg: int = 0, scale: float = 1.0, o_d
     code = _lib.fwd_cp_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(ST),
                            int(nseg), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                            _stream(q.device))
+    _lib.check(code)
+    return o, ST
+
+
+def kda_fwd_cp_noalloc(q, k, v, g, beta, S0=None, nseg: int = 0, scale: float = 1.0, o_dtype=None,
+                       want_state: bool = True, out=None, state_out=None, precise: bool = False):
+    """kda_fwd_cp without a workspace (kda_fwd_cp_noalloc): the library's fixed per-device scratch
+    array holds the segment states, so the C call allocates nothing (pass out/state_out to allocate
+    nothing here either).  Calls that overlap in time on one device race on that array.
+    Raises KdaError with KDA_ERR_SCRATCH_LIMIT if the plan needs more than the array holds."""
+    desc, o, ST = _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, 0, precise, scale)
+    code = _lib.fwd_cp_noalloc_raw(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                                   _ptr(ST), int(nseg), _stream(q.device))
     _lib.check(code)
     return o, ST
 

@@ -13,6 +13,8 @@ KDA_ERR_INVALID_ARG = -1
 KDA_ERR_UNSUPPORTED = -2
 KDA_ERR_HIP = -3
 KDA_ERR_WORKSPACE = -4
+KDA_ERR_SCRATCH_LIMIT = -5
+KDA_CP_NOALLOC_SCRATCH_BYTES = 32 << 20  # the fixed per-device scratch of kda_fwd_cp_noalloc
 KDA_F32 = 0
 KDA_BF16 = 1
 KDA_FWD_PRECISE = 1  # kda_fwd_desc.flags
@@ -20,6 +22,7 @@ KDA_VALIDATE = 2
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_fwd_workspace_size", "kda_fwd", "kda_fwd_ckpt", "kda_decode", "kda_fwd_cp_workspace_size", "kda_fwd_cp",
+           "kda_fwd_cp_noalloc",
            "kda_bwd_workspace_size", "kda_bwd", "kda_layer_workspace_size", "kda_layer_fwd", "kda_error_string", "kda_version")
 
 
@@ -75,6 +78,9 @@ def lib():
             L.kda_fwd_cp.restype = ctypes.c_int
             L.kda_fwd_cp.argtypes = ([ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 8 + [ctypes.c_int, ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p])
+            L.kda_fwd_cp_noalloc.restype = ctypes.c_int
+            L.kda_fwd_cp_noalloc.argtypes = ([ctypes.POINTER(FwdDesc)] + [ctypes.c_void_p] * 8 + [ctypes.c_int,
+                                             ctypes.c_void_p])
             L.kda_bwd_workspace_size.restype = ctypes.c_size_t
             L.kda_bwd_workspace_size.argtypes = [ctypes.POINTER(FwdDesc)]
             L.kda_bwd.restype = ctypes.c_int
@@ -134,6 +140,11 @@ def decode_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, stream) -> int:
 
 def cp_workspace_size(desc: FwdDesc, nseg: int) -> int:
     return lib().kda_fwd_cp_workspace_size(ctypes.byref(desc), nseg)
+
+
+def fwd_cp_noalloc_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, nseg, stream) -> int:
+    """Call kda_fwd_cp_noalloc with integer device addresses (0 = NULL); returns the status code."""
+    return lib().kda_fwd_cp_noalloc(ctypes.byref(desc), q, k, v, g, beta, S0, o, S_T, nseg, stream)
 
 
 def fwd_cp_raw(desc: FwdDesc, q, k, v, g, beta, S0, o, S_T, nseg, ws, ws_bytes, stream) -> int:

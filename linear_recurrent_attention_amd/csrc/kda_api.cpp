@@ -88,6 +88,19 @@ kda_status run_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+// Params of the context-parallel forward (the bf16 path; every optional field off).
+kda::Params cp_params(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, const float* S0, void* o, float* S_T) {
+    kda::Params p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0; p.o = o; p.S_T = S_T;
+    p.B = desc->B; p.T = desc->T; p.H = desc->H; p.Dk = desc->Dk; p.Dv = desc->Dv; p.tstride = desc->T;
+    p.scale = desc->scale;
+    p.o_f32 = desc->o_dtype == KDA_F32;
+    p.precise = (desc->flags & KDA_FWD_PRECISE) != 0;
+    p.ckpt_chunks = 1;
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -164,14 +177,23 @@ kda_status kda_fwd_cp(const kda_fwd_desc* desc, const void* q, const void* k, co
     const size_t need = kda::cp_workspace_bytes(desc->B, desc->T, desc->H, nseg);
     if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return KDA_ERR_WORKSPACE;
     if (desc->T == 0) return run_fwd(desc, q, k, v, g, beta, S0, o, S_T, nullptr, 0, stream);
-    kda::Params p{};  // zero: every optional field off
-    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S0; p.o = o; p.S_T = S_T;
-    p.B = desc->B; p.T = desc->T; p.H = desc->H; p.Dk = desc->Dk; p.Dv = desc->Dv; p.tstride = desc->T;
-    p.scale = desc->scale;
-    p.o_f32 = desc->o_dtype == KDA_F32;
-    p.precise = (desc->flags & KDA_FWD_PRECISE) != 0;
-    p.ckpt_chunks = 1;
+    const kda::Params p = cp_params(desc, q, k, v, g, beta, S0, o, S_T);
     const hipError_t e = kda::launch_fwd_cp(p, nseg, static_cast<float*>(ws), stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_fwd_cp_noalloc(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const float* S0, void* o, float* S_T, int nseg, hipStream_t stream) {
+    const kda_status st = check_fwd(desc, q, k, v, g, beta, S0, o, S_T);
+    if (st != KDA_OK) return st;
+    if (nseg < 0 || nseg > 4096) return KDA_ERR_INVALID_ARG;
+    if (desc->io_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if ((long long)desc->B * desc->H * (nseg ? nseg : 1) > (1LL << 30)) return KDA_ERR_INVALID_ARG;
+    if (kda::cp_workspace_bytes(desc->B, desc->T, desc->H, nseg) > KDA_CP_NOALLOC_SCRATCH_BYTES)
+        return KDA_ERR_SCRATCH_LIMIT;
+    if (desc->T == 0) return run_fwd(desc, q, k, v, g, beta, S0, o, S_T, nullptr, 0, stream);
+    const kda::Params p = cp_params(desc, q, k, v, g, beta, S0, o, S_T);
+    const hipError_t e = kda::launch_fwd_cp_noalloc(p, nseg, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -227,6 +249,9 @@ const char* kda_error_string(kda_status s) {
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: no kernel for this configuration";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error at launch";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+        case KDA_ERR_SCRATCH_LIMIT:
+            return "KDA_ERR_SCRATCH_LIMIT: the problem needs more scratch than the fixed buffer of an allocation-free "
+                   "entry point holds";
     }
     return "unknown kda_status";
 }

@@ -16,6 +16,9 @@
 // the whole multiple of nseg*32 this way and the remaining tail with the plain kernel from the last
 // segment's state.  This is three passes of work in exchange for nseg times more workgroups: worth it
 // when 2*B*H workgroups leave most of the 256 compute units idle.
+#include <mutex>
+
+#include "kda.h"
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -181,6 +184,49 @@ hipError_t launch_fwd_cp(const Params& u, int nseg_req, float* ws, hipStream_t s
         }
     }
     return e;
+}
+
+// Scratch of kda_fwd_cp_noalloc: the segment states (S_hat, M, S_start) in a fixed device array, so
+// that the call allocates nothing.  Each device holds its own copy of the array from the moment the
+// library's code object is loaded on it until the process ends.  Every call on a device shares that
+// device's copy; nothing in it needs to start at zero (each pass writes what the next one reads).
+namespace {
+
+constexpr size_t kNoallocScratchBytes = KDA_CP_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoallocScratchBytes % 256 == 0, "whole 256-byte blocks");
+static __device__ __align__(256) float scratch[kNoallocScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};  // device address of `scratch` per device, looked up once
+
+// Device address of the current device's copy of `scratch`.  In host code the array's name stands
+// for a host-side shadow, not device memory, so kernels are given this address instead.
+hipError_t scratch_on_current_device(float** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch[dev] = static_cast<float*>(ptr);
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_cp_noalloc(const Params& u, int nseg_req, hipStream_t stream) {
+    if (cp_workspace_bytes(u.B, u.T, u.H, nseg_req) > kNoallocScratchBytes) return hipErrorInvalidValue;
+    float* ws = nullptr;
+    const hipError_t e = scratch_on_current_device(&ws);
+    if (e != hipSuccess) return e;
+    return launch_fwd_cp(u, nseg_req, ws, stream);
 }
 
 }  // namespace kda

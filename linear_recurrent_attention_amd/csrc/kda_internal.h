@@ -60,6 +60,9 @@ hipError_t launch_decode(const Params& p, bool in_bf16, hipStream_t stream);  //
 // in-device context parallelism (bf16 I/O, Dk = Dv = 128): segment count nseg_req (0 = automatic)
 size_t cp_workspace_bytes(int B, int T, int H, int nseg_req);
 hipError_t launch_fwd_cp(const Params& p, int nseg_req, float* ws, hipStream_t stream);
+// launch_fwd_cp with the library's static per-device scratch array (KDA_CP_NOALLOC_SCRATCH_BYTES);
+// hipErrorInvalidValue if the plan needs more than that
+hipError_t launch_fwd_cp_noalloc(const Params& p, int nseg_req, hipStream_t stream);
 // backward: intervals of 32 tokens (bf16 inputs, D = 128) or 16 (float32 inputs, D in {64, 128})
 size_t bwd_workspace_bytes(int B, int T, int H, int D, bool in_bf16);
 hipError_t launch_bwd(const BwdParams& p, bool in_bf16, bool do_bf16, bool precise, float* ws, hipStream_t stream);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_error_strings():
     L = _lib.lib()
     assert L.kda_version() >= 100
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -5, 7):
         assert L.kda_error_string(code)
 
 
@@ -239,6 +239,30 @@ def test_cp_argument_checks():
     assert call_cp(desc(B=0), 2) == _lib.KDA_ERR_INVALID_ARG
     # T = 0: the state copy only (nothing launched without S_T)
     assert call_cp(desc(T=0), 4, q=0, k=0, v=0, g=0, beta=0, o=0) == _lib.KDA_OK
+
+
+def call_cp_noalloc(d, nseg, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=0, o=FAKE + 0x100000, S_T=0)
+    a.update(kw)
+    return _lib.fwd_cp_noalloc_raw(d, a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["o"], a["S_T"], nseg, None)
+
+
+def test_cp_noalloc_argument_checks_and_scratch_limit():
+    """kda_fwd_cp_noalloc checks what kda_fwd_cp checks, and refuses, before any device call, a plan
+    whose segment states exceed its fixed scratch array."""
+    limit = _lib.KDA_CP_NOALLOC_SCRATCH_BYTES
+    big = desc(B=1, T=1 << 20, H=32)
+    assert _lib.cp_workspace_size(big, 8) > limit
+    assert call_cp_noalloc(big, 8) == _lib.KDA_ERR_SCRATCH_LIMIT
+    assert call_cp_noalloc(desc(B=4, T=1 << 16, H=16), 4) == _lib.KDA_ERR_SCRATCH_LIMIT  # 4 rows x 4 segments x 16 heads
+    assert _lib.cp_workspace_size(desc(B=1, T=1 << 20, H=16), 0) <= limit                # the long-context plan fits
+    assert "SCRATCH_LIMIT" in _lib.lib().kda_error_string(_lib.KDA_ERR_SCRATCH_LIMIT).decode()
+    assert call_cp_noalloc(big, -1) == _lib.KDA_ERR_INVALID_ARG
+    assert call_cp_noalloc(desc(B=0), 2) == _lib.KDA_ERR_INVALID_ARG
+    assert call_cp_noalloc(desc(io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_F32, Dk=64, Dv=64), 2) == _lib.KDA_ERR_UNSUPPORTED
+    assert _lib.lib().kda_fwd_cp_noalloc(None, *([None] * 8), 2, None) == _lib.KDA_ERR_INVALID_ARG
+    # T = 0: the state copy only (nothing launched without S_T), so no scratch is touched
+    assert call_cp_noalloc(desc(T=0), 4, q=0, k=0, v=0, g=0, beta=0, o=0) == _lib.KDA_OK
 
 
 def test_bwd_workspace_size():
