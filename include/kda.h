@@ -19,9 +19,9 @@
  *     covers argument validation and launch errors only; a fault inside a kernel surfaces at the
  *     caller's next synchronisation.
  *   - Tensors are dense, row-major, without padding, in the layouts given per argument.
- *   - kda_fwd keeps no global mutable state; kda_layer_fwd keeps one rocBLAS handle per device,
- *     created on first use under a lock.  Calls from several host threads are safe, except
- *     overlapping calls of kda_fwd_cp_noalloc on one device, which share its fixed scratch array.
+ *   - No entry point keeps global mutable state, except kda_fwd_cp_noalloc's fixed scratch array
+ *     (one per device).  Calls from several host threads are safe, except overlapping calls of
+ *     kda_fwd_cp_noalloc on one device, which share that array.
  *   - Outputs must not alias inputs, except S_T == S0 (in-place state carry), which is allowed:
  *     each workgroup reads its slice of S0 before it writes the same slice of S_T.
  */
@@ -234,9 +234,9 @@ kda_status kda_bwd(const kda_fwd_desc* desc, const void* q, const void* k, const
  * --------------------------------------------------------------------------------------------- */
 typedef struct {
     int B, T;           /* batch, tokens (T >= 1) */
-    int d_model;        /* width of x and y (multiple of 8) */
+    int d_model;        /* width of x and y (multiple of 32; other widths are KDA_ERR_UNSUPPORTED) */
     int H, Dk, Dv;      /* heads; Dk = Dv = 128 */
-    int rank;           /* rank of the decay projection W_down W_up (multiple of 8) */
+    int rank;           /* rank of the decay projection W_down W_up (multiple of 16) */
     int conv;           /* short-convolution taps; 4 */
     float scale;        /* multiplies q in the readout; 1.0 for the plain readout */
     int flags;          /* reserved, must be 0 */
@@ -265,17 +265,20 @@ size_t kda_layer_workspace_size(const kda_layer_desc* desc);
 
 /*
  * kda_layer_fwd -- y = layer(x).
- *   x              : [B, T, d_model] bf16
+ *   x              : [B, T, d_model] bf16, 16-byte aligned
  *   S0, S_T        : [B, H, Dk, Dv] float32 KDA state in / out (NULL: zeros / not written; may alias)
  *   conv_state_in  : [B, 3, 2*H*Dk] float32, the last 3 pre-convolution q rows then k rows of the
  *                    previous segment, oldest first (NULL: zeros)
  *   conv_state_out : same layout for this segment's end (NULL: not written); must not alias the input
- *   y              : [B, T, d_model] bf16
+ *   y              : [B, T, d_model] bf16, 16-byte aligned
  *   ws             : device workspace of at least kda_layer_workspace_size(desc) bytes, 256-byte aligned
- * The eight projections run through rocBLAS (bf16 operands, float32 accumulation; the rank-R
- * up-projection in float32); rocBLAS keeps one handle per device for the life of the process and
- * may allocate its own device memory on first use.  Returns KDA_OK, KDA_ERR_INVALID_ARG,
- * KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE or KDA_ERR_HIP.
+ * The projections run on the library's bf16 matrix-core GEMM with float32 sums: one product over
+ * the concatenated q, k, v, gate, decay-down and beta weights; the rank-R up-projection over the
+ * hi and lo bf16 halves of the float32 down-projection (about 16 significant bits), with the decay
+ * gate applied in its epilogue; the output projection.  The weights are transposed into the
+ * workspace on each call.  Nothing is allocated and no state is kept between calls.
+ * Returns KDA_OK, KDA_ERR_INVALID_ARG (also for a misaligned x or y), KDA_ERR_UNSUPPORTED,
+ * KDA_ERR_WORKSPACE or KDA_ERR_HIP.
  */
 kda_status kda_layer_fwd(const kda_layer_desc* desc, const void* x, const kda_layer_weights* weights,
                          const float* S0, const float* conv_state_in, void* y, float* S_T,

@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libkda.so")
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["kda_api.cpp", "kda_fwd_bf16.hip", "kda_fwd_f32.hip", "kda_layer.hip", "kda_decode.hip", "kda_cp.hip", "kda_bwd.hip",
-           "kda_validate.hip"]
+           "kda_validate.hip", "kda_gemm.hip"]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 # packed-fp32 instructions are disabled for all device code
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -41,8 +41,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-L/opt/rocm/lib", "-lrocblas",
-           "-Wl,-rpath,/opt/rocm/lib"]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

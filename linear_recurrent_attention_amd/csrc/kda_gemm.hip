@@ -1,0 +1,280 @@
+// bf16 matrix-core GEMM for the fused layer's projections, on gfx950.
+//
+//   C[m][n] = sum_k A[m][k] * Bt[n][k]      (A: [M][K] row-major, Bt: [N][K] row-major, float32 sums)
+//
+// Both operands are read along k, so their tiles go to LDS row by row and every matrix-core operand
+// is one 16-byte LDS read.  The layer's weights are stored [in][out]; they are transposed into this
+// form on each call (transpose_kernel), which costs a few microseconds against the products.
+//
+// Mapping.  A workgroup computes a 256 x 256 tile of C with 8 waves (2 x 4), each a 128 x 64 block
+// of 8 x 4 products v_mfma_f32_16x16x32_bf16.  The operand tiles move 32 columns of k at a time,
+// straight from global memory into a four-deep ring of LDS stages (global_load_lds_dwordx4: each
+// lane's 16 bytes land at the stage base plus 16 * lane, so the lanes are given the global chunks
+// that the XOR-swizzled layout puts there), issued three steps ahead; a step waits for its own
+// loads with an explicit vmcnt and then meets the other waves at one barrier.  Tiles are numbered
+// so that each XCD (the hardware deals workgroups to the eight XCDs in turn) gets one contiguous
+// range of them, ordered in groups of eight tile rows, so that the workgroups running together on
+// one XCD share A and Bt panels in its L2.
+//
+// Epilogue.  Each wave rewrites its block row-major through LDS and stores whole rows (16 lanes per
+// 256-byte row segment).  The columns of C may be split into up to six segments, each written to
+// its own matrix (pointer and row stride), so that one product over concatenated weights fills
+// separate buffers; or the decay gate of the layer is applied on the way out (GEMM_GATE).
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace gemm {
+
+constexpr int BM = 256, BN = 256, BK = 32, NST = 4;
+constexpr int NW = 8, NTHR = 64 * NW;
+constexpr int WM = 128, WN = 64;  // per wave
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void g_void;
+
+// LDS tiles [rows][32] bf16 (64-byte rows): 16-byte chunk c of row r is stored at chunk
+// c ^ ((r >> 2) & 3), so that the 16 rows of a matrix-core operand read (one chunk each) fall in 16
+// distinct bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + 8 * (chunk ^ ((row >> 2) & 3)); }
+
+struct alignas(16) Smem {
+    uint16_t a[NST][BM * BK];
+    uint16_t b[NST][BN * BK];
+};
+static_assert(sizeof(Smem) >= NW * 64 * 64 * sizeof(float), "the epilogue's staging fits in the operand ring");
+
+// s_waitcnt with only vmcnt <= N (N < 64) constrained
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
+// execution barrier without a memory fence: the operand loads are waited for explicitly above it
+__device__ __forceinline__ void exec_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __builtin_amdgcn_exp2f(-x * kLog2e)); }
+
+template <bool OUT_F32, int EPI>
+__global__ void __launch_bounds__(NTHR, 1) gemm_nt_kernel(const uint16_t* __restrict__ A, int lda,
+                                                          const uint16_t* __restrict__ Bt, int ldb, GemmOut out,
+                                                          int M, int N, int K) {
+    __shared__ Smem sm;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    // tile of this workgroup: XCD-contiguous ranges, grouped by eight tile rows
+    const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN, total = tm * tn;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, q = total >> 3, rem = total & 7;
+    const int pid = xcd * q + min(xcd, rem) + slot;
+    constexpr int GM = 8;
+    const int in_group = GM * tn, first_m = (pid / in_group) * GM, gsize = min(tm - first_m, GM);
+    const int im = first_m + (pid % in_group) % gsize, jn = (pid % in_group) / gsize;
+    const int m0 = im * BM, n0 = jn * BN;
+
+    // loads: wave w moves rows [16w, 16w + 16) and [16w + 128, 16w + 144) of both tiles, one 1 KB
+    // instruction each; lane l takes row base + l/4 at physical chunk l%4, i.e. logical chunk
+    // (l%4) ^ ((row >> 2) & 3).  Rows past M (N) read row M-1 (N-1); their results are never stored.
+    const uint16_t* ag[2];
+    const uint16_t* bg[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = 16 * wave + 128 * h + (lane >> 2);
+        const int lc = (lane & 3) ^ ((row >> 2) & 3);
+        ag[h] = A + (size_t)min(m0 + row, M - 1) * lda + 8 * lc;
+        bg[h] = Bt + (size_t)min(n0 + row, N - 1) * ldb + 8 * lc;
+    }
+    auto issue = [&](int kt, int st) {
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = 16 * wave + 128 * h;
+            __builtin_amdgcn_global_load_lds((g_void*)(ag[h] + k0), (lds_void*)&sm.a[st][row * BK], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((g_void*)(bg[h] + k0), (lds_void*)&sm.b[st][row * BK], 16, 0, 0);
+        }
+    };
+
+    const int wm = wave >> 2, wn = wave & 3;
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = K / BK;
+    for (int s = 0; s < NST - 1 && s < nk; ++s) issue(s, s);
+    for (int kt = 0; kt < nk; ++kt) {
+        // tile kt in LDS: this wave's later loads (at most two tiles, four instructions each) may stay
+        // in flight; the barrier then covers every wave's loads of tile kt, and every wave is done with
+        // stage (kt - 1) % 4, which tile kt + 3 refills
+        const int later = min(2, nk - 1 - kt);
+        if (later == 2) wait_vm<8>(); else if (later == 1) wait_vm<4>(); else wait_vm<0>();
+        exec_barrier();
+        if (kt + NST - 1 < nk) issue(kt + NST - 1, (kt + NST - 1) % NST);
+        const uint16_t* sa = sm.a[kt % NST];
+        const uint16_t* sb = sm.b[kt % NST];
+        u32x4 af[8], bf[4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const u32x4*>(&sa[swz(WM * wm + 16 * i + l16, g4)]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const u32x4*>(&sb[swz(WN * wn + 16 * j + l16, g4)]);
+        // Bt as the first operand: lane (l16, g4) gets row m = l16 of the block, columns 4*g4 .. 4*g4+3
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(bf[j], af[i], acc[i][j]);
+    }
+
+    // epilogue through LDS: each wave rewrites its 128 x 64 block row-major in its own 16 KB of the
+    // ring (64 rows at a time, 16-byte blocks XOR-swizzled by row), then stores whole rows: lane
+    // (sr, l16) stores columns 4*l16 .. 4*l16+3 of row 4*r4 + sr
+    wait_lgkm0();
+    exec_barrier();  // every wave is done with the operand tiles
+    float* stage = reinterpret_cast<float*>(&sm) + wave * (64 * 64);
+    const int sr = lane >> 4, sc = 4 * (lane & 15);
+    const int nb = n0 + WN * wn + sc;  // this lane's first column
+    int seg = 0;
+#pragma unroll
+    for (int t = 1; t < GemmOut::kMaxSeg; ++t) seg += (t < out.nseg && nb >= out.start[t]) ? 1 : 0;
+    const int c = nb - out.start[seg];
+    const int lim = min(min(4, N - nb), out.start[seg + 1] - nb);  // segments start on multiples of 4
+    char* base = static_cast<char*>(out.ptr[seg]);
+    const size_t ld = (size_t)out.ld[seg];
+    const bool vec = lim == 4 && (out.ld[seg] & 3) == 0;  // (segment bases are 16-byte aligned)
+    f32x4 gb = {0.f, 0.f, 0.f, 0.f};
+    float ga = 0.f;
+    if constexpr (EPI == GEMM_GATE) {  // log decay -5 sigmoid(exp(A_h) (z + b)), head h = column / 128
+        if (lim > 0) {
+            for (int e = 0; e < lim; ++e) gb[e] = out.bias[nb + e];
+            ga = __builtin_amdgcn_exp2f(out.head_scale[nb >> 7] * kLog2e);
+        }
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4*>(&stage[(16 * i + l16) * 64 + 4 * ((4 * j + g4) ^ l16)]) = acc[4 * half + i][j];
+        wait_lgkm0();
+#pragma unroll
+        for (int r4 = 0; r4 < 16; ++r4) {
+            const int rl = 4 * r4 + sr;
+            f32x4 v = *reinterpret_cast<const f32x4*>(&stage[rl * 64 + 4 * ((sc >> 2) ^ (rl & 15))]);
+            const int m = m0 + WM * wm + 64 * half + rl;
+            if (m >= M || lim <= 0) continue;
+            if constexpr (EPI == GEMM_GATE) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = -5.f * sigmoid_f(ga * (v[e] + gb[e]));
+            }
+            if constexpr (OUT_F32) {
+                float* dst = reinterpret_cast<float*>(base) + (size_t)m * ld + c;
+                if (vec) *reinterpret_cast<f32x4*>(dst) = v;
+                else for (int e = 0; e < lim; ++e) dst[e] = v[e];
+            } else {
+                uint16_t* dst = reinterpret_cast<uint16_t*>(base) + (size_t)m * ld + c;
+                if (vec) *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+                else for (int e = 0; e < lim; ++e) dst[e] = (uint16_t)(pack_bf16(v[e], 0.f) & 0xffffu);
+            }
+        }
+        wait_lgkm0();  // the next half overwrites the staging rows
+    }
+}
+
+// dst[n * ldd + k] = src[k * lds + n] for k < K, n < N (bf16), through a 64 x 64 tile.  VEC: rows of
+// src and dst hold whole aligned 16-byte chunks (lds, ldd multiples of 8, 16-byte aligned bases)
+template <bool VEC>
+__global__ void __launch_bounds__(256) transpose_kernel(const uint16_t* __restrict__ src, int lds, int K, int N,
+                                                        uint16_t* __restrict__ dst, int ldd) {
+    __shared__ uint16_t t[64][72];  // [k][n], rows padded by 16 bytes
+    const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+        const int r = e >> 3, c8 = 8 * (e & 7);  // k row, first n of the chunk
+        const int k = k0 + r, n = n0 + c8;
+        if (VEC && k < K && n + 8 <= N) {
+            *reinterpret_cast<u32x4*>(&t[r][c8]) = *reinterpret_cast<const u32x4*>(src + (size_t)k * lds + n);
+        } else {
+            for (int x = 0; x < 8; ++x) t[r][c8 + x] = (k < K && n + x < N) ? src[(size_t)k * lds + n + x] : (uint16_t)0;
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+        const int r = e >> 3, c8 = 8 * (e & 7);  // n row, first k of the chunk
+        const int n = n0 + r, k = k0 + c8;
+        if (n >= N) continue;
+        uint16_t v[8];
+        for (int x = 0; x < 8; ++x) v[x] = t[c8 + x][r];
+        if (VEC && k + 8 <= K) {
+            u32x4 w;
+            for (int x = 0; x < 4; ++x) w[x] = (uint32_t)v[2 * x] | ((uint32_t)v[2 * x + 1] << 16);
+            *reinterpret_cast<u32x4*>(dst + (size_t)n * ldd + k) = w;
+        } else {
+            for (int x = 0; x < 8; ++x)
+                if (k + x < K) dst[(size_t)n * ldd + k + x] = v[x];
+        }
+    }
+}
+
+// float32 [M][R] (row stride lds) -> bf16 [M][2R]: hi = bf16(x) in columns [0, R), lo = bf16(x - hi) in [R, 2R)
+__global__ void split_rows_kernel(const float* __restrict__ src, int lds, int M, int R, uint16_t* __restrict__ dst) {
+    for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < (long)M * R; e += (long)gridDim.x * blockDim.x) {
+        const long m = e / R, c = e % R;
+        const float x = src[m * lds + c];
+        const uint32_t h = pack_bf16(x, 0.f) & 0xffffu;
+        const uint32_t l = pack_bf16(x - __uint_as_float(h << 16), 0.f) & 0xffffu;
+        dst[m * 2 * R + c] = (uint16_t)h;
+        dst[m * 2 * R + R + c] = (uint16_t)l;
+    }
+}
+
+unsigned grid1(long n) {
+    const long b = (n + 255) / 256;
+    return (unsigned)(b < 1 ? 1 : (b > 8192 ? 8192 : b));
+}
+
+}  // namespace gemm
+
+hipError_t launch_gemm_nt(const uint16_t* A, int lda, const uint16_t* Bt, int ldb, const GemmOut& out, bool out_f32,
+                          int M, int N, int K, hipStream_t stream) {
+    using namespace gemm;
+    if (M <= 0 || N <= 0 || K <= 0 || K % BK || lda % 8 || ldb % 8 || out.nseg < 1 || out.nseg > GemmOut::kMaxSeg)
+        return hipErrorInvalidValue;
+    if ((reinterpret_cast<uintptr_t>(A) & 15) || (reinterpret_cast<uintptr_t>(Bt) & 15)) return hipErrorInvalidValue;
+    for (int s = 0; s < out.nseg; ++s)
+        if (out.start[s] % 4 || out.start[s + 1] <= out.start[s] || !out.ptr[s] || out.ld[s] < 1 ||
+            (reinterpret_cast<uintptr_t>(out.ptr[s]) & 15))
+            return hipErrorInvalidValue;
+    if (out.start[0] != 0 || out.start[out.nseg] < N) return hipErrorInvalidValue;
+    if (out.epi == GEMM_GATE && (out.nseg != 1 || !out_f32 || !out.bias || !out.head_scale)) return hipErrorInvalidValue;
+    const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (tiles > (1L << 30)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)tiles), block(NTHR);
+    if (out.epi == GEMM_GATE)
+        hipLaunchKernelGGL((gemm_nt_kernel<true, GEMM_GATE>), grid, block, 0, stream, A, lda, Bt, ldb, out, M, N, K);
+    else if (out_f32)
+        hipLaunchKernelGGL((gemm_nt_kernel<true, GEMM_STORE>), grid, block, 0, stream, A, lda, Bt, ldb, out, M, N, K);
+    else
+        hipLaunchKernelGGL((gemm_nt_kernel<false, GEMM_STORE>), grid, block, 0, stream, A, lda, Bt, ldb, out, M, N, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* src, int lds, int K, int N, uint16_t* dst, int ldd, hipStream_t stream) {
+    if (K <= 0 || N <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((K + 63) / 64));
+    const bool vec = lds % 8 == 0 && ldd % 8 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+    if (vec)
+        hipLaunchKernelGGL(gemm::transpose_kernel<true>, grid, dim3(256), 0, stream, src, lds, K, N, dst, ldd);
+    else
+        hipLaunchKernelGGL(gemm::transpose_kernel<false>, grid, dim3(256), 0, stream, src, lds, K, N, dst, ldd);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_rows(const float* src, int lds, int M, int R, uint16_t* dst, hipStream_t stream) {
+    hipLaunchKernelGGL(gemm::split_rows_kernel, dim3(gemm::grid1((long)M * R)), dim3(256), 0, stream, src, lds, M, R,
+                       dst);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -60,6 +60,29 @@ hipError_t launch_decode(const Params& p, bool in_bf16, hipStream_t stream);  //
 // in-device context parallelism (bf16 I/O, Dk = Dv = 128): segment count nseg_req (0 = automatic)
 size_t cp_workspace_bytes(int B, int T, int H, int nseg_req);
 hipError_t launch_fwd_cp(const Params& p, int nseg_req, float* ws, hipStream_t stream);
+// bf16 GEMM C = A Bt^T (A [M][K], Bt [N][K] row-major; K a multiple of 32, both row strides multiples
+// of 8, A and Bt 16-byte aligned), float32 sums; the columns of C split into segments
+// [start[s], start[s+1]), each written to ptr[s] (row stride ld[s], column start[s] at column 0,
+// 16-byte aligned), as float32 or bf16.  Segment starts must be multiples of 4, start[0] = 0 and
+// start[nseg] >= N.  epi = GEMM_GATE (one float32 segment) writes -5 sigmoid(exp(head_scale[n / 128])
+// (C + bias[n])) instead of C: the decay gate of the fused layer.
+enum { GEMM_STORE = 0, GEMM_GATE = 1 };
+struct GemmOut {
+    static constexpr int kMaxSeg = 6;
+    void* ptr[kMaxSeg];
+    int start[kMaxSeg + 1];
+    int ld[kMaxSeg];
+    int nseg;
+    int epi;
+    const float* bias;
+    const float* head_scale;
+};
+hipError_t launch_gemm_nt(const uint16_t* A, int lda, const uint16_t* Bt, int ldb, const GemmOut& out, bool out_f32,
+                          int M, int N, int K, hipStream_t stream);
+// dst[n * ldd + k] = src[k * lds + n] for k < K, n < N (bf16)
+hipError_t launch_transpose_bf16(const uint16_t* src, int lds, int K, int N, uint16_t* dst, int ldd, hipStream_t stream);
+// float32 [M][R] (row stride lds) -> bf16 [M][2R]: bf16(x) in columns [0, R), bf16(x - that) in [R, 2R)
+hipError_t launch_split_rows(const float* src, int lds, int M, int R, uint16_t* dst, hipStream_t stream);
 // launch_fwd_cp with the library's static per-device scratch array (KDA_CP_NOALLOC_SCRATCH_BYTES);
 // hipErrorInvalidValue if the plan needs more than that
 hipError_t launch_fwd_cp_noalloc(const Params& p, int nseg_req, hipStream_t stream);

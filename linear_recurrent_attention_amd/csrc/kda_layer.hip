@@ -12,9 +12,12 @@
 // of the previous 3 tokens comes from conv_state_in (zeros if absent) and the last 3 pre-conv
 // rows go to conv_state_out.  L2 and RMSNorm use eps = 1e-6 inside the square root.
 //
-// The plain projections run on rocBLAS (bf16 operands, float32 accumulate and output; the
-// rank-128 up-projection in float32).  The element-wise work around the core is fused into two
-// kernels, one wave per (token, head) with two channels per lane:
+// The projections run on the library's bf16 matrix-core GEMM (float32 sums): one product over the
+// concatenated q, k, v, gate, decay-down and beta weights, whose column segments land in separate
+// buffers; the rank-R decay up-projection as a product over [hi | lo] bf16 halves of the float32
+// down-projection (about 16 significant bits), and the output projection.  The weights are taken
+// into the products' [out][in] form in the workspace on each call.  The element-wise work around
+// the core is fused into two kernels, one wave per (token, head) with two channels per lane:
 //   prologue: short conv + SiLU + L2 on q and k, the decay gate, beta (q, k, v stay float32:
 //             the core's float32-input variant reads them, so the per-head RMSNorm does not
 //             amplify a bf16 rounding of the core's inputs);
@@ -22,11 +25,6 @@
 #include "kda_common.h"
 #include "kda_internal.h"
 #include "../../include/kda.h"
-
-#include <rocblas/rocblas.h>
-
-#include <mutex>
-#include <vector>
 
 namespace kda {
 namespace layer {
@@ -39,17 +37,13 @@ struct ProParams {
     const float* pq;       // [B*T, HD] pre-conv q projection
     const float* pk;       // [B*T, HD] pre-conv k projection
     const float* pv;       // [B*T, HD]
-    const float* pz;       // [B*T, HD] low-rank decay logit (without bias)
     const float* pbeta;    // [B*T, H]  beta logit
     const float* conv_q;   // [HD, 4]
     const float* conv_k;   // [HD, 4]
-    const float* b_alpha;  // [HD]
-    const float* A;        // [H]
     const float* state_in; // [B, 3, 2*HD] or null
     float* q;              // [B*T, HD] = [B, T, H, D]
     float* k;
     float* v;
-    float* g;              // [B*T, HD]
     float* beta;           // [B*T, H]
 };
 
@@ -103,19 +97,16 @@ __global__ void __launch_bounds__(256) prologue_kernel(ProParams p) {
             xk[j] = *reinterpret_cast<const float2*>(sw + p.HD + c);
         }
     }
-    const float2 ba = *reinterpret_cast<const float2*>(p.b_alpha + c);
-    const float ea = fexp(p.A[h]);
     // PRO_U tokens at a time: all their projection rows are read first (rows past t1 read row t1 - 1
     // and are not used), so that each wave keeps 3 * PRO_U reads in flight instead of 3
     for (int t = t0; t < t1; t += PRO_U) {
-        float2 cq[PRO_U], ck[PRO_U], z[PRO_U];
+        float2 cq[PRO_U], ck[PRO_U];
         float bl[PRO_U];
 #pragma unroll
         for (int u = 0; u < PRO_U; ++u) {
             const size_t row = (size_t)b * p.T + min(t + u, t1 - 1);
             cq[u] = *reinterpret_cast<const float2*>(p.pq + row * p.HD + c);
             ck[u] = *reinterpret_cast<const float2*>(p.pk + row * p.HD + c);
-            z[u] = *reinterpret_cast<const float2*>(p.pz + row * p.HD + c);
             bl[u] = p.pbeta[row * p.H + h];
         }
 #pragma unroll
@@ -138,8 +129,6 @@ __global__ void __launch_bounds__(256) prologue_kernel(ProParams p) {
             const float kn = rsqrtf(wave_sum(k0 * k0 + k1 * k1) + EPS);
             *reinterpret_cast<float2*>(p.q + rc) = make_float2(q0 * qn, q1 * qn);
             *reinterpret_cast<float2*>(p.k + rc) = make_float2(k0 * kn, k1 * kn);
-            *reinterpret_cast<float2*>(p.g + rc) =
-                make_float2(-5.f * sigmoidf_(ea * (z[u].x + ba.x)), -5.f * sigmoidf_(ea * (z[u].y + ba.y)));
             if (lane == 0) p.beta[row * p.H + h] = sigmoidf_(bl[u]);
         }
     }
@@ -187,33 +176,9 @@ __global__ void bf16_to_f32_kernel(const uint16_t* src, float* dst, long n) {
         dst[i] = __uint_as_float((uint32_t)src[i] << 16);
 }
 
-// ------------------------------------------------------------------------------------------------
-// rocBLAS handles, one per device, created on first use and kept for the process
-std::mutex g_blas_mu;
-std::vector<rocblas_handle> g_blas;
-
-rocblas_handle blas_handle(int dev) {
-    std::lock_guard<std::mutex> lk(g_blas_mu);
-    if ((int)g_blas.size() <= dev) g_blas.resize(dev + 1, nullptr);
-    if (!g_blas[dev]) {
-        rocblas_handle hd = nullptr;
-        if (rocblas_create_handle(&hd) != rocblas_status_success) return nullptr;
-        g_blas[dev] = hd;
-    }
-    return g_blas[dev];
-}
-
-// row-major C[M,N] = A[M,K] B[K,N], i.e. column-major C^T = B^T A^T
-rocblas_status gemm_rm(rocblas_handle hd, int M, int N, int K, const void* Am, rocblas_datatype at, const void* Bm,
-                       rocblas_datatype bt, void* Cm, rocblas_datatype ct) {
-    const float alpha = 1.f, beta = 0.f;
-    return rocblas_gemm_ex(hd, rocblas_operation_none, rocblas_operation_none, N, M, K, &alpha, Bm, bt, N, Am, at, K,
-                           &beta, Cm, ct, N, Cm, ct, N, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-}
-
 struct Workspace {
-    float *pq, *pk, *pv, *pg, *pz, *pdown, *pbeta, *wup32, *g, *beta, *o, *q, *k, *cp;
-    uint16_t* gated;
+    float *pq, *pk, *pv, *pg, *pdown, *pbeta, *g, *beta, *o, *q, *k, *cp;
+    uint16_t *gated, *wcat, *wup2, *wo, *down2;
     size_t bytes;
 };
 
@@ -230,16 +195,19 @@ Workspace carve(const kda_layer_desc* d, char* base) {
     w.pk = (float*)take(BT * HD * 4);
     w.pv = (float*)take(BT * HD * 4);
     w.pg = (float*)take(BT * HD * 4);
-    w.pz = (float*)take(BT * HD * 4);
     w.pdown = (float*)take(BT * d->rank * 4);
     w.pbeta = (float*)take(BT * d->H * 4);
-    w.wup32 = (float*)take((size_t)d->rank * HD * 4);
     w.g = (float*)take(BT * HD * 4);
     w.beta = (float*)take(BT * d->H * 4);
     w.o = (float*)take(BT * HD * 4);
     w.q = (float*)take(BT * HD * 4);
     w.k = (float*)take(BT * HD * 4);
     w.gated = (uint16_t*)take(BT * HD * 2);
+    const size_t ncat = 4 * HD + d->rank + d->H;  // rows of the concatenated input-projection weights
+    w.wcat = (uint16_t*)take(ncat * d->d_model * 2);
+    w.wup2 = (uint16_t*)take(HD * 2 * d->rank * 2);
+    w.wo = (uint16_t*)take((size_t)d->d_model * HD * 2);
+    w.down2 = (uint16_t*)take(BT * 2 * d->rank * 2);
     w.cp = (float*)take(cp_workspace_bytes(d->B, d->T, d->H, 0));  // the core's context parallelism
     w.bytes = off;
     return w;
@@ -255,7 +223,9 @@ kda_status check_layer(const kda_layer_desc* d, const void* x, const kda_layer_w
     if (!d || !w || !x || !y) return KDA_ERR_INVALID_ARG;
     if (d->B < 1 || d->T < 1 || d->H < 1 || d->d_model < 1 || d->rank < 1 || d->flags != 0) return KDA_ERR_INVALID_ARG;
     if (d->Dk != D || d->Dv != D || d->conv != 4) return KDA_ERR_UNSUPPORTED;
-    if (d->d_model % 8 != 0 || d->rank % 8 != 0) return KDA_ERR_UNSUPPORTED;
+    if (d->d_model % 32 != 0 || d->rank % 16 != 0) return KDA_ERR_UNSUPPORTED;  // the GEMMs' k steps
+    if ((reinterpret_cast<uintptr_t>(x) & 15) != 0 || (reinterpret_cast<uintptr_t>(y) & 15) != 0)
+        return KDA_ERR_INVALID_ARG;
     if ((long long)d->B * d->T > (1LL << 30) || (long long)d->B * d->T * d->H * D > (1LL << 40)) return KDA_ERR_INVALID_ARG;
     if (!w->Wq || !w->Wk || !w->Wv || !w->Wg || !w->Wo || !w->Wbeta || !w->Wdown || !w->Wup || !w->conv_q ||
         !w->conv_k || !w->b_alpha || !w->A || !w->rms_w)
@@ -281,36 +251,56 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
     if (!ws || ws_bytes < W.bytes) return KDA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return KDA_ERR_INVALID_ARG;
 
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
-    rocblas_handle hd = blas_handle(dev);
-    if (!hd) return KDA_ERR_HIP;
     const int M = d->B * d->T, HD = d->H * D, dm = d->d_model, R = d->rank;
-    const rocblas_datatype bf = rocblas_datatype_bf16_r, f32 = rocblas_datatype_f32_r;
-
-    std::lock_guard<std::mutex> lk(g_blas_mu);  // the handle's stream is per call
-    if (rocblas_set_stream(hd, stream) != rocblas_status_success) return KDA_ERR_HIP;
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    auto wb = [](const void* p) { return static_cast<const uint16_t*>(p); };
     bool ok = true;
-    ok &= gemm_rm(hd, M, HD, dm, x, bf, w->Wq, bf, W.pq, f32) == rocblas_status_success;
-    ok &= gemm_rm(hd, M, HD, dm, x, bf, w->Wk, bf, W.pk, f32) == rocblas_status_success;
-    ok &= gemm_rm(hd, M, HD, dm, x, bf, w->Wv, bf, W.pv, f32) == rocblas_status_success;
-    ok &= gemm_rm(hd, M, HD, dm, x, bf, w->Wg, bf, W.pg, f32) == rocblas_status_success;
-    ok &= gemm_rm(hd, M, R, dm, x, bf, w->Wdown, bf, W.pdown, f32) == rocblas_status_success;
-    ok &= gemm_rm(hd, M, d->H, dm, x, bf, w->Wbeta, bf, W.pbeta, f32) == rocblas_status_success;
+    // weights in the products' [out][in] form: [Wq | Wk | Wv | Wg | Wdown | Wbeta]^T, [Wup^T | Wup^T]
+    // (the up-projection runs over the hi and lo halves of its input), Wo^T
+    const int ncat = 4 * HD + R + d->H;
+    const int noff[6] = {0, HD, 2 * HD, 3 * HD, 4 * HD, 4 * HD + R};
+    const void* wsrc[6] = {w->Wq, w->Wk, w->Wv, w->Wg, w->Wdown, w->Wbeta};
+    const int wn[6] = {HD, HD, HD, HD, R, d->H};
+    for (int i = 0; i < 6; ++i)
+        ok &= kda::launch_transpose_bf16(wb(wsrc[i]), wn[i], dm, wn[i], W.wcat + (size_t)noff[i] * dm, dm, stream) ==
+              hipSuccess;
+    ok &= kda::launch_transpose_bf16(wb(w->Wup), HD, R, HD, W.wup2, 2 * R, stream) == hipSuccess;
+    ok &= kda::launch_transpose_bf16(wb(w->Wup), HD, R, HD, W.wup2 + R, 2 * R, stream) == hipSuccess;
+    ok &= kda::launch_transpose_bf16(wb(w->Wo), dm, HD, dm, W.wo, HD, stream) == hipSuccess;
     if (!ok) return KDA_ERR_HIP;
     {
-        const long n = (long)R * HD;
-        hipLaunchKernelGGL(bf16_to_f32_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
-                           dim3(256), 0, stream, (const uint16_t*)w->Wup, W.wup32, n);
+        kda::GemmOut go{};
+        float* dst[6] = {W.pq, W.pk, W.pv, W.pg, W.pdown, W.pbeta};
+        for (int i = 0; i < 6; ++i) {
+            go.ptr[i] = dst[i];
+            go.start[i] = noff[i];
+            go.ld[i] = wn[i];
+        }
+        go.start[6] = ncat;
+        go.nseg = 6;
+        if (kda::launch_gemm_nt(xb, dm, W.wcat, dm, go, true, M, ncat, dm, stream) != hipSuccess) return KDA_ERR_HIP;
     }
-    if (gemm_rm(hd, M, HD, R, W.pdown, f32, W.wup32, f32, W.pz, f32) != rocblas_status_success) return KDA_ERR_HIP;
+    if (kda::launch_split_rows(W.pdown, R, M, R, W.down2, stream) != hipSuccess) return KDA_ERR_HIP;
+    {  // the rank-R up-projection, with the decay gate -5 sigmoid(exp(A_h) (z + b_alpha)) on the way out
+        kda::GemmOut go{};
+        go.ptr[0] = W.g;
+        go.start[0] = 0;
+        go.start[1] = HD;
+        go.ld[0] = HD;
+        go.nseg = 1;
+        go.epi = kda::GEMM_GATE;
+        go.bias = w->b_alpha;
+        go.head_scale = w->A;
+        if (kda::launch_gemm_nt(W.down2, 2 * R, W.wup2, 2 * R, go, true, M, HD, 2 * R, stream) != hipSuccess)
+            return KDA_ERR_HIP;
+    }
 
     ProParams pp;
     pp.B = d->B; pp.T = d->T; pp.H = d->H; pp.HD = HD;
-    pp.pq = W.pq; pp.pk = W.pk; pp.pv = W.pv; pp.pz = W.pz; pp.pbeta = W.pbeta;
-    pp.conv_q = w->conv_q; pp.conv_k = w->conv_k; pp.b_alpha = w->b_alpha; pp.A = w->A;
+    pp.pq = W.pq; pp.pk = W.pk; pp.pv = W.pv; pp.pbeta = W.pbeta;
+    pp.conv_q = w->conv_q; pp.conv_k = w->conv_k;
     pp.state_in = conv_state_in;
-    pp.q = W.q; pp.k = W.k; pp.v = nullptr; pp.g = W.g; pp.beta = W.beta;
+    pp.q = W.q; pp.k = W.k; pp.v = nullptr; pp.beta = W.beta;
     const long nw = (long)M * d->H;
     {
         const long npw = (long)d->B * d->H * ((d->T + PRO_TOK - 1) / PRO_TOK);  // prologue waves
@@ -332,7 +322,15 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
 
     hipLaunchKernelGGL(epilogue_kernel, dim3((unsigned)((nw + 3) / 4)), dim3(256), 0, stream, M, d->H, HD, W.o, W.pg,
                        w->rms_w, W.gated);
-    if (gemm_rm(hd, M, dm, HD, W.gated, bf, w->Wo, bf, y, bf) != rocblas_status_success) return KDA_ERR_HIP;
+    {
+        kda::GemmOut go{};
+        go.ptr[0] = y;
+        go.start[0] = 0;
+        go.start[1] = dm;
+        go.ld[0] = dm;
+        go.nseg = 1;
+        if (kda::launch_gemm_nt(W.gated, HD, W.wo, HD, go, false, M, dm, HD, stream) != hipSuccess) return KDA_ERR_HIP;
+    }
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -296,3 +296,23 @@ def test_bwd_argument_checks():
     assert call_bwd(desc(B=0), ws=ws, ws_bytes=need) == _lib.KDA_ERR_INVALID_ARG
     # T = 0: dS0 = dS_T; with dS0 = NULL nothing is launched
     assert call_bwd(desc(T=0), q=0, k=0, v=0, g=0, beta=0, dO=0) == _lib.KDA_OK
+
+
+def call_layer(d_model=256, rank=32, x=FAKE, y=FAKE + 0x100000, **kw):
+    d = _lib.LayerDesc(1, 8, d_model, 2, 128, 128, rank, 4, 1.0, 0)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    w = _lib.LayerWeights(*([FAKE + 0x200000] * len(_lib.LAYER_WEIGHT_FIELDS)))
+    need = _lib.layer_workspace_size(d)
+    return _lib.layer_fwd_raw(d, x, w, 0, 0, y, 0, 0, FAKE + 0x400000, need, None)
+
+
+def test_layer_argument_checks():
+    """The layer's GEMMs step k by 32 columns and move 16-byte chunks: other widths are unsupported and
+    misaligned activations are rejected, before any device call."""
+    assert call_layer(d_model=40) == _lib.KDA_ERR_UNSUPPORTED      # not a multiple of 32
+    assert call_layer(rank=24) == _lib.KDA_ERR_UNSUPPORTED         # not a multiple of 16
+    assert call_layer(x=FAKE + 8) == _lib.KDA_ERR_INVALID_ARG      # x not 16-byte aligned
+    assert call_layer(y=FAKE + 0x100004) == _lib.KDA_ERR_INVALID_ARG
+    assert call_layer(flags=1) == _lib.KDA_ERR_INVALID_ARG
+    assert _lib.layer_workspace_size(_lib.LayerDesc(0, 8, 256, 2, 128, 128, 32, 4, 1.0, 0)) == 0
