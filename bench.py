@@ -448,6 +448,46 @@ def bench_core(args, torch, synth, kda, wid):
     print(json.dumps(out), flush=True)
 
 
+def bench_layer_decode(args, torch, synth, kda):
+    """kda_layer_decode: one new token for each of B=16 sequences through the layer of the prefill
+    workload (d_model 2048, H=16, D=128, rank 128), state and window updated in place.  Bound by reading
+    the weights (about 43 MB of bf16) and reading and writing the float32 state once per call."""
+    L = synth.gen.LAYER
+    B, T, d, H, D, R = 16, 1, L["d"], L["H"], L["Dk"], L["rank"]
+    x, p = synth.layer_inputs(seed=0, B=B, T=T)
+    dev = torch.device("cuda:0")
+    bf = ("Wq", "Wk", "Wv", "Wg", "Wo", "Wbeta", "Wdown", "Wup")
+    W = {n: torch.from_numpy(np.ascontiguousarray(a)).to(dev) for n, a in p.items()}
+    for n in bf:
+        W[n] = W[n].to(torch.bfloat16)
+    xt = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    S = torch.randn((B, H, D, D), device=dev, generator=gen) * 0.3
+    cs = torch.randn((B, 3, 2 * H * D), device=dev, generator=gen)
+    from linear_recurrent_attention_amd import _lib
+    ws = torch.empty(_lib.layer_decode_workspace_size(_lib.LayerDesc(B, T, d, H, D, D, R, 4, 1.0, 0)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step():
+        kda.kda_layer_decode(xt, W, S, cs, workspace=ws)
+
+    wall, launch_ms = time_steps(torch, step, stream, args)
+    stats = launch_stats(launch_ms)
+    wbytes = 2 * (d * (4 * H * D + R + H) + R * H * D + H * D * d)
+    abytes = wbytes + B * H * D * D * 4 * 2 + B * T * d * 2 * 2
+    out = {
+        "metric": "KDA layer decode tokens/s (B16 one token each, d2048 H16 D128, state in place)",
+        "value": B * T / (wall / args.steps), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "kda_layer_decode_bf16_B16_T1_d2048_H16_D128", "B": B, "T": T, "d_model": d, "H": H,
+                   "D": D, "rank": R},
+        "roofline": hbm_roofline(abytes, stats, None, "kda_layer_decode_kernel"),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -456,12 +496,14 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run one plain 512 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=("core", "f32_small", "bf16_4k", "layer", "decode", "longctx", "bwd"),
+    ap.add_argument("--workload", choices=("core", "f32_small", "bf16_4k", "layer", "decode", "longctx", "bwd",
+                                           "layer_decode"),
                     default="core",
                     help="core: kda_fwd on B4 H32 T16384 (the headline line); layer: kda_layer_fwd on "
                          "B2 T8192 d_model 2048 H16; decode: kda_decode on B128 H32, one token; longctx: "
                          "kda_fwd_cp on B1 H16 T1M; bwd: kda_bwd on B4 H32 T16384; f32_small: kda_fwd on "
-                         "B1 H2 T256 D64 float32; bf16_4k: kda_fwd on B1 H16 T4096 (separate lines)")
+                         "B1 H2 T256 D64 float32; bf16_4k: kda_fwd on B1 H16 T4096; layer_decode: kda_layer_decode "
+                         "on B16 one token each (separate lines)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus N with N > 1 is not supported "
@@ -477,6 +519,9 @@ def main():
         return
     if args.workload == "decode":
         bench_decode(args, torch, synth, kda)
+        return
+    if args.workload == "layer_decode":
+        bench_layer_decode(args, torch, synth, kda)
         return
     if args.workload == "longctx":
         bench_longctx(args, torch, synth, kda)

@@ -284,6 +284,46 @@ kda_status kda_layer_fwd(const kda_layer_desc* desc, const void* x, const kda_la
                          const float* S0, const float* conv_state_in, void* y, float* S_T,
                          float* conv_state_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * kda_layer_decode -- the layer (as kda_layer_fwd) over T new tokens of each of B sequences, from a
+ * given state and convolution window: the decode step of the explainer page, section 13.10 (one fused
+ * call for the projections, the state update and the readout, with a projection-input cache), with
+ * the speculative-decoding rollback of section 13.4 (the state is updated in place, so rejected draft
+ * tokens cannot be undone from it; each token's projection inputs are cached instead, far fewer
+ * numbers than a state).  One cooperative launch, one workgroup per compute unit.
+ *   desc          : as kda_layer_fwd (d_model any positive value, rank <= 512); B*T <= 16 rows;
+ *                   flags = 0 or KDA_DECODE_SPECULATIVE
+ *   x             : [B, T, d_model] bf16;  y: [B, T, d_model] bf16 (output)
+ *   S             : [B, H, Dk, Dv] float32 state (required).  Read, then overwritten with the state
+ *                   after the T tokens -- unless KDA_DECODE_SPECULATIVE, which leaves it unchanged
+ *   conv_state    : [B, 3, 2*H*Dk] float32 window as kda_layer_fwd (NULL: zeros, not written); updated
+ *                   like S
+ *   cache         : the tokens' cache entries (kda_layer_decode_cache_bytes(desc) bytes, float32, planar
+ *                   with N = B*T token rows in [b][t] order: k [N][H*Dk] after conv/SiLU/L2, v [N][H*Dv],
+ *                   g (log decay) [N][H*Dk], beta [N][H], pre-convolution q rows [N][H*Dk], pre-convolution
+ *                   k rows [N][H*Dk]); required with KDA_DECODE_SPECULATIVE, else may be NULL
+ *   ws            : device workspace of kda_layer_decode_workspace_size(desc) bytes, 256-byte aligned
+ * With KDA_DECODE_SPECULATIVE the T tokens are drafts: token t's output is computed as if drafts
+ * 0..t-1 were accepted.  Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE or
+ * KDA_ERR_HIP (also if the device cannot run the cooperative launch).
+ */
+#define KDA_DECODE_SPECULATIVE 1
+size_t kda_layer_decode_workspace_size(const kda_layer_desc* desc);  /* 0 for an invalid descriptor */
+size_t kda_layer_decode_cache_bytes(const kda_layer_desc* desc);      /* 0 for an invalid descriptor */
+kda_status kda_layer_decode(const kda_layer_desc* desc, const void* x, const kda_layer_weights* weights,
+                            float* S, float* conv_state, void* y, float* cache, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
+ * kda_layer_decode_commit -- accept the first n_accept (0 <= n_accept <= desc->T) tokens of each
+ * sequence of a speculative kda_layer_decode call: advances S (in place) and conv_state (if not NULL)
+ * over their cache entries with the token-by-token step, without the projections (section 13.4's
+ * rollback: the rejected drafts never touched S).  desc is the speculative call's (its flags are
+ * ignored).  Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED or KDA_ERR_HIP.
+ */
+kda_status kda_layer_decode_commit(const kda_layer_desc* desc, const float* cache, int n_accept, float* S,
+                                   float* conv_state, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kda_error_string(kda_status status);
 

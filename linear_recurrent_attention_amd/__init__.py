@@ -10,7 +10,7 @@ import torch
 from . import _lib
 from ._lib import KdaError  # noqa: F401
 
-__all__ = ["kda_fwd", "kda_fwd_ckpt", "kda_fwd_cp", "kda_fwd_cp_noalloc", "kda_bwd", "kda_decode", "kda_layer_fwd", "KdaError"]
+__all__ = ["kda_fwd", "kda_fwd_ckpt", "kda_fwd_cp", "kda_fwd_cp_noalloc", "kda_layer_decode", "kda_layer_decode_commit", "kda_bwd", "kda_decode", "kda_layer_fwd", "KdaError"]
 
 _DT = {torch.float32: _lib.KDA_F32, torch.bfloat16: _lib.KDA_BF16}
 
@@ -180,3 +180,42 @@ def kda_layer_fwd(x, weights: dict, S0=None, conv_state=None, scale: float = 1.0
                               cs.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device))
     _lib.check(code)
     return y, ST, cs
+
+
+def _layer_desc(weights: dict, B: int, T: int, dm: int, scale: float, flags: int):
+    H = weights["A"].shape[0]
+    HD = weights["Wq"].shape[1]
+    return _lib.LayerDesc(B, T, dm, H, HD // H, weights["Wv"].shape[1] // H, weights["Wdown"].shape[1], 4,
+                          float(scale), flags)
+
+
+def kda_layer_decode(x, weights: dict, S, conv_state=None, scale: float = 1.0, speculative: bool = False,
+                     cache=None, workspace=None):
+    """Layer decode step (kda_layer_decode) over x [B,T,d_model] bf16 (B*T <= 16): S [B,H,Dk,Dv] float32 and
+    conv_state [B,3,2*H*Dk] float32 are updated in place unless speculative.  Returns (y, cache), cache a
+    float32 tensor of the tokens' projection-input entries (allocated when speculative and not given)."""
+    B, T, dm = x.shape
+    desc = _layer_desc(weights, B, T, dm, scale, _lib.KDA_DECODE_SPECULATIVE if speculative else 0)
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 GPU tensor")
+    if S.dtype != torch.float32 or not S.is_contiguous():
+        raise ValueError("S must be a contiguous float32 tensor")
+    if cache is None and speculative:
+        cache = torch.empty(_lib.layer_decode_cache_bytes(desc) // 4, dtype=torch.float32, device=x.device)
+    need = _lib.layer_decode_workspace_size(desc)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    y = torch.empty((B, T, dm), dtype=torch.bfloat16, device=x.device)
+    W = _lib.LayerWeights(*[weights[n].data_ptr() for n in _lib.LAYER_WEIGHT_FIELDS])
+    code = _lib.layer_decode_raw(desc, x.data_ptr(), W, S.data_ptr(), _ptr(conv_state), y.data_ptr(), _ptr(cache),
+                                 ws.data_ptr(), ws.numel(), _stream(x.device))
+    _lib.check(code)
+    return y, cache
+
+
+def kda_layer_decode_commit(cache, n_accept: int, S, conv_state, weights: dict, B: int, T: int, d_model: int):
+    """Accept the first n_accept of the T draft tokens of a speculative kda_layer_decode call
+    (kda_layer_decode_commit): S and conv_state advance in place over their cache entries."""
+    desc = _layer_desc(weights, B, T, d_model, 1.0, 0)
+    code = _lib.layer_decode_commit_raw(desc, _ptr(cache), int(n_accept), S.data_ptr(), _ptr(conv_state),
+                                        _stream(S.device))
+    _lib.check(code)

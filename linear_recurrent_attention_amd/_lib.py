@@ -18,12 +18,15 @@ KDA_CP_NOALLOC_SCRATCH_BYTES = 32 << 20  # the fixed per-device scratch of kda_f
 KDA_F32 = 0
 KDA_BF16 = 1
 KDA_FWD_PRECISE = 1  # kda_fwd_desc.flags
+KDA_DECODE_SPECULATIVE = 1  # kda_layer_desc.flags for kda_layer_decode
 KDA_VALIDATE = 2
 
 # every symbol include/kda.h declares
 EXPORTS = ("kda_fwd_workspace_size", "kda_fwd", "kda_fwd_ckpt", "kda_decode", "kda_fwd_cp_workspace_size", "kda_fwd_cp",
            "kda_fwd_cp_noalloc",
-           "kda_bwd_workspace_size", "kda_bwd", "kda_layer_workspace_size", "kda_layer_fwd", "kda_error_string", "kda_version")
+           "kda_bwd_workspace_size", "kda_bwd", "kda_layer_workspace_size", "kda_layer_fwd",
+           "kda_layer_decode_workspace_size", "kda_layer_decode_cache_bytes", "kda_layer_decode", "kda_layer_decode_commit",
+           "kda_error_string", "kda_version")
 
 
 class FwdDesc(ctypes.Structure):
@@ -95,6 +98,15 @@ def lib():
             L.kda_layer_fwd.restype = ctypes.c_int
             L.kda_layer_fwd.argtypes = ([ctypes.POINTER(LayerDesc), ctypes.c_void_p, ctypes.POINTER(LayerWeights)] +
                                         [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p])
+            for n in ("kda_layer_decode_workspace_size", "kda_layer_decode_cache_bytes"):
+                getattr(L, n).restype = ctypes.c_size_t
+                getattr(L, n).argtypes = [ctypes.POINTER(LayerDesc)]
+            L.kda_layer_decode.restype = ctypes.c_int
+            L.kda_layer_decode.argtypes = ([ctypes.POINTER(LayerDesc), ctypes.c_void_p, ctypes.POINTER(LayerWeights)] +
+                                           [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p])
+            L.kda_layer_decode_commit.restype = ctypes.c_int
+            L.kda_layer_decode_commit.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_void_p, ctypes.c_int,
+                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
             L.kda_error_string.restype = ctypes.c_char_p
             L.kda_error_string.argtypes = [ctypes.c_int]
             L.kda_version.restype = ctypes.c_int
@@ -117,6 +129,25 @@ def layer_fwd_raw(desc: LayerDesc, x, weights: LayerWeights, S0, conv_in, y, S_T
     """Call kda_layer_fwd with integer device addresses (0 = NULL); returns the status code."""
     return lib().kda_layer_fwd(ctypes.byref(desc), x, ctypes.byref(weights), S0, conv_in, y, S_T, conv_out, ws,
                                ws_bytes, stream)
+
+
+def layer_decode_workspace_size(desc: LayerDesc) -> int:
+    return lib().kda_layer_decode_workspace_size(ctypes.byref(desc))
+
+
+def layer_decode_cache_bytes(desc: LayerDesc) -> int:
+    return lib().kda_layer_decode_cache_bytes(ctypes.byref(desc))
+
+
+def layer_decode_raw(desc: LayerDesc, x, weights: LayerWeights, S, conv_state, y, cache, ws, ws_bytes, stream) -> int:
+    """Call kda_layer_decode with integer device addresses (0 = NULL); returns the status code."""
+    return lib().kda_layer_decode(ctypes.byref(desc), x, ctypes.byref(weights), S, conv_state, y, cache, ws, ws_bytes,
+                                  stream)
+
+
+def layer_decode_commit_raw(desc: LayerDesc, cache, n_accept, S, conv_state, stream) -> int:
+    """Call kda_layer_decode_commit with integer device addresses (0 = NULL); returns the status code."""
+    return lib().kda_layer_decode_commit(ctypes.byref(desc), cache, n_accept, S, conv_state, stream)
 
 
 def fwd_workspace_size(desc: FwdDesc) -> int:

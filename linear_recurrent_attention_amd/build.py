@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libkda.so")
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["kda_api.cpp", "kda_fwd_bf16.hip", "kda_fwd_f32.hip", "kda_layer.hip", "kda_decode.hip", "kda_cp.hip", "kda_bwd.hip",
-           "kda_validate.hip", "kda_gemm.hip"]
+           "kda_validate.hip", "kda_gemm.hip", "kda_layer_decode.hip"]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 # packed-fp32 instructions are disabled for all device code
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

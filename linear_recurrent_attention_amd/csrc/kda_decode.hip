@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(NTHR) kda_decode_kernel(Params p) {
         }
         po[rg][j] = o;
         __syncthreads();
-        if (rg == 0) {
+        if (rg == 0 && p.o) {  // (o == NULL: state only)
             const float ot = ((po[0][j] + po[1][j]) + (po[2][j] + po[3][j])) * p.scale;
             if constexpr (OUT_BF16) {
                 const uint32_t pk = pack_bf16(ot, 0.f);

@@ -83,6 +83,28 @@ hipError_t launch_gemm_nt(const uint16_t* A, int lda, const uint16_t* Bt, int ld
 hipError_t launch_transpose_bf16(const uint16_t* src, int lds, int K, int N, uint16_t* dst, int ldd, hipStream_t stream);
 // float32 [M][R] (row stride lds) -> bf16 [M][2R]: bf16(x) in columns [0, R), bf16(x - that) in [R, 2R)
 hipError_t launch_split_rows(const float* src, int lds, int M, int R, uint16_t* dst, hipStream_t stream);
+// Fused layer decode step (one cooperative launch); see kda_layer_decode.hip.
+struct LayerDecodeParams {
+    const uint16_t* x;              // [B*T][dm] bf16
+    const uint16_t* W[6];           // Wq, Wk, Wv, Wg, Wdown, Wbeta ([dm][wn[i]] bf16)
+    int wn[6];
+    int noff[7];                    // column offsets of the six in the partial-sum rows; noff[6] = total
+    const uint16_t* Wup;            // [R][H*D]
+    const uint16_t* Wo;             // [H*D][dm]
+    const float *conv_q, *conv_k, *b_alpha, *A, *rms_w;
+    float* S;                       // [B][H][D][D], read; written unless spec
+    float* conv;                    // [B][3][2*H*D] or NULL (zeros in, nothing out)
+    uint16_t* y;                    // [B*T][dm]
+    float* cache;                   // planar cache entries or NULL
+    float* part;                    // partial sums (layer_decode_part_floats)
+    float* gated;                   // [B*T][H*D]
+    int B, T, H, dm, R, spec;
+    float scale;
+};
+size_t layer_decode_part_floats(int M, int dm, int HD, int ntot);
+hipError_t launch_layer_decode(const LayerDecodeParams& p, hipStream_t stream);
+hipError_t launch_window_commit(float* conv, const float* qpre, const float* kpre, int B, int T, int HD, int n,
+                                hipStream_t stream);
 // launch_fwd_cp with the library's static per-device scratch array (KDA_CP_NOALLOC_SCRATCH_BYTES);
 // hipErrorInvalidValue if the plan needs more than that
 hipError_t launch_fwd_cp_noalloc(const Params& p, int nseg_req, hipStream_t stream);

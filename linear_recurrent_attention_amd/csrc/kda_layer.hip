@@ -334,4 +334,119 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+// ------------------------------------------------------------------------------------------------
+// Decode step with the projection-input cache (kda_layer_decode.hip)
+
+namespace {
+constexpr int kDecodeMaxRows = 16;  // B*T rows per decode call
+constexpr int kDecodeMaxRank = 512;
+
+kda_status check_decode(const kda_layer_desc* d) {
+    if (!d || d->B < 1 || d->T < 1 || d->H < 1 || d->d_model < 1 || d->rank < 1) return KDA_ERR_INVALID_ARG;
+    if (d->flags & ~KDA_DECODE_SPECULATIVE) return KDA_ERR_INVALID_ARG;
+    if (d->Dk != D || d->Dv != D || d->conv != 4) return KDA_ERR_UNSUPPORTED;
+    if ((long long)d->B * d->T > kDecodeMaxRows || d->rank > kDecodeMaxRank) return KDA_ERR_UNSUPPORTED;
+    if (!(d->scale == d->scale)) return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
+size_t decode_cache_floats(const kda_layer_desc* d) {
+    return (size_t)d->B * d->T * (5 * (size_t)d->H * D + d->H);
+}
+
+struct DecodeWs {
+    float *part, *gated;
+    size_t bytes;
+};
+DecodeWs carve_decode(const kda_layer_desc* d, char* base) {
+    const int M = d->B * d->T, HD = d->H * D;
+    const int ntot = 4 * HD + d->rank + d->H;
+    size_t off = 0;
+    auto take = [&](size_t nbytes) {
+        char* p = base ? base + off : nullptr;
+        off += (nbytes + 255) & ~(size_t)255;
+        return p;
+    };
+    DecodeWs w;
+    w.part = (float*)take(kda::layer_decode_part_floats(M, d->d_model, HD, ntot) * 4);
+    w.gated = (float*)take((size_t)M * HD * 4);
+    w.bytes = off;
+    return w;
+}
+}  // namespace
+
+size_t kda_layer_decode_workspace_size(const kda_layer_desc* desc) {
+    if (check_decode(desc) != KDA_OK) return 0;
+    return carve_decode(desc, nullptr).bytes;
+}
+
+size_t kda_layer_decode_cache_bytes(const kda_layer_desc* desc) {
+    if (check_decode(desc) != KDA_OK) return 0;
+    return decode_cache_floats(desc) * sizeof(float);
+}
+
+kda_status kda_layer_decode(const kda_layer_desc* d, const void* x, const kda_layer_weights* w, float* S,
+                            float* conv_state, void* y, float* cache, void* ws, size_t ws_bytes, hipStream_t stream) {
+    kda_status st = check_decode(d);
+    if (st != KDA_OK) return st;
+    if (!x || !w || !S || !y) return KDA_ERR_INVALID_ARG;
+    if ((d->flags & KDA_DECODE_SPECULATIVE) && !cache) return KDA_ERR_INVALID_ARG;
+    if (!w->Wq || !w->Wk || !w->Wv || !w->Wg || !w->Wo || !w->Wbeta || !w->Wdown || !w->Wup || !w->conv_q ||
+        !w->conv_k || !w->b_alpha || !w->A || !w->rms_w)
+        return KDA_ERR_INVALID_ARG;
+    const DecodeWs W = carve_decode(d, (char*)ws);
+    if (!ws || ws_bytes < W.bytes) return KDA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return KDA_ERR_INVALID_ARG;
+    const int HD = d->H * D, R = d->rank;
+    kda::LayerDecodeParams p{};
+    p.x = static_cast<const uint16_t*>(x);
+    const void* wsrc[6] = {w->Wq, w->Wk, w->Wv, w->Wg, w->Wdown, w->Wbeta};
+    const int wn[6] = {HD, HD, HD, HD, R, d->H};
+    int off = 0;
+    for (int i = 0; i < 6; ++i) {
+        p.W[i] = static_cast<const uint16_t*>(wsrc[i]);
+        p.wn[i] = wn[i];
+        p.noff[i] = off;
+        off += wn[i];
+    }
+    p.noff[6] = off;
+    p.Wup = static_cast<const uint16_t*>(w->Wup);
+    p.Wo = static_cast<const uint16_t*>(w->Wo);
+    p.conv_q = w->conv_q; p.conv_k = w->conv_k; p.b_alpha = w->b_alpha; p.A = w->A; p.rms_w = w->rms_w;
+    p.S = S; p.conv = conv_state; p.y = static_cast<uint16_t*>(y); p.cache = cache;
+    p.part = W.part; p.gated = W.gated;
+    p.B = d->B; p.T = d->T; p.H = d->H; p.dm = d->d_model; p.R = R;
+    p.spec = (d->flags & KDA_DECODE_SPECULATIVE) ? 1 : 0;
+    p.scale = d->scale;
+    return kda::launch_layer_decode(p, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_layer_decode_commit(const kda_layer_desc* d, const float* cache, int n_accept, float* S,
+                                   float* conv_state, hipStream_t stream) {
+    kda_layer_desc dd;
+    if (!d) return KDA_ERR_INVALID_ARG;
+    dd = *d;
+    dd.flags = 0;
+    kda_status st = check_decode(&dd);
+    if (st != KDA_OK) return st;
+    if (!cache || !S || n_accept < 0 || n_accept > d->T) return KDA_ERR_INVALID_ARG;
+    if (n_accept == 0) return KDA_OK;
+    const size_t HD = (size_t)d->H * D, ntok = (size_t)d->B * d->T;
+    const float* k = cache;
+    const float* v = cache + ntok * HD;
+    const float* g = cache + 2 * ntok * HD;
+    const float* beta = cache + 3 * ntok * HD;
+    const float* qpre = beta + ntok * d->H;
+    const float* kpre = qpre + ntok * HD;
+    kda::Params p{};  // the token-by-token step over the accepted entries, state in place, no output
+    p.q = k; p.k = k; p.v = v; p.g = g; p.beta = beta; p.S0 = S; p.S_T = S; p.o = nullptr;
+    p.B = d->B; p.T = n_accept; p.tstride = d->T; p.H = d->H; p.Dk = D; p.Dv = D; p.scale = 1.f;
+    p.o_f32 = 1; p.in_f32 = 1; p.ckpt_chunks = 1;
+    if (kda::launch_decode(p, false, stream) != hipSuccess) return KDA_ERR_HIP;
+    if (conv_state && kda::launch_window_commit(conv_state, qpre, kpre, d->B, d->T, (int)HD, n_accept, stream) !=
+                          hipSuccess)
+        return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
 }  // extern "C"

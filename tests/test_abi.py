@@ -316,3 +316,25 @@ def test_layer_argument_checks():
     assert call_layer(y=FAKE + 0x100004) == _lib.KDA_ERR_INVALID_ARG
     assert call_layer(flags=1) == _lib.KDA_ERR_INVALID_ARG
     assert _lib.layer_workspace_size(_lib.LayerDesc(0, 8, 256, 2, 128, 128, 32, 4, 1.0, 0)) == 0
+
+
+def test_layer_decode_argument_checks():
+    """Rows per call, rank, flags and the speculative cache are checked before any device call."""
+    def desc_(B=1, T=1, rank=32, flags=0):
+        return _lib.LayerDesc(B, T, 256, 2, 128, 128, rank, 4, 1.0, flags)
+    assert _lib.layer_decode_workspace_size(desc_()) > 0
+    assert _lib.layer_decode_cache_bytes(desc_(B=2, T=3)) == 2 * 3 * (5 * 2 * 128 + 2) * 4
+    assert _lib.layer_decode_workspace_size(desc_(B=4, T=5)) == 0         # 20 rows > 16
+    assert _lib.layer_decode_workspace_size(desc_(rank=1024)) == 0
+    w = _lib.LayerWeights(*([FAKE + 0x200000] * len(_lib.LAYER_WEIGHT_FIELDS)))
+    d = desc_(flags=_lib.KDA_DECODE_SPECULATIVE)
+    ws = _lib.layer_decode_workspace_size(d)
+    assert _lib.layer_decode_raw(d, FAKE, w, FAKE, 0, FAKE, 0, FAKE, ws, None) == _lib.KDA_ERR_INVALID_ARG  # no cache
+    assert _lib.layer_decode_raw(desc_(flags=2), FAKE, w, FAKE, 0, FAKE, 0, FAKE, ws, None) == _lib.KDA_ERR_INVALID_ARG
+    assert _lib.layer_decode_raw(desc_(B=4, T=5), FAKE, w, FAKE, 0, FAKE, 0, FAKE, ws, None) == _lib.KDA_ERR_UNSUPPORTED
+    assert _lib.layer_decode_raw(desc_(), FAKE, w, 0, 0, FAKE, 0, FAKE, ws, None) == _lib.KDA_ERR_INVALID_ARG  # no S
+    assert _lib.layer_decode_raw(desc_(), FAKE, w, FAKE, 0, FAKE, 0, FAKE, ws - 1, None) == _lib.KDA_ERR_WORKSPACE
+    assert _lib.layer_decode_commit_raw(desc_(T=4), FAKE, 5, FAKE, 0, None) == _lib.KDA_ERR_INVALID_ARG
+    assert _lib.layer_decode_commit_raw(desc_(T=4), FAKE, -1, FAKE, 0, None) == _lib.KDA_ERR_INVALID_ARG
+    assert _lib.layer_decode_commit_raw(desc_(T=4), 0, 2, FAKE, 0, None) == _lib.KDA_ERR_INVALID_ARG
+    assert _lib.layer_decode_commit_raw(desc_(T=4), FAKE, 0, FAKE, 0, None) == _lib.KDA_OK  # nothing accepted
