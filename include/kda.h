@@ -291,9 +291,9 @@ kda_status kda_layer_fwd(const kda_layer_desc* desc, const void* x, const kda_la
  * the speculative-decoding rollback of section 13.4 (the state is updated in place, so rejected draft
  * tokens cannot be undone from it; each token's projection inputs are cached instead, far fewer
  * numbers than a state).  One cooperative launch, one workgroup per compute unit.
- *   desc          : as kda_layer_fwd (d_model any positive value, rank <= 512); B*T <= 16 rows;
- *                   flags = 0 or KDA_DECODE_SPECULATIVE
- *   x             : [B, T, d_model] bf16;  y: [B, T, d_model] bf16 (output)
+ *   desc          : as kda_layer_fwd, with d_model a multiple of 4, rank <= 128, B*T <= 16 rows (else
+ *                   KDA_ERR_UNSUPPORTED); flags = 0 or KDA_DECODE_SPECULATIVE
+ *   x             : [B, T, d_model] bf16;  y: [B, T, d_model] bf16 (output); both 16-byte aligned
  *   S             : [B, H, Dk, Dv] float32 state (required).  Read, then overwritten with the state
  *                   after the T tokens -- unless KDA_DECODE_SPECULATIVE, which leaves it unchanged
  *   conv_state    : [B, 3, 2*H*Dk] float32 window as kda_layer_fwd (NULL: zeros, not written); updated

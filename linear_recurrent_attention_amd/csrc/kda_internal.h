@@ -97,6 +97,7 @@ struct LayerDecodeParams {
     uint16_t* y;                    // [B*T][dm]
     float* cache;                   // planar cache entries or NULL
     float* part;                    // partial sums (layer_decode_part_floats)
+    float* proj;                    // [B*T][noff[6]] projected rows
     float* gated;                   // [B*T][H*D]
     int B, T, H, dm, R, spec;
     float scale;

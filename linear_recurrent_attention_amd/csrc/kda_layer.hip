@@ -339,13 +339,13 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
 
 namespace {
 constexpr int kDecodeMaxRows = 16;  // B*T rows per decode call
-constexpr int kDecodeMaxRank = 512;
+constexpr int kDecodeMaxRank = 128;
 
 kda_status check_decode(const kda_layer_desc* d) {
     if (!d || d->B < 1 || d->T < 1 || d->H < 1 || d->d_model < 1 || d->rank < 1) return KDA_ERR_INVALID_ARG;
     if (d->flags & ~KDA_DECODE_SPECULATIVE) return KDA_ERR_INVALID_ARG;
     if (d->Dk != D || d->Dv != D || d->conv != 4) return KDA_ERR_UNSUPPORTED;
-    if ((long long)d->B * d->T > kDecodeMaxRows || d->rank > kDecodeMaxRank) return KDA_ERR_UNSUPPORTED;
+    if ((long long)d->B * d->T > kDecodeMaxRows || d->rank > kDecodeMaxRank || d->d_model % 4) return KDA_ERR_UNSUPPORTED;
     if (!(d->scale == d->scale)) return KDA_ERR_INVALID_ARG;
     return KDA_OK;
 }
@@ -355,12 +355,12 @@ size_t decode_cache_floats(const kda_layer_desc* d) {
 }
 
 struct DecodeWs {
-    float *part, *gated;
+    float *part, *proj, *gated;
     size_t bytes;
 };
 DecodeWs carve_decode(const kda_layer_desc* d, char* base) {
     const int M = d->B * d->T, HD = d->H * D;
-    const int ntot = 4 * HD + d->rank + d->H;
+    const int ntot = (4 * HD + d->rank + d->H + 3) & ~3;  // padded row length
     size_t off = 0;
     auto take = [&](size_t nbytes) {
         char* p = base ? base + off : nullptr;
@@ -369,6 +369,7 @@ DecodeWs carve_decode(const kda_layer_desc* d, char* base) {
     };
     DecodeWs w;
     w.part = (float*)take(kda::layer_decode_part_floats(M, d->d_model, HD, ntot) * 4);
+    w.proj = (float*)take((size_t)M * ntot * 4);
     w.gated = (float*)take((size_t)M * HD * 4);
     w.bytes = off;
     return w;
@@ -391,6 +392,7 @@ kda_status kda_layer_decode(const kda_layer_desc* d, const void* x, const kda_la
     if (st != KDA_OK) return st;
     if (!x || !w || !S || !y) return KDA_ERR_INVALID_ARG;
     if ((d->flags & KDA_DECODE_SPECULATIVE) && !cache) return KDA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(y) & 15)) return KDA_ERR_INVALID_ARG;
     if (!w->Wq || !w->Wk || !w->Wv || !w->Wg || !w->Wo || !w->Wbeta || !w->Wdown || !w->Wup || !w->conv_q ||
         !w->conv_k || !w->b_alpha || !w->A || !w->rms_w)
         return KDA_ERR_INVALID_ARG;
@@ -414,7 +416,7 @@ kda_status kda_layer_decode(const kda_layer_desc* d, const void* x, const kda_la
     p.Wo = static_cast<const uint16_t*>(w->Wo);
     p.conv_q = w->conv_q; p.conv_k = w->conv_k; p.b_alpha = w->b_alpha; p.A = w->A; p.rms_w = w->rms_w;
     p.S = S; p.conv = conv_state; p.y = static_cast<uint16_t*>(y); p.cache = cache;
-    p.part = W.part; p.gated = W.gated;
+    p.part = W.part; p.proj = W.proj; p.gated = W.gated;
     p.B = d->B; p.T = d->T; p.H = d->H; p.dm = d->d_model; p.R = R;
     p.spec = (d->flags & KDA_DECODE_SPECULATIVE) ? 1 : 0;
     p.scale = d->scale;

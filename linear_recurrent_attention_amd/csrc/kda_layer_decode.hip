@@ -17,15 +17,16 @@
 // before it were accepted; kda_layer_decode_commit then advances the state and the window over the
 // accepted tokens from their entries, without touching the projections again.
 //
-// One cooperative launch (every workgroup resident) in four phases separated by grid barriers:
+// One cooperative launch (every workgroup resident) in phases separated by grid barriers:
 //   1. the input projections of the M rows (q, k, v, gate, decay-down, beta weights, as given,
-//      [in][out]): work items of 512 columns x 64 rows of the weight, partial sums per item;
-//   2. one workgroup per (sequence, head): sums the partials of its columns, the decay
+//      [in][out]): work items of 1024 columns x 64 rows of the weight, partial sums per item, then
+//      (after a barrier) the sums of the partials, one projected row per token;
+//   2. one workgroup per (sequence, head): reads its columns of the projected rows, the decay
 //      up-projection of its head, convolution window, gates, then the recurrence token by token
 //      with the state in registers (thread (column j, half r) holds rows 64r..64r+63 of column j),
 //      readout, RMSNorm and gate; writes the gated output rows, the cache entries and (unless
 //      speculative) the state and window;
-//   3. the output projection of the gated rows, partial sums per item as in 1;
+//   3. the output projection of the gated rows, partial sums per item of 16 weight rows;
 //   4. the sum of those partials, to bf16 y.
 // The weights are read once per call, so with a few rows the call is bound by reading them and the
 // state; the products are plain float32 FMAs with the rows of x staged in LDS.
@@ -41,8 +42,10 @@ namespace cg = cooperative_groups;
 
 constexpr int D = 128;
 constexpr int NTHR = 256;
-constexpr int KSL = 64;   // weight rows per projection work item
-constexpr int CB = 512;   // weight columns per projection work item (two per thread)
+constexpr int KSL1 = 64;   // weight rows per input-projection work item
+constexpr int KSL3 = 16;   // weight rows per output-projection work item
+constexpr int KMAX = 64;
+constexpr int CB = 1024;  // weight columns per projection work item (four per thread)
 constexpr float EPS = 1e-6f;
 
 __device__ __forceinline__ float bf(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -60,60 +63,107 @@ __device__ __forceinline__ float sum128(float v, float* red) {
 }
 
 // part[(ks * M + m) * ldp + off + n] = sum over rows k of slice ks of in(m, k) * W[k][n], for the
-// column pair (n, n + 1) of each thread.  ROWS: M rounded up to a supported count.
+// four columns n .. n + 3 of each thread.  ROWS: M rounded up to a supported count.  The weight rows
+// are loaded sixteen at a time before they are used, so that each thread keeps sixteen loads in flight.
 template <int ROWS, typename In>
-__device__ void gemv_item(const uint16_t* __restrict__ W, int nw, bool pair_ok, int k0, int kn, int cb, int M,
-                          In in, float (*xs)[16], float* __restrict__ part, int ks, int ldp, int off) {
+__device__ void gemv_item(const uint16_t* W_, int nw, bool quad_ok, int k0, int kn, int cb, int M, In in,
+                          float (*xs)[16], float* __restrict__ part, int ks, int ldp, int off) {
+    typedef __attribute__((address_space(1))) const uint16_t g16;
+    typedef __attribute__((address_space(1))) const u32x2 g32x2;
+    g16* W = (g16*)(W_);  // the weights are global memory
     const int tid = threadIdx.x;
     __syncthreads();  // the previous item's reads of xs are done
-    for (int e = tid; e < KSL * 16; e += NTHR) {
+    for (int e = tid; e < KMAX * 16; e += NTHR) {
         const int kk = e >> 4, m = e & 15;
         xs[kk][m] = (m < M && kk < kn) ? in(m, k0 + kk) : 0.f;
     }
     __syncthreads();
-    const int n = cb * CB + 2 * tid;
+    const int n = cb * CB + 4 * tid;
     if (n >= nw) return;
-    const bool two = n + 1 < nw;
-    float a0[ROWS], a1[ROWS];
+    float acc[ROWS][4];
 #pragma unroll
-    for (int m = 0; m < ROWS; ++m) a0[m] = a1[m] = 0.f;
-    const uint16_t* wp = W + (size_t)k0 * nw + n;
-    for (int kk = 0; kk < kn; ++kk) {
-        float w0, w1;
-        if (pair_ok && two) {
-            const uint32_t u = *reinterpret_cast<const uint32_t*>(wp + (size_t)kk * nw);
-            w0 = __uint_as_float(u << 16);
-            w1 = __uint_as_float(u & 0xffff0000u);
-        } else {
-            w0 = bf(wp[(size_t)kk * nw]);
-            w1 = two ? bf(wp[(size_t)kk * nw + 1]) : 0.f;
+    for (int m = 0; m < ROWS; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[m][c] = 0.f;
+#define KDA_FMA_ROW(kk, w0, w1, w2, w3)                             \
+    _Pragma("unroll") for (int m = 0; m < ROWS; ++m) {              \
+        const float xv = xs[kk][m];                                 \
+        acc[m][0] = __builtin_fmaf(xv, (w0), acc[m][0]);            \
+        acc[m][1] = __builtin_fmaf(xv, (w1), acc[m][1]);            \
+        acc[m][2] = __builtin_fmaf(xv, (w2), acc[m][2]);            \
+        acc[m][3] = __builtin_fmaf(xv, (w3), acc[m][3]);            \
+    }
+    if (quad_ok && n + 3 < nw) {
+        // four whole columns: 8-byte loads, sixteen rows in flight
+        g16* wp = W + (size_t)k0 * nw + n;
+        for (int kb = 0; kb < kn; kb += 16) {
+            u32x2 v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = *reinterpret_cast<g32x2*>(wp + (size_t)min(kb + u, kn - 1) * nw);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (kb + u < kn) {
+                    const float w0 = __uint_as_float(v[u][0] << 16), w1 = __uint_as_float(v[u][0] & 0xffff0000u);
+                    const float w2 = __uint_as_float(v[u][1] << 16), w3 = __uint_as_float(v[u][1] & 0xffff0000u);
+                    KDA_FMA_ROW(kb + u, w0, w1, w2, w3)
+                }
+            }
         }
-#pragma unroll
-        for (int m = 0; m < ROWS; ++m) {
-            a0[m] = __builtin_fmaf(xs[kk][m], w0, a0[m]);
-            a1[m] = __builtin_fmaf(xs[kk][m], w1, a1[m]);
+    } else {
+        // the ragged edge (or an unaligned matrix): element loads
+        for (int kk = 0; kk < kn; ++kk) {
+            g16* r = W + (size_t)(k0 + kk) * nw + n;
+            const float w0 = bf(r[0]), w1 = n + 1 < nw ? bf(r[1]) : 0.f;
+            const float w2 = n + 2 < nw ? bf(r[2]) : 0.f, w3 = n + 3 < nw ? bf(r[3]) : 0.f;
+            KDA_FMA_ROW(kk, w0, w1, w2, w3)
         }
     }
-    for (int m = 0; m < M && m < ROWS; ++m) {
-        float* dst = part + ((size_t)ks * M + m) * ldp + off + n;
-        dst[0] = a0[m];
-        if (two) dst[1] = a1[m];
+#undef KDA_FMA_ROW
+#pragma unroll
+    for (int m = 0; m < ROWS; ++m) {
+        if (m < M) {
+            float* dst = part + ((size_t)ks * M + m) * ldp + off + n;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (n + c < nw) dst[c] = acc[m][c];
+        }
     }
 }
 
 template <typename In>
-__device__ void gemv_dispatch(const uint16_t* W, int nw, bool pair_ok, int k0, int kn, int cb, int M, In in,
+__device__ void gemv_dispatch(const uint16_t* W, int nw, bool quad_ok, int k0, int kn, int cb, int M, In in,
                               float (*xs)[16], float* part, int ks, int ldp, int off) {
-    if (M <= 1) gemv_item<1>(W, nw, pair_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
-    else if (M <= 2) gemv_item<2>(W, nw, pair_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
-    else if (M <= 4) gemv_item<4>(W, nw, pair_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
-    else if (M <= 8) gemv_item<8>(W, nw, pair_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
-    else gemv_item<16>(W, nw, pair_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
+    if (M <= 1) gemv_item<1>(W, nw, quad_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
+    else if (M <= 2) gemv_item<2>(W, nw, quad_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
+    else if (M <= 4) gemv_item<4>(W, nw, quad_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
+    else if (M <= 8) gemv_item<8>(W, nw, quad_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
+    else gemv_item<16>(W, nw, quad_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
+}
+
+// dst[e .. e+3] = sum over ks < nks of src[ks * stride + e .. +3] for every e = 4i < n (n and stride
+// multiples of 4), grid-stride; the slices are read sixteen at a time, all in flight together
+template <typename Store>
+__device__ __forceinline__ void sum_slices4(const float* __restrict__ src, size_t stride, int nks, long n, Store st) {
+    for (long e = 4 * ((long)blockIdx.x * blockDim.x + threadIdx.x); e < n; e += 4L * gridDim.x * blockDim.x) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < nks; k0 += 16) {
+            f32x4 v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = k0 + u < nks ? *reinterpret_cast<const f32x4*>(src + (size_t)(k0 + u) * stride + e)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 16; ++u) a += v[u];
+        }
+        st(e, a);
+    }
 }
 
 struct Smem {
-    float xs[KSL][16];
-    float qp[D], kp[D], vv[D], gl[D], q[D], k[D], ga[D], dn[512];
+    float xs[KMAX][16];
+    uint16_t wup[128][D];  // the decay up-projection's columns of this head (rank <= 128)
+    float qp[D], kp[D], vv[D], gl[D], q[D], k[D], ga[D], dn[128];
     float cw[2][3][D];  // convolution window of this head: [q/k][oldest..newest][channel]
     float pw[2][D], po[2][D];
     float red[2];
@@ -125,29 +175,32 @@ __global__ void __launch_bounds__(NTHR) kda_layer_decode_kernel(LayerDecodeParam
     cg::grid_group grid = cg::this_grid();
     const int tid = threadIdx.x;
     const int M = p.B * p.T, HD = p.H * D, dm = p.dm, R = p.R;
-    const int ntot = p.noff[6];
+    const int ntot = (p.noff[6] + 3) & ~3;  // row length of the partial sums and projected rows
 
-    // ---------------- 1. input projections: partial sums over slices of KSL weight rows
+    // ---------------- 1. input projections: partial sums over slices of KSL1 weight rows
+    const int nks1 = (dm + KSL1 - 1) / KSL1;
     {
-        const int nks = (dm + KSL - 1) / KSL;
         int items = 0;
-        for (int i = 0; i < 6; ++i) items += ((p.wn[i] + CB - 1) / CB) * nks;
+        for (int i = 0; i < 6; ++i) items += ((p.wn[i] + CB - 1) / CB) * nks1;
         auto xin = [&](int m, int k) { return bf(p.x[(size_t)m * dm + k]); };
         for (int it = blockIdx.x; it < items; it += gridDim.x) {
             int i = 0, rem = it;
-            while (rem >= ((p.wn[i] + CB - 1) / CB) * nks) { rem -= ((p.wn[i] + CB - 1) / CB) * nks; ++i; }
-            const int cb = rem / nks, ks = rem - cb * nks;
-            const int k0 = ks * KSL, kn = min(KSL, dm - k0);
-            const bool pair_ok = (p.wn[i] & 1) == 0 && (reinterpret_cast<uintptr_t>(p.W[i]) & 3) == 0;
-            gemv_dispatch(p.W[i], p.wn[i], pair_ok, k0, kn, cb, M, xin, sm.xs, p.part, ks, ntot, p.noff[i]);
+            while (rem >= ((p.wn[i] + CB - 1) / CB) * nks1) { rem -= ((p.wn[i] + CB - 1) / CB) * nks1; ++i; }
+            const int cb = rem / nks1, ks = rem - cb * nks1;
+            const int k0 = ks * KSL1, kn = min(KSL1, dm - k0);
+            const bool quad_ok = (p.wn[i] & 3) == 0 && (reinterpret_cast<uintptr_t>(p.W[i]) & 7) == 0;
+            gemv_dispatch(p.W[i], p.wn[i], quad_ok, k0, kn, cb, M, xin, sm.xs, p.part, ks, ntot, p.noff[i]);
         }
     }
+    grid.sync();
+    // ---------------- 1b. the projected rows: sums of the slices' partials
+    sum_slices4(p.part, (size_t)M * ntot, nks1, (long)M * ntot,
+                [&](long e, f32x4 a) { *reinterpret_cast<f32x4*>(p.proj + e) = a; });
     grid.sync();
 
     // ---------------- 2. per (sequence, head): gates, convolution, recurrence, readout, norm
     for (int bh = blockIdx.x; bh < p.B * p.H; bh += gridDim.x) {
         const int b = bh / p.H, h = bh - b * p.H;
-        const int nks = (dm + KSL - 1) / KSL;
         const int j = tid & (D - 1), rh = tid >> 7;  // state column, row half
         float s[64];
         {
@@ -160,29 +213,27 @@ __global__ void __launch_bounds__(NTHR) kda_layer_decode_kernel(LayerDecodeParam
             sm.cw[qk][r][c] = p.conv ? p.conv[((size_t)b * 3 + r) * 2 * HD + qk * HD + h * D + c] : 0.f;
         }
         const float ea = fexp(p.A[h]);
+        // this head's columns of the decay up-projection, 16 bytes per load
+        if ((reinterpret_cast<uintptr_t>(p.Wup) & 15) == 0) {
+            for (int e = tid; e < R * (D / 8); e += NTHR) {
+                const int r = e >> 4, c8 = 8 * (e & 15);
+                *reinterpret_cast<u32x4*>(&sm.wup[r][c8]) =
+                    *reinterpret_cast<const u32x4*>(p.Wup + (size_t)r * HD + h * D + c8);
+            }
+        } else {
+            for (int e = tid; e < R * D; e += NTHR) sm.wup[e >> 7][e & 127] = p.Wup[(size_t)(e >> 7) * HD + h * D + (e & 127)];
+        }
         for (int t = 0; t < p.T; ++t) {
             const int m = b * p.T + t;
             __syncthreads();  // every read of the previous token's rows (and of the window) is done
-            // sums of this token's partials: q, k (threads 0-127), v, gate (128-255); decay-down; beta
+            // this token's projected row: q, k (threads 0-127), v, gate (128-255); decay-down; beta
             {
+                const float* pr = p.proj + (size_t)m * ntot;
                 const int c = j, base = rh ? 2 * HD : 0;
-                float a = 0.f, bb = 0.f;
-                for (int ks = 0; ks < nks; ++ks) {
-                    const float* pr = p.part + ((size_t)ks * M + m) * ntot;
-                    a += pr[base + h * D + c];
-                    bb += pr[base + HD + h * D + c];
-                }
+                const float a = pr[base + h * D + c], bb = pr[base + HD + h * D + c];
                 if (rh == 0) { sm.qp[c] = a; sm.kp[c] = bb; } else { sm.vv[c] = a; sm.gl[c] = bb; }
-                for (int r = tid; r < R; r += NTHR) {
-                    float z = 0.f;
-                    for (int ks = 0; ks < nks; ++ks) z += p.part[((size_t)ks * M + m) * ntot + 4 * HD + r];
-                    sm.dn[r] = z;
-                }
-                if (tid == NTHR - 1) {
-                    float z = 0.f;
-                    for (int ks = 0; ks < nks; ++ks) z += p.part[((size_t)ks * M + m) * ntot + 4 * HD + R + h];
-                    sm.beta = sigm(z);
-                }
+                for (int r = tid; r < R; r += NTHR) sm.dn[r] = pr[4 * HD + r];
+                if (tid == NTHR - 1) sm.beta = sigm(pr[4 * HD + R + h]);
             }
             __syncthreads();
             // short convolution + SiLU of q (threads 0-127) and k (128-255); decay gate (0-127)
@@ -195,9 +246,14 @@ __global__ void __launch_bounds__(NTHR) kda_layer_decode_kernel(LayerDecodeParam
                                 taps[3] * xcur;
                 act = y * sigm(y);
                 if (rh == 0) {
-                    float z = p.b_alpha[hc];
-                    for (int r = 0; r < R; ++r) z = __builtin_fmaf(sm.dn[r], bf(p.Wup[(size_t)r * HD + hc]), z);
-                    sm.ga[c] = -5.f * sigm(ea * z);
+                    float z[4] = {p.b_alpha[hc], 0.f, 0.f, 0.f};
+                    int r = 0;
+                    for (; r + 4 <= R; r += 4) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) z[u] = __builtin_fmaf(sm.dn[r + u], bf(sm.wup[r + u][c]), z[u]);
+                    }
+                    for (; r < R; ++r) z[0] = __builtin_fmaf(sm.dn[r], bf(sm.wup[r][c]), z[0]);
+                    sm.ga[c] = -5.f * sigm(ea * ((z[0] + z[1]) + (z[2] + z[3])));
                 }
             }
             // L2 norms: q over threads 0-127, k over 128-255 (each half sums its own two waves)
@@ -281,30 +337,24 @@ __global__ void __launch_bounds__(NTHR) kda_layer_decode_kernel(LayerDecodeParam
     }
     grid.sync();
 
-    // ---------------- 3. output projection of the gated rows: partial sums over slices of KSL rows
+    // ---------------- 3. output projection of the gated rows: partial sums over slices of KSL3 rows
+    const int nks3 = (HD + KSL3 - 1) / KSL3;
     {
-        const int nks = (HD + KSL - 1) / KSL;
-        const int items = ((dm + CB - 1) / CB) * nks;
+        const int items = ((dm + CB - 1) / CB) * nks3;
         auto gin = [&](int m, int k) { return p.gated[(size_t)m * HD + k]; };
-        const bool pair_ok = (dm & 1) == 0 && (reinterpret_cast<uintptr_t>(p.Wo) & 3) == 0;
+        const bool quad_ok = (dm & 3) == 0 && (reinterpret_cast<uintptr_t>(p.Wo) & 7) == 0;
         for (int it = blockIdx.x; it < items; it += gridDim.x) {
-            const int cb = it / nks, ks = it - cb * nks;
-            const int k0 = ks * KSL, kn = min(KSL, HD - k0);
-            gemv_dispatch(p.Wo, dm, pair_ok, k0, kn, cb, M, gin, sm.xs, p.part, ks, dm, 0);
+            const int cb = it / nks3, ks = it - cb * nks3;
+            const int k0 = ks * KSL3, kn = min(KSL3, HD - k0);
+            gemv_dispatch(p.Wo, dm, quad_ok, k0, kn, cb, M, gin, sm.xs, p.part, ks, dm, 0);
         }
     }
     grid.sync();
 
     // ---------------- 4. y = bf16(sum of the partials)
-    {
-        const int nks = (HD + KSL - 1) / KSL;
-        for (long e = (long)blockIdx.x * NTHR + tid; e < (long)M * dm; e += (long)gridDim.x * NTHR) {
-            const long m = e / dm, n = e - m * dm;
-            float a = 0.f;
-            for (int ks = 0; ks < nks; ++ks) a += p.part[((size_t)ks * M + m) * dm + n];
-            p.y[e] = (uint16_t)(pack_bf16(a, 0.f) & 0xffffu);
-        }
-    }
+    sum_slices4(p.part, (size_t)M * dm, nks3, (long)M * dm, [&](long e, f32x4 a) {
+        *reinterpret_cast<u32x2*>(p.y + e) = u32x2{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3])};
+    });
 }
 
 // Advance the convolution window over the first n tokens of the cache: the last 3 of
@@ -331,8 +381,8 @@ __global__ void window_commit_kernel(float* __restrict__ conv, const float* __re
 }  // namespace ldec
 
 size_t layer_decode_part_floats(int M, int dm, int HD, int ntot) {
-    const size_t a = (size_t)((dm + ldec::KSL - 1) / ldec::KSL) * M * ntot;
-    const size_t b = (size_t)((HD + ldec::KSL - 1) / ldec::KSL) * M * dm;
+    const size_t a = (size_t)((dm + ldec::KSL1 - 1) / ldec::KSL1) * M * ntot;
+    const size_t b = (size_t)((HD + ldec::KSL3 - 1) / ldec::KSL3) * M * dm;
     return a > b ? a : b;
 }
 
@@ -345,7 +395,9 @@ hipError_t launch_layer_decode(const LayerDecodeParams& p, hipStream_t stream) {
                                                          ldec::NTHR, 0);
     if (e != hipSuccess) return e;
     if (occ < 1 || ncu < 1) return hipErrorLaunchFailure;
-    const dim3 grid((unsigned)ncu), block(ldec::NTHR);  // one workgroup per compute unit, all resident
+    // one workgroup per compute unit, all resident: every workgroup's barrier fences write back and
+    // invalidate its XCD's L2, so more workgroups per XCD make each grid barrier dearer
+    const dim3 grid((unsigned)ncu), block(ldec::NTHR);
     LayerDecodeParams pc = p;
     void* args[] = {&pc};
     return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(ldec::kda_layer_decode_kernel), grid, block, args,

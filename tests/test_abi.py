@@ -325,7 +325,7 @@ def test_layer_decode_argument_checks():
     assert _lib.layer_decode_workspace_size(desc_()) > 0
     assert _lib.layer_decode_cache_bytes(desc_(B=2, T=3)) == 2 * 3 * (5 * 2 * 128 + 2) * 4
     assert _lib.layer_decode_workspace_size(desc_(B=4, T=5)) == 0         # 20 rows > 16
-    assert _lib.layer_decode_workspace_size(desc_(rank=1024)) == 0
+    assert _lib.layer_decode_workspace_size(desc_(rank=256)) == 0         # rank > 128
     w = _lib.LayerWeights(*([FAKE + 0x200000] * len(_lib.LAYER_WEIGHT_FIELDS)))
     d = desc_(flags=_lib.KDA_DECODE_SPECULATIVE)
     ws = _lib.layer_decode_workspace_size(d)
