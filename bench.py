@@ -35,8 +35,8 @@ CSRC = os.path.join(ROOT, "linear_recurrent_attention_amd", "csrc")
 # 512 MiB copy (factors 2.0 and 1.0); valid only for the kernel source with the recorded hash.
 MEASURED_TRAFFIC = {
     "core": {"source": "kda_fwd_bf16.hip",
-             "kernel_sha256": "e9baa09909ae3767971cb8e47f2533e089868f024df0d5e202652dd629a2e607",
-             "bytes": (1343891 * 2.0 + 532480 * 1.0) * 1024,
+             "kernel_sha256": "dd8f887ccb06e5417a3457ad6ac0d141853a3c6d747242f4f60da2ce01d9b3dc",
+             "bytes": (1366950 * 2.0 + 532480 * 1.0) * 1024,
              "profile": "profiles/kda_fwd_bf16_B4_H32_T16384_D128.md"},
     "decode": {"source": "kda_decode.hip",
                "kernel_sha256": "cd969b686b6b0e06382e0dbd651015bdea5d1895790e77c3248f0d1df9a3c844",
