@@ -39,8 +39,8 @@ MEASURED_TRAFFIC = {
              "bytes": (1366950 * 2.0 + 532480 * 1.0) * 1024,
              "profile": "profiles/kda_fwd_bf16_B4_H32_T16384_D128.md"},
     "decode": {"source": "kda_decode.hip",
-               "kernel_sha256": "cd969b686b6b0e06382e0dbd651015bdea5d1895790e77c3248f0d1df9a3c844",
-               "bytes": (135790 * 2.0 + 263168 * 1.0) * 1024,
+               "kernel_sha256": "dbd91e6252347cccc113e9aee31ec2cb7dfa39e7ea8196a81cff33dafa790ae2",
+               "bytes": (135791 * 2.0 + 263168 * 1.0) * 1024,
                "profile": "profiles/kda_decode_bf16_B128_H32_T1_D128.md"},
 }
 
