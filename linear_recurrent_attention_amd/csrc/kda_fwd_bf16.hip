@@ -42,8 +42,9 @@
 // A step has three parts separated by workgroup barriers.  A single wave issues at most one vector
 // instruction every ~9 clocks on gfx950, while a SIMD shared by four waves issues one every ~2.5;
 // the parts are laid out so that each SIMD always has its four waves' work to interleave, and the
-// value waves, which carry the serial chain, issue at a raised priority.  Tiles pass between roles
-// through LDS, double buffered by chunk parity (the state scalings by chunk index mod 3).
+// value waves, which carry the serial chain, issue at the highest priority (the helper waves next).
+// Tiles pass between roles through LDS, double buffered by chunk parity (the state scalings by chunk
+// index mod 3).
 
 // Matrix-core operands (v_mfma_f32_16x16x32_bf16 and 16x16x16, float32 accumulate; "split" is
 // hi = bf16(x), lo = bf16(x - hi), products hi*hi + hi*lo + lo*hi):
@@ -455,7 +456,7 @@ __device__ void helper_waves(Smem& sm, const Params& p, size_t row0, int half, i
         adst[k] = (SUB * R + i) * LDA + sw(SUB * R + i, tperm(SUB * S + jj));
         azero[k] = R == S && jj > i;                              // above the diagonal of a diagonal block
     }
-    __builtin_amdgcn_s_setprio(3);  // the substitution is a chain of dependent steps: issue it first
+    __builtin_amdgcn_s_setprio(2);  // the substitution is a chain of dependent steps: issue it early
     for (int n = -1; n <= nchunk; ++n) {
         const bool gwork = n >= 0 && n < nchunk;
         ChunkTiles& H = sm.ch[n & 1];
@@ -602,7 +603,7 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
         ooff[R] = ((uint32_t)(SUB * R + l16) * (uint32_t)p.H * DV + half * DVH + 16 * vw + 4 * g4) * (OUT_F32 ? 4u : 2u);
     const float oscale = -kDown * p.scale;
 
-    __builtin_amdgcn_s_setprio(2);  // the value waves carry the serial chain: issue them first
+    __builtin_amdgcn_s_setprio(3);  // the value waves carry the serial chain: issue them first
 
     for (int n = -1; n <= nchunk; ++n) {
         const bool work = n >= 1;  // this step handles chunk n-1
