@@ -33,11 +33,12 @@
 // Each workgroup runs 16 waves, four per SIMD, in three roles:
 //   key waves 0-7     wave kw owns tokens 4kw..4kw+3 of a chunk (two key channels per lane): decay
 //                     sums, exponentials and operand tiles, two chunks ahead of the value waves;
-//                     the A Gram products (six half-sums) and Kbar^T one chunk ahead;
+//                     Kbar^T one chunk ahead;
 //   value waves 8-11  wave 8+w owns 16 value columns of the float32 state (all 128 rows) in
 //                     matrix-core accumulator layout for the whole run: the products with the state,
 //                     U, the output and the state update of one chunk per step;
-//   helper waves 12-15  the L Gram products, the UT inverse and A from its half-sums, one chunk ahead;
+//   helper waves 12-15  the L Gram products (waves 12, 13) and the A Gram half-sums (14, 15), the UT
+//                     inverse and A from its half-sums, one chunk ahead;
 //                     the v loads of the value waves (staged through LDS).
 // A step has three parts separated by workgroup barriers.  A single wave issues at most one vector
 // instruction every ~9 clocks on gfx950, while a SIMD shared by four waves issues one every ~2.5;
@@ -248,7 +249,7 @@ struct Carry {
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) { split_bf16(a, b, hi, lo); }
 
 // ------------------------------------------------------------------------------------------------
-// key waves.  Step n forms the factors of chunk n+1, and the A Gram products and the Kbar^T tile of
+// key waves.  Step n forms the factors of chunk n+1 and the Kbar^T tile of
 // chunk n.  Three barriers per step; steps n = -1 .. nchunk.
 // ------------------------------------------------------------------------------------------------
 template <bool IN_F32>
@@ -261,7 +262,7 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
     const int tq = TPW * kw;
     const int nf = n + 1;                     // chunk whose factors this step forms
     const bool fwork = nf < nchunk;
-    const bool gwork = n >= 0 && n < nchunk;  // chunk n: A Gram products and Kbar^T
+    const bool gwork = n >= 0 && n < nchunk;  // chunk n: Kbar^T
     const int t0 = nf * C;
     const int tn = min(t0 + C, (nchunk - 1) * C);  // the chunk prefetched this step (see load_chunk)
     ChunkTiles& Hf = sm.ch[nf & 1];
@@ -293,28 +294,8 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
     }
     lds_barrier();  // ---- barrier 1
 
-    // ---------------- part 2: A Gram half-sums of chunk n (waves 0-5); decays and exponentials of n+1
-    if (gwork && kw < 6) {
-        // A block (R,S) = (0,0), (1,0), (1,1) for kw >> 1, over channel blocks 2(kw & 1), 2(kw & 1) + 1,
-        // split bf16; the float32 partial sum goes to apart (a helper wave adds the two halves)
-        const int blk = kw >> 1, mh = kw & 1;
-        const int R = blk == 0 ? 0 : 1, S = blk == 2 ? 1 : 0;
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-            const int kc = 32 * (2 * mh + mm) + 8 * g4;
-            const u32x4 aH = ld16(&Hg.qmh[SUB * R + l16][kc]);
-            const u32x4 aL = ld16(&Hg.qml[SUB * R + l16][kc]);
-            const u32x4 bH = ld16(&sm.key.khh[SUB * S + l16][kc]);
-            const u32x4 bL = ld16(&sm.key.khl[SUB * S + l16][kc]);
-            f32x4& a = mm ? a1 : a0;
-            a = mfma_bf16(aH, bH, a);
-            a = mfma_bf16(aH, bL, a);
-            a = mfma_bf16(aL, bH, a);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.s.apart[kw][r][lane] = a0[r] + a1[r];
-    }
+    // ---------------- part 2: decays and exponentials of chunk n+1 (the A Gram products of chunk n are
+    // the helper waves')
     if (fwork) {
         float tt0[NKW], tt1[NKW];
 #pragma unroll
@@ -513,6 +494,31 @@ __device__ void helper_waves(Smem& sm, const Params& p, size_t row0, int half, i
                     H.th[SUB + i][sw(SUB + i, tperm(l16))] = hi & 0xffffu;
                     H.tl[SUB + i][sw(SUB + i, tperm(l16))] = lo & 0xffffu;
                 }
+            }
+        }
+        // ---------------- part 2: the A Gram half-sums of chunk n (waves 2, 3): blocks (R,S) = (0,0),
+        // (1,0), (1,1) of Qm Kh^T over channels 0-63 (wave 2) or 64-127 (wave 3), split bf16; the
+        // float32 half-sums go to apart, which part 3 adds
+        if (gwork && hw >= 2) {
+            const int mh = hw - 2;
+#pragma unroll
+            for (int blk = 0; blk < 3; ++blk) {
+                const int R = blk == 0 ? 0 : 1, S = blk == 2 ? 1 : 0;
+                f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    const int kc = 32 * (2 * mh + mm) + 8 * g4;
+                    const u32x4 aH = ld16(&H.qmh[SUB * R + l16][kc]);
+                    const u32x4 aL = ld16(&H.qml[SUB * R + l16][kc]);
+                    const u32x4 bH = ld16(&sm.key.khh[SUB * S + l16][kc]);
+                    const u32x4 bL = ld16(&sm.key.khl[SUB * S + l16][kc]);
+                    f32x4& a = mm ? a1 : a0;
+                    a = mfma_bf16(aH, bH, a);
+                    a = mfma_bf16(aH, bL, a);
+                    a = mfma_bf16(aL, bH, a);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.s.apart[2 * blk + mh][r][lane] = a0[r] + a1[r];
             }
         }
         lds_barrier();  // ---- barrier 2
