@@ -33,9 +33,20 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 // Split a pair into bf16 hi + bf16 lo with a ~= hi + lo to about 16 significant bits.
+// The remainders a - hi_a and b - hi_b are exact in float32.  Each is one v_dot2c_f32_bf16 of the
+// packed hi with (-1, 0) or (0, -1), accumulated onto a or b, which saves unpacking hi into two
+// floats; the result is bit for bit that of the plain subtraction (denormals included) for every
+// finite pair whose hi does not round to infinity.  The (-1, 0) pair (0x0000bf80) is kept in a
+// scalar register: the compiler folds it into the inline constant -1.0, which this instruction
+// applies as the float32 bit pattern 0xbf800000, i.e. as (0, -1).
 __device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
     hi = pack_bf16(a, b);
-    lo = pack_bf16(a - bf16lo_to_f(hi), b - bf16hi_to_f(hi));
+    uint32_t m_lo;
+    asm("s_mov_b32 %0, 0xbf80" : "=s"(m_lo));
+    const bf16x2 h = __builtin_bit_cast(bf16x2, hi);
+    const float ra = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m_lo), a, false);
+    const float rb = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, 0xbf800000u), b, false);
+    lo = pack_bf16(ra, rb);
 }
 
 // Workgroup barrier that orders LDS only (in-flight global loads and stores are not waited for).
