@@ -39,14 +39,19 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // finite pair whose hi does not round to infinity.  The (-1, 0) pair (0x0000bf80) is kept in a
 // scalar register: the compiler folds it into the inline constant -1.0, which this instruction
 // applies as the float32 bit pattern 0xbf800000, i.e. as (0, -1).
-__device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
-    hi = pack_bf16(a, b);
+// a - (low half of hi as a float), b - (high half of hi as a float)
+__device__ __forceinline__ float remainder_lo(uint32_t hi, float a) {
     uint32_t m_lo;
     asm("s_mov_b32 %0, 0xbf80" : "=s"(m_lo));
-    const bf16x2 h = __builtin_bit_cast(bf16x2, hi);
-    const float ra = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m_lo), a, false);
-    const float rb = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, 0xbf800000u), b, false);
-    lo = pack_bf16(ra, rb);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, hi), __builtin_bit_cast(bf16x2, m_lo), a, false);
+}
+__device__ __forceinline__ float remainder_hi(uint32_t hi, float b) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, hi), __builtin_bit_cast(bf16x2, 0xbf800000u), b,
+                                           false);
+}
+__device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = pack_bf16(a, b);
+    lo = pack_bf16(remainder_lo(hi, a), remainder_hi(hi, b));
 }
 
 // Workgroup barrier that orders LDS only (in-flight global loads and stores are not waited for).

@@ -345,14 +345,36 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
     // loads are spread over the step rather than queued all at once
     load_chunk<LOAD_QK>(nxt, p, kl, row0, tn);
     if (fwork) {
+        // Layer by layer across the quad (unpack and products, hi, remainders, lo), with scheduling
+        // barriers between layers: each layer is a set of independent instructions, so a wave
+        // issues them back to back instead of waiting on each result in turn.
         uint32_t wqh[TPW], wql[TPW], wkm[TPW], wkh[TPW], wkl[TPW];
+        f32x2 qe[TPW], ke[TPW], kf[TPW];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const f32x2 qq = unpack_q(cur.q[i]), kk = unpack_q(cur.k[i]);
-            split2(qq[0] * cy.e[i][0], qq[1] * cy.e[i][1], wqh[i], wql[i]);
-            wkm[i] = pack_bf16(kk[0] * cy.e[i][0], kk[1] * cy.e[i][1]);
+            qe[i] = f32x2{qq[0] * cy.e[i][0], qq[1] * cy.e[i][1]};
+            ke[i] = f32x2{kk[0] * cy.e[i][0], kk[1] * cy.e[i][1]};
             cy.kh[i][0] = kk[0] * cy.f[i][0]; cy.kh[i][1] = kk[1] * cy.f[i][1];
-            split2(cy.kh[i][0], cy.kh[i][1], wkh[i], wkl[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            wqh[i] = pack_bf16(qe[i][0], qe[i][1]);
+            wkm[i] = pack_bf16(ke[i][0], ke[i][1]);
+            wkh[i] = pack_bf16(cy.kh[i][0], cy.kh[i][1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            qe[i] = f32x2{remainder_lo(wqh[i], qe[i][0]), remainder_hi(wqh[i], qe[i][1])};
+            kf[i] = f32x2{remainder_lo(wkh[i], cy.kh[i][0]), remainder_hi(wkh[i], cy.kh[i][1])};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            wql[i] = pack_bf16(qe[i][0], qe[i][1]);
+            wkl[i] = pack_bf16(kf[i][0], kf[i][1]);
         }
         // one array at a time, so that stores of neighbouring tokens pair up
 #pragma unroll
