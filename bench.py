@@ -34,13 +34,13 @@ CSRC = os.path.join(ROOT, "linear_recurrent_attention_amd", "csrc")
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by the same counters on a
 # 512 MiB copy (factors 2.0 and 1.0); valid only for the kernel source with the recorded hash.
 MEASURED_TRAFFIC = {
-    "core": {"source": "kda_fwd_bf16.hip",
-             "kernel_sha256": "dd8f887ccb06e5417a3457ad6ac0d141853a3c6d747242f4f60da2ce01d9b3dc",
-             "bytes": (1366950 * 2.0 + 532480 * 1.0) * 1024,
+    "core": {"sources": ("kda_fwd_bf16.hip", "kda_common.h"),
+             "sha256": "8973092e33def20d7fa5f1602f92fde661af9d46310ca14fbb5a47ced7d113d2",
+             "bytes": (1351001 * 2.0 + 532480 * 1.0) * 1024,
              "profile": "profiles/kda_fwd_bf16_B4_H32_T16384_D128.md"},
-    "decode": {"source": "kda_decode.hip",
-               "kernel_sha256": "dbd91e6252347cccc113e9aee31ec2cb7dfa39e7ea8196a81cff33dafa790ae2",
-               "bytes": (135791 * 2.0 + 263168 * 1.0) * 1024,
+    "decode": {"sources": ("kda_decode.hip", "kda_common.h"),
+               "sha256": "27169bbf2dad64f9f864da57513ef39a0250b622edfad8163610ea21d502356f",
+               "bytes": (135790 * 2.0 + 263168 * 1.0) * 1024,
                "profile": "profiles/kda_decode_bf16_B128_H32_T1_D128.md"},
 }
 
@@ -63,13 +63,20 @@ def algorithmic_flops(B, T, H, Dk, Dv, C=32):
     return B * H * (T / C) * per_chunk
 
 
+def source_digest(names):
+    """sha256 over the kernel sources a counter profile was taken on (concatenated in order)."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(which="core"):
     """HBM bytes per launch from the committed counter profile, or None if the kernel changed since."""
-    import hashlib
     m = MEASURED_TRAFFIC[which]
-    with open(os.path.join(CSRC, m["source"]), "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    return m["bytes"] if digest == m["kernel_sha256"] else None
+    return m["bytes"] if m["bytes"] is not None and source_digest(m["sources"]) == m["sha256"] else None
 
 
 def cpu_baseline(d, threads):
