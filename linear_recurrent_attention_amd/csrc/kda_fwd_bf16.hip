@@ -252,7 +252,7 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
 // key waves.  Step n forms the factors of chunk n+1 and the Kbar^T tile of
 // chunk n.  Three barriers per step; steps n = -1 .. nchunk.
 // ------------------------------------------------------------------------------------------------
-template <bool IN_F32>
+template <bool IN_F32, bool SO>
 __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoad& kl, size_t row0, int n,
                                          int nchunk, Raw<IN_F32>& cur, Raw<IN_F32>& nxt, Carry& cy) {
     const int kw = kl.kw, lane = kl.lane;
@@ -348,50 +348,81 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         // Layer by layer across the quad (unpack and products, hi, remainders, lo), with scheduling
         // barriers between layers: each layer is a set of independent instructions, so a wave
         // issues them back to back instead of waiting on each result in turn.
-        uint32_t wqh[TPW], wql[TPW], wkm[TPW], wkh[TPW], wkl[TPW];
-        f32x2 qe[TPW], ke[TPW], kf[TPW];
+        // Qm serves only the output (Qm P and A): the state-only instantiation forms the key tiles alone.
+        if constexpr (!SO) {
+            uint32_t wqh[TPW], wql[TPW], wkm[TPW], wkh[TPW], wkl[TPW];
+            f32x2 qe[TPW], ke[TPW], kf[TPW];
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const f32x2 qq = unpack_q(cur.q[i]), kk = unpack_q(cur.k[i]);
-            qe[i] = f32x2{qq[0] * cy.e[i][0], qq[1] * cy.e[i][1]};
-            ke[i] = f32x2{kk[0] * cy.e[i][0], kk[1] * cy.e[i][1]};
-            cy.kh[i][0] = kk[0] * cy.f[i][0]; cy.kh[i][1] = kk[1] * cy.f[i][1];
+            for (int i = 0; i < TPW; ++i) {
+                const f32x2 qq = unpack_q(cur.q[i]), kk = unpack_q(cur.k[i]);
+                qe[i] = f32x2{qq[0] * cy.e[i][0], qq[1] * cy.e[i][1]};
+                ke[i] = f32x2{kk[0] * cy.e[i][0], kk[1] * cy.e[i][1]};
+                cy.kh[i][0] = kk[0] * cy.f[i][0]; cy.kh[i][1] = kk[1] * cy.f[i][1];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                wqh[i] = pack_bf16(qe[i][0], qe[i][1]);
+                wkm[i] = pack_bf16(ke[i][0], ke[i][1]);
+                wkh[i] = pack_bf16(cy.kh[i][0], cy.kh[i][1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                qe[i] = f32x2{remainder_lo(wqh[i], qe[i][0]), remainder_hi(wqh[i], qe[i][1])};
+                kf[i] = f32x2{remainder_lo(wkh[i], cy.kh[i][0]), remainder_hi(wkh[i], cy.kh[i][1])};
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                wql[i] = pack_bf16(qe[i][0], qe[i][1]);
+                wkl[i] = pack_bf16(kf[i][0], kf[i][1]);
+            }
+            // one array at a time, so that stores of neighbouring tokens pair up
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&Hf.qmh[tq + i][pc0]) = wqh[i];
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&Hf.qml[tq + i][pc0]) = wql[i];
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&Hf.km[tq + i][pc0]) = wkm[i];
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khh[tq + i][pc0]) = wkh[i];
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khl[tq + i][pc0]) = wkl[i];
+        } else {
+            uint32_t wkm[TPW], wkh[TPW], wkl[TPW];
+            f32x2 ke[TPW], kf[TPW];
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const f32x2 kk = unpack_q(cur.k[i]);
+                ke[i] = f32x2{kk[0] * cy.e[i][0], kk[1] * cy.e[i][1]};
+                cy.kh[i][0] = kk[0] * cy.f[i][0]; cy.kh[i][1] = kk[1] * cy.f[i][1];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                wkm[i] = pack_bf16(ke[i][0], ke[i][1]);
+                wkh[i] = pack_bf16(cy.kh[i][0], cy.kh[i][1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) kf[i] = f32x2{remainder_lo(wkh[i], cy.kh[i][0]), remainder_hi(wkh[i], cy.kh[i][1])};
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) wkl[i] = pack_bf16(kf[i][0], kf[i][1]);
+            // one array at a time, so that stores of neighbouring tokens pair up
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&Hf.km[tq + i][pc0]) = wkm[i];
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khh[tq + i][pc0]) = wkh[i];
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khl[tq + i][pc0]) = wkl[i];
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            wqh[i] = pack_bf16(qe[i][0], qe[i][1]);
-            wkm[i] = pack_bf16(ke[i][0], ke[i][1]);
-            wkh[i] = pack_bf16(cy.kh[i][0], cy.kh[i][1]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            qe[i] = f32x2{remainder_lo(wqh[i], qe[i][0]), remainder_hi(wqh[i], qe[i][1])};
-            kf[i] = f32x2{remainder_lo(wkh[i], cy.kh[i][0]), remainder_hi(wkh[i], cy.kh[i][1])};
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            wql[i] = pack_bf16(qe[i][0], qe[i][1]);
-            wkl[i] = pack_bf16(kf[i][0], kf[i][1]);
-        }
-        // one array at a time, so that stores of neighbouring tokens pair up
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&Hf.qmh[tq + i][pc0]) = wqh[i];
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&Hf.qml[tq + i][pc0]) = wql[i];
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&Hf.km[tq + i][pc0]) = wkm[i];
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khh[tq + i][pc0]) = wkh[i];
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint32_t*>(&sm.key.khl[tq + i][pc0]) = wkl[i];
     }
     lds_barrier();  // ---- barrier 3
 }
 
-template <bool IN_F32>
+template <bool IN_F32, bool SO>
 __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int kw, int lane, int nchunk) {
     KeyLoad kl;
     kl.kw = kw;
@@ -406,15 +437,15 @@ __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int kw, int la
     load_chunk<LOAD_ALL>(ra, p, kl, row0, 0);
     // two steps per iteration so the prefetch target alternates between two register sets
     for (int n = -1; n <= nchunk; n += 2) {
-        key_step<IN_F32>(sm, p, kl, row0, n, nchunk, ra, rb, cy);
-        if (n + 1 <= nchunk) key_step<IN_F32>(sm, p, kl, row0, n + 1, nchunk, rb, ra, cy);
+        key_step<IN_F32, SO>(sm, p, kl, row0, n, nchunk, ra, rb, cy);
+        if (n + 1 <= nchunk) key_step<IN_F32, SO>(sm, p, kl, row0, n + 1, nchunk, rb, ra, cy);
     }
 }
 
 // ------------------------------------------------------------------------------------------------
 // helper waves.  Step n: the L Gram products (part 2), then the UT inverse and A (part 3) of chunk n.
 // ------------------------------------------------------------------------------------------------
-template <bool IN_F32, bool HP>
+template <bool IN_F32, bool HP, bool SO>
 __device__ void helper_waves(Smem& sm, const Params& p, size_t row0, int half, int hw, int lane, int nchunk) {
     const int l16 = lane & 15, g4 = lane >> 4;
     // v for value wave hw: this lane's values are tokens 16R + 4*g4 + r of a chunk, column col, read one
@@ -520,8 +551,8 @@ __device__ void helper_waves(Smem& sm, const Params& p, size_t row0, int half, i
         }
         // ---------------- part 2: the A Gram half-sums of chunk n (waves 2, 3): blocks (R,S) = (0,0),
         // (1,0), (1,1) of Qm Kh^T over channels 0-63 (wave 2) or 64-127 (wave 3), split bf16; the
-        // float32 half-sums go to apart, which part 3 adds
-        if (gwork && hw >= 2) {
+        // float32 half-sums go to apart, which part 3 adds (A serves only the output: not in a state-only run)
+        if (!SO && gwork && hw >= 2) {
             const int mh = hw - 2;
 #pragma unroll
             for (int blk = 0; blk < 3; ++blk) {
@@ -588,16 +619,19 @@ __device__ void helper_waves(Smem& sm, const Params& p, size_t row0, int half, i
             H.th[o + i][cb] = hi >> 16;
             H.tl[o + i][ca] = lo & 0xffffu;
             H.tl[o + i][cb] = lo >> 16;
-            // A'' = -2^64 A from the two channel-half sums (lower triangle on the diagonal blocks)
+            // A'' = -2^64 A from the two channel-half sums (lower triangle on the diagonal blocks); only
+            // with an output
+            if constexpr (!SO) {
 #pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                const float* ap = &sm.s.apart[2 * k][0][0];
-                float v = -kUp * (ap[asrc[k]] + ap[256 + asrc[k]]);
-                if (azero[k]) v = 0.f;
-                uint32_t h2, l2;
-                split2(v, 0.f, h2, l2);
-                (&H.ah[0][0])[adst[k]] = h2 & 0xffffu;
-                (&H.al[0][0])[adst[k]] = l2 & 0xffffu;
+                for (int k = 0; k < 3; ++k) {
+                    const float* ap = &sm.s.apart[2 * k][0][0];
+                    float v = -kUp * (ap[asrc[k]] + ap[256 + asrc[k]]);
+                    if (azero[k]) v = 0.f;
+                    uint32_t h2, l2;
+                    split2(v, 0.f, h2, l2);
+                    (&H.ah[0][0])[adst[k]] = h2 & 0xffffu;
+                    (&H.al[0][0])[adst[k]] = l2 & 0xffffu;
+                }
             }
         }
         lds_barrier();  // ---- barrier 3
@@ -607,7 +641,7 @@ __device__ void helper_waves(Smem& sm, const Params& p, size_t row0, int half, i
 // ------------------------------------------------------------------------------------------------
 // value waves.  Step n handles chunk n-1 (nothing for n < 1); three barriers per step.
 // ------------------------------------------------------------------------------------------------
-template <bool OUT_F32, bool IN_F32, bool CKPT>
+template <bool OUT_F32, bool IN_F32, bool CKPT, bool SO>
 __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int half, int vw, int lane, int nchunk) {
     const int l16 = lane & 15, g4 = lane >> 4;
 
@@ -643,8 +677,17 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
         f32x4 oacc[2];
         // ---------------- part 1: P = -2^64 Diag(exp(b_15)) S as split-bf16 operands; Qm P
         // (each product chain below has its own accumulators, interleaved, so that consecutive matrix
-        // instructions never wait for each other's results)
-        if (work) {
+        // instructions never wait for each other's results).  A state-only run needs P_hi alone (for X~).
+        if (SO && work) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 e0 = *reinterpret_cast<const f32x4*>(&Sc.ep[32 * m + 4 * g4]);
+                const f32x4 e1 = *reinterpret_cast<const f32x4*>(&Sc.ep[32 * m + 16 + 4 * g4]);
+                const f32x4 a = st[2 * m] * e0, b = st[2 * m + 1] * e1;
+                ph[m] = u32x4{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]), pack_bf16(b[2], b[3])};
+            }
+        }
+        if (!SO && work) {
             f32x4 q[2][3];
 #pragma unroll
             for (int R = 0; R < 2; ++R)
@@ -730,7 +773,7 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
 
         // ---------------- part 3: O = -2^-64 (Qm P + A'' U), output; S <- Diag(Gamma_31) S + Kbar^T U
         if (work) {
-            if (p.o) {  // (o == NULL: a state-only run of the in-device context parallelism)
+            if (!SO && p.o) {  // (o == NULL: a state-only run of the in-device context parallelism)
                 gchar* ob = (gchar*)uniform_gptr((const char*)p.o + ((row0 + (size_t)t0 * p.H) * DV) * (OUT_F32 ? 4 : 2));
                 f32x4 o1[2], o2[2];
 #pragma unroll
@@ -793,7 +836,8 @@ __device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int 
 }
 
 // CKPT: S_ckpt is set (a separate instantiation keeps the plain forward free of the checkpoint code)
-template <bool OUT_F32, bool IN_F32, bool HP, bool CKPT>
+// SO: a state-only run (o == NULL): the output and everything only it needs (Qm, A, Qm P) is skipped
+template <bool OUT_F32, bool IN_F32, bool HP, bool CKPT, bool SO>
 __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
     __shared__ Smem sm;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -815,11 +859,11 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
     if (nchunk == 0) return;  // (the host runs the state copy instead; every wave leaves here alike)
 
     if (wave < NKW)
-        key_waves<IN_F32>(sm, p, row0, wave, lane, nchunk);
+        key_waves<IN_F32, SO>(sm, p, row0, wave, lane, nchunk);
     else if (wave < NKW + NVW)
-        value_waves<OUT_F32, IN_F32, CKPT>(sm, p, bh, row0, half, wave - NKW, lane, nchunk);
+        value_waves<OUT_F32, IN_F32, CKPT, SO>(sm, p, bh, row0, half, wave - NKW, lane, nchunk);
     else
-        helper_waves<IN_F32, HP>(sm, p, row0, half, wave - NKW - NVW, lane, nchunk);
+        helper_waves<IN_F32, HP, SO>(sm, p, row0, half, wave - NKW - NVW, lane, nchunk);
 }
 
 }  // namespace bf16path
@@ -827,14 +871,18 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
 namespace bf16path {
 template <bool CKPT>
 void launch_bf16_io(const Params& p, hipStream_t stream, dim3 grid, dim3 block) {
-    if (p.o_f32 && p.precise)
-        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, false, true, CKPT>), grid, block, 0, stream, p);
+    if (!p.o && p.precise)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, false, true, CKPT, true>), grid, block, 0, stream, p);
+    else if (!p.o)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, false, false, CKPT, true>), grid, block, 0, stream, p);
+    else if (p.o_f32 && p.precise)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, false, true, CKPT, false>), grid, block, 0, stream, p);
     else if (p.o_f32)
-        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, false, false, CKPT>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, false, false, CKPT, false>), grid, block, 0, stream, p);
     else if (p.precise)
-        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, false, true, CKPT>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, false, true, CKPT, false>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, false, false, CKPT>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, false, false, CKPT, false>), grid, block, 0, stream, p);
 }
 }  // namespace bf16path
 
@@ -842,8 +890,10 @@ hipError_t launch_fwd_bf16(const Params& p, hipStream_t stream) {
     using namespace bf16path;
     if (p.T == 0) return launch_state_copy(p, stream);
     const dim3 grid(2 * p.B * p.H), block(NTHR);
-    if (p.in_f32)  // the layer's variant (it records no checkpoints)
-        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, true, true, false>), grid, block, 0, stream, p);
+    if (p.in_f32 && !p.o)  // the layer's variant (it records no checkpoints)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<false, true, true, false, true>), grid, block, 0, stream, p);
+    else if (p.in_f32)
+        hipLaunchKernelGGL((kda_fwd_bf16_kernel<true, true, true, false, false>), grid, block, 0, stream, p);
     else if (p.S_ckpt)
         launch_bf16_io<true>(p, stream, grid, block);
     else
