@@ -157,7 +157,8 @@ __device__ __forceinline__ f32x2 unpack_q(f32x2 w) { return w; }
 
 // Per-thread constants of the key waves' chunk loads (byte offsets within a chunk).
 struct KeyLoad {
-    uint32_t off[TPW];   // token TPW*kw + i, key channels 2*lane, 2*lane+1 of q/k (g: twice this)
+    uint32_t off[TPW];   // token TPW*kw + i, key channels 2*lane, 2*lane+1 of bf16 q/k
+    uint32_t goff[TPW];  // the same for float32 g (and float32 q/k): twice off
     uint32_t boff;       // beta of token TPW*kw + (lane % TPW)
     uint32_t lane_b, tok_b;  // for the clamped tail loads
     int kw, lane;
@@ -200,25 +201,20 @@ __device__ __forceinline__ void load_chunk(Raw<IN_F32>& r, const Params& p, cons
     const gchar* gc = uniform_gptr(p.g + ce);
     const gchar* bc = uniform_gptr(p.beta + row0 + (size_t)t0 * p.H);
     using QT = typename Raw<IN_F32>::QT;
-    if (t0 + C <= p.T) {
+    // Offsets grow with the token, so tokens past the end are clamped to the last valid one by a min on
+    // the byte offset (no clamp at all for a full chunk: a bound of ~0).
+    const bool full = t0 + C <= p.T;
+    const uint32_t lim = (uint32_t)(p.T - 1 - t0);
+    const uint32_t lq = full ? ~0u : lim * kl.tok_b + kl.lane_b;  // bf16 q/k bound
+    const uint32_t lg = full ? ~0u : 2u * (lim * kl.tok_b + kl.lane_b);
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            if constexpr (LQ) r.q[i] = gload<QT>(qc, qs * kl.off[i]);
-            if constexpr (LQ) r.k[i] = gload<QT>(kc, qs * kl.off[i]);
-            if constexpr (LG) r.g[i] = gload<f32x2>(gc, 2 * kl.off[i]);
-        }
-        if constexpr (LG) r.beta = gload<float>(bc, kl.boff);
-    } else {
-        const int lim = p.T - 1 - t0;
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const uint32_t o = (uint32_t)min(TPW * kl.kw + i, lim) * kl.tok_b + kl.lane_b;  // < 2^31
-            if constexpr (LQ) r.q[i] = gload<QT>(qc, qs * o);
-            if constexpr (LQ) r.k[i] = gload<QT>(kc, qs * o);
-            if constexpr (LG) r.g[i] = gload<f32x2>(gc, 2 * o);
-        }
-        if constexpr (LG) r.beta = gload<float>(bc, (uint32_t)min(TPW * kl.kw + (kl.lane % TPW), lim) * 4u * p.H);
+    for (int i = 0; i < TPW; ++i) {
+        const uint32_t oq = IN_F32 ? min(kl.goff[i], lg) : min(kl.off[i], lq);
+        if constexpr (LQ) r.q[i] = gload<QT>(qc, oq);
+        if constexpr (LQ) r.k[i] = gload<QT>(kc, oq);
+        if constexpr (LG) r.g[i] = gload<f32x2>(gc, min(kl.goff[i], lg));
     }
+    if constexpr (LG) r.beta = gload<float>(bc, min(kl.boff, full ? ~0u : lim * 4u * (uint32_t)p.H));
 }
 
 // Zero the tokens at or past T (k = v = 0, beta = 0, g = 0 leaves the state unchanged; the value
@@ -430,7 +426,10 @@ __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int kw, int la
     kl.tok_b = (uint32_t)p.H * DK * 2;
     kl.lane_b = 4 * lane;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) kl.off[i] = (uint32_t)(TPW * kw + i) * kl.tok_b + kl.lane_b;
+    for (int i = 0; i < TPW; ++i) {
+        kl.off[i] = (uint32_t)(TPW * kw + i) * kl.tok_b + kl.lane_b;
+        kl.goff[i] = 2u * kl.off[i];
+    }
     kl.boff = (uint32_t)(TPW * kw + (lane % TPW)) * 4u * p.H;
     Raw<IN_F32> ra, rb;
     Carry cy;
@@ -458,16 +457,20 @@ __device__ void helper_waves(Smem& sm, const Params& p, size_t row0, int half, i
     const uint32_t vrow = (uint32_t)p.H * DV * (uint32_t)sizeof(VT);  // bytes between tokens
     const uint32_t vcol = (uint32_t)col * (uint32_t)sizeof(VT);
     VT vr[2][4];
+    uint32_t voff[2][4];  // byte offsets of this lane's values within a chunk
+#pragma unroll
+    for (int R = 0; R < 2; ++R)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) voff[R][r] = (uint32_t)(SUB * R + 4 * g4 + r) * vrow + vcol;
     auto load_v = [&](int tc0) {
         const size_t e0 = (row0 + (size_t)tc0 * p.H) * DV;
         const gchar* vb = uniform_gptr(p.v ? (const void*)((const VT*)p.v + e0) : (const void*)(p.g + e0));
         // offsets grow with the row, so a row past T is clamped to row T-1 by a min on the offset
-        const uint32_t last = (uint32_t)min(p.T - 1 - tc0, C - 1) * vrow + vcol;
+        const uint32_t last = tc0 + C <= p.T ? 0xffffffffu : (uint32_t)(p.T - 1 - tc0) * vrow + vcol;
 #pragma unroll
         for (int R = 0; R < 2; ++R)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                vr[R][r] = gload<VT>(vb, min((uint32_t)(SUB * R + 4 * g4 + r) * vrow + vcol, last));
+            for (int r = 0; r < 4; ++r) vr[R][r] = gload<VT>(vb, min(voff[R][r], last));
     };
     load_v(0);
     // A's block (0,1) is zero in both buffers; no chunk writes it
@@ -498,15 +501,25 @@ __device__ void helper_waves(Smem& sm, const Params& p, size_t row0, int half, i
         if (gwork) {
             float x[8];
             const int t0 = n * C;
+            // (rows past T and v == NULL, where the loads read g, are replaced by 0; full chunks of v, the
+            // common case, take no per-lane test)
 #pragma unroll
             for (int R = 0; R < 2; ++R)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float v;
-                    if constexpr (IN_F32) v = vr[R][r];
-                    else v = __uint_as_float((uint32_t)vr[R][r] << 16);
-                    x[4 * R + r] = (p.v && t0 + SUB * R + 4 * g4 + r < p.T) ? kUp * v : 0.f;
+                    if constexpr (IN_F32) x[4 * R + r] = vr[R][r];
+                    else x[4 * R + r] = __uint_as_float((uint32_t)vr[R][r] << 16);
                 }
+            if (p.v && t0 + C <= p.T) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] *= kUp;
+            } else {
+#pragma unroll
+                for (int R = 0; R < 2; ++R)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        x[4 * R + r] = (p.v && t0 + SUB * R + 4 * g4 + r < p.T) ? kUp * x[4 * R + r] : 0.f;
+            }
             f32x4* dst = reinterpret_cast<f32x4*>(&sm.vs[n & 1].x[hw][lane][0]);
             dst[0] = f32x4{x[0], x[1], x[2], x[3]};
             dst[1] = f32x4{x[4], x[5], x[6], x[7]};
