@@ -35,8 +35,8 @@ CSRC = os.path.join(ROOT, "linear_recurrent_attention_amd", "csrc")
 # 512 MiB copy (factors 2.0 and 1.0); valid only for the kernel source with the recorded hash.
 MEASURED_TRAFFIC = {
     "core": {"sources": ("kda_fwd_bf16.hip", "kda_common.h"),
-             "sha256": "8973092e33def20d7fa5f1602f92fde661af9d46310ca14fbb5a47ced7d113d2",
-             "bytes": (1351001 * 2.0 + 532480 * 1.0) * 1024,
+             "sha256": "3974b36a2969e6b1876b507e348d0ac98d92da0182bbccc795efa6abf546a3b5",
+             "bytes": (1349042 * 2.0 + 532480 * 1.0) * 1024,
              "profile": "profiles/kda_fwd_bf16_B4_H32_T16384_D128.md"},
     "decode": {"sources": ("kda_decode.hip", "kda_common.h"),
                "sha256": "27169bbf2dad64f9f864da57513ef39a0250b622edfad8163610ea21d502356f",
