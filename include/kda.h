@@ -91,7 +91,9 @@ typedef struct {
  *                                      Values outside the bound can overflow intermediate factors.
  *   beta   : [B, T, H]      float32    write strength, usually in (0, 1)
  *   S0     : [B, H, Dk, Dv] float32    initial state (rows = key channels), or NULL for zeros
- *   o      : [B, T, H, Dv]  o_dtype    output
+ *   o      : [B, T, H, Dv]  o_dtype    output; on the bf16 path NULL computes the state alone (a
+ *                                      leaner kernel that skips the readout: to fill a prefix cache,
+ *                                      section 13.9); then S_T must be given
  *   S_T    : [B, H, Dk, Dv] float32    final state, or NULL to skip it; may equal S0
  *   ws     : device workspace of at least kda_fwd_workspace_size(desc) bytes, 256-byte aligned; NULL
  *            when that size is 0 (the plain forward needs none); contents are scratch
@@ -124,6 +126,8 @@ kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const
  *            sequence at token (m+1)*every.  Resuming there with kda_fwd reproduces the remaining
  *            outputs and S_T of the uninterrupted call bit for bit.  May be NULL only when n_ckpt = 0;
  *            must not alias any other argument; 8-byte aligned.
+ * o may be NULL on the bf16 path, as for kda_fwd (then S_T or a checkpoint must be written): the
+ * states alone, the cheap way to fill a prefix cache.
  * Every other argument and the return codes are those of kda_fwd.
  */
 kda_status kda_fwd_ckpt(const kda_fwd_desc* desc, const void* q, const void* k, const void* v,

@@ -23,7 +23,8 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, chunk, precise, scale, validate=False):
+def _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, chunk, precise, scale, validate=False,
+              want_output=True):
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     for t in (q, k, v, g, beta):
@@ -38,7 +39,9 @@ def _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, chunk, 
     if S0 is not None and (S0.dtype != torch.float32 or S0.shape != (B, H, Dk, Dv) or not S0.is_contiguous()):
         raise ValueError("S0 must be a contiguous float32 [B,H,Dk,Dv] tensor")
     o_dtype = q.dtype if o_dtype is None else o_dtype
-    o = out if out is not None else torch.empty((B, T, H, Dv), dtype=o_dtype, device=q.device)
+    o = None
+    if want_output:
+        o = out if out is not None else torch.empty((B, T, H, Dv), dtype=o_dtype, device=q.device)
     ST = None
     if want_state:
         ST = state_out if state_out is not None else torch.empty((B, H, Dk, Dv), dtype=torch.float32,
@@ -50,17 +53,18 @@ def _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, chunk, 
 
 def kda_fwd(q, k, v, g, beta, S0=None, scale: float = 1.0, o_dtype=None, want_state: bool = True,
             out=None, state_out=None, chunk: int = 0, precise: bool = False, validate: bool = False,
-            workspace=None):
+            workspace=None, want_output: bool = True):
     """Gated delta rule forward.  Shapes: q, k, g [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H];
     S0 [B,H,Dk,Dv] float32 or None.  q, k, v float32 or bfloat16; g, beta float32.
     precise: split-bf16 key Gram matrix and state update on the bf16 path (KDA_FWD_PRECISE).
     validate: check g in [-5, 0] and finite inputs first (KDA_VALIDATE; synchronises the stream and
     raises KdaError with KDA_ERR_INVALID_ARG on a finding).
+    want_output=False (bf16 inputs): the state alone, on the leaner state-only kernel.
 
-    Returns (o [B,T,H,Dv], S_T [B,H,Dk,Dv] float32 or None).
+    Returns (o [B,T,H,Dv] or None, S_T [B,H,Dk,Dv] float32 or None).
     """
     desc, o, ST = _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, out, state_out, chunk, precise, scale,
-                            validate)
+                            validate, want_output)
     need = _lib.fwd_workspace_size(desc)
     ws = workspace
     if ws is None and need > 0:
@@ -72,12 +76,14 @@ def kda_fwd(q, k, v, g, beta, S0=None, scale: float = 1.0, o_dtype=None, want_st
 
 
 def kda_fwd_ckpt(q, k, v, g, beta, every: int, S0=None, scale: float = 1.0, o_dtype=None,
-                 want_state: bool = True, chunk: int = 0, precise: bool = False):
+                 want_state: bool = True, chunk: int = 0, precise: bool = False, want_output: bool = True):
     """kda_fwd that also returns state checkpoints: S_ckpt [B,H,T//every,Dk,Dv] float32, entry m being
     the state after tokens [0, (m+1)*every) (the S0 that resumes the sequence there).
+    want_output=False (bf16 inputs): the states alone (filling a prefix cache).
 
-    Returns (o, S_T, S_ckpt)."""
-    desc, o, ST = _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, None, None, chunk, precise, scale)
+    Returns (o or None, S_T, S_ckpt)."""
+    desc, o, ST = _fwd_args(q, k, v, g, beta, S0, o_dtype, want_state, None, None, chunk, precise, scale,
+                            want_output=want_output)
     B, T, H, Dk = q.shape
     n = T // every if every > 0 else 0
     ck = torch.empty((B, H, n, Dk, v.shape[-1]), dtype=torch.float32, device=q.device)

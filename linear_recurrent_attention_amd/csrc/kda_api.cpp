@@ -36,10 +36,12 @@ bool chunk_ok(const kda_fwd_desc* d, int kernel_chunk) {
     return d->chunk == 0 || (d->chunk >= kernel_chunk && d->chunk <= 64 && d->chunk % kernel_chunk == 0);
 }
 
+// allow_no_o: o may be NULL on the bf16 path (a state-only run; the float32 path always writes o)
 kda_status check_fwd(const kda_fwd_desc* d, const void* q, const void* k, const void* v, const float* g,
                      const float* beta, const float* S0, const void* o, const float* S_T,
-                     int allowed_flags = KDA_FWD_PRECISE) {
-    const kda_status st = check_common(d, q, k, v, g, beta, S0, o, S_T, true, allowed_flags);
+                     int allowed_flags = KDA_FWD_PRECISE, bool allow_no_o = false) {
+    const bool need_o = !(allow_no_o && d && d->io_dtype == KDA_BF16);
+    const kda_status st = check_common(d, q, k, v, g, beta, S0, o, S_T, need_o, allowed_flags);
     if (st != KDA_OK) return st;
     if (d->io_dtype == KDA_BF16) {
         if (d->Dk != 128 || d->Dv != 128) return KDA_ERR_UNSUPPORTED;
@@ -112,8 +114,9 @@ size_t kda_fwd_workspace_size(const kda_fwd_desc* desc) {
 kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
                    const float* beta, const float* S0, void* o, float* S_T, void* ws, size_t ws_bytes,
                    hipStream_t stream) {
-    const kda_status st = check_fwd(desc, q, k, v, g, beta, S0, o, S_T, KDA_FWD_PRECISE | KDA_VALIDATE);
+    const kda_status st = check_fwd(desc, q, k, v, g, beta, S0, o, S_T, KDA_FWD_PRECISE | KDA_VALIDATE, true);
     if (st != KDA_OK) return st;
+    if (desc->T > 0 && !o && !S_T) return KDA_ERR_INVALID_ARG;  // nothing to compute
     if ((desc->flags & KDA_VALIDATE) && desc->T > 0) {
         if (!ws || ws_bytes < kValidateWs || !aligned(ws, 256)) return KDA_ERR_WORKSPACE;
         kda::Params p{};
@@ -133,11 +136,12 @@ kda_status kda_fwd(const kda_fwd_desc* desc, const void* q, const void* k, const
 kda_status kda_fwd_ckpt(const kda_fwd_desc* desc, const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const float* S0, void* o, float* S_T, float* S_ckpt, int every,
                         hipStream_t stream) {
-    const kda_status st = check_fwd(desc, q, k, v, g, beta, S0, o, S_T);
+    const kda_status st = check_fwd(desc, q, k, v, g, beta, S0, o, S_T, KDA_FWD_PRECISE, true);
     if (st != KDA_OK) return st;
     if (every <= 0 || every % chunk_of(desc) != 0) return KDA_ERR_INVALID_ARG;
     const int n_ckpt = desc->T / every;
     if (n_ckpt > 0 && !S_ckpt) return KDA_ERR_INVALID_ARG;
+    if (desc->T > 0 && !o && !S_T && n_ckpt == 0) return KDA_ERR_INVALID_ARG;  // nothing to compute
     if (!aligned(S_ckpt, 8)) return KDA_ERR_INVALID_ARG;
     if (S_ckpt && ((const void*)S_ckpt == o || S_ckpt == S_T || S_ckpt == S0)) return KDA_ERR_INVALID_ARG;
     return run_fwd(desc, q, k, v, g, beta, S0, o, S_T, n_ckpt > 0 ? S_ckpt : nullptr, every, stream);

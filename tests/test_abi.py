@@ -127,6 +127,15 @@ def test_validate_flag_only_on_kda_fwd():
                            0, None) == _lib.KDA_ERR_INVALID_ARG
 
 
+def test_state_only_forward_needs_a_state_output():
+    # o = NULL asks for the state alone (bf16 path): with no S_T (and no checkpoint) nothing is computed
+    assert call(desc(), o=0, S_T=0) == _lib.KDA_ERR_INVALID_ARG
+    # the float32 path always writes o
+    assert call(desc(io_dtype=_lib.KDA_F32, o_dtype=_lib.KDA_F32, Dk=64, Dv=64), o=0,
+                S_T=FAKE + 0x300000) == _lib.KDA_ERR_INVALID_ARG
+    assert call_ckpt(desc(T=64), 128, o=0, S_ckpt=0) == _lib.KDA_ERR_INVALID_ARG
+
+
 def test_output_aliasing_input_rejected():
     assert call(desc(), o=FAKE) == _lib.KDA_ERR_INVALID_ARG
 
