@@ -5,13 +5,18 @@
 // section 13.3.2 states the decomposition that makes the merge possible: the state after segment i
 // is M_i S_start(i) + S_hat_i, with M_i the segment's accumulated transition and S_hat_i its local
 // state estimate (the segment run from a zero state).  Here, for nseg segments of Ls tokens:
-//   1. S_hat_i: the chunkwise kernel over every segment at once from S = 0 (no output);
-//      M_i:     the same kernel with v = 0 and S = I (no output): the gated delta rule is linear in
-//               (S, v), so with v = 0 it maps the initial state through the segment, and from I it
-//               yields the transition matrix itself;
-//   2. the scan S_start(0) = S0, S_start(i+1) = M_i S_start(i) + S_hat_i, in float32;
+//   1. S_hat_i: the chunkwise kernel from S = 0 (no output), for segments 1..nseg-2; segment 0 runs
+//               from the call's S0 instead, which gives S_start(1) itself;
+//      M_i:     the same kernel with v = 0 and S = I (no output), for segments 1..nseg-2: the gated
+//               delta rule is linear in (S, v), so with v = 0 it maps the initial state through the
+//               segment, and from I it yields the transition matrix itself;
+//      (the last segment needs neither, and segment 0 no transition);
+//   2. the scan S_start(0) = S0, S_start(1) = the first pass's segment 0,
+//      S_start(i+1) = M_i S_start(i) + S_hat_i, in float32;
 //   3. the chunkwise kernel over every segment at once from S_start(i), writing o and the segment's
 //      final state; the last segment's is S_T.
+// Both first-pass launches run only the segments they need (the kernel's batch-row subset) and use
+// its state-only instantiation.
 // A sequence too short for B*H*nseg to matter, or T not a multiple of nseg*32, is handled by running
 // the whole multiple of nseg*32 this way and the remaining tail with the plain kernel from the last
 // segment's state.  This is three passes of work in exchange for nseg times more workgroups: worth it
@@ -47,11 +52,17 @@ __global__ void __launch_bounds__(NTHR) kda_cp_scan_kernel(const float* __restri
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int row = rg * 8 + i;
-        acc[i] = S0 ? S0[(size_t)bh * D * D + (size_t)row * D + col] : 0.f;
-        Sc[row][c] = acc[i];
-        Sst[at(0) + (size_t)row * D + col] = acc[i];
+        Sst[at(0) + (size_t)row * D + col] = S0 ? S0[(size_t)bh * D * D + (size_t)row * D + col] : 0.f;
     }
-    for (int s = 0; s + 1 < nseg; ++s) {
+    // S_start(1): segment 0's final state, which the first pass computed from S0 (nseg >= 2 here)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = rg * 8 + i;
+        acc[i] = Shat[at(0) + (size_t)row * D + col];
+        Sc[row][c] = acc[i];
+        Sst[at(1) + (size_t)row * D + col] = acc[i];
+    }
+    for (int s = 1; s + 1 < nseg; ++s) {
         __syncthreads();  // Sc holds S_start(s); the previous step is done with Ms
         const float4* src = reinterpret_cast<const float4*>(M + at(s));
         for (int e = tid; e < D * D / 4; e += NTHR) {
@@ -78,6 +89,17 @@ __global__ void __launch_bounds__(NTHR) kda_cp_scan_kernel(const float* __restri
 }
 
 size_t seg_floats(int Bg, int nseg, int H) { return (size_t)Bg * nseg * H * D * D; }
+
+// Initial states of the first pass: S0 (or 0) for segment 0 of each of Bg sequences, 0 for the others.
+// Sst: [Bg][nseg][H][D][D]; S0: [Bg][H][D][D] or NULL.
+__global__ void kda_cp_seed_kernel(const float* __restrict__ S0, float* __restrict__ Sst, int Bg, int nseg, int H) {
+    const size_t mat = (size_t)D * D, n = (size_t)Bg * nseg * H * mat;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+        const size_t m = e / mat, w = e - m * mat;  // m = (b * nseg + s) * H + h
+        const int h = (int)(m % H), s = (int)((m / H) % nseg), b = (int)(m / ((size_t)H * nseg));
+        Sst[e] = (s == 0 && S0) ? S0[((size_t)b * H + h) * mat + w] : 0.f;
+    }
+}
 
 // n D x D identity matrices, back to back.
 __global__ void kda_cp_identity_kernel(float* __restrict__ S, size_t n) {
@@ -140,17 +162,25 @@ hipError_t launch_fwd_cp(const Params& u, int nseg_req, float* ws, hipStream_t s
     float* Sst = ws + 2 * n;
     hipError_t e = hipSuccess;
     for (int b0 = 0; b0 < u.B && e == hipSuccess; b0 += Bg) {
-        // 1. local states and transitions of all segments
-        Params p = cp::seg_params(u, b0, Bg, nseg, Ls);
-        p.S0 = nullptr; p.o = nullptr; p.S_T = Shat;
-        if ((e = launch_fwd_bf16(p, stream)) != hipSuccess) break;
-        const size_t nm = (size_t)Bg * nseg * u.H;  // identity initial states, in the buffer step 2 fills later
-        hipLaunchKernelGGL(cp::kda_cp_identity_kernel, dim3(1024), dim3(256), 0, stream, Sst, nm);
-        if ((e = hipGetLastError()) != hipSuccess) break;
-        p.v = nullptr; p.S0 = Sst; p.S_T = M;
-        if ((e = launch_fwd_bf16(p, stream)) != hipSuccess) break;
-        // 2. initial state of every segment
         const float* S0 = u.S0 ? u.S0 + (size_t)b0 * u.H * cp::D * cp::D : nullptr;
+        // 1. segments 0..nseg-2 from their first-pass states (S0 for segment 0, else 0, seeded into the
+        //    buffer step 2 fills later): segment 0's final state and the others' local states
+        hipLaunchKernelGGL(cp::kda_cp_seed_kernel, dim3(1024), dim3(256), 0, stream, S0, Sst, Bg, nseg, u.H);
+        if ((e = hipGetLastError()) != hipSuccess) break;
+        Params p = cp::seg_params(u, b0, Bg, nseg, Ls);
+        p.o = nullptr; p.S0 = Sst; p.S_T = Shat;
+        p.B = Bg * (nseg - 1); p.seg_lo = 0; p.seg_cnt = nseg - 1; p.seg_n = nseg;
+        if ((e = launch_fwd_bf16(p, stream)) != hipSuccess) break;
+        //    the transitions of segments 1..nseg-2 (v = 0 from I, in place in M)
+        if (nseg > 2) {
+            hipLaunchKernelGGL(cp::kda_cp_identity_kernel, dim3(1024), dim3(256), 0, stream, M,
+                               (size_t)Bg * nseg * u.H);
+            if ((e = hipGetLastError()) != hipSuccess) break;
+            p.v = nullptr; p.S0 = M; p.S_T = M;
+            p.B = Bg * (nseg - 2); p.seg_lo = 1; p.seg_cnt = nseg - 2;
+            if ((e = launch_fwd_bf16(p, stream)) != hipSuccess) break;
+        }
+        // 2. initial state of every segment
         hipLaunchKernelGGL(cp::kda_cp_scan_kernel, dim3((unsigned)(Bg * u.H * (cp::D / cp::SCOLS))), dim3(cp::NTHR), 0,
                            stream, Shat, M, S0, Sst, nseg, u.H);
         if ((e = hipGetLastError()) != hipSuccess) break;

@@ -866,7 +866,12 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
         bh = blockIdx.x >> 1;
         half = blockIdx.x & 1;
     }
-    const int b = bh / p.H, h = bh - b * p.H;
+    int b = bh / p.H;
+    const int h = bh - b * p.H;
+    if (p.seg_cnt > 0) {  // a subset of the batch rows (see Params)
+        b = (b / p.seg_cnt) * p.seg_n + p.seg_lo + b % p.seg_cnt;
+        bh = b * p.H + h;
+    }
     const size_t row0 = (size_t)b * p.tstride * p.H + h;  // row of token 0: (b*tstride + t)*H + h = row0 + t*H
     const int nchunk = (p.T + C - 1) / C;
     if (nchunk == 0) return;  // (the host runs the state copy instead; every wave leaves here alike)

@@ -24,6 +24,10 @@ struct Params {
     float* S_ckpt;     // may be null: [B, H, n_ckpt, Dk, Dv] states at every ckpt_chunks-th chunk boundary
     int ckpt_chunks;   // chunks between checkpoints (>= 1 when S_ckpt is set)
     int n_ckpt;        // checkpoints per sequence: full multiples of ckpt_chunks chunks within T
+    // bf16 path, optional (seg_cnt = 0: off): run batch rows (b / seg_cnt) * seg_n + seg_lo + b % seg_cnt
+    // for b < B, i.e. seg_cnt of every seg_n rows, starting at row seg_lo (the context-parallel passes
+    // that need only some segments of each sequence); every tensor is indexed by that row
+    int seg_lo, seg_cnt, seg_n;
 };
 
 // Backward problem (all float32 gradients; NULL outputs are skipped).
