@@ -10,11 +10,19 @@
 // of 8 x 4 products v_mfma_f32_16x16x32_bf16.  The operand tiles move 32 columns of k at a time,
 // straight from global memory into a four-deep ring of LDS stages (global_load_lds_dwordx4: each
 // lane's 16 bytes land at the stage base plus 16 * lane, so the lanes are given the global chunks
-// that the XOR-swizzled layout puts there), issued three steps ahead; a step waits for its own
-// loads with an explicit vmcnt and then meets the other waves at one barrier.  Tiles are numbered
-// so that each XCD (the hardware deals workgroups to the eight XCDs in turn) gets one contiguous
-// range of them, ordered in groups of eight tile rows, so that the workgroups running together on
-// one XCD share A and Bt panels in its L2.
+// that the XOR-swizzled layout puts there), issued three steps ahead.  Tiles are numbered so that
+// each XCD (the hardware deals workgroups to the eight XCDs in turn) gets one contiguous range of
+// them, ordered in groups of four tile rows, so that the workgroups running together on one XCD
+// share A and Bt panels in its L2.
+//
+// Schedule.  Waves w and w + 4 share a SIMD.  They run half a step apart ("ping-pong"): in every
+// phase between two barriers one of them reads its operand fragments of a stage from LDS while the
+// other issues its 32 products of the stage before, so the matrix core of each SIMD is fed by one
+// wave while the other waits on LDS.  Waves 0-3 read stage k in phase 2k and multiply it in phase
+// 2k + 1; waves 4-7 read it in phase 2k + 1 and multiply it in phase 2k + 2.  The wave that reads a
+// stage first issues its part of the loads of stage k + 3, into the slot of stage k - 1, which every
+// wave finished reading before phase 2k; each wave waits for its own loads of stage k + 1 (explicit
+// vmcnt) before the barrier that closes phase 2k + 1.  The sums are those of a plain k-ordered loop.
 //
 // Epilogue.  Each wave rewrites its block row-major through LDS and stores whole rows (16 lanes per
 // 256-byte row segment).  The columns of C may be split into up to six segments, each written to
@@ -68,7 +76,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_nt_kernel(const uint16_t* __rest
     const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN, total = tm * tn;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, q = total >> 3, rem = total & 7;
     const int pid = xcd * q + min(xcd, rem) + slot;
-    constexpr int GM = 8;
+    constexpr int GM = 4;
     const int in_group = GM * tn, first_m = (pid / in_group) * GM, gsize = min(tm - first_m, GM);
     const int im = first_m + (pid % in_group) % gsize, jn = (pid % in_group) / gsize;
     const int m0 = im * BM, n0 = jn * BN;
@@ -96,41 +104,55 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_nt_kernel(const uint16_t* __rest
     };
 
     const int wm = wave >> 2, wn = wave & 3;
+    const bool late = wave >= 4;  // waves 4-7: half a step behind
     f32x4 acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nk = K / BK;
-    for (int s = 0; s < NST - 1 && s < nk; ++s) issue(s, s);
-    for (int kt = 0; kt < nk; ++kt) {
-        // tile kt in LDS: this wave's later loads (at most two tiles, four instructions each) may stay
-        // in flight; the barrier then covers every wave's loads of tile kt, and every wave is done with
-        // stage (kt - 1) % 4, which tile kt + 3 refills
-        const int later = min(2, nk - 1 - kt);
-        if (later == 2) wait_vm<8>(); else if (later == 1) wait_vm<4>(); else wait_vm<0>();
-        exec_barrier();
-        if (kt + NST - 1 < nk) issue(kt + NST - 1, (kt + NST - 1) % NST);
-        const uint16_t* sa = sm.a[kt % NST];
-        const uint16_t* sb = sm.b[kt % NST];
-        u32x4 af[8], bf[4];
+    u32x4 af[8], bf[4];
+    auto frags = [&](int st) {
+        const uint16_t* sa = sm.a[st];
+        const uint16_t* sb = sm.b[st];
 #pragma unroll
         for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const u32x4*>(&sa[swz(WM * wm + 16 * i + l16, g4)]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const u32x4*>(&sb[swz(WN * wn + 16 * j + l16, g4)]);
-        // Bt as the first operand: lane (l16, g4) gets row m = l16 of the block, columns 4*g4 .. 4*g4+3
+        wait_lgkm0();
+    };
+    // Bt as the first operand: lane (l16, g4) gets row m = l16 of the block, columns 4*g4 .. 4*g4+3
+    auto mma = [&]() {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(bf[j], af[i], acc[i][j]);
+    };
+    // this wave's loads of a stage are complete once at most `later` later stages (four loads each)
+    // are in flight
+    auto wait_stage = [&](int later) {
+        if (later >= 2) wait_vm<8>(); else if (later == 1) wait_vm<4>(); else wait_vm<0>();
+    };
+
+    constexpr int L = NST - 1;  // stages issued ahead
+    const int nk = K / BK;
+    for (int s = 0; s < L && s < nk; ++s) issue(s, s);
+    wait_stage(min(L - 1, nk - 1));
+    exec_barrier();
+    if (late) exec_barrier();  // waves 4-7 sit out phase 0 (and waves 0-3 the last phase, 2nk)
+    for (int k = 0; k < nk; ++k) {
+        if (k + L < nk) issue(k + L, (k + L) % NST);
+        frags(k % NST);
+        if (late && k + 1 < nk) wait_stage(min(L - 1, nk - 2 - k));
+        exec_barrier();
+        mma();
+        if (!late && k + 1 < nk) wait_stage(min(L - 1, nk - 2 - k));
+        if (!late || k + 1 < nk) exec_barrier();
     }
 
     // epilogue through LDS: each wave rewrites its 128 x 64 block row-major in its own 16 KB of the
     // ring (64 rows at a time, 16-byte blocks XOR-swizzled by row), then stores whole rows: lane
-    // (sr, l16) stores columns 4*l16 .. 4*l16+3 of row 4*r4 + sr
-    wait_lgkm0();
-    exec_barrier();  // every wave is done with the operand tiles
+    // (sr, l16) stores columns 4*l16 .. 4*l16+3 of row 4*r4 + sr.  Every operand read and load
+    // finished before the last barrier, so no wave waits for the others here.
     float* stage = reinterpret_cast<float*>(&sm) + wave * (64 * 64);
     const int sr = lane >> 4, sc = 4 * (lane & 15);
     const int nb = n0 + WN * wn + sc;  // this lane's first column
