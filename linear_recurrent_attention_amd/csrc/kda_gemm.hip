@@ -4,7 +4,7 @@
 //
 // Both operands are read along k, so their tiles go to LDS row by row and every matrix-core operand
 // is one 16-byte LDS read.  The layer's weights are stored [in][out]; they are transposed into this
-// form on each call (transpose_kernel), which costs a few microseconds against the products.
+// form on each call (transpose_batch_kernel, all of them in one launch).
 //
 // Mapping.  A workgroup computes a 256 x 256 tile of C with 8 waves (2 x 4), each a 128 x 64 block
 // of 8 x 4 products v_mfma_f32_16x16x32_bf16.  The operand tiles move 32 columns of k at a time,
@@ -205,20 +205,27 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_nt_kernel(const uint16_t* __rest
     }
 }
 
-// dst[n * ldd + k] = src[k * lds + n] for k < K, n < N (bf16), through a 64 x 64 tile.  VEC: rows of
-// src and dst hold whole aligned 16-byte chunks (lds, ldd multiples of 8, 16-byte aligned bases)
-template <bool VEC>
-__global__ void __launch_bounds__(256) transpose_kernel(const uint16_t* __restrict__ src, int lds, int K, int N,
-                                                        uint16_t* __restrict__ dst, int ldd) {
+// Batched transpose: job j writes dst[n * ldd + k] = src[k * lds + n] for k < K, n < N (bf16), one
+// 64 x 64 tile per workgroup, every job of a call in one launch (the layer's weights are a handful
+// of small matrices, so separate launches would cost more than their bytes).  A job's rows are
+// moved as 16-byte chunks when both matrices allow it (vec).
+__global__ void __launch_bounds__(256) transpose_batch_kernel(TransposeBatch batch) {
     __shared__ uint16_t t[64][72];  // [k][n], rows padded by 16 bytes
-    const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    TransposeJob J = batch.job[0];
+#pragma unroll
+    for (int i = 1; i < TransposeBatch::kMax; ++i)
+        if (i < batch.njobs && (int)blockIdx.x >= batch.job[i].first) J = batch.job[i];
+    const int local = (int)blockIdx.x - J.first;
+    const int k0 = (local / J.tiles_n) * 64, n0 = (local % J.tiles_n) * 64;
+    const int K = J.K, N = J.N;
     for (int e = threadIdx.x; e < 64 * 8; e += 256) {
         const int r = e >> 3, c8 = 8 * (e & 7);  // k row, first n of the chunk
         const int k = k0 + r, n = n0 + c8;
-        if (VEC && k < K && n + 8 <= N) {
-            *reinterpret_cast<u32x4*>(&t[r][c8]) = *reinterpret_cast<const u32x4*>(src + (size_t)k * lds + n);
+        if (J.vec && k < K && n + 8 <= N) {
+            *reinterpret_cast<u32x4*>(&t[r][c8]) = *reinterpret_cast<const u32x4*>(J.src + (size_t)k * J.lds + n);
         } else {
-            for (int x = 0; x < 8; ++x) t[r][c8 + x] = (k < K && n + x < N) ? src[(size_t)k * lds + n + x] : (uint16_t)0;
+            for (int x = 0; x < 8; ++x)
+                t[r][c8 + x] = (k < K && n + x < N) ? J.src[(size_t)k * J.lds + n + x] : (uint16_t)0;
         }
     }
     __syncthreads();
@@ -228,13 +235,13 @@ __global__ void __launch_bounds__(256) transpose_kernel(const uint16_t* __restri
         if (n >= N) continue;
         uint16_t v[8];
         for (int x = 0; x < 8; ++x) v[x] = t[c8 + x][r];
-        if (VEC && k + 8 <= K) {
+        if (J.vec && k + 8 <= K) {
             u32x4 w;
             for (int x = 0; x < 4; ++x) w[x] = (uint32_t)v[2 * x] | ((uint32_t)v[2 * x + 1] << 16);
-            *reinterpret_cast<u32x4*>(dst + (size_t)n * ldd + k) = w;
+            *reinterpret_cast<u32x4*>(J.dst + (size_t)n * J.ldd + k) = w;
         } else {
             for (int x = 0; x < 8; ++x)
-                if (k + x < K) dst[(size_t)n * ldd + k + x] = v[x];
+                if (k + x < K) J.dst[(size_t)n * J.ldd + k + x] = v[x];
         }
     }
 }
@@ -282,15 +289,20 @@ hipError_t launch_gemm_nt(const uint16_t* A, int lda, const uint16_t* Bt, int ld
     return hipGetLastError();
 }
 
-hipError_t launch_transpose_bf16(const uint16_t* src, int lds, int K, int N, uint16_t* dst, int ldd, hipStream_t stream) {
-    if (K <= 0 || N <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((K + 63) / 64));
-    const bool vec = lds % 8 == 0 && ldd % 8 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
-                     (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
-    if (vec)
-        hipLaunchKernelGGL(gemm::transpose_kernel<true>, grid, dim3(256), 0, stream, src, lds, K, N, dst, ldd);
-    else
-        hipLaunchKernelGGL(gemm::transpose_kernel<false>, grid, dim3(256), 0, stream, src, lds, K, N, dst, ldd);
+hipError_t launch_transpose_batch(TransposeBatch& b, hipStream_t stream) {
+    if (b.njobs < 1 || b.njobs > TransposeBatch::kMax) return hipErrorInvalidValue;
+    long total = 0;
+    for (int i = 0; i < b.njobs; ++i) {
+        TransposeJob& J = b.job[i];
+        if (J.K < 1 || J.N < 1 || !J.src || !J.dst) return hipErrorInvalidValue;
+        J.tiles_n = (J.N + 63) / 64;
+        J.first = (int)total;
+        J.vec = J.lds % 8 == 0 && J.ldd % 8 == 0 && (reinterpret_cast<uintptr_t>(J.src) & 15) == 0 &&
+                (reinterpret_cast<uintptr_t>(J.dst) & 15) == 0;
+        total += (long)J.tiles_n * ((J.K + 63) / 64);
+        if (total > (1L << 30)) return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL(gemm::transpose_batch_kernel, dim3((unsigned)total), dim3(256), 0, stream, b);
     return hipGetLastError();
 }
 

@@ -83,8 +83,20 @@ struct GemmOut {
 };
 hipError_t launch_gemm_nt(const uint16_t* A, int lda, const uint16_t* Bt, int ldb, const GemmOut& out, bool out_f32,
                           int M, int N, int K, hipStream_t stream);
-// dst[n * ldd + k] = src[k * lds + n] for k < K, n < N (bf16)
-hipError_t launch_transpose_bf16(const uint16_t* src, int lds, int K, int N, uint16_t* dst, int ldd, hipStream_t stream);
+// Transposes in one launch: job i writes dst[n * ldd + k] = src[k * lds + n] for k < K, n < N (bf16).
+// The caller fills src, dst, lds, ldd, K, N; the launch fills the rest.
+struct TransposeJob {
+    const uint16_t* src;
+    uint16_t* dst;
+    int lds, ldd, K, N;
+    int tiles_n, first, vec;
+};
+struct TransposeBatch {
+    static constexpr int kMax = 12;
+    TransposeJob job[kMax];
+    int njobs;
+};
+hipError_t launch_transpose_batch(TransposeBatch& b, hipStream_t stream);
 // float32 [M][R] (row stride lds) -> bf16 [M][2R]: bf16(x) in columns [0, R), bf16(x - that) in [R, 2R)
 hipError_t launch_split_rows(const float* src, int lds, int M, int R, uint16_t* dst, hipStream_t stream);
 // Fused layer decode step (one cooperative launch); see kda_layer_decode.hip.

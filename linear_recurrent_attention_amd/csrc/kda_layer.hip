@@ -254,20 +254,24 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
     const int M = d->B * d->T, HD = d->H * D, dm = d->d_model, R = d->rank;
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     auto wb = [](const void* p) { return static_cast<const uint16_t*>(p); };
-    bool ok = true;
     // weights in the products' [out][in] form: [Wq | Wk | Wv | Wg | Wdown | Wbeta]^T, [Wup^T | Wup^T]
     // (the up-projection runs over the hi and lo halves of its input), Wo^T
     const int ncat = 4 * HD + R + d->H;
     const int noff[6] = {0, HD, 2 * HD, 3 * HD, 4 * HD, 4 * HD + R};
     const void* wsrc[6] = {w->Wq, w->Wk, w->Wv, w->Wg, w->Wdown, w->Wbeta};
     const int wn[6] = {HD, HD, HD, HD, R, d->H};
-    for (int i = 0; i < 6; ++i)
-        ok &= kda::launch_transpose_bf16(wb(wsrc[i]), wn[i], dm, wn[i], W.wcat + (size_t)noff[i] * dm, dm, stream) ==
-              hipSuccess;
-    ok &= kda::launch_transpose_bf16(wb(w->Wup), HD, R, HD, W.wup2, 2 * R, stream) == hipSuccess;
-    ok &= kda::launch_transpose_bf16(wb(w->Wup), HD, R, HD, W.wup2 + R, 2 * R, stream) == hipSuccess;
-    ok &= kda::launch_transpose_bf16(wb(w->Wo), dm, HD, dm, W.wo, HD, stream) == hipSuccess;
-    if (!ok) return KDA_ERR_HIP;
+    {
+        kda::TransposeBatch tb{};
+        auto job = [&](const void* src, int lds, int K, int N, uint16_t* dst, int ldd) {
+            kda::TransposeJob& J = tb.job[tb.njobs++];
+            J.src = wb(src); J.lds = lds; J.K = K; J.N = N; J.dst = dst; J.ldd = ldd;
+        };
+        for (int i = 0; i < 6; ++i) job(wsrc[i], wn[i], dm, wn[i], W.wcat + (size_t)noff[i] * dm, dm);
+        job(w->Wup, HD, R, HD, W.wup2, 2 * R);
+        job(w->Wup, HD, R, HD, W.wup2 + R, 2 * R);
+        job(w->Wo, dm, HD, dm, W.wo, HD);
+        if (kda::launch_transpose_batch(tb, stream) != hipSuccess) return KDA_ERR_HIP;
+    }
     {
         kda::GemmOut go{};
         float* dst[6] = {W.pq, W.pk, W.pv, W.pg, W.pdown, W.pbeta};
