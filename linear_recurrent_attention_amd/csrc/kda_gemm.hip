@@ -7,22 +7,23 @@
 // form on each call (transpose_batch_kernel, all of them in one launch).
 //
 // Mapping.  A workgroup computes a 256 x 256 tile of C with 8 waves (2 x 4), each a 128 x 64 block
-// of 8 x 4 products v_mfma_f32_16x16x32_bf16.  The operand tiles move 32 columns of k at a time,
-// straight from global memory into a four-deep ring of LDS stages (global_load_lds_dwordx4: each
-// lane's 16 bytes land at the stage base plus 16 * lane, so the lanes are given the global chunks
-// that the XOR-swizzled layout puts there), issued three steps ahead.  Tiles are numbered so that
+// of 8 x 4 products v_mfma_f32_16x16x32_bf16.  The operand tiles move 64 columns of k at a time
+// (128-byte rows, so that every request to L2 is a whole cache line: with 64-byte rows the loads
+// were bound by the requests in flight), straight from global memory into two LDS stages
+// (global_load_lds_dwordx4: each lane's 16 bytes land at the stage base plus 16 * lane, so the lanes
+// are given the global chunks that the XOR-swizzled layout puts there).  Tiles are numbered so that
 // each XCD (the hardware deals workgroups to the eight XCDs in turn) gets one contiguous range of
 // them, ordered in groups of four tile rows, so that the workgroups running together on one XCD
 // share A and Bt panels in its L2.
 //
 // Schedule.  Waves w and w + 4 share a SIMD.  They run half a step apart ("ping-pong"): in every
-// phase between two barriers one of them reads its operand fragments of a stage from LDS while the
-// other issues its 32 products of the stage before, so the matrix core of each SIMD is fed by one
-// wave while the other waits on LDS.  Waves 0-3 read stage k in phase 2k and multiply it in phase
-// 2k + 1; waves 4-7 read it in phase 2k + 1 and multiply it in phase 2k + 2.  The wave that reads a
-// stage first issues its part of the loads of stage k + 3, into the slot of stage k - 1, which every
-// wave finished reading before phase 2k; each wave waits for its own loads of stage k + 1 (explicit
-// vmcnt) before the barrier that closes phase 2k + 1.  The sums are those of a plain k-ordered loop.
+// phase between two barriers one of them reads its operand fragments of a k step (32 columns) from
+// LDS while the other issues its 32 products of the step before, so the matrix core of each SIMD is
+// fed by one wave while the other waits on LDS.  Waves 0-3 read step u in phase 2u and multiply it
+// in phase 2u + 1; waves 4-7 read it in phase 2u + 1 and multiply it in phase 2u + 2.  In the first
+// step of stage s a wave issues its part of the loads of stage s + 1, into the other slot, which
+// every wave finished reading before; each wave waits for its own loads (vmcnt 0) before the barrier
+// that closes the last phase of stage s.  The sums are those of a plain k-ordered loop.
 //
 // Epilogue.  Each wave rewrites its block row-major through LDS and stores whole rows (16 lanes per
 // 256-byte row segment), as nontemporal stores: every workgroup of a round stores at about the same
@@ -35,21 +36,22 @@
 namespace kda {
 namespace gemm {
 
-constexpr int BM = 256, BN = 256, BK = 32, NST = 4;
+constexpr int BM = 256, BN = 256, BK = 32;  // BK: the k columns of one matrix-core step
+constexpr int BK2 = 64, NST = 2;            // k columns per LDS stage, stages in the ring
 constexpr int NW = 8, NTHR = 64 * NW;
 constexpr int WM = 128, WN = 64;  // per wave
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void g_void;
 
-// LDS tiles [rows][32] bf16 (64-byte rows): 16-byte chunk c of row r is stored at chunk
-// c ^ ((r >> 2) & 3), so that the 16 rows of a matrix-core operand read (one chunk each) fall in 16
+// LDS tiles [rows][64] bf16 (128-byte rows): 16-byte chunk c of row r is stored at chunk
+// c ^ ((r >> 1) & 7), so that the 16 rows of a matrix-core operand read (one chunk each) fall in 16
 // distinct bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + 8 * (chunk ^ ((row >> 2) & 3)); }
+__device__ __forceinline__ int swz64(int row, int chunk) { return row * BK2 + 8 * (chunk ^ ((row >> 1) & 7)); }
 
 struct alignas(16) Smem {
-    uint16_t a[NST][BM * BK];
-    uint16_t b[NST][BN * BK];
+    uint16_t a[NST][BM * BK2];
+    uint16_t b[NST][BN * BK2];
 };
 static_assert(sizeof(Smem) >= NW * 64 * 64 * sizeof(float), "the epilogue's staging fits in the operand ring");
 
@@ -64,96 +66,92 @@ __device__ __forceinline__ void exec_barrier() { asm volatile("s_barrier" ::: "m
 
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __builtin_amdgcn_exp2f(-x * kLog2e)); }
 
-template <bool OUT_F32, int EPI>
-__global__ void __launch_bounds__(NTHR, 1) gemm_nt_kernel(const uint16_t* __restrict__ A, int lda,
-                                                          const uint16_t* __restrict__ Bt, int ldb, GemmOut out,
-                                                          int M, int N, int K) {
-    __shared__ Smem sm;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// One tile (or one piece of a split tile) of C: rows [pm0, pm0 + 32 NI) of the tile whose first row
+// is the A stage's row 0 at pm0, columns [n0, n0 + 256).  Each wave multiplies NI 16-row blocks by
+// its four 16-column blocks: NI = 8 for a whole 256-row tile, 4 or 2 for a half or quarter.
+template <bool OUT_F32, int EPI, int NI>
+__device__ __forceinline__ void gemm_tile(Smem& sm, const uint16_t* __restrict__ A, int lda,
+                                          const uint16_t* __restrict__ Bt, int ldb, const GemmOut& out, int M, int N,
+                                          int K, int pm0, int n0, int wave, int lane) {
     const int l16 = lane & 15, g4 = lane >> 4;
+    constexpr int WR = 16 * NI;  // rows per wave
 
-    // tile of this workgroup: XCD-contiguous ranges, grouped by eight tile rows
-    const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN, total = tm * tn;
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, q = total >> 3, rem = total & 7;
-    const int pid = xcd * q + min(xcd, rem) + slot;
-    constexpr int GM = 4;
-    const int in_group = GM * tn, first_m = (pid / in_group) * GM, gsize = min(tm - first_m, GM);
-    const int im = first_m + (pid % in_group) % gsize, jn = (pid % in_group) / gsize;
-    const int m0 = im * BM, n0 = jn * BN;
-
-    // loads: wave w moves rows [16w, 16w + 16) and [16w + 128, 16w + 144) of both tiles, one 1 KB
-    // instruction each; lane l takes row base + l/4 at physical chunk l%4, i.e. logical chunk
-    // (l%4) ^ ((row >> 2) & 3).  Rows past M (N) read row M-1 (N-1); their results are never stored.
-    const uint16_t* ag[2];
-    const uint16_t* bg[2];
+    // loads: wave w moves rows [32w, 32w + 32) of both stages, four 1 KB instructions (8 rows of
+    // 128 bytes each); lane l takes row base + l/8 at physical chunk l%8, i.e. logical chunk
+    // (l%8) ^ ((row >> 1) & 7).  Rows past M (N) read row M-1 (N-1); their results are never stored.
+    // A last stage of 32 k columns (K = 32 mod 64) reads its first half again in place of the second.
+    const int lr = 32 * wave + (lane >> 3);
+    const uint16_t* ag[4];
+    const uint16_t* bg[4];
+    int lch[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int row = 16 * wave + 128 * h + (lane >> 2);
-        const int lc = (lane & 3) ^ ((row >> 2) & 3);
-        ag[h] = A + (size_t)min(m0 + row, M - 1) * lda + 8 * lc;
-        bg[h] = Bt + (size_t)min(n0 + row, N - 1) * ldb + 8 * lc;
+    for (int h = 0; h < 4; ++h) {
+        const int row = lr + 8 * h;
+        lch[h] = (lane & 7) ^ ((row >> 1) & 7);
+        ag[h] = A + (size_t)min(pm0 + row, M - 1) * lda;
+        bg[h] = Bt + (size_t)min(n0 + row, N - 1) * ldb;
     }
+    const int nsub = K / BK, nk = (nsub + 1) / 2;  // k32 sub-steps, 64-column stages
     auto issue = [&](int kt, int st) {
-        const int k0 = kt * BK;
+        const int k0 = kt * BK2;
+        const bool half = 2 * kt + 1 >= nsub;  // only the first 32 columns exist
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = 16 * wave + 128 * h;
-            __builtin_amdgcn_global_load_lds((g_void*)(ag[h] + k0), (lds_void*)&sm.a[st][row * BK], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((g_void*)(bg[h] + k0), (lds_void*)&sm.b[st][row * BK], 16, 0, 0);
+        for (int h = 0; h < 4; ++h) {
+            const int row = 32 * wave + 8 * h;
+            const int c = half ? (lch[h] & 3) : lch[h];
+            __builtin_amdgcn_global_load_lds((g_void*)(ag[h] + k0 + 8 * c), (lds_void*)&sm.a[st][row * BK2], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((g_void*)(bg[h] + k0 + 8 * c), (lds_void*)&sm.b[st][row * BK2], 16, 0, 0);
         }
     };
 
     const int wm = wave >> 2, wn = wave & 3;
     const bool late = wave >= 4;  // waves 4-7: half a step behind
-    f32x4 acc[8][4];
+    f32x4 acc[NI][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 af[8], bf[4];
-    auto frags = [&](int st) {
+    u32x4 af[NI], bf[4];
+    auto frags = [&](int st, int sub) {
         const uint16_t* sa = sm.a[st];
         const uint16_t* sb = sm.b[st];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const u32x4*>(&sa[swz(WM * wm + 16 * i + l16, g4)]);
+        for (int i = 0; i < NI; ++i) af[i] = *reinterpret_cast<const u32x4*>(&sa[swz64(WR * wm + 16 * i + l16, g4 + 4 * sub)]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const u32x4*>(&sb[swz(WN * wn + 16 * j + l16, g4)]);
+        for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const u32x4*>(&sb[swz64(WN * wn + 16 * j + l16, g4 + 4 * sub)]);
         wait_lgkm0();
     };
     // Bt as the first operand: lane (l16, g4) gets row m = l16 of the block, columns 4*g4 .. 4*g4+3
     auto mma = [&]() {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(bf[j], af[i], acc[i][j]);
     };
-    // this wave's loads of a stage are complete once at most `later` later stages (four loads each)
-    // are in flight
-    auto wait_stage = [&](int later) {
-        if (later >= 2) wait_vm<8>(); else if (later == 1) wait_vm<4>(); else wait_vm<0>();
-    };
 
-    constexpr int L = NST - 1;  // stages issued ahead
-    const int nk = K / BK;
-    for (int s = 0; s < L && s < nk; ++s) issue(s, s);
-    wait_stage(min(L - 1, nk - 1));
+    // phases as before, one per k32 sub-step and group; stage st + 1 is issued in the first sub-step
+    // of stage st (into the other slot, whose stage every wave finished reading before) and waited
+    // for (vmcnt 0: nothing later is in flight) before the barrier that closes stage st's last phase
+    issue(0, 0);
+    wait_vm<0>();
     exec_barrier();
-    if (late) exec_barrier();  // waves 4-7 sit out phase 0 (and waves 0-3 the last phase, 2nk)
-    for (int k = 0; k < nk; ++k) {
-        if (k + L < nk) issue(k + L, (k + L) % NST);
-        frags(k % NST);
-        if (late && k + 1 < nk) wait_stage(min(L - 1, nk - 2 - k));
+    if (late) exec_barrier();  // waves 4-7 sit out phase 0 (and waves 0-3 the last phase)
+    for (int u = 0; u < nsub; ++u) {
+        const int st = u >> 1, sub = u & 1;
+        if (sub == 0 && st + 1 < nk) issue(st + 1, (st + 1) & 1);
+        frags(st & 1, sub);
+        const bool last_of_stage = sub == 1 || u + 1 == nsub;
+        if (late && last_of_stage && st + 1 < nk) wait_vm<0>();
         exec_barrier();
         mma();
-        if (!late && k + 1 < nk) wait_stage(min(L - 1, nk - 2 - k));
-        if (!late || k + 1 < nk) exec_barrier();
+        if (!late && last_of_stage && st + 1 < nk) wait_vm<0>();
+        if (!late || u + 1 < nsub) exec_barrier();
     }
 
-    // epilogue through LDS: each wave rewrites its 128 x 64 block row-major in its own 16 KB of the
-    // ring (64 rows at a time, 16-byte blocks XOR-swizzled by row), then stores whole rows: lane
-    // (sr, l16) stores columns 4*l16 .. 4*l16+3 of row 4*r4 + sr.  Every operand read and load
-    // finished before the last barrier, so no wave waits for the others here.
+    // epilogue through LDS: each wave rewrites its block row-major in its own 16 KB of the ring (64
+    // rows at a time, 16-byte blocks XOR-swizzled by row), then stores whole rows: lane (sr, l16)
+    // stores columns 4*l16 .. 4*l16+3 of row 4*r4 + sr.  Every operand read and load finished before
+    // the last barrier, so no wave waits for the others here.
     float* stage = reinterpret_cast<float*>(&sm) + wave * (64 * 64);
     const int sr = lane >> 4, sc = 4 * (lane & 15);
     const int nb = n0 + WN * wn + sc;  // this lane's first column
@@ -174,18 +172,19 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_nt_kernel(const uint16_t* __rest
         }
     }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < (NI + 3) / 4; ++half) {
+        constexpr int NH = NI < 4 ? NI : 4;  // 16-row blocks per staged half
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NH; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 *reinterpret_cast<f32x4*>(&stage[(16 * i + l16) * 64 + 4 * ((4 * j + g4) ^ l16)]) = acc[4 * half + i][j];
         wait_lgkm0();
 #pragma unroll
-        for (int r4 = 0; r4 < 16; ++r4) {
+        for (int r4 = 0; r4 < 4 * NH; ++r4) {
             const int rl = 4 * r4 + sr;
             f32x4 v = *reinterpret_cast<const f32x4*>(&stage[rl * 64 + 4 * ((sc >> 2) ^ (rl & 15))]);
-            const int m = m0 + WM * wm + 64 * half + rl;
+            const int m = pm0 + WR * wm + 64 * half + rl;
             if (m >= M || lim <= 0) continue;
             if constexpr (EPI == GEMM_GATE) {
 #pragma unroll
@@ -203,6 +202,43 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_nt_kernel(const uint16_t* __rest
         }
         wait_lgkm0();  // the next half overwrites the staging rows
     }
+}
+
+// Tiles are numbered so that each XCD gets a contiguous range of them (see the header).  When the
+// tile count leaves a partial last round (at most half of the 256 compute units busy), that round's
+// tiles are split along M into sf = 4 (or 2) pieces of 64 (128) rows, each a workgroup of its own on
+// the XCD of its tile: the first nfull workgroups take whole tiles, the rest the pieces.
+template <bool OUT_F32, int EPI>
+__global__ void __launch_bounds__(NTHR, 1) gemm_nt_kernel(const uint16_t* __restrict__ A, int lda,
+                                                          const uint16_t* __restrict__ Bt, int ldb, GemmOut out,
+                                                          int M, int N, int K, int nfull, int sf) {
+    __shared__ Smem sm;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN, total = tm * tn;
+    const int xcd = blockIdx.x & 7, q = total >> 3, rem = total & 7;
+    const int first = xcd * q + min(xcd, rem);  // this XCD's first tile
+    int pid, piece = -1;
+    if ((int)blockIdx.x < nfull) {
+        pid = first + (blockIdx.x >> 3);
+    } else {
+        const int v = (blockIdx.x - nfull) >> 3;  // piece index within this XCD
+        const int t = v / sf, cnt = q + (xcd < rem ? 1 : 0) - nfull / 8;
+        if (t >= cnt) return;  // (the whole workgroup)
+        pid = first + nfull / 8 + t;
+        piece = v % sf;
+    }
+    constexpr int GM = 4;
+    const int in_group = GM * tn, first_m = (pid / in_group) * GM, gsize = min(tm - first_m, GM);
+    const int im = first_m + (pid % in_group) % gsize, jn = (pid % in_group) / gsize;
+    const int m0 = im * BM, n0 = jn * BN;
+    if (piece < 0)
+        gemm_tile<OUT_F32, EPI, 8>(sm, A, lda, Bt, ldb, out, M, N, K, m0, n0, wave, lane);
+    else if (sf == 2)
+        gemm_tile<OUT_F32, EPI, 4>(sm, A, lda, Bt, ldb, out, M, N, K, m0 + 128 * piece, n0, wave, lane);
+    else
+        gemm_tile<OUT_F32, EPI, 2>(sm, A, lda, Bt, ldb, out, M, N, K, m0 + 64 * piece, n0, wave, lane);
 }
 
 // Batched transpose: job j writes dst[n * ldd + k] = src[k * lds + n] for k < K, n < N (bf16), one
@@ -279,13 +315,22 @@ hipError_t launch_gemm_nt(const uint16_t* A, int lda, const uint16_t* Bt, int ld
     if (out.epi == GEMM_GATE && (out.nseg != 1 || !out_f32 || !out.bias || !out.head_scale)) return hipErrorInvalidValue;
     const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     if (tiles > (1L << 30)) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)tiles), block(NTHR);
+    // a partial last round of at most 64 (128) tiles runs as 64-row (128-row) pieces
+    const long nfull = tiles / 256 * 256, tail = tiles - nfull;
+    const int sf = (nfull > 0 && tail > 0) ? (tail <= 64 ? 4 : tail <= 128 ? 2 : 1) : 1;
+    long nwg = tiles;
+    if (sf > 1) nwg = nfull + 8L * sf * ((tiles / 8 - nfull / 8) + (tiles % 8 ? 1 : 0));
+    const int nf = sf > 1 ? (int)nfull : (int)tiles;
+    const dim3 grid((unsigned)nwg), block(NTHR);
     if (out.epi == GEMM_GATE)
-        hipLaunchKernelGGL((gemm_nt_kernel<true, GEMM_GATE>), grid, block, 0, stream, A, lda, Bt, ldb, out, M, N, K);
+        hipLaunchKernelGGL((gemm_nt_kernel<true, GEMM_GATE>), grid, block, 0, stream, A, lda, Bt, ldb, out, M, N, K,
+                           nf, sf);
     else if (out_f32)
-        hipLaunchKernelGGL((gemm_nt_kernel<true, GEMM_STORE>), grid, block, 0, stream, A, lda, Bt, ldb, out, M, N, K);
+        hipLaunchKernelGGL((gemm_nt_kernel<true, GEMM_STORE>), grid, block, 0, stream, A, lda, Bt, ldb, out, M, N, K,
+                           nf, sf);
     else
-        hipLaunchKernelGGL((gemm_nt_kernel<false, GEMM_STORE>), grid, block, 0, stream, A, lda, Bt, ldb, out, M, N, K);
+        hipLaunchKernelGGL((gemm_nt_kernel<false, GEMM_STORE>), grid, block, 0, stream, A, lda, Bt, ldb, out, M, N, K,
+                           nf, sf);
     return hipGetLastError();
 }
 
