@@ -154,16 +154,17 @@ kda_status kda_decode(const kda_fwd_desc* desc, const void* q, const void* k, co
  * kda_fwd_cp -- kda_fwd for few, long sequences: in-device context parallelism (explainer page,
  * section 13.3.1, with the decomposition of section 13.3.2: the state after a segment is its
  * accumulated transition M_i times its initial state plus its local state estimate S_hat_i).
- * Each sequence is cut into nseg segments that run side by side: a pass from S = 0 gives every
- * S_hat_i, a pass with v = 0 from S = I gives every M_i, a float32 scan over segments gives every
- * initial state, and a last pass from those states writes o and S_T.  About three times the work
- * of kda_fwd spread over nseg times more workgroups: it pays when 2*B*H is well below the 256
- * compute units (e.g. B = 1, H = 16 at a million tokens).
+ * Each sequence is cut into nseg segments that run side by side: one pass gives every S_hat_i (from
+ * S = 0) and every M_i (v = 0 from S = I), a float32 scan over segments gives every initial state,
+ * and a last pass from those states writes o and S_T.  About three times the work of kda_fwd spread
+ * over nseg times more workgroups: it pays when 2*B*H is well below the 256 compute units (e.g.
+ * B = 1, H = 16 at a million tokens, or B = 2, H = 16 at 8192 tokens).
  *   desc    : as kda_fwd, bf16 I/O only (Dk = Dv = 128; float32 I/O is KDA_ERR_UNSUPPORTED)
- *   nseg    : segments per sequence; 0 = automatic (enough for about one workgroup per compute
- *             unit, segments of at least 1024 tokens), 1 = kda_fwd.  T need not be a multiple of
- *             anything: the largest multiple of nseg*32 tokens is run in segments and the rest
- *             after it, from the last segment's state.
+ *   nseg    : segments per sequence; 0 = automatic (the count of least modelled time among those
+ *             with segments of at least 1024 tokens; 1 when none pays), 1 = kda_fwd.  T need not
+ *             be a multiple of anything: the first nseg - 1 segments hold floor(T / (32 nseg))
+ *             chunks of 32 tokens each and the last one the rest (nseg larger than T / 32 runs
+ *             kda_fwd).
  *   ws      : device workspace of at least kda_fwd_cp_workspace_size(desc, nseg) bytes, 256-byte
  *             aligned (may be NULL when that size is 0); its contents are scratch.
  * Other arguments as kda_fwd (S_T may equal S0).  The result matches kda_fwd to within the bf16

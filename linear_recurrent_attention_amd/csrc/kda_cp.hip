@@ -4,23 +4,24 @@
 // evaluated side by side on one device, then merges them to recover each segment's initial state;
 // section 13.3.2 states the decomposition that makes the merge possible: the state after segment i
 // is M_i S_start(i) + S_hat_i, with M_i the segment's accumulated transition and S_hat_i its local
-// state estimate (the segment run from a zero state).  Here, for nseg segments of Ls tokens:
-//   1. S_hat_i: the chunkwise kernel from S = 0 (no output), for segments 1..nseg-2; segment 0 runs
-//               from the call's S0 instead, which gives S_start(1) itself;
-//      M_i:     the same kernel with v = 0 and S = I (no output), for segments 1..nseg-2: the gated
-//               delta rule is linear in (S, v), so with v = 0 it maps the initial state through the
-//               segment, and from I it yields the transition matrix itself;
+// state estimate (the segment run from a zero state).  Here each sequence is cut into nseg segments,
+// the first nseg - 1 of Ls tokens (whole chunks) and the last one the rest, and:
+//   1. one launch of the chunkwise kernel's state-only instantiation runs
+//        S_hat_i: segments 0..nseg-2 from S = 0, except segment 0, which runs from the call's S0 and
+//                 so gives S_start(1) itself, and
+//        M_i:     segments 1..nseg-2 with v = 0 from S = I: the gated delta rule is linear in (S, v),
+//                 so with v = 0 it maps the initial state through the segment, and from I it yields
+//                 the transition matrix itself
 //      (the last segment needs neither, and segment 0 no transition);
 //   2. the scan S_start(0) = S0, S_start(1) = the first pass's segment 0,
 //      S_start(i+1) = M_i S_start(i) + S_hat_i, in float32;
 //   3. the chunkwise kernel over every segment at once from S_start(i), writing o and the segment's
 //      final state; the last segment's is S_T.
-// Both first-pass launches run only the segments they need (the kernel's batch-row subset) and use
-// its state-only instantiation.
-// A sequence too short for B*H*nseg to matter, or T not a multiple of nseg*32, is handled by running
-// the whole multiple of nseg*32 this way and the remaining tail with the plain kernel from the last
-// segment's state.  This is three passes of work in exchange for nseg times more workgroups: worth it
-// when 2*B*H workgroups leave most of the 256 compute units idle.
+// This is about three passes of work in exchange for nseg times more workgroups: worth it when
+// 2*B*H workgroups leave most of the 256 compute units idle.  The automatic segment count minimises
+// a small model of the three passes' time (rounds of 256 workgroups times tokens per segment, plus
+// the scan's steps).
+#include <cmath>
 #include <mutex>
 
 #include "kda.h"
@@ -90,53 +91,77 @@ __global__ void __launch_bounds__(NTHR) kda_cp_scan_kernel(const float* __restri
 
 size_t seg_floats(int Bg, int nseg, int H) { return (size_t)Bg * nseg * H * D * D; }
 
-// Initial states of the first pass: S0 (or 0) for segment 0 of each of Bg sequences, 0 for the others.
-// Sst: [Bg][nseg][H][D][D]; S0: [Bg][H][D][D] or NULL.
-__global__ void kda_cp_seed_kernel(const float* __restrict__ S0, float* __restrict__ Sst, int Bg, int nseg, int H) {
-    const size_t mat = (size_t)D * D, n = (size_t)Bg * nseg * H * mat;
-    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
-        const size_t m = e / mat, w = e - m * mat;  // m = (b * nseg + s) * H + h
-        const int h = (int)(m % H), s = (int)((m / H) % nseg), b = (int)(m / ((size_t)H * nseg));
-        Sst[e] = (s == 0 && S0) ? S0[((size_t)b * H + h) * mat + w] : 0.f;
+// Initial states of the first pass, in one launch: Sst gets S0 (or 0) for segment 0 of each of the B
+// sequences and 0 for segments 1..nseg-2; M gets I for segments 1..nseg-2 (the transitions' start).
+// Sst, M: [B][nseg][H][D][D]; S0: [B][H][D][D] or NULL.
+__global__ void kda_cp_init_kernel(const float* __restrict__ S0, float* __restrict__ Sst, float* __restrict__ M,
+                                   int B, int nseg, int H) {
+    const size_t mat = (size_t)D * D, per_b = (size_t)(nseg - 1) * H * mat;  // segments 0..nseg-2
+    const size_t n = (size_t)B * per_b;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < 2 * n; e += (size_t)gridDim.x * blockDim.x) {
+        const bool ism = e >= n;
+        const size_t f = ism ? e - n : e;
+        const int b = (int)(f / per_b);
+        const size_t r = f - (size_t)b * per_b;           // within sequence b: (s * H + h) * mat + w
+        const int s = (int)(r / ((size_t)H * mat)), h = (int)((r / mat) % H);
+        const size_t w = r % mat;
+        const size_t at = (size_t)b * nseg * H * mat + r;  // [b][s][h][w]
+        if (!ism)
+            Sst[at] = (s == 0 && S0) ? S0[((size_t)b * H + h) * mat + w] : 0.f;
+        else if (s > 0)
+            M[at] = (w / D == w % D) ? 1.f : 0.f;
     }
 }
 
-// n D x D identity matrices, back to back.
-__global__ void kda_cp_identity_kernel(float* __restrict__ S, size_t n) {
-    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n * D * D; e += (size_t)gridDim.x * blockDim.x) {
-        const int w = (int)(e % ((size_t)D * D));
-        S[e] = (w / D == w % D) ? 1.f : 0.f;
+// S_T[b] = the last segment's final state of sequence b (Shat: [B][nseg][H][D][D]; S_T: [B][H][D][D]).
+__global__ void kda_cp_last_state_kernel(const float* __restrict__ Shat, float* __restrict__ ST, int B, int nseg,
+                                         int H) {
+    const size_t mat = (size_t)D * D, per_b = (size_t)H * mat;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < (size_t)B * per_b;
+         e += (size_t)gridDim.x * blockDim.x) {
+        const size_t b = e / per_b;
+        ST[e] = Shat[(b * nseg + nseg - 1) * per_b + (e - b * per_b)];
     }
 }
 
-// Params of the chunkwise kernel over the nseg segments of Bg batches starting at batch b0: each
-// segment is a batch row of its own (row stride Ls tokens), which matches the [B, T, H, D] layout
-// when the group's sequences are exactly nseg * Ls tokens long, or when the group is one sequence.
-Params seg_params(const Params& u, int b0, int Bg, int nseg, int Ls) {
+// Params of the chunkwise kernel over the nseg segments of all B sequences: row r is segment r % nseg
+// of sequence r / nseg (Ls tokens, the last one the rest of the sequence).
+Params seg_params(const Params& u, int nseg, int Ls) {
     Params p = u;
-    const size_t tok = (size_t)b0 * u.T * u.H;  // first row of batch b0
-    const size_t esz = u.in_f32 ? 4 : 2;        // q, k, v element size
-    p.q = (const char*)u.q + tok * D * esz;
-    p.k = (const char*)u.k + tok * D * esz;
-    p.v = (const char*)u.v + tok * D * esz;
-    p.g = u.g + tok * D;
-    p.beta = u.beta + tok;
-    p.o = u.o ? (char*)u.o + tok * D * (u.o_f32 ? 4 : 2) : nullptr;
-    p.B = Bg * nseg;
+    p.B = u.B * nseg;
     p.T = Ls;
     p.tstride = Ls;
+    p.seg_T = u.T;
+    p.seg_n = nseg;
     p.S_ckpt = nullptr; p.ckpt_chunks = 1; p.n_ckpt = 0;
     return p;
 }
 
+// Modelled time of a plan, in units of one chunk step of one round of workgroups: the first pass
+// (state-only, about 0.8 of a full step) and the output pass over T / nseg tokens, each in rounds of
+// 256 workgroups, plus four chunk steps per scan step; nseg = 1 is the plain kernel.
+double plan_cost(int B, int T, int H, int nseg) {
+    const double n0 = 2.0 * B * H, chunks = T / 32.0;
+    auto rounds = [](double wg) { return std::ceil(wg / 256.0); };
+    if (nseg == 1) return chunks * rounds(n0);
+    const double w1 = n0 * (nseg - 1) + n0 * (nseg > 2 ? nseg - 2 : 0);
+    return chunks / nseg * (0.8 * rounds(w1) + rounds(n0 * nseg)) + 4.0 * (nseg - 2);
+}
+
 }  // namespace cp
 
-// Number of segments the orchestration below will use, and the tokens per segment (0: plain run).
+// Number of segments the orchestration below will use, and the tokens of each but the last (0: plain
+// run).  A requested count is kept if every segment gets at least one chunk; 0 picks the count of
+// least modelled time among those with segments of at least 1024 tokens.
 void cp_plan(int B, int T, int H, int nseg_req, int& nseg, int& Ls) {
     nseg = nseg_req;
-    if (nseg == 0) {  // enough segments for about one workgroup per compute unit, each >= 1024 tokens
+    if (nseg == 0) {
         nseg = 1;
-        while (2 * B * H * nseg * 2 <= 256 && T / (nseg * 2) >= 1024) nseg *= 2;
+        double best = cp::plan_cost(B, T, H, 1);
+        for (int n = 2; n <= 64 && T / n >= 1024; ++n) {
+            const double c = cp::plan_cost(B, T, H, n);
+            if (c < best) { best = c; nseg = n; }
+        }
     }
     Ls = nseg >= 2 ? (T / (nseg * 32)) * 32 : 0;
     if (Ls == 0) nseg = 1;
@@ -146,74 +171,47 @@ size_t cp_workspace_bytes(int B, int T, int H, int nseg_req) {
     int nseg, Ls;
     cp_plan(B, T, H, nseg_req, nseg, Ls);
     if (nseg == 1) return 0;
-    const int Bg = (nseg * Ls == T) ? B : 1;
-    return 3 * cp::seg_floats(Bg, nseg, H) * sizeof(float);
+    return 3 * cp::seg_floats(B, nseg, H) * sizeof(float);
 }
 
 hipError_t launch_fwd_cp(const Params& u, int nseg_req, float* ws, hipStream_t stream) {
     int nseg, Ls;
     cp_plan(u.B, u.T, u.H, nseg_req, nseg, Ls);
     if (nseg == 1) return launch_fwd_bf16(u, stream);
-    const int Tm = nseg * Ls;
-    const int Bg = (Tm == u.T) ? u.B : 1;  // a ragged tail is run per sequence
-    const size_t n = cp::seg_floats(Bg, nseg, u.H);
+    const size_t n = cp::seg_floats(u.B, nseg, u.H);
     float* Shat = ws;
     float* M = ws + n;
     float* Sst = ws + 2 * n;
-    hipError_t e = hipSuccess;
-    for (int b0 = 0; b0 < u.B && e == hipSuccess; b0 += Bg) {
-        const float* S0 = u.S0 ? u.S0 + (size_t)b0 * u.H * cp::D * cp::D : nullptr;
-        // 1. segments 0..nseg-2 from their first-pass states (S0 for segment 0, else 0, seeded into the
-        //    buffer step 2 fills later): segment 0's final state and the others' local states
-        hipLaunchKernelGGL(cp::kda_cp_seed_kernel, dim3(1024), dim3(256), 0, stream, S0, Sst, Bg, nseg, u.H);
-        if ((e = hipGetLastError()) != hipSuccess) break;
-        Params p = cp::seg_params(u, b0, Bg, nseg, Ls);
-        p.o = nullptr; p.S0 = Sst; p.S_T = Shat;
-        p.B = Bg * (nseg - 1); p.seg_lo = 0; p.seg_cnt = nseg - 1; p.seg_n = nseg;
-        if ((e = launch_fwd_bf16(p, stream)) != hipSuccess) break;
-        //    the transitions of segments 1..nseg-2 (v = 0 from I, in place in M)
-        if (nseg > 2) {
-            hipLaunchKernelGGL(cp::kda_cp_identity_kernel, dim3(1024), dim3(256), 0, stream, M,
-                               (size_t)Bg * nseg * u.H);
-            if ((e = hipGetLastError()) != hipSuccess) break;
-            p.v = nullptr; p.S0 = M; p.S_T = M;
-            p.B = Bg * (nseg - 2); p.seg_lo = 1; p.seg_cnt = nseg - 2;
-            if ((e = launch_fwd_bf16(p, stream)) != hipSuccess) break;
-        }
-        // 2. initial state of every segment
-        hipLaunchKernelGGL(cp::kda_cp_scan_kernel, dim3((unsigned)(Bg * u.H * (cp::D / cp::SCOLS))), dim3(cp::NTHR), 0,
-                           stream, Shat, M, S0, Sst, nseg, u.H);
-        if ((e = hipGetLastError()) != hipSuccess) break;
-        // 3. outputs, and each segment's final state (into Shat, no longer needed)
-        p = cp::seg_params(u, b0, Bg, nseg, Ls);
-        p.S0 = Sst; p.S_T = Shat;
-        if ((e = launch_fwd_bf16(p, stream)) != hipSuccess) break;
-        // the sequence's final state: the last segment's, or carried through the tail
-        for (int b = 0; b < Bg && e == hipSuccess; ++b) {
-            const float* last = Shat + ((size_t)(b * nseg + nseg - 1) * u.H) * cp::D * cp::D;
-            float* ST = u.S_T ? u.S_T + (size_t)(b0 + b) * u.H * cp::D * cp::D : nullptr;
-            Params t = u;
-            t.B = 1; t.S0 = last; t.S_T = ST;
-            t.S_ckpt = nullptr; t.ckpt_chunks = 1; t.n_ckpt = 0;
-            if (Tm < u.T) {  // Bg == 1 here
-                const size_t tok = ((size_t)(b0 + b) * u.T + Tm) * u.H;
-                const size_t esz = u.in_f32 ? 4 : 2;
-                t.q = (const char*)u.q + tok * cp::D * esz;
-                t.k = (const char*)u.k + tok * cp::D * esz;
-                t.v = (const char*)u.v + tok * cp::D * esz;
-                t.g = u.g + tok * cp::D;
-                t.beta = u.beta + tok;
-                t.o = (char*)u.o + tok * cp::D * (u.o_f32 ? 4 : 2);
-                t.T = u.T - Tm;
-                t.tstride = t.T;
-                e = launch_fwd_bf16(t, stream);
-            } else if (ST) {
-                t.T = 0;
-                e = launch_state_copy(t, stream);
-            }
-        }
+    hipError_t e;
+    // 1. first-pass initial states (S0 or 0 into Sst, I into M), then one state-only launch: segments
+    //    0..nseg-2 with v from their initial states into Shat (segment 0's final state, the others'
+    //    local states), and as the launch's second row set the transitions of segments 1..nseg-2
+    //    (v = 0 from I, in place in M)
+    hipLaunchKernelGGL(cp::kda_cp_init_kernel, dim3(1024), dim3(256), 0, stream, u.S0, Sst, M, u.B, nseg, u.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    Params p = cp::seg_params(u, nseg, Ls);
+    p.o = nullptr; p.S0 = Sst; p.S_T = Shat;
+    p.B = u.B * (nseg - 1); p.seg_lo = 0; p.seg_cnt = nseg - 1;
+    if (nseg > 2) {
+        p.alt_b0 = p.B;
+        p.B += u.B * (nseg - 2);
+        p.alt_seg_lo = 1; p.alt_seg_cnt = nseg - 2;
+        p.alt_S0 = M; p.alt_ST = M;
     }
-    return e;
+    if ((e = launch_fwd_bf16(p, stream)) != hipSuccess) return e;
+    // 2. initial state of every segment
+    hipLaunchKernelGGL(cp::kda_cp_scan_kernel, dim3((unsigned)(u.B * u.H * (cp::D / cp::SCOLS))), dim3(cp::NTHR), 0,
+                       stream, Shat, M, u.S0, Sst, nseg, u.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 3. outputs, and each segment's final state (into Shat, no longer needed); S_T is the last one's
+    p = cp::seg_params(u, nseg, Ls);
+    p.S0 = Sst; p.S_T = Shat;
+    if ((e = launch_fwd_bf16(p, stream)) != hipSuccess) return e;
+    if (u.S_T) {
+        hipLaunchKernelGGL(cp::kda_cp_last_state_kernel, dim3(1024), dim3(256), 0, stream, Shat, u.S_T, u.B, nseg, u.H);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // Scratch of kda_fwd_cp_noalloc: the segment states (S_hat, M, S_start) in a fixed device array, so

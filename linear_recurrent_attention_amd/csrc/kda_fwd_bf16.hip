@@ -419,7 +419,7 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
 }
 
 template <bool IN_F32, bool SO>
-__device__ void key_waves(Smem& sm, const Params& p, size_t row0, int kw, int lane, int nchunk) {
+__device__ __forceinline__ void key_waves(Smem& sm, const Params& p, size_t row0, int kw, int lane, int nchunk) {
     KeyLoad kl;
     kl.kw = kw;
     kl.lane = lane;
@@ -445,7 +445,7 @@ __device__ void key_waves(Smem& sm, const Params& p, size_t row0, int kw, int la
 // helper waves.  Step n: the L Gram products (part 2), then the UT inverse and A (part 3) of chunk n.
 // ------------------------------------------------------------------------------------------------
 template <bool IN_F32, bool HP, bool SO>
-__device__ void helper_waves(Smem& sm, const Params& p, size_t row0, int half, int hw, int lane, int nchunk) {
+__device__ __forceinline__ void helper_waves(Smem& sm, const Params& p, size_t row0, int half, int hw, int lane, int nchunk) {
     const int l16 = lane & 15, g4 = lane >> 4;
     // v for value wave hw: this lane's values are tokens 16R + 4*g4 + r of a chunk, column col, read one
     // step ahead into registers and staged in LDS a step before their use.  Rows past T read the last
@@ -655,7 +655,7 @@ __device__ void helper_waves(Smem& sm, const Params& p, size_t row0, int half, i
 // value waves.  Step n handles chunk n-1 (nothing for n < 1); three barriers per step.
 // ------------------------------------------------------------------------------------------------
 template <bool OUT_F32, bool IN_F32, bool CKPT, bool SO>
-__device__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int half, int vw, int lane, int nchunk) {
+__device__ __forceinline__ void value_waves(Smem& sm, const Params& p, int bh, size_t row0, int half, int vw, int lane, int nchunk) {
     const int l16 = lane & 15, g4 = lane >> 4;
 
     // state: st[cb][r] = S[16*cb + 4*g4 + r][col]
@@ -868,20 +868,35 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_bf16_kernel(Params p) {
     }
     int b = bh / p.H;
     const int h = bh - b * p.H;
-    if (p.seg_cnt > 0) {  // a subset of the batch rows (see Params)
-        b = (b / p.seg_cnt) * p.seg_n + p.seg_lo + b % p.seg_cnt;
-        bh = b * p.H + h;
+    Params q = p;  // this workgroup's view (wave-uniform)
+    if (p.alt_b0 > 0 && b >= p.alt_b0) {  // the second row set of a merged launch (see Params)
+        b -= p.alt_b0;
+        q.v = nullptr;
+        q.S0 = p.alt_S0;
+        q.S_T = p.alt_ST;
+        q.seg_lo = p.alt_seg_lo;
+        q.seg_cnt = p.alt_seg_cnt;
     }
-    const size_t row0 = (size_t)b * p.tstride * p.H + h;  // row of token 0: (b*tstride + t)*H + h = row0 + t*H
-    const int nchunk = (p.T + C - 1) / C;
+    if (q.seg_cnt > 0)  // a subset of the batch rows (see Params)
+        b = (b / q.seg_cnt) * q.seg_n + q.seg_lo + b % q.seg_cnt;
+    bh = b * p.H + h;
+    size_t row0;  // row of token 0: (first token + t)*H + h = row0 + t*H
+    if (p.seg_T > 0) {  // row b = segment b % seg_n of sequence b / seg_n; the last segment runs to seg_T
+        const int s = b % p.seg_n;
+        row0 = ((size_t)(b / p.seg_n) * p.seg_T + (size_t)s * p.tstride) * p.H + h;
+        q.T = s == p.seg_n - 1 ? p.seg_T - (p.seg_n - 1) * p.tstride : p.tstride;
+    } else {
+        row0 = (size_t)b * p.tstride * p.H + h;
+    }
+    const int nchunk = (q.T + C - 1) / C;
     if (nchunk == 0) return;  // (the host runs the state copy instead; every wave leaves here alike)
 
     if (wave < NKW)
-        key_waves<IN_F32, SO>(sm, p, row0, wave, lane, nchunk);
+        key_waves<IN_F32, SO>(sm, q, row0, wave, lane, nchunk);
     else if (wave < NKW + NVW)
-        value_waves<OUT_F32, IN_F32, CKPT, SO>(sm, p, bh, row0, half, wave - NKW, lane, nchunk);
+        value_waves<OUT_F32, IN_F32, CKPT, SO>(sm, q, bh, row0, half, wave - NKW, lane, nchunk);
     else
-        helper_waves<IN_F32, HP, SO>(sm, p, row0, half, wave - NKW - NVW, lane, nchunk);
+        helper_waves<IN_F32, HP, SO>(sm, q, row0, half, wave - NKW - NVW, lane, nchunk);
 }
 
 }  // namespace bf16path

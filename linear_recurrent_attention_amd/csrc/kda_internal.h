@@ -28,6 +28,16 @@ struct Params {
     // for b < B, i.e. seg_cnt of every seg_n rows, starting at row seg_lo (the context-parallel passes
     // that need only some segments of each sequence); every tensor is indexed by that row
     int seg_lo, seg_cnt, seg_n;
+    // bf16 path, optional (seg_T = 0: off): rows are the seg_n segments of sequences of seg_T tokens;
+    // row r is segment r % seg_n of sequence r / seg_n, starting at token (r % seg_n) * tstride of it,
+    // tstride tokens long except the last segment, which runs to seg_T (T is then ignored)
+    int seg_T;
+    // bf16 path, optional (alt_b0 = 0: off): batch rows b >= alt_b0 of a launch are rows b - alt_b0 of a
+    // second run with v = 0, initial and final states alt_S0 / alt_ST (may be the same array) and the
+    // row subset alt_seg_lo, alt_seg_cnt (same seg_n): two state-only runs in one launch
+    int alt_b0, alt_seg_lo, alt_seg_cnt;
+    const float* alt_S0;
+    float* alt_ST;
 };
 
 // Backward problem (all float32 gradients; NULL outputs are skipped).

@@ -18,10 +18,11 @@ def _kda():
 
 
 @pytest.mark.parametrize("B,H,T,nseg,s0,precise", [
-    (1, 4, 8192 + 37, 4, True, False),    # ragged: segments per sequence, then a 37-token tail
+    (1, 4, 8192 + 37, 4, True, False),    # ragged: three segments of 2048 tokens, the last one 2085
     (2, 2, 4096, 4, True, False),         # T = 4 x 1024: both sequences' segments in one launch
-    (2, 3, 3000, 2, False, True),         # ragged with two sequences (one group each), precise plan
-    (1, 2, 70000, 0, True, False),        # automatic plan: 32 segments of 2176 tokens and a 368-token tail
+    (2, 3, 3000, 2, False, True),         # ragged with two sequences, precise plan (1472 + 1528 tokens)
+    (2, 16, 8192, 3, False, True),        # three segments (2720, 2720, 2752 tokens), first pass merged
+    (1, 2, 70000, 0, True, False),        # automatic plan: 31 segments (30 of 2240 tokens, then 2800)
 ])
 def test_cp_matches_oracle(B, H, T, nseg, s0, precise):
     d, S0 = rand_small(31, B, T, H, s0=s0)
