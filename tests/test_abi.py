@@ -218,9 +218,11 @@ def test_cp_workspace_size_plan():
     assert _lib.cp_workspace_size(d, 1) == 0                       # nseg = 1 is kda_fwd
     # enough heads already: the automatic plan is one segment
     assert _lib.cp_workspace_size(desc(B=4, T=16384, H=32), 0) == 0
-    # a ragged T runs the segments per sequence: one batch row of buffers
-    assert _lib.cp_workspace_size(desc(B=2, T=4096 + 5, H=2), 4) == 3 * 4 * 2 * 128 * 128 * 4
+    # a ragged T: the last segment takes the rest; every sequence's segments run together
+    assert _lib.cp_workspace_size(desc(B=2, T=4096 + 5, H=2), 4) == 3 * 2 * 4 * 2 * 128 * 128 * 4
     assert _lib.cp_workspace_size(desc(B=2, T=4096, H=2), 4) == 3 * 2 * 4 * 2 * 128 * 128 * 4
+    # the automatic plan for two sequences of 16 heads at 8192 tokens: three segments
+    assert _lib.cp_workspace_size(desc(B=2, T=8192, H=16), 0) == 3 * 2 * 3 * 16 * 128 * 128 * 4
     # too short for the requested segments (T < nseg * 32)
     assert _lib.cp_workspace_size(desc(T=100), 4) == 0
     # invalid descriptors
