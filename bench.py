@@ -35,8 +35,8 @@ CSRC = os.path.join(ROOT, "linear_recurrent_attention_amd", "csrc")
 # 512 MiB copy (factors 2.0 and 1.0); valid only for the kernel source with the recorded hash.
 MEASURED_TRAFFIC = {
     "core": {"sources": ("kda_fwd_bf16.hip", "kda_common.h"),
-             "sha256": "8c028f8e6c5cca9529a93ad80cd03d090a88f339dc7246e7f8792cfc871ae43b",
-             "bytes": (1344568 * 2.0 + 532480 * 1.0) * 1024,
+             "sha256": "f93625c09e36ee1c3914e973954e67c9446e0111d06e1ee0bc4931fc84683cf0",
+             "bytes": (1345042 * 2.0 + 532480 * 1.0) * 1024,
              "profile": "profiles/kda_fwd_bf16_B4_H32_T16384_D128.md"},
     "decode": {"sources": ("kda_decode.hip", "kda_common.h"),
                "sha256": "27169bbf2dad64f9f864da57513ef39a0250b622edfad8163610ea21d502356f",
