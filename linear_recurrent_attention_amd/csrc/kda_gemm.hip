@@ -52,6 +52,7 @@ __device__ __forceinline__ int swz64(int row, int chunk) { return row * BK2 + 8 
 struct alignas(16) Smem {
     uint16_t a[NST][BM * BK2];
     uint16_t b[NST][BN * BK2];
+    float qx[16 * 3 * 64 + 2 * 8 * 64];  // the q/k epilogue's halo rows and per-row partial sums
 };
 static_assert(sizeof(Smem) >= NW * 64 * 64 * sizeof(float), "the epilogue's staging fits in the operand ring");
 
@@ -65,6 +66,156 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (
 __device__ __forceinline__ void exec_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __builtin_amdgcn_exp2f(-x * kLog2e)); }
+
+// The q/k epilogue of GEMM_QKCONV, for a 256-row tile whose columns start below qk_cols.  Staged
+// through LDS like the plain epilogue (64 rows of the wave's 128 x 64 block at a time); per element
+// the 4-tap convolution over rows r-3..r, SiLU, then the L2 norm of the row over the head's 128
+// columns: the blocks of waves 2p and 2p + 1, whose partial sums of squares meet in LDS.  The rows
+// above a staged half come from halos: a wave's own rows 61-63 for its second half, and for the
+// waves of rows 128-255 the last three rows of the waves above (written from the accumulators first).
+// Column pairs past qk_cols (a tile straddling the end of k) are stored as plain sums.
+__device__ __forceinline__ void qk_epilogue(Smem& sm, f32x4 (&acc)[8][4], const GemmOut& out, int M, int N, int m0,
+                                            int n0, int wave, int lane) {
+    const int l16 = lane & 15, g4 = lane >> 4, wm = wave >> 2, wn = wave & 3;
+    float* stage = reinterpret_cast<float*>(&sm) + wave * (64 * 64);
+    float* haloA = sm.qx;             // [wave][3][64]: raw rows 125-127 of each wave's block
+    float* haloB = sm.qx + 8 * 192;   // [wave][3][64]: raw rows 61-63 of this wave's block
+    float* psum = sm.qx + 16 * 192;   // [half][wave][64 rows]: sums of squares over the wave's columns
+    const int colb = n0 + WN * wn;    // first column of this wave's block
+    const bool fused = n0 + 128 * (wn >> 1) < out.qk_cols;
+    const int tr = m0 / BM;
+    const size_t qkc = (size_t)out.qk_cols;
+    if (l16 >= 13) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<f32x4*>(&haloA[(wave * 3 + l16 - 13) * 64 + 16 * j + 4 * g4]) = acc[7][j];
+    }
+    if (fused) {  // the tile's first three and last three raw rows
+        if (wm == 0 && l16 < 3) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4*>(&out.side[((size_t)tr * 6 + l16) * qkc + colb + 16 * j + 4 * g4]) = acc[0][j];
+        }
+        if (wm == 1 && l16 >= 13) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4*>(&out.side[((size_t)tr * 6 + l16 - 10) * qkc + colb + 16 * j + 4 * g4]) =
+                    acc[7][j];
+        }
+    }
+    // lane (sr, l16) takes rows 16 sr .. 16 sr + 15 of each staged half, columns c0 .. c0 + 3
+    const int sr = lane >> 4, sc = 4 * (lane & 15);
+    const int c0 = colb + sc;
+    f32x4 tw[4] = {};  // tw[t][e]: tap t of column c0 + e
+    if (fused) {
+        const float* taps = c0 < out.qk_hd ? out.conv_q + (size_t)c0 * 4 : out.conv_k + (size_t)(c0 - out.qk_hd) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f32x4 w = *reinterpret_cast<const f32x4*>(taps + 4 * e);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) tw[t][e] = w[t];
+        }
+    }
+    int seg = 0;
+#pragma unroll
+    for (int t = 1; t < GemmOut::kMaxSeg; ++t) seg += (t < out.nseg && c0 >= out.start[t]) ? 1 : 0;
+    const int c = c0 - out.start[seg];
+    const int lim = min(min(4, N - c0), out.start[seg + 1] - c0);
+    float* base = static_cast<float*>(out.ptr[seg]);
+    const size_t ld = (size_t)out.ld[seg];
+    const bool vec = lim == 4 && (out.ld[seg] & 3) == 0;
+    wait_lgkm0();
+    exec_barrier();  // every wave's halo rows are in LDS
+    auto row_at = [&](const float* st, int r) {
+        return *reinterpret_cast<const f32x4*>(&st[r * 64 + 4 * ((sc >> 2) ^ (r & 15))]);
+    };
+    // sum over the 16 lanes of a row of lanes, left in the row's last lane (DPP row shifts)
+    auto row_sum = [](float v) {
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, true));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, true));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, true));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, true));
+        return v;
+    };
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4*>(&stage[(16 * i + l16) * 64 + 4 * ((4 * j + g4) ^ l16)]) = acc[4 * half + i][j];
+        wait_lgkm0();
+        f32x4 x[19];  // raw rows 16 sr - 3 .. 16 sr + 15
+        if (fused) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[3 + r] = row_at(stage, 16 * sr + r);
+            if (sr > 0) {
+#pragma unroll
+                for (int r = 0; r < 3; ++r) x[r] = row_at(stage, 16 * sr - 3 + r);
+            } else if (half == 1) {
+#pragma unroll
+                for (int r = 0; r < 3; ++r) x[r] = *reinterpret_cast<const f32x4*>(&haloB[(wave * 3 + r) * 64 + sc]);
+            } else if (wm == 1) {
+#pragma unroll
+                for (int r = 0; r < 3; ++r) x[r] = *reinterpret_cast<const f32x4*>(&haloA[((wave - 4) * 3 + r) * 64 + sc]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 3; ++r) x[r] = f32x4{0.f, 0.f, 0.f, 0.f};  // tile rows 0-2: finished by the caller
+            }
+            if (half == 0 && sr == 3) {  // raw rows 61-63 for the second half
+#pragma unroll
+                for (int r = 0; r < 3; ++r) *reinterpret_cast<f32x4*>(&haloB[(wave * 3 + r) * 64 + sc]) = x[16 + r];
+            }
+            // convolution and SiLU in place (row r reads raw rows r .. r + 3 of x, so go from the top)
+#pragma unroll
+            for (int r = 15; r >= 0; --r) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float y = 0.f;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) y = __builtin_fmaf(tw[t][e], x[r + t][e], y);
+                    y = y * (1.f / (1.f + __builtin_amdgcn_exp2f(-y * kLog2e)));
+                    x[r + 3][e] = y;
+                    ss = __builtin_fmaf(y, y, ss);
+                }
+                ss = row_sum(ss);
+                if (l16 == 15) psum[(half * 8 + wave) * 64 + 16 * sr + r] = ss;
+            }
+        }
+        wait_lgkm0();
+        exec_barrier();  // both waves' partial sums of every row of this half
+        f32x4 inv[4];
+        if (fused) {
+            const int pa = (half * 8 + (wave & ~1)) * 64 + 16 * sr, pb = (half * 8 + (wave | 1)) * 64 + 16 * sr;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 sa = *reinterpret_cast<const f32x4*>(&psum[pa + 4 * q4]);
+                const f32x4 sb = *reinterpret_cast<const f32x4*>(&psum[pb + 4 * q4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) inv[q4][e] = __builtin_amdgcn_rsqf(sa[e] + sb[e] + out.eps);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int rl = 16 * sr + r;
+            const int m = m0 + WM * wm + 64 * half + rl;
+            if (m >= M || lim <= 0) continue;
+            f32x4 v;
+            if (fused) {
+                if (half == 0 && wm == 0 && rl < 3) continue;  // tile rows 0-2
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = x[r + 3][e] * inv[r >> 2][r & 3];
+            } else {
+                v = row_at(stage, rl);
+            }
+            float* dst = base + (size_t)m * ld + c;
+            if (vec) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+            else for (int e = 0; e < lim; ++e) dst[e] = v[e];
+        }
+        wait_lgkm0();  // the next half overwrites the staging rows
+    }
+}
 
 // One tile (or one piece of a split tile) of C: rows [pm0, pm0 + 32 NI) of the tile whose first row
 // is the A stage's row 0 at pm0, columns [n0, n0 + 256).  Each wave multiplies NI 16-row blocks by
@@ -146,6 +297,13 @@ __device__ __forceinline__ void gemm_tile(Smem& sm, const uint16_t* __restrict__
         mma();
         if (!late && last_of_stage && st + 1 < nk) wait_vm<0>();
         if (!late || u + 1 < nsub) exec_barrier();
+    }
+
+    if constexpr (EPI == GEMM_QKCONV && NI == 8) {
+        if (n0 < out.qk_cols) {  // (workgroup-uniform)
+            qk_epilogue(sm, acc, out, M, N, pm0, n0, wave, lane);
+            return;
+        }
     }
 
     // epilogue through LDS: each wave rewrites its block row-major in its own 16 KB of the ring (64
@@ -313,17 +471,33 @@ hipError_t launch_gemm_nt(const uint16_t* A, int lda, const uint16_t* Bt, int ld
             return hipErrorInvalidValue;
     if (out.start[0] != 0 || out.start[out.nseg] < N) return hipErrorInvalidValue;
     if (out.epi == GEMM_GATE && (out.nseg != 1 || !out_f32 || !out.bias || !out.head_scale)) return hipErrorInvalidValue;
+    if (out.epi == GEMM_QKCONV &&
+        (!out_f32 || M % BM || out.qk_cols < 128 || out.qk_cols % 128 || out.qk_hd % 128 || out.qk_hd > out.qk_cols ||
+         out.qk_cols > N || !out.conv_q || !out.conv_k || !out.side || (reinterpret_cast<uintptr_t>(out.side) & 15)))
+        return hipErrorInvalidValue;
     const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     if (tiles > (1L << 30)) return hipErrorInvalidValue;
-    // a partial last round of at most 64 (128) tiles runs as 64-row (128-row) pieces
+    // a partial last round of at most 64 (128) tiles runs as 64-row (128-row) pieces (not when one of
+    // them holds q/k columns of GEMM_QKCONV, whose epilogue needs whole tiles)
     const long nfull = tiles / 256 * 256, tail = tiles - nfull;
-    const int sf = (nfull > 0 && tail > 0) ? (tail <= 64 ? 4 : tail <= 128 ? 2 : 1) : 1;
+    int sf = (nfull > 0 && tail > 0) ? (tail <= 64 ? 4 : tail <= 128 ? 2 : 1) : 1;
+    if (sf > 1 && out.epi == GEMM_QKCONV) {
+        const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN, in_group = 4 * tn;
+        for (long pid = nfull; pid < tiles; ++pid) {  // the tail tiles, numbered as in the kernel
+            const int first_m = (int)(pid / in_group) * 4, gsize = min(tm - first_m, 4);
+            const int jn = (int)(pid % in_group) / gsize;
+            if (jn * BN < out.qk_cols) sf = 1;
+        }
+    }
     long nwg = tiles;
     if (sf > 1) nwg = nfull + 8L * sf * ((tiles / 8 - nfull / 8) + (tiles % 8 ? 1 : 0));
     const int nf = sf > 1 ? (int)nfull : (int)tiles;
     const dim3 grid((unsigned)nwg), block(NTHR);
     if (out.epi == GEMM_GATE)
         hipLaunchKernelGGL((gemm_nt_kernel<true, GEMM_GATE>), grid, block, 0, stream, A, lda, Bt, ldb, out, M, N, K,
+                           nf, sf);
+    else if (out.epi == GEMM_QKCONV)
+        hipLaunchKernelGGL((gemm_nt_kernel<true, GEMM_QKCONV>), grid, block, 0, stream, A, lda, Bt, ldb, out, M, N, K,
                            nf, sf);
     else if (out_f32)
         hipLaunchKernelGGL((gemm_nt_kernel<true, GEMM_STORE>), grid, block, 0, stream, A, lda, Bt, ldb, out, M, N, K,

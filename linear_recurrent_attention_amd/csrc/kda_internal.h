@@ -79,8 +79,14 @@ hipError_t launch_fwd_cp(const Params& p, int nseg_req, float* ws, hipStream_t s
 // [start[s], start[s+1]), each written to ptr[s] (row stride ld[s], column start[s] at column 0,
 // 16-byte aligned), as float32 or bf16.  Segment starts must be multiples of 4, start[0] = 0 and
 // start[nseg] >= N.  epi = GEMM_GATE (one float32 segment) writes -5 sigmoid(exp(head_scale[n / 128])
-// (C + bias[n])) instead of C: the decay gate of the fused layer.
-enum { GEMM_STORE = 0, GEMM_GATE = 1 };
+// (C + bias[n])) instead of C: the decay gate of the fused layer.  epi = GEMM_QKCONV (float32 output,
+// M a multiple of 256, qk_cols and qk_hd multiples of 128): columns [0, qk_cols) are the layer's q
+// (the first qk_hd) and k projections, heads of 128 columns; each of their rows r of a 256-row tile
+// gets the causal depthwise convolution over rows r-3..r (taps conv_q / conv_k, [column][4], tap 3
+// on row r), SiLU and L2 over its head (x / sqrt(sum x^2 + eps)); rows 0-2 of each tile are not
+// written (their window reaches into the tile above) and the tile's first and last three raw rows go
+// to side[tile row][6][qk_cols] for the caller to finish them.
+enum { GEMM_STORE = 0, GEMM_GATE = 1, GEMM_QKCONV = 2 };
 struct GemmOut {
     static constexpr int kMaxSeg = 6;
     void* ptr[kMaxSeg];
@@ -90,6 +96,11 @@ struct GemmOut {
     int epi;
     const float* bias;
     const float* head_scale;
+    const float* conv_q;  // GEMM_QKCONV
+    const float* conv_k;
+    float* side;
+    int qk_cols, qk_hd;
+    float eps;
 };
 hipError_t launch_gemm_nt(const uint16_t* A, int lda, const uint16_t* Bt, int ldb, const GemmOut& out, bool out_f32,
                           int M, int N, int K, hipStream_t stream);

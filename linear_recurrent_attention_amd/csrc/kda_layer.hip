@@ -155,6 +155,84 @@ __global__ void conv_state_kernel(int B, int T, int HD, const float* pq, const f
     }
 }
 
+// The fused path (T a multiple of 256): the input projection's epilogue already applied the short
+// convolution, SiLU and L2 to q and k except on rows 0-2 of each 256-row tile, whose window reaches
+// into the tile above; it kept each tile's first and last three raw rows in side[tile][6][2*HD] (q
+// columns, then k).  This kernel finishes those rows, one wave per (tile, head of q or k, row) with
+// two channels per lane (the window from the tile above, or from the incoming window at a sequence
+// start), and beyond those waves computes beta = sigmoid(beta logit) for every row.
+struct FixParams {
+    int B, T, H, HD;
+    const float* side;
+    const float* conv_q;    // [HD, 4]
+    const float* conv_k;
+    const float* state_in;  // [B, 3, 2*HD] or null
+    const float* pbeta;     // [B*T, H] beta logit
+    float* q;               // [B*T, HD]
+    float* k;
+    float* beta;            // [B*T, H]
+    int fix_blocks;         // workgroups of the row fixups; the rest compute beta
+};
+
+__global__ void __launch_bounds__(256) qk_fixup_kernel(FixParams p) {
+    if ((int)blockIdx.x >= p.fix_blocks) {
+        const long n = (long)p.B * p.T * p.H;
+        for (long e = (long)(blockIdx.x - p.fix_blocks) * blockDim.x + threadIdx.x; e < n;
+             e += (long)(gridDim.x - p.fix_blocks) * blockDim.x)
+            p.beta[e] = sigmoidf_(p.pbeta[e]);
+        return;
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int ntile = p.B * p.T / 256, nhg = 2 * p.H;
+    const long gw = (long)blockIdx.x * 4 + wave;
+    if (gw >= (long)ntile * nhg * 3) return;
+    const int r = (int)(gw % 3), hg = (int)((gw / 3) % nhg), tr = (int)(gw / (3L * nhg));
+    const int ch = 128 * hg + 2 * lane;  // column in [0, 2*HD): q, then k
+    const size_t qkc = 2 * (size_t)p.HD;
+    const long m = 256L * tr + r;
+    const int b = (int)(m / p.T);
+    float2 x[4];  // raw rows m-3 .. m
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const long g = m - 3 + j;
+        const float* src;
+        if (g >= 256L * tr) src = p.side + ((size_t)tr * 6 + (size_t)(g - 256L * tr)) * qkc;
+        else if (g >= (long)b * p.T) src = p.side + ((size_t)(tr - 1) * 6 + 3 + (size_t)(g - (256L * tr - 3))) * qkc;
+        else if (p.state_in) src = p.state_in + ((size_t)b * 3 + 3 + (g - (long)b * p.T)) * qkc;
+        else src = nullptr;
+        x[j] = src ? *reinterpret_cast<const float2*>(src + ch) : make_float2(0.f, 0.f);
+    }
+    const bool isq = ch < p.HD;
+    const float* taps = isq ? p.conv_q + (size_t)ch * 4 : p.conv_k + (size_t)(ch - p.HD) * 4;
+    const float4 w0 = *reinterpret_cast<const float4*>(taps), w1 = *reinterpret_cast<const float4*>(taps + 4);
+    const float a0[4] = {w0.x, w0.y, w0.z, w0.w}, a1[4] = {w1.x, w1.y, w1.z, w1.w};
+    float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        y0 += a0[j] * x[j].x;
+        y1 += a1[j] * x[j].y;
+    }
+    y0 = silu(y0);
+    y1 = silu(y1);
+    const float inv = rsqrtf(wave_sum(y0 * y0 + y1 * y1) + EPS);
+    float* dst = isq ? p.q + (size_t)m * p.HD + ch : p.k + (size_t)m * p.HD + (ch - p.HD);
+    *reinterpret_cast<float2*>(dst) = make_float2(y0 * inv, y1 * inv);
+}
+
+// The outgoing window on the fused path: the last three raw rows of each sequence, kept in the side
+// buffer by the tile that ends it.
+__global__ void conv_state_side_kernel(int B, int T, int HD, const float* side, float* state_out) {
+    const size_t qkc = 2 * (size_t)HD;
+    const long n = (long)B * 3 * (long)qkc;
+    for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
+        const int ch = (int)(e % (long)qkc);
+        const long r = e / (long)qkc;
+        const int s = (int)(r % 3), b = (int)(r / 3);
+        const long tr_last = ((long)(b + 1) * T) / 256 - 1;
+        state_out[e] = side[((size_t)tr_last * 6 + 3 + s) * qkc + ch];
+    }
+}
+
 __global__ void __launch_bounds__(256) epilogue_kernel(int rows, int H, int HD, const float* o, const float* pg,
                                                       const float* rms_w, uint16_t* gated) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -177,7 +255,7 @@ __global__ void bf16_to_f32_kernel(const uint16_t* src, float* dst, long n) {
 }
 
 struct Workspace {
-    float *pq, *pk, *pv, *pg, *pdown, *pbeta, *g, *beta, *o, *q, *k, *cp;
+    float *pq, *pk, *pv, *pg, *pdown, *pbeta, *g, *beta, *o, *q, *k, *cp, *side;
     uint16_t *gated, *wcat, *wup2, *wo, *down2;
     size_t bytes;
 };
@@ -209,6 +287,7 @@ Workspace carve(const kda_layer_desc* d, char* base) {
     w.wo = (uint16_t*)take((size_t)d->d_model * HD * 2);
     w.down2 = (uint16_t*)take(BT * 2 * d->rank * 2);
     w.cp = (float*)take(cp_workspace_bytes(d->B, d->T, d->H, 0));  // the core's context parallelism
+    w.side = (float*)take((BT + 255) / 256 * 6 * 2 * HD * 4);      // raw rows at the q/k product's tile edges
     w.bytes = off;
     return w;
 }
@@ -252,6 +331,9 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
     if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return KDA_ERR_INVALID_ARG;
 
     const int M = d->B * d->T, HD = d->H * D, dm = d->d_model, R = d->rank;
+    // every 256-row tile of the q/k product inside one sequence: the short convolution, SiLU and L2 run
+    // in the product's epilogue and a small kernel finishes the tile-edge rows (else the prologue kernel)
+    const bool fused = d->T % 256 == 0;
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     auto wb = [](const void* p) { return static_cast<const uint16_t*>(p); };
     // weights in the products' [out][in] form: [Wq | Wk | Wv | Wg | Wdown | Wbeta]^T, [Wup^T | Wup^T]
@@ -282,6 +364,17 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
         }
         go.start[6] = ncat;
         go.nseg = 6;
+        if (fused) {  // q and k come out convolved, activated and normalised (but for the tile-edge rows)
+            go.ptr[0] = W.q;
+            go.ptr[1] = W.k;
+            go.epi = kda::GEMM_QKCONV;
+            go.conv_q = w->conv_q;
+            go.conv_k = w->conv_k;
+            go.side = W.side;
+            go.qk_cols = 2 * HD;
+            go.qk_hd = HD;
+            go.eps = EPS;
+        }
         if (kda::launch_gemm_nt(xb, dm, W.wcat, dm, go, true, M, ncat, dm, stream) != hipSuccess) return KDA_ERR_HIP;
     }
     if (kda::launch_split_rows(W.pdown, R, M, R, W.down2, stream) != hipSuccess) return KDA_ERR_HIP;
@@ -306,13 +399,24 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
     pp.state_in = conv_state_in;
     pp.q = W.q; pp.k = W.k; pp.v = nullptr; pp.beta = W.beta;
     const long nw = (long)M * d->H;
-    {
+    if (fused) {
+        FixParams fp;
+        fp.B = d->B; fp.T = d->T; fp.H = d->H; fp.HD = HD;
+        fp.side = W.side; fp.conv_q = w->conv_q; fp.conv_k = w->conv_k; fp.state_in = conv_state_in;
+        fp.pbeta = W.pbeta; fp.q = W.q; fp.k = W.k; fp.beta = W.beta;
+        const long nfw = (long)(M / 256) * 2 * d->H * 3;  // fixup waves
+        fp.fix_blocks = (int)((nfw + 3) / 4);
+        hipLaunchKernelGGL(qk_fixup_kernel, dim3((unsigned)(fp.fix_blocks + 256)), dim3(256), 0, stream, fp);
+        if (conv_state_out)
+            hipLaunchKernelGGL(conv_state_side_kernel, dim3(256), dim3(256), 0, stream, d->B, d->T, HD, W.side,
+                               conv_state_out);
+    } else {
         const long npw = (long)d->B * d->H * ((d->T + PRO_TOK - 1) / PRO_TOK);  // prologue waves
         hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)((npw + 3) / 4)), dim3(256), 0, stream, pp);
+        if (conv_state_out)
+            hipLaunchKernelGGL(conv_state_kernel, dim3(256), dim3(256), 0, stream, d->B, d->T, HD, W.pq, W.pk,
+                               conv_state_in, conv_state_out);
     }
-    if (conv_state_out)
-        hipLaunchKernelGGL(conv_state_kernel, dim3(256), dim3(256), 0, stream, d->B, d->T, HD, W.pq, W.pk,
-                           conv_state_in, conv_state_out);
 
     kda::Params p{};  // zero: every optional field off
     // the core reads q, k, v in float32 (v straight from the projection output): rounding them to

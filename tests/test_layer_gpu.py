@@ -96,3 +96,22 @@ def test_layer_long_ragged_with_state_and_window():
     assert rel_max_bf16_out(y, y_ref) <= TOL_BF16
     assert rel_max(ST, S_ref) <= TOL_BF16
     np.testing.assert_allclose(cs, cs_ref, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("B,T,H", [
+    (2, 512, 3),   # two 256-row tiles per sequence; three heads: one tile holds q head 2 and k head 0
+    (1, 256, 2),   # every tile starts a sequence
+])
+def test_layer_fused_qk_epilogue(B, T, H):
+    """T a multiple of 256: the short convolution, SiLU and L2 of q and k run in the input projection's
+    epilogue, and the rows at tile edges are finished from the raw rows kept beside it (with the
+    incoming window at a sequence start)."""
+    x, p = small(11, B=B, T=T, H=H)
+    rng = np.random.default_rng(12)
+    S0 = (rng.standard_normal((B, H, 128, 128)) * 0.3).astype(np.float32)
+    cs0 = rng.standard_normal((B, 3, 2 * H * 128)).astype(np.float32)
+    y_ref, S_ref, cs_ref = L.forward(x, p, S0=S0, conv_state=cs0)
+    y, ST, cs = run(x, p, S0=S0, cs=cs0)
+    assert rel_max_bf16_out(y, y_ref) <= TOL_BF16
+    assert rel_max(ST, S_ref) <= TOL_BF16
+    np.testing.assert_allclose(cs, cs_ref, rtol=1e-5, atol=1e-5)
