@@ -321,6 +321,8 @@ __device__ __forceinline__ void gemm_tile(Smem& sm, const uint16_t* __restrict__
     char* base = static_cast<char*>(out.ptr[seg]);
     const size_t ld = (size_t)out.ld[seg];
     const bool vec = lim == 4 && (out.ld[seg] & 3) == 0;  // (segment bases are 16-byte aligned)
+    const bool split = OUT_F32 && ((out.split_segs >> seg) & 1);  // (lim == 4 there: checked at launch)
+    const int split_w = out.start[seg + 1] - out.start[seg];
     f32x4 gb = {0.f, 0.f, 0.f, 0.f};
     float ga = 0.f;
     if constexpr (EPI == GEMM_GATE) {  // log decay -5 sigmoid(exp(A_h) (z + b)), head h = column / 128
@@ -349,6 +351,15 @@ __device__ __forceinline__ void gemm_tile(Smem& sm, const uint16_t* __restrict__
                 for (int e = 0; e < 4; ++e) v[e] = -5.f * sigmoid_f(ga * (v[e] + gb[e]));
             }
             if constexpr (OUT_F32) {
+                if (split) {  // bf16 hi in columns [0, W), the remainder in [W, 2W) of the row
+                    uint16_t* dst = reinterpret_cast<uint16_t*>(base) + (size_t)m * ld + c;
+                    uint32_t h01, l01, h23, l23;
+                    split_bf16(v[0], v[1], h01, l01);
+                    split_bf16(v[2], v[3], h23, l23);
+                    *reinterpret_cast<u32x2*>(dst) = u32x2{h01, h23};
+                    *reinterpret_cast<u32x2*>(dst + split_w) = u32x2{l01, l23};
+                    continue;
+                }
                 float* dst = reinterpret_cast<float*>(base) + (size_t)m * ld + c;
                 if (vec) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
                 else for (int e = 0; e < lim; ++e) dst[e] = v[e];
@@ -440,22 +451,6 @@ __global__ void __launch_bounds__(256) transpose_batch_kernel(TransposeBatch bat
     }
 }
 
-// float32 [M][R] (row stride lds) -> bf16 [M][2R]: hi = bf16(x) in columns [0, R), lo = bf16(x - hi) in [R, 2R)
-__global__ void split_rows_kernel(const float* __restrict__ src, int lds, int M, int R, uint16_t* __restrict__ dst) {
-    for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < (long)M * R; e += (long)gridDim.x * blockDim.x) {
-        const long m = e / R, c = e % R;
-        const float x = src[m * lds + c];
-        const uint32_t h = pack_bf16(x, 0.f) & 0xffffu;
-        const uint32_t l = pack_bf16(x - __uint_as_float(h << 16), 0.f) & 0xffffu;
-        dst[m * 2 * R + c] = (uint16_t)h;
-        dst[m * 2 * R + R + c] = (uint16_t)l;
-    }
-}
-
-unsigned grid1(long n) {
-    const long b = (n + 255) / 256;
-    return (unsigned)(b < 1 ? 1 : (b > 8192 ? 8192 : b));
-}
 
 }  // namespace gemm
 
@@ -471,6 +466,12 @@ hipError_t launch_gemm_nt(const uint16_t* A, int lda, const uint16_t* Bt, int ld
             return hipErrorInvalidValue;
     if (out.start[0] != 0 || out.start[out.nseg] < N) return hipErrorInvalidValue;
     if (out.epi == GEMM_GATE && (out.nseg != 1 || !out_f32 || !out.bias || !out.head_scale)) return hipErrorInvalidValue;
+    for (int s = 0; s < out.nseg; ++s)  // hi + lo segments: whole 4-column groups inside N, room for both halves
+        if (((out.split_segs >> s) & 1) &&
+            (!out_f32 || out.start[s + 1] > N || out.ld[s] < 2 * (out.start[s + 1] - out.start[s]) || out.ld[s] % 4 ||
+             (out.epi == GEMM_QKCONV && out.start[s] < out.qk_cols)))
+            return hipErrorInvalidValue;
+    if (out.split_segs >> out.nseg) return hipErrorInvalidValue;
     if (out.epi == GEMM_QKCONV &&
         (!out_f32 || M % BM || out.qk_cols < 128 || out.qk_cols % 128 || out.qk_hd % 128 || out.qk_hd > out.qk_cols ||
          out.qk_cols > N || !out.conv_q || !out.conv_k || !out.side || (reinterpret_cast<uintptr_t>(out.side) & 15)))
@@ -525,10 +526,5 @@ hipError_t launch_transpose_batch(TransposeBatch& b, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_split_rows(const float* src, int lds, int M, int R, uint16_t* dst, hipStream_t stream) {
-    hipLaunchKernelGGL(gemm::split_rows_kernel, dim3(gemm::grid1((long)M * R)), dim3(256), 0, stream, src, lds, M, R,
-                       dst);
-    return hipGetLastError();
-}
 
 }  // namespace kda

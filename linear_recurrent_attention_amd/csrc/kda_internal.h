@@ -101,6 +101,10 @@ struct GemmOut {
     float* side;
     int qk_cols, qk_hd;
     float eps;
+    // bit s: segment s (float32 sums, width W = start[s+1] - start[s]) is written as bf16 hi + lo
+    // halves into ptr[s] (bf16, row stride ld[s] >= 2W): hi = bf16(C) in columns [0, W), lo =
+    // bf16(C - hi) in [W, 2W)
+    int split_segs;
 };
 hipError_t launch_gemm_nt(const uint16_t* A, int lda, const uint16_t* Bt, int ldb, const GemmOut& out, bool out_f32,
                           int M, int N, int K, hipStream_t stream);
@@ -118,8 +122,6 @@ struct TransposeBatch {
     int njobs;
 };
 hipError_t launch_transpose_batch(TransposeBatch& b, hipStream_t stream);
-// float32 [M][R] (row stride lds) -> bf16 [M][2R]: bf16(x) in columns [0, R), bf16(x - that) in [R, 2R)
-hipError_t launch_split_rows(const float* src, int lds, int M, int R, uint16_t* dst, hipStream_t stream);
 // Fused layer decode step (one cooperative launch); see kda_layer_decode.hip.
 struct LayerDecodeParams {
     const uint16_t* x;              // [B*T][dm] bf16

@@ -171,15 +171,30 @@ struct FixParams {
     float* q;               // [B*T, HD]
     float* k;
     float* beta;            // [B*T, H]
-    int fix_blocks;         // workgroups of the row fixups; the rest compute beta
+    float* state_out;       // [B, 3, 2*HD] or null: the outgoing window
+    int fix_blocks;         // workgroups of the row fixups; the rest compute beta and the window
 };
 
 __global__ void __launch_bounds__(256) qk_fixup_kernel(FixParams p) {
     if ((int)blockIdx.x >= p.fix_blocks) {
-        const long n = (long)p.B * p.T * p.H;
+        // beta for every row, then the outgoing window: the last three raw rows of each sequence,
+        // kept in the side buffer by the tile that ends it
+        const long nb = (long)p.B * p.T * p.H;
+        const size_t qkc = 2 * (size_t)p.HD;
+        const long n = nb + (p.state_out ? (long)p.B * 3 * (long)qkc : 0);
         for (long e = (long)(blockIdx.x - p.fix_blocks) * blockDim.x + threadIdx.x; e < n;
-             e += (long)(gridDim.x - p.fix_blocks) * blockDim.x)
-            p.beta[e] = sigmoidf_(p.pbeta[e]);
+             e += (long)(gridDim.x - p.fix_blocks) * blockDim.x) {
+            if (e < nb) {
+                p.beta[e] = sigmoidf_(p.pbeta[e]);
+            } else {
+                const long f = e - nb;
+                const int ch = (int)(f % (long)qkc);
+                const long r = f / (long)qkc;
+                const int s = (int)(r % 3), b = (int)(r / 3);
+                const long tr_last = ((long)(b + 1) * p.T) / 256 - 1;
+                p.state_out[f] = p.side[((size_t)tr_last * 6 + 3 + s) * qkc + ch];
+            }
+        }
         return;
     }
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -219,20 +234,6 @@ __global__ void __launch_bounds__(256) qk_fixup_kernel(FixParams p) {
     *reinterpret_cast<float2*>(dst) = make_float2(y0 * inv, y1 * inv);
 }
 
-// The outgoing window on the fused path: the last three raw rows of each sequence, kept in the side
-// buffer by the tile that ends it.
-__global__ void conv_state_side_kernel(int B, int T, int HD, const float* side, float* state_out) {
-    const size_t qkc = 2 * (size_t)HD;
-    const long n = (long)B * 3 * (long)qkc;
-    for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
-        const int ch = (int)(e % (long)qkc);
-        const long r = e / (long)qkc;
-        const int s = (int)(r % 3), b = (int)(r / 3);
-        const long tr_last = ((long)(b + 1) * T) / 256 - 1;
-        state_out[e] = side[((size_t)tr_last * 6 + 3 + s) * qkc + ch];
-    }
-}
-
 __global__ void __launch_bounds__(256) epilogue_kernel(int rows, int H, int HD, const float* o, const float* pg,
                                                       const float* rms_w, uint16_t* gated) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -255,7 +256,7 @@ __global__ void bf16_to_f32_kernel(const uint16_t* src, float* dst, long n) {
 }
 
 struct Workspace {
-    float *pq, *pk, *pv, *pg, *pdown, *pbeta, *g, *beta, *o, *q, *k, *cp, *side;
+    float *pq, *pk, *pv, *pg, *pbeta, *g, *beta, *o, *q, *k, *cp, *side;
     uint16_t *gated, *wcat, *wup2, *wo, *down2;
     size_t bytes;
 };
@@ -273,7 +274,6 @@ Workspace carve(const kda_layer_desc* d, char* base) {
     w.pk = (float*)take(BT * HD * 4);
     w.pv = (float*)take(BT * HD * 4);
     w.pg = (float*)take(BT * HD * 4);
-    w.pdown = (float*)take(BT * d->rank * 4);
     w.pbeta = (float*)take(BT * d->H * 4);
     w.g = (float*)take(BT * HD * 4);
     w.beta = (float*)take(BT * d->H * 4);
@@ -356,12 +356,14 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
     }
     {
         kda::GemmOut go{};
-        float* dst[6] = {W.pq, W.pk, W.pv, W.pg, W.pdown, W.pbeta};
+        void* dst[6] = {W.pq, W.pk, W.pv, W.pg, W.down2, W.pbeta};
         for (int i = 0; i < 6; ++i) {
             go.ptr[i] = dst[i];
             go.start[i] = noff[i];
             go.ld[i] = wn[i];
         }
+        go.ld[4] = 2 * R;  // the decay-down projection as bf16 [hi | lo] halves, the up-projection's input
+        go.split_segs = 1 << 4;
         go.start[6] = ncat;
         go.nseg = 6;
         if (fused) {  // q and k come out convolved, activated and normalised (but for the tile-edge rows)
@@ -377,7 +379,6 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
         }
         if (kda::launch_gemm_nt(xb, dm, W.wcat, dm, go, true, M, ncat, dm, stream) != hipSuccess) return KDA_ERR_HIP;
     }
-    if (kda::launch_split_rows(W.pdown, R, M, R, W.down2, stream) != hipSuccess) return KDA_ERR_HIP;
     {  // the rank-R up-projection, with the decay gate -5 sigmoid(exp(A_h) (z + b_alpha)) on the way out
         kda::GemmOut go{};
         go.ptr[0] = W.g;
@@ -403,13 +404,10 @@ kda_status kda_layer_fwd(const kda_layer_desc* d, const void* x, const kda_layer
         FixParams fp;
         fp.B = d->B; fp.T = d->T; fp.H = d->H; fp.HD = HD;
         fp.side = W.side; fp.conv_q = w->conv_q; fp.conv_k = w->conv_k; fp.state_in = conv_state_in;
-        fp.pbeta = W.pbeta; fp.q = W.q; fp.k = W.k; fp.beta = W.beta;
+        fp.pbeta = W.pbeta; fp.q = W.q; fp.k = W.k; fp.beta = W.beta; fp.state_out = conv_state_out;
         const long nfw = (long)(M / 256) * 2 * d->H * 3;  // fixup waves
         fp.fix_blocks = (int)((nfw + 3) / 4);
         hipLaunchKernelGGL(qk_fixup_kernel, dim3((unsigned)(fp.fix_blocks + 256)), dim3(256), 0, stream, fp);
-        if (conv_state_out)
-            hipLaunchKernelGGL(conv_state_side_kernel, dim3(256), dim3(256), 0, stream, d->B, d->T, HD, W.side,
-                               conv_state_out);
     } else {
         const long npw = (long)d->B * d->H * ((d->T + PRO_TOK - 1) / PRO_TOK);  // prologue waves
         hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)((npw + 3) / 4)), dim3(256), 0, stream, pp);
