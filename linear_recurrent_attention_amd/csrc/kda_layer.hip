@@ -14,14 +14,19 @@
 //
 // The projections run on the library's bf16 matrix-core GEMM (float32 sums): one product over the
 // concatenated q, k, v, gate, decay-down and beta weights, whose column segments land in separate
-// buffers; the rank-R decay up-projection as a product over [hi | lo] bf16 halves of the float32
-// down-projection (about 16 significant bits), and the output projection.  The weights are taken
-// into the products' [out][in] form in the workspace on each call.  The element-wise work around
-// the core is fused into two kernels, one wave per (token, head) with two channels per lane:
-//   prologue: short conv + SiLU + L2 on q and k, the decay gate, beta (q, k, v stay float32:
-//             the core's float32-input variant reads them, so the per-head RMSNorm does not
-//             amplify a bf16 rounding of the core's inputs);
-//   epilogue: RMSNorm of the core output, times sigmoid(gate), to bf16 for the output projection.
+// buffers (the decay-down one as bf16 hi + lo halves, the up-projection's input); the rank-R decay
+// up-projection as a product over those halves (about 16 significant bits), and the output
+// projection.  The weights are taken into the products' [out][in] form in the workspace on each call.
+// The element-wise work around the core:
+//   T a multiple of 256: the input projection's epilogue applies the short conv, SiLU and L2 to q
+//             and k on all rows but the first three of each 256-row tile; qk_fixup_kernel finishes
+//             those from the raw rows the product kept, computes beta and the outgoing window;
+//   otherwise: prologue_kernel, one wave per (token block, head): short conv + SiLU + L2 on q and
+//             k, beta; conv_state_kernel for the window;
+//   (q, k, v stay float32: the core's float32-input variant reads them, so the per-head RMSNorm does
+//   not amplify a bf16 rounding of the core's inputs);
+//   epilogue_kernel: RMSNorm of the core output, times sigmoid(gate), to bf16 for the output
+//             projection.
 #include "kda_common.h"
 #include "kda_internal.h"
 #include "../../include/kda.h"
