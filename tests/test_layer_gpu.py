@@ -115,3 +115,16 @@ def test_layer_fused_qk_epilogue(B, T, H):
     assert rel_max_bf16_out(y, y_ref) <= TOL_BF16
     assert rel_max(ST, S_ref) <= TOL_BF16
     np.testing.assert_allclose(cs, cs_ref, rtol=1e-5, atol=1e-5)
+
+
+def test_layer_gemm_tail_pieces_partial_rows():
+    """B=2, T=4100, d=256, H=4: the input projection has 33 x 9 = 297 tiles, so its last 41 run as
+    64-row pieces, and the last row tile holds 8 rows (T is not a multiple of 256: prologue path)."""
+    x, p = small(13, B=2, T=4100, d=256, H=4, R=32)
+    rng = np.random.default_rng(14)
+    cs0 = rng.standard_normal((2, 3, 2 * 4 * 128)).astype(np.float32)
+    y_ref, S_ref, cs_ref = L.forward(x, p, conv_state=cs0)
+    y, ST, cs = run(x, p, cs=cs0)
+    assert rel_max_bf16_out(y, y_ref) <= TOL_BF16
+    assert rel_max(ST, S_ref) <= TOL_BF16
+    np.testing.assert_allclose(cs, cs_ref, rtol=1e-5, atol=1e-5)
