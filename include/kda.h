@@ -295,7 +295,8 @@ kda_status kda_layer_fwd(const kda_layer_desc* desc, const void* x, const kda_la
  * call for the projections, the state update and the readout, with a projection-input cache), with
  * the speculative-decoding rollback of section 13.4 (the state is updated in place, so rejected draft
  * tokens cannot be undone from it; each token's projection inputs are cached instead, far fewer
- * numbers than a state).  One cooperative launch, one workgroup per compute unit.
+ * numbers than a state).  Four stream-ordered launches: the input projections, one workgroup per
+ * (sequence, head) for the gates, convolution, recurrence and readout, the output projection, its sum.
  *   desc          : as kda_layer_fwd, with d_model a multiple of 4, rank <= 128, B*T <= 16 rows (else
  *                   KDA_ERR_UNSUPPORTED); flags = 0 or KDA_DECODE_SPECULATIVE
  *   x             : [B, T, d_model] bf16;  y: [B, T, d_model] bf16 (output); both 16-byte aligned
@@ -310,7 +311,7 @@ kda_status kda_layer_fwd(const kda_layer_desc* desc, const void* x, const kda_la
  *   ws            : device workspace of kda_layer_decode_workspace_size(desc) bytes, 256-byte aligned
  * With KDA_DECODE_SPECULATIVE the T tokens are drafts: token t's output is computed as if drafts
  * 0..t-1 were accepted.  Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE or
- * KDA_ERR_HIP (also if the device cannot run the cooperative launch).
+ * KDA_ERR_HIP.
  */
 #define KDA_DECODE_SPECULATIVE 1
 size_t kda_layer_decode_workspace_size(const kda_layer_desc* desc);  /* 0 for an invalid descriptor */

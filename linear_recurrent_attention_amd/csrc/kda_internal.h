@@ -122,7 +122,7 @@ struct TransposeBatch {
     int njobs;
 };
 hipError_t launch_transpose_batch(TransposeBatch& b, hipStream_t stream);
-// Fused layer decode step (one cooperative launch); see kda_layer_decode.hip.
+// Fused layer decode step (four launches); see kda_layer_decode.hip.
 struct LayerDecodeParams {
     const uint16_t* x;              // [B*T][dm] bf16
     const uint16_t* W[6];           // Wq, Wk, Wv, Wg, Wdown, Wbeta ([dm][wn[i]] bf16)
@@ -136,7 +136,6 @@ struct LayerDecodeParams {
     uint16_t* y;                    // [B*T][dm]
     float* cache;                   // planar cache entries or NULL
     float* part;                    // partial sums (layer_decode_part_floats)
-    float* proj;                    // [B*T][noff[6]] projected rows
     float* gated;                   // [B*T][H*D]
     int B, T, H, dm, R, spec;
     float scale;

@@ -466,7 +466,7 @@ size_t decode_cache_floats(const kda_layer_desc* d) {
 }
 
 struct DecodeWs {
-    float *part, *proj, *gated;
+    float *part, *gated;
     size_t bytes;
 };
 DecodeWs carve_decode(const kda_layer_desc* d, char* base) {
@@ -480,7 +480,6 @@ DecodeWs carve_decode(const kda_layer_desc* d, char* base) {
     };
     DecodeWs w;
     w.part = (float*)take(kda::layer_decode_part_floats(M, d->d_model, HD, ntot) * 4);
-    w.proj = (float*)take((size_t)M * ntot * 4);
     w.gated = (float*)take((size_t)M * HD * 4);
     w.bytes = off;
     return w;
@@ -527,7 +526,7 @@ kda_status kda_layer_decode(const kda_layer_desc* d, const void* x, const kda_la
     p.Wo = static_cast<const uint16_t*>(w->Wo);
     p.conv_q = w->conv_q; p.conv_k = w->conv_k; p.b_alpha = w->b_alpha; p.A = w->A; p.rms_w = w->rms_w;
     p.S = S; p.conv = conv_state; p.y = static_cast<uint16_t*>(y); p.cache = cache;
-    p.part = W.part; p.proj = W.proj; p.gated = W.gated;
+    p.part = W.part; p.gated = W.gated;
     p.B = d->B; p.T = d->T; p.H = d->H; p.dm = d->d_model; p.R = R;
     p.spec = (d->flags & KDA_DECODE_SPECULATIVE) ? 1 : 0;
     p.scale = d->scale;

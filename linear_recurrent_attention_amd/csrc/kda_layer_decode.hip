@@ -17,35 +17,33 @@
 // before it were accepted; kda_layer_decode_commit then advances the state and the window over the
 // accepted tokens from their entries, without touching the projections again.
 //
-// One cooperative launch (every workgroup resident) in phases separated by grid barriers:
-//   1. the input projections of the M rows (q, k, v, gate, decay-down, beta weights, as given,
-//      [in][out]): work items of 1024 columns x 64 rows of the weight, partial sums per item, then
-//      (after a barrier) the sums of the partials, one projected row per token;
-//   2. one workgroup per (sequence, head): reads its columns of the projected rows, the decay
-//      up-projection of its head, convolution window, gates, then the recurrence token by token
-//      with the state in registers (thread (column j, half r) holds rows 64r..64r+63 of column j),
-//      readout, RMSNorm and gate; writes the gated output rows, the cache entries and (unless
-//      speculative) the state and window;
-//   3. the output projection of the gated rows, partial sums per item of 16 weight rows;
-//   4. the sum of those partials, to bf16 y.
+// Four launches:
+//   1. ldec_proj_kernel: the input projections of the M rows (q, k, v, gate, decay-down, beta weights,
+//      as given, [in][out]): one workgroup of 16 waves per (64 columns of one weight, half of the
+//      input rows), one column per lane, the rows of x staged in LDS; the 16 waves' sums meet in LDS;
+//   2. ldec_head_kernel, one workgroup per (sequence, head): its columns of the projected rows (the
+//      two halves' sums), the decay up-projection of its head, convolution window, gates, then the
+//      recurrence token by token with the state in registers (thread (column j, half r) holds rows
+//      64r..64r+63 of column j), readout, RMSNorm and gate; writes the gated output rows, the cache
+//      entries and (unless speculative) the state and window;
+//   3. ldec_proj_kernel over the output projection of the gated rows: 64 columns x one eighth of the
+//      rows per workgroup;
+//   4. the sum of those eight partials, to bf16 y.
 // The weights are read once per call, so with a few rows the call is bound by reading them and the
-// state; the products are plain float32 FMAs with the rows of x staged in LDS.
-#include <hip/hip_cooperative_groups.h>
-
+// state; the products are plain float32 FMAs.
 #include "kda_common.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace ldec {
 
-namespace cg = cooperative_groups;
-
 constexpr int D = 128;
 constexpr int NTHR = 256;
-constexpr int KSL1 = 64;   // weight rows per input-projection work item
-constexpr int KSL3 = 16;   // weight rows per output-projection work item
-constexpr int KMAX = 64;
-constexpr int CB = 1024;  // weight columns per projection work item (four per thread)
+constexpr int PT = 1024;   // threads of a projection workgroup (16 waves)
+constexpr int PCOLS = 64;  // weight columns per projection workgroup, one per lane
+constexpr int KCH = 1024;  // input rows staged in LDS at a time
+constexpr int KS1 = 2;     // splits of the input rows: input projections
+constexpr int KS3 = 8;     // splits of the input rows: output projection
 constexpr float EPS = 1e-6f;
 
 __device__ __forceinline__ float bf(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -62,83 +60,55 @@ __device__ __forceinline__ float sum128(float v, float* red) {
     return red[0] + red[1];
 }
 
-// part[(ks * M + m) * ldp + off + n] = sum over rows k of slice ks of in(m, k) * W[k][n], for the
-// four columns n .. n + 3 of each thread.  ROWS: M rounded up to a supported count.  The weight rows
-// are loaded sixteen at a time before they are used, so that each thread keeps sixteen loads in flight.
-template <int ROWS, typename In>
-__device__ void gemv_item(const uint16_t* W_, int nw, bool quad_ok, int k0, int kn, int cb, int M, In in,
-                          float (*xs)[16], float* __restrict__ part, int ks, int ldp, int off) {
-    typedef __attribute__((address_space(1))) const uint16_t g16;
-    typedef __attribute__((address_space(1))) const u32x2 g32x2;
-    g16* W = (g16*)(W_);  // the weights are global memory
-    const int tid = threadIdx.x;
-    __syncthreads();  // the previous item's reads of xs are done
-    for (int e = tid; e < KMAX * 16; e += NTHR) {
-        const int kk = e >> 4, m = e & 15;
-        xs[kk][m] = (m < M && kk < kn) ? in(m, k0 + kk) : 0.f;
-    }
-    __syncthreads();
-    const int n = cb * CB + 4 * tid;
-    if (n >= nw) return;
-    float acc[ROWS][4];
+// part[m * ldp + col0 + c] = sum over k in [k0, k1) of xin(m, k) * W[k][n0 + c] for c < 64 with
+// n0 + c < nw, m < M (M <= 16).  Wave w takes the rows k0 + w, k0 + w + 16, ... with sixteen
+// weight-row loads in flight per lane, lane c one column; the 16 waves' sums meet in LDS and are
+// added in wave order.  xs: [KCH][16] floats; red: [16][16][64] floats.
+template <typename In>
+__device__ void proj_block(const uint16_t* __restrict__ W, int nw, int n0, int k0, int k1, int M, In xin, float* xs,
+                           float* red, float* __restrict__ part, int ldp, int col0) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = min(n0 + lane, nw - 1);  // (a valid column for every lane; the others are not stored)
+    float acc[16];
 #pragma unroll
-    for (int m = 0; m < ROWS; ++m)
+    for (int m = 0; m < 16; ++m) acc[m] = 0.f;
+    for (int kc = k0; kc < k1; kc += KCH) {
+        const int kn = min(KCH, k1 - kc);
+        __syncthreads();  // the previous chunk's reads of xs are done
+        for (int e = tid; e < kn * 16; e += PT) {
+            const int kk = e >> 4, m = e & 15;
+            xs[e] = m < M ? xin(m, kc + kk) : 0.f;
+        }
+        __syncthreads();
+        const uint16_t* wp = W + (size_t)kc * nw + n;
+        for (int kb = wave; kb < kn; kb += 16 * 16) {
+            uint16_t wv[16];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[m][c] = 0.f;
-#define KDA_FMA_ROW(kk, w0, w1, w2, w3)                             \
-    _Pragma("unroll") for (int m = 0; m < ROWS; ++m) {              \
-        const float xv = xs[kk][m];                                 \
-        acc[m][0] = __builtin_fmaf(xv, (w0), acc[m][0]);            \
-        acc[m][1] = __builtin_fmaf(xv, (w1), acc[m][1]);            \
-        acc[m][2] = __builtin_fmaf(xv, (w2), acc[m][2]);            \
-        acc[m][3] = __builtin_fmaf(xv, (w3), acc[m][3]);            \
-    }
-    if (quad_ok && n + 3 < nw) {
-        // four whole columns: 8-byte loads, sixteen rows in flight
-        g16* wp = W + (size_t)k0 * nw + n;
-        for (int kb = 0; kb < kn; kb += 16) {
-            u32x2 v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                v[u] = *reinterpret_cast<g32x2*>(wp + (size_t)min(kb + u, kn - 1) * nw);
+            for (int u = 0; u < 16; ++u) wv[u] = wp[(size_t)min(kb + 16 * u, kn - 1) * nw];
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
-                if (kb + u < kn) {
-                    const float w0 = __uint_as_float(v[u][0] << 16), w1 = __uint_as_float(v[u][0] & 0xffff0000u);
-                    const float w2 = __uint_as_float(v[u][1] << 16), w3 = __uint_as_float(v[u][1] & 0xffff0000u);
-                    KDA_FMA_ROW(kb + u, w0, w1, w2, w3)
+                const int kk = kb + 16 * u;
+                if (kk < kn) {  // (wave-uniform)
+                    const float w = bf(wv[u]);
+                    const f32x4* xr = reinterpret_cast<const f32x4*>(xs + kk * 16);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 xv = xr[q];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[4 * q + e] = __builtin_fmaf(xv[e], w, acc[4 * q + e]);
+                    }
                 }
             }
         }
-    } else {
-        // the ragged edge (or an unaligned matrix): element loads
-        for (int kk = 0; kk < kn; ++kk) {
-            g16* r = W + (size_t)(k0 + kk) * nw + n;
-            const float w0 = bf(r[0]), w1 = n + 1 < nw ? bf(r[1]) : 0.f;
-            const float w2 = n + 2 < nw ? bf(r[2]) : 0.f, w3 = n + 3 < nw ? bf(r[3]) : 0.f;
-            KDA_FMA_ROW(kk, w0, w1, w2, w3)
-        }
     }
-#undef KDA_FMA_ROW
 #pragma unroll
-    for (int m = 0; m < ROWS; ++m) {
-        if (m < M) {
-            float* dst = part + ((size_t)ks * M + m) * ldp + off + n;
+    for (int m = 0; m < 16; ++m) red[(wave * 16 + m) * PCOLS + lane] = acc[m];
+    __syncthreads();
+    const int m = wave, c = lane;  // thread (row m, column c) adds the 16 waves' sums
+    float sum = 0.f;
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (n + c < nw) dst[c] = acc[m][c];
-        }
-    }
-}
-
-template <typename In>
-__device__ void gemv_dispatch(const uint16_t* W, int nw, bool quad_ok, int k0, int kn, int cb, int M, In in,
-                              float (*xs)[16], float* part, int ks, int ldp, int off) {
-    if (M <= 1) gemv_item<1>(W, nw, quad_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
-    else if (M <= 2) gemv_item<2>(W, nw, quad_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
-    else if (M <= 4) gemv_item<4>(W, nw, quad_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
-    else if (M <= 8) gemv_item<8>(W, nw, quad_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
-    else gemv_item<16>(W, nw, quad_ok, k0, kn, cb, M, in, xs, part, ks, ldp, off);
+    for (int w = 0; w < 16; ++w) sum += red[(w * 16 + m) * PCOLS + c];
+    if (m < M && n0 + c < nw) part[(size_t)m * ldp + col0 + c] = sum;
 }
 
 // dst[e .. e+3] = sum over ks < nks of src[ks * stride + e .. +3] for every e = 4i < n (n and stride
@@ -161,7 +131,6 @@ __device__ __forceinline__ void sum_slices4(const float* __restrict__ src, size_
 }
 
 struct Smem {
-    float xs[KMAX][16];
     uint16_t wup[128][D];  // the decay up-projection's columns of this head (rank <= 128)
     float qp[D], kp[D], vv[D], gl[D], q[D], k[D], ga[D], dn[128];
     float cw[2][3][D];  // convolution window of this head: [q/k][oldest..newest][channel]
@@ -170,35 +139,51 @@ struct Smem {
     float beta;
 };
 
-__global__ void __launch_bounds__(NTHR) kda_layer_decode_kernel(LayerDecodeParams p) {
+// Column blocks of 64 of weight i of the input projections.
+__device__ __forceinline__ int nblk(const LayerDecodeParams& p, int i) { return (p.wn[i] + PCOLS - 1) / PCOLS; }
+
+// 1. the input projections: workgroup (column block, row split ks) -> part[ks][m][column]
+__global__ void __launch_bounds__(PT) ldec_proj_kernel(LayerDecodeParams p) {
+    __shared__ float xs[KCH * 16];
+    __shared__ float red[16 * 16 * PCOLS];
+    const int M = p.B * p.T, dm = p.dm;
+    const int ntot = (p.noff[6] + 3) & ~3;  // row length of the partial sums
+    int blk = blockIdx.x / KS1, i = 0;
+    const int ks = blockIdx.x - blk * KS1;
+    while (i < 5 && blk >= nblk(p, i)) { blk -= nblk(p, i); ++i; }  // (workgroup-uniform)
+    const int kper = (dm + KS1 - 1) / KS1, k0 = ks * kper, k1 = min(dm, k0 + kper);
+    proj_block(p.W[i], p.wn[i], PCOLS * blk, k0, k1, M, [&](int m, int k) { return bf(p.x[(size_t)m * dm + k]); },
+               xs, red, p.part + (size_t)ks * M * ntot, ntot, p.noff[i] + PCOLS * blk);
+}
+
+// 3. the output projection of the gated rows: workgroup (column block, row split ks) -> part[ks][m][column]
+__global__ void __launch_bounds__(PT) ldec_out_kernel(LayerDecodeParams p) {
+    __shared__ float xs[KCH * 16];
+    __shared__ float red[16 * 16 * PCOLS];
+    const int M = p.B * p.T, dm = p.dm, HD = p.H * D;
+    const int blk = blockIdx.x / KS3, ks = blockIdx.x - blk * KS3;
+    const int kper = (HD + KS3 - 1) / KS3, k0 = ks * kper, k1 = min(HD, k0 + kper);
+    proj_block(p.Wo, dm, PCOLS * blk, k0, k1, M, [&](int m, int k) { return p.gated[(size_t)m * HD + k]; }, xs, red,
+               p.part + (size_t)ks * M * dm, dm, PCOLS * blk);
+}
+
+// 4. y = bf16(sum of the output projection's partials, in split order)
+__global__ void ldec_sum_kernel(LayerDecodeParams p) {
+    const int M = p.B * p.T, dm = p.dm;
+    sum_slices4(p.part, (size_t)M * dm, KS3, (long)M * dm, [&](long e, f32x4 a) {
+        *reinterpret_cast<u32x2*>(p.y + e) = u32x2{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3])};
+    });
+}
+
+// 2. per (sequence, head): gates, convolution, recurrence, readout, norm
+__global__ void __launch_bounds__(NTHR) ldec_head_kernel(LayerDecodeParams p) {
     __shared__ Smem sm;
-    cg::grid_group grid = cg::this_grid();
     const int tid = threadIdx.x;
-    const int M = p.B * p.T, HD = p.H * D, dm = p.dm, R = p.R;
-    const int ntot = (p.noff[6] + 3) & ~3;  // row length of the partial sums and projected rows
-
-    // ---------------- 1. input projections: partial sums over slices of KSL1 weight rows
-    const int nks1 = (dm + KSL1 - 1) / KSL1;
-    {
-        int items = 0;
-        for (int i = 0; i < 6; ++i) items += ((p.wn[i] + CB - 1) / CB) * nks1;
-        auto xin = [&](int m, int k) { return bf(p.x[(size_t)m * dm + k]); };
-        for (int it = blockIdx.x; it < items; it += gridDim.x) {
-            int i = 0, rem = it;
-            while (rem >= ((p.wn[i] + CB - 1) / CB) * nks1) { rem -= ((p.wn[i] + CB - 1) / CB) * nks1; ++i; }
-            const int cb = rem / nks1, ks = rem - cb * nks1;
-            const int k0 = ks * KSL1, kn = min(KSL1, dm - k0);
-            const bool quad_ok = (p.wn[i] & 3) == 0 && (reinterpret_cast<uintptr_t>(p.W[i]) & 7) == 0;
-            gemv_dispatch(p.W[i], p.wn[i], quad_ok, k0, kn, cb, M, xin, sm.xs, p.part, ks, ntot, p.noff[i]);
-        }
-    }
-    grid.sync();
-    // ---------------- 1b. the projected rows: sums of the slices' partials
-    sum_slices4(p.part, (size_t)M * ntot, nks1, (long)M * ntot,
-                [&](long e, f32x4 a) { *reinterpret_cast<f32x4*>(p.proj + e) = a; });
-    grid.sync();
-
-    // ---------------- 2. per (sequence, head): gates, convolution, recurrence, readout, norm
+    const int M = p.B * p.T, HD = p.H * D, R = p.R;
+    const int ntot = (p.noff[6] + 3) & ~3;
+    // the projected rows: the sum of the input projection's two row-split partials
+    auto proj = [&](int m, int col) { return p.part[(size_t)m * ntot + col] + p.part[((size_t)M + m) * ntot + col]; };
+    static_assert(KS1 == 2, "the head kernel adds two partials");
     for (int bh = blockIdx.x; bh < p.B * p.H; bh += gridDim.x) {
         const int b = bh / p.H, h = bh - b * p.H;
         const int j = tid & (D - 1), rh = tid >> 7;  // state column, row half
@@ -228,12 +213,11 @@ __global__ void __launch_bounds__(NTHR) kda_layer_decode_kernel(LayerDecodeParam
             __syncthreads();  // every read of the previous token's rows (and of the window) is done
             // this token's projected row: q, k (threads 0-127), v, gate (128-255); decay-down; beta
             {
-                const float* pr = p.proj + (size_t)m * ntot;
                 const int c = j, base = rh ? 2 * HD : 0;
-                const float a = pr[base + h * D + c], bb = pr[base + HD + h * D + c];
+                const float a = proj(m, base + h * D + c), bb = proj(m, base + HD + h * D + c);
                 if (rh == 0) { sm.qp[c] = a; sm.kp[c] = bb; } else { sm.vv[c] = a; sm.gl[c] = bb; }
-                for (int r = tid; r < R; r += NTHR) sm.dn[r] = pr[4 * HD + r];
-                if (tid == NTHR - 1) sm.beta = sigm(pr[4 * HD + R + h]);
+                for (int r = tid; r < R; r += NTHR) sm.dn[r] = proj(m, 4 * HD + r);
+                if (tid == NTHR - 1) sm.beta = sigm(proj(m, 4 * HD + R + h));
             }
             __syncthreads();
             // short convolution + SiLU of q (threads 0-127) and k (128-255); decay gate (0-127)
@@ -335,26 +319,6 @@ __global__ void __launch_bounds__(NTHR) kda_layer_decode_kernel(LayerDecodeParam
         }
         __syncthreads();  // the next (sequence, head) rewrites the shared arrays
     }
-    grid.sync();
-
-    // ---------------- 3. output projection of the gated rows: partial sums over slices of KSL3 rows
-    const int nks3 = (HD + KSL3 - 1) / KSL3;
-    {
-        const int items = ((dm + CB - 1) / CB) * nks3;
-        auto gin = [&](int m, int k) { return p.gated[(size_t)m * HD + k]; };
-        const bool quad_ok = (dm & 3) == 0 && (reinterpret_cast<uintptr_t>(p.Wo) & 7) == 0;
-        for (int it = blockIdx.x; it < items; it += gridDim.x) {
-            const int cb = it / nks3, ks = it - cb * nks3;
-            const int k0 = ks * KSL3, kn = min(KSL3, HD - k0);
-            gemv_dispatch(p.Wo, dm, quad_ok, k0, kn, cb, M, gin, sm.xs, p.part, ks, dm, 0);
-        }
-    }
-    grid.sync();
-
-    // ---------------- 4. y = bf16(sum of the partials)
-    sum_slices4(p.part, (size_t)M * dm, nks3, (long)M * dm, [&](long e, f32x4 a) {
-        *reinterpret_cast<u32x2*>(p.y + e) = u32x2{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3])};
-    });
 }
 
 // Advance the convolution window over the first n tokens of the cache: the last 3 of
@@ -381,27 +345,23 @@ __global__ void window_commit_kernel(float* __restrict__ conv, const float* __re
 }  // namespace ldec
 
 size_t layer_decode_part_floats(int M, int dm, int HD, int ntot) {
-    const size_t a = (size_t)((dm + ldec::KSL1 - 1) / ldec::KSL1) * M * ntot;
-    const size_t b = (size_t)((HD + ldec::KSL3 - 1) / ldec::KSL3) * M * dm;
+    (void)HD;
+    const size_t a = (size_t)ldec::KS1 * M * ((ntot + 3) & ~3);
+    const size_t b = (size_t)ldec::KS3 * M * dm;
     return a > b ? a : b;
 }
 
 hipError_t launch_layer_decode(const LayerDecodeParams& p, hipStream_t stream) {
-    int dev = 0, ncu = 0, occ = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(ldec::kda_layer_decode_kernel),
-                                                         ldec::NTHR, 0);
-    if (e != hipSuccess) return e;
-    if (occ < 1 || ncu < 1) return hipErrorLaunchFailure;
-    // one workgroup per compute unit, all resident: every workgroup's barrier fences write back and
-    // invalidate its XCD's L2, so more workgroups per XCD make each grid barrier dearer
-    const dim3 grid((unsigned)ncu), block(ldec::NTHR);
-    LayerDecodeParams pc = p;
-    void* args[] = {&pc};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(ldec::kda_layer_decode_kernel), grid, block, args,
-                                      0, stream);
+    using namespace ldec;
+    int nb = 0;
+    for (int i = 0; i < 6; ++i) nb += (p.wn[i] + PCOLS - 1) / PCOLS;
+    hipLaunchKernelGGL(ldec_proj_kernel, dim3((unsigned)(nb * KS1)), dim3(PT), 0, stream, p);
+    hipLaunchKernelGGL(ldec_head_kernel, dim3((unsigned)(p.B * p.H)), dim3(NTHR), 0, stream, p);
+    hipLaunchKernelGGL(ldec_out_kernel, dim3((unsigned)(((p.dm + PCOLS - 1) / PCOLS) * KS3)), dim3(PT), 0, stream, p);
+    const long n4 = (long)p.B * p.T * p.dm / 4;
+    hipLaunchKernelGGL(ldec_sum_kernel, dim3((unsigned)((n4 + 255) / 256 < 2048 ? (n4 + 255) / 256 : 2048)), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_window_commit(float* conv, const float* qpre, const float* kpre, int B, int T, int HD, int n,
