@@ -20,9 +20,11 @@
 // Four launches:
 //   1. ldec_proj_kernel: the input projections of the M rows (q, k, v, gate, decay-down, beta weights,
 //      as given, [in][out]): one workgroup of 16 waves per (64 columns of one weight, half of the
-//      input rows), one column per lane, the rows of x staged in LDS; the 16 waves' sums meet in LDS;
+//      input rows; a sixteenth for the narrow decay-down and beta weights, so that those add short
+//      workgroups rather than a second round), one column per lane, the rows of x staged in LDS; the
+//      16 waves' sums meet in LDS;
 //   2. ldec_head_kernel, one workgroup per (sequence, head): its columns of the projected rows (the
-//      two halves' sums), the decay up-projection of its head, convolution window, gates, then the
+//      partials' sums), the decay up-projection of its head, convolution window, gates, then the
 //      recurrence token by token with the state in registers (thread (column j, half r) holds rows
 //      64r..64r+63 of column j), readout, RMSNorm and gate; writes the gated output rows, the cache
 //      entries and (unless speculative) the state and window;
@@ -42,7 +44,9 @@ constexpr int NTHR = 256;
 constexpr int PT = 1024;   // threads of a projection workgroup (16 waves)
 constexpr int PCOLS = 64;  // weight columns per projection workgroup, one per lane
 constexpr int KCH = 1024;  // input rows staged in LDS at a time
-constexpr int KS1 = 2;     // splits of the input rows: input projections
+constexpr int NLD = 32;    // weight rows in flight per lane
+constexpr int KS1 = 2;     // splits of the input rows: input projections of q, k, v, gate
+constexpr int KSB = 16;    // splits of the input rows: input projections of decay-down and beta
 constexpr int KS3 = 8;     // splits of the input rows: output projection
 constexpr float EPS = 1e-6f;
 
@@ -61,13 +65,13 @@ __device__ __forceinline__ float sum128(float v, float* red) {
 }
 
 // part[m * ldp + col0 + c] = sum over k in [k0, k1) of xin(m, k) * W[k][n0 + c] for c < 64 with
-// n0 + c < nw, m < M (M <= 16).  Wave w takes the rows k0 + w, k0 + w + 16, ... with sixteen
+// n0 + c < nw, m < M (M <= 16).  Wave w takes the rows k0 + w, k0 + w + 16, ... with up to NLD
 // weight-row loads in flight per lane, lane c one column; the 16 waves' sums meet in LDS and are
 // added in wave order.  xs: [KCH][16] floats; red: [16][16][64] floats.
 template <typename In>
 __device__ void proj_block(const uint16_t* __restrict__ W, int nw, int n0, int k0, int k1, int M, In xin, float* xs,
                            float* red, float* __restrict__ part, int ldp, int col0) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = min(n0 + lane, nw - 1);  // (a valid column for every lane; the others are not stored)
     float acc[16];
 #pragma unroll
@@ -75,18 +79,28 @@ __device__ void proj_block(const uint16_t* __restrict__ W, int nw, int n0, int k
     for (int kc = k0; kc < k1; kc += KCH) {
         const int kn = min(KCH, k1 - kc);
         __syncthreads();  // the previous chunk's reads of xs are done
-        for (int e = tid; e < kn * 16; e += PT) {
-            const int kk = e >> 4, m = e & 15;
-            xs[e] = m < M ? xin(m, kc + kk) : 0.f;
+        {  // consecutive threads read consecutive elements of a row of x; all of a thread's loads in flight
+            constexpr int SU = KCH * 16 / PT;
+            float xv[SU];
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int e = tid + u * PT, m = e / kn, kk = e - m * kn;
+                xv[u] = e < kn * 16 && m < M ? xin(m, kc + kk) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int e = tid + u * PT, m = e / kn, kk = e - m * kn;
+                if (e < kn * 16) xs[kk * 16 + m] = xv[u];
+            }
         }
         __syncthreads();
-        const uint16_t* wp = W + (size_t)kc * nw + n;
-        for (int kb = wave; kb < kn; kb += 16 * 16) {
-            uint16_t wv[16];
+        for (int kb = wave; kb < kn; kb += 16 * NLD) {
+            uint16_t wv[NLD];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) wv[u] = wp[(size_t)min(kb + 16 * u, kn - 1) * nw];
+            for (int u = 0; u < NLD; ++u)  // a wave-uniform row base plus the lane's column
+                if (kb + 16 * u < kn) wv[u] = (W + (size_t)(kc + kb + 16 * u) * nw)[n];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
+            for (int u = 0; u < NLD; ++u) {
                 const int kk = kb + 16 * u;
                 if (kk < kn) {  // (wave-uniform)
                     const float w = bf(wv[u]);
@@ -143,15 +157,25 @@ struct Smem {
 __device__ __forceinline__ int nblk(const LayerDecodeParams& p, int i) { return (p.wn[i] + PCOLS - 1) / PCOLS; }
 
 // 1. the input projections: workgroup (column block, row split ks) -> part[ks][m][column]
+// Workgroups: first the narrow decay-down and beta weights (their column blocks x KSB row splits, short
+// and dispatched first), then q, k, v, gate (column blocks x KS1 row splits).
+__device__ __forceinline__ int small_units(const LayerDecodeParams& p) { return (nblk(p, 4) + nblk(p, 5)) * KSB; }
+
 __global__ void __launch_bounds__(PT) ldec_proj_kernel(LayerDecodeParams p) {
     __shared__ float xs[KCH * 16];
     __shared__ float red[16 * 16 * PCOLS];
     const int M = p.B * p.T, dm = p.dm;
     const int ntot = (p.noff[6] + 3) & ~3;  // row length of the partial sums
-    int blk = blockIdx.x / KS1, i = 0;
-    const int ks = blockIdx.x - blk * KS1;
-    while (i < 5 && blk >= nblk(p, i)) { blk -= nblk(p, i); ++i; }  // (workgroup-uniform)
-    const int kper = (dm + KS1 - 1) / KS1, k0 = ks * kper, k1 = min(dm, k0 + kper);
+    const int nsmall = small_units(p);
+    int blk, i, ks, nks;
+    if ((int)blockIdx.x < nsmall) {
+        blk = blockIdx.x / KSB; ks = blockIdx.x - blk * KSB; nks = KSB; i = 4;
+        if (blk >= nblk(p, 4)) { blk -= nblk(p, 4); i = 5; }
+    } else {
+        blk = (blockIdx.x - nsmall) / KS1; ks = (blockIdx.x - nsmall) - blk * KS1; nks = KS1; i = 0;
+        while (i < 3 && blk >= nblk(p, i)) { blk -= nblk(p, i); ++i; }  // (workgroup-uniform)
+    }
+    const int kper = (dm + nks - 1) / nks, k0 = min(dm, ks * kper), k1 = min(dm, k0 + kper);
     proj_block(p.W[i], p.wn[i], PCOLS * blk, k0, k1, M, [&](int m, int k) { return bf(p.x[(size_t)m * dm + k]); },
                xs, red, p.part + (size_t)ks * M * ntot, ntot, p.noff[i] + PCOLS * blk);
 }
@@ -181,29 +205,81 @@ __global__ void __launch_bounds__(NTHR) ldec_head_kernel(LayerDecodeParams p) {
     const int tid = threadIdx.x;
     const int M = p.B * p.T, HD = p.H * D, R = p.R;
     const int ntot = (p.noff[6] + 3) & ~3;
-    // the projected rows: the sum of the input projection's two row-split partials
-    auto proj = [&](int m, int col) { return p.part[(size_t)m * ntot + col] + p.part[((size_t)M + m) * ntot + col]; };
-    static_assert(KS1 == 2, "the head kernel adds two partials");
+    // the projected rows: the sums of the input projection's row-split partials (KS1 of them for q,
+    // k, v, gate, KSB for decay-down and beta), in split order
+    auto psum = [&](int m, int col, auto nks) {  // nks partials, all loads issued together
+        float v[decltype(nks)::value];
+#pragma unroll
+        for (int s = 0; s < decltype(nks)::value; ++s) v[s] = p.part[((size_t)s * M + m) * ntot + col];
+        float r = 0.f;
+#pragma unroll
+        for (int s = 0; s < decltype(nks)::value; ++s) r += v[s];
+        return r;
+    };
+    auto proj = [&](int m, int col) { return psum(m, col, std::integral_constant<int, KS1>{}); };      // q, k, v, gate
+    auto proj_small = [&](int m, int col) { return psum(m, col, std::integral_constant<int, KSB>{}); };  // decay-down, beta
     for (int bh = blockIdx.x; bh < p.B * p.H; bh += gridDim.x) {
         const int b = bh / p.H, h = bh - b * p.H;
         const int j = tid & (D - 1), rh = tid >> 7;  // state column, row half
+        const int hc = h * D + j;
+        // Every global load that does not depend on the token is issued here, together, so that the
+        // head pays about one memory round trip before its first token: this thread's convolution taps,
+        // decay bias and RMSNorm weight, the state, the window, the up-projection's columns of this
+        // head, and the first token's projected values.
+        float taps[4];
+        {
+            const float* tp = (rh ? p.conv_k : p.conv_q) + (size_t)hc * 4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) taps[u] = tp[u];
+        }
+        const float balpha = rh == 0 ? p.b_alpha[hc] : 0.f;
+        const float rw = p.rms_w[j];
+        const float ea = fexp(p.A[h]);
         float s[64];
         {
             const float* Sb = p.S + (size_t)bh * D * D + (size_t)(64 * rh) * D + j;
 #pragma unroll
             for (int i = 0; i < 64; ++i) s[i] = p.S ? Sb[(size_t)i * D] : 0.f;
         }
-        for (int e = tid; e < 2 * 3 * D; e += NTHR) {
-            const int qk = e / (3 * D), r = (e / D) % 3, c = e % D;
-            sm.cw[qk][r][c] = p.conv ? p.conv[((size_t)b * 3 + r) * 2 * HD + qk * HD + h * D + c] : 0.f;
+        float cwv[3];
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int e = tid + u * NTHR, qk = e / (3 * D), r = (e / D) % 3, c = e % D;
+            cwv[u] = p.conv ? p.conv[((size_t)b * 3 + r) * 2 * HD + qk * HD + h * D + c] : 0.f;
         }
-        const float ea = fexp(p.A[h]);
-        // this head's columns of the decay up-projection, 16 bytes per load
-        if ((reinterpret_cast<uintptr_t>(p.Wup) & 15) == 0) {
-            for (int e = tid; e < R * (D / 8); e += NTHR) {
-                const int r = e >> 4, c8 = 8 * (e & 15);
-                *reinterpret_cast<u32x4*>(&sm.wup[r][c8]) =
-                    *reinterpret_cast<const u32x4*>(p.Wup + (size_t)r * HD + h * D + c8);
+        static_assert(2 * 3 * D == 3 * NTHR, "three window values per thread");
+        const bool wal = (reinterpret_cast<uintptr_t>(p.Wup) & 15) == 0;  // 16-byte loads of the up-projection
+        u32x4 wv[128 * (D / 8) / NTHR];  // rank <= 128
+        if (wal) {
+#pragma unroll
+            for (int u = 0; u < 128 * (D / 8) / NTHR; ++u) {
+                const int e = tid + u * NTHR;
+                if (e < R * (D / 8)) wv[u] = *reinterpret_cast<const u32x4*>(p.Wup + (size_t)(e >> 4) * HD + h * D + 8 * (e & 15));
+            }
+        }
+        // this token's projected values: q, k (threads 0-127) or v, gate (128-255) of column j;
+        // decay-down column tid (tid < R); beta (the last thread)
+        struct Tok { float a, bb, dn, beta; };
+        auto fetch = [&](int t) {
+            const int m = b * p.T + t, base = rh ? 2 * HD : 0;
+            Tok v;
+            v.a = proj(m, base + hc);
+            v.bb = proj(m, base + HD + hc);
+            v.dn = tid < R ? proj_small(m, 4 * HD + tid) : 0.f;
+            v.beta = tid == NTHR - 1 ? proj_small(m, 4 * HD + R + h) : 0.f;
+            return v;
+        };
+        Tok cur = fetch(0);
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int e = tid + u * NTHR;
+            sm.cw[e / (3 * D)][(e / D) % 3][e % D] = cwv[u];
+        }
+        if (wal) {
+#pragma unroll
+            for (int u = 0; u < 128 * (D / 8) / NTHR; ++u) {
+                const int e = tid + u * NTHR;
+                if (e < R * (D / 8)) *reinterpret_cast<u32x4*>(&sm.wup[e >> 4][8 * (e & 15)]) = wv[u];
             }
         } else {
             for (int e = tid; e < R * D; e += NTHR) sm.wup[e >> 7][e & 127] = p.Wup[(size_t)(e >> 7) * HD + h * D + (e & 127)];
@@ -211,26 +287,21 @@ __global__ void __launch_bounds__(NTHR) ldec_head_kernel(LayerDecodeParams p) {
         for (int t = 0; t < p.T; ++t) {
             const int m = b * p.T + t;
             __syncthreads();  // every read of the previous token's rows (and of the window) is done
-            // this token's projected row: q, k (threads 0-127), v, gate (128-255); decay-down; beta
-            {
-                const int c = j, base = rh ? 2 * HD : 0;
-                const float a = proj(m, base + h * D + c), bb = proj(m, base + HD + h * D + c);
-                if (rh == 0) { sm.qp[c] = a; sm.kp[c] = bb; } else { sm.vv[c] = a; sm.gl[c] = bb; }
-                for (int r = tid; r < R; r += NTHR) sm.dn[r] = proj(m, 4 * HD + r);
-                if (tid == NTHR - 1) sm.beta = sigm(proj(m, 4 * HD + R + h));
-            }
+            if (rh == 0) { sm.qp[j] = cur.a; sm.kp[j] = cur.bb; } else { sm.vv[j] = cur.a; sm.gl[j] = cur.bb; }
+            if (tid < R) sm.dn[tid] = cur.dn;
+            if (tid == NTHR - 1) sm.beta = sigm(cur.beta);
+            if (t + 1 < p.T) cur = fetch(t + 1);  // in flight during this token's work
             __syncthreads();
             // short convolution + SiLU of q (threads 0-127) and k (128-255); decay gate (0-127)
             float act;
             {
-                const int c = j, hc = h * D + c;
-                const float* taps = (rh ? p.conv_k : p.conv_q) + (size_t)hc * 4;
+                const int c = j;
                 const float xcur = rh ? sm.kp[c] : sm.qp[c];
                 const float y = taps[0] * sm.cw[rh][0][c] + taps[1] * sm.cw[rh][1][c] + taps[2] * sm.cw[rh][2][c] +
                                 taps[3] * xcur;
                 act = y * sigm(y);
                 if (rh == 0) {
-                    float z[4] = {p.b_alpha[hc], 0.f, 0.f, 0.f};
+                    float z[4] = {balpha, 0.f, 0.f, 0.f};
                     int r = 0;
                     for (; r + 4 <= R; r += 4) {
 #pragma unroll
@@ -300,7 +371,7 @@ __global__ void __launch_bounds__(NTHR) ldec_head_kernel(LayerDecodeParams p) {
                 const float ot = (sm.po[0][j] + sm.po[1][j]) * p.scale;
                 const float ss = sum128(rh == 0 ? ot * ot : 0.f, sm.red);
                 if (rh == 0) {
-                    const float on = ot / sqrtf(ss * (1.f / D) + EPS) * p.rms_w[j] * sigm(sm.gl[j]);
+                    const float on = ot / sqrtf(ss * (1.f / D) + EPS) * rw * sigm(sm.gl[j]);
                     p.gated[(size_t)m * HD + h * D + j] = on;
                 }
             }
@@ -346,16 +417,17 @@ __global__ void window_commit_kernel(float* __restrict__ conv, const float* __re
 
 size_t layer_decode_part_floats(int M, int dm, int HD, int ntot) {
     (void)HD;
-    const size_t a = (size_t)ldec::KS1 * M * ((ntot + 3) & ~3);
+    const size_t a = (size_t)ldec::KSB * M * ((ntot + 3) & ~3);
     const size_t b = (size_t)ldec::KS3 * M * dm;
     return a > b ? a : b;
 }
 
 hipError_t launch_layer_decode(const LayerDecodeParams& p, hipStream_t stream) {
     using namespace ldec;
-    int nb = 0;
-    for (int i = 0; i < 6; ++i) nb += (p.wn[i] + PCOLS - 1) / PCOLS;
-    hipLaunchKernelGGL(ldec_proj_kernel, dim3((unsigned)(nb * KS1)), dim3(PT), 0, stream, p);
+    int nbig = 0;
+    for (int i = 0; i < 4; ++i) nbig += (p.wn[i] + PCOLS - 1) / PCOLS;
+    const int nsmall = ((p.wn[4] + PCOLS - 1) / PCOLS + (p.wn[5] + PCOLS - 1) / PCOLS) * KSB;
+    hipLaunchKernelGGL(ldec_proj_kernel, dim3((unsigned)(nsmall + nbig * KS1)), dim3(PT), 0, stream, p);
     hipLaunchKernelGGL(ldec_head_kernel, dim3((unsigned)(p.B * p.H)), dim3(NTHR), 0, stream, p);
     hipLaunchKernelGGL(ldec_out_kernel, dim3((unsigned)(((p.dm + PCOLS - 1) / PCOLS) * KS3)), dim3(PT), 0, stream, p);
     const long n4 = (long)p.B * p.T * p.dm / 4;
