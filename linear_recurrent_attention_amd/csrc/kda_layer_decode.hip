@@ -33,6 +33,8 @@
 //   4. the sum of those eight partials, to bf16 y.
 // The weights are read once per call, so with a few rows the call is bound by reading them and the
 // state; the products are plain float32 FMAs.
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -41,13 +43,11 @@ namespace ldec {
 
 constexpr int D = 128;
 constexpr int NTHR = 256;
-constexpr int PT = 1024;   // threads of a projection workgroup (16 waves)
-constexpr int PCOLS = 64;  // weight columns per projection workgroup, one per lane
-constexpr int KCH = 1024;  // input rows staged in LDS at a time
-constexpr int NLD = 32;    // weight rows in flight per lane
-constexpr int KS1 = 2;     // splits of the input rows: input projections of q, k, v, gate
-constexpr int KSB = 16;    // splits of the input rows: input projections of decay-down and beta
-constexpr int KS3 = 8;     // splits of the input rows: output projection
+constexpr int MW = 8;        // waves of a projection workgroup
+constexpr int MT = 64 * MW;  // its threads
+constexpr int MCOLS = 128;   // weight columns per projection workgroup: 8 per lane, 16 lanes
+constexpr int KS1 = 3;       // splits of the input rows: input projections (66 x 3 workgroups at H = 16)
+constexpr int KS3 = 8;       // splits of the input rows: output projection
 constexpr float EPS = 1e-6f;
 
 __device__ __forceinline__ float bf(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -64,66 +64,145 @@ __device__ __forceinline__ float sum128(float v, float* red) {
     return red[0] + red[1];
 }
 
-// part[m * ldp + col0 + c] = sum over k in [k0, k1) of xin(m, k) * W[k][n0 + c] for c < 64 with
-// n0 + c < nw, m < M (M <= 16).  Wave w takes the rows k0 + w, k0 + w + 16, ... with up to NLD
-// weight-row loads in flight per lane, lane c one column; the 16 waves' sums meet in LDS and are
-// added in wave order.  xs: [KCH][16] floats; red: [16][16][64] floats.
-template <typename In>
-__device__ void proj_block(const uint16_t* __restrict__ W, int nw, int n0, int k0, int k1, int M, In xin, float* xs,
-                           float* red, float* __restrict__ part, int ldp, int col0) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = min(n0 + lane, nw - 1);  // (a valid column for every lane; the others are not stored)
-    float acc[16];
+// Rows k..k+7, columns n..n+7 of a [K][nw] bf16 weight as eight 16-byte rows (zeros past row k1 or
+// column nw).  vec: 16-byte loads (nw a multiple of 8, W 16-byte aligned).
+__device__ __forceinline__ void load_w8(const uint16_t* __restrict__ W, int nw, int k1, int k, int n, bool vec,
+                                        u32x4 (&r)[8]) {
+    if (vec && n + 8 <= nw) {
 #pragma unroll
-    for (int m = 0; m < 16; ++m) acc[m] = 0.f;
-    for (int kc = k0; kc < k1; kc += KCH) {
-        const int kn = min(KCH, k1 - kc);
-        __syncthreads();  // the previous chunk's reads of xs are done
-        {  // consecutive threads read consecutive elements of a row of x; all of a thread's loads in flight
-            constexpr int SU = KCH * 16 / PT;
-            float xv[SU];
-#pragma unroll
-            for (int u = 0; u < SU; ++u) {
-                const int e = tid + u * PT, m = e / kn, kk = e - m * kn;
-                xv[u] = e < kn * 16 && m < M ? xin(m, kc + kk) : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < SU; ++u) {
-                const int e = tid + u * PT, m = e / kn, kk = e - m * kn;
-                if (e < kn * 16) xs[kk * 16 + m] = xv[u];
-            }
+        for (int i = 0; i < 8; ++i) {
+            r[i] = u32x4{0u, 0u, 0u, 0u};
+            if (k + i < k1) r[i] = *reinterpret_cast<const u32x4*>(W + (size_t)(k + i) * nw + n);
         }
-        __syncthreads();
-        for (int kb = wave; kb < kn; kb += 16 * NLD) {
-            uint16_t wv[NLD];
+    } else {
 #pragma unroll
-            for (int u = 0; u < NLD; ++u)  // a wave-uniform row base plus the lane's column
-                if (kb + 16 * u < kn) wv[u] = (W + (size_t)(kc + kb + 16 * u) * nw)[n];
+        for (int i = 0; i < 8; ++i) {
+            uint32_t w[8];
 #pragma unroll
-            for (int u = 0; u < NLD; ++u) {
-                const int kk = kb + 16 * u;
-                if (kk < kn) {  // (wave-uniform)
-                    const float w = bf(wv[u]);
-                    const f32x4* xr = reinterpret_cast<const f32x4*>(xs + kk * 16);
+            for (int c = 0; c < 8; ++c) w[c] = k + i < k1 && n + c < nw ? W[(size_t)(k + i) * nw + n + c] : 0u;
+            r[i] = u32x4{w[0] | w[1] << 16, w[2] | w[3] << 16, w[4] | w[5] << 16, w[6] | w[7] << 16};
+        }
+    }
+}
+
+// Column c of an 8 x 8 bf16 block held as eight rows: its eight elements in row order, two per word
+// (the operand layout of one lane of a 16x16x32 product: contraction indices 8g .. 8g+7).
+template <int c>
+__device__ __forceinline__ u32x4 col8(const u32x4 (&r)[8]) {
+    u32x4 o;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 xv = xr[q];
+    for (int kp = 0; kp < 4; ++kp) {
+        const uint32_t a = r[2 * kp][c >> 1], b = r[2 * kp + 1][c >> 1];
+        o[kp] = (c & 1) ? (a >> 16) | (b & 0xffff0000u) : (a & 0xffffu) | (b << 16);
+    }
+    return o;
+}
+
+// Elements k..k+7 of row m of x (zeros past column k1 or row M): bf16 x as is; float32 x as bf16
+// hi + lo halves (x = hi + lo to about 2^-17 relative).
+__device__ __forceinline__ void load_x8(const uint16_t* __restrict__ x, int ldx, int M, int k1, int m, int k,
+                                        bool vec, u32x4& hi, u32x4&) {
+    hi = u32x4{0u, 0u, 0u, 0u};
+    if (m >= M) return;
+    if (vec && k + 8 <= k1) {
+        hi = *reinterpret_cast<const u32x4*>(x + (size_t)m * ldx + k);
+    } else {
+        uint32_t w[8];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[4 * q + e] = __builtin_fmaf(xv[e], w, acc[4 * q + e]);
-                    }
-                }
-            }
+        for (int c = 0; c < 8; ++c) w[c] = k + c < k1 ? x[(size_t)m * ldx + k + c] : 0u;
+        hi = u32x4{w[0] | w[1] << 16, w[2] | w[3] << 16, w[4] | w[5] << 16, w[6] | w[7] << 16};
+    }
+}
+__device__ __forceinline__ void load_x8(const float* __restrict__ x, int ldx, int M, int k1, int m, int k, bool vec,
+                                        u32x4& hi, u32x4& lo) {
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = 0.f;
+    if (m < M) {
+        if (vec && k + 8 <= k1) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(x + (size_t)m * ldx + k);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(x + (size_t)m * ldx + k + 4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) { v[c] = a[c]; v[4 + c] = b[c]; }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) v[c] = k + c < k1 ? x[(size_t)m * ldx + k + c] : 0.f;
         }
     }
 #pragma unroll
-    for (int m = 0; m < 16; ++m) red[(wave * 16 + m) * PCOLS + lane] = acc[m];
-    __syncthreads();
-    const int m = wave, c = lane;  // thread (row m, column c) adds the 16 waves' sums
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < 16; ++w) sum += red[(w * 16 + m) * PCOLS + c];
-    if (m < M && n0 + c < nw) part[(size_t)m * ldp + col0 + c] = sum;
+    for (int i = 0; i < 4; ++i) {
+        uint32_t h, l;
+        split_bf16(v[2 * i], v[2 * i + 1], h, l);
+        hi[i] = h;
+        lo[i] = l;
+    }
 }
+
+// part[m * ldp + col0 + c] = sum over k in [k0, k1) of x[m][k] * W[k][n0 + c] for c < 128 with
+// n0 + c < nw, m < M (M <= 16), on the matrix cores (16x16x32 bf16, float32 sums).  Lane (l16, g)
+// of a wave reads weight rows k + 8g .. k + 8g + 7, columns n0 + 8 l16 .. + 7 (one 16-byte load per
+// row, coalesced along the rows) for each 32-row step k, and transposes that 8 x 8 block in
+// registers into the operands of eight products, product c covering columns n0 + 8j + c (j < 16),
+// with x's rows as the other operand; a float32 x takes two products, its bf16 hi and lo halves.
+// Wave w takes the steps w, w + 8, ..., NB at a time in flight; the waves' sums meet in LDS and
+// are added in wave order.  red: [8][16][128] floats.
+template <int NB, typename X>
+__device__ void mproj_block(const uint16_t* __restrict__ W, int nw, int n0, int k0, int k1, int M,
+                            const X* __restrict__ x, int ldx, float* red, float* __restrict__ part, int ldp, int col0) {
+    constexpr bool XF32 = sizeof(X) == 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
+    const int n = n0 + 8 * l16;
+    const bool wvec = (nw & 7) == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0;
+    const bool xvec = (ldx & 7) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+    f32x4 acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto step = [&](const u32x4 (&r)[8], u32x4 xh, u32x4 xl) {  // columns in word order, so that the
+        auto one = [&](auto cc) {                                     // rows' words die as they are used
+            constexpr int c = decltype(cc)::value;
+            const u32x4 b = col8<c>(r);
+            acc[c] = mfma_bf16(xh, b, acc[c]);
+            if constexpr (XF32) acc[c] = mfma_bf16(xl, b, acc[c]);
+        };
+        one(std::integral_constant<int, 0>{}); one(std::integral_constant<int, 1>{});
+        one(std::integral_constant<int, 2>{}); one(std::integral_constant<int, 3>{});
+        one(std::integral_constant<int, 4>{}); one(std::integral_constant<int, 5>{});
+        one(std::integral_constant<int, 6>{}); one(std::integral_constant<int, 7>{});
+    };
+    const int nsteps = (k1 - k0 + 31) / 32;
+    for (int s0 = wave; s0 < nsteps; s0 += NB * MW) {
+        u32x4 r[NB][8], xh[NB], xl[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+            if (s0 + u * MW < nsteps) load_w8(W, nw, k1, k0 + 32 * (s0 + u * MW) + 8 * g, n, wvec, r[u]);  // (wave-uniform)
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+            if (s0 + u * MW < nsteps) load_x8(x, ldx, M, k1, l16, k0 + 32 * (s0 + u * MW) + 8 * g, xvec, xh[u], xl[u]);
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+            if (s0 + u * MW < nsteps) step(r[u], xh[u], xl[u]);
+    }
+    // lane (l16, g) holds rows 4g .. 4g+3 (element e of each product), columns n0 + 8 l16 + c
+    float* rw = red + wave * (16 * MCOLS);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float* row = rw + (4 * g + e) * MCOLS + 8 * l16;
+        *reinterpret_cast<f32x4*>(row) = f32x4{acc[0][e], acc[1][e], acc[2][e], acc[3][e]};
+        *reinterpret_cast<f32x4*>(row + 4) = f32x4{acc[4][e], acc[5][e], acc[6][e], acc[7][e]};
+    }
+    __syncthreads();
+    const int m = tid >> 5, c4 = 4 * (tid & 31);  // thread: row m, columns c4 .. c4+3
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < MW; ++w) v += *reinterpret_cast<const f32x4*>(red + (w * 16 + m) * MCOLS + c4);
+    if (m < M) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n0 + c4 + e < nw) part[(size_t)m * ldp + col0 + c4 + e] = v[e];
+    }
+}
+static_assert(MT == 16 * (MCOLS / 4), "one thread per (row, 4 columns) in the reduction");
 
 // dst[e .. e+3] = sum over ks < nks of src[ks * stride + e .. +3] for every e = 4i < n (n and stride
 // multiples of 4), grid-stride; the slices are read sixteen at a time, all in flight together
@@ -153,42 +232,32 @@ struct Smem {
     float beta;
 };
 
-// Column blocks of 64 of weight i of the input projections.
-__device__ __forceinline__ int nblk(const LayerDecodeParams& p, int i) { return (p.wn[i] + PCOLS - 1) / PCOLS; }
+// Column blocks of weight i of the input projections.
+__device__ __forceinline__ int nblk(const LayerDecodeParams& p, int i) { return (p.wn[i] + MCOLS - 1) / MCOLS; }
 
-// 1. the input projections: workgroup (column block, row split ks) -> part[ks][m][column]
-// Workgroups: first the narrow decay-down and beta weights (their column blocks x KSB row splits, short
-// and dispatched first), then q, k, v, gate (column blocks x KS1 row splits).
-__device__ __forceinline__ int small_units(const LayerDecodeParams& p) { return (nblk(p, 4) + nblk(p, 5)) * KSB; }
+// Rows of x per split of k: a multiple of the 32-row step
+__host__ __device__ __forceinline__ int split_rows(int K, int nks) { return ((K + nks - 1) / nks + 31) & ~31; }
 
-__global__ void __launch_bounds__(PT) ldec_proj_kernel(LayerDecodeParams p) {
-    __shared__ float xs[KCH * 16];
-    __shared__ float red[16 * 16 * PCOLS];
+// 1. the input projections: workgroup (column block of weight i, row split ks) -> part[ks][m][column]
+__global__ void __launch_bounds__(MT) ldec_proj_kernel(LayerDecodeParams p) {
+    __shared__ float red[MW * 16 * MCOLS];
     const int M = p.B * p.T, dm = p.dm;
     const int ntot = (p.noff[6] + 3) & ~3;  // row length of the partial sums
-    const int nsmall = small_units(p);
-    int blk, i, ks, nks;
-    if ((int)blockIdx.x < nsmall) {
-        blk = blockIdx.x / KSB; ks = blockIdx.x - blk * KSB; nks = KSB; i = 4;
-        if (blk >= nblk(p, 4)) { blk -= nblk(p, 4); i = 5; }
-    } else {
-        blk = (blockIdx.x - nsmall) / KS1; ks = (blockIdx.x - nsmall) - blk * KS1; nks = KS1; i = 0;
-        while (i < 3 && blk >= nblk(p, i)) { blk -= nblk(p, i); ++i; }  // (workgroup-uniform)
-    }
-    const int kper = (dm + nks - 1) / nks, k0 = min(dm, ks * kper), k1 = min(dm, k0 + kper);
-    proj_block(p.W[i], p.wn[i], PCOLS * blk, k0, k1, M, [&](int m, int k) { return bf(p.x[(size_t)m * dm + k]); },
-               xs, red, p.part + (size_t)ks * M * ntot, ntot, p.noff[i] + PCOLS * blk);
+    int blk = blockIdx.x / KS1, i = 0;
+    const int ks = blockIdx.x - blk * KS1;
+    while (i < 5 && blk >= nblk(p, i)) { blk -= nblk(p, i); ++i; }  // (workgroup-uniform)
+    const int kper = split_rows(dm, KS1), k0 = min(dm, ks * kper), k1 = min(dm, k0 + kper);
+    mproj_block<3>(p.W[i], p.wn[i], MCOLS * blk, k0, k1, M, p.x, dm, red, p.part + (size_t)ks * M * ntot, ntot,
+                p.noff[i] + MCOLS * blk);
 }
 
 // 3. the output projection of the gated rows: workgroup (column block, row split ks) -> part[ks][m][column]
-__global__ void __launch_bounds__(PT) ldec_out_kernel(LayerDecodeParams p) {
-    __shared__ float xs[KCH * 16];
-    __shared__ float red[16 * 16 * PCOLS];
+__global__ void __launch_bounds__(MT) ldec_out_kernel(LayerDecodeParams p) {
+    __shared__ float red[MW * 16 * MCOLS];
     const int M = p.B * p.T, dm = p.dm, HD = p.H * D;
     const int blk = blockIdx.x / KS3, ks = blockIdx.x - blk * KS3;
-    const int kper = (HD + KS3 - 1) / KS3, k0 = ks * kper, k1 = min(HD, k0 + kper);
-    proj_block(p.Wo, dm, PCOLS * blk, k0, k1, M, [&](int m, int k) { return p.gated[(size_t)m * HD + k]; }, xs, red,
-               p.part + (size_t)ks * M * dm, dm, PCOLS * blk);
+    const int kper = split_rows(HD, KS3), k0 = min(HD, ks * kper), k1 = min(HD, k0 + kper);
+    mproj_block<1>(p.Wo, dm, MCOLS * blk, k0, k1, M, p.gated, HD, red, p.part + (size_t)ks * M * dm, dm, MCOLS * blk);
 }
 
 // 4. y = bf16(sum of the output projection's partials, in split order)
@@ -205,19 +274,17 @@ __global__ void __launch_bounds__(NTHR) ldec_head_kernel(LayerDecodeParams p) {
     const int tid = threadIdx.x;
     const int M = p.B * p.T, HD = p.H * D, R = p.R;
     const int ntot = (p.noff[6] + 3) & ~3;
-    // the projected rows: the sums of the input projection's row-split partials (KS1 of them for q,
-    // k, v, gate, KSB for decay-down and beta), in split order
-    auto psum = [&](int m, int col, auto nks) {  // nks partials, all loads issued together
-        float v[decltype(nks)::value];
+    // the projected rows: the sums of the input projection's KS1 row-split partials, in split order,
+    // all loads issued together
+    auto proj = [&](int m, int col) {
+        float v[KS1];
 #pragma unroll
-        for (int s = 0; s < decltype(nks)::value; ++s) v[s] = p.part[((size_t)s * M + m) * ntot + col];
+        for (int s = 0; s < KS1; ++s) v[s] = p.part[((size_t)s * M + m) * ntot + col];
         float r = 0.f;
 #pragma unroll
-        for (int s = 0; s < decltype(nks)::value; ++s) r += v[s];
+        for (int s = 0; s < KS1; ++s) r += v[s];
         return r;
     };
-    auto proj = [&](int m, int col) { return psum(m, col, std::integral_constant<int, KS1>{}); };      // q, k, v, gate
-    auto proj_small = [&](int m, int col) { return psum(m, col, std::integral_constant<int, KSB>{}); };  // decay-down, beta
     for (int bh = blockIdx.x; bh < p.B * p.H; bh += gridDim.x) {
         const int b = bh / p.H, h = bh - b * p.H;
         const int j = tid & (D - 1), rh = tid >> 7;  // state column, row half
@@ -265,8 +332,8 @@ __global__ void __launch_bounds__(NTHR) ldec_head_kernel(LayerDecodeParams p) {
             Tok v;
             v.a = proj(m, base + hc);
             v.bb = proj(m, base + HD + hc);
-            v.dn = tid < R ? proj_small(m, 4 * HD + tid) : 0.f;
-            v.beta = tid == NTHR - 1 ? proj_small(m, 4 * HD + R + h) : 0.f;
+            v.dn = tid < R ? proj(m, 4 * HD + tid) : 0.f;
+            v.beta = tid == NTHR - 1 ? proj(m, 4 * HD + R + h) : 0.f;
             return v;
         };
         Tok cur = fetch(0);
@@ -417,19 +484,18 @@ __global__ void window_commit_kernel(float* __restrict__ conv, const float* __re
 
 size_t layer_decode_part_floats(int M, int dm, int HD, int ntot) {
     (void)HD;
-    const size_t a = (size_t)ldec::KSB * M * ((ntot + 3) & ~3);
+    const size_t a = (size_t)ldec::KS1 * M * ((ntot + 3) & ~3);
     const size_t b = (size_t)ldec::KS3 * M * dm;
     return a > b ? a : b;
 }
 
 hipError_t launch_layer_decode(const LayerDecodeParams& p, hipStream_t stream) {
     using namespace ldec;
-    int nbig = 0;
-    for (int i = 0; i < 4; ++i) nbig += (p.wn[i] + PCOLS - 1) / PCOLS;
-    const int nsmall = ((p.wn[4] + PCOLS - 1) / PCOLS + (p.wn[5] + PCOLS - 1) / PCOLS) * KSB;
-    hipLaunchKernelGGL(ldec_proj_kernel, dim3((unsigned)(nsmall + nbig * KS1)), dim3(PT), 0, stream, p);
+    int nb = 0;
+    for (int i = 0; i < 6; ++i) nb += (p.wn[i] + MCOLS - 1) / MCOLS;
+    hipLaunchKernelGGL(ldec_proj_kernel, dim3((unsigned)(nb * KS1)), dim3(MT), 0, stream, p);
     hipLaunchKernelGGL(ldec_head_kernel, dim3((unsigned)(p.B * p.H)), dim3(NTHR), 0, stream, p);
-    hipLaunchKernelGGL(ldec_out_kernel, dim3((unsigned)(((p.dm + PCOLS - 1) / PCOLS) * KS3)), dim3(PT), 0, stream, p);
+    hipLaunchKernelGGL(ldec_out_kernel, dim3((unsigned)(((p.dm + MCOLS - 1) / MCOLS) * KS3)), dim3(MT), 0, stream, p);
     const long n4 = (long)p.B * p.T * p.dm / 4;
     hipLaunchKernelGGL(ldec_sum_kernel, dim3((unsigned)((n4 + 255) / 256 < 2048 ? (n4 + 255) / 256 : 2048)), dim3(256), 0,
                        stream, p);

@@ -53,6 +53,20 @@ def test_decode_steps_match_oracle(B, T):
     np.testing.assert_allclose(cs.cpu().numpy(), cs_ref, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("B,T,d,H,R", [(4, 4, 260, 3, 20), (16, 1, 2048, 16, 128)])
+def test_decode_projection_shapes(B, T, d, H, R):
+    """Projection shapes: d_model and rank not multiples of 8 and three heads (element-wise weight and x
+    loads, partial column blocks, a 4-column last block of the output projection); and 16 sequences of
+    one token at d_model 2048, 16 heads, rank 128."""
+    x, p, W, S0, cs0 = setup(50 + d, B=B, T=T, d=d, H=H, R=R)
+    y_ref, S_ref, cs_ref = L.forward(x, p, S0=S0, conv_state=cs0)
+    S, cs = dev(S0), dev(cs0)
+    y, _ = decode(x, W, S, cs)
+    assert rel_max_bf16_out(y, y_ref) <= TOL_BF16
+    assert rel_max(S.cpu().numpy(), S_ref) <= TOL_F32
+    np.testing.assert_allclose(cs.cpu().numpy(), cs_ref, rtol=1e-5, atol=1e-5)
+
+
 def test_speculative_drafts_and_rollback():
     """Four drafts per sequence checked speculatively (state and window untouched, each draft's output as if
     the earlier drafts were accepted); two accepted from the cache; then one more token decoded from there."""
