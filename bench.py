@@ -458,7 +458,8 @@ def bench_core(args, torch, synth, kda, wid):
 def bench_layer_decode(args, torch, synth, kda):
     """kda_layer_decode: one new token for each of B=16 sequences through the layer of the prefill
     workload (d_model 2048, H=16, D=128, rank 128), state and window updated in place.  Bound by reading
-    the weights (about 43 MB of bf16) and reading and writing the float32 state once per call."""
+    the weights (about 43 MB of bf16) and reading and writing the float32 state once per call; the
+    projections are bf16 matrix-core products with float32 sums, the recurrence float32."""
     L = synth.gen.LAYER
     B, T, d, H, D, R = 16, 1, L["d"], L["H"], L["Dk"], L["rank"]
     x, p = synth.layer_inputs(seed=0, B=B, T=T)
@@ -487,10 +488,10 @@ def bench_layer_decode(args, torch, synth, kda):
         "metric": "KDA layer decode tokens/s (B16 one token each, d2048 H16 D128, state in place)",
         "value": B * T / (wall / args.steps), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "kda_layer_decode_bf16_B16_T1_d2048_H16_D128", "B": B, "T": T, "d_model": d, "H": H,
                    "D": D, "rank": R},
-        "roofline": hbm_roofline(abytes, stats, None, "kda_layer_decode_kernel"),
+        "roofline": hbm_roofline(abytes, stats, None, "kda_layer_decode (all four kernels)"),
     }
     print(json.dumps(out), flush=True)
 

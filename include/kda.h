@@ -295,8 +295,10 @@ kda_status kda_layer_fwd(const kda_layer_desc* desc, const void* x, const kda_la
  * call for the projections, the state update and the readout, with a projection-input cache), with
  * the speculative-decoding rollback of section 13.4 (the state is updated in place, so rejected draft
  * tokens cannot be undone from it; each token's projection inputs are cached instead, far fewer
- * numbers than a state).  Four stream-ordered launches: the input projections, one workgroup per
- * (sequence, head) for the gates, convolution, recurrence and readout, the output projection, its sum.
+ * numbers than a state).  Four stream-ordered launches: the input projections (bf16 matrix-core
+ * products of the weights as given, float32 sums), one workgroup per (sequence, head) for the gates,
+ * convolution, recurrence and readout, the output projection (the float32 gated rows as bf16 hi + lo
+ * halves), its sum.
  *   desc          : as kda_layer_fwd, with d_model a multiple of 4, rank <= 128, B*T <= 16 rows (else
  *                   KDA_ERR_UNSUPPORTED); flags = 0 or KDA_DECODE_SPECULATIVE
  *   x             : [B, T, d_model] bf16;  y: [B, T, d_model] bf16 (output); both 16-byte aligned
