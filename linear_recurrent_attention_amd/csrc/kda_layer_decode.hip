@@ -223,9 +223,11 @@ __device__ __forceinline__ void sum_slices4(const float* __restrict__ src, size_
     }
 }
 
-struct Smem {
-    uint16_t wup[128][D];  // the decay up-projection's columns of this head (rank <= 128)
-    float qp[D], kp[D], vv[D], gl[D], q[D], k[D], ga[D], dn[128];
+struct alignas(16) Smem {
+    uint16_t wupT[D][128 + 8];  // this head's columns of the decay up-projection, channel-major (rank
+                                // <= 128, zeros past R; rows padded so 16-byte reads spread over banks)
+    float qp[D], kp[D], vv[D], gl[D], q[D], k[D], ga[D], ega[D], dn[128];
+    float zp[2][D];  // the decay logit's two half-sums over the rank
     float cw[2][3][D];  // convolution window of this head: [q/k][oldest..newest][channel]
     float pw[2][D], po[2][D];
     float red[2];
@@ -315,15 +317,18 @@ __global__ void __launch_bounds__(NTHR) ldec_head_kernel(LayerDecodeParams p) {
             cwv[u] = p.conv ? p.conv[((size_t)b * 3 + r) * 2 * HD + qk * HD + h * D + c] : 0.f;
         }
         static_assert(2 * 3 * D == 3 * NTHR, "three window values per thread");
-        const bool wal = (reinterpret_cast<uintptr_t>(p.Wup) & 15) == 0;  // 16-byte loads of the up-projection
-        u32x4 wv[128 * (D / 8) / NTHR];  // rank <= 128
+        // the up-projection's 8 x 8 block (ranks 8rb.., channels 8cb..) of thread (rb, cb), 16-byte loads
+        const bool wal = (reinterpret_cast<uintptr_t>(p.Wup) & 15) == 0;
+        const int rb = tid >> 4, cb = tid & 15;
+        u32x4 wv[8];
         if (wal) {
 #pragma unroll
-            for (int u = 0; u < 128 * (D / 8) / NTHR; ++u) {
-                const int e = tid + u * NTHR;
-                if (e < R * (D / 8)) wv[u] = *reinterpret_cast<const u32x4*>(p.Wup + (size_t)(e >> 4) * HD + h * D + 8 * (e & 15));
+            for (int i = 0; i < 8; ++i) {
+                wv[i] = u32x4{0u, 0u, 0u, 0u};
+                if (8 * rb + i < R) wv[i] = *reinterpret_cast<const u32x4*>(p.Wup + (size_t)(8 * rb + i) * HD + h * D + 8 * cb);
             }
         }
+        static_assert(NTHR == (128 / 8) * (D / 8), "one 8 x 8 block of the up-projection per thread");
         // this token's projected values: q, k (threads 0-127) or v, gate (128-255) of column j;
         // decay-down column tid (tid < R); beta (the last thread)
         struct Tok { float a, bb, dn, beta; };
@@ -342,24 +347,31 @@ __global__ void __launch_bounds__(NTHR) ldec_head_kernel(LayerDecodeParams p) {
             const int e = tid + u * NTHR;
             sm.cw[e / (3 * D)][(e / D) % 3][e % D] = cwv[u];
         }
-        if (wal) {
-#pragma unroll
-            for (int u = 0; u < 128 * (D / 8) / NTHR; ++u) {
-                const int e = tid + u * NTHR;
-                if (e < R * (D / 8)) *reinterpret_cast<u32x4*>(&sm.wup[e >> 4][8 * (e & 15)]) = wv[u];
-            }
+        if (wal) {  // transposed in registers: channel 8cb + c gets ranks 8rb .. 8rb+7 in one 16-byte write
+            *reinterpret_cast<u32x4*>(&sm.wupT[8 * cb + 0][8 * rb]) = col8<0>(wv);
+            *reinterpret_cast<u32x4*>(&sm.wupT[8 * cb + 1][8 * rb]) = col8<1>(wv);
+            *reinterpret_cast<u32x4*>(&sm.wupT[8 * cb + 2][8 * rb]) = col8<2>(wv);
+            *reinterpret_cast<u32x4*>(&sm.wupT[8 * cb + 3][8 * rb]) = col8<3>(wv);
+            *reinterpret_cast<u32x4*>(&sm.wupT[8 * cb + 4][8 * rb]) = col8<4>(wv);
+            *reinterpret_cast<u32x4*>(&sm.wupT[8 * cb + 5][8 * rb]) = col8<5>(wv);
+            *reinterpret_cast<u32x4*>(&sm.wupT[8 * cb + 6][8 * rb]) = col8<6>(wv);
+            *reinterpret_cast<u32x4*>(&sm.wupT[8 * cb + 7][8 * rb]) = col8<7>(wv);
         } else {
-            for (int e = tid; e < R * D; e += NTHR) sm.wup[e >> 7][e & 127] = p.Wup[(size_t)(e >> 7) * HD + h * D + (e & 127)];
+            for (int e = tid; e < 128 * D; e += NTHR) {
+                const int r = e >> 7, c = e & 127;
+                sm.wupT[c][r] = r < R ? p.Wup[(size_t)r * HD + h * D + c] : (uint16_t)0;
+            }
         }
         for (int t = 0; t < p.T; ++t) {
             const int m = b * p.T + t;
             __syncthreads();  // every read of the previous token's rows (and of the window) is done
             if (rh == 0) { sm.qp[j] = cur.a; sm.kp[j] = cur.bb; } else { sm.vv[j] = cur.a; sm.gl[j] = cur.bb; }
-            if (tid < R) sm.dn[tid] = cur.dn;
+            if (tid < 128) sm.dn[tid] = cur.dn;  // (zero past R)
             if (tid == NTHR - 1) sm.beta = sigm(cur.beta);
             if (t + 1 < p.T) cur = fetch(t + 1);  // in flight during this token's work
             __syncthreads();
-            // short convolution + SiLU of q (threads 0-127) and k (128-255); decay gate (0-127)
+            // short convolution + SiLU of q (threads 0-127) and k (128-255); the decay logit's half-sum of
+            // channel j over ranks 64rh .. 64rh+63
             float act;
             {
                 const int c = j;
@@ -367,18 +379,24 @@ __global__ void __launch_bounds__(NTHR) ldec_head_kernel(LayerDecodeParams p) {
                 const float y = taps[0] * sm.cw[rh][0][c] + taps[1] * sm.cw[rh][1][c] + taps[2] * sm.cw[rh][2][c] +
                                 taps[3] * xcur;
                 act = y * sigm(y);
-                if (rh == 0) {
-                    float z[4] = {balpha, 0.f, 0.f, 0.f};
-                    int r = 0;
-                    for (; r + 4 <= R; r += 4) {
+                const u32x4* wr = reinterpret_cast<const u32x4*>(&sm.wupT[c][64 * rh]);
+                const f32x4* dr = reinterpret_cast<const f32x4*>(&sm.dn[64 * rh]);
+                float z[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) z[u] = __builtin_fmaf(sm.dn[r + u], bf(sm.wup[r + u][c]), z[u]);
+                for (int u = 0; u < 8; ++u) {
+                    const u32x4 w8 = wr[u];
+                    const f32x4 d0 = dr[2 * u], d1 = dr[2 * u + 1];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float de = e < 2 ? d0[2 * e] : d1[2 * e - 4], dodd = e < 2 ? d0[2 * e + 1] : d1[2 * e - 3];
+                        z[e] = __builtin_fmaf(de, __uint_as_float(w8[e] << 16), z[e]);
+                        z[e] = __builtin_fmaf(dodd, __uint_as_float(w8[e] & 0xffff0000u), z[e]);
                     }
-                    for (; r < R; ++r) z[0] = __builtin_fmaf(sm.dn[r], bf(sm.wup[r][c]), z[0]);
-                    sm.ga[c] = -5.f * sigm(ea * ((z[0] + z[1]) + (z[2] + z[3])));
                 }
+                sm.zp[rh][c] = (z[0] + z[1]) + (z[2] + z[3]);
             }
-            // L2 norms: q over threads 0-127, k over 128-255 (each half sums its own two waves)
+            // L2 norms: q over threads 0-127, k over 128-255 (each half sums its own two waves); the decay
+            // gate g and exp(g) of channel j (threads 0-127)
             {
                 float v = act * act;
 #pragma unroll
@@ -388,7 +406,14 @@ __global__ void __launch_bounds__(NTHR) ldec_head_kernel(LayerDecodeParams p) {
                 __syncthreads();
                 const float ss = rh ? sm.pw[0][2] + sm.pw[0][3] : sm.pw[0][0] + sm.pw[0][1];
                 const float nv = act / sqrtf(ss + EPS);
-                if (rh == 0) sm.q[j] = nv; else sm.k[j] = nv;
+                if (rh == 0) {
+                    sm.q[j] = nv;
+                    const float ga = -5.f * sigm(ea * (balpha + (sm.zp[0][j] + sm.zp[1][j])));
+                    sm.ga[j] = ga;
+                    sm.ega[j] = fexp(ga);
+                } else {
+                    sm.k[j] = nv;
+                }
             }
             // cache entry of this token (before the window moves): k, v, g, beta, pre-conv q and k rows
             if (p.cache) {
@@ -419,7 +444,7 @@ __global__ void __launch_bounds__(NTHR) ldec_head_kernel(LayerDecodeParams p) {
             float w = 0.f;
 #pragma unroll
             for (int i = 0; i < 64; ++i) {
-                s[i] *= fexp(sm.ga[64 * rh + i]);
+                s[i] *= sm.ega[64 * rh + i];
                 w = __builtin_fmaf(s[i], sm.k[64 * rh + i], w);
             }
             sm.pw[rh][j] = w;
