@@ -376,7 +376,7 @@ __device__ __forceinline__ void gemm_tile(Smem& sm, const uint16_t* __restrict__
 // Tiles are numbered so that each XCD gets a contiguous range of them (see the header).  When the
 // tile count leaves a partial last round (at most half of the 256 compute units busy), that round's
 // tiles are split along M into sf = 4 (or 2) pieces of 64 (128) rows, each a workgroup of its own on
-// the XCD of its tile: the first nfull workgroups take whole tiles, the rest the pieces.
+// the XCD of its tile; on each XCD up to 16 pieces run first, then the whole tiles, then the rest.
 template <bool OUT_F32, int EPI>
 __global__ void __launch_bounds__(NTHR, 1) gemm_nt_kernel(const uint16_t* __restrict__ A, int lda,
                                                           const uint16_t* __restrict__ Bt, int ldb, GemmOut out,
@@ -389,14 +389,25 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_nt_kernel(const uint16_t* __rest
     const int xcd = blockIdx.x & 7, q = total >> 3, rem = total & 7;
     const int first = xcd * q + min(xcd, rem);  // this XCD's first tile
     int pid, piece = -1;
-    if ((int)blockIdx.x < nfull) {
+    if (sf == 1) {  // whole tiles only (nfull = the tile count)
+        if ((int)blockIdx.x >= nfull) return;
         pid = first + (blockIdx.x >> 3);
     } else {
-        const int v = (blockIdx.x - nfull) >> 3;  // piece index within this XCD
-        const int t = v / sf, cnt = q + (xcd < rem ? 1 : 0) - nfull / 8;
-        if (t >= cnt) return;  // (the whole workgroup)
-        pid = first + nfull / 8 + t;
-        piece = v % sf;
+        // nfull (a multiple of 256) whole tiles, then the pieces.  w: ordinal on this XCD in the order
+        // [whole tiles][pieces]; the first half of the XCD's compute units start with one piece each
+        // and the others with whole tiles, so the two halves run a quarter tile apart and their
+        // epilogue stores do not all reach HBM at once.
+        const int F = nfull / 8, cnt = q + (xcd < rem ? 1 : 0) - F;  // whole and split tiles of this XCD
+        const int v = blockIdx.x >> 3, hs = min(16, sf * cnt);
+        const int w = v < hs ? F + v : v < hs + F ? v - hs : v;
+        if (w < F) {
+            pid = first + w;
+        } else {
+            const int t = (w - F) / sf;
+            if (t >= cnt) return;  // (the whole workgroup)
+            pid = first + F + t;
+            piece = (w - F) % sf;
+        }
     }
     constexpr int GM = 4;
     const int in_group = GM * tn, first_m = (pid / in_group) * GM, gsize = min(tm - first_m, GM);
