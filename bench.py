@@ -9,7 +9,8 @@ launch over the average launch time measured with HIP events on the launch strea
 minimum beside it, and the fraction of the HBM bandwidth a plain device copy reaches in the same
 process) and the float64 CPU oracle's throughput on a bounded sample of the same workload.
 --workload f32_small / bf16_4k time the two smaller forward workloads (B1 H2 T256 D64 in float32;
-B1 H16 T4096 D128 bf16 with an initial state) the same way, one line each.
+B1 H16 T4096 D128 bf16 with an initial state) the same way, one line each; bf16_4k_cp times the
+second through kda_fwd_cp with the automatic segment plan.
 """
 from __future__ import annotations
 
@@ -393,9 +394,11 @@ def bench_layer(args, torch, synth, kda):
     print(json.dumps(out), flush=True)
 
 
-def bench_core(args, torch, synth, kda, wid):
+def bench_core(args, torch, synth, kda, wid, cp=False):
     """kda_fwd on forward workload wid (2: the headline B4 H32 T16384 D128 bf16 line; 0: B1 H2 T256 D64
-    float32; 1: B1 H16 T4096 D128 bf16 with an initial state)."""
+    float32; 1: B1 H16 T4096 D128 bf16 with an initial state).  cp: kda_fwd_cp with the automatic
+    segment plan instead (32 workgroups of workload 1 leave most of the chip idle; the plan cuts each
+    sequence into segments that run side by side)."""
     w = synth.WORKLOADS[wid]
     B, T, H, Dk, Dv = w.B, w.T, w.H, w.Dk, w.Dv
     d = synth.core_inputs(wid, seed=0)
@@ -410,8 +413,18 @@ def bench_core(args, torch, synth, kda, wid):
     ST = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream(device=dev)
 
-    def step():
-        kda.kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=S0, out=o, state_out=ST)
+    if cp:
+        from linear_recurrent_attention_amd import _lib
+        desc = _lib.FwdDesc(B, T, H, Dk, Dv, 0, _lib.KDA_BF16, _lib.KDA_BF16, 1.0, 0)
+        nws = _lib.cp_workspace_size(desc, 0)
+        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+
+        def step():
+            kda.kda_fwd_cp(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=S0, nseg=0, out=o, state_out=ST,
+                           workspace=ws)
+    else:
+        def step():
+            kda.kda_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], S0=S0, out=o, state_out=ST)
 
     wall, launch_ms = time_steps(torch, step, stream, args)
     if args.calibrate_copy:
@@ -431,18 +444,21 @@ def bench_core(args, torch, synth, kda, wid):
     abytes = algorithmic_bytes(B, T, H, Dk, Dv, io_bytes=2 if bf16 else 4, has_S0=S0 is not None)
     aflops = algorithmic_flops(B, T, H, Dk, Dv, C=32 if bf16 else 16)
     achieved_tflops = aflops / avg_launch_s / 1e12
-    kernel = "kda_fwd_bf16_kernel" if bf16 else "kda_fwd_f32_kernel"
+    kernel = ("kda_fwd_cp (all passes)" if cp else "kda_fwd_bf16_kernel") if bf16 else "kda_fwd_f32_kernel"
     mm_peak = BF16_PEAK_TFLOPS if bf16 else FP32_VALU_PEAK_TFLOPS
 
     out = {
-        "metric": METRIC if wid == WORKLOAD else f"KDA prefill tokens/s ({w.name})", "value": value,
+        "metric": METRIC if wid == WORKLOAD and not cp else
+                  f"KDA prefill tokens/s ({w.name}{', kda_fwd_cp automatic plan' if cp else ''})", "value": value,
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "T": T, "Dk": Dk, "Dv": Dv, "chunk": 32 if bf16 else 16,
+        "config": {"workload": w.name + ("_cp" if cp else ""), "B": B, "H": H, "T": T, "Dk": Dk, "Dv": Dv,
+                   "chunk": 32 if bf16 else 16,
                    "io": ("bf16 q/k/v/o" if bf16 else "float32 q/k/v/o") + ", float32 g/beta/state"
                          + (", S0 given" if S0 is not None else "")},
-        "roofline": hbm_roofline(abytes, stats, copy, kernel, measured_traffic() if wid == WORKLOAD else None),
+        "roofline": hbm_roofline(abytes, stats, copy, kernel,
+                                 measured_traffic() if wid == WORKLOAD and not cp else None),
         ("mfma" if bf16 else "valu"): {"achieved": achieved_tflops, "peak": mm_peak, "unit": "TFLOP/s",
                                        "frac": achieved_tflops / mm_peak, "algorithmic_flops": aflops},
     }
@@ -504,13 +520,14 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run one plain 512 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=("core", "f32_small", "bf16_4k", "layer", "decode", "longctx", "bwd",
-                                           "layer_decode"),
+    ap.add_argument("--workload", choices=("core", "f32_small", "bf16_4k", "bf16_4k_cp", "layer", "decode", "longctx",
+                                           "bwd", "layer_decode"),
                     default="core",
                     help="core: kda_fwd on B4 H32 T16384 (the headline line); layer: kda_layer_fwd on "
                          "B2 T8192 d_model 2048 H16; decode: kda_decode on B128 H32, one token; longctx: "
                          "kda_fwd_cp on B1 H16 T1M; bwd: kda_bwd on B4 H32 T16384; f32_small: kda_fwd on "
-                         "B1 H2 T256 D64 float32; bf16_4k: kda_fwd on B1 H16 T4096; layer_decode: kda_layer_decode "
+                         "B1 H2 T256 D64 float32; bf16_4k: kda_fwd on B1 H16 T4096 (bf16_4k_cp: the same "
+                         "through kda_fwd_cp, automatic plan); layer_decode: kda_layer_decode "
                          "on B16 one token each (separate lines)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -542,6 +559,9 @@ def main():
         return
     if args.workload == "bf16_4k":
         bench_core(args, torch, synth, kda, 1)
+        return
+    if args.workload == "bf16_4k_cp":
+        bench_core(args, torch, synth, kda, 1, cp=True)
         return
     bench_core(args, torch, synth, kda, WORKLOAD)
 

@@ -23,6 +23,7 @@ def _kda():
     (2, 3, 3000, 2, False, True),         # ragged with two sequences, precise plan (1472 + 1528 tokens)
     (2, 16, 8192, 3, False, True),        # three segments (2720, 2720, 2752 tokens), first pass merged
     (1, 2, 70000, 0, True, False),        # automatic plan: 31 segments (30 of 2240 tokens, then 2800)
+    (1, 16, 4096, 0, True, False),        # the B1 H16 T4096 forward workload's shape, automatic plan
 ])
 def test_cp_matches_oracle(B, H, T, nseg, s0, precise):
     d, S0 = rand_small(31, B, T, H, s0=s0)
