@@ -22,6 +22,7 @@ struct alignas(16) Smem {
     float qg[C][D], kg[C][D], kb[C][D];   // chunk-start / chunk-end referenced factors
     float w[C][D];                        // W = T Kg
     float u[C][D + 1];                    // U
+    float vv[C][D];                       // the chunk's v rows (zeros past the end)
     float L[C][C + 1], A[C][C + 1], X[C][C + 1];
     float beta[C];
     float gamc[D];
@@ -81,6 +82,20 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_f32_kernel(Params p) {
             const float bld = p.beta[row0 + (size_t)(tid < n ? t0 + tid : p.T - 1) * p.H];
             sm.beta[tid] = tid < n ? bld : 0.f;
         }
+        {  // the chunk's v rows into LDS, every load of a thread in flight together
+            constexpr int NV = C * D / NTHR;
+            float vl[NV];
+#pragma unroll
+            for (int u = 0; u < NV; ++u) {
+                const int e = tid + u * NTHR, r = e / D, j = e % D;
+                vl[u] = v[(row0 + (size_t)(r < n ? t0 + r : p.T - 1) * p.H) * D + j];  // (clamped address)
+            }
+#pragma unroll
+            for (int u = 0; u < NV; ++u) {
+                const int e = tid + u * NTHR, r = e / D, j = e % D;
+                sm.vv[r][j] = r < n ? vl[u] : 0.f;
+            }
+        }
         __syncthreads();
         // L (strictly lower) and A (lower with diagonal)
         {
@@ -118,11 +133,7 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_f32_kernel(Params p) {
         for (int e = tid; e < C * D; e += NTHR) {
             const int r = e / D, j = e % D;
             float u = 0.f;
-            for (int s = 0; s <= r; ++s) {
-                const float vld = v[(row0 + (size_t)(s < n ? t0 + s : p.T - 1) * p.H) * D + j];
-                const float vv = s < n ? vld : 0.f;
-                u += sm.X[r][s] * vv;
-            }
+            for (int s = 0; s <= r; ++s) u += sm.X[r][s] * sm.vv[s][j];
             for (int c = 0; c < D; ++c) u -= sm.w[r][c] * sm.S[c][j];
             sm.u[r][j] = u;
         }
