@@ -18,8 +18,10 @@ constexpr int NTHR = 256;
 template <int D>
 struct alignas(16) Smem {
     float S[D][D + 1];
-    float qm[C][D], km[C][D], kh[C][D];   // sub-tile referenced factors
-    float qg[C][D], kg[C][D], kb[C][D];   // chunk-start / chunk-end referenced factors
+    // (rows padded by four floats: the Gram products read 16 rows at one column across a wave, and
+    // rows stay 16-byte aligned for 16-byte reads)
+    float qm[C][D + 4], km[C][D + 4], kh[C][D + 4];  // sub-tile referenced factors
+    float qg[C][D + 4], kg[C][D + 4], kb[C][D + 4];  // chunk-start / chunk-end referenced factors
     float w[C][D];                        // W = T Kg
     float u[C][D + 1];                    // U
     float vv[C][D];                       // the chunk's v rows (zeros past the end)
@@ -129,31 +131,61 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_f32_kernel(Params p) {
             sm.w[r][c] = w;
         }
         __syncthreads();
-        // U = T V - W S
-        for (int e = tid; e < C * D; e += NTHR) {
-            const int r = e / D, j = e % D;
-            float u = 0.f;
-            for (int s = 0; s <= r; ++s) u += sm.X[r][s] * sm.vv[s][j];
-            for (int c = 0; c < D; ++c) u -= sm.w[r][c] * sm.S[c][j];
-            sm.u[r][j] = u;
+        // U = T V - W S.  Thread (column j, row group) takes the RB rows r = rg + k * RS of column j
+        // together, so that each S[c][j] read from LDS serves all of them (every row's sum keeps its
+        // own order).
+        constexpr int RS = NTHR / D, RB = C / RS;  // row groups, rows per thread
+        {
+            const int j = tid % D, rg = tid / D;
+            float u[RB];
+#pragma unroll
+            for (int k = 0; k < RB; ++k) {
+                const int r = rg + k * RS;
+                float a = 0.f;
+                for (int s = 0; s <= r; ++s) a += sm.X[r][s] * sm.vv[s][j];
+                u[k] = a;
+            }
+            for (int c = 0; c < D; ++c) {
+                const float sc = sm.S[c][j];
+#pragma unroll
+                for (int k = 0; k < RB; ++k) u[k] -= sm.w[rg + k * RS][c] * sc;
+            }
+#pragma unroll
+            for (int k = 0; k < RB; ++k) sm.u[rg + k * RS][j] = u[k];
         }
         __syncthreads();
-        // O = Qg S + A U (skipped when o == NULL: a state-only run)
-        for (int e = tid; o && e < C * D; e += NTHR) {
-            const int r = e / D, j = e % D;
-            if (r >= n) continue;
-            float acc = 0.f;
-            for (int c = 0; c < D; ++c) acc += sm.qg[r][c] * sm.S[c][j];
-            for (int s = 0; s <= r; ++s) acc += sm.A[r][s] * sm.u[s][j];
-            o[(row0 + (size_t)(t0 + r) * p.H) * D + j] = acc * p.scale;
+        // O = Qg S + A U (skipped when o == NULL: a state-only run), rows grouped the same way
+        if (o) {
+            const int j = tid % D, rg = tid / D;
+            float acc[RB];
+#pragma unroll
+            for (int k = 0; k < RB; ++k) acc[k] = 0.f;
+            for (int c = 0; c < D; ++c) {
+                const float sc = sm.S[c][j];
+#pragma unroll
+                for (int k = 0; k < RB; ++k) acc[k] += sm.qg[rg + k * RS][c] * sc;
+            }
+#pragma unroll
+            for (int k = 0; k < RB; ++k) {
+                const int r = rg + k * RS;
+                for (int s = 0; s <= r; ++s) acc[k] += sm.A[r][s] * sm.u[s][j];
+                if (r < n) o[(row0 + (size_t)(t0 + r) * p.H) * D + j] = acc[k] * p.scale;
+            }
         }
         __syncthreads();
-        // S <- Diag(Gamma_last) S + Kb^T U
-        for (int e = tid; e < D * D; e += NTHR) {
-            const int c = e / D, j = e % D;
-            float acc = sm.gamc[c] * sm.S[c][j];
-            for (int s = 0; s < C; ++s) acc += sm.kb[s][c] * sm.u[s][j];
-            sm.S[c][j] = acc;
+        // S <- Diag(Gamma_last) S + Kb^T U: thread (column j, row group) holds U's column j in
+        // registers and updates rows cg, cg + RS, ... of it (entry tid + m * NTHR, m = 0, 1, ...)
+        {
+            const int j = tid % D, cg = tid / D;
+            float uj[C];
+#pragma unroll
+            for (int s = 0; s < C; ++s) uj[s] = sm.u[s][j];
+            for (int c = cg; c < D; c += RS) {
+                float acc = sm.gamc[c] * sm.S[c][j];
+#pragma unroll
+                for (int s = 0; s < C; ++s) acc += sm.kb[s][c] * uj[s];
+                sm.S[c][j] = acc;
+            }
         }
         if (p.S_ckpt && (ch + 1) % p.ckpt_chunks == 0 && (ch + 1) / p.ckpt_chunks <= p.n_ckpt) {
             // the state after tokens [0, (ch+1)*C); each thread copies the entries it just wrote
