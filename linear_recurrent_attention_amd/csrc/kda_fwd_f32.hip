@@ -28,6 +28,7 @@ struct alignas(16) Smem {
     float L[C][C + 1], A[C][C + 1], X[C][C + 1];
     float beta[C];
     float gamc[D];
+    float gtot[NTHR / D][D];  // per token group: the sum of its tokens' decay logits
 };
 
 template <int D>
@@ -47,56 +48,80 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_f32_kernel(Params p) {
         sm.S[c][j] = p.S0 ? p.S0[(size_t)bh * D * D + e] : 0.f;
     }
     const int nchunk = (p.T + C - 1) / C;
+    // Thread (channel cc, token group tg) handles tokens tg*TG .. tg*TG + TG-1 of every chunk for the
+    // decay sums and the factors.  A chunk's raw inputs (g, q, k of those tokens, the thread's share of
+    // v, one beta) are loaded into registers during the chunk before it.
+    constexpr int RS = NTHR / D, TG = C / RS, NV = C * D / NTHR;  // token groups, tokens per group
+    static_assert(TG == 4 || TG == 8, "token 7 ends a token group");
+    const int cc = tid % D, tg = tid / D;
+    struct Raw { float g[TG], q[TG], k[TG], v[NV], beta; };
+    auto load_raw = [&](int ch, Raw& R) {
+        const int t0 = ch * C, n = min(C, p.T - t0);
+#pragma unroll
+        for (int i = 0; i < TG; ++i) {
+            const int r = tg * TG + i;
+            const size_t idx = (row0 + (size_t)(r < n ? t0 + r : p.T - 1) * p.H) * D + cc;  // (clamped address)
+            R.g[i] = p.g[idx];
+            R.q[i] = q[idx];
+            R.k[i] = k[idx];
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int e = tid + u * NTHR, r = e / D, j = e % D;
+            R.v[u] = v[(row0 + (size_t)(r < n ? t0 + r : p.T - 1) * p.H) * D + j];
+        }
+        R.beta = tid < C ? p.beta[row0 + (size_t)(tid < n ? t0 + tid : p.T - 1) * p.H] : 0.f;
+    };
+    Raw cur, nxt;
+    load_raw(0, cur);
     for (int ch = 0; ch < nchunk; ++ch) {
         const int t0 = ch * C;
         const int n = min(C, p.T - t0);
-        __syncthreads();
-        // per-channel cumulative decay and the decay-scaled factors
-        if (tid < D) {
-            const int c = tid;
-            float bcum[C];
+        __syncthreads();  // every read of the previous chunk's tiles is done
+        if (ch + 1 < nchunk) load_raw(ch + 1, nxt);  // in flight during this chunk
+        // decay sums within the token group, the chunk's v rows and beta
+        float gl[TG];
+        {
             float a = 0.f;
-            for (int r = 0; r < C; ++r) {
-                const int tc = r < n ? t0 + r : p.T - 1;  // clamped: every address stays valid
-                const float gv = p.g[(row0 + (size_t)tc * p.H) * D + c];
-                const float gr = r < n ? gv : 0.f;
-                a += gr;
-                bcum[r] = a;
+#pragma unroll
+            for (int i = 0; i < TG; ++i) {
+                a += tg * TG + i < n ? cur.g[i] : 0.f;
+                gl[i] = a;
             }
-            const float ref = bcum[7], last = bcum[C - 1];
-            for (int r = 0; r < C; ++r) {
-                const size_t idx = (row0 + (size_t)(r < n ? t0 + r : p.T - 1) * p.H) * D + c;
-                const float qld = q[idx], kld = k[idx];
-                const float qv = r < n ? qld : 0.f;
-                const float kv = r < n ? kld : 0.f;
-                const float e = fexp(bcum[r] - ref), rinv = fexp(ref - bcum[r]);
-                sm.qm[r][c] = qv * e;
-                sm.km[r][c] = kv * e;
-                sm.kh[r][c] = kv * rinv;
-                const float gam = fexp(bcum[r]);
-                sm.qg[r][c] = qv * gam;
-                sm.kg[r][c] = kv * gam;
-                sm.kb[r][c] = kv * fexp(last - bcum[r]);
-            }
-            sm.gamc[c] = fexp(last);
-        }
-        if (tid < C) {
-            const float bld = p.beta[row0 + (size_t)(tid < n ? t0 + tid : p.T - 1) * p.H];
-            sm.beta[tid] = tid < n ? bld : 0.f;
-        }
-        {  // the chunk's v rows into LDS, every load of a thread in flight together
-            constexpr int NV = C * D / NTHR;
-            float vl[NV];
+            sm.gtot[tg][cc] = a;
 #pragma unroll
             for (int u = 0; u < NV; ++u) {
                 const int e = tid + u * NTHR, r = e / D, j = e % D;
-                vl[u] = v[(row0 + (size_t)(r < n ? t0 + r : p.T - 1) * p.H) * D + j];  // (clamped address)
+                sm.vv[r][j] = r < n ? cur.v[u] : 0.f;
+            }
+            if (tid < C) sm.beta[tid] = tid < n ? cur.beta : 0.f;
+        }
+        __syncthreads();
+        // cumulative decay b_r of the thread's tokens, relative to token 7 (ref) and to the chunk's
+        // end (last), and the decay-scaled factors
+        {
+            float off = 0.f;
+            for (int g2 = 0; g2 < tg; ++g2) off += sm.gtot[g2][cc];
+            float ref = 0.f, last = 0.f;
+            for (int g2 = 0; g2 < RS; ++g2) {
+                last += sm.gtot[g2][cc];
+                if (g2 == 7 / TG) ref = last;  // token 7 ends its group
             }
 #pragma unroll
-            for (int u = 0; u < NV; ++u) {
-                const int e = tid + u * NTHR, r = e / D, j = e % D;
-                sm.vv[r][j] = r < n ? vl[u] : 0.f;
+            for (int i = 0; i < TG; ++i) {
+                const int r = tg * TG + i;
+                const float b = off + gl[i];
+                const float qv = r < n ? cur.q[i] : 0.f, kv = r < n ? cur.k[i] : 0.f;
+                const float e = fexp(b - ref), rinv = fexp(ref - b);
+                sm.qm[r][cc] = qv * e;
+                sm.km[r][cc] = kv * e;
+                sm.kh[r][cc] = kv * rinv;
+                const float gam = fexp(b);
+                sm.qg[r][cc] = qv * gam;
+                sm.kg[r][cc] = kv * gam;
+                sm.kb[r][cc] = kv * fexp(last - b);
             }
+            if (tg == 0) sm.gamc[cc] = fexp(last);
         }
         __syncthreads();
         // L (strictly lower) and A (lower with diagonal)
@@ -134,7 +159,7 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_f32_kernel(Params p) {
         // U = T V - W S.  Thread (column j, row group) takes the RB rows r = rg + k * RS of column j
         // together, so that each S[c][j] read from LDS serves all of them (every row's sum keeps its
         // own order).
-        constexpr int RS = NTHR / D, RB = C / RS;  // row groups, rows per thread
+        constexpr int RB = C / RS;  // rows per thread (RS row groups)
         {
             const int j = tid % D, rg = tid / D;
             float u[RB];
@@ -192,6 +217,7 @@ __global__ void __launch_bounds__(NTHR, 1) kda_fwd_f32_kernel(Params p) {
             float* dst = p.S_ckpt + ((size_t)bh * p.n_ckpt + ((ch + 1) / p.ckpt_chunks - 1)) * D * D;
             for (int e = tid; e < D * D; e += NTHR) dst[e] = sm.S[e / D][e % D];
         }
+        cur = nxt;
     }
     __syncthreads();
     if (p.S_T)
