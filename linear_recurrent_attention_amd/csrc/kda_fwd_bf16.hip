@@ -16,16 +16,23 @@
 // of sections 3.1-3.2 each factor lies in [e^-80, e^80], inside the normal range of float32 and
 // bf16; the products that enter L and A (t >= s) are at most 1.  The inter-chunk products reuse
 // the same tiles by moving exp(b_15) onto the state: (K*Gamma) S = Km (Diag(exp(b_15)) S), and
-// likewise for Q.  That row-scaled state is formed as P = -2^64 Diag(exp(b_15)) S: with the factor
-// 2^64 both P (>= 2^-51 |S|) and every product Km P (<= 2^64 |S|) stay normal for any state with
+// likewise for Q.  The value waves keep the state in that row-scaled frame for the whole run,
+// R = -2^(64 + kappa) S per row, with kappa = round(b_15 log2 e) an integer: the power of two is exact,
+// and the rest of exp(b_15), 2^delta with |delta| <= 1/2, is carried by the factor tiles (Qm, Km and
+// Kh take 2^(+-delta); the Gram products do not see it).  R itself is the state operand, so no
+// per-row scaling is applied when it is split into matrix-core operands.  With the factor 2^64 both R
+// (>= 2^-52 |S|) and every product Km R (<= 2^64 |S|) stay normal for any state with
 // 2^-75 <= |S| < 2^60, so the result does not depend on the scale of v and S0 (the recurrence is
 // linear in them).  The rest of the value path carries the matching powers of two, all exact:
-//   X~ = 2^64 V + Km P              = 2^64 (V - (K*Gamma) S)
+//   X~ = 2^64 V + Km R              = 2^64 (V - (K*Gamma) S)
 //   T' = 2^-64 T,  L10' = 2^64 L10  so U = T' X~ comes out unscaled (block forward substitution
 //                                   over the two 16-token sub-tiles: U0 = T'00 X~0,
 //                                   U1 = T'11 (X~1 - L10' U0))
-//   A'' = -2^64 A,                  O = -2^-64 (Qm P + A'' U)
-//   S <- Diag(Gamma_31) S + Kbar^T U,  Kbar = K*exp(b_31 - b) = Kh*exp(b_31 - b_15)  (<= 1).
+//   A'' = -2^64 A,                  O = -2^-64 (Qm R + A'' U)
+//   R <- Diag(rho) R + Kbar'^T U    rho = 2^(kappa' - kappa) exp(b_31),  Kbar' = -2^(64 + kappa') K exp(b_31 - b)
+// with kappa' that of the next chunk (0 after the last one, which leaves R = -2^64 S_T).  S0 enters as
+// Diag(-2^(64 + kappa)) S0 and checkpoints leave as R times the exact reciprocal of that power of two,
+// so a run resumed from a checkpoint or cut at a chunk boundary reproduces the uncut run bit for bit.
 //
 // Mapping.  One workgroup per (batch, head, value half): the 128 value columns are split over two
 // workgroups that both compute the key-side products, so 2*B*H workgroups fill the chip; the two
@@ -50,7 +57,7 @@
 // Matrix-core operands (v_mfma_f32_16x16x32_bf16 and 16x16x16, float32 accumulate; "split" is
 // hi = bf16(x), lo = bf16(x - hi), products hi*hi + hi*lo + lo*hi):
 //   L = Km Kh^T         bf16 (PRECISE: Kh split)       A = Qm Kh^T        split
-//   X~ = 2^64 V + Km P  Km bf16, P split                Qm P               split
+//   X~ = 2^64 V + Km R  Km bf16, R split                Qm R               split
 //   U = T' X~           split                          A'' U              split
 //   Kbar^T U            split
 // The inverse solves the two 16x16 diagonal blocks of (I + Diag(beta) L) by forward substitution
@@ -116,8 +123,9 @@ struct alignas(16) ChunkTiles {              // between roles, double buffered b
     float beta[C];
 };
 struct alignas(16) Scalings {                // state scalings of one chunk, by chunk index mod 3
-    float ep[DK];                            // -2^64 exp(b_15)           row scale of the state operand
-    float gam[DK];                           // exp(b_31)
+    float ep[DK];                            // -2^(64 + kappa)           row scale R = ep S of the state entering
+                                             //                           the chunk (kappa = round(b_15 log2 e))
+    float gam[DK];                           // rho = 2^(kappa' - kappa) exp(b_31), kappa' the next chunk's
 };
 struct alignas(16) VStage {                  // 2^64 v of one chunk, loaded by the helper waves for the value
     float x[NVW][64][8];                     // waves: [value wave][lane][4R + r] = token 16R + 4*g4 + r of the
@@ -236,9 +244,10 @@ __device__ __forceinline__ void mask_tail(Raw<IN_F32>& r, int T, int t0, int kw,
 // part 2 (used in part 3), and the factors its Kbar^T tile is made from (used in part 1 of the next
 // step).
 struct Carry {
-    float e[TPW][2], f[TPW][2];  // exp(b - b_15), exp(b_15 - b)
-    float kh[TPW][2];            // K times exp(b_15 - b)
-    float eC[2];                 // exp(b_31 - b_15)
+    float e[TPW][2], f[TPW][2];  // 2^(y + delta), 2^-(y + delta) with y = (b - b_15) log2(e)
+    float kh[TPW][2];            // K times 2^-(y + delta)
+    float eC[2];                 // 2^((b_31 - b_15) log2(e) + delta)
+    float a[2];                  // b_31 log2(e) - kappa (key wave 0: the row decay of the next step)
 };
 
 // Split x into bf16 hi + lo, packing the pair (a, b) into one word of each (a in the low half).
@@ -264,7 +273,7 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
     ChunkTiles& Hf = sm.ch[nf & 1];
     ChunkTiles& Hg = sm.ch[n & 1];
 
-    // ---------------- part 1: decay sums of chunk n+1 over the quad; prefetch; Kbar^T of chunk n
+    // ---------------- part 1: decay sums of chunk n+1 over the quad; prefetch
     if (fwork) {
         if (t0 + C > p.T) mask_tail(cur, p.T, t0, kw, lane);
         float a0 = 0.f, a1 = 0.f;
@@ -273,25 +282,12 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         *reinterpret_cast<float2*>(&sm.key.tot[lane][2 * kw]) = make_float2(a0, a1);
     }
     load_chunk<LOAD_GB>(nxt, p, kl, row0, tn);  // part of the chunk after
-    if (gwork) {
-        // per channel, token pairs (0,1) and (2,3) of the quad, contiguous after tperm
-        uint32_t h[2][2], l[2][2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            split2(cy.kh[0][c] * cy.eC[c], cy.kh[1][c] * cy.eC[c], h[c][0], l[c][0]);
-            split2(cy.kh[2][c] * cy.eC[c], cy.kh[3][c] * cy.eC[c], h[c][1], l[c][1]);
-        }
-        const int pt = tperm(tq);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            *reinterpret_cast<u32x2*>(&Hg.kbh[c0 + c][sw(c0 + c, pt)]) = u32x2{h[c][0], h[c][1]};
-            *reinterpret_cast<u32x2*>(&Hg.kbl[c0 + c][sw(c0 + c, pt)]) = u32x2{l[c][0], l[c][1]};
-        }
-    }
     lds_barrier();  // ---- barrier 1
 
-    // ---------------- part 2: decays and exponentials of chunk n+1 (the A Gram products of chunk n are
-    // the helper waves')
+    // ---------------- part 2: decays, row scales and exponentials of chunk n+1; the row decay and the
+    // Kbar^T tile of chunk n (the Gram products of chunk n are the helper waves')
+    float kap0 = 0.f, kap1 = 0.f;  // kappa of chunk n+1 (0 past the last chunk: the state leaves unscaled)
+    float eCn0 = 0.f, eCn1 = 0.f, an0 = 0.f, an1 = 0.f;
     if (fwork) {
         float tt0[NKW], tt1[NKW];
 #pragma unroll
@@ -316,13 +312,19 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
             case 6: o0 = s45a; o1 = s45b; break;
             default: o0 = s45a + tt0[6]; o1 = s45b + tt1[6]; break;
         }
-        o0 *= kLog2e; o1 *= kLog2e;
-        cy.eC[0] = fexp(q0); cy.eC[1] = fexp(q1);
-        if (kw == 0) {  // the state scalings of chunk n+1, read by its value step
-            const float e0 = fexp(p0), e1 = fexp(p1);
+        // b_15 log2(e) = kappa + delta, kappa an integer, |delta| <= 1/2: the state carries 2^kappa of
+        // exp(b_15) (exactly, as a power of two) and the factors carry 2^delta
+        const float lp0 = p0 * kLog2e, lp1 = p1 * kLog2e;
+        kap0 = __builtin_rintf(lp0); kap1 = __builtin_rintf(lp1);
+        const float d0 = lp0 - kap0, d1 = lp1 - kap1;
+        o0 = __builtin_fmaf(o0, kLog2e, d0); o1 = __builtin_fmaf(o1, kLog2e, d1);
+        eCn0 = __builtin_amdgcn_exp2f(__builtin_fmaf(q0, kLog2e, d0));
+        eCn1 = __builtin_amdgcn_exp2f(__builtin_fmaf(q1, kLog2e, d1));
+        an0 = __builtin_fmaf(p0 + q0, kLog2e, -kap0); an1 = __builtin_fmaf(p1 + q1, kLog2e, -kap1);
+        if (kw == 0) {  // the row scale -2^(64 + kappa) of chunk n+1 (the state's entry scaling, checkpoints)
             Scalings& Sf = sm.sc[nf % 3];
-            *reinterpret_cast<float2*>(&Sf.ep[c0]) = make_float2(-kUp * e0, -kUp * e1);
-            *reinterpret_cast<float2*>(&Sf.gam[c0]) = make_float2(e0 * cy.eC[0], e1 * cy.eC[1]);
+            *reinterpret_cast<float2*>(&Sf.ep[c0]) =
+                make_float2(__builtin_amdgcn_ldexpf(-1.f, 64 + (int)kap0), __builtin_amdgcn_ldexpf(-1.f, 64 + (int)kap1));
         }
         float y0 = o0, y1 = o1;
 #pragma unroll
@@ -333,6 +335,43 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
             cy.f[i][0] = __builtin_amdgcn_exp2f(-y0); cy.f[i][1] = __builtin_amdgcn_exp2f(-y1);
         }
         if (lane < TPW) Hf.beta[TPW * kw + lane] = cur.beta;
+    }
+    if (gwork) {
+        // chunk n, in the state's row-scaled frame R = -2^(64 + kappa) S: R <- rho R + Kbar'^T U with
+        //   rho   = 2^(kappa_{n+1} - kappa_n) exp(b_31)          = 2^kappa_{n+1} 2^(b_31 log2(e) - kappa_n)
+        //   Kbar' = -2^(64 + kappa_{n+1}) K exp(b_31 - b)        = -2^(64 + kappa_{n+1}) Kh eC
+        // (the powers of two applied last, exactly, so that a run cut at a chunk boundary and resumed from
+        // its unscaled state reproduces the uncut run bit for bit)
+        if (kw == 0) {
+            Scalings& Sg = sm.sc[n % 3];
+            *reinterpret_cast<float2*>(&Sg.gam[c0]) =
+                make_float2(__builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(cy.a[0]), (int)kap0),
+                            __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(cy.a[1]), (int)kap1));
+        }
+        // per channel, token pairs (0,1) and (2,3) of the quad, contiguous after tperm
+        const int s0 = 64 + (int)kap0, s1 = 64 + (int)kap1;
+        uint32_t h[2][2], l[2][2];
+        float x[2][TPW];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            x[0][i] = __builtin_amdgcn_ldexpf(-(cy.kh[i][0] * cy.eC[0]), s0);
+            x[1][i] = __builtin_amdgcn_ldexpf(-(cy.kh[i][1] * cy.eC[1]), s1);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            split2(x[c][0], x[c][1], h[c][0], l[c][0]);
+            split2(x[c][2], x[c][3], h[c][1], l[c][1]);
+        }
+        const int pt = tperm(tq);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            *reinterpret_cast<u32x2*>(&Hg.kbh[c0 + c][sw(c0 + c, pt)]) = u32x2{h[c][0], h[c][1]};
+            *reinterpret_cast<u32x2*>(&Hg.kbl[c0 + c][sw(c0 + c, pt)]) = u32x2{l[c][0], l[c][1]};
+        }
+    }
+    if (fwork) {
+        cy.eC[0] = eCn0; cy.eC[1] = eCn1;
+        cy.a[0] = an0; cy.a[1] = an1;
     }
     lds_barrier();  // ---- barrier 2
 
@@ -570,7 +609,7 @@ __device__ __forceinline__ void helper_waves(Smem& sm, const Params& p, size_t r
 #pragma unroll
             for (int blk = 0; blk < 3; ++blk) {
                 const int R = blk == 0 ? 0 : 1, S = blk == 2 ? 1 : 0;
-                f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int mm = 0; mm < 2; ++mm) {
                     const int kc = 32 * (2 * mh + mm) + 8 * g4;
@@ -578,13 +617,12 @@ __device__ __forceinline__ void helper_waves(Smem& sm, const Params& p, size_t r
                     const u32x4 aL = ld16(&H.qml[SUB * R + l16][kc]);
                     const u32x4 bH = ld16(&sm.key.khh[SUB * S + l16][kc]);
                     const u32x4 bL = ld16(&sm.key.khl[SUB * S + l16][kc]);
-                    f32x4& a = mm ? a1 : a0;
                     a = mfma_bf16(aH, bH, a);
                     a = mfma_bf16(aH, bL, a);
                     a = mfma_bf16(aL, bH, a);
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sm.s.apart[2 * blk + mh][r][lane] = a0[r] + a1[r];
+                for (int r = 0; r < 4; ++r) sm.s.apart[2 * blk + mh][r][lane] = a[r];
             }
         }
         lds_barrier();  // ---- barrier 2
@@ -680,39 +718,41 @@ __device__ __forceinline__ void value_waves(Smem& sm, const Params& p, int bh, s
 
     __builtin_amdgcn_s_setprio(3);  // the value waves carry the serial chain: issue them first
 
-    for (int n = -1; n <= nchunk; ++n) {
-        const bool work = n >= 1;  // this step handles chunk n-1
+    // steps -1 and 0 have no chunk yet (the first chunk's tiles are being formed)
+    for (int n = -1; n <= 0; ++n) {
+        lds_barrier();
+        lds_barrier();
+        lds_barrier();
+    }
+    // the state enters the row-scaled frame R = Diag(ep) S of chunk 0 (exact: powers of two)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) st[cb] *= *reinterpret_cast<const f32x4*>(&sm.sc[0].ep[16 * cb + 4 * g4]);
+
+    for (int n = 1; n <= nchunk; ++n) {
+        constexpr bool work = true;  // step n handles chunk n-1
         const int c = n - 1;
         const int t0 = c * C;
         const ChunkTiles& H = sm.ch[c & 1];
-        const Scalings& Sc = sm.sc[(c + 3) % 3];
+        const Scalings& Sc = sm.sc[c % 3];
         u32x4 ph[4];
         f32x4 oacc[2];
-        // ---------------- part 1: P = -2^64 Diag(exp(b_15)) S as split-bf16 operands; Qm P
-        // (each product chain below has its own accumulators, interleaved, so that consecutive matrix
-        // instructions never wait for each other's results).  A state-only run needs P_hi alone (for X~).
+        // ---------------- part 1: the state operand P = R as split-bf16 operands; Qm P
+        // (the two row blocks' chains alternate, so consecutive matrix instructions are independent; each
+        // chain accumulates in place, which the matrix core forwards without a vector add).  A state-only
+        // run needs P_hi alone (for X~).
         if (SO && work) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const f32x4 e0 = *reinterpret_cast<const f32x4*>(&Sc.ep[32 * m + 4 * g4]);
-                const f32x4 e1 = *reinterpret_cast<const f32x4*>(&Sc.ep[32 * m + 16 + 4 * g4]);
-                const f32x4 a = st[2 * m] * e0, b = st[2 * m + 1] * e1;
+                const f32x4 a = st[2 * m], b = st[2 * m + 1];
                 ph[m] = u32x4{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]), pack_bf16(b[2], b[3])};
             }
         }
         if (!SO && work) {
-            f32x4 q[2][3];
-#pragma unroll
-            for (int R = 0; R < 2; ++R)
-#pragma unroll
-                for (int t = 0; t < 3; ++t) q[R][t] = f32x4{0.f, 0.f, 0.f, 0.f};
             // K-step m over channels 32m..32m+31 in the order {32m + 4*g4 + r} then {32m + 16 + 4*g4 + r};
             // as an A operand it is P^T.  Qm P as O^T: lane (token l16, group g4) gets columns 4*g4..4*g4+3
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const f32x4 e0 = *reinterpret_cast<const f32x4*>(&Sc.ep[32 * m + 4 * g4]);
-                const f32x4 e1 = *reinterpret_cast<const f32x4*>(&Sc.ep[32 * m + 16 + 4 * g4]);
-                const f32x4 a = st[2 * m] * e0, b = st[2 * m + 1] * e1;
+                const f32x4 a = st[2 * m], b = st[2 * m + 1];
                 uint32_t h0, h1, h2, h3, q0, q1, q2, q3;
                 split2(a[0], a[1], h0, q0);
                 split2(a[2], a[3], h1, q1);
@@ -722,15 +762,13 @@ __device__ __forceinline__ void value_waves(Smem& sm, const Params& p, int bh, s
                 const u32x4 pl = u32x4{q0, q1, q2, q3};
                 const u32x4 bH0 = ld16(&H.qmh[l16][32 * m + 8 * g4]), bL0 = ld16(&H.qml[l16][32 * m + 8 * g4]);
                 const u32x4 bH1 = ld16(&H.qmh[SUB + l16][32 * m + 8 * g4]), bL1 = ld16(&H.qml[SUB + l16][32 * m + 8 * g4]);
-                q[0][0] = mfma_bf16(ph[m], bH0, q[0][0]);
-                q[1][0] = mfma_bf16(ph[m], bH1, q[1][0]);
-                q[0][1] = mfma_bf16(pl, bH0, q[0][1]);
-                q[1][1] = mfma_bf16(pl, bH1, q[1][1]);
-                q[0][2] = mfma_bf16(ph[m], bL0, q[0][2]);
-                q[1][2] = mfma_bf16(ph[m], bL1, q[1][2]);
+                oacc[0] = mfma_bf16(ph[m], bH0, m ? oacc[0] : f32x4{0.f, 0.f, 0.f, 0.f});
+                oacc[1] = mfma_bf16(ph[m], bH1, m ? oacc[1] : f32x4{0.f, 0.f, 0.f, 0.f});
+                oacc[0] = mfma_bf16(pl, bH0, oacc[0]);
+                oacc[1] = mfma_bf16(pl, bH1, oacc[1]);
+                oacc[0] = mfma_bf16(ph[m], bL0, oacc[0]);
+                oacc[1] = mfma_bf16(ph[m], bL1, oacc[1]);
             }
-#pragma unroll
-            for (int R = 0; R < 2; ++R) oacc[R] = q[R][0] + (q[R][1] + q[R][2]);
         }
         lds_barrier();  // ---- barrier 1
 
@@ -739,16 +777,12 @@ __device__ __forceinline__ void value_waves(Smem& sm, const Params& p, int bh, s
         if (work) {
             // 2^64 V in accumulator layout (tokens 16R + 4*g4 + r, column col), staged by a helper wave
             const f32x4* vx = reinterpret_cast<const f32x4*>(&sm.vs[c & 1].x[vw][lane][0]);
-            f32x4 xr[2] = {vx[0], vx[1]}, xs[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            f32x4 xr[2] = {vx[0], vx[1]};
 #pragma unroll
-            for (int m = 0; m < 4; m += 2)
+            for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int R = 0; R < 2; ++R) {
+                for (int R = 0; R < 2; ++R)
                     xr[R] = mfma_bf16(ld16(&H.km[SUB * R + l16][32 * m + 8 * g4]), ph[m], xr[R]);
-                    xs[R] = mfma_bf16(ld16(&H.km[SUB * R + l16][32 * (m + 1) + 8 * g4]), ph[m + 1], xs[R]);
-                }
-            xr[0] += xs[0];
-            xr[1] += xs[1];
             // U by block forward substitution over the two sub-tiles (T is block lower triangular):
             //   U0 = T'00 X~0,   U1 = T'11 (X~1 - L'10 U0),
             // as split-bf16 16x16x16 products whose contraction index is token 4*g4 + r of a sub-tile
@@ -784,22 +818,26 @@ __device__ __forceinline__ void value_waves(Smem& sm, const Params& p, int bh, s
         }
         lds_barrier();  // ---- barrier 2
 
-        // ---------------- part 3: O = -2^-64 (Qm P + A'' U), output; S <- Diag(Gamma_31) S + Kbar^T U
+        // ---------------- part 3: O = -2^-64 (Qm P + A'' U), output; R <- Diag(rho) R + Kbar'^T U
         if (work) {
             if (!SO && p.o) {  // (o == NULL: a state-only run of the in-device context parallelism)
                 gchar* ob = (gchar*)uniform_gptr((const char*)p.o + ((row0 + (size_t)t0 * p.H) * DV) * (OUT_F32 ? 4 : 2));
-                f32x4 o1[2], o2[2];
+                u32x4 aH[2], aL[2];
 #pragma unroll
                 for (int R = 0; R < 2; ++R) {
-                    const u32x4 aH = ld16(&H.ah[SUB * R + l16][sw(l16, 8 * g4)]);
-                    const u32x4 aL = ld16(&H.al[SUB * R + l16][sw(l16, 8 * g4)]);
-                    oacc[R] = mfma_bf16(uh, aH, oacc[R]);
-                    o1[R] = mfma_bf16(ul, aH, f32x4{0.f, 0.f, 0.f, 0.f});
-                    o2[R] = mfma_bf16(uh, aL, f32x4{0.f, 0.f, 0.f, 0.f});
+                    aH[R] = ld16(&H.ah[SUB * R + l16][sw(l16, 8 * g4)]);
+                    aL[R] = ld16(&H.al[SUB * R + l16][sw(l16, 8 * g4)]);
                 }
+                f32x4 oc[2];
+#pragma unroll
+                for (int R = 0; R < 2; ++R) oc[R] = mfma_bf16(uh, aH[R], oacc[R]);
+#pragma unroll
+                for (int R = 0; R < 2; ++R) oc[R] = mfma_bf16(ul, aH[R], oc[R]);
+#pragma unroll
+                for (int R = 0; R < 2; ++R) oc[R] = mfma_bf16(uh, aL[R], oc[R]);
 #pragma unroll
                 for (int R = 0; R < 2; ++R) {
-                    const f32x4 acc = (oacc[R] + (o1[R] + o2[R])) * oscale;
+                    const f32x4 acc = oc[R] * oscale;
                     if (t0 + SUB * R + l16 < p.T) {
                         if constexpr (OUT_F32)
                             gstore<f32x4>(ob, ooff[R], acc);
@@ -830,21 +868,32 @@ __device__ __forceinline__ void value_waves(Smem& sm, const Params& p, int bh, s
                 gchar* dst = uniform_gptr(p.S_ckpt + ((size_t)bh * p.n_ckpt + (n / p.ckpt_chunks - 1)) * DK * DV);
                 uint32_t o = soff;
                 asm volatile("" : "+v"(o));  // formed here: offsets held across the loop would spill
+                // S = R / ep with ep = -2^(64 + kappa) of chunk n (-2^64 past the last chunk): the exact
+                // reciprocal of a power of two, by its exponent field
+                const Scalings& Sn = sm.sc[n % 3];
 #pragma unroll
-                for (int cb = 0; cb < 8; ++cb)
+                for (int cb = 0; cb < 8; ++cb) {
+                    f32x4 ie = f32x4{-kDown, -kDown, -kDown, -kDown};
+                    if (n < nchunk) {
+                        const f32x4 e = *reinterpret_cast<const f32x4*>(&Sn.ep[16 * cb + 4 * g4]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) gstore<float>(dst, o + (uint32_t)((16 * cb + r) * DV * 4), st[cb][r]);
+                        for (int r = 0; r < 4; ++r)
+                            ie[r] = __int_as_float((int)(0xff000000u - ((uint32_t)__float_as_int(e[r]) & 0x7f800000u)));
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) gstore<float>(dst, o + (uint32_t)((16 * cb + r) * DV * 4), st[cb][r] * ie[r]);
+                }
             }
         }
         lds_barrier();  // ---- barrier 3
     }
 
-    if (p.S_T) {
+    if (p.S_T) {  // the last chunk left R = -2^64 S
         gchar* sT = uniform_gptr(p.S_T + (size_t)bh * DK * DV);
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) gstore<float>(sT, sidx(cb, r), st[cb][r]);
+            for (int r = 0; r < 4; ++r) gstore<float>(sT, sidx(cb, r), st[cb][r] * -kDown);
     }
 }
 
