@@ -36,8 +36,8 @@ CSRC = os.path.join(ROOT, "linear_recurrent_attention_amd", "csrc")
 # 512 MiB copy (factors 2.0 and 1.0); valid only for the kernel source with the recorded hash.
 MEASURED_TRAFFIC = {
     "core": {"sources": ("kda_fwd_bf16.hip", "kda_common.h"),
-             "sha256": "f93625c09e36ee1c3914e973954e67c9446e0111d06e1ee0bc4931fc84683cf0",
-             "bytes": (1345042 * 2.0 + 532480 * 1.0) * 1024,
+             "sha256": "fc7c872a1c949f39cc001f785ed5e8a78142d0bac52fc1ba07484c5beb6f6b3f",
+             "bytes": (1343798 * 2.0 + 532480 * 1.0) * 1024,
              "profile": "profiles/kda_fwd_bf16_B4_H32_T16384_D128.md"},
     "decode": {"sources": ("kda_decode.hip", "kda_common.h"),
                "sha256": "27169bbf2dad64f9f864da57513ef39a0250b622edfad8163610ea21d502356f",
