@@ -104,6 +104,12 @@ __device__ __forceinline__ constexpr int tperm(int j) { return ((j >> 2) & 3) * 
 __device__ __forceinline__ constexpr int cperm(int c) { return (c & ~31) + tperm(c & 31); }
 // column position of element (row, col) of a [rows][C] tile: 16-byte blocks XOR-swizzled by row
 __device__ __forceinline__ constexpr int sw(int row, int col) { return col ^ (((row >> 1) & 3) << 3); }
+// Physical row of channel r in the Kbar^T tiles.  A key wave stores one 8-byte quarter-row of 64
+// channels 2 apart in one instruction; with rows in channel order those stores fall on 8 of the 16
+// reachable 8-byte bank positions of a 256-byte LDS line (row bit 1 repeats the swizzle's bit), and
+// row bits 3-4 folded into bits 0-1 of the row spread them over all 16.  The reads of a 16-row slab
+// touch the same rows in another order.
+__device__ __forceinline__ constexpr int kbrow(int r) { return r ^ ((r >> 3) & 3); }
 
 // Token-major tiles store channels in cperm order, so that a 16-byte read of a row gives the eight
 // channels a lane contracts over in the state products (whose operand comes straight from the
@@ -116,7 +122,7 @@ struct alignas(16) KeyTiles {                // key waves (written in part 3, re
 struct alignas(16) ChunkTiles {              // between roles, double buffered by chunk parity
     uint16_t qmh[C][LDK], qml[C][LDK];       // Q * exp(b - b_15)         split bf16
     uint16_t km[C][LDK];                     // K * exp(b - b_15)         bf16
-    uint16_t kbh[DK][LDT], kbl[DK][LDT];     // (K * exp(b_31 - b))^T     split bf16, tokens tperm'd
+    uint16_t kbh[DK][LDT], kbl[DK][LDT];     // Kbar'^T split bf16, tokens tperm'd, rows kbrow(channel)
     uint16_t ah[C][LDA], al[C][LDA];         // -2^64 A                   split bf16, columns tperm'd
     uint16_t th[C][LDA], tl[C][LDA];         // 2^-64 T split bf16, columns tperm'd; block (1,0) holds
                                              // 2^64 L(1,0)
@@ -365,8 +371,8 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         const int pt = tperm(tq);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            *reinterpret_cast<u32x2*>(&Hg.kbh[c0 + c][sw(c0 + c, pt)]) = u32x2{h[c][0], h[c][1]};
-            *reinterpret_cast<u32x2*>(&Hg.kbl[c0 + c][sw(c0 + c, pt)]) = u32x2{l[c][0], l[c][1]};
+            *reinterpret_cast<u32x2*>(&Hg.kbh[kbrow(c0 + c)][sw(c0 + c, pt)]) = u32x2{h[c][0], h[c][1]};
+            *reinterpret_cast<u32x2*>(&Hg.kbl[kbrow(c0 + c)][sw(c0 + c, pt)]) = u32x2{l[c][0], l[c][1]};
         }
     }
     if (fwork) {
@@ -852,8 +858,8 @@ __device__ __forceinline__ void value_waves(Smem& sm, const Params& p, int bh, s
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int cb = c4 + j;
-                    aH[j] = ld16(&H.kbh[16 * cb + l16][sw(l16, 8 * g4)]);
-                    aL[j] = ld16(&H.kbl[16 * cb + l16][sw(l16, 8 * g4)]);
+                    aH[j] = ld16(&H.kbh[kbrow(16 * cb + l16)][sw(l16, 8 * g4)]);
+                    aL[j] = ld16(&H.kbl[kbrow(16 * cb + l16)][sw(l16, 8 * g4)]);
                     st[cb] *= *reinterpret_cast<const f32x4*>(&Sc.gam[16 * cb + 4 * g4]);
                 }
 #pragma unroll
