@@ -108,8 +108,10 @@ __device__ __forceinline__ constexpr int sw(int row, int col) { return col ^ (((
 // channels 2 apart in one instruction; with rows in channel order those stores fall on 8 of the 16
 // reachable 8-byte bank positions of a 256-byte LDS line (row bit 1 repeats the swizzle's bit), and
 // row bits 3-4 folded into bits 0-1 of the row spread them over all 16.  The reads of a 16-row slab
-// touch the same rows in another order.
-__device__ __forceinline__ constexpr int kbrow(int r) { return r ^ ((r >> 3) & 3); }
+// touch the same rows in another order.  (The float32-input variant keeps channel order: it has no
+// VGPRs to spare for the permuted addresses.)
+template <bool IN_F32>
+__device__ __forceinline__ constexpr int kbrow(int r) { return IN_F32 ? r : r ^ ((r >> 3) & 3); }
 
 // Token-major tiles store channels in cperm order, so that a 16-byte read of a row gives the eight
 // channels a lane contracts over in the state products (whose operand comes straight from the
@@ -371,8 +373,8 @@ __device__ __forceinline__ void key_step(Smem& sm, const Params& p, const KeyLoa
         const int pt = tperm(tq);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            *reinterpret_cast<u32x2*>(&Hg.kbh[kbrow(c0 + c)][sw(c0 + c, pt)]) = u32x2{h[c][0], h[c][1]};
-            *reinterpret_cast<u32x2*>(&Hg.kbl[kbrow(c0 + c)][sw(c0 + c, pt)]) = u32x2{l[c][0], l[c][1]};
+            *reinterpret_cast<u32x2*>(&Hg.kbh[kbrow<IN_F32>(c0 + c)][sw(c0 + c, pt)]) = u32x2{h[c][0], h[c][1]};
+            *reinterpret_cast<u32x2*>(&Hg.kbl[kbrow<IN_F32>(c0 + c)][sw(c0 + c, pt)]) = u32x2{l[c][0], l[c][1]};
         }
     }
     if (fwork) {
@@ -852,15 +854,28 @@ __device__ __forceinline__ void value_waves(Smem& sm, const Params& p, int bh, s
                     }
                 }
             }
+            // kbrow(16 cb + l16) = 16 cb + (lr ^ 2 (cb & 1)): two lane offsets, the rest immediate
+            constexpr int kodd = IN_F32 ? 0 : 2;
+            const int lr = IN_F32 ? l16 : l16 ^ (l16 >> 3), kcol = sw(l16, 8 * g4);
 #pragma unroll
             for (int c4 = 0; c4 < 8; c4 += 4) {  // four row blocks at a time, term by term
                 u32x4 aH[4], aL[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int cb = c4 + j;
-                    aH[j] = ld16(&H.kbh[kbrow(16 * cb + l16)][sw(l16, 8 * g4)]);
-                    aL[j] = ld16(&H.kbl[kbrow(16 * cb + l16)][sw(l16, 8 * g4)]);
-                    st[cb] *= *reinterpret_cast<const f32x4*>(&Sc.gam[16 * cb + 4 * g4]);
+                    aH[j] = ld16(&H.kbh[16 * cb + (lr ^ ((cb & 1) * kodd))][kcol]);
+                    aL[j] = ld16(&H.kbl[16 * cb + (lr ^ ((cb & 1) * kodd))][kcol]);
+                    if constexpr (!IN_F32) {
+                        // rho of rows 16cb + 4g4 + r: lane r of each 16-lane row reads it, and the multiply
+                        // takes it by row broadcast (a quarter of the LDS bytes of a 16-byte read per lane)
+                        const float rh = Sc.gam[16 * cb + 4 * g4 + (l16 & 3)];
+                        st[cb][0] *= row_bcast<0>(rh);
+                        st[cb][1] *= row_bcast<1>(rh);
+                        st[cb][2] *= row_bcast<2>(rh);
+                        st[cb][3] *= row_bcast<3>(rh);
+                    } else {  // (the float32-input variant has no registers to spare for it)
+                        st[cb] *= *reinterpret_cast<const f32x4*>(&Sc.gam[16 * cb + 4 * g4]);
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) st[c4 + j] = mfma_bf16(aH[j], uh, st[c4 + j]);
