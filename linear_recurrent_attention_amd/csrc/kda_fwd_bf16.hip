@@ -136,8 +136,9 @@ struct alignas(16) Scalings {                // state scalings of one chunk, by 
     float gam[DK];                           // rho = 2^(kappa' - kappa) exp(b_31), kappa' the next chunk's
 };
 struct alignas(16) VStage {                  // 2^64 v of one chunk, loaded by the helper waves for the value
-    float x[NVW][64][8];                     // waves: [value wave][lane][4R + r] = token 16R + 4*g4 + r of the
-                                             // lane's column (zero past T, or when v == NULL)
+    float x[NVW][2][64][4];                  // waves: [value wave][R][lane][r] = token 16R + 4*g4 + r of the
+                                             // lane's column (zero past T, or when v == NULL); each 16-byte
+                                             // access of a wave covers 1 KB contiguously (no bank conflicts)
 };
 struct alignas(16) Single {                  // written and read within one step
     float lf[C][LDF];                        // -Diag(beta) L on the two diagonal blocks
@@ -567,9 +568,8 @@ __device__ __forceinline__ void helper_waves(Smem& sm, const Params& p, size_t r
                     for (int r = 0; r < 4; ++r)
                         x[4 * R + r] = (p.v && t0 + SUB * R + 4 * g4 + r < p.T) ? kUp * x[4 * R + r] : 0.f;
             }
-            f32x4* dst = reinterpret_cast<f32x4*>(&sm.vs[n & 1].x[hw][lane][0]);
-            dst[0] = f32x4{x[0], x[1], x[2], x[3]};
-            dst[1] = f32x4{x[4], x[5], x[6], x[7]};
+            *reinterpret_cast<f32x4*>(&sm.vs[n & 1].x[hw][0][lane][0]) = f32x4{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<f32x4*>(&sm.vs[n & 1].x[hw][1][lane][0]) = f32x4{x[4], x[5], x[6], x[7]};
         }
         load_v(min(n + 1, nchunk - 1) * C);  // v of the chunk after (unconditionally, as in load_chunk)
         lds_barrier();  // ---- barrier 1
@@ -784,8 +784,8 @@ __device__ __forceinline__ void value_waves(Smem& sm, const Params& p, int bh, s
         u32x4 uh, ul;
         if (work) {
             // 2^64 V in accumulator layout (tokens 16R + 4*g4 + r, column col), staged by a helper wave
-            const f32x4* vx = reinterpret_cast<const f32x4*>(&sm.vs[c & 1].x[vw][lane][0]);
-            f32x4 xr[2] = {vx[0], vx[1]};
+            f32x4 xr[2] = {*reinterpret_cast<const f32x4*>(&sm.vs[c & 1].x[vw][0][lane][0]),
+                           *reinterpret_cast<const f32x4*>(&sm.vs[c & 1].x[vw][1][lane][0])};
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
