@@ -36,8 +36,8 @@ CSRC = os.path.join(ROOT, "linear_recurrent_attention_amd", "csrc")
 # 512 MiB copy (factors 2.0 and 1.0); valid only for the kernel source with the recorded hash.
 MEASURED_TRAFFIC = {
     "core": {"sources": ("kda_fwd_bf16.hip", "kda_common.h"),
-             "sha256": "fc7c872a1c949f39cc001f785ed5e8a78142d0bac52fc1ba07484c5beb6f6b3f",
-             "bytes": (1343798 * 2.0 + 532480 * 1.0) * 1024,
+             "sha256": "9bbeb734738b0ab09f697de23b40b272d44bf3f233b3068f2ef463322f1d75a3",
+             "bytes": (1343653 * 2.0 + 532480 * 1.0) * 1024,
              "profile": "profiles/kda_fwd_bf16_B4_H32_T16384_D128.md"},
     "decode": {"sources": ("kda_decode.hip", "kda_common.h"),
                "sha256": "27169bbf2dad64f9f864da57513ef39a0250b622edfad8163610ea21d502356f",
